@@ -1,0 +1,69 @@
+"""Seeded synthetic inputs for the h_aggregate forward and backward.
+
+Shared by the tests, the benchmark and the smoke check. It holds none of the
+operation's arithmetic: it only draws random numbers and stores them in the
+operation's input formats (bf16 bit patterns via torch's CPU conversion,
+fp32 as drawn).
+
+Recipe (the pages print no value distributions; these follow the shapes of
+the page "Add batch-invariant h_aggregate kernel", sections Correctness and
+Performance):
+  rng = numpy.random.default_rng(seed)      (PCG64), draws in this order:
+  residual [T,4,H] = bf16(rng.standard_normal(float32))
+  pre      [T,4]   = rng.random(float32)                 U[0,1), gate-like
+  grad_out [T,H]   = bf16(rng.normal(0, 0.1) as float32)   (if requested)
+  outliers         = rng.random((T,4,H)) < 0.01 scales residual by 64 before
+                     the bf16 conversion (if requested; exact power of two)
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+HC = 4
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 array -> uint16 bf16 bit patterns, through torch's CPU cast."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def make_inputs(T: int, H: int, seed: int = 0, *, grad: bool = False,
+                outliers: bool = False) -> dict[str, np.ndarray]:
+    """Host inputs: residual (uint16 [T,4,H]), pre (float32 [T,4]) and,
+    if grad, grad_out (uint16 [T,H])."""
+    rng = np.random.default_rng(seed)
+    res = rng.standard_normal((T, HC, H), dtype=np.float32)
+    pre = rng.random((T, HC), dtype=np.float32)
+    out = {"pre": pre}
+    if grad:
+        out["grad_out"] = to_bf16_bits(rng.normal(0.0, 0.1, (T, H)).astype(np.float32))
+    if outliers:
+        mask = rng.random((T, HC, H)) < 0.01
+        res = np.where(mask, res * np.float32(64.0), res).astype(np.float32)
+    out["residual"] = to_bf16_bits(res)
+    return out
+
+
+def bits_to_bf16_tensor(bits: np.ndarray, device="cpu") -> torch.Tensor:
+    """uint16 bf16 patterns -> torch.bfloat16 tensor (same bits)."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    return t.to(device)
+
+
+def bf16_tensor_to_bits(t: torch.Tensor) -> np.ndarray:
+    """torch.bfloat16 (any device) -> uint16 bit patterns on the host."""
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def to_device(inputs: dict[str, np.ndarray], device) -> dict[str, torch.Tensor]:
+    """Copy host inputs to the device with identical bytes."""
+    out = {}
+    for k, v in inputs.items():
+        if v.dtype == np.uint16:
+            out[k] = bits_to_bf16_tensor(v, device)
+        else:
+            out[k] = torch.from_numpy(np.ascontiguousarray(v)).to(device)
+    return out

@@ -1,0 +1,605 @@
+"""Pins of the CPU oracle (oracle/h_aggregate.py) to things other than itself.
+
+Each test states what it pins and why a plausible mistake in the oracle would
+fail it. Sources: page "Add batch-invariant h_aggregate kernel" (RL-Kernel
+pull request 366), sections Summary (formula, shapes), Batch invariance
+(fp32 round-to-nearest mul/add, (0+1)+(2+3) tree, bf16 only at the
+boundaries), Correctness (tolerance of the PyTorch comparison), and the
+review comments (backward requested). The page prints no output values, so
+the expected values here come from hand derivations (written out in each
+test), exact rational arithmetic, closed forms and invariants.
+"""
+
+from __future__ import annotations
+
+import functools
+import json
+import os
+from fractions import Fraction
+from pathlib import Path
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import h_aggregate as O
+from hyper_connection_residual_mhc_amd.workloads import make_inputs, to_bf16_bits
+
+GOLDEN = Path(__file__).resolve().parent / "golden"
+
+F32 = np.float32
+
+
+def f32_from_bits(u: int) -> np.float32:
+    return np.array([u], dtype=np.uint32).view(np.float32)[0]
+
+
+def bits_of_f32(x) -> int:
+    return int(np.array([x], dtype=np.float32).view(np.uint32)[0])
+
+
+def bf16_bits(x: float) -> np.uint16:
+    """bf16 pattern of a value that bf16 represents exactly (asserted)."""
+    u = bits_of_f32(np.float32(x))
+    assert u & 0xFFFF == 0, f"{x} is not a bf16 value"
+    return np.uint16(u >> 16)
+
+
+# ---------------------------------------------------------------------------
+# Independent references used by the pins (not the oracle's code paths)
+# ---------------------------------------------------------------------------
+
+def indep_bf16_round(bits: np.ndarray) -> np.ndarray:
+    """bf16 RNE of finite fp32 patterns via float64 arithmetic: scale by the
+    bf16 spacing of the value's binade, np.rint (half to even), scale back.
+    Shares nothing with the oracle's integer carry trick."""
+    bits = bits.astype(np.uint32)
+    x = bits.view(np.float32).astype(np.float64)
+    a = np.abs(x)
+    _, e = np.frexp(a)
+    expo = np.maximum(e - 1, -126)
+    ulp = np.ldexp(1.0, expo - 7)
+    v = np.rint(a / ulp) * ulp
+    with np.errstate(over="ignore"):
+        mag = np.where(v >= 2.0 ** 128, np.uint32(0x7F800000),
+                       v.astype(np.float32).view(np.uint32))
+    return ((mag >> np.uint32(16)) | ((bits >> np.uint32(31)) << np.uint32(15))).astype(np.uint16)
+
+
+def round_to_f32(x: Fraction) -> Fraction:
+    """Round an exact rational to the nearest fp32 value (ties to even, with
+    gradual underflow), as a rational. Overflow is not needed here."""
+    if x == 0:
+        return Fraction(0)
+    sign = -1 if x < 0 else 1
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    e = max(e, -126)                      # subnormal spacing below 2**-126
+    ulp = Fraction(2) ** (e - 23)
+    q, r = divmod(a, ulp)
+    q = int(q)
+    half = ulp / 2
+    if r > half or (r == half and q % 2 == 1):
+        q += 1
+    return sign * q * ulp
+
+
+def round_to_bf16(x: Fraction) -> Fraction:
+    """Round an exact rational to the nearest bf16 value (ties to even)."""
+    if x == 0:
+        return Fraction(0)
+    sign = -1 if x < 0 else 1
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    e = max(e, -126)
+    ulp = Fraction(2) ** (e - 7)
+    q, r = divmod(a, ulp)
+    q = int(q)
+    half = ulp / 2
+    if r > half or (r == half and q % 2 == 1):
+        q += 1
+    return sign * q * ulp
+
+
+def frac_bf16_bits(v: Fraction) -> int:
+    return int(bf16_bits(float(v)))
+
+
+# ---------------------------------------------------------------------------
+# bf16 rounding (Batch invariance: one bf16 conversion at the output)
+# ---------------------------------------------------------------------------
+
+def test_bf16_hand_cases():
+    """Hand-derived patterns. 1+2^-8 lies halfway between bf16 1.0 (0x3F80)
+    and 1+2^-7 (0x3F81): ties go to the even pattern 0x3F80. 1+3*2^-8 lies
+    halfway between 0x3F81 and 0x3F82: the even one is 0x3F82. The largest
+    finite fp32 is above bf16's largest finite + half a spacing: Inf. The
+    smallest bf16 subnormal (fp32 bits 0x00010000) is kept; fp32's smallest
+    subnormal rounds to zero; exactly half of the smallest bf16 subnormal
+    ties to even (zero); one and a half of it ties to 2 (even)."""
+    cases = {
+        0x3F808000: 0x3F80, 0x3F818000: 0x3F82, 0x3F808001: 0x3F81,
+        0x7F7FFFFF: 0x7F80, 0xFF7FFFFF: 0xFF80, 0x7F800000: 0x7F80, 0xFF800000: 0xFF80,
+        0x00010000: 0x0001, 0x00000001: 0x0000, 0x00008000: 0x0000, 0x00018000: 0x0002,
+        0x80000001: 0x8000, 0x00000000: 0x0000, 0x80000000: 0x8000,
+        0x3F7FFFFF: 0x3F80,   # just below 1.0: rounds up across the binade
+        0x7F7F8000: 0x7F80,   # tie at the top: 0x7F7F is odd -> rounds up to Inf
+        0x7F7E8000: 0x7F7E,   # tie with even low pattern stays
+    }
+    got = O.bf16_rne(np.array(list(cases), dtype=np.uint32).view(np.float32))
+    assert [hex(int(g)) for g in got] == [hex(v) for v in cases.values()]
+
+
+def test_bf16_nan_stays_nan():
+    """NaN handling is unspecified on the page; the reading is 'NaN in, NaN out'."""
+    pats = np.array([0x7F800001, 0x7FC00000, 0xFFFFFFFF, 0x7F80FFFF, 0xFF800001], dtype=np.uint32)
+    got = O.bf16_rne(pats.view(np.float32))
+    widened = O.widen_bf16(got)
+    assert np.isnan(widened).all()
+
+
+def _stratified_patterns() -> np.ndarray:
+    """Every fp32 high half combined with every low half at which round to
+    nearest even can change its decision (0, 1, just below / at / above the
+    midpoint 0x8000, the top), plus pseudo-random low halves."""
+    hi = np.arange(1 << 16, dtype=np.uint32) << np.uint32(16)
+    lows = [0x0000, 0x0001, 0x0002, 0x3FFF, 0x4000, 0x7FFE, 0x7FFF, 0x8000, 0x8001, 0x8002,
+            0xBFFF, 0xC000, 0xFFFE, 0xFFFF]
+    rng = np.random.default_rng(1234)
+    lows += [int(v) for v in rng.integers(0, 1 << 16, 24)]
+    return (hi[:, None] | np.array(lows, dtype=np.uint32)[None, :]).ravel()
+
+
+def test_bf16_matches_independent_rounding_on_all_decision_boundaries():
+    """Oracle bf16 RNE == float64 rint-based rounding for every fp32 high half
+    with the low halves where the rounding decision flips, and 4M random
+    patterns. NaNs are excluded (only 'is NaN' is specified)."""
+    pats = np.concatenate([_stratified_patterns(),
+                           np.random.default_rng(7).integers(0, 1 << 32, 1 << 22,
+                                                             dtype=np.uint64).astype(np.uint32)])
+    finite = (pats & np.uint32(0x7FFFFFFF)) <= np.uint32(0x7F800000)
+    pats = pats[finite]
+    got = O.bf16_rne(pats.view(np.float32))
+    want = indep_bf16_round(pats)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, f"{bad.size} mismatches, first pattern 0x{int(pats[bad[0]]):08x}"
+
+
+@pytest.mark.skipif(os.environ.get("MHC_EXHAUSTIVE") != "1",
+                    reason="full 2^32 sweep takes ~30 CPU-minutes; set MHC_EXHAUSTIVE=1")
+def test_bf16_exhaustive_all_2pow32():
+    """All 2^32 fp32 patterns (NaNs excluded) against the independent rounding."""
+    chunk = 1 << 24
+    for start in range(0, 1 << 32, chunk):
+        pats = np.arange(start, start + chunk, dtype=np.uint64).astype(np.uint32)
+        pats = pats[(pats & np.uint32(0x7FFFFFFF)) <= np.uint32(0x7F800000)]
+        assert np.array_equal(O.bf16_rne(pats.view(np.float32)), indep_bf16_round(pats)), hex(start)
+
+
+def test_widen_is_exact():
+    """Widening puts the 16 bits on top of a zero low half: every bf16 pattern
+    maps to the fp32 pattern (b << 16), and narrowing it back is the identity."""
+    b = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    w = O.widen_bf16(b)
+    assert np.array_equal(w.view(np.uint32), b.astype(np.uint32) << np.uint32(16))
+    not_nan = ~np.isnan(w)
+    assert np.array_equal(O.bf16_rne(w)[not_nan], b[not_nan])
+
+
+# ---------------------------------------------------------------------------
+# fp32 arithmetic model (Batch invariance: fp32 round-to-nearest mul and add)
+# ---------------------------------------------------------------------------
+
+def test_numpy_f32_ops_are_round_to_nearest_with_denormals():
+    """The oracle's model: one np.float32 multiply or add == the exact
+    rational result rounded to nearest even fp32, with gradual underflow.
+    Checked with exact rationals on random operands, including products
+    that land in the subnormal range."""
+    rng = np.random.default_rng(3)
+    n = 4000
+    a = (rng.standard_normal(n) * np.exp2(rng.integers(-70, 10, n))).astype(F32)
+    b = (rng.standard_normal(n) * np.exp2(rng.integers(-70, 10, n))).astype(F32)
+    prod = np.multiply(a, b)
+    summ = np.add(a, b)
+    assert (np.abs(prod) < np.finfo(np.float32).tiny).sum() > 100   # subnormals exercised
+    for i in range(n):
+        fa, fb = Fraction(float(a[i])), Fraction(float(b[i]))
+        assert Fraction(float(prod[i])) == round_to_f32(fa * fb), i
+        assert Fraction(float(summ[i])) == round_to_f32(fa + fb), i
+
+
+# ---------------------------------------------------------------------------
+# Forward (Summary formula; Batch invariance arithmetic)
+# ---------------------------------------------------------------------------
+
+def fwd_one(pre4, r4) -> int:
+    """Oracle forward of one element: pre4 fp32 values, r4 bf16-exact values."""
+    residual = np.array([bf16_bits(v) for v in r4], dtype=np.uint16).reshape(1, 4, 1)
+    pre = np.array(pre4, dtype=np.float32).reshape(1, 4)
+    return int(O.h_aggregate_fwd(residual, pre)[0, 0])
+
+
+def load_golden(name: str) -> dict:
+    return json.loads((GOLDEN / name).read_text())
+
+
+def test_forward_golden_vectors():
+    """Hand-derived single-element cases stored in tests/golden/ (each entry
+    carries its derivation). They pin the association (0+1)+(2+3), the
+    absence of fused multiply-add, and the bf16 tie rule."""
+    doc = load_golden("forward_hand_vectors.json")
+    for case in doc["cases"]:
+        pre = [f32_from_bits(int(p, 16)) for p in case["pre_bits"]]
+        res = np.array([int(r, 16) for r in case["residual_bits"]], dtype=np.uint16).reshape(1, 4, 1)
+        got = int(O.h_aggregate_fwd(res, np.array(pre, dtype=np.float32).reshape(1, 4))[0, 0])
+        assert got == int(case["out_bits"], 16), case["name"]
+
+
+def test_forward_tree_discriminator_rejects_other_associations():
+    """With pre = [1+2^-8, 0, 1, 1] and r = [1, 5, 2^-24, 2^-24] the page's tree
+    gives (1+2^-8) + 2^-23, which bf16-rounds up to 0x3F81. Sequential
+    ((0+1)+2)+3 and (0+2)+(1+3) both lose the 2^-24 terms to ties-to-even in
+    fp32 and give 0x3F80. Checked here with exact rationals so that the
+    alternatives are computed, not asserted."""
+    pre = [Fraction(1) + Fraction(1, 256), Fraction(0), Fraction(1), Fraction(1)]
+    r = [Fraction(1), Fraction(5), Fraction(1, 2 ** 24), Fraction(1, 2 ** 24)]
+    p = [round_to_f32(a * b) for a, b in zip(pre, r)]
+    add = lambda x, y: round_to_f32(x + y)  # noqa: E731
+    spec = frac_bf16_bits(round_to_bf16(add(add(p[0], p[1]), add(p[2], p[3]))))
+    seq = frac_bf16_bits(round_to_bf16(add(add(add(p[0], p[1]), p[2]), p[3])))
+    alt = frac_bf16_bits(round_to_bf16(add(add(p[0], p[2]), add(p[1], p[3]))))
+    assert (spec, seq, alt) == (0x3F81, 0x3F80, 0x3F80)
+    assert fwd_one([float(x) for x in pre], [float(x) for x in r]) == spec
+
+
+def test_forward_fma_discriminator():
+    """pre0 = 0x3F7F01FD (16712189 * 2^-24), r0 = 1+2^-7, pre1 = 2^-25, r1 = 1,
+    pre2 = pre3 = 0. The exact p0 is 1 + 2^-8 + 125*2^-31; fp32 rounds it to
+    1+2^-8 (125 < 128 = half a spacing). Without contraction the sum stays
+    1+2^-8 (2^-25 is below half a spacing) and bf16 ties to 0x3F80. A fused
+    fma(pre0, r0, p1) sees 1 + 2^-8 + 189*2^-31, rounds up to 1+2^-8+2^-23
+    and gives 0x3F81 - as does the exact value, which is why the fp64 gate
+    allows more than half an ulp."""
+    pre0 = Fraction(16712189, 2 ** 24)
+    assert bits_of_f32(np.float32(float(pre0))) == 0x3F7F01FD
+    r0 = Fraction(1) + Fraction(1, 128)
+    exact_p0 = pre0 * r0
+    assert exact_p0 == 1 + Fraction(1, 256) + Fraction(125, 2 ** 31)
+    p1 = Fraction(1, 2 ** 25)
+    fused = round_to_f32(exact_p0 + p1)
+    assert frac_bf16_bits(round_to_bf16(fused)) == 0x3F81
+    assert frac_bf16_bits(round_to_bf16(exact_p0 + p1)) == 0x3F81
+    got = fwd_one([float(pre0), 2.0 ** -25, 0.0, 0.0], [float(r0), 1.0, 1.0, 1.0])
+    assert got == 0x3F80
+
+
+def test_forward_matches_exact_rational_evaluation_small():
+    """Brute force on a tiny random batch: every element recomputed with
+    exact rationals, each operation rounded to fp32, one bf16 rounding."""
+    inp = make_inputs(2, 24, seed=5)
+    res, pre = inp["residual"], inp["pre"]
+    got = O.h_aggregate_fwd(res, pre)
+    r = O.widen_bf16(res)
+    add = lambda x, y: round_to_f32(x + y)  # noqa: E731
+    for t in range(2):
+        for h in range(24):
+            p = [round_to_f32(Fraction(float(pre[t, i])) * Fraction(float(r[t, i, h])))
+                 for i in range(4)]
+            y = add(add(p[0], p[1]), add(p[2], p[3]))
+            assert int(got[t, h]) == frac_bf16_bits(round_to_bf16(y)), (t, h)
+
+
+def test_forward_one_hot_pre_copies_stream():
+    """pre = e_i makes out = r_i: 1*r is exact, the other products are signed
+    zeros, adding zeros keeps the value (only the sign of a zero may differ)."""
+    inp = make_inputs(3, 257, seed=11)
+    for i in range(4):
+        pre = np.zeros((3, 4), np.float32)
+        pre[:, i] = 1.0
+        out = O.h_aggregate_fwd(inp["residual"], pre)
+        assert np.array_equal(O.widen_bf16(out), O.widen_bf16(inp["residual"][:, i, :]))
+
+
+def test_forward_equal_quarters_average():
+    """pre = 1/4 each and four equal streams: 0.25r + 0.25r = 0.5r exactly,
+    0.5r + 0.5r = r exactly, so out == r bit for bit (normal r)."""
+    inp = make_inputs(2, 300, seed=2)
+    r = inp["residual"][:, :1, :].repeat(4, axis=1)
+    out = O.h_aggregate_fwd(r, np.full((2, 4), 0.25, np.float32))
+    assert np.array_equal(out, inp["residual"][:, 0, :])
+
+
+def test_forward_power_of_two_scaling_is_exact():
+    """Scaling all of pre by 2^k scales every product, sum and the bf16 result
+    by exactly 2^k (no overflow or underflow at these magnitudes)."""
+    inp = make_inputs(4, 512, seed=3)
+    base = O.widen_bf16(O.h_aggregate_fwd(inp["residual"], inp["pre"])).astype(np.float64)
+    for k in (-5, 3, 9):
+        scaled = O.widen_bf16(O.h_aggregate_fwd(inp["residual"],
+                                                (inp["pre"] * np.float32(2.0 ** k)).astype(np.float32)))
+        assert np.array_equal(scaled.astype(np.float64), base * 2.0 ** k)
+
+
+def test_forward_tree_symmetries():
+    """The tree (0+1)+(2+3) is unchanged by swapping 0<->1, 2<->3, or the pairs
+    (0,1)<->(2,3) (fp32 addition commutes), so the output bytes are too. The
+    transposition 1<->2 is not a symmetry: the discriminator case changes."""
+    inp = make_inputs(8, 640, seed=4, outliers=True)
+    res, pre = inp["residual"], inp["pre"]
+    base = O.h_aggregate_fwd(res, pre)
+    for perm in ([1, 0, 2, 3], [0, 1, 3, 2], [2, 3, 0, 1], [3, 2, 1, 0]):
+        assert np.array_equal(O.h_aggregate_fwd(res[:, perm, :].copy(), pre[:, perm].copy()), base)
+    pre_d = [1 + 2.0 ** -8, 0.0, 1.0, 1.0]
+    r_d = [1.0, 5.0, 2.0 ** -24, 2.0 ** -24]
+    swapped = [pre_d[0], pre_d[2], pre_d[1], pre_d[3]], [r_d[0], r_d[2], r_d[1], r_d[3]]
+    assert fwd_one(pre_d, r_d) != fwd_one(*swapped)
+
+
+def test_forward_fp64_gate_with_outliers():
+    """Against the fp64 value of sum pre_i r_i: every output is within one bf16
+    ulp, or (cancellation) within the depth-3 fp32 bound plus half an ulp.
+    Inputs have the 1% x64 outliers of the bandwidth workload."""
+    inp = make_inputs(64, 7168, seed=0, outliers=True)
+    out = O.h_aggregate_fwd(inp["residual"], inp["pre"])
+    exact, mag = O.h_aggregate_fwd_exact(inp["residual"], inp["pre"])
+    c = O.classify_fwd(out, exact, mag)
+    assert c["fail"] == 0, c
+    assert c["within_1ulp"] >= 0.999 * out.size, c
+
+
+def test_forward_fp64_gate_catches_a_dropped_term():
+    """The gate is sharp enough to see a missing product: dropping stream 3
+    from the sum fails it for most elements."""
+    inp = make_inputs(4, 1024, seed=9)
+    pre = inp["pre"].copy()
+    exact, mag = O.h_aggregate_fwd_exact(inp["residual"], pre)
+    pre[:, 3] = 0.0
+    wrong = O.h_aggregate_fwd(inp["residual"], pre)
+    assert O.classify_fwd(wrong, exact, mag)["fail"] > 0.5 * wrong.size
+
+
+def test_forward_matches_torch_reference_within_page_tolerance():
+    """The page's test compares with a PyTorch reference at atol 5e-2 and rtol
+    1e-2 (section Correctness). Here the reference is torch fp32 on the CPU
+    (its own summation order), then bf16."""
+    inp = make_inputs(16, 4096, seed=0)
+    out = O.widen_bf16(O.h_aggregate_fwd(inp["residual"], inp["pre"]))
+    r = torch.from_numpy(O.widen_bf16(inp["residual"]))
+    p = torch.from_numpy(inp["pre"])
+    ref = (p[:, :, None] * r).sum(dim=1).to(torch.bfloat16).float()
+    torch.testing.assert_close(torch.from_numpy(out), ref, atol=5e-2, rtol=1e-2)
+
+
+def test_forward_is_per_token():
+    """Batch invariance in the oracle: a token's output does not depend on the
+    other tokens (here: the full batch vs each token alone)."""
+    inp = make_inputs(9, 100, seed=6)
+    full = O.h_aggregate_fwd(inp["residual"], inp["pre"])
+    for t in range(9):
+        one = O.h_aggregate_fwd(inp["residual"][t:t + 1], inp["pre"][t:t + 1])
+        assert np.array_equal(one[0], full[t])
+
+
+# ---------------------------------------------------------------------------
+# Backward: grad_residual
+# ---------------------------------------------------------------------------
+
+def test_grad_residual_power_of_two_pre_is_exact():
+    """pre = 2^k makes pre*g exact and representable in bf16: the result is g's
+    pattern with the exponent moved by k."""
+    inp = make_inputs(3, 200, seed=8, grad=True)
+    for k in (-3, 0, 2):
+        pre = np.full((3, 4), 2.0 ** k, np.float32)
+        gr = O.grad_residual_ref(pre, inp["grad_out"])
+        g = O.widen_bf16(inp["grad_out"]).astype(np.float64)
+        assert np.array_equal(O.widen_bf16(gr).astype(np.float64), np.repeat(g[:, None, :] * 2.0 ** k, 4, 1))
+
+
+def test_grad_residual_within_one_ulp_of_exact():
+    """One fp32 product then one bf16 rounding: within one bf16 ulp of the
+    exact product pre*g (strict, no cancellation possible)."""
+    inp = make_inputs(16, 2048, seed=1, grad=True)
+    gr = O.grad_residual_ref(inp["pre"], inp["grad_out"])
+    exact = inp["pre"].astype(np.float64)[:, :, None] * O.widen_bf16(inp["grad_out"]).astype(np.float64)[:, None, :]
+    err = np.abs(O.widen_bf16(gr).astype(np.float64) - exact)
+    assert (err <= O.bf16_ulp(gr)).all()
+
+
+def test_grad_residual_matches_exact_rational_small():
+    inp = make_inputs(2, 16, seed=12, grad=True)
+    gr = O.grad_residual_ref(inp["pre"], inp["grad_out"])
+    g = O.widen_bf16(inp["grad_out"])
+    for t in range(2):
+        for i in range(4):
+            for h in range(16):
+                y = round_to_f32(Fraction(float(inp["pre"][t, i])) * Fraction(float(g[t, h])))
+                assert int(gr[t, i, h]) == frac_bf16_bits(round_to_bf16(y))
+
+
+# ---------------------------------------------------------------------------
+# Backward: grad_pre and the fixed reduction order
+# ---------------------------------------------------------------------------
+
+def test_grad_pre_products_exact_assertion():
+    """bf16 x bf16 has at most 16 significant bits: the fp32 product equals the
+    fp64 product (the oracle asserts this; here it is exercised on the
+    backward workload's distributions)."""
+    inp = make_inputs(8, 7168, seed=0, grad=True)
+    q = O.grad_pre_products(inp["residual"], inp["grad_out"])
+    assert q.shape == (8, 4, 7168)
+
+
+def test_grad_pre_integer_inputs_are_exact():
+    """g = 1 and small-integer residuals: every partial sum is an integer below
+    2^24, so any order is exact and grad_pre equals the integer sum."""
+    T, H = 3, 5000
+    rng = np.random.default_rng(0)
+    rint = rng.integers(-8, 9, (T, 4, H))
+    res = np.vectorize(lambda v: int(bf16_bits(float(v))), otypes=[np.uint16])(rint)
+    g = np.full((T, H), bf16_bits(1.0), np.uint16)
+    gp = O.grad_pre_ref(res, g)
+    assert np.array_equal(gp.astype(np.int64), rint.sum(axis=2))
+
+
+def test_grad_pre_one_hot_grad_out():
+    """grad_out = 1 at one position h0, 0 elsewhere: grad_pre[t,i] = r_i[h0]
+    exactly (adding signed zeros to +0 or to a value never changes it)."""
+    inp = make_inputs(2, 3000, seed=13)
+    for h0 in (0, 7, 8, 2047, 2048, 2999):
+        g = np.zeros((2, 3000), np.uint16)
+        g[:, h0] = bf16_bits(1.0)
+        gp = O.grad_pre_ref(inp["residual"], g)
+        assert np.array_equal(gp, O.widen_bf16(inp["residual"][:, :, h0]))
+
+
+def test_grad_pre_short_rows_are_sequential_sums():
+    """For H <= 8 the whole row is group 0 of lane 0: the result is the plain
+    left-to-right fp32 sum of the products (all other lanes add +0)."""
+    for H in range(1, 9):
+        inp = make_inputs(3, H, seed=H, grad=True)
+        q = O.grad_pre_products(inp["residual"], inp["grad_out"])
+        want = np.array([[functools.reduce(lambda a, b: np.float32(a + b), q[t, i], np.float32(0.0))
+                          for i in range(4)] for t in range(3)], np.float32)
+        assert np.array_equal(O.grad_pre_ref(inp["residual"], inp["grad_out"]), want)
+
+
+def _tree_case(H: int, entries: dict[int, float]) -> np.float32:
+    q = np.zeros((1, H), np.float32)
+    for h, v in entries.items():
+        q[0, h] = v
+    return O.canonical_tree_sum(q)[0]
+
+
+E = 2.0 ** -24   # half an fp32 spacing at 1.0: 1 + E ties back to 1
+
+
+def test_tree_hand_cases_pin_each_level():
+    """Hand-derived values that pin each level of the fixed order. x + E
+    with x = 1 ties to even (stays 1); E + E = 2E is exact; 1 + 2E is exact.
+
+    * chain order inside a lane: q[0]=1, q[1]=E, q[2]=E (one group, lane 0):
+      ((1+E)+E) = 1. A pairwise or reversed chain would give 1+2E.
+    * lane assignment k mod 256: groups 0 and 256 share lane 0; with q[0]=1 and
+      q[2048]=E, q[2056]=E (groups 256, 257: lanes 0, 1): lane 0 = 1+E = 1,
+      lane 1 = E; wave tree adds them at off=1: 1+E = 1. Contiguous lane
+      ownership would put the two E together (2E) and give 1+2E.
+    * wave tree order (32, 16, ..., 1): q at groups 0, 1, 33 (lanes 0, 1, 33):
+      1, E, E. off=32 makes lane 1 = E+E = 2E; off=1 gives 1+2E. Adjacent-first
+      (offsets 1..32) would add 1+E first and give 1.
+    * block stage (y0+y2)+(y1+y3): waves 0, 1, 3 hold 1, E, E (groups 0, 64,
+      192): (1+0)+(E+E) = 1+2E. Pairing (y0+y1)+(y2+y3) gives 1.
+    """
+    one_plus_2e = np.float32(1.0 + 2 * E)
+    assert _tree_case(8, {0: 1.0, 1: E, 2: E}) == np.float32(1.0)
+    assert _tree_case(8 * 258, {0: 1.0, 8 * 256: E, 8 * 257: E}) == np.float32(1.0)
+    assert _tree_case(8 * 34, {0: 1.0, 8 * 1: E, 8 * 33: E}) == one_plus_2e
+    assert _tree_case(8 * 193, {0: 1.0, 8 * 64: E, 8 * 192: E}) == one_plus_2e
+
+
+def _sequential(q):
+    acc = np.zeros(q.shape[:-1], np.float32)
+    for h in range(q.shape[-1]):
+        acc = np.add(acc, q[..., h])
+    return acc
+
+
+def _stride_halving(q):
+    x = q.copy()
+    n = 1
+    while n < x.shape[-1]:
+        n *= 2
+    x = np.concatenate([x, np.zeros(x.shape[:-1] + (n - x.shape[-1],), np.float32)], -1)
+    while x.shape[-1] > 1:
+        half = x.shape[-1] // 2
+        x = np.add(x[..., :half], x[..., half:])
+    return x[..., 0]
+
+
+def test_alternative_orders_differ_on_backward_workload():
+    """The bit-exact grad_pre comparison can tell orders apart: on the backward
+    workload's distributions, a sequential sum, a global stride-halving tree
+    and numpy's pairwise float32 sum each differ from the fixed order on
+    some elements."""
+    inp = make_inputs(64, 7168, seed=0, grad=True)
+    q = O.grad_pre_products(inp["residual"], inp["grad_out"])
+    ref = O.canonical_tree_sum(q)
+    for alt in (_sequential(q), _stride_halving(q), q.sum(axis=-1, dtype=np.float32)):
+        assert (alt.view(np.uint32) != ref.view(np.uint32)).sum() > 0
+
+
+def test_grad_pre_fp64_gate():
+    """Against the fp64 sum: |err| <= 1e-6 * sum|q| per element (the chosen
+    reading of 'within 1e-6 relative of an fp64 sum' that survives
+    cancellation), and below the rigorous depth bound of the fixed order."""
+    inp = make_inputs(128, 7168, seed=0, grad=True)
+    gp = O.grad_pre_ref(inp["residual"], inp["grad_out"]).astype(np.float64)
+    exact, mag = O.grad_pre_exact(inp["residual"], inp["grad_out"])
+    err = np.abs(gp - exact)
+    assert (err <= 1e-6 * mag).all()
+    assert (err <= O.tree_error_bound(7168) * mag + 1e-300).all()
+    assert np.max(err) / np.max(np.abs(exact)) <= 1e-6
+
+
+def test_grad_pre_fp64_gate_catches_a_transposed_operand():
+    """Summing grad_out against the wrong stream (a transposed index) breaks
+    the fp64 gate."""
+    inp = make_inputs(8, 2048, seed=1, grad=True)
+    exact, mag = O.grad_pre_exact(inp["residual"], inp["grad_out"])
+    wrong = O.grad_pre_ref(inp["residual"][:, ::-1, :].copy(), inp["grad_out"]).astype(np.float64)
+    assert (np.abs(wrong - exact) > 1e-6 * mag).mean() > 0.5
+
+
+def test_grad_pre_is_per_token_and_depends_only_on_h():
+    inp = make_inputs(5, 3001, seed=14, grad=True)
+    full = O.grad_pre_ref(inp["residual"], inp["grad_out"])
+    for t in range(5):
+        one = O.grad_pre_ref(inp["residual"][t:t + 1], inp["grad_out"][t:t + 1])
+        assert np.array_equal(one[0], full[t])
+
+
+def test_backward_is_gradient_of_forward():
+    """Consistency with autograd of the exact formula: torch fp64 autograd of
+    sum_h g * sum_i pre_i r_i gives grad_pre = sum_h g r_i and
+    grad_residual = pre_i g; the oracle is within its error bounds of both."""
+    inp = make_inputs(4, 1500, seed=15, grad=True)
+    r = torch.from_numpy(O.widen_bf16(inp["residual"]).astype(np.float64)).requires_grad_(True)
+    p = torch.from_numpy(inp["pre"].astype(np.float64)).requires_grad_(True)
+    g = torch.from_numpy(O.widen_bf16(inp["grad_out"]).astype(np.float64))
+    y = (p[:, :, None] * r).sum(dim=1)
+    y.backward(g)
+    gr, gp = O.h_aggregate_bwd(inp["residual"], inp["pre"], inp["grad_out"])
+    mag = (g.abs()[:, None, :] * r.detach().abs()).sum(-1).numpy()
+    assert (np.abs(gp.astype(np.float64) - p.grad.numpy()) <= 1e-6 * mag).all()
+    err = np.abs(O.widen_bf16(gr).astype(np.float64) - r.grad.numpy())
+    assert (err <= O.bf16_ulp(gr)).all()
+
+
+# ---------------------------------------------------------------------------
+# Input generator
+# ---------------------------------------------------------------------------
+
+def test_inputs_are_seeded_and_shaped():
+    a = make_inputs(16, 4096, seed=0, grad=True, outliers=True)
+    b = make_inputs(16, 4096, seed=0, grad=True, outliers=True)
+    for k in a:
+        assert np.array_equal(a[k], b[k])
+    assert a["residual"].shape == (16, 4, 4096) and a["residual"].dtype == np.uint16
+    assert a["pre"].shape == (16, 4) and a["pre"].dtype == np.float32
+    assert a["grad_out"].shape == (16, 4096)
+    r = O.widen_bf16(make_inputs(16, 4096, seed=0)["residual"])
+    assert abs(float(r.mean())) < 0.01 and abs(float(r.std()) - 1) < 0.01
+    g = O.widen_bf16(a["grad_out"])
+    assert abs(float(g.std()) - 0.1) < 0.002
+    big = np.abs(O.widen_bf16(a["residual"])) > 8
+    assert 0.005 < big.mean() < 0.015
+    assert (a["pre"] >= 0).all() and (a["pre"] < 1).all()
+
+
+def test_to_bf16_bits_is_round_to_nearest_even():
+    """The generator's torch CPU conversion rounds like an independent RNE."""
+    x = np.random.default_rng(2).standard_normal(1 << 16).astype(np.float32)
+    assert np.array_equal(to_bf16_bits(x), indep_bf16_round(x.view(np.uint32)))
