@@ -124,7 +124,7 @@ def h_aggregate_fwd(residual: np.ndarray, pre: np.ndarray) -> np.ndarray:
     """
     T, H = _check_fwd_args(residual, pre)
     r = widen_bf16(residual)                                   # [T,4,H] fp32, exact
-    with np.errstate(over="ignore"):                           # overflow to Inf is IEEE
+    with np.errstate(over="ignore", invalid="ignore"):         # Inf / NaN are IEEE results
         p = [np.multiply(pre[:, i:i + 1], r[:, i, :]) for i in range(HC)]
         s01 = np.add(p[0], p[1])
         s23 = np.add(p[2], p[3])
@@ -178,17 +178,22 @@ def grad_pre_products(residual: np.ndarray, grad_out: np.ndarray) -> np.ndarray:
     """q[t,i,h] = grad_out[t,h] * residual[t,i,h] in fp32.
 
     Both factors are bf16 (8 significant bits each), so the product has at
-    most 16 significant bits and the fp32 multiply is exact unless it leaves
-    the fp32 range. The function asserts that exactness against fp64.
+    most 16 significant bits and the fp32 multiply is exact whenever the
+    product lies in fp32's normal range. Products below 2**-126 fall into the
+    subnormal range, where fewer bits are available, and are rounded to
+    nearest like any other fp32 product; products above the largest finite
+    fp32 overflow. The function asserts exactness against fp64 for the
+    products in the normal range.
     """
     g = widen_bf16(grad_out)
     r = widen_bf16(residual)
     with np.errstate(over="ignore"):
         q = np.multiply(g[:, None, :], r)
     q64 = g.astype(np.float64)[:, None, :] * r.astype(np.float64)
-    finite = np.isfinite(q64) & (np.abs(q64) <= np.finfo(np.float32).max)
-    assert np.array_equal(q.astype(np.float64)[finite], q64[finite]), \
-        "bf16 x bf16 product not exact in fp32"
+    a64 = np.abs(q64)
+    normal = (a64 >= np.finfo(np.float32).tiny) & (a64 <= np.finfo(np.float32).max)
+    assert np.array_equal(q.astype(np.float64)[normal], q64[normal]), \
+        "bf16 x bf16 product in the normal range not exact in fp32"
     return q
 
 

@@ -426,11 +426,24 @@ def test_grad_residual_matches_exact_rational_small():
 
 def test_grad_pre_products_exact_assertion():
     """bf16 x bf16 has at most 16 significant bits: the fp32 product equals the
-    fp64 product (the oracle asserts this; here it is exercised on the
-    backward workload's distributions)."""
+    fp64 product in fp32's normal range (the oracle asserts this; here it is
+    exercised on the backward workload's distributions)."""
     inp = make_inputs(8, 7168, seed=0, grad=True)
     q = O.grad_pre_products(inp["residual"], inp["grad_out"])
     assert q.shape == (8, 4, 7168)
+
+
+def test_grad_pre_products_round_in_the_subnormal_range():
+    """Below 2^-126 the product can lose bits: 2^-70 * (1+2^-7) * 2^-70 *
+    (1+2^-7) = 2^-140 * (1 + 2^-6 + 2^-14); fp32 subnormals are multiples of
+    2^-149, so the 2^-154 term is rounded off (to nearest: it is below half
+    a spacing) and the product is 2^-140 * (1 + 2^-6)."""
+    a = bf16_bits(2.0 ** -70 * (1 + 2.0 ** -7))
+    res = np.full((1, 4, 1), a, np.uint16)
+    g = np.full((1, 1), a, np.uint16)
+    q = O.grad_pre_products(res, g)
+    assert float(q[0, 0, 0]) == 2.0 ** -140 * (1 + 2.0 ** -6)
+    assert Fraction(float(q[0, 0, 0])) == round_to_f32(Fraction(2.0 ** -70 * (1 + 2.0 ** -7)) ** 2)
 
 
 def test_grad_pre_integer_inputs_are_exact():
