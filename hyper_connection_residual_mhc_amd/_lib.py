@@ -1,0 +1,92 @@
+"""ctypes view of the C ABI in include/mhc_h_aggregate.h.
+
+Loading fails loudly (ImportError) when the shared library has not been
+built: there is no other implementation to fall back on.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from ctypes import POINTER, c_char_p, c_int, c_int32, c_int64, c_uint32, c_void_p
+
+from ._build import LIB_PATH
+
+MHC_SUCCESS = 0
+MHC_ERROR_INVALID_VALUE = 1
+MHC_ERROR_ALIASING = 2
+MHC_ERROR_HIP = 3
+MHC_ABI_VERSION = 1
+MHC_MAX_H = 1 << 26
+
+
+class mhc_launch(ctypes.Structure):
+    """Launch shape (see the header): 0 in a field means "policy chooses"."""
+    _fields_ = [
+        ("block_threads", c_int32),
+        ("vec_width", c_int32),
+        ("units_per_thread", c_int32),
+        ("tokens_per_block", c_int32),
+    ]
+
+    def as_dict(self) -> dict:
+        return {name: int(getattr(self, name)) for name, _ in self._fields_}
+
+
+# name -> (restype, argtypes); every symbol the header declares.
+SIGNATURES = {
+    "mhc_abi_version": (c_int, []),
+    "mhc_status_string": (c_char_p, [c_int]),
+    "mhc_last_error_message": (c_char_p, []),
+    "mhc_h_aggregate_fwd": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_void_p]),
+    "mhc_h_aggregate_fwd_ex": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_void_p,
+                                       POINTER(mhc_launch)]),
+    "mhc_h_aggregate_bwd": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                    c_int64, c_int64, c_void_p]),
+    "mhc_h_aggregate_bwd_ex": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                       c_int64, c_int64, c_void_p, POINTER(mhc_launch)]),
+    "mhc_h_aggregate_validate_fwd": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64]),
+    "mhc_h_aggregate_validate_bwd": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                             c_int64, c_int64]),
+    "mhc_h_aggregate_plan_fwd": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64,
+                                         POINTER(mhc_launch), POINTER(mhc_launch),
+                                         POINTER(c_int64)]),
+    "mhc_h_aggregate_plan_bwd": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                         c_int64, c_int64, POINTER(mhc_launch),
+                                         POINTER(mhc_launch), POINTER(c_int64)]),
+    "mhc_bf16_rne_probe": (c_int, [c_uint32, c_int64, c_void_p, c_void_p]),
+}
+
+_lib: ctypes.CDLL | None = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loaded once). Raises ImportError if not built."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                "(the operation has no other implementation)")
+        handle = ctypes.CDLL(str(LIB_PATH))
+        for name, (restype, argtypes) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = restype
+            fn.argtypes = argtypes
+        if handle.mhc_abi_version() != MHC_ABI_VERSION:
+            raise ImportError("libmhc_h_aggregate ABI version mismatch")
+        _lib = handle
+    return _lib
+
+
+class MhcError(RuntimeError):
+    """A non-success status from the library, with its message."""
+
+    def __init__(self, status: int, message: str):
+        self.status = status
+        name = lib().mhc_status_string(status).decode()
+        super().__init__(f"{name}: {message}")
+
+
+def check(status: int) -> None:
+    if status != MHC_SUCCESS:
+        raise MhcError(status, lib().mhc_last_error_message().decode())

@@ -1,0 +1,205 @@
+/*
+ * mhc_h_aggregate.h - C ABI of the MI355X (gfx950) mHC pre / H-aggregate
+ * library: the forward collapse of the hyper-connection residual stream and
+ * its backward.
+ *
+ * Operation (page "Add batch-invariant h_aggregate kernel", RL-Kernel pull
+ * request 366, section Summary):
+ *
+ *     residual [T, 4, H]  bf16      (hyper-connection expansion 4)
+ *     pre      [T, 4]     fp32
+ *     out      [T, H]     bf16
+ *     out[t,h] = bf16( (pre[t,0]*r0 + pre[t,1]*r1) + (pre[t,2]*r2 + pre[t,3]*r3) ),
+ *     r_i = residual[t,i,h]
+ *
+ * Arithmetic contract (same page, section Batch invariance): every product
+ * and sum is one fp32 operation rounded to nearest even, never fused into a
+ * multiply-add; the association is the fixed tree (0+1)+(2+3); bf16 inputs
+ * are widened exactly and the result is rounded to bf16 (nearest even) once.
+ * Denormals are kept. Each output element is produced by one thread with no
+ * atomics, so the bytes of out[t,:] depend only on residual[t], pre[t] and H:
+ * never on T, on the batch partition, or on the launch configuration.
+ *
+ * Backward (asked for in the same page's review comments so that training
+ * can converge; the formulas are the derivative of the forward):
+ *
+ *     grad_residual[t,i,h] = bf16( pre[t,i] * grad_out[t,h] )       (written)
+ *     grad_pre[t,i]        = sum over h of grad_out[t,h] * residual[t,i,h]
+ *
+ * Each grad_out*residual product is one fp32 round-to-nearest multiply; it
+ * is exact (two 8-bit significands) unless it falls below fp32's normal range.
+ * The sum over h follows one fixed order that depends only on H, so
+ * grad_pre is batch invariant:
+ *   1. 256 fp32 accumulator lanes start at +0.0;
+ *   2. group k holds the 8 consecutive elements h = 8k..8k+7 (the last group
+ *      may be short); groups are visited in ascending k and group k is
+ *      added, element by element in ascending h, to lane (k mod 256);
+ *   3. lanes form 4 waves of 64; in each wave, for off = 32,16,8,4,2,1 in
+ *      that order, x[j] += x[j+off] for all j < off; the wave result is x[0];
+ *   4. grad_pre = (y0 + y2) + (y1 + y3) over the four wave results.
+ * Every addition is one fp32 round-to-nearest-even operation.
+ *
+ * Common rules for every entry point below
+ *   - All tensor pointers are DEVICE pointers on the current HIP device; the
+ *     caller owns every buffer. bf16 tensors are passed as raw uint16_t bit
+ *     patterns. Tensors are contiguous and row-major in the shapes above.
+ *   - `stream` is a hipStream_t cast to void*; NULL means the null stream.
+ *     Calls only enqueue work: they never synchronise, and inputs must stay
+ *     valid until the stream reaches the call. The library allocates no
+ *     memory and keeps no mutable global state; it is reentrant.
+ *   - T == 0 is a successful no-op (pointers may then be NULL). T < 0,
+ *     H < 1, H > MHC_MAX_H, a NULL pointer when T > 0, a pointer that is not
+ *     aligned to its element size, or sizes whose byte counts overflow
+ *     int64 give MHC_ERROR_INVALID_VALUE. Any overlap between an output and
+ *     an input, or between the two backward outputs, gives
+ *     MHC_ERROR_ALIASING. On either error nothing is launched and no output
+ *     is touched. A failed kernel launch gives MHC_ERROR_HIP.
+ *   - A misaligned or odd-H buffer is not an error: it only narrows the
+ *     vector width, which never changes a result bit.
+ *   - mhc_last_error_message() returns a text describing the most recent
+ *     failure on the calling thread.
+ */
+#ifndef MHC_H_AGGREGATE_H
+#define MHC_H_AGGREGATE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MHC_ABI_VERSION 1
+
+/* Hyper-connection expansion rate, fixed at 4 (Summary: residual [T, 4, H]). */
+#define MHC_HC 4
+
+/* Largest hidden size accepted. */
+#define MHC_MAX_H (1LL << 26)
+
+typedef enum mhc_status {
+  MHC_SUCCESS = 0,
+  MHC_ERROR_INVALID_VALUE = 1,
+  MHC_ERROR_ALIASING = 2,
+  MHC_ERROR_HIP = 3
+} mhc_status;
+
+/*
+ * Launch shape. Passed to the *_ex entry points as an override (a field of
+ * 0 means "let the launch policy choose") and returned by the plan queries
+ * with every field filled in. No field changes any result bit: they exist so
+ * that tests can prove that and benchmarks can sweep shapes.
+ *   block_threads     forward: threads per block, a multiple of 64 in
+ *                     [64, 1024]; backward: must be 0 or 256 (one block of
+ *                     4 waves owns a token's reduction).
+ *   vec_width         bf16 elements per vector access: 1, 2, 4 or 8. It must
+ *                     divide H and match the alignment of every bf16 buffer.
+ *   units_per_thread  forward: vector units each thread handles; backward:
+ *                     8-element groups each lane loads before its
+ *                     arithmetic. 1, 2 or 4.
+ *   tokens_per_block  backward only: tokens one block handles in sequence,
+ *                     1..4096.
+ */
+typedef struct mhc_launch {
+  int32_t block_threads;
+  int32_t vec_width;
+  int32_t units_per_thread;
+  int32_t tokens_per_block;
+} mhc_launch;
+
+/* Version of this ABI (MHC_ABI_VERSION of the built library). */
+int mhc_abi_version(void);
+
+/* Static name of a status code ("MHC_SUCCESS", ...). Never NULL. */
+const char* mhc_status_string(mhc_status status);
+
+/* Text describing the last failure on the calling thread ("" if none).
+ * Valid until the next call into this library on that thread. */
+const char* mhc_last_error_message(void);
+
+/*
+ * Forward (Summary and Batch invariance of "Add batch-invariant h_aggregate
+ * kernel").
+ *   residual  [T,4,H] bf16 bits, read
+ *   pre       [T,4]   fp32, read
+ *   out       [T,H]   bf16 bits, written (every element, once)
+ */
+mhc_status mhc_h_aggregate_fwd(const uint16_t* residual, const float* pre,
+                               uint16_t* out, int64_t T, int64_t H,
+                               void* stream);
+
+/* Forward with a launch-shape override (NULL = same as mhc_h_aggregate_fwd).
+ * An override the buffers cannot honour gives MHC_ERROR_INVALID_VALUE. */
+mhc_status mhc_h_aggregate_fwd_ex(const uint16_t* residual, const float* pre,
+                                  uint16_t* out, int64_t T, int64_t H,
+                                  void* stream, const mhc_launch* launch);
+
+/*
+ * Backward (review comments of "Add batch-invariant h_aggregate kernel":
+ * the gradient of the forward formula).
+ *   residual       [T,4,H] bf16 bits, read
+ *   pre            [T,4]   fp32, read
+ *   grad_out       [T,H]   bf16 bits, read
+ *   grad_residual  [T,4,H] bf16 bits, written: bf16(pre[t,i]*grad_out[t,h])
+ *   grad_pre       [T,4]   fp32, written: the fixed-order sum above
+ * Both gradients are overwritten, never accumulated into.
+ */
+mhc_status mhc_h_aggregate_bwd(const uint16_t* residual, const float* pre,
+                               const uint16_t* grad_out,
+                               uint16_t* grad_residual, float* grad_pre,
+                               int64_t T, int64_t H, void* stream);
+
+/* Backward with a launch-shape override (NULL = same as the plain call). */
+mhc_status mhc_h_aggregate_bwd_ex(const uint16_t* residual, const float* pre,
+                                  const uint16_t* grad_out,
+                                  uint16_t* grad_residual, float* grad_pre,
+                                  int64_t T, int64_t H, void* stream,
+                                  const mhc_launch* launch);
+
+/*
+ * Host-only checks and plan queries. They touch no device and no memory
+ * behind the pointers (the pointers are used only as numbers for alignment
+ * and overlap tests), so they run without a GPU.
+ *
+ * validate_*: the status the matching compute call would return before any
+ * launch (argument, alignment and aliasing rules above).
+ * plan_*: validates like the compute call, then writes the launch shape it
+ * would use into *plan and the number of blocks it would launch in total
+ * into *grid_blocks (either output pointer may be NULL).
+ */
+mhc_status mhc_h_aggregate_validate_fwd(const uint16_t* residual,
+                                        const float* pre, const uint16_t* out,
+                                        int64_t T, int64_t H);
+mhc_status mhc_h_aggregate_validate_bwd(const uint16_t* residual,
+                                        const float* pre,
+                                        const uint16_t* grad_out,
+                                        const uint16_t* grad_residual,
+                                        const float* grad_pre, int64_t T,
+                                        int64_t H);
+mhc_status mhc_h_aggregate_plan_fwd(const uint16_t* residual, const float* pre,
+                                    const uint16_t* out, int64_t T, int64_t H,
+                                    const mhc_launch* launch, mhc_launch* plan,
+                                    int64_t* grid_blocks);
+mhc_status mhc_h_aggregate_plan_bwd(const uint16_t* residual, const float* pre,
+                                    const uint16_t* grad_out,
+                                    const uint16_t* grad_residual,
+                                    const float* grad_pre, int64_t T,
+                                    int64_t H, const mhc_launch* launch,
+                                    mhc_launch* plan, int64_t* grid_blocks);
+
+/*
+ * Conversion probe: out[k] = bf16 bits of the fp32 value whose bit pattern
+ * is (first_bits + k) mod 2^32, for k in [0, n), rounded by the same device
+ * routine the kernels use for every bf16 result (round to nearest even,
+ * the single output rounding of Batch invariance).
+ * Lets tests compare the device rounding with an independent one over any
+ * range of fp32 patterns, including all 2^32. out: [n] uint16, device.
+ * 0 <= n <= 2^32.
+ */
+mhc_status mhc_bf16_rne_probe(uint32_t first_bits, int64_t n, uint16_t* out,
+                              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHC_H_AGGREGATE_H */

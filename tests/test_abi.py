@@ -1,0 +1,249 @@
+"""The C ABI on the host: symbols, argument rules and the launch policy.
+
+These run without a GPU: they load the library and call only its host-only
+entry points (validate / plan / status strings), which never touch a device.
+Rules under test are the ones include/mhc_h_aggregate.h states.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import re
+import subprocess
+from pathlib import Path
+
+import pytest
+import torch
+
+from hyper_connection_residual_mhc_amd import _build, _lib, ops
+from hyper_connection_residual_mhc_amd._lib import (MHC_ERROR_ALIASING, MHC_ERROR_INVALID_VALUE,
+                                                    MHC_SUCCESS, MhcError)
+
+HEADER = _build.HEADER
+GiB = 1 << 30
+BASE = 16 * GiB          # a 256-byte-aligned fake device address
+
+
+@pytest.fixture(scope="module")
+def lib(built_library):
+    return _lib.lib()
+
+
+def declared_functions() -> list[str]:
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mhc_\w+)\s*\(", text)))
+
+
+def test_header_declarations_are_all_exported(lib, built_library):
+    names = declared_functions()
+    assert len(names) >= 12
+    out = subprocess.run(["nm", "-D", "--defined-only", str(built_library)],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (mhc_\w+)$", out, flags=re.M))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(lib, n)
+    assert set(_lib.SIGNATURES) == set(names)
+
+
+def test_exports_are_c_symbols_only(built_library):
+    """Nothing but the mhc_ C names is exported from the library's own code."""
+    out = subprocess.run(["nm", "-D", "--defined-only", str(built_library)],
+                         capture_output=True, text=True, check=True).stdout
+    text_syms = re.findall(r"\bT (\S+)$", out, flags=re.M)
+    ours = [s for s in text_syms if "mhc" in s or "hagg" in s]
+    assert all(s.startswith("mhc_") for s in ours), ours
+
+
+def test_version_and_status_strings(lib):
+    assert lib.mhc_abi_version() == _lib.MHC_ABI_VERSION
+    assert lib.mhc_status_string(0) == b"MHC_SUCCESS"
+    assert lib.mhc_status_string(1) == b"MHC_ERROR_INVALID_VALUE"
+    assert lib.mhc_status_string(2) == b"MHC_ERROR_ALIASING"
+    assert lib.mhc_status_string(3) == b"MHC_ERROR_HIP"
+    assert lib.mhc_status_string(99) == b"MHC_ERROR_UNKNOWN"
+
+
+def fwd_ptrs(T, H, base=BASE):
+    res = base
+    pre = res + 8 * T * H + 4096
+    out = pre + 16 * T + 4096
+    return res, pre, out
+
+
+def bwd_ptrs(T, H, base=BASE):
+    res = base
+    pre = res + 8 * T * H + 4096
+    g = pre + 16 * T + 4096
+    gr = g + 2 * T * H + 4096
+    gp = gr + 8 * T * H + 4096
+    return res, pre, g, gr, gp
+
+
+def test_validate_fwd_rules(lib):
+    T, H = 16, 4096
+    r, p, o = fwd_ptrs(T, H)
+    v = ops.mhc_h_aggregate_validate_fwd
+    assert v(r, p, o, T, H) == MHC_SUCCESS
+    assert v(0, 0, 0, 0, H) == MHC_SUCCESS                 # T == 0: no-op, NULL allowed
+    assert v(r, p, o, -1, H) == MHC_ERROR_INVALID_VALUE
+    assert v(r, p, o, T, 0) == MHC_ERROR_INVALID_VALUE
+    assert v(r, p, o, 0, 0) == MHC_ERROR_INVALID_VALUE
+    assert v(r, p, o, T, _lib.MHC_MAX_H + 1) == MHC_ERROR_INVALID_VALUE
+    for args in ((0, p, o), (r, 0, o), (r, p, 0)):
+        assert v(*args, T, H) == MHC_ERROR_INVALID_VALUE
+    assert v(r + 1, p, o, T, H) == MHC_ERROR_INVALID_VALUE  # bf16 must be 2-byte aligned
+    assert v(r, p + 2, o, T, H) == MHC_ERROR_INVALID_VALUE  # fp32 must be 4-byte aligned
+    assert v(r, p, o + 1, T, H) == MHC_ERROR_INVALID_VALUE
+    # byte counts overflowing int64
+    assert v(r, p, o, (1 << 62), 8) == MHC_ERROR_INVALID_VALUE
+
+
+def test_validate_fwd_aliasing(lib):
+    T, H = 16, 4096
+    r, p, o = fwd_ptrs(T, H)
+    v = ops.mhc_h_aggregate_validate_fwd
+    assert v(r, p, r, T, H) == MHC_ERROR_ALIASING                      # out == residual
+    assert v(r, p, r + 8 * T * H - 2, T, H) == MHC_ERROR_ALIASING      # last element overlaps
+    far = r + 64 * GiB
+    assert v(r, far, r + 8 * T * H, T, H) == MHC_SUCCESS               # adjacent is fine
+    assert v(r, far, far - 2 * T * H + 2, T, H) == MHC_ERROR_ALIASING  # out runs into pre
+    assert v(r, far, far - 2 * T * H, T, H) == MHC_SUCCESS
+    # inputs may overlap each other (both are read-only)
+    assert v(r, r, o, T, H) == MHC_SUCCESS
+
+
+def test_validate_bwd_rules_and_aliasing(lib):
+    T, H = 8, 1279
+    r, p, g, gr, gp = bwd_ptrs(T, H)
+    v = ops.mhc_h_aggregate_validate_bwd
+    assert v(r, p, g, gr, gp, T, H) == MHC_SUCCESS
+    assert v(0, 0, 0, 0, 0, 0, H) == MHC_SUCCESS
+    for i in range(5):
+        args = [r, p, g, gr, gp]
+        args[i] = 0
+        assert v(*args, T, H) == MHC_ERROR_INVALID_VALUE, i
+    assert v(r, p, g, gr, gp + 2, T, H) == MHC_ERROR_INVALID_VALUE
+    assert v(r, p, g, r, gp, T, H) == MHC_ERROR_ALIASING          # grad_residual == residual
+    assert v(r, p, g, gr, g, T, H) == MHC_ERROR_ALIASING          # grad_pre inside grad_out
+    assert v(r, p, g, gr, gr + 64, T, H) == MHC_ERROR_ALIASING    # the two outputs overlap
+    assert v(r, p, g, gr, p, T, H) == MHC_ERROR_ALIASING          # grad_pre == pre
+
+
+def test_error_message_names_the_problem(lib):
+    T, H = 4, 64
+    r, p, o = fwd_ptrs(T, H)
+    with pytest.raises(MhcError, match="ALIASING.*out overlaps input residual"):
+        ops.mhc_h_aggregate_plan_fwd(r, p, r, T, H)
+    with pytest.raises(MhcError, match="INVALID_VALUE.*pre is NULL"):
+        ops.mhc_h_aggregate_plan_fwd(r, 0, o, T, H)
+
+
+def test_forward_plan_changes_with_T_but_not_the_math(lib):
+    """The batch-split check needs different launch shapes for a 129-token
+    batch and a 1-token call (the page's own check used 512 vs 1024 threads)."""
+    r, p, o = fwd_ptrs(129, 4096)
+    full, g_full = ops.mhc_h_aggregate_plan_fwd(r, p, o, 129, 4096)
+    one, g_one = ops.mhc_h_aggregate_plan_fwd(r, p, o, 1, 4096)
+    assert full["block_threads"] != one["block_threads"]
+    assert full["vec_width"] == one["vec_width"] == 8
+    assert g_full == 129 * (512 // full["block_threads"])
+
+
+def test_forward_plan_vector_width_follows_alignment_and_H(lib):
+    T = 4
+    cases = [(4096, 0, 8), (4096, 2, 1), (4096, 4, 2), (4096, 8, 4), (4100, 0, 4),
+             (4098, 0, 2), (1279, 0, 1), (1, 0, 1), (8, 0, 8)]
+    for H, shift, want in cases:
+        r, p, o = fwd_ptrs(T, H)
+        plan, _ = ops.mhc_h_aggregate_plan_fwd(r + shift, p, o, T, H)
+        assert plan["vec_width"] == want, (H, shift, plan)
+
+
+def test_forward_plan_grid_covers_every_unit(lib):
+    for T, H in [(1, 4096), (8, 4096), (128, 7168), (1024, 7168), (8192, 7168), (3, 1279),
+                 (5, 1), (2, 65536)]:
+        r, p, o = fwd_ptrs(T, H)
+        plan, grid = ops.mhc_h_aggregate_plan_fwd(r, p, o, T, H)
+        units = H // plan["vec_width"]
+        per_block = plan["block_threads"] * plan["units_per_thread"]
+        assert grid == T * -(-units // per_block), (T, H, plan)
+        assert grid * plan["block_threads"] >= T * units / plan["units_per_thread"]
+
+
+def test_forward_overrides(lib):
+    T, H = 16, 4096
+    r, p, o = fwd_ptrs(T, H)
+    plan, _ = ops.mhc_h_aggregate_plan_fwd(r, p, o, T, H, launch={"block_threads": 1024,
+                                                                   "vec_width": 2,
+                                                                   "units_per_thread": 4})
+    assert plan == {"block_threads": 1024, "vec_width": 2, "units_per_thread": 4,
+                    "tokens_per_block": 0}
+    for bad in ({"block_threads": 100}, {"block_threads": 2048}, {"vec_width": 3},
+                {"units_per_thread": 3}, {"units_per_thread": 9}):
+        with pytest.raises(MhcError, match="INVALID_VALUE"):
+            ops.mhc_h_aggregate_plan_fwd(r, p, o, T, H, launch=bad)
+    with pytest.raises(MhcError, match="vec_width 8 not allowed"):
+        ops.mhc_h_aggregate_plan_fwd(r, p, o, T, 4100, launch={"vec_width": 8})
+    with pytest.raises(MhcError, match="vec_width 4 not allowed"):
+        ops.mhc_h_aggregate_plan_fwd(r + 4, p, o, T, H, launch={"vec_width": 4})
+
+
+def test_backward_plan_and_overrides(lib):
+    T, H = 2048, 7168
+    r, p, g, gr, gp = bwd_ptrs(T, H)
+    plan, grid = ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T, H)
+    assert plan["block_threads"] == 256 and plan["vec_width"] == 8
+    assert grid == -(-T // plan["tokens_per_block"])
+    plan, grid = ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T, H,
+                                              launch={"tokens_per_block": 3, "vec_width": 4,
+                                                      "units_per_thread": 1})
+    assert plan["tokens_per_block"] == 3 and plan["vec_width"] == 4 and grid == -(-T // 3)
+    for bad in ({"block_threads": 128}, {"tokens_per_block": 5000}, {"vec_width": 16},
+                {"units_per_thread": 3}):
+        with pytest.raises(MhcError, match="INVALID_VALUE"):
+            ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T, H, launch=bad)
+    # grad_out misaligned by one element forces the scalar path
+    plan, _ = ops.mhc_h_aggregate_plan_bwd(r, p, g + 2, gr, gp, T, H)
+    assert plan["vec_width"] == 1
+
+
+def test_probe_rejects_bad_sizes(lib):
+    assert lib.mhc_bf16_rne_probe(0, -1, 1024, None) == MHC_ERROR_INVALID_VALUE
+    assert lib.mhc_bf16_rne_probe(0, (1 << 32) + 1, 1024, None) == MHC_ERROR_INVALID_VALUE
+    assert lib.mhc_bf16_rne_probe(0, 0, 0, None) == MHC_SUCCESS
+    assert lib.mhc_bf16_rne_probe(0, 16, 0, None) == MHC_ERROR_INVALID_VALUE
+    assert lib.mhc_bf16_rne_probe(0, 16, 1025, None) == MHC_ERROR_INVALID_VALUE
+
+
+def test_binding_rejects_host_tensors_without_calling_the_library(lib):
+    res = torch.zeros((2, 4, 8), dtype=torch.bfloat16)
+    pre = torch.zeros((2, 4), dtype=torch.float32)
+    with pytest.raises(TypeError, match="must be on a GPU"):
+        ops.h_aggregate(res, pre)
+    with pytest.raises(ValueError, match=r"\[T, 4, H\]"):
+        ops.h_aggregate(torch.zeros((2, 3, 8), dtype=torch.bfloat16), pre)
+
+
+def test_compute_call_with_invalid_args_returns_before_any_hip_call(lib):
+    """Argument errors are reported by the compute entry points themselves
+    (no launch is attempted, so this runs without a GPU)."""
+    T, H = 4, 64
+    r, p, o = fwd_ptrs(T, H)
+    assert lib.mhc_h_aggregate_fwd(r, p, r, T, H, None) == MHC_ERROR_ALIASING
+    assert lib.mhc_h_aggregate_fwd(r, p, o, -3, H, None) == MHC_ERROR_INVALID_VALUE
+    assert lib.mhc_h_aggregate_fwd(0, 0, 0, 0, H, None) == MHC_SUCCESS
+    rr, pp, g, gr, gp = bwd_ptrs(T, H)
+    assert lib.mhc_h_aggregate_bwd(rr, pp, g, gr, gr, T, H, None) == MHC_ERROR_ALIASING
+    bad = _lib.mhc_launch(block_threads=64)
+    assert lib.mhc_h_aggregate_bwd_ex(rr, pp, g, gr, gp, T, H, None,
+                                      ctypes.byref(bad)) == MHC_ERROR_INVALID_VALUE
+
+
+def test_missing_library_raises_import_error(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", Path(tmp_path) / "absent.so")
+    with pytest.raises(ImportError, match="missing"):
+        _lib.lib()

@@ -1,0 +1,148 @@
+"""gradient_accuracy: the gfx950 backward against the CPU oracle.
+
+The backward is the derivative of the forward of page "Add batch-invariant
+h_aggregate kernel" (RL-Kernel pull request 366), asked for in its review
+comments. Tolerances: grad_residual 0 ulp; grad_pre bit-exact against the
+oracle's fixed reduction order, and within 1e-6 * sum|g*r| of the fp64 sum.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import assert_bytes_equal
+from gpu_util import offset_copy_bf16, run_bwd, say
+from hyper_connection_residual_mhc_amd import ops
+from hyper_connection_residual_mhc_amd.workloads import (bf16_tensor_to_bits, make_inputs,
+                                                         to_device)
+from oracle import h_aggregate as O
+
+pytestmark = pytest.mark.gpu
+
+
+def check_bwd(host, got_gr, got_gp, what):
+    want_gr, want_gp = O.h_aggregate_bwd(host["residual"], host["pre"], host["grad_out"])
+    assert_bytes_equal(got_gr, want_gr, f"{what} grad_residual")
+    assert_bytes_equal(got_gp, want_gp, f"{what} grad_pre")
+
+
+def test_backward_bit_exact_backward_workload(device):
+    """T=2048, H=7168: every element of both gradients, plus the fp64 gate."""
+    say("backward parity T=2048 H=7168")
+    host = make_inputs(2048, 7168, seed=0, grad=True)
+    gr, gp = run_bwd(host, device)
+    check_bwd(host, gr, gp, "T=2048")
+    exact, mag = O.grad_pre_exact(host["residual"], host["grad_out"])
+    assert (np.abs(gp.astype(np.float64) - exact) <= 1e-6 * mag).all()
+
+
+@pytest.mark.parametrize("T,H", [(1, 4096), (8, 4096), (128, 7168), (1024, 7168), (129, 4096),
+                                 (3, 1279)])
+def test_backward_bit_exact_page_shapes(device, T, H):
+    say(f"backward parity T={T} H={H}")
+    host = make_inputs(T, H, seed=T + H, grad=True)
+    gr, gp = run_bwd(host, device)
+    check_bwd(host, gr, gp, f"T={T} H={H}")
+
+
+@pytest.mark.parametrize("H", [1, 2, 3, 7, 8, 9, 15, 16, 17, 100, 511, 512, 513, 1276, 1278, 2047,
+                               2048, 2049, 2056, 4100, 16392, 20001])
+def test_backward_bit_exact_ragged_hidden_sizes(device, H):
+    """Short and long rows: fewer groups than lanes, exactly one group per
+    lane, several rounds per lane (H > 2048), short last groups, every
+    vector width."""
+    say(f"backward ragged H={H}")
+    host = make_inputs(4, H, seed=H, grad=True)
+    gr, gp = run_bwd(host, device)
+    check_bwd(host, gr, gp, f"H={H}")
+
+
+def test_backward_large_batch_sampled_tokens(device):
+    """T=8192, H=7168 in one call; 128 sampled tokens against the oracle."""
+    T, H = 8192, 7168
+    say(f"backward parity T={T} H={H} sampled")
+    host = make_inputs(T, H, seed=3, grad=True, outliers=True)
+    gr, gp = run_bwd(host, device)
+    toks = np.unique(np.concatenate([[0, T - 1],
+                                     np.random.default_rng(5).choice(T, 126, replace=False)]))
+    sub = {k: v[toks] for k, v in host.items()}
+    check_bwd(sub, gr[toks], gp[toks], "sampled")
+
+
+def test_backward_special_values(device):
+    """Signed zeros, subnormal products, overflow: bit-exact for finite
+    results, NaN where the oracle has NaN."""
+    rng = np.random.default_rng(8)
+    T, H = 8, 2056
+    from hyper_connection_residual_mhc_amd.workloads import to_bf16_bits
+    with np.errstate(over="ignore"):
+        res = (rng.standard_normal((T, 4, H)) * np.exp2(rng.integers(-130, 120, (T, 4, H)))).astype(np.float32)
+        g = (rng.standard_normal((T, H)) * np.exp2(rng.integers(-130, 120, (T, H)))).astype(np.float32)
+    res[0] = -0.0
+    g[1] = 0.0
+    host = {"residual": to_bf16_bits(res), "pre": np.exp2(rng.integers(-40, 40, (T, 4))).astype(np.float32),
+            "grad_out": to_bf16_bits(g)}
+    gr, gp = run_bwd(host, device)
+    want_gr, want_gp = O.h_aggregate_bwd(host["residual"], host["pre"], host["grad_out"])
+    nan = np.isnan(O.widen_bf16(want_gr))
+    assert np.array_equal(np.isnan(O.widen_bf16(gr)), nan)
+    assert_bytes_equal(gr[~nan], want_gr[~nan], "special grad_residual")
+    nanp = np.isnan(want_gp)
+    assert np.array_equal(np.isnan(gp), nanp)
+    assert_bytes_equal(gp[~nanp], want_gp[~nanp], "special grad_pre")
+
+
+def test_backward_misaligned_buffers(device):
+    T, H = 9, 4096
+    host = make_inputs(T, H, seed=9, grad=True)
+    want_gr, want_gp = O.h_aggregate_bwd(host["residual"], host["pre"], host["grad_out"])
+    pre = torch.from_numpy(host["pre"]).to(device)
+    for off in (1, 2, 4):
+        say(f"backward misaligned +{off}")
+        res = offset_copy_bf16(host["residual"], device, off)
+        g = offset_copy_bf16(host["grad_out"], device, 0)
+        grbuf = torch.empty(T * 4 * H + off, dtype=torch.bfloat16, device=device)
+        gr = grbuf[off:].view(T, 4, H)
+        gp = torch.empty((T, 4), dtype=torch.float32, device=device)
+        ops.mhc_h_aggregate_bwd(res, pre, g, gr, gp)
+        torch.cuda.synchronize()
+        assert_bytes_equal(bf16_tensor_to_bits(gr), want_gr, f"misaligned {off}")
+        assert_bytes_equal(gp.cpu().numpy(), want_gp, f"misaligned {off}")
+
+
+def test_backward_empty_batch_is_a_no_op(device):
+    say("backward T=0")
+    z = lambda *s, dt=torch.bfloat16: torch.empty(s, dtype=dt, device=device)  # noqa: E731
+    ops.mhc_h_aggregate_bwd(z(0, 4, 7), z(0, 4, dt=torch.float32), z(0, 7), z(0, 4, 7),
+                            z(0, 4, dt=torch.float32))
+    torch.cuda.synchronize()
+
+
+def test_autograd_function_runs_the_kernels(device):
+    """HAggregate.apply: forward and backward equal the direct calls."""
+    say("autograd")
+    host = make_inputs(16, 4096, seed=10, grad=True)
+    d = to_device(host, device)
+    res = d["residual"].clone().requires_grad_(True)
+    pre = d["pre"].clone().requires_grad_(True)
+    out = ops.h_aggregate_autograd(res, pre)
+    out.backward(d["grad_out"])
+    torch.cuda.synchronize()
+    assert_bytes_equal(bf16_tensor_to_bits(out), O.h_aggregate_fwd(host["residual"], host["pre"]),
+                       "autograd forward")
+    check_bwd(host, bf16_tensor_to_bits(res.grad), pre.grad.cpu().numpy(), "autograd")
+
+
+def test_backward_matches_torch_autograd_loosely(device):
+    """Loose cross-check with torch autograd of the fp32 formula on the GPU."""
+    say("backward vs torch autograd")
+    host = make_inputs(64, 4096, seed=11, grad=True)
+    d = to_device(host, device)
+    r32 = d["residual"].float().requires_grad_(True)
+    p32 = d["pre"].clone().requires_grad_(True)
+    ((p32[:, :, None] * r32).sum(dim=1)).backward(d["grad_out"].float())
+    gr, gp = ops.h_aggregate_backward(d["residual"], d["pre"], d["grad_out"])
+    torch.testing.assert_close(gr.float(), r32.grad.to(torch.bfloat16).float(), atol=1e-2, rtol=1e-2)
+    torch.testing.assert_close(gp, p32.grad, atol=1e-3, rtol=1e-4)

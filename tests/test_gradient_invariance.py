@@ -1,0 +1,104 @@
+"""gradient_invariance: the backward's bytes never depend on the batch, the
+partition or the launch shape.
+
+The reduction order of grad_pre depends only on H (see the public header),
+so repeats, batch splits, tokens-per-block, vector width and load batching
+must all give identical bytes. Mirrors the forward checks of page "Add
+batch-invariant h_aggregate kernel" (RL-Kernel pull request 366), section
+Correctness, for the gradients its review comments ask for.
+"""
+
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import assert_bytes_equal
+from gpu_util import GUARD, SENTINELS, guarded_empty_bf16, guards_untouched, run_bwd, say
+from hyper_connection_residual_mhc_amd import ops
+from hyper_connection_residual_mhc_amd.workloads import bf16_tensor_to_bits, make_inputs, to_device
+from oracle import h_aggregate as O
+
+pytestmark = pytest.mark.gpu
+
+
+def test_backward_100_repeats_byte_identical(device):
+    T, H = 129, 4096
+    say(f"backward 100 repeats T={T} H={H}")
+    host = make_inputs(T, H, seed=0, grad=True)
+    d = to_device(host, device)
+    grs = torch.empty((100, T, 4, H), dtype=torch.bfloat16, device=device)
+    gps = torch.empty((100, T, 4), dtype=torch.float32, device=device)
+    for k in range(100):
+        ops.mhc_h_aggregate_bwd(d["residual"], d["pre"], d["grad_out"], grs[k], gps[k])
+    torch.cuda.synchronize()
+    gb = grs.view(torch.int16)
+    pb = gps.view(torch.int32)
+    assert bool((gb == gb[0:1]).all()) and bool((pb == pb[0:1]).all())
+    want_gr, want_gp = O.h_aggregate_bwd(host["residual"], host["pre"], host["grad_out"])
+    assert_bytes_equal(bf16_tensor_to_bits(grs[0]), want_gr, "repeat grad_residual")
+    assert_bytes_equal(gps[0].cpu().numpy(), want_gp, "repeat grad_pre")
+
+
+@pytest.mark.parametrize("T,H,splits", [(2048, 7168, (1, 7, 129, 1911)),
+                                        (129, 4096, (1,) * 129),
+                                        (3, 1279, (1, 1, 1))])
+def test_backward_batch_split(device, T, H, splits):
+    say(f"backward batch split T={T} H={H}")
+    host = make_inputs(T, H, seed=1, grad=True)
+    d = to_device(host, device)
+    gr = torch.empty((T, 4, H), dtype=torch.bfloat16, device=device)
+    gp = torch.empty((T, 4), dtype=torch.float32, device=device)
+    ops.mhc_h_aggregate_bwd(d["residual"], d["pre"], d["grad_out"], gr, gp)
+    gr2, gp2 = torch.empty_like(gr), torch.empty_like(gp)
+    lo = 0
+    for n in splits:
+        sl = slice(lo, lo + n)
+        ops.mhc_h_aggregate_bwd(d["residual"][sl], d["pre"][sl], d["grad_out"][sl], gr2[sl], gp2[sl])
+        lo += n
+    assert lo == T
+    torch.cuda.synchronize()
+    assert_bytes_equal(bf16_tensor_to_bits(gr2), bf16_tensor_to_bits(gr), "split grad_residual")
+    assert_bytes_equal(gp2.cpu().numpy(), gp.cpu().numpy(), "split grad_pre")
+
+
+@pytest.mark.parametrize("T,H", [(37, 7168), (9, 1279), (5, 4100), (4, 20001)])
+def test_backward_every_launch_shape_gives_the_same_bytes(device, T, H):
+    host = make_inputs(T, H, seed=2, grad=True)
+    want_gr, want_gp = O.h_aggregate_bwd(host["residual"], host["pre"], host["grad_out"])
+    widths = [v for v in (1, 2, 4, 8) if H % v == 0]
+    for v, u, tpb in itertools.product(widths, (1, 2, 4), (1, 2, 3, 8)):
+        launch = {"vec_width": v, "units_per_thread": u, "tokens_per_block": tpb}
+        say(f"backward launch {launch} T={T} H={H}")
+        gr, gp = run_bwd(host, device, launch=launch)
+        assert_bytes_equal(gr, want_gr, f"grad_residual {launch}")
+        assert_bytes_equal(gp, want_gp, f"grad_pre {launch}")
+
+
+def test_backward_canaries(device):
+    """Both gradients fully overwritten (two sentinels give the same bytes),
+    nothing written outside them."""
+    T, H = 33, 1000
+    host = make_inputs(T, H, seed=3, grad=True)
+    d = to_device(host, device)
+    res = []
+    for s in SENTINELS:
+        for launch in (None, {"vec_width": 2, "tokens_per_block": 4}, {"vec_width": 1}):
+            say(f"backward canary 0x{s:x} {launch}")
+            gr, grbuf = guarded_empty_bf16((T, 4, H), device, s)
+            gpbuf = torch.full((T * 4 + 2 * GUARD,), float("nan"), dtype=torch.float32, device=device)
+            gp = gpbuf[GUARD:GUARD + T * 4].view(T, 4)
+            ops.mhc_h_aggregate_bwd(d["residual"], d["pre"], d["grad_out"], gr, gp, launch=launch)
+            torch.cuda.synchronize()
+            assert guards_untouched(grbuf, T * 4 * H, s)
+            g = gpbuf.cpu().numpy()
+            assert np.isnan(g[:GUARD]).all() and np.isnan(g[GUARD + T * 4:]).all()
+            res.append((bf16_tensor_to_bits(gr), gp.cpu().numpy()))
+    for gr, gp in res[1:]:
+        assert np.array_equal(gr, res[0][0]) and np.array_equal(gp.view(np.uint32), res[0][1].view(np.uint32))
+    want_gr, want_gp = O.h_aggregate_bwd(host["residual"], host["pre"], host["grad_out"])
+    assert_bytes_equal(res[0][0], want_gr, "canary grad_residual")
+    assert_bytes_equal(res[0][1], want_gp, "canary grad_pre")
