@@ -1,0 +1,416 @@
+"""Benchmark of the mHC pre / H-aggregate hot path on one MI355X.
+
+A step is one pass of the whole path on one batch: the forward
+(residual[T,4,H], pre[T,4] -> out[T,H]) followed by the backward
+(-> grad_residual[T,4,H], grad_pre[T,4]) at T=1024, H=7168, HC=4 - the
+bandwidth shape of the page "Add batch-invariant h_aggregate kernel"
+(RL-Kernel pull request 366), section Performance.
+
+Cold caches: the inputs and outputs rotate over `--sets` independent buffer
+sets (default 8, about 1.2 GB) and the forward and backward of one step use
+different sets, so every set's bytes leave the 256 MB Infinity Cache and
+the L2s before they are touched again. Inputs are resident in HBM before the
+timed region starts.
+
+Output: one JSON line. `value` is the step's algorithmic bytes (forward
+10H+16 and backward 18H+32 per token) divided by the measured time per step.
+`roofline` is for the backward kernel (the larger of the two), its duration
+taken from HIP events that the library attaches to every backward dispatch
+in the timed region (start and end timestamps of the dispatch itself).
+`cpu_baseline` times the CPU oracle on a token sample of the same workload.
+
+Helpers for the profiles: --summarize-stats and --summarize-pmc turn
+rocprofv3 CSV output into the short text summaries kept in profiles/.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import platform
+import re
+import statistics
+import sys
+import time
+from pathlib import Path
+
+REPO = Path(__file__).resolve().parent
+if str(REPO) not in sys.path:
+    sys.path.insert(0, str(REPO))
+
+METRIC = "h_aggregate fwd/bwd achieved HBM GB/s + µs/call at T=1024,H=7168 (1 GPU)"
+HC = 4
+PEAK_HBM_GBPS = 8000.0            # MI355X HBM3E peak, 8 TB/s
+TRAFFIC_FILE = REPO / "profiles" / "hagg_bwd_T1024_H7168_traffic.md"
+KERNEL_SRC = REPO / "hyper_connection_residual_mhc_amd" / "csrc" / "mhc_h_aggregate.hip"
+
+
+def fwd_bytes(T: int, H: int) -> int:
+    """Algorithmic bytes of one forward call: read residual (8H) and pre (16),
+    write out (2H), per token."""
+    return T * (10 * H + 16)
+
+
+def bwd_bytes(T: int, H: int) -> int:
+    """Algorithmic bytes of one backward call: read residual (8H), grad_out
+    (2H), pre (16); write grad_residual (8H), grad_pre (16), per token."""
+    return T * (18 * H + 32)
+
+
+def source_sha256() -> str:
+    return hashlib.sha256(KERNEL_SRC.read_bytes()).hexdigest()
+
+
+def recorded_traffic() -> int | None:
+    """HBM bytes per backward launch from the committed counter summary, or
+    None when there is none or the kernel source changed since it was taken."""
+    if not TRAFFIC_FILE.exists():
+        return None
+    text = TRAFFIC_FILE.read_text()
+    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_val = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
+    if not (m_sha and m_val) or m_sha.group(1) != source_sha256():
+        return None
+    return int(m_val.group(1))
+
+
+# ---------------------------------------------------------------------------
+# GPU part
+# ---------------------------------------------------------------------------
+
+class BufferSet:
+    """One independent set of device inputs and outputs for a step."""
+
+    def __init__(self, host: dict, dev):
+        import torch
+        from hyper_connection_residual_mhc_amd.workloads import to_device
+        d = to_device(host, dev)
+        self.residual, self.pre, self.grad_out = d["residual"], d["pre"], d["grad_out"]
+        T, _, H = self.residual.shape
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        self.grad_residual = torch.empty((T, HC, H), dtype=torch.bfloat16, device=dev)
+        self.grad_pre = torch.empty((T, HC), dtype=torch.float32, device=dev)
+
+
+def make_sets(T: int, H: int, n: int, dev) -> list[BufferSet]:
+    from hyper_connection_residual_mhc_amd.workloads import make_inputs
+    return [BufferSet(make_inputs(T, H, seed=s, grad=True), dev) for s in range(n)]
+
+
+def copy_probe(dev, nbytes: int = 1 << 28, reps: int = 3) -> None:
+    """A plain device copy of known size (read nbytes, write nbytes), run
+    outside the timed region so counter runs can scale FETCH/WRITE sizes."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+class HipEvents:
+    """Timing events from the HIP runtime (created with timing enabled). The
+    library attaches them to its kernel dispatches, so their elapsed time is
+    the kernels' own execution time."""
+
+    def __init__(self, n: int):
+        import ctypes
+        self._ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.handles = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.handles.append(h.value)
+
+    def elapsed_us(self, a: int, b: int) -> float:
+        ms = self._ct.c_float()
+        if self.hip.hipEventElapsedTime(self._ct.byref(ms), self.handles[a], self.handles[b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value * 1e3
+
+    def close(self) -> None:
+        for h in self.handles:
+            self.hip.hipEventDestroy(h)
+        self.handles = []
+
+
+def run_gpu(T: int, H: int, steps: int, warmup: int, nsets: int, probe: bool,
+            sample_every: int) -> dict:
+    import torch
+    from hyper_connection_residual_mhc_amd import _build, _lib, ops
+
+    if not _build.library_is_built():
+        _build.build_library()
+    lib = _lib.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sets = make_sets(T, H, nsets, dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = int(stream.cuda_stream)
+
+    # Plans (host-only queries) and the pre-marshalled argument tuples.
+    s0 = sets[0]
+    fwd_plan, fwd_grid = ops.mhc_h_aggregate_plan_fwd(s0.residual, s0.pre, s0.out, T, H)
+    bwd_plan, bwd_grid = ops.mhc_h_aggregate_plan_bwd(s0.residual, s0.pre, s0.grad_out,
+                                                      s0.grad_residual, s0.grad_pre, T, H)
+    fargs = [(s.residual.data_ptr(), s.pre.data_ptr(), s.out.data_ptr(), T, H, sh) for s in sets]
+    bargs = [(s.residual.data_ptr(), s.pre.data_ptr(), s.grad_out.data_ptr(),
+              s.grad_residual.data_ptr(), s.grad_pre.data_ptr(), T, H, sh) for s in sets]
+    fwd, bwd = lib.mhc_h_aggregate_fwd, lib.mhc_h_aggregate_bwd
+    fwd_t, bwd_t = lib.mhc_h_aggregate_fwd_timed, lib.mhc_h_aggregate_bwd_timed
+
+    if probe:
+        copy_probe(dev)
+
+    # Every `sample_every`-th step goes through the timed entry points, which
+    # attach HIP events to the two kernel dispatches themselves. Recording
+    # events costs the host more than a plain launch, so sampling keeps the
+    # host ahead of the GPU and the stream free of gaps.
+    sampled = [k for k in range(steps) if k % sample_every == 0]
+    ev = HipEvents(4 * len(sampled))
+    E = ev.handles
+
+    # Step k: forward on set 2k mod n, backward on set 2k+1 mod n.
+    def step(k: int) -> int:
+        return (fwd(*fargs[(2 * k) % nsets]) |
+                bwd(*bargs[(2 * k + 1) % nsets]))
+
+    def timed_step(k: int, j: int) -> int:
+        return (fwd_t(*fargs[(2 * k) % nsets], None, E[4 * j], E[4 * j + 1]) |
+                bwd_t(*bargs[(2 * k + 1) % nsets], None, E[4 * j + 2], E[4 * j + 3]))
+
+    for k in range(warmup):
+        st = step(k)
+        if st:
+            _lib.check(st)
+    torch.cuda.synchronize()
+
+    st = 0
+    j = 0
+    t0 = time.perf_counter()
+    for k in range(steps):
+        if k % sample_every == 0:
+            st |= timed_step(warmup + k, j)
+            j += 1
+        else:
+            st |= step(warmup + k)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if st:
+        _lib.check(st)
+
+    fwd_us = [ev.elapsed_us(4 * j, 4 * j + 1) for j in range(len(sampled))]
+    bwd_us = [ev.elapsed_us(4 * j + 2, 4 * j + 3) for j in range(len(sampled))]
+    ev.close()
+    return {
+        "wall_s": t1 - t0,
+        "timed_launches": len(sampled),
+        "fwd_us": fwd_us,
+        "bwd_us": bwd_us,
+        "fwd_plan": fwd_plan, "fwd_grid": fwd_grid,
+        "bwd_plan": bwd_plan, "bwd_grid": bwd_grid,
+        "device": torch.cuda.get_device_name(dev),
+        "torch": torch.__version__,
+        "hip": getattr(torch.version, "hip", None),
+    }
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a token sample
+# ---------------------------------------------------------------------------
+
+def run_cpu_baseline(T: int, H: int, min_seconds: float) -> dict:
+    """The oracle, as it stands, on the step's workload: the forward and
+    backward of one seed-0 input set of T tokens, repeated until at least
+    `min_seconds` of CPU time have passed (one thread: numpy ufuncs)."""
+    from hyper_connection_residual_mhc_amd.workloads import make_inputs
+    from oracle import h_aggregate as O
+    host = make_inputs(T, H, seed=0, grad=True)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        O.h_aggregate_fwd(host["residual"], host["pre"])
+        O.h_aggregate_bwd(host["residual"], host["pre"], host["grad_out"])
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or reps >= 1000:
+            break
+    gb = reps * (fwd_bytes(T, H) + bwd_bytes(T, H)) / 1e9
+    return {
+        "value": round(gb / dt, 6),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{reps} oracle steps (forward + backward) on one seed-0 input set of "
+                   f"T={T}, H={H} (numpy float32 ufuncs, one thread), {dt:.1f} s; "
+                   f"GB/s of the same algorithmic bytes"),
+        "host_cpu": cpu_model(),
+        "host_cores_visible": len(os.sched_getaffinity(0)),
+    }
+
+
+def cpu_model() -> str:
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries (for the text files in profiles/)
+# ---------------------------------------------------------------------------
+
+def _rows(path: str) -> list[dict]:
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_stats(path: str) -> None:
+    """Markdown table of a rocprofv3 --stats kernel_stats.csv."""
+    rows = _rows(path)
+    print("| kernel | calls | avg us | min us | max us | total % |")
+    print("|---|---|---|---|---|---|")
+    for r in rows:
+        name = r.get("Name", "")
+        short = re.sub(r"\(.*", "", name)[:90]
+        avg = float(r.get("AverageNs", 0)) / 1e3
+        mn = float(r.get("MinNs", 0)) / 1e3
+        mx = float(r.get("MaxNs", 0)) / 1e3
+        print(f"| {short} | {r.get('Calls')} | {avg:.3f} | {mn:.3f} | {mx:.3f} | "
+              f"{float(r.get('Percentage', 0)):.2f} |")
+
+
+def summarize_pmc(paths: list[str]) -> None:
+    """Per-kernel average of each counter (KiB for FETCH_SIZE / WRITE_SIZE)
+    from rocprofv3 --pmc counter_collection.csv files."""
+    acc: dict[tuple[str, str], list[float]] = {}
+    for p in paths:
+        for r in _rows(p):
+            name = re.sub(r"\(.*", "", r.get("Kernel_Name", ""))[:90]
+            key = (name, r.get("Counter_Name", ""))
+            acc.setdefault(key, []).append(float(r.get("Counter_Value", 0)))
+    print("| kernel | counter | dispatches | average per dispatch |")
+    print("|---|---|---|---|")
+    for (name, ctr), vals in sorted(acc.items()):
+        print(f"| {name} | {ctr} | {len(vals)} | {statistics.fmean(vals):.1f} |")
+
+
+# ---------------------------------------------------------------------------
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--sets", type=int, default=8, help="rotating buffer sets (cold caches)")
+    ap.add_argument("--tokens", type=int, default=1024)
+    ap.add_argument("--hidden", type=int, default=7168)
+    ap.add_argument("--time-every", type=int, default=8,
+                    help="attach timing events to every N-th step's dispatches")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run a 256 MiB device copy first (counter calibration)")
+    ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV")
+    ap.add_argument("--summarize-pmc", metavar="COUNTER_CSV", nargs="+")
+    args = ap.parse_args()
+
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats)
+        return 0
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this operation is token-parallel with no "
+              f"communication, and runs here on a single MI355X (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        return 2
+    if args.sets < 2:
+        print("--sets must be >= 2 (forward and backward use different sets)", file=sys.stderr)
+        return 2
+
+    T, H = args.tokens, args.hidden
+    if args.time_every < 1:
+        print("--time-every must be >= 1", file=sys.stderr)
+        return 2
+    g = run_gpu(T, H, args.steps, args.warmup, args.sets, args.copy_probe, args.time_every)
+    ms_per_step = g["wall_s"] * 1e3 / args.steps
+    step_bytes = fwd_bytes(T, H) + bwd_bytes(T, H)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    fwd_avg = statistics.fmean(g["fwd_us"])
+    bwd_avg = statistics.fmean(g["bwd_us"])
+    achieved = bwd_bytes(T, H) / (bwd_avg * 1e-6) / 1e9
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"h_aggregate forward+backward, T={T}, H={H}, HC=4, bf16 in/out, "
+                        f"fp32 pre and arithmetic",
+            "T": T, "H": H, "hc": HC,
+            "rotating_sets": args.sets,
+            "bytes_per_step": step_bytes,
+        },
+        "fwd": {
+            "us_per_call": round(fwd_avg, 3),
+            "us_p20_p50_p80": [round(x, 3) for x in statistics.quantiles(g["fwd_us"], n=10)[1:8:3]],
+            "gbps": round(fwd_bytes(T, H) / (fwd_avg * 1e-6) / 1e9, 1),
+            "bytes_per_call": fwd_bytes(T, H),
+            "plan": g["fwd_plan"], "grid_blocks": g["fwd_grid"],
+        },
+        "bwd": {
+            "us_per_call": round(bwd_avg, 3),
+            "us_p20_p50_p80": [round(x, 3) for x in statistics.quantiles(g["bwd_us"], n=10)[1:8:3]],
+            "gbps": round(achieved, 1),
+            "bytes_per_call": bwd_bytes(T, H),
+            "plan": g["bwd_plan"], "grid_blocks": g["bwd_grid"],
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": recorded_traffic(),
+            "kernel": "hagg_bwd_kernel (backward)",
+        },
+        "timing": {"per_kernel": "HIP events attached to the dispatches of every "
+                                 f"{args.time_every}th step ({g['timed_launches']} launches "
+                                 "of each kernel)",
+                   "per_step": "host wall clock over the timed steps, synchronized on both sides"},
+        "device": g["device"],
+        "torch": g["torch"],
+        "hip": g["hip"],
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = run_cpu_baseline(T, H, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -44,6 +44,11 @@ SIGNATURES = {
                                     c_int64, c_int64, c_void_p]),
     "mhc_h_aggregate_bwd_ex": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                        c_int64, c_int64, c_void_p, POINTER(mhc_launch)]),
+    "mhc_h_aggregate_fwd_timed": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64,
+                                          c_void_p, POINTER(mhc_launch), c_void_p, c_void_p]),
+    "mhc_h_aggregate_bwd_timed": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                          c_int64, c_int64, c_void_p, POINTER(mhc_launch),
+                                          c_void_p, c_void_p]),
     "mhc_h_aggregate_validate_fwd": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64]),
     "mhc_h_aggregate_validate_bwd": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                              c_int64, c_int64]),

@@ -25,6 +25,7 @@
 //    kept (the kernel descriptor's default mode), and every bf16 result goes
 //    through the hardware round-to-nearest-even pack conversion.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <stdarg.h>
@@ -67,22 +68,25 @@ __device__ __forceinline__ float bf16_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// A V-element bf16 vector as the widest plain integer type of that size.
+// A V-element bf16 vector as a native vector of 32-bit words (V = 8, 4), one
+// word (V = 2) or one half-word (V = 1).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 template <int V> struct Vec;
-template <> struct Vec<8> { typedef uint4 type; };
-template <> struct Vec<4> { typedef uint2 type; };
+template <> struct Vec<8> { typedef u32x4 type; };
+template <> struct Vec<4> { typedef u32x2 type; };
 template <> struct Vec<2> { typedef uint32_t type; };
 template <> struct Vec<1> { typedef uint16_t type; };
 
-// Element e of a vector, widened to fp32.
+// Element e (compile-time after unrolling) of a vector, widened to fp32.
 template <int V>
 __device__ __forceinline__ float elem(const typename Vec<V>::type& v, int e);
-template <> __device__ __forceinline__ float elem<8>(const uint4& v, int e) {
-  const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+template <> __device__ __forceinline__ float elem<8>(const u32x4& v, int e) {
+  const uint32_t w = v[e >> 1];
   return (e & 1) ? hi_f32(w) : lo_f32(w);
 }
-template <> __device__ __forceinline__ float elem<4>(const uint2& v, int e) {
-  const uint32_t w = e < 2 ? v.x : v.y;
+template <> __device__ __forceinline__ float elem<4>(const u32x2& v, int e) {
+  const uint32_t w = v[e >> 1];
   return (e & 1) ? hi_f32(w) : lo_f32(w);
 }
 template <> __device__ __forceinline__ float elem<2>(const uint32_t& v, int e) {
@@ -95,12 +99,12 @@ template <> __device__ __forceinline__ float elem<1>(const uint16_t& v, int) {
 // V fp32 values -> one bf16 vector.
 template <int V>
 __device__ __forceinline__ typename Vec<V>::type pack(const float (&y)[V]);
-template <> __device__ __forceinline__ uint4 pack<8>(const float (&y)[8]) {
-  return make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
-                    pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
+template <> __device__ __forceinline__ u32x4 pack<8>(const float (&y)[8]) {
+  return u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+               pack_bf16x2(y[6], y[7])};
 }
-template <> __device__ __forceinline__ uint2 pack<4>(const float (&y)[4]) {
-  return make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+template <> __device__ __forceinline__ u32x2 pack<4>(const float (&y)[4]) {
+  return u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
 }
 template <> __device__ __forceinline__ uint32_t pack<2>(const float (&y)[2]) {
   return pack_bf16x2(y[0], y[1]);
@@ -109,13 +113,60 @@ template <> __device__ __forceinline__ uint16_t pack<1>(const float (&y)[1]) {
   return to_bf16(y[0]);
 }
 
-template <int V>
-__device__ __forceinline__ typename Vec<V>::type load_vec(const uint16_t* p) {
-  return *reinterpret_cast<const typename Vec<V>::type*>(p);
+// Memory access: CDNA buffer instructions. A token's rows are described by a
+// buffer resource (base address and byte length, held in scalar registers,
+// wave-uniform), each lane supplies one 32-bit byte offset. Accesses past the
+// resource's length are dropped by the hardware (loads return 0), so no lane
+// can touch memory outside the row it was given. Every tensor byte is touched
+// exactly once, so every access carries the nontemporal (streaming) hint.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kRsrcFormat = 0x00020000;  // gfx9 resource word 3: raw 32-bit data
+constexpr int kNontemporal = 2;          // cache-policy bit 1: nt
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), kRsrcFormat);
 }
+
+// Load V bf16 elements at element `off` (per lane) plus `soff` bytes
+// (wave-uniform, carried in a scalar register) into the resource.
 template <int V>
-__device__ __forceinline__ void store_vec(uint16_t* p, const typename Vec<V>::type& v) {
-  *reinterpret_cast<typename Vec<V>::type*>(p) = v;
+__device__ __forceinline__ typename Vec<V>::type load_vec(Rsrc rs, uint32_t off, uint32_t soff);
+template <> __device__ __forceinline__ u32x4 load_vec<8>(Rsrc rs, uint32_t off, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(rs, off * 2, soff, kNontemporal);
+}
+template <> __device__ __forceinline__ u32x2 load_vec<4>(Rsrc rs, uint32_t off, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b64(rs, off * 2, soff, kNontemporal);
+}
+template <> __device__ __forceinline__ uint32_t load_vec<2>(Rsrc rs, uint32_t off, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(rs, off * 2, soff, kNontemporal);
+}
+template <> __device__ __forceinline__ uint16_t load_vec<1>(Rsrc rs, uint32_t off, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(rs, off * 2, soff, kNontemporal);
+}
+
+// Stores take no scalar offset: the whole byte offset travels in the VGPR.
+// A store of more than 8 bytes reads its data registers over several cycles,
+// and an instruction right after it must not overwrite them. The compiler
+// inserts that wait state for stores whose scalar offset is the constant 0,
+// but not for stores with a scalar-register offset, and gfx950 needs it in
+// both cases (a register-offset dwordx4 store followed at once by a write to
+// its second data register was measured to store the new value from the
+// last lanes of each 16). tests/test_build_guards.py checks the machine code
+// for this pattern.
+template <int V>
+__device__ __forceinline__ void store_vec(Rsrc rs, uint32_t off, const typename Vec<V>::type& v);
+template <> __device__ __forceinline__ void store_vec<8>(Rsrc rs, uint32_t off, const u32x4& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, rs, off * 2, 0, kNontemporal);
+}
+template <> __device__ __forceinline__ void store_vec<4>(Rsrc rs, uint32_t off, const u32x2& v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, rs, off * 2, 0, kNontemporal);
+}
+template <> __device__ __forceinline__ void store_vec<2>(Rsrc rs, uint32_t off, const uint32_t& v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, rs, off * 2, 0, kNontemporal);
+}
+template <> __device__ __forceinline__ void store_vec<1>(Rsrc rs, uint32_t off, const uint16_t& v) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, rs, off * 2, 0, kNontemporal);
 }
 
 // ---------------------------------------------------------------------------
@@ -141,11 +192,10 @@ __global__ __launch_bounds__(1024) void hagg_fwd_kernel(
 
   const float* p = pre + 4 * static_cast<int64_t>(t);
   const float w0 = p[0], w1 = p[1], w2 = p[2], w3 = p[3];
-  const uint16_t* r0 = residual + static_cast<int64_t>(t) * 4 * H;
-  const uint16_t* r1 = r0 + H;
-  const uint16_t* r2 = r1 + H;
-  const uint16_t* r3 = r2 + H;
-  uint16_t* o = out + static_cast<int64_t>(t) * H;
+  // The token's four residual rows (8H bytes) and its output row (2H bytes).
+  const Rsrc res = make_rsrc(residual + static_cast<int64_t>(t) * 4 * H, 8 * H);
+  const Rsrc o = make_rsrc(out + static_cast<int64_t>(t) * H, 2 * H);
+  const uint32_t row = 2 * static_cast<uint32_t>(H);  // bytes between residual streams
 
   const uint32_t first = c * blockDim.x * UPT + threadIdx.x;
 
@@ -154,11 +204,11 @@ __global__ __launch_bounds__(1024) void hagg_fwd_kernel(
   for (int k = 0; k < UPT; ++k) {
     const uint32_t u = first + k * blockDim.x;
     if (u < units_per_token) {
-      const int64_t h = static_cast<int64_t>(u) * V;
-      x0[k] = load_vec<V>(r0 + h);
-      x1[k] = load_vec<V>(r1 + h);
-      x2[k] = load_vec<V>(r2 + h);
-      x3[k] = load_vec<V>(r3 + h);
+      const uint32_t h = u * V;
+      x0[k] = load_vec<V>(res, h, 0);
+      x1[k] = load_vec<V>(res, h, row);
+      x2[k] = load_vec<V>(res, h, 2 * row);
+      x3[k] = load_vec<V>(res, h, 3 * row);
     }
   }
 #pragma unroll
@@ -177,7 +227,7 @@ __global__ __launch_bounds__(1024) void hagg_fwd_kernel(
         const float s23 = p2 + p3;
         y[e] = s01 + s23;
       }
-      store_vec<V>(o + static_cast<int64_t>(u) * V, pack<V>(y));
+      store_vec<V>(o, u * V, pack<V>(y));
     }
   }
 }
@@ -198,11 +248,13 @@ __global__ __launch_bounds__(1024) void hagg_fwd_kernel(
 constexpr int kGroup = 8;
 constexpr int kLanes = 256;
 
+// At most 128 VGPRs (4 waves per SIMD), so that 4 blocks fit on a CU and a
+// 1024-token call is resident at once.
 template <int V, int U>
-__global__ __launch_bounds__(256) void hagg_bwd_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void hagg_bwd_kernel(
     const uint16_t* __restrict__ residual, const float* __restrict__ pre,
     const uint16_t* __restrict__ grad_out, uint16_t* __restrict__ grad_residual,
-    float* __restrict__ grad_pre, int64_t T, int64_t H, int64_t ngroups,
+    float* __restrict__ grad_pre, int64_t T, int64_t H, uint32_t ngroups,
     int32_t tokens_per_block) {
   typedef typename Vec<V>::type VT;
   constexpr int NV = kGroup / V;  // accesses per full group
@@ -217,48 +269,53 @@ __global__ __launch_bounds__(256) void hagg_bwd_kernel(
 
     const float* p = pre + 4 * t;
     const float w[4] = {p[0], p[1], p[2], p[3]};
-    const uint16_t* g_row = grad_out + t * H;
-    const uint16_t* r_row = residual + t * 4 * H;
-    uint16_t* gr_row = grad_residual + t * 4 * H;
+    // The token's grad_out row (2H bytes) and residual / grad_residual rows
+    // (8H bytes each).
+    const Rsrc g_row = make_rsrc(grad_out + t * H, 2 * H);
+    const Rsrc r_row = make_rsrc(residual + t * 4 * H, 8 * H);
+    const Rsrc gr_row = make_rsrc(grad_residual + t * 4 * H, 8 * H);
+    const uint32_t hs = static_cast<uint32_t>(H);  // elements between streams
+    const uint32_t row = 2 * hs;                   // bytes between streams
 
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (int64_t k0 = lane; k0 < ngroups; k0 += static_cast<int64_t>(kLanes) * U) {
+    for (uint32_t k0 = lane; k0 < ngroups; k0 += kLanes * U) {
       VT g[U][NV];
       VT r[U][NV][4];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int64_t k = k0 + static_cast<int64_t>(u) * kLanes;
+        const uint32_t k = k0 + u * kLanes;
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-          const int64_t h = k * kGroup + v * V;
+          const uint32_t h = k * kGroup + v * V;
           if (k < ngroups && h < H) {
-            g[u][v] = load_vec<V>(g_row + h);
+            g[u][v] = load_vec<V>(g_row, h, 0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) r[u][v][i] = load_vec<V>(r_row + i * H + h);
+            for (int i = 0; i < 4; ++i) r[u][v][i] = load_vec<V>(r_row, h, i * row);
           }
         }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int64_t k = k0 + static_cast<int64_t>(u) * kLanes;
+        const uint32_t k = k0 + u * kLanes;
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-          const int64_t h = k * kGroup + v * V;
+          const uint32_t h = k * kGroup + v * V;
           if (k < ngroups && h < H) {
-            float gr[4][V];
+            // Stream by stream, so only one stream's values are live at a
+            // time; each accumulator still adds its elements in ascending h.
 #pragma unroll
-            for (int e = 0; e < V; ++e) {
-              const float ge = elem<V>(g[u][v], e);
+            for (int i = 0; i < 4; ++i) {
+              float gr[V];
 #pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                gr[i][e] = w[i] * ge;
+              for (int e = 0; e < V; ++e) {
+                const float ge = elem<V>(g[u][v], e);
+                gr[e] = w[i] * ge;
                 const float q = ge * elem<V>(r[u][v][i], e);  // exact in the normal range
                 acc[i] = acc[i] + q;
               }
+              store_vec<V>(gr_row, i * hs + h, pack<V>(gr));
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) store_vec<V>(gr_row + i * H + h, pack<V>(gr[i]));
           }
         }
       }
@@ -388,8 +445,6 @@ bool vec_allowed(int V, int64_t H, const void* const* bufs, int nbufs) {
   return true;
 }
 
-// MI355X: 256 compute units (8 XCDs x 32).
-constexpr int64_t kTargetCUs = 256;
 // One dispatch covers at most 2^31 work-items (the AQL packet's grid size is a
 // 32-bit work-item count); larger problems are split over whole tokens.
 constexpr int64_t kMaxLaunchThreads = int64_t(1) << 31;
@@ -418,22 +473,16 @@ mhc_status plan_fwd(const uint16_t* residual, const uint16_t* out, int64_t T, in
       return fail(MHC_ERROR_INVALID_VALUE, "units_per_thread must be 1, 2 or 4");
     upt = ov->units_per_thread;
   }
-  int block;
+  // One wave per block: on gfx950 the 64-thread shape measured fastest at
+  // every bandwidth shape swept (T = 1024 and 8192, H = 7168), since the
+  // most independent blocks give the workgroup dispatcher the most freedom
+  // to spread the stream over 8 XCDs x 32 CUs; small problems gain from it
+  // too (more CUs busy).
+  int block = 64;
   if (ov && ov->block_threads != 0) {
     if (ov->block_threads < 64 || ov->block_threads > 1024 || ov->block_threads % 64 != 0)
       return fail(MHC_ERROR_INVALID_VALUE, "block_threads must be a multiple of 64 in [64, 1024]");
     block = ov->block_threads;
-  } else if (T * upt_units < kTargetCUs * 256) {
-    // Fewer units than one 256-thread block per CU: small blocks spread the
-    // few units over as many CUs as possible (latency-bound regime).
-    block = 64;
-  } else {
-    // Bandwidth regime: the larger of 256 / 128 that leaves the fewest idle
-    // lanes in a token's last block.
-    const int64_t span256 = 256LL * upt, span128 = 128LL * upt;
-    const int64_t idle256 = ((upt_units + span256 - 1) / span256) * span256 - upt_units;
-    const int64_t idle128 = ((upt_units + span128 - 1) / span128) * span128 - upt_units;
-    block = idle128 < idle256 ? 128 : 256;
   }
   const int64_t span = static_cast<int64_t>(block) * upt;
   const int64_t bpt = (upt_units + span - 1) / span;
@@ -468,15 +517,19 @@ mhc_status plan_bwd(const uint16_t* residual, const uint16_t* grad_out,
   }
   if (ov && ov->block_threads != 0 && ov->block_threads != kLanes)
     return fail(MHC_ERROR_INVALID_VALUE, "backward block_threads must be 0 or 256");
-  // Groups each lane loads before its arithmetic: two 16-byte groups (160
-  // bytes of input) keep the kernel near 80 VGPRs, so all blocks of a
-  // 1024-token call are resident at once; narrower accesses already issue
-  // many loads per group.
-  int U = V == 8 ? 2 : 1;
+  // Groups each lane loads before its arithmetic. Four (up to 320 bytes of
+  // input per lane: all of a lane's groups at H = 7168) fit the 128-VGPR
+  // budget, so every byte a lane needs is in flight at once while all blocks
+  // of a 1024-token call stay resident; this measured fastest at T = 1024,
+  // 2048 and 8192. The scalar path batches two.
+  int U = V == 1 ? 2 : 4;
   if (ov && ov->units_per_thread != 0) {
     if (ov->units_per_thread != 1 && ov->units_per_thread != 2 && ov->units_per_thread != 4)
       return fail(MHC_ERROR_INVALID_VALUE, "units_per_thread must be 1, 2 or 4");
     U = ov->units_per_thread;
+    if (V == 1 && U == 4)
+      return fail(MHC_ERROR_INVALID_VALUE,
+                  "units_per_thread 4 needs vec_width >= 2 in the backward");
   }
   int tpb = 1;
   if (ov && ov->tokens_per_block != 0) {
@@ -532,42 +585,128 @@ mhc_status launch_error(const char* what) {
   return ok();
 }
 
+// Kernel launches go through hipExtLaunchKernelGGL so that a caller's timing
+// events can be attached to the dispatch itself: the start event takes the
+// dispatch's start timestamp and the stop event its end timestamp, with no
+// extra marker packets between kernels. Null events give a plain launch.
+struct Events {
+  hipEvent_t start, stop;
+};
+
 template <int V, int UPT>
 void launch_fwd_t(const FwdPlan& pl, const uint16_t* residual, const float* pre, uint16_t* out,
-                  int64_t tokens, int64_t H, hipStream_t stream) {
+                  int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
   const uint32_t blocks = static_cast<uint32_t>(tokens * pl.blocks_per_token);
-  hagg_fwd_kernel<V, UPT><<<dim3(blocks), dim3(pl.block), 0, stream>>>(
-      residual, pre, out, H, pl.units_per_token, pl.blocks_per_token);
+  hipExtLaunchKernelGGL(hagg_fwd_kernel<V, UPT>, dim3(blocks), dim3(pl.block), 0, stream,
+                        ev.start, ev.stop, 0, residual, pre, out, H, pl.units_per_token,
+                        pl.blocks_per_token);
 }
 
 template <int V>
 void launch_fwd_v(const FwdPlan& pl, const uint16_t* residual, const float* pre, uint16_t* out,
-                  int64_t tokens, int64_t H, hipStream_t stream) {
+                  int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
   switch (pl.upt) {
-    case 1: launch_fwd_t<V, 1>(pl, residual, pre, out, tokens, H, stream); break;
-    case 2: launch_fwd_t<V, 2>(pl, residual, pre, out, tokens, H, stream); break;
-    default: launch_fwd_t<V, 4>(pl, residual, pre, out, tokens, H, stream); break;
+    case 1: launch_fwd_t<V, 1>(pl, residual, pre, out, tokens, H, stream, ev); break;
+    case 2: launch_fwd_t<V, 2>(pl, residual, pre, out, tokens, H, stream, ev); break;
+    default: launch_fwd_t<V, 4>(pl, residual, pre, out, tokens, H, stream, ev); break;
   }
 }
 
 template <int V, int U>
 void launch_bwd_t(const BwdPlan& pl, const uint16_t* residual, const float* pre,
                   const uint16_t* grad_out, uint16_t* grad_residual, float* grad_pre,
-                  int64_t tokens, int64_t H, hipStream_t stream) {
+                  int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
   const uint32_t blocks = static_cast<uint32_t>((tokens + pl.tpb - 1) / pl.tpb);
-  hagg_bwd_kernel<V, U><<<dim3(blocks), dim3(kLanes), 0, stream>>>(
-      residual, pre, grad_out, grad_residual, grad_pre, tokens, H, pl.ngroups, pl.tpb);
+  hipExtLaunchKernelGGL(hagg_bwd_kernel<V, U>, dim3(blocks), dim3(kLanes), 0, stream, ev.start,
+                        ev.stop, 0, residual, pre, grad_out, grad_residual, grad_pre, tokens, H,
+                        static_cast<uint32_t>(pl.ngroups), static_cast<int32_t>(pl.tpb));
 }
 
 template <int V>
 void launch_bwd_v(const BwdPlan& pl, const uint16_t* residual, const float* pre,
                   const uint16_t* grad_out, uint16_t* grad_residual, float* grad_pre,
-                  int64_t tokens, int64_t H, hipStream_t stream) {
+                  int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
+  // The scalar path batches at most 2 groups: 4 groups of 40 scalar loads
+  // would not fit the 128-VGPR budget (the plan rejects that shape).
+  constexpr int kMaxU = V == 1 ? 2 : 4;
   switch (pl.U) {
-    case 1: launch_bwd_t<V, 1>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream); break;
-    case 2: launch_bwd_t<V, 2>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream); break;
-    default: launch_bwd_t<V, 4>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream); break;
+    case 1: launch_bwd_t<V, 1>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
+    case 2: launch_bwd_t<V, 2>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
+    default: launch_bwd_t<V, kMaxU>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
   }
+}
+
+// Events of the i-th of n launches of one call: start on the first, stop on
+// the last.
+Events chunk_events(const Events& ev, int64_t first_token, int64_t next_token, int64_t T) {
+  return Events{first_token == 0 ? ev.start : nullptr, next_token >= T ? ev.stop : nullptr};
+}
+
+// A call that launches nothing (T == 0) still records the caller's events,
+// so their elapsed time is defined (zero work).
+mhc_status record_empty(const Events& ev, hipStream_t s) {
+  if (ev.start && hipEventRecord(ev.start, s) != hipSuccess)
+    return fail(MHC_ERROR_HIP, "hipEventRecord(start) failed");
+  if (ev.stop && hipEventRecord(ev.stop, s) != hipSuccess)
+    return fail(MHC_ERROR_HIP, "hipEventRecord(stop) failed");
+  return ok();
+}
+
+mhc_status run_fwd(const uint16_t* residual, const float* pre, uint16_t* out, int64_t T,
+                   int64_t H, void* stream, const mhc_launch* launch, Events ev) {
+  mhc_status st = validate_fwd(residual, pre, out, T, H);
+  if (st != MHC_SUCCESS) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) return record_empty(ev, s);
+  FwdPlan pl;
+  if ((st = plan_fwd(residual, out, T, H, launch, &pl)) != MHC_SUCCESS) return st;
+  (void)hipGetLastError();  // start from a clean per-thread error state
+  for (int64_t t0 = 0; t0 < T; t0 += pl.tokens_per_launch) {
+    const int64_t n = (T - t0 < pl.tokens_per_launch) ? T - t0 : pl.tokens_per_launch;
+    const Events e = chunk_events(ev, t0, t0 + n, T);
+    const uint16_t* r = residual + t0 * 4 * H;
+    const float* p = pre + 4 * t0;
+    uint16_t* o = out + t0 * H;
+    switch (pl.V) {
+      case 8: launch_fwd_v<8>(pl, r, p, o, n, H, s, e); break;
+      case 4: launch_fwd_v<4>(pl, r, p, o, n, H, s, e); break;
+      case 2: launch_fwd_v<2>(pl, r, p, o, n, H, s, e); break;
+      default: launch_fwd_v<1>(pl, r, p, o, n, H, s, e); break;
+    }
+    if ((st = launch_error("h_aggregate forward")) != MHC_SUCCESS) return st;
+  }
+  return ok();
+}
+
+mhc_status run_bwd(const uint16_t* residual, const float* pre, const uint16_t* grad_out,
+                   uint16_t* grad_residual, float* grad_pre, int64_t T, int64_t H, void* stream,
+                   const mhc_launch* launch, Events ev) {
+  mhc_status st = validate_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, H);
+  if (st != MHC_SUCCESS) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) return record_empty(ev, s);
+  BwdPlan pl;
+  if ((st = plan_bwd(residual, grad_out, grad_residual, T, H, launch, &pl)) != MHC_SUCCESS)
+    return st;
+  const int64_t tokens_per_launch = pl.blocks_per_launch * pl.tpb;
+  (void)hipGetLastError();
+  for (int64_t t0 = 0; t0 < T; t0 += tokens_per_launch) {
+    const int64_t n = (T - t0 < tokens_per_launch) ? T - t0 : tokens_per_launch;
+    const Events e = chunk_events(ev, t0, t0 + n, T);
+    const uint16_t* r = residual + t0 * 4 * H;
+    const float* p = pre + 4 * t0;
+    const uint16_t* g = grad_out + t0 * H;
+    uint16_t* gr = grad_residual + t0 * 4 * H;
+    float* gp = grad_pre + 4 * t0;
+    switch (pl.V) {
+      case 8: launch_bwd_v<8>(pl, r, p, g, gr, gp, n, H, s, e); break;
+      case 4: launch_bwd_v<4>(pl, r, p, g, gr, gp, n, H, s, e); break;
+      case 2: launch_bwd_v<2>(pl, r, p, g, gr, gp, n, H, s, e); break;
+      default: launch_bwd_v<1>(pl, r, p, g, gr, gp, n, H, s, e); break;
+    }
+    if ((st = launch_error("h_aggregate backward")) != MHC_SUCCESS) return st;
+  }
+  return ok();
 }
 
 }  // namespace
@@ -635,68 +774,44 @@ mhc_status mhc_h_aggregate_plan_bwd(const uint16_t* residual, const float* pre,
 mhc_status mhc_h_aggregate_fwd_ex(const uint16_t* residual, const float* pre, uint16_t* out,
                                   int64_t T, int64_t H, void* stream,
                                   const mhc_launch* launch) {
-  mhc_status st = validate_fwd(residual, pre, out, T, H);
-  if (st != MHC_SUCCESS || T == 0) return st;
-  FwdPlan pl;
-  if ((st = plan_fwd(residual, out, T, H, launch, &pl)) != MHC_SUCCESS) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  (void)hipGetLastError();  // start from a clean per-thread error state
-  for (int64_t t0 = 0; t0 < T; t0 += pl.tokens_per_launch) {
-    const int64_t n = (T - t0 < pl.tokens_per_launch) ? T - t0 : pl.tokens_per_launch;
-    const uint16_t* r = residual + t0 * 4 * H;
-    const float* p = pre + 4 * t0;
-    uint16_t* o = out + t0 * H;
-    switch (pl.V) {
-      case 8: launch_fwd_v<8>(pl, r, p, o, n, H, s); break;
-      case 4: launch_fwd_v<4>(pl, r, p, o, n, H, s); break;
-      case 2: launch_fwd_v<2>(pl, r, p, o, n, H, s); break;
-      default: launch_fwd_v<1>(pl, r, p, o, n, H, s); break;
-    }
-    if ((st = launch_error("h_aggregate forward")) != MHC_SUCCESS) return st;
-  }
-  return ok();
+  return run_fwd(residual, pre, out, T, H, stream, launch, Events{nullptr, nullptr});
 }
 
 mhc_status mhc_h_aggregate_fwd(const uint16_t* residual, const float* pre, uint16_t* out,
                                int64_t T, int64_t H, void* stream) {
-  return mhc_h_aggregate_fwd_ex(residual, pre, out, T, H, stream, nullptr);
+  return run_fwd(residual, pre, out, T, H, stream, nullptr, Events{nullptr, nullptr});
+}
+
+mhc_status mhc_h_aggregate_fwd_timed(const uint16_t* residual, const float* pre, uint16_t* out,
+                                     int64_t T, int64_t H, void* stream,
+                                     const mhc_launch* launch, void* start_event,
+                                     void* stop_event) {
+  return run_fwd(residual, pre, out, T, H, stream, launch,
+                 Events{static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)});
 }
 
 mhc_status mhc_h_aggregate_bwd_ex(const uint16_t* residual, const float* pre,
                                   const uint16_t* grad_out, uint16_t* grad_residual,
                                   float* grad_pre, int64_t T, int64_t H, void* stream,
                                   const mhc_launch* launch) {
-  mhc_status st = validate_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, H);
-  if (st != MHC_SUCCESS || T == 0) return st;
-  BwdPlan pl;
-  if ((st = plan_bwd(residual, grad_out, grad_residual, T, H, launch, &pl)) != MHC_SUCCESS)
-    return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t tokens_per_launch = pl.blocks_per_launch * pl.tpb;
-  (void)hipGetLastError();
-  for (int64_t t0 = 0; t0 < T; t0 += tokens_per_launch) {
-    const int64_t n = (T - t0 < tokens_per_launch) ? T - t0 : tokens_per_launch;
-    const uint16_t* r = residual + t0 * 4 * H;
-    const float* p = pre + 4 * t0;
-    const uint16_t* g = grad_out + t0 * H;
-    uint16_t* gr = grad_residual + t0 * 4 * H;
-    float* gp = grad_pre + 4 * t0;
-    switch (pl.V) {
-      case 8: launch_bwd_v<8>(pl, r, p, g, gr, gp, n, H, s); break;
-      case 4: launch_bwd_v<4>(pl, r, p, g, gr, gp, n, H, s); break;
-      case 2: launch_bwd_v<2>(pl, r, p, g, gr, gp, n, H, s); break;
-      default: launch_bwd_v<1>(pl, r, p, g, gr, gp, n, H, s); break;
-    }
-    if ((st = launch_error("h_aggregate backward")) != MHC_SUCCESS) return st;
-  }
-  return ok();
+  return run_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, H, stream, launch,
+                 Events{nullptr, nullptr});
 }
 
 mhc_status mhc_h_aggregate_bwd(const uint16_t* residual, const float* pre,
                                const uint16_t* grad_out, uint16_t* grad_residual,
                                float* grad_pre, int64_t T, int64_t H, void* stream) {
-  return mhc_h_aggregate_bwd_ex(residual, pre, grad_out, grad_residual, grad_pre, T, H, stream,
-                                nullptr);
+  return run_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, H, stream, nullptr,
+                 Events{nullptr, nullptr});
+}
+
+mhc_status mhc_h_aggregate_bwd_timed(const uint16_t* residual, const float* pre,
+                                     const uint16_t* grad_out, uint16_t* grad_residual,
+                                     float* grad_pre, int64_t T, int64_t H, void* stream,
+                                     const mhc_launch* launch, void* start_event,
+                                     void* stop_event) {
+  return run_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, H, stream, launch,
+                 Events{static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)});
 }
 
 mhc_status mhc_bf16_rne_probe(uint32_t first_bits, int64_t n, uint16_t* out, void* stream) {

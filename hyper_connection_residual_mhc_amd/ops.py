@@ -104,6 +104,48 @@ def mhc_h_aggregate_bwd(residual: torch.Tensor, pre: torch.Tensor, grad_out: tor
     return grad_residual, grad_pre
 
 
+def mhc_h_aggregate_fwd_timed(residual: torch.Tensor, pre: torch.Tensor, out: torch.Tensor,
+                              start_event: int | None, stop_event: int | None,
+                              stream: torch.cuda.Stream | None = None, launch=None
+                              ) -> torch.Tensor:
+    """Forward whose first / last kernel dispatch records the given raw
+    hipEvent_t handles (ints; None for no event) at its own start / end."""
+    T, H = _fwd_shapes(residual)
+    dev = residual.device
+    _require(residual, "residual", torch.bfloat16, (T, HC, H))
+    _require(pre, "pre", torch.float32, (T, HC), dev)
+    _require(out, "out", torch.bfloat16, (T, H), dev)
+    with torch.cuda.device(dev):
+        st = _lib.lib().mhc_h_aggregate_fwd_timed(
+            residual.data_ptr(), pre.data_ptr(), out.data_ptr(), T, H,
+            _stream_handle(dev, stream), _launch_arg(launch), start_event, stop_event)
+    check(st)
+    return out
+
+
+def mhc_h_aggregate_bwd_timed(residual: torch.Tensor, pre: torch.Tensor, grad_out: torch.Tensor,
+                              grad_residual: torch.Tensor, grad_pre: torch.Tensor,
+                              start_event: int | None, stop_event: int | None,
+                              stream: torch.cuda.Stream | None = None, launch=None
+                              ) -> tuple[torch.Tensor, torch.Tensor]:
+    """Backward whose first / last kernel dispatch records the given raw
+    hipEvent_t handles at its own start / end."""
+    T, H = _fwd_shapes(residual)
+    dev = residual.device
+    _require(residual, "residual", torch.bfloat16, (T, HC, H))
+    _require(pre, "pre", torch.float32, (T, HC), dev)
+    _require(grad_out, "grad_out", torch.bfloat16, (T, H), dev)
+    _require(grad_residual, "grad_residual", torch.bfloat16, (T, HC, H), dev)
+    _require(grad_pre, "grad_pre", torch.float32, (T, HC), dev)
+    with torch.cuda.device(dev):
+        st = _lib.lib().mhc_h_aggregate_bwd_timed(
+            residual.data_ptr(), pre.data_ptr(), grad_out.data_ptr(),
+            grad_residual.data_ptr(), grad_pre.data_ptr(), T, H,
+            _stream_handle(dev, stream), _launch_arg(launch), start_event, stop_event)
+    check(st)
+    return grad_residual, grad_pre
+
+
 def mhc_bf16_rne_probe(first_bits: int, out: torch.Tensor,
                        stream: torch.cuda.Stream | None = None) -> torch.Tensor:
     """out[k] = device bf16 rounding of the fp32 pattern first_bits + k (out: int16/uint16)."""

@@ -95,7 +95,8 @@ typedef enum mhc_status {
  *                     divide H and match the alignment of every bf16 buffer.
  *   units_per_thread  forward: vector units each thread handles; backward:
  *                     8-element groups each lane loads before its
- *                     arithmetic. 1, 2 or 4.
+ *                     arithmetic. 1, 2 or 4 (backward with vec_width 1:
+ *                     1 or 2).
  *   tokens_per_block  backward only: tokens one block handles in sequence,
  *                     1..4096.
  */
@@ -154,6 +155,27 @@ mhc_status mhc_h_aggregate_bwd_ex(const uint16_t* residual, const float* pre,
                                   uint16_t* grad_residual, float* grad_pre,
                                   int64_t T, int64_t H, void* stream,
                                   const mhc_launch* launch);
+
+/*
+ * Timed variants: identical to the *_ex calls, plus two caller-created HIP
+ * events (hipEvent_t cast to void*, created with timing enabled; either may
+ * be NULL). start_event takes the start timestamp of the call's first kernel
+ * dispatch and stop_event the end timestamp of its last, taken by the
+ * dispatch itself (hipExtLaunchKernel), so hipEventElapsedTime between them
+ * is the kernels' own execution time with no marker packets in the stream.
+ * With T == 0 both events are recorded on the stream with nothing between
+ * them. The events stay owned by the caller.
+ */
+mhc_status mhc_h_aggregate_fwd_timed(const uint16_t* residual, const float* pre,
+                                     uint16_t* out, int64_t T, int64_t H,
+                                     void* stream, const mhc_launch* launch,
+                                     void* start_event, void* stop_event);
+mhc_status mhc_h_aggregate_bwd_timed(const uint16_t* residual, const float* pre,
+                                     const uint16_t* grad_out,
+                                     uint16_t* grad_residual, float* grad_pre,
+                                     int64_t T, int64_t H, void* stream,
+                                     const mhc_launch* launch,
+                                     void* start_event, void* stop_event);
 
 /*
  * Host-only checks and plan queries. They touch no device and no memory

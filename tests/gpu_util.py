@@ -62,3 +62,33 @@ def offset_copy_bf16(bits: np.ndarray, dev, offset_elems: int) -> torch.Tensor:
     view = buf[offset_elems:].view(bits.shape)
     view.copy_(bits_to_bf16_tensor(bits, dev))
     return view
+
+
+class HipEvents:
+    """Raw timing events from the HIP runtime, for the *_timed entry points."""
+
+    def __init__(self, n: int):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.h = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+            self.h.append(e.value)
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = self.ct.c_float()
+        assert self.hip.hipEventSynchronize(self.h[b]) == 0
+        assert self.hip.hipEventElapsedTime(self.ct.byref(ms), self.h[a], self.h[b]) == 0
+        return ms.value
+
+    def close(self):
+        for e in self.h:
+            self.hip.hipEventDestroy(e)
+        self.h = []

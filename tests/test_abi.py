@@ -141,15 +141,16 @@ def test_error_message_names_the_problem(lib):
         ops.mhc_h_aggregate_plan_fwd(r, 0, o, T, H)
 
 
-def test_forward_plan_changes_with_T_but_not_the_math(lib):
-    """The batch-split check needs different launch shapes for a 129-token
-    batch and a 1-token call (the page's own check used 512 vs 1024 threads)."""
+def test_forward_plan_one_wave_blocks(lib):
+    """The policy uses one 64-lane wave per block at every size (the fastest
+    shape measured); the grid follows T, so a 129-token batch and a 1-token
+    call are different partitions of the same work."""
     r, p, o = fwd_ptrs(129, 4096)
     full, g_full = ops.mhc_h_aggregate_plan_fwd(r, p, o, 129, 4096)
     one, g_one = ops.mhc_h_aggregate_plan_fwd(r, p, o, 1, 4096)
-    assert full["block_threads"] != one["block_threads"]
+    assert full["block_threads"] == one["block_threads"] == 64
     assert full["vec_width"] == one["vec_width"] == 8
-    assert g_full == 129 * (512 // full["block_threads"])
+    assert (g_full, g_one) == (129 * 8, 8)
 
 
 def test_forward_plan_vector_width_follows_alignment_and_H(lib):
@@ -196,6 +197,7 @@ def test_backward_plan_and_overrides(lib):
     r, p, g, gr, gp = bwd_ptrs(T, H)
     plan, grid = ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T, H)
     assert plan["block_threads"] == 256 and plan["vec_width"] == 8
+    assert plan["units_per_thread"] == 4
     assert grid == -(-T // plan["tokens_per_block"])
     plan, grid = ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T, H,
                                               launch={"tokens_per_block": 3, "vec_width": 4,
@@ -205,6 +207,9 @@ def test_backward_plan_and_overrides(lib):
                 {"units_per_thread": 3}):
         with pytest.raises(MhcError, match="INVALID_VALUE"):
             ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T, H, launch=bad)
+    with pytest.raises(MhcError, match="needs vec_width >= 2"):
+        ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T, H,
+                                     launch={"vec_width": 1, "units_per_thread": 4})
     # grad_out misaligned by one element forces the scalar path
     plan, _ = ops.mhc_h_aggregate_plan_bwd(r, p, g + 2, gr, gp, T, H)
     assert plan["vec_width"] == 1
@@ -240,6 +245,10 @@ def test_compute_call_with_invalid_args_returns_before_any_hip_call(lib):
     bad = _lib.mhc_launch(block_threads=64)
     assert lib.mhc_h_aggregate_bwd_ex(rr, pp, g, gr, gp, T, H, None,
                                       ctypes.byref(bad)) == MHC_ERROR_INVALID_VALUE
+    assert lib.mhc_h_aggregate_fwd_timed(r, p, r, T, H, None, None, None,
+                                         None) == MHC_ERROR_ALIASING
+    assert lib.mhc_h_aggregate_bwd_timed(rr, pp, g, gr, gp, -1, H, None, None, None,
+                                         None) == MHC_ERROR_INVALID_VALUE
 
 
 def test_missing_library_raises_import_error(monkeypatch, tmp_path):

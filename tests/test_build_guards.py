@@ -8,6 +8,9 @@ own gfx950 machine code (compiled here; no GPU needed).
 * bf16 results produced by the round-to-nearest-even pack conversion;
 * a fast-math build is refused at compile time;
 * no register spills to scratch in the kernels;
+* no store of more than 8 bytes is followed at once by an instruction that
+  overwrites its data registers (gfx950 reads such data over several cycles;
+  an immediate overwrite was measured to corrupt the last lanes' data);
 * the product path never imports the oracle.
 """
 
@@ -63,6 +66,76 @@ def test_separate_fp32_mul_and_add_present(asm):
 def test_bf16_results_use_rne_pack_conversion(asm):
     for name, body in kernel_blocks(asm).items():
         assert "v_cvt_pk_bf16_f32" in body, name
+
+
+STORE_WIDE = re.compile(
+    r"^\s*(buffer_store_dwordx[34]|global_store_dwordx[34]|flat_store_dwordx[34]|"
+    r"scratch_store_dwordx[34])\s+(.*)$")
+
+
+def _regs(text: str) -> set[int]:
+    """VGPR numbers named by one operand (v7 or v[4:7])."""
+    m = re.fullmatch(r"v(\d+)", text)
+    if m:
+        return {int(m.group(1))}
+    m = re.fullmatch(r"v\[(\d+):(\d+)\]", text)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    return set()
+
+
+def store_data_regs(line: str) -> set[int]:
+    """Data VGPRs of a wide store (buffer: first operand; global/flat:
+    second operand)."""
+    m = STORE_WIDE.match(line)
+    ops = [o.strip() for o in m.group(2).split(",")]
+    return _regs(ops[0] if m.group(1).startswith("buffer") else ops[1])
+
+
+def written_vgprs(line: str) -> set[int]:
+    """VGPRs written by a VALU instruction (its first operand)."""
+    t = line.strip()
+    if not t.startswith("v_"):
+        return set()
+    parts = t.split(None, 1)
+    if len(parts) < 2:
+        return set()
+    return _regs(parts[1].split(",")[0].strip())
+
+
+def instructions(body: str) -> list[str]:
+    out = []
+    for ln in body.splitlines():
+        t = ln.split(";")[0].rstrip()
+        if not t.strip() or t.strip().startswith(".") or t.rstrip().endswith(":"):
+            continue
+        out.append(t)
+    return out
+
+
+def test_no_immediate_overwrite_of_wide_store_data(asm):
+    checked = 0
+    for name, body in kernel_blocks(asm).items():
+        ins = instructions(body)
+        for i, line in enumerate(ins[:-1]):
+            if not STORE_WIDE.match(line):
+                continue
+            checked += 1
+            clash = store_data_regs(line) & written_vgprs(ins[i + 1])
+            assert not clash, f"{name}: '{line.strip()}' then '{ins[i + 1].strip()}'"
+    assert checked > 0
+
+
+def test_hazard_scan_detects_the_pattern():
+    """The scan itself flags the measured corrupting sequence."""
+    body = ("\tbuffer_store_dwordx4 v[60:63], v56, s[36:39], s22 offen nt\n"
+            "\tv_lshlrev_b32_e32 v61, 16, v30\n")
+    ins = instructions(body)
+    assert store_data_regs(ins[0]) & written_vgprs(ins[1]) == {61}
+    ok = ("\tbuffer_store_dwordx4 v[60:63], v56, s[36:39], 0 offen nt\n"
+          "\ts_nop 0\n\tv_lshlrev_b32_e32 v61, 16, v30\n")
+    ins = instructions(ok)
+    assert not store_data_regs(ins[0]) & written_vgprs(ins[1])
 
 
 def test_fp32_denormals_kept_in_every_kernel(asm):

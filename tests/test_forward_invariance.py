@@ -42,9 +42,10 @@ def test_forward_100_repeats_byte_identical(device):
 
 @pytest.mark.parametrize("T,H", [(129, 4096), (3, 1279)])
 def test_forward_full_batch_equals_one_token_calls(device, T, H):
-    """One call over T tokens vs T calls of one token each, addressed by
-    pointer offsets into the same buffers. The launch policy picks different
-    block sizes for the two (asserted), the bytes must not change."""
+    """One call over T tokens (default launch: 64-thread blocks) vs T calls of
+    one token each made with 1024-thread blocks, as in the page's check
+    (different block size and partition), addressed by pointer offsets into
+    the same buffers. The bytes must not change."""
     say(f"forward batch split T={T} H={H}")
     host = make_inputs(T, H, seed=1)
     d = to_device(host, device)
@@ -52,12 +53,11 @@ def test_forward_full_batch_equals_one_token_calls(device, T, H):
     ops.mhc_h_aggregate_fwd(d["residual"], d["pre"], full)
     split = torch.empty((T, H), dtype=torch.bfloat16, device=device)
     for t in range(T):
-        ops.mhc_h_aggregate_fwd(d["residual"][t:t + 1], d["pre"][t:t + 1], split[t:t + 1])
+        ops.mhc_h_aggregate_fwd(d["residual"][t:t + 1], d["pre"][t:t + 1], split[t:t + 1],
+                                launch={"block_threads": 1024})
     torch.cuda.synchronize()
     plan_full, _ = ops.mhc_h_aggregate_plan_fwd(d["residual"], d["pre"], full, T, H)
-    plan_one, _ = ops.mhc_h_aggregate_plan_fwd(d["residual"], d["pre"], full, 1, H)
-    if T == 129:
-        assert plan_full["block_threads"] != plan_one["block_threads"]
+    assert plan_full["block_threads"] != 1024
     assert_bytes_equal(bf16_tensor_to_bits(split), bf16_tensor_to_bits(full), "batch split")
 
 

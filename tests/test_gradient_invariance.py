@@ -71,6 +71,8 @@ def test_backward_every_launch_shape_gives_the_same_bytes(device, T, H):
     want_gr, want_gp = O.h_aggregate_bwd(host["residual"], host["pre"], host["grad_out"])
     widths = [v for v in (1, 2, 4, 8) if H % v == 0]
     for v, u, tpb in itertools.product(widths, (1, 2, 4), (1, 2, 3, 8)):
+        if v == 1 and u == 4:
+            continue   # rejected by the plan (register budget)
         launch = {"vec_width": v, "units_per_thread": u, "tokens_per_block": tpb}
         say(f"backward launch {launch} T={T} H={H}")
         gr, gp = run_bwd(host, device, launch=launch)
