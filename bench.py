@@ -225,6 +225,79 @@ def run_gpu(T: int, H: int, steps: int, warmup: int, nsets: int, probe: bool,
 
 
 # ---------------------------------------------------------------------------
+# Shape sweep: per-call time of each kernel at the configured shapes
+# ---------------------------------------------------------------------------
+
+SWEEP_SHAPES = [  # (T, H): latency sweep, bandwidth shapes, backward shape
+    (1, 4096), (8, 4096), (128, 4096), (1, 7168), (8, 7168), (128, 7168),
+    (1024, 7168), (2048, 7168), (8192, 7168),
+]
+
+
+def run_sweep(path: str, launches: int = 200) -> None:
+    """Per-call forward and backward times at SWEEP_SHAPES, one JSON line per
+    (shape, direction) into `path`. Every launch carries dispatch events, so
+    launches run one at a time (each from cold caches: 8 rotating sets, 3 at
+    T=8192) - the per-call latency a caller sees, as in the page's table."""
+    import statistics as st
+    import torch
+    from hyper_connection_residual_mhc_amd import _lib, ops
+
+    lib = _lib.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sh = int(torch.cuda.current_stream(dev).cuda_stream)
+    ev = HipEvents(2 * launches)
+    E = ev.handles
+    with open(path, "w") as f:
+        for T, H in SWEEP_SHAPES:
+            sets = make_sets(T, H, 8 if T <= 2048 else 3, dev)
+            n = len(sets)
+            s0 = sets[0]
+            for direction in ("fwd", "bwd"):
+                if direction == "fwd":
+                    plan, _ = ops.mhc_h_aggregate_plan_fwd(s0.residual, s0.pre, s0.out, T, H)
+                    nbytes = fwd_bytes(T, H)
+
+                    def call(k, a, b):
+                        x = sets[k % n]
+                        return lib.mhc_h_aggregate_fwd_timed(
+                            x.residual.data_ptr(), x.pre.data_ptr(), x.out.data_ptr(), T, H, sh,
+                            None, a, b)
+                else:
+                    plan, _ = ops.mhc_h_aggregate_plan_bwd(s0.residual, s0.pre, s0.grad_out,
+                                                           s0.grad_residual, s0.grad_pre, T, H)
+                    nbytes = bwd_bytes(T, H)
+
+                    def call(k, a, b):
+                        x = sets[k % n]
+                        return lib.mhc_h_aggregate_bwd_timed(
+                            x.residual.data_ptr(), x.pre.data_ptr(), x.grad_out.data_ptr(),
+                            x.grad_residual.data_ptr(), x.grad_pre.data_ptr(), T, H, sh, None,
+                            a, b)
+                for k in range(10):
+                    _lib.check(call(k, None, None))
+                torch.cuda.synchronize()
+                for k in range(launches):
+                    _lib.check(call(k, E[2 * k], E[2 * k + 1]))
+                torch.cuda.synchronize()
+                us = [ev.elapsed_us(2 * k, 2 * k + 1) for k in range(launches)]
+                q = st.quantiles(us, n=10)
+                rec = {"direction": direction, "T": T, "H": H, "bytes": nbytes,
+                       "us_mean": round(st.fmean(us), 3),
+                       "us_p20_p50_p80": [round(q[1], 3), round(q[4], 3), round(q[7], 3)],
+                       "gbps": round(nbytes / st.fmean(us) / 1e3, 1),
+                       "frac_of_8TBps": round(nbytes / st.fmean(us) / 1e3 / PEAK_HBM_GBPS, 4),
+                       "plan": plan}
+                f.write(json.dumps(rec) + "\n")
+                f.flush()
+                print(json.dumps(rec), file=sys.stderr, flush=True)
+            del sets
+            torch.cuda.empty_cache()
+    ev.close()
+
+
+# ---------------------------------------------------------------------------
 # CPU baseline: the oracle on a token sample
 # ---------------------------------------------------------------------------
 
@@ -324,6 +397,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run a 256 MiB device copy first (counter calibration)")
+    ap.add_argument("--sweep", metavar="OUT_JSONL",
+                    help="instead of the step benchmark, time each kernel per call at the "
+                         "latency / bandwidth / backward shapes and write JSON lines")
     ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV")
     ap.add_argument("--summarize-pmc", metavar="COUNTER_CSV", nargs="+")
     args = ap.parse_args()
@@ -333,6 +409,12 @@ def main() -> int:
         return 0
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc)
+        return 0
+    if args.sweep:
+        if args.gpus != 1:
+            print("the sweep runs on one GPU", file=sys.stderr)
+            return 2
+        run_sweep(args.sweep)
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this operation is token-parallel with no "

@@ -15,7 +15,7 @@ MHC_SUCCESS = 0
 MHC_ERROR_INVALID_VALUE = 1
 MHC_ERROR_ALIASING = 2
 MHC_ERROR_HIP = 3
-MHC_ABI_VERSION = 1
+MHC_ABI_VERSION = 2
 MHC_MAX_H = 1 << 26
 
 
@@ -26,6 +26,7 @@ class mhc_launch(ctypes.Structure):
         ("vec_width", c_int32),
         ("units_per_thread", c_int32),
         ("tokens_per_block", c_int32),
+        ("streams_per_block", c_int32),
     ]
 
     def as_dict(self) -> dict:

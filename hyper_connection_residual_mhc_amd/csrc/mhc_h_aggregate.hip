@@ -173,22 +173,20 @@ template <> __device__ __forceinline__ void store_vec<1>(Rsrc rs, uint32_t off, 
 // Forward kernel
 // ---------------------------------------------------------------------------
 //
-// Grid: blocks_per_token * T blocks of blockDim.x threads (a multiple of 64).
-// Block b serves token t = b / blocks_per_token and, within it, the units
-// [c * blockDim.x * UPT, (c + 1) * blockDim.x * UPT) with c = b mod
-// blocks_per_token; a unit is V consecutive hidden elements. Lane x of the
-// block owns units c*blockDim.x*UPT + k*blockDim.x + x for k < UPT, so every
-// load and store instruction of a wave covers 64 consecutive units.
-// All loads of a lane are issued before any arithmetic.
+// Grid: (blocks_per_token, T) blocks of blockDim.x threads (a multiple of
+// 64). Block (c, t) serves token t and, within it, the units
+// [c * blockDim.x * UPT, (c + 1) * blockDim.x * UPT); a unit is V consecutive
+// hidden elements. Lane x of the block owns units
+// c*blockDim.x*UPT + k*blockDim.x + x for k < UPT, so every load and store
+// instruction of a wave covers 64 consecutive units. All loads of a lane are
+// issued before any arithmetic.
 template <int V, int UPT>
 __global__ __launch_bounds__(1024) void hagg_fwd_kernel(
     const uint16_t* __restrict__ residual, const float* __restrict__ pre,
-    uint16_t* __restrict__ out, int64_t H, uint32_t units_per_token,
-    uint32_t blocks_per_token) {
+    uint16_t* __restrict__ out, int64_t H, uint32_t units_per_token) {
   typedef typename Vec<V>::type VT;
-  const uint32_t b = blockIdx.x;
-  const uint32_t t = b / blocks_per_token;
-  const uint32_t c = b - t * blocks_per_token;
+  const uint32_t c = blockIdx.x;
+  const uint32_t t = blockIdx.y;
 
   const float* p = pre + 4 * static_cast<int64_t>(t);
   const float w0 = p[0], w1 = p[1], w2 = p[2], w3 = p[3];
@@ -235,22 +233,50 @@ __global__ __launch_bounds__(1024) void hagg_fwd_kernel(
 // ---------------------------------------------------------------------------
 // Backward kernel
 // ---------------------------------------------------------------------------
-//
-// Grid: ceil(T / tokens_per_block) blocks of exactly 256 threads. Lane l
-// (= threadIdx.x) is accumulator lane l of the fixed order: it visits groups
-// k = l, l + 256, l + 512, ... (group k = hidden elements 8k .. 8k+7), U of
-// them per batch of loads, and for each element adds grad_out*residual_i to
-// its accumulator i in ascending h. It also writes grad_residual for every
-// element it visits. Then each wave halves its 64 accumulators with
-// offsets 32..1 and the four wave results meet in LDS as (y0+y2)+(y1+y3).
-// V elements are moved per access; V divides 8 and H, so a group is 8/V
-// accesses (fewer for a short last group).
+
 constexpr int kGroup = 8;
 constexpr int kLanes = 256;
 
+// Lane j (< OFF) of a wave receives x from lane j + OFF; other lanes receive
+// values that are never read. Register-only lane movement on gfx950:
+// permlane32_swap brings the upper half-wave down, permlane16_swap the odd
+// 16-lane rows onto the even ones, and DPP row_shl:n reads lane j + n within
+// a 16-lane row. The whole wave must be active (it is: the tree runs after
+// the divergent loop has reconverged).
+template <int OFF>
+__device__ __forceinline__ float from_lane_plus(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if constexpr (OFF == 32) {
+    return __uint_as_float(__builtin_amdgcn_permlane32_swap(u, u, false, false)[1]);
+  } else if constexpr (OFF == 16) {
+    return __uint_as_float(__builtin_amdgcn_permlane16_swap(u, u, false, false)[1]);
+  } else {
+    static_assert(OFF == 8 || OFF == 4 || OFF == 2 || OFF == 1, "row shift within 16 lanes");
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, static_cast<int>(u), 0x100 + OFF, 0xF,
+                                                      0xF, false));
+  }
+}
+
+// Grid: (ceil(T / tokens_per_block), 4 / S) blocks of exactly 256 threads.
+// Block (b, j) handles streams S*j .. S*j + S-1 of tokens
+// b*tokens_per_block .. (b+1)*tokens_per_block - 1, one token after the
+// other. The fixed order is defined per (token, stream), so splitting a
+// token's streams over blocks changes no bit and needs no communication
+// between blocks: S = 4 keeps a token in one block (grad_out read once), S = 1
+// gives four times as many blocks for short batches.
+//
+// Lane l (= threadIdx.x) is accumulator lane l of the fixed order: it visits
+// groups k = l, l + 256, l + 512, ... (group k = hidden elements 8k .. 8k+7),
+// U of them per batch of loads, and for each element adds grad_out*residual_i
+// to its accumulator i in ascending h. It also writes grad_residual for every
+// element it visits. Then each wave halves its 64 accumulators with offsets
+// 32..1 and the four wave results meet in LDS as (y0+y2)+(y1+y3).
+// V elements are moved per access; V divides 8 and H, so a group is 8/V
+// accesses (fewer for a short last group).
+//
 // At most 128 VGPRs (4 waves per SIMD), so that 4 blocks fit on a CU and a
 // 1024-token call is resident at once.
-template <int V, int U>
+template <int V, int U, int S>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void hagg_bwd_kernel(
     const uint16_t* __restrict__ residual, const float* __restrict__ pre,
     const uint16_t* __restrict__ grad_out, uint16_t* __restrict__ grad_residual,
@@ -258,30 +284,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void h
     int32_t tokens_per_block) {
   typedef typename Vec<V>::type VT;
   constexpr int NV = kGroup / V;  // accesses per full group
-  __shared__ float wave_sum[4][4];  // [wave][stream]
+  __shared__ float wave_sum[4][S];  // [wave][stream of this block]
 
   const int lane = threadIdx.x;
   const int wave = lane >> 6;
+  const int i0 = static_cast<int>(blockIdx.y) * S;  // first stream of this block
 
   for (int32_t tt = 0; tt < tokens_per_block; ++tt) {
     const int64_t t = static_cast<int64_t>(blockIdx.x) * tokens_per_block + tt;
     if (t >= T) break;  // uniform across the block
 
-    const float* p = pre + 4 * t;
-    const float w[4] = {p[0], p[1], p[2], p[3]};
-    // The token's grad_out row (2H bytes) and residual / grad_residual rows
-    // (8H bytes each).
+    const float* p = pre + 4 * t + i0;
+    float w[S];
+#pragma unroll
+    for (int i = 0; i < S; ++i) w[i] = p[i];
+    // The token's grad_out row (2H bytes) and the block's S residual /
+    // grad_residual rows (2SH bytes each).
     const Rsrc g_row = make_rsrc(grad_out + t * H, 2 * H);
-    const Rsrc r_row = make_rsrc(residual + t * 4 * H, 8 * H);
-    const Rsrc gr_row = make_rsrc(grad_residual + t * 4 * H, 8 * H);
+    const Rsrc r_row = make_rsrc(residual + (t * 4 + i0) * H, 2 * S * H);
+    const Rsrc gr_row = make_rsrc(grad_residual + (t * 4 + i0) * H, 2 * S * H);
     const uint32_t hs = static_cast<uint32_t>(H);  // elements between streams
     const uint32_t row = 2 * hs;                   // bytes between streams
 
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float acc[S];
+#pragma unroll
+    for (int i = 0; i < S; ++i) acc[i] = 0.0f;
 
     for (uint32_t k0 = lane; k0 < ngroups; k0 += kLanes * U) {
       VT g[U][NV];
-      VT r[U][NV][4];
+      VT r[U][NV][S];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint32_t k = k0 + u * kLanes;
@@ -291,7 +322,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void h
           if (k < ngroups && h < H) {
             g[u][v] = load_vec<V>(g_row, h, 0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) r[u][v][i] = load_vec<V>(r_row, h, i * row);
+            for (int i = 0; i < S; ++i) r[u][v][i] = load_vec<V>(r_row, h, i * row);
           }
         }
       }
@@ -305,7 +336,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void h
             // Stream by stream, so only one stream's values are live at a
             // time; each accumulator still adds its elements in ascending h.
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < S; ++i) {
               float gr[V];
 #pragma unroll
               for (int e = 0; e < V; ++e) {
@@ -324,19 +355,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void h
     // Wave stage: x[j] = x[j] + x[j + off] for off = 32, 16, 8, 4, 2, 1.
     // Lanes j >= off compute values nobody reads.
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
+    for (int i = 0; i < S; ++i) acc[i] = acc[i] + from_lane_plus<32>(acc[i]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = acc[i] + __shfl_down(acc[i], off, 64);
-    }
+    for (int i = 0; i < S; ++i) acc[i] = acc[i] + from_lane_plus<16>(acc[i]);
+#pragma unroll
+    for (int i = 0; i < S; ++i) acc[i] = acc[i] + from_lane_plus<8>(acc[i]);
+#pragma unroll
+    for (int i = 0; i < S; ++i) acc[i] = acc[i] + from_lane_plus<4>(acc[i]);
+#pragma unroll
+    for (int i = 0; i < S; ++i) acc[i] = acc[i] + from_lane_plus<2>(acc[i]);
+#pragma unroll
+    for (int i = 0; i < S; ++i) acc[i] = acc[i] + from_lane_plus<1>(acc[i]);
     if ((lane & 63) == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) wave_sum[wave][i] = acc[i];
+      for (int i = 0; i < S; ++i) wave_sum[wave][i] = acc[i];
     }
     __syncthreads();
-    if (lane < 4) {
+    if (lane < S) {
       const float y02 = wave_sum[0][lane] + wave_sum[2][lane];
       const float y13 = wave_sum[1][lane] + wave_sum[3][lane];
-      grad_pre[4 * t + lane] = y02 + y13;
+      grad_pre[4 * t + i0 + lane] = y02 + y13;
     }
     __syncthreads();  // wave_sum is reused by the next token
   }
@@ -448,6 +486,10 @@ bool vec_allowed(int V, int64_t H, const void* const* bufs, int nbufs) {
 // One dispatch covers at most 2^31 work-items (the AQL packet's grid size is a
 // 32-bit work-item count); larger problems are split over whole tokens.
 constexpr int64_t kMaxLaunchThreads = int64_t(1) << 31;
+constexpr int64_t kMaxGridY = 65535;
+// Backward streams per block by batch length (see plan_bwd).
+constexpr int64_t kTwoStreamsFromT = 128;
+constexpr int64_t kFourStreamsFromT = 512;
 
 struct FwdPlan {
   int V, block, upt;
@@ -466,6 +508,9 @@ mhc_status plan_fwd(const uint16_t* residual, const uint16_t* out, int64_t T, in
                   ov->vec_width, (long long)H);
     V = ov->vec_width;
   }
+  if (ov && (ov->tokens_per_block != 0 || ov->streams_per_block != 0))
+    return fail(MHC_ERROR_INVALID_VALUE,
+                "tokens_per_block and streams_per_block are backward-only fields");
   const int64_t upt_units = H / V;  // units per token
   int upt = 1;
   if (ov && ov->units_per_thread != 0) {
@@ -491,7 +536,10 @@ mhc_status plan_fwd(const uint16_t* residual, const uint16_t* out, int64_t T, in
   pl->upt = upt;
   pl->units_per_token = static_cast<uint32_t>(upt_units);
   pl->blocks_per_token = static_cast<uint32_t>(bpt);
+  // Tokens run along the grid's y dimension, at most 65535 per launch, and a
+  // launch stays within 2^31 work-items.
   int64_t tpl = kMaxLaunchThreads / (bpt * block);
+  if (tpl > kMaxGridY) tpl = kMaxGridY;
   if (tpl < 1) tpl = 1;  // cannot happen for H <= MHC_MAX_H
   pl->tokens_per_launch = tpl;
   pl->total_blocks = T * bpt;
@@ -499,7 +547,7 @@ mhc_status plan_fwd(const uint16_t* residual, const uint16_t* out, int64_t T, in
 }
 
 struct BwdPlan {
-  int V, U, tpb;
+  int V, U, S, tpb;
   int64_t ngroups, blocks_per_launch, total_blocks;
 };
 
@@ -531,6 +579,16 @@ mhc_status plan_bwd(const uint16_t* residual, const uint16_t* grad_out,
       return fail(MHC_ERROR_INVALID_VALUE,
                   "units_per_thread 4 needs vec_width >= 2 in the backward");
   }
+  // Streams per block: a token's four streams in one block once there are
+  // enough tokens to cover the CUs (grad_out is then read once per token);
+  // shorter batches spread each token over 2 or 4 blocks to use more CUs.
+  // Thresholds measured at H = 4096 and 7168 (T from 1 to 2048).
+  int S = T >= kFourStreamsFromT ? 4 : (T >= kTwoStreamsFromT ? 2 : 1);
+  if (ov && ov->streams_per_block != 0) {
+    if (ov->streams_per_block != 1 && ov->streams_per_block != 2 && ov->streams_per_block != 4)
+      return fail(MHC_ERROR_INVALID_VALUE, "streams_per_block must be 1, 2 or 4");
+    S = ov->streams_per_block;
+  }
   int tpb = 1;
   if (ov && ov->tokens_per_block != 0) {
     if (ov->tokens_per_block < 1 || ov->tokens_per_block > 4096)
@@ -539,10 +597,11 @@ mhc_status plan_bwd(const uint16_t* residual, const uint16_t* grad_out,
   }
   pl->V = V;
   pl->U = U;
+  pl->S = S;
   pl->tpb = tpb;
   pl->ngroups = (H + kGroup - 1) / kGroup;
   pl->blocks_per_launch = kMaxLaunchThreads / kLanes;
-  pl->total_blocks = (T + tpb - 1) / tpb;
+  pl->total_blocks = (T + tpb - 1) / tpb * (4 / S);
   return ok();
 }
 
@@ -596,10 +655,10 @@ struct Events {
 template <int V, int UPT>
 void launch_fwd_t(const FwdPlan& pl, const uint16_t* residual, const float* pre, uint16_t* out,
                   int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
-  const uint32_t blocks = static_cast<uint32_t>(tokens * pl.blocks_per_token);
-  hipExtLaunchKernelGGL(hagg_fwd_kernel<V, UPT>, dim3(blocks), dim3(pl.block), 0, stream,
-                        ev.start, ev.stop, 0, residual, pre, out, H, pl.units_per_token,
-                        pl.blocks_per_token);
+  hipExtLaunchKernelGGL(hagg_fwd_kernel<V, UPT>,
+                        dim3(pl.blocks_per_token, static_cast<uint32_t>(tokens)),
+                        dim3(pl.block), 0, stream, ev.start, ev.stop, 0, residual, pre, out, H,
+                        pl.units_per_token);
 }
 
 template <int V>
@@ -612,14 +671,26 @@ void launch_fwd_v(const FwdPlan& pl, const uint16_t* residual, const float* pre,
   }
 }
 
-template <int V, int U>
+template <int V, int U, int S>
 void launch_bwd_t(const BwdPlan& pl, const uint16_t* residual, const float* pre,
                   const uint16_t* grad_out, uint16_t* grad_residual, float* grad_pre,
                   int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
   const uint32_t blocks = static_cast<uint32_t>((tokens + pl.tpb - 1) / pl.tpb);
-  hipExtLaunchKernelGGL(hagg_bwd_kernel<V, U>, dim3(blocks), dim3(kLanes), 0, stream, ev.start,
-                        ev.stop, 0, residual, pre, grad_out, grad_residual, grad_pre, tokens, H,
-                        static_cast<uint32_t>(pl.ngroups), static_cast<int32_t>(pl.tpb));
+  hipExtLaunchKernelGGL(hagg_bwd_kernel<V, U, S>, dim3(blocks, 4 / S), dim3(kLanes), 0, stream,
+                        ev.start, ev.stop, 0, residual, pre, grad_out, grad_residual, grad_pre,
+                        tokens, H, static_cast<uint32_t>(pl.ngroups),
+                        static_cast<int32_t>(pl.tpb));
+}
+
+template <int V, int U>
+void launch_bwd_u(const BwdPlan& pl, const uint16_t* residual, const float* pre,
+                  const uint16_t* grad_out, uint16_t* grad_residual, float* grad_pre,
+                  int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
+  switch (pl.S) {
+    case 1: launch_bwd_t<V, U, 1>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
+    case 2: launch_bwd_t<V, U, 2>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
+    default: launch_bwd_t<V, U, 4>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
+  }
 }
 
 template <int V>
@@ -630,9 +701,9 @@ void launch_bwd_v(const BwdPlan& pl, const uint16_t* residual, const float* pre,
   // would not fit the 128-VGPR budget (the plan rejects that shape).
   constexpr int kMaxU = V == 1 ? 2 : 4;
   switch (pl.U) {
-    case 1: launch_bwd_t<V, 1>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
-    case 2: launch_bwd_t<V, 2>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
-    default: launch_bwd_t<V, kMaxU>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
+    case 1: launch_bwd_u<V, 1>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
+    case 2: launch_bwd_u<V, 2>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
+    default: launch_bwd_u<V, kMaxU>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
   }
 }
 
@@ -751,7 +822,7 @@ mhc_status mhc_h_aggregate_plan_fwd(const uint16_t* residual, const float* pre,
   if (st != MHC_SUCCESS) return st;
   FwdPlan pl;
   if ((st = plan_fwd(residual, out, T, H, launch, &pl)) != MHC_SUCCESS) return st;
-  if (plan) *plan = mhc_launch{pl.block, pl.V, pl.upt, 0};
+  if (plan) *plan = mhc_launch{pl.block, pl.V, pl.upt, 0, 0};
   if (grid_blocks) *grid_blocks = pl.total_blocks;
   return ok();
 }
@@ -766,7 +837,7 @@ mhc_status mhc_h_aggregate_plan_bwd(const uint16_t* residual, const float* pre,
   BwdPlan pl;
   if ((st = plan_bwd(residual, grad_out, grad_residual, T, H, launch, &pl)) != MHC_SUCCESS)
     return st;
-  if (plan) *plan = mhc_launch{kLanes, pl.V, pl.U, pl.tpb};
+  if (plan) *plan = mhc_launch{kLanes, pl.V, pl.U, pl.tpb, pl.S};
   if (grid_blocks) *grid_blocks = pl.total_blocks;
   return ok();
 }

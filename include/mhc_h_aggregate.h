@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define MHC_ABI_VERSION 1
+#define MHC_ABI_VERSION 2
 
 /* Hyper-connection expansion rate, fixed at 4 (Summary: residual [T, 4, H]). */
 #define MHC_HC 4
@@ -99,12 +99,18 @@ typedef enum mhc_status {
  *                     1 or 2).
  *   tokens_per_block  backward only: tokens one block handles in sequence,
  *                     1..4096.
+ *   streams_per_block backward only: residual streams one block handles,
+ *                     1, 2 or 4. The summation order is defined per
+ *                     (token, stream), so a token's streams may be spread
+ *                     over blocks without any change in the result.
+ * Forward calls reject non-zero backward-only fields.
  */
 typedef struct mhc_launch {
   int32_t block_threads;
   int32_t vec_width;
   int32_t units_per_thread;
   int32_t tokens_per_block;
+  int32_t streams_per_block;
 } mhc_launch;
 
 /* Version of this ABI (MHC_ABI_VERSION of the built library). */

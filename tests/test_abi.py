@@ -181,9 +181,10 @@ def test_forward_overrides(lib):
                                                                    "vec_width": 2,
                                                                    "units_per_thread": 4})
     assert plan == {"block_threads": 1024, "vec_width": 2, "units_per_thread": 4,
-                    "tokens_per_block": 0}
+                    "tokens_per_block": 0, "streams_per_block": 0}
     for bad in ({"block_threads": 100}, {"block_threads": 2048}, {"vec_width": 3},
-                {"units_per_thread": 3}, {"units_per_thread": 9}):
+                {"units_per_thread": 3}, {"units_per_thread": 9}, {"tokens_per_block": 2},
+                {"streams_per_block": 1}):
         with pytest.raises(MhcError, match="INVALID_VALUE"):
             ops.mhc_h_aggregate_plan_fwd(r, p, o, T, H, launch=bad)
     with pytest.raises(MhcError, match="vec_width 8 not allowed"):
@@ -197,14 +198,21 @@ def test_backward_plan_and_overrides(lib):
     r, p, g, gr, gp = bwd_ptrs(T, H)
     plan, grid = ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T, H)
     assert plan["block_threads"] == 256 and plan["vec_width"] == 8
-    assert plan["units_per_thread"] == 4
+    assert plan["units_per_thread"] == 4 and plan["streams_per_block"] == 4
     assert grid == -(-T // plan["tokens_per_block"])
     plan, grid = ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T, H,
                                               launch={"tokens_per_block": 3, "vec_width": 4,
                                                       "units_per_thread": 1})
     assert plan["tokens_per_block"] == 3 and plan["vec_width"] == 4 and grid == -(-T // 3)
+    plan, grid = ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T, H,
+                                              launch={"streams_per_block": 2})
+    assert plan["streams_per_block"] == 2 and grid == 2 * T
+    # short batches spread each token's streams over more blocks
+    for T_, spb in ((8, 1), (127, 1), (128, 2), (511, 2), (512, 4)):
+        plan, grid = ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T_, H)
+        assert plan["streams_per_block"] == spb and grid == T_ * (4 // spb), (T_, plan)
     for bad in ({"block_threads": 128}, {"tokens_per_block": 5000}, {"vec_width": 16},
-                {"units_per_thread": 3}):
+                {"units_per_thread": 3}, {"streams_per_block": 3}):
         with pytest.raises(MhcError, match="INVALID_VALUE"):
             ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T, H, launch=bad)
     with pytest.raises(MhcError, match="needs vec_width >= 2"):

@@ -70,10 +70,11 @@ def test_backward_every_launch_shape_gives_the_same_bytes(device, T, H):
     host = make_inputs(T, H, seed=2, grad=True)
     want_gr, want_gp = O.h_aggregate_bwd(host["residual"], host["pre"], host["grad_out"])
     widths = [v for v in (1, 2, 4, 8) if H % v == 0]
-    for v, u, tpb in itertools.product(widths, (1, 2, 4), (1, 2, 3, 8)):
+    for v, u, tpb, spb in itertools.product(widths, (1, 2, 4), (1, 3, 8), (1, 2, 4)):
         if v == 1 and u == 4:
             continue   # rejected by the plan (register budget)
-        launch = {"vec_width": v, "units_per_thread": u, "tokens_per_block": tpb}
+        launch = {"vec_width": v, "units_per_thread": u, "tokens_per_block": tpb,
+                  "streams_per_block": spb}
         say(f"backward launch {launch} T={T} H={H}")
         gr, gp = run_bwd(host, device, launch=launch)
         assert_bytes_equal(gr, want_gr, f"grad_residual {launch}")
@@ -88,7 +89,8 @@ def test_backward_canaries(device):
     d = to_device(host, device)
     res = []
     for s in SENTINELS:
-        for launch in (None, {"vec_width": 2, "tokens_per_block": 4}, {"vec_width": 1}):
+        for launch in (None, {"vec_width": 2, "tokens_per_block": 4}, {"vec_width": 1},
+                       {"streams_per_block": 1}, {"streams_per_block": 2, "tokens_per_block": 3}):
             say(f"backward canary 0x{s:x} {launch}")
             gr, grbuf = guarded_empty_bf16((T, 4, H), device, s)
             gpbuf = torch.full((T * 4 + 2 * GUARD,), float("nan"), dtype=torch.float32, device=device)
