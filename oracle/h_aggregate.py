@@ -174,6 +174,23 @@ def grad_residual_ref(pre: np.ndarray, grad_out: np.ndarray) -> np.ndarray:
     return bf16_rne(prod)
 
 
+def grad_residual_acc_ref(pre: np.ndarray, grad_out: np.ndarray,
+                          grad_residual_in: np.ndarray) -> np.ndarray:
+    """Accumulating form: grad_residual[t,i,h] += pre[t,i] * grad_out[t,h].
+
+    Reading taken (the pages only ask for a backward): the existing bf16
+    value is widened exactly, the fp32 product pre*g (one rounding) is added
+    to it in fp32 (one rounding), and the sum is rounded to bf16 once.
+    grad_residual_in: uint16 [T,4,H]. Returns the updated uint16 [T,4,H].
+    """
+    g = widen_bf16(grad_out)
+    old = widen_bf16(grad_residual_in)
+    with np.errstate(over="ignore", invalid="ignore"):
+        prod = np.multiply(pre[:, :, None], g[:, None, :])    # [T,4,H] fp32 RN
+        total = np.add(old, prod)                              # fp32 RN
+    return bf16_rne(total)
+
+
 def grad_pre_products(residual: np.ndarray, grad_out: np.ndarray) -> np.ndarray:
     """q[t,i,h] = grad_out[t,h] * residual[t,i,h] in fp32.
 
@@ -268,6 +285,18 @@ def h_aggregate_bwd(residual: np.ndarray, pre: np.ndarray, grad_out: np.ndarray
     return grad_residual_ref(pre, grad_out), grad_pre_ref(residual, grad_out)
 
 
+def h_aggregate_bwd_acc(residual: np.ndarray, pre: np.ndarray, grad_out: np.ndarray,
+                        grad_residual_in: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Backward that accumulates into an existing grad_residual (see
+    grad_residual_acc_ref) and writes grad_pre. Returns (updated
+    grad_residual uint16 [T,4,H], grad_pre float32 [T,4])."""
+    _check_bwd_args(residual, pre, grad_out)
+    if grad_residual_in.dtype != np.uint16 or grad_residual_in.shape != residual.shape:
+        raise ValueError("grad_residual_in must be uint16 bf16 bits of shape [T, 4, H]")
+    return (grad_residual_acc_ref(pre, grad_out, grad_residual_in),
+            grad_pre_ref(residual, grad_out))
+
+
 def grad_pre_exact(residual: np.ndarray, grad_out: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     """fp64 sum over h of grad_out*residual_i, and of its absolute values.
 
@@ -339,7 +368,7 @@ __all__ = [
     "HC", "GROUP", "LANES", "WAVE", "WAVES",
     "widen_bf16", "bf16_rne",
     "h_aggregate_fwd", "h_aggregate_fwd_exact",
-    "grad_residual_ref", "grad_pre_products", "canonical_tree_sum", "grad_pre_ref",
-    "h_aggregate_bwd", "grad_pre_exact",
+    "grad_residual_ref", "grad_residual_acc_ref", "grad_pre_products", "canonical_tree_sum",
+    "grad_pre_ref", "h_aggregate_bwd", "h_aggregate_bwd_acc", "grad_pre_exact",
     "bf16_ulp", "fwd_error_bound", "classify_fwd", "tree_error_bound",
 ]

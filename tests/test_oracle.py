@@ -421,6 +421,68 @@ def test_grad_residual_matches_exact_rational_small():
 
 
 # ---------------------------------------------------------------------------
+# Backward, accumulating form: grad_residual += pre * g
+# ---------------------------------------------------------------------------
+
+def test_grad_residual_acc_onto_negative_zero_equals_the_write_form():
+    """-0 is the identity of fp32 addition ((-0) + x = x for every x,
+    including +0 and -0), so accumulating onto -0.0 must give exactly the
+    bits of the non-accumulating gradient."""
+    inp = make_inputs(6, 1000, seed=20, grad=True)
+    neg0 = np.full((6, 4, 1000), 0x8000, np.uint16)
+    assert np.array_equal(O.grad_residual_acc_ref(inp["pre"], inp["grad_out"], neg0),
+                          O.grad_residual_ref(inp["pre"], inp["grad_out"]))
+
+
+def test_grad_residual_acc_single_rounding_discriminator():
+    """old = 1, g = 1, pre = 2^-8 + 2^-17: the fp32 sum 1 + 2^-8 + 2^-17 lies
+    above the bf16 midpoint 1 + 2^-8 and rounds up to 0x3F81. Rounding the
+    product to bf16 first (2^-8, since 2^-17 is below half a bf16 spacing at
+    2^-8) would give the tie 1 + 2^-8 and round to even, 0x3F80."""
+    pre = np.array([[2.0 ** -8 + 2.0 ** -17] * 4], np.float32)
+    g = np.array([[bf16_bits(1.0)]], np.uint16)
+    old = np.full((1, 4, 1), bf16_bits(1.0), np.uint16)
+    assert (O.grad_residual_acc_ref(pre, g, old) == 0x3F81).all()
+    double = O.bf16_rne(np.add(O.widen_bf16(old), O.widen_bf16(O.grad_residual_ref(pre, g))))
+    assert (double == 0x3F80).all()
+
+
+def test_grad_residual_acc_matches_exact_rational_small():
+    inp = make_inputs(2, 16, seed=21, grad=True)
+    old = make_inputs(2, 16, seed=22)["residual"]
+    got = O.grad_residual_acc_ref(inp["pre"], inp["grad_out"], old)
+    g = O.widen_bf16(inp["grad_out"])
+    ow = O.widen_bf16(old)
+    for t in range(2):
+        for i in range(4):
+            for h in range(16):
+                prod = round_to_f32(Fraction(float(inp["pre"][t, i])) * Fraction(float(g[t, h])))
+                tot = round_to_f32(Fraction(float(ow[t, i, h])) + prod)
+                assert int(got[t, i, h]) == frac_bf16_bits(round_to_bf16(tot)), (t, i, h)
+
+
+def test_grad_residual_acc_fp64_gate():
+    """Within half a bf16 ulp of the result plus the two fp32 roundings
+    (2 * 2^-24 * (|old| + |pre g|)) of the exact old + pre*g."""
+    inp = make_inputs(8, 2048, seed=23, grad=True)
+    old = make_inputs(8, 2048, seed=24)["residual"]
+    got = O.grad_residual_acc_ref(inp["pre"], inp["grad_out"], old)
+    p = inp["pre"].astype(np.float64)[:, :, None] * O.widen_bf16(inp["grad_out"]).astype(np.float64)[:, None, :]
+    ow = O.widen_bf16(old).astype(np.float64)
+    exact = ow + p
+    err = np.abs(O.widen_bf16(got).astype(np.float64) - exact)
+    bound = 0.5 * O.bf16_ulp(got) + 2.0 ** -23 * (np.abs(ow) + np.abs(p)) * 1.0000001
+    assert (err <= bound).all()
+
+
+def test_bwd_acc_returns_fresh_grad_pre():
+    inp = make_inputs(3, 300, seed=25, grad=True)
+    old = make_inputs(3, 300, seed=26)["residual"]
+    gr, gp = O.h_aggregate_bwd_acc(inp["residual"], inp["pre"], inp["grad_out"], old)
+    assert np.array_equal(gp, O.grad_pre_ref(inp["residual"], inp["grad_out"]))
+
+
+# ---------------------------------------------------------------------------
 # Backward: grad_pre and the fixed reduction order
 # ---------------------------------------------------------------------------
 
