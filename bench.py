@@ -60,6 +60,12 @@ def bwd_bytes(T: int, H: int) -> int:
     return T * (18 * H + 32)
 
 
+def bwd_acc_bytes(T: int, H: int) -> int:
+    """Accumulating backward: the plain backward's bytes plus reading the
+    stored grad_residual (8H) per token."""
+    return T * (26 * H + 32)
+
+
 def source_sha256() -> str:
     return hashlib.sha256(KERNEL_SRC.read_bytes()).hexdigest()
 
@@ -254,7 +260,8 @@ def run_sweep(path: str, launches: int = 200) -> None:
             sets = make_sets(T, H, 8 if T <= 2048 else 3, dev)
             n = len(sets)
             s0 = sets[0]
-            for direction in ("fwd", "bwd"):
+            directions = ("fwd", "bwd", "bwd_acc") if T >= 1024 else ("fwd", "bwd")
+            for direction in directions:
                 if direction == "fwd":
                     plan, _ = ops.mhc_h_aggregate_plan_fwd(s0.residual, s0.pre, s0.out, T, H)
                     nbytes = fwd_bytes(T, H)
@@ -264,6 +271,17 @@ def run_sweep(path: str, launches: int = 200) -> None:
                         return lib.mhc_h_aggregate_fwd_timed(
                             x.residual.data_ptr(), x.pre.data_ptr(), x.out.data_ptr(), T, H, sh,
                             None, a, b)
+                elif direction == "bwd_acc":
+                    plan, _ = ops.mhc_h_aggregate_plan_bwd_acc(s0.residual, s0.pre, s0.grad_out,
+                                                               s0.grad_residual, s0.grad_pre, T, H)
+                    nbytes = bwd_acc_bytes(T, H)
+
+                    def call(k, a, b):
+                        x = sets[k % n]
+                        return lib.mhc_h_aggregate_bwd_acc(
+                            x.residual.data_ptr(), x.pre.data_ptr(), x.grad_out.data_ptr(),
+                            x.grad_residual.data_ptr(), x.grad_pre.data_ptr(), T, H, sh, None,
+                            a, b)
                 else:
                     plan, _ = ops.mhc_h_aggregate_plan_bwd(s0.residual, s0.pre, s0.grad_out,
                                                            s0.grad_residual, s0.grad_pre, T, H)

@@ -269,14 +269,15 @@ __device__ __forceinline__ float from_lane_plus(float x) {
 // groups k = l, l + 256, l + 512, ... (group k = hidden elements 8k .. 8k+7),
 // U of them per batch of loads, and for each element adds grad_out*residual_i
 // to its accumulator i in ascending h. It also writes grad_residual for every
-// element it visits. Then each wave halves its 64 accumulators with offsets
-// 32..1 and the four wave results meet in LDS as (y0+y2)+(y1+y3).
+// element it visits (ACC: adds the product to the stored gradient in fp32 and
+// rounds the sum once). Then each wave halves its 64 accumulators with
+// offsets 32..1 and the four wave results meet in LDS as (y0+y2)+(y1+y3).
 // V elements are moved per access; V divides 8 and H, so a group is 8/V
 // accesses (fewer for a short last group).
 //
 // At most 128 VGPRs (4 waves per SIMD), so that 4 blocks fit on a CU and a
 // 1024-token call is resident at once.
-template <int V, int U, int S>
+template <int V, int U, int S, bool ACC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void hagg_bwd_kernel(
     const uint16_t* __restrict__ residual, const float* __restrict__ pre,
     const uint16_t* __restrict__ grad_out, uint16_t* __restrict__ grad_residual,
@@ -313,6 +314,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void h
     for (uint32_t k0 = lane; k0 < ngroups; k0 += kLanes * U) {
       VT g[U][NV];
       VT r[U][NV][S];
+      VT old[ACC ? U : 1][NV][S];  // accumulating form: the stored gradient
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint32_t k = k0 + u * kLanes;
@@ -323,6 +325,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void h
             g[u][v] = load_vec<V>(g_row, h, 0);
 #pragma unroll
             for (int i = 0; i < S; ++i) r[u][v][i] = load_vec<V>(r_row, h, i * row);
+            if constexpr (ACC) {
+#pragma unroll
+              for (int i = 0; i < S; ++i) old[u][v][i] = load_vec<V>(gr_row, h, i * row);
+            }
           }
         }
       }
@@ -342,6 +348,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void h
               for (int e = 0; e < V; ++e) {
                 const float ge = elem<V>(g[u][v], e);
                 gr[e] = w[i] * ge;
+                if constexpr (ACC) gr[e] = elem<V>(old[u][v][i], e) + gr[e];
                 const float q = ge * elem<V>(r[u][v][i], e);  // exact in the normal range
                 acc[i] = acc[i] + q;
               }
@@ -546,13 +553,23 @@ mhc_status plan_fwd(const uint16_t* residual, const uint16_t* out, int64_t T, in
   return ok();
 }
 
+// Largest load batch U in {1, 2, 4} whose loaded data fits 96 VGPRs: per
+// group NV = 8/V accesses of each of the 1 + S (+ S stored gradients when
+// accumulating) rows, each access max(V/2, 1) registers. With the rest of
+// the kernel this stays under the 128-VGPR budget without spills.
+constexpr int bwd_max_u(int V, int S, bool acc) {
+  const int per_group = (kGroup / V) * (1 + (acc ? 2 : 1) * S) * (V >= 2 ? V / 2 : 1);
+  return 4 * per_group <= 96 ? 4 : (2 * per_group <= 96 ? 2 : 1);
+}
+
 struct BwdPlan {
   int V, U, S, tpb;
+  bool acc;
   int64_t ngroups, blocks_per_launch, total_blocks;
 };
 
 mhc_status plan_bwd(const uint16_t* residual, const uint16_t* grad_out,
-                    const uint16_t* grad_residual, int64_t T, int64_t H,
+                    const uint16_t* grad_residual, int64_t T, int64_t H, bool acc,
                     const mhc_launch* ov, BwdPlan* pl) {
   const void* bufs[3] = {residual, grad_out, grad_residual};
   int V = widest_vec(H, bufs, 3);
@@ -565,20 +582,6 @@ mhc_status plan_bwd(const uint16_t* residual, const uint16_t* grad_out,
   }
   if (ov && ov->block_threads != 0 && ov->block_threads != kLanes)
     return fail(MHC_ERROR_INVALID_VALUE, "backward block_threads must be 0 or 256");
-  // Groups each lane loads before its arithmetic. Four (up to 320 bytes of
-  // input per lane: all of a lane's groups at H = 7168) fit the 128-VGPR
-  // budget, so every byte a lane needs is in flight at once while all blocks
-  // of a 1024-token call stay resident; this measured fastest at T = 1024,
-  // 2048 and 8192. The scalar path batches two.
-  int U = V == 1 ? 2 : 4;
-  if (ov && ov->units_per_thread != 0) {
-    if (ov->units_per_thread != 1 && ov->units_per_thread != 2 && ov->units_per_thread != 4)
-      return fail(MHC_ERROR_INVALID_VALUE, "units_per_thread must be 1, 2 or 4");
-    U = ov->units_per_thread;
-    if (V == 1 && U == 4)
-      return fail(MHC_ERROR_INVALID_VALUE,
-                  "units_per_thread 4 needs vec_width >= 2 in the backward");
-  }
   // Streams per block: a token's four streams in one block once there are
   // enough tokens to cover the CUs (grad_out is then read once per token);
   // shorter batches spread each token over 2 or 4 blocks to use more CUs.
@@ -588,6 +591,22 @@ mhc_status plan_bwd(const uint16_t* residual, const uint16_t* grad_out,
     if (ov->streams_per_block != 1 && ov->streams_per_block != 2 && ov->streams_per_block != 4)
       return fail(MHC_ERROR_INVALID_VALUE, "streams_per_block must be 1, 2 or 4");
     S = ov->streams_per_block;
+  }
+  // Groups each lane loads before its arithmetic: as many as the register
+  // budget allows, up to four (all of a lane's groups at H = 7168), so every
+  // byte a lane needs is in flight at once while all blocks of a 1024-token
+  // call stay resident; four measured fastest at T = 1024, 2048 and 8192.
+  const int max_u = bwd_max_u(V, S, acc);
+  int U = max_u;
+  if (ov && ov->units_per_thread != 0) {
+    if (ov->units_per_thread != 1 && ov->units_per_thread != 2 && ov->units_per_thread != 4)
+      return fail(MHC_ERROR_INVALID_VALUE, "units_per_thread must be 1, 2 or 4");
+    U = ov->units_per_thread;
+    if (U > max_u)
+      return fail(MHC_ERROR_INVALID_VALUE,
+                  "units_per_thread %d exceeds the register budget (at most %d for vec_width "
+                  "%d, %d streams per block%s)",
+                  U, max_u, V, S, acc ? ", accumulating" : "");
   }
   int tpb = 1;
   if (ov && ov->tokens_per_block != 0) {
@@ -599,6 +618,7 @@ mhc_status plan_bwd(const uint16_t* residual, const uint16_t* grad_out,
   pl->U = U;
   pl->S = S;
   pl->tpb = tpb;
+  pl->acc = acc;
   pl->ngroups = (H + kGroup - 1) / kGroup;
   pl->blocks_per_launch = kMaxLaunchThreads / kLanes;
   pl->total_blocks = (T + tpb - 1) / tpb * (4 / S);
@@ -671,25 +691,40 @@ void launch_fwd_v(const FwdPlan& pl, const uint16_t* residual, const float* pre,
   }
 }
 
-template <int V, int U, int S>
+template <int V, int U, int S, bool ACC>
 void launch_bwd_t(const BwdPlan& pl, const uint16_t* residual, const float* pre,
                   const uint16_t* grad_out, uint16_t* grad_residual, float* grad_pre,
                   int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
   const uint32_t blocks = static_cast<uint32_t>((tokens + pl.tpb - 1) / pl.tpb);
-  hipExtLaunchKernelGGL(hagg_bwd_kernel<V, U, S>, dim3(blocks, 4 / S), dim3(kLanes), 0, stream,
-                        ev.start, ev.stop, 0, residual, pre, grad_out, grad_residual, grad_pre,
-                        tokens, H, static_cast<uint32_t>(pl.ngroups),
+  hipExtLaunchKernelGGL(hagg_bwd_kernel<V, U, S, ACC>, dim3(blocks, 4 / S), dim3(kLanes), 0,
+                        stream, ev.start, ev.stop, 0, residual, pre, grad_out, grad_residual,
+                        grad_pre, tokens, H, static_cast<uint32_t>(pl.ngroups),
                         static_cast<int32_t>(pl.tpb));
 }
 
-template <int V, int U>
-void launch_bwd_u(const BwdPlan& pl, const uint16_t* residual, const float* pre,
+// Instantiates only the batches the register budget allows (the plan never
+// asks for more): U is clamped to bwd_max_u at compile time.
+template <int V, int S, bool ACC>
+void launch_bwd_s(const BwdPlan& pl, const uint16_t* residual, const float* pre,
+                  const uint16_t* grad_out, uint16_t* grad_residual, float* grad_pre,
+                  int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
+  constexpr int kMaxU = bwd_max_u(V, S, ACC);
+  constexpr int kU2 = kMaxU < 2 ? kMaxU : 2;
+  switch (pl.U) {
+    case 1: launch_bwd_t<V, 1, S, ACC>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
+    case 2: launch_bwd_t<V, kU2, S, ACC>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
+    default: launch_bwd_t<V, kMaxU, S, ACC>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
+  }
+}
+
+template <int V, bool ACC>
+void launch_bwd_a(const BwdPlan& pl, const uint16_t* residual, const float* pre,
                   const uint16_t* grad_out, uint16_t* grad_residual, float* grad_pre,
                   int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
   switch (pl.S) {
-    case 1: launch_bwd_t<V, U, 1>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
-    case 2: launch_bwd_t<V, U, 2>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
-    default: launch_bwd_t<V, U, 4>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
+    case 1: launch_bwd_s<V, 1, ACC>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
+    case 2: launch_bwd_s<V, 2, ACC>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
+    default: launch_bwd_s<V, 4, ACC>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
   }
 }
 
@@ -697,14 +732,10 @@ template <int V>
 void launch_bwd_v(const BwdPlan& pl, const uint16_t* residual, const float* pre,
                   const uint16_t* grad_out, uint16_t* grad_residual, float* grad_pre,
                   int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
-  // The scalar path batches at most 2 groups: 4 groups of 40 scalar loads
-  // would not fit the 128-VGPR budget (the plan rejects that shape).
-  constexpr int kMaxU = V == 1 ? 2 : 4;
-  switch (pl.U) {
-    case 1: launch_bwd_u<V, 1>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
-    case 2: launch_bwd_u<V, 2>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
-    default: launch_bwd_u<V, kMaxU>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
-  }
+  if (pl.acc)
+    launch_bwd_a<V, true>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
+  else
+    launch_bwd_a<V, false>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
 }
 
 // Events of the i-th of n launches of one call: start on the first, stop on
@@ -751,13 +782,13 @@ mhc_status run_fwd(const uint16_t* residual, const float* pre, uint16_t* out, in
 
 mhc_status run_bwd(const uint16_t* residual, const float* pre, const uint16_t* grad_out,
                    uint16_t* grad_residual, float* grad_pre, int64_t T, int64_t H, void* stream,
-                   const mhc_launch* launch, Events ev) {
+                   const mhc_launch* launch, Events ev, bool acc) {
   mhc_status st = validate_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, H);
   if (st != MHC_SUCCESS) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (T == 0) return record_empty(ev, s);
   BwdPlan pl;
-  if ((st = plan_bwd(residual, grad_out, grad_residual, T, H, launch, &pl)) != MHC_SUCCESS)
+  if ((st = plan_bwd(residual, grad_out, grad_residual, T, H, acc, launch, &pl)) != MHC_SUCCESS)
     return st;
   const int64_t tokens_per_launch = pl.blocks_per_launch * pl.tpb;
   (void)hipGetLastError();
@@ -835,7 +866,7 @@ mhc_status mhc_h_aggregate_plan_bwd(const uint16_t* residual, const float* pre,
   mhc_status st = validate_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, H);
   if (st != MHC_SUCCESS) return st;
   BwdPlan pl;
-  if ((st = plan_bwd(residual, grad_out, grad_residual, T, H, launch, &pl)) != MHC_SUCCESS)
+  if ((st = plan_bwd(residual, grad_out, grad_residual, T, H, false, launch, &pl)) != MHC_SUCCESS)
     return st;
   if (plan) *plan = mhc_launch{kLanes, pl.V, pl.U, pl.tpb, pl.S};
   if (grid_blocks) *grid_blocks = pl.total_blocks;
@@ -866,14 +897,14 @@ mhc_status mhc_h_aggregate_bwd_ex(const uint16_t* residual, const float* pre,
                                   float* grad_pre, int64_t T, int64_t H, void* stream,
                                   const mhc_launch* launch) {
   return run_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, H, stream, launch,
-                 Events{nullptr, nullptr});
+                 Events{nullptr, nullptr}, false);
 }
 
 mhc_status mhc_h_aggregate_bwd(const uint16_t* residual, const float* pre,
                                const uint16_t* grad_out, uint16_t* grad_residual,
                                float* grad_pre, int64_t T, int64_t H, void* stream) {
   return run_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, H, stream, nullptr,
-                 Events{nullptr, nullptr});
+                 Events{nullptr, nullptr}, false);
 }
 
 mhc_status mhc_h_aggregate_bwd_timed(const uint16_t* residual, const float* pre,
@@ -882,7 +913,33 @@ mhc_status mhc_h_aggregate_bwd_timed(const uint16_t* residual, const float* pre,
                                      const mhc_launch* launch, void* start_event,
                                      void* stop_event) {
   return run_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, H, stream, launch,
-                 Events{static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)});
+                 Events{static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)},
+                 false);
+}
+
+mhc_status mhc_h_aggregate_bwd_acc(const uint16_t* residual, const float* pre,
+                                   const uint16_t* grad_out, uint16_t* grad_residual,
+                                   float* grad_pre, int64_t T, int64_t H, void* stream,
+                                   const mhc_launch* launch, void* start_event,
+                                   void* stop_event) {
+  return run_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, H, stream, launch,
+                 Events{static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)},
+                 true);
+}
+
+mhc_status mhc_h_aggregate_plan_bwd_acc(const uint16_t* residual, const float* pre,
+                                        const uint16_t* grad_out, const uint16_t* grad_residual,
+                                        const float* grad_pre, int64_t T, int64_t H,
+                                        const mhc_launch* launch, mhc_launch* plan,
+                                        int64_t* grid_blocks) {
+  mhc_status st = validate_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, H);
+  if (st != MHC_SUCCESS) return st;
+  BwdPlan pl;
+  if ((st = plan_bwd(residual, grad_out, grad_residual, T, H, true, launch, &pl)) != MHC_SUCCESS)
+    return st;
+  if (plan) *plan = mhc_launch{kLanes, pl.V, pl.U, pl.tpb, pl.S};
+  if (grid_blocks) *grid_blocks = pl.total_blocks;
+  return ok();
 }
 
 mhc_status mhc_bf16_rne_probe(uint32_t first_bits, int64_t n, uint16_t* out, void* stream) {

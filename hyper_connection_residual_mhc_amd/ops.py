@@ -146,6 +146,29 @@ def mhc_h_aggregate_bwd_timed(residual: torch.Tensor, pre: torch.Tensor, grad_ou
     return grad_residual, grad_pre
 
 
+def mhc_h_aggregate_bwd_acc(residual: torch.Tensor, pre: torch.Tensor, grad_out: torch.Tensor,
+                            grad_residual: torch.Tensor, grad_pre: torch.Tensor,
+                            stream: torch.cuda.Stream | None = None, launch=None,
+                            start_event: int | None = None, stop_event: int | None = None
+                            ) -> tuple[torch.Tensor, torch.Tensor]:
+    """Accumulating backward: grad_residual += pre * grad_out (in place, one
+    bf16 rounding of the fp32 sum); grad_pre is written. Asynchronous."""
+    T, H = _fwd_shapes(residual)
+    dev = residual.device
+    _require(residual, "residual", torch.bfloat16, (T, HC, H))
+    _require(pre, "pre", torch.float32, (T, HC), dev)
+    _require(grad_out, "grad_out", torch.bfloat16, (T, H), dev)
+    _require(grad_residual, "grad_residual", torch.bfloat16, (T, HC, H), dev)
+    _require(grad_pre, "grad_pre", torch.float32, (T, HC), dev)
+    with torch.cuda.device(dev):
+        st = _lib.lib().mhc_h_aggregate_bwd_acc(
+            residual.data_ptr(), pre.data_ptr(), grad_out.data_ptr(),
+            grad_residual.data_ptr(), grad_pre.data_ptr(), T, H,
+            _stream_handle(dev, stream), _launch_arg(launch), start_event, stop_event)
+    check(st)
+    return grad_residual, grad_pre
+
+
 def mhc_bf16_rne_probe(first_bits: int, out: torch.Tensor,
                        stream: torch.cuda.Stream | None = None) -> torch.Tensor:
     """out[k] = device bf16 rounding of the fp32 pattern first_bits + k (out: int16/uint16)."""
@@ -191,6 +214,19 @@ def mhc_h_aggregate_plan_bwd(residual, pre, grad_out, grad_residual, grad_pre, T
                                               _addr(grad_residual), _addr(grad_pre), T, H,
                                               _launch_arg(launch), ctypes.byref(plan),
                                               ctypes.byref(grid)))
+    return plan.as_dict(), int(grid.value)
+
+
+def mhc_h_aggregate_plan_bwd_acc(residual, pre, grad_out, grad_residual, grad_pre, T: int,
+                                 H: int, launch=None) -> tuple[dict, int]:
+    """Host-only: the launch shape and block count an accumulating backward
+    call would use."""
+    plan = mhc_launch()
+    grid = ctypes.c_int64(0)
+    check(_lib.lib().mhc_h_aggregate_plan_bwd_acc(_addr(residual), _addr(pre), _addr(grad_out),
+                                                  _addr(grad_residual), _addr(grad_pre), T, H,
+                                                  _launch_arg(launch), ctypes.byref(plan),
+                                                  ctypes.byref(grid)))
     return plan.as_dict(), int(grid.value)
 
 

@@ -95,8 +95,10 @@ typedef enum mhc_status {
  *                     divide H and match the alignment of every bf16 buffer.
  *   units_per_thread  forward: vector units each thread handles; backward:
  *                     8-element groups each lane loads before its
- *                     arithmetic. 1, 2 or 4 (backward with vec_width 1:
- *                     1 or 2).
+ *                     arithmetic. 1, 2 or 4; in the backward at most what
+ *                     the register budget allows for the vec_width and
+ *                     streams_per_block (the plan query reports it; more
+ *                     gives MHC_ERROR_INVALID_VALUE).
  *   tokens_per_block  backward only: tokens one block handles in sequence,
  *                     1..4096.
  *   streams_per_block backward only: residual streams one block handles,
@@ -184,6 +186,25 @@ mhc_status mhc_h_aggregate_bwd_timed(const uint16_t* residual, const float* pre,
                                      void* start_event, void* stop_event);
 
 /*
+ * Accumulating backward (for training, where the residual stream's gradient
+ * also receives contributions from other branches):
+ *   grad_residual[t,i,h] = bf16( fp32(grad_residual[t,i,h]) + RN32(pre[t,i] *
+ *                                grad_out[t,h]) )
+ * i.e. the stored bf16 gradient is widened exactly, the fp32-rounded product
+ * is added in fp32 and the sum is rounded to bf16 once. grad_residual is
+ * read and written in place (it must still not overlap any input or
+ * grad_pre); grad_pre is written as in mhc_h_aggregate_bwd. `launch`,
+ * `start_event` and `stop_event` may each be NULL (same meaning as in the
+ * *_ex and *_timed calls). Moves 26H + 32 bytes per token.
+ */
+mhc_status mhc_h_aggregate_bwd_acc(const uint16_t* residual, const float* pre,
+                                   const uint16_t* grad_out,
+                                   uint16_t* grad_residual, float* grad_pre,
+                                   int64_t T, int64_t H, void* stream,
+                                   const mhc_launch* launch, void* start_event,
+                                   void* stop_event);
+
+/*
  * Host-only checks and plan queries. They touch no device and no memory
  * behind the pointers (the pointers are used only as numbers for alignment
  * and overlap tests), so they run without a GPU.
@@ -213,6 +234,13 @@ mhc_status mhc_h_aggregate_plan_bwd(const uint16_t* residual, const float* pre,
                                     const float* grad_pre, int64_t T,
                                     int64_t H, const mhc_launch* launch,
                                     mhc_launch* plan, int64_t* grid_blocks);
+mhc_status mhc_h_aggregate_plan_bwd_acc(const uint16_t* residual,
+                                        const float* pre,
+                                        const uint16_t* grad_out,
+                                        const uint16_t* grad_residual,
+                                        const float* grad_pre, int64_t T,
+                                        int64_t H, const mhc_launch* launch,
+                                        mhc_launch* plan, int64_t* grid_blocks);
 
 /*
  * Conversion probe: out[k] = bf16 bits of the fp32 value whose bit pattern

@@ -215,7 +215,7 @@ def test_backward_plan_and_overrides(lib):
                 {"units_per_thread": 3}, {"streams_per_block": 3}):
         with pytest.raises(MhcError, match="INVALID_VALUE"):
             ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T, H, launch=bad)
-    with pytest.raises(MhcError, match="needs vec_width >= 2"):
+    with pytest.raises(MhcError, match="exceeds the register budget"):
         ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T, H,
                                      launch={"vec_width": 1, "units_per_thread": 4})
     # grad_out misaligned by one element forces the scalar path
@@ -264,3 +264,23 @@ def test_missing_library_raises_import_error(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", Path(tmp_path) / "absent.so")
     with pytest.raises(ImportError, match="missing"):
         _lib.lib()
+
+
+def test_accumulating_backward_plan(lib):
+    """The accumulating backward also loads the stored gradient, so its load
+    batch is smaller where the register budget requires it; it follows the
+    same streams-per-block policy and the same argument rules."""
+    T, H = 2048, 7168
+    r, p, g, gr, gp = bwd_ptrs(T, H)
+    plan, grid = ops.mhc_h_aggregate_plan_bwd_acc(r, p, g, gr, gp, T, H)
+    assert plan["streams_per_block"] == 4 and plan["units_per_thread"] == 2 and grid == T
+    plan, _ = ops.mhc_h_aggregate_plan_bwd_acc(r, p, g, gr, gp, 64, H)
+    assert plan["streams_per_block"] == 1 and plan["units_per_thread"] == 4
+    with pytest.raises(MhcError, match="exceeds the register budget"):
+        ops.mhc_h_aggregate_plan_bwd_acc(r, p, g, gr, gp, T, H, launch={"units_per_thread": 4})
+    with pytest.raises(MhcError, match="ALIASING"):
+        ops.mhc_h_aggregate_plan_bwd_acc(r, p, g, r, gp, T, H)
+    assert lib.mhc_h_aggregate_bwd_acc(r, p, g, gr, gr, T, H, None, None, None,
+                                       None) == MHC_ERROR_ALIASING
+    assert lib.mhc_h_aggregate_bwd_acc(0, 0, 0, 0, 0, 0, H, None, None, None,
+                                       None) == MHC_SUCCESS

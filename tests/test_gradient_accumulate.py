@@ -1,0 +1,116 @@
+"""Accumulating backward (grad_residual += pre * grad_out) against the oracle.
+
+Reading (documented in the public header): the stored bf16 gradient is
+widened exactly, the fp32-rounded product is added in fp32 and the sum is
+rounded to bf16 once; grad_pre is written as in the plain backward. The
+operation is the backward of page "Add batch-invariant h_aggregate kernel"
+(RL-Kernel pull request 366, review comments) in the form a training step
+needs when the residual stream also receives gradient from other branches.
+Tolerance: 0 ulp for both outputs.
+"""
+
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import assert_bytes_equal
+from gpu_util import run_bwd, say
+from hyper_connection_residual_mhc_amd import ops
+from hyper_connection_residual_mhc_amd.workloads import (bf16_tensor_to_bits, bits_to_bf16_tensor,
+                                                         make_inputs, to_device)
+from oracle import h_aggregate as O
+
+pytestmark = pytest.mark.gpu
+
+
+def run_acc(host, old_bits, dev, launch=None):
+    d = to_device(host, dev)
+    gr = bits_to_bf16_tensor(old_bits, dev).contiguous()
+    gp = torch.empty((host["residual"].shape[0], 4), dtype=torch.float32, device=dev)
+    ops.mhc_h_aggregate_bwd_acc(d["residual"], d["pre"], d["grad_out"], gr, gp, launch=launch)
+    torch.cuda.synchronize()
+    return bf16_tensor_to_bits(gr), gp.cpu().numpy()
+
+
+@pytest.mark.parametrize("T,H", [(1, 4096), (8, 7168), (128, 7168), (129, 4096), (1024, 7168),
+                                 (2048, 7168), (3, 1279), (5, 4100), (4, 20001)])
+def test_accumulate_bit_exact(device, T, H):
+    say(f"accumulate parity T={T} H={H}")
+    host = make_inputs(T, H, seed=T + 3 * H, grad=True)
+    old = make_inputs(T, H, seed=T + 3 * H + 1)["residual"]
+    got_gr, got_gp = run_acc(host, old, device)
+    want_gr, want_gp = O.h_aggregate_bwd_acc(host["residual"], host["pre"], host["grad_out"], old)
+    assert_bytes_equal(got_gr, want_gr, f"accumulated grad_residual T={T} H={H}")
+    assert_bytes_equal(got_gp, want_gp, f"grad_pre T={T} H={H}")
+
+
+def test_accumulate_onto_negative_zero_equals_plain_backward(device):
+    """-0 is the additive identity, so accumulating onto a -0 buffer gives the
+    plain backward's bytes exactly."""
+    say("accumulate onto -0")
+    host = make_inputs(300, 7168, seed=5, grad=True)
+    neg0 = np.full((300, 4, 7168), 0x8000, np.uint16)
+    acc_gr, acc_gp = run_acc(host, neg0, device)
+    gr, gp = run_bwd(host, device)
+    assert_bytes_equal(acc_gr, gr, "grad_residual")
+    assert_bytes_equal(acc_gp, gp, "grad_pre")
+
+
+def test_accumulate_twice_is_two_roundings(device):
+    """Two calls accumulate twice: the oracle applied twice, byte for byte."""
+    say("accumulate twice")
+    host = make_inputs(64, 4096, seed=6, grad=True)
+    old = make_inputs(64, 4096, seed=7)["residual"]
+    d = to_device(host, device)
+    gr = bits_to_bf16_tensor(old, device).contiguous()
+    gp = torch.empty((64, 4), dtype=torch.float32, device=device)
+    ops.mhc_h_aggregate_bwd_acc(d["residual"], d["pre"], d["grad_out"], gr, gp)
+    ops.mhc_h_aggregate_bwd_acc(d["residual"], d["pre"], d["grad_out"], gr, gp)
+    torch.cuda.synchronize()
+    once = O.grad_residual_acc_ref(host["pre"], host["grad_out"], old)
+    twice = O.grad_residual_acc_ref(host["pre"], host["grad_out"], once)
+    assert_bytes_equal(bf16_tensor_to_bits(gr), twice, "twice")
+
+
+@pytest.mark.parametrize("T,H", [(37, 7168), (9, 1279)])
+def test_accumulate_every_launch_shape_same_bytes(device, T, H):
+    host = make_inputs(T, H, seed=8, grad=True)
+    old = make_inputs(T, H, seed=9)["residual"]
+    want_gr, want_gp = O.h_aggregate_bwd_acc(host["residual"], host["pre"], host["grad_out"], old)
+    widths = [v for v in (1, 2, 4, 8) if H % v == 0]
+    for v, spb, tpb in itertools.product(widths, (1, 2, 4), (1, 3)):
+        plan, _ = ops.mhc_h_aggregate_plan_bwd_acc(1 << 34, 1 << 35, 1 << 36, 1 << 37, 1 << 38,
+                                                   T, H, launch={"vec_width": v,
+                                                                 "streams_per_block": spb})
+        for u in (1, 2, 4):
+            if u > plan["units_per_thread"]:
+                continue   # beyond the register budget (rejected by the plan)
+            launch = {"vec_width": v, "units_per_thread": u, "tokens_per_block": tpb,
+                      "streams_per_block": spb}
+            say(f"accumulate launch {launch} T={T} H={H}")
+            gr, gp = run_acc(host, old, device, launch=launch)
+            assert_bytes_equal(gr, want_gr, f"grad_residual {launch}")
+            assert_bytes_equal(gp, want_gp, f"grad_pre {launch}")
+
+
+def test_accumulate_batch_split(device):
+    T, H = 700, 7168
+    say(f"accumulate batch split T={T}")
+    host = make_inputs(T, H, seed=10, grad=True)
+    old = make_inputs(T, H, seed=11)["residual"]
+    d = to_device(host, device)
+    gr = bits_to_bf16_tensor(old, device).contiguous()
+    gp = torch.empty((T, 4), dtype=torch.float32, device=device)
+    lo = 0
+    for n in (1, 7, 129, 563):
+        sl = slice(lo, lo + n)
+        ops.mhc_h_aggregate_bwd_acc(d["residual"][sl], d["pre"][sl], d["grad_out"][sl], gr[sl], gp[sl])
+        lo += n
+    torch.cuda.synchronize()
+    want_gr, want_gp = O.h_aggregate_bwd_acc(host["residual"], host["pre"], host["grad_out"], old)
+    assert_bytes_equal(bf16_tensor_to_bits(gr), want_gr, "split grad_residual")
+    assert_bytes_equal(gp.cpu().numpy(), want_gp, "split grad_pre")
