@@ -9,8 +9,8 @@ Recipe (the pages print no value distributions; these follow the shapes of
 the page "Add batch-invariant h_aggregate kernel", sections Correctness and
 Performance):
   rng = numpy.random.default_rng(seed)      (PCG64), draws in this order:
-  residual [T,4,H] = bf16(rng.standard_normal(float32))
-  pre      [T,4]   = rng.random(float32)                 U[0,1), gate-like
+  residual [T,n,H] = bf16(rng.standard_normal(float32))   n = 4 (or 2, 8)
+  pre      [T,n]   = rng.random(float32)                 U[0,1), gate-like
   grad_out [T,H]   = bf16(rng.normal(0, 0.1) as float32)   (if requested)
   outliers         = rng.random((T,4,H)) < 0.01 scales residual by 64 before
                      the bf16 conversion (if requested; exact power of two)
@@ -31,17 +31,18 @@ def to_bf16_bits(x: np.ndarray) -> np.ndarray:
 
 
 def make_inputs(T: int, H: int, seed: int = 0, *, grad: bool = False,
-                outliers: bool = False) -> dict[str, np.ndarray]:
-    """Host inputs: residual (uint16 [T,4,H]), pre (float32 [T,4]) and,
-    if grad, grad_out (uint16 [T,H])."""
+                outliers: bool = False, hc: int = HC) -> dict[str, np.ndarray]:
+    """Host inputs: residual (uint16 [T,hc,H]), pre (float32 [T,hc]) and,
+    if grad, grad_out (uint16 [T,H]). hc is the expansion rate (4 on the
+    page; 2 and 8 for the generalised operation)."""
     rng = np.random.default_rng(seed)
-    res = rng.standard_normal((T, HC, H), dtype=np.float32)
-    pre = rng.random((T, HC), dtype=np.float32)
+    res = rng.standard_normal((T, hc, H), dtype=np.float32)
+    pre = rng.random((T, hc), dtype=np.float32)
     out = {"pre": pre}
     if grad:
         out["grad_out"] = to_bf16_bits(rng.normal(0.0, 0.1, (T, H)).astype(np.float32))
     if outliers:
-        mask = rng.random((T, HC, H)) < 0.01
+        mask = rng.random((T, hc, H)) < 0.01
         res = np.where(mask, res * np.float32(64.0), res).astype(np.float32)
     out["residual"] = to_bf16_bits(res)
     return out

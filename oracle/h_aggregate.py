@@ -24,6 +24,11 @@ Sources (the pages this repository works from):
 Readings taken where the pages are silent (each is listed in the design
 notes of this repository):
 
+* Expansion rates 2 and 8 (the second page's sibling implementation covers
+  HC in {2, 4, 8}; the first page fixes 4): the forward's association is the
+  balanced pairwise tree that reduces to (0+1)+(2+3) at 4; the backward is
+  per stream and needs no change.
+
 * fp32 rounding is round-to-nearest-even; bf16 rounding is
   round-to-nearest-even; denormals are kept (gradual underflow).
 * NaN: the bf16 result of a NaN is a quiet NaN; only "is NaN" is specified.
@@ -104,12 +109,33 @@ def bf16_rne(x: np.ndarray) -> np.ndarray:
 # Batch invariance)
 # ---------------------------------------------------------------------------
 
-def _check_fwd_args(residual: np.ndarray, pre: np.ndarray) -> tuple[int, int]:
-    if residual.dtype != np.uint16 or residual.ndim != 3 or residual.shape[1] != HC:
-        raise ValueError("residual must be uint16 bf16 bits of shape [T, 4, H]")
-    if pre.dtype != np.float32 or pre.shape != (residual.shape[0], HC):
-        raise ValueError("pre must be float32 of shape [T, 4]")
+# Expansion rates this oracle evaluates: the page's 4, and 2 and 8 (the
+# sibling implementation of the second page covers HC in {2, 4, 8}).
+SUPPORTED_HC = (2, 4, 8)
+
+
+def _check_fwd_args(residual: np.ndarray, pre: np.ndarray, n: int | None = HC
+                    ) -> tuple[int, int]:
+    """Shapes [T, n, H] / [T, n]; n=None accepts any supported expansion."""
+    if residual.dtype != np.uint16 or residual.ndim != 3:
+        raise ValueError("residual must be uint16 bf16 bits of shape [T, n, H]")
+    got_n = residual.shape[1]
+    if (n is not None and got_n != n) or got_n not in SUPPORTED_HC:
+        raise ValueError(f"residual has {got_n} streams; expected {n if n else SUPPORTED_HC}")
+    if pre.dtype != np.float32 or pre.shape != (residual.shape[0], got_n):
+        raise ValueError("pre must be float32 of shape [T, n]")
     return residual.shape[0], residual.shape[2]
+
+
+def pairwise_tree(p: list[np.ndarray]) -> np.ndarray:
+    """Balanced pairwise fp32 sum of 2, 4 or 8 arrays: adjacent pairs first,
+    then pairs of pairs. For 4 terms this is the page's (0+1)+(2+3); for 8 it
+    is ((0+1)+(2+3))+((4+5)+(6+7)); for 2 it is 0+1."""
+    level = list(p)
+    while len(level) > 1:
+        with np.errstate(over="ignore", invalid="ignore"):
+            level = [np.add(level[2 * j], level[2 * j + 1]) for j in range(len(level) // 2)]
+    return level[0]
 
 
 def h_aggregate_fwd(residual: np.ndarray, pre: np.ndarray) -> np.ndarray:
@@ -133,20 +159,39 @@ def h_aggregate_fwd(residual: np.ndarray, pre: np.ndarray) -> np.ndarray:
     return bf16_rne(y)
 
 
+def h_aggregate_fwd_n(residual: np.ndarray, pre: np.ndarray) -> np.ndarray:
+    """Forward for any supported expansion n (residual [T,n,H], pre [T,n]):
+    out = bf16( pairwise_tree(pre_i * r_i) ). For n = 4 it is exactly
+    h_aggregate_fwd (the page's formula); n = 2 and 8 generalise its
+    association as a balanced pairwise tree."""
+    T, H = _check_fwd_args(residual, pre, None)
+    n = residual.shape[1]
+    r = widen_bf16(residual)
+    with np.errstate(over="ignore", invalid="ignore"):
+        p = [np.multiply(pre[:, i:i + 1], r[:, i, :]) for i in range(n)]
+    y = pairwise_tree(p)
+    assert y.dtype == np.float32 and y.shape == (T, H)
+    return bf16_rne(y)
+
+
 def h_aggregate_fwd_exact(residual: np.ndarray, pre: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
-    """fp64 value of sum_i pre_i * r_i, and of sum_i |pre_i * r_i|.
+    """fp64 value of sum_i pre_i * r_i, and of sum_i |pre_i * r_i| (any
+    supported n).
 
     Used only to check the fp32 oracle. Every product of an fp32 and a bf16
     number has at most 24 + 8 significant bits and is exact in fp64; the
-    three fp64 additions add a relative error of at most 3 * 2**-53 of
+    n-1 fp64 additions add a relative error of at most (n-1) * 2**-53 of
     sum |pre_i * r_i|, far below a bf16 ulp.
     """
-    _check_fwd_args(residual, pre)
+    _check_fwd_args(residual, pre, None)
     r = widen_bf16(residual).astype(np.float64)
     pw = pre.astype(np.float64)[:, :, None]
     prod = pw * r                                              # exact
-    exact = ((prod[:, 0] + prod[:, 1]) + prod[:, 2]) + prod[:, 3]
-    mag = ((np.abs(prod[:, 0]) + np.abs(prod[:, 1])) + np.abs(prod[:, 2])) + np.abs(prod[:, 3])
+    exact = np.zeros(prod.shape[0:1] + prod.shape[2:], np.float64)
+    mag = np.zeros_like(exact)
+    for i in range(prod.shape[1]):
+        exact = exact + prod[:, i]
+        mag = mag + np.abs(prod[:, i])
     return exact, mag
 
 
@@ -156,7 +201,7 @@ def h_aggregate_fwd_exact(residual: np.ndarray, pre: np.ndarray) -> tuple[np.nda
 # ---------------------------------------------------------------------------
 
 def _check_bwd_args(residual, pre, grad_out) -> tuple[int, int]:
-    T, H = _check_fwd_args(residual, pre)
+    T, H = _check_fwd_args(residual, pre, None)
     if grad_out.dtype != np.uint16 or grad_out.shape != (T, H):
         raise ValueError("grad_out must be uint16 bf16 bits of shape [T, H]")
     return T, H
@@ -165,7 +210,7 @@ def _check_bwd_args(residual, pre, grad_out) -> tuple[int, int]:
 def grad_residual_ref(pre: np.ndarray, grad_out: np.ndarray) -> np.ndarray:
     """grad_residual[t,i,h] = bf16( pre[t,i] * grad_out[t,h] ), one fp32 product.
 
-    pre: float32 [T,4]; grad_out: uint16 [T,H]. Returns uint16 [T,4,H].
+    pre: float32 [T,n]; grad_out: uint16 [T,H]. Returns uint16 [T,n,H].
     The gradient is written, not accumulated into an existing buffer.
     """
     g = widen_bf16(grad_out)                                   # [T,H]
@@ -303,7 +348,7 @@ def grad_pre_exact(residual: np.ndarray, grad_out: np.ndarray) -> tuple[np.ndarr
     Used only to check the oracle: the terms are exact fp32 products, their
     fp64 sum has a relative error below H * 2**-53 of sum |q|.
     """
-    _check_bwd_args(residual, np.zeros((residual.shape[0], HC), np.float32), grad_out)
+    _check_bwd_args(residual, np.zeros(residual.shape[:2], np.float32), grad_out)
     q = grad_pre_products(residual, grad_out).astype(np.float64)
     return q.sum(axis=-1), np.abs(q).sum(axis=-1)
 
@@ -324,28 +369,30 @@ def bf16_ulp(bits: np.ndarray) -> np.ndarray:
     return np.ldexp(1.0, expo - 7)
 
 
-def fwd_error_bound(out_bits: np.ndarray, mag: np.ndarray) -> np.ndarray:
+def fwd_error_bound(out_bits: np.ndarray, mag: np.ndarray, n: int = HC) -> np.ndarray:
     """Largest |out - exact| the forward may show, per element.
 
-    The fp32 evaluation has depth 3 (one product, then two levels of sums),
-    so its error is at most ((1+u)**3 - 1) * sum|pre_i r_i| with u = 2**-24,
-    plus 3 * 2**-150 for results that fall into the subnormal range; one
-    bf16 rounding adds at most half a bf16 ulp of the result. A further
-    4 * 2**-53 * sum|pre_i r_i| covers the fp64 reference's own rounding.
+    The fp32 evaluation has depth d = 1 + log2(n) (one product, then log2(n)
+    levels of sums: 3 for the page's n = 4), so its error is at most
+    ((1+u)**d - 1) * sum|pre_i r_i| with u = 2**-24, plus d * 2**-150 for
+    results in the subnormal range; one bf16 rounding adds at most half a
+    bf16 ulp of the result. A further (n+1) * 2**-53 * sum|pre_i r_i| covers
+    the fp64 reference's own rounding.
     """
     u = 2.0 ** -24
-    gamma3 = (1.0 + u) ** 3 - 1.0
-    return 0.5 * bf16_ulp(out_bits) + (gamma3 + 4 * 2.0 ** -53) * mag + 3 * 2.0 ** -150
+    depth = 1 + int(np.log2(n))
+    gamma = (1.0 + u) ** depth - 1.0
+    return 0.5 * bf16_ulp(out_bits) + (gamma + (n + 1) * 2.0 ** -53) * mag + depth * 2.0 ** -150
 
 
-def classify_fwd(out_bits: np.ndarray, exact: np.ndarray, mag: np.ndarray) -> dict:
+def classify_fwd(out_bits: np.ndarray, exact: np.ndarray, mag: np.ndarray, n: int = HC) -> dict:
     """Count forward outputs within 1 bf16 ulp of the fp64 value, beyond 1 ulp
     but inside fwd_error_bound (cancellation), and outside both (a failure)."""
     out = widen_bf16(out_bits).astype(np.float64)
     err = np.abs(out - exact)
     ulp = bf16_ulp(out_bits)
     within_ulp = err <= ulp
-    within_bound = err <= fwd_error_bound(out_bits, mag)
+    within_bound = err <= fwd_error_bound(out_bits, mag, n)
     return {
         "within_1ulp": int(within_ulp.sum()),
         "cancellation_bound": int((~within_ulp & within_bound).sum()),
@@ -365,9 +412,9 @@ def tree_error_bound(H: int) -> float:
 
 
 __all__ = [
-    "HC", "GROUP", "LANES", "WAVE", "WAVES",
-    "widen_bf16", "bf16_rne",
-    "h_aggregate_fwd", "h_aggregate_fwd_exact",
+    "HC", "SUPPORTED_HC", "GROUP", "LANES", "WAVE", "WAVES",
+    "widen_bf16", "bf16_rne", "pairwise_tree",
+    "h_aggregate_fwd", "h_aggregate_fwd_n", "h_aggregate_fwd_exact",
     "grad_residual_ref", "grad_residual_acc_ref", "grad_pre_products", "canonical_tree_sum",
     "grad_pre_ref", "h_aggregate_bwd", "h_aggregate_bwd_acc", "grad_pre_exact",
     "bf16_ulp", "fwd_error_bound", "classify_fwd", "tree_error_bound",

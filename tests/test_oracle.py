@@ -385,6 +385,105 @@ def test_forward_is_per_token():
 
 
 # ---------------------------------------------------------------------------
+# Other expansion rates (2 and 8): balanced pairwise tree
+# ---------------------------------------------------------------------------
+
+def fwd_one_n(pre_n, r_n) -> int:
+    n = len(pre_n)
+    residual = np.array([bf16_bits(v) for v in r_n], dtype=np.uint16).reshape(1, n, 1)
+    pre = np.array(pre_n, dtype=np.float32).reshape(1, n)
+    return int(O.h_aggregate_fwd_n(residual, pre)[0, 0])
+
+
+def test_fwd_n_at_four_is_the_page_formula():
+    inp = make_inputs(7, 700, seed=30, outliers=True)
+    assert np.array_equal(O.h_aggregate_fwd_n(inp["residual"], inp["pre"]),
+                          O.h_aggregate_fwd(inp["residual"], inp["pre"]))
+
+
+def test_fwd_eight_tree_hand_cases():
+    """With P = 1+2^-8 and E = 2^-24 (P + E ties back to P in fp32; P + 2E =
+    P + 2^-23 is exact and bf16-rounds up to 0x3F81, P alone is a bf16 tie
+    that goes to 0x3F80), terms placed so that only
+    ((0+1)+(2+3))+((4+5)+(6+7)) keeps both E terms:
+    * [P,0,0,0, E,E,0,0]: the right half is 2E before it meets P -> 0x3F81
+      (a sequential sum adds each E to P alone -> 0x3F80);
+    * [0,0,0,0, P,0,E,E]: inside the right half (P+0)+(E+E) -> 0x3F81;
+    * [P,0,E,0, E,0,0,0]: the tree adds one E to P in each half -> 0x3F80."""
+    P, E = 1 + 2.0 ** -8, 2.0 ** -24
+    ones = [1.0] * 8
+    assert fwd_one_n([P, 0, 0, 0, E, E, 0, 0], ones) == 0x3F81
+    assert fwd_one_n([0, 0, 0, 0, P, 0, E, E], ones) == 0x3F81
+    assert fwd_one_n([P, 0, E, 0, E, 0, 0, 0], ones) == 0x3F80
+
+
+def test_fwd_two_is_one_sum():
+    """n = 2: out = bf16(p0 + p1); P + E ties back to P, bf16 ties to even."""
+    P, E = 1 + 2.0 ** -8, 2.0 ** -24
+    assert fwd_one_n([P, E], [1.0, 1.0]) == 0x3F80
+    assert fwd_one_n([P, 2 * E], [1.0, 1.0]) == 0x3F81
+
+
+@pytest.mark.parametrize("n", [2, 8])
+def test_fwd_n_matches_exact_rational_small(n):
+    inp = make_inputs(2, 12, seed=31 + n, hc=n)
+    got = O.h_aggregate_fwd_n(inp["residual"], inp["pre"])
+    r = O.widen_bf16(inp["residual"])
+    for t in range(2):
+        for h in range(12):
+            level = [round_to_f32(Fraction(float(inp["pre"][t, i])) * Fraction(float(r[t, i, h])))
+                     for i in range(n)]
+            while len(level) > 1:
+                level = [round_to_f32(level[2 * j] + level[2 * j + 1]) for j in range(len(level) // 2)]
+            assert int(got[t, h]) == frac_bf16_bits(round_to_bf16(level[0])), (n, t, h)
+
+
+@pytest.mark.parametrize("n", [2, 8])
+def test_fwd_n_one_hot(n):
+    inp = make_inputs(3, 257, seed=40 + n, hc=n)
+    for i in range(n):
+        pre = np.zeros((3, n), np.float32)
+        pre[:, i] = 1.0
+        out = O.h_aggregate_fwd_n(inp["residual"], pre)
+        assert np.array_equal(O.widen_bf16(out), O.widen_bf16(inp["residual"][:, i, :]))
+
+
+def test_fwd_eight_symmetries():
+    """Swaps inside a pair, of the pairs inside a half, and of the halves
+    leave the bytes unchanged; the transposition 1<->2 is not a symmetry."""
+    inp = make_inputs(6, 640, seed=44, hc=8, outliers=True)
+    res, pre = inp["residual"], inp["pre"]
+    base = O.h_aggregate_fwd_n(res, pre)
+    for perm in ([1, 0, 2, 3, 4, 5, 6, 7], [2, 3, 0, 1, 4, 5, 6, 7], [4, 5, 6, 7, 0, 1, 2, 3],
+                 [0, 1, 2, 3, 5, 4, 7, 6]):
+        assert np.array_equal(O.h_aggregate_fwd_n(res[:, perm, :].copy(), pre[:, perm].copy()), base)
+    P, E = 1 + 2.0 ** -8, 2.0 ** -24
+    a = [P, 0, E, E, 0, 0, 0, 0]
+    b = [a[0], a[2], a[1], a[3]] + a[4:]
+    assert fwd_one_n(a, [1.0] * 8) != fwd_one_n(b, [1.0] * 8)
+
+
+@pytest.mark.parametrize("n", [2, 8])
+def test_fwd_n_fp64_gate(n):
+    inp = make_inputs(32, 4096, seed=50 + n, hc=n, outliers=True)
+    out = O.h_aggregate_fwd_n(inp["residual"], inp["pre"])
+    exact, mag = O.h_aggregate_fwd_exact(inp["residual"], inp["pre"])
+    c = O.classify_fwd(out, exact, mag, n)
+    assert c["fail"] == 0 and c["within_1ulp"] >= 0.999 * out.size, c
+
+
+def test_backward_n_is_per_stream():
+    """The backward of the n-stream operation is the 4-stream one stream by
+    stream: the first 4 streams of an 8-stream input give the same bytes as
+    a 4-stream call on them."""
+    inp = make_inputs(4, 1000, seed=60, hc=8, grad=True)
+    gr8, gp8 = O.h_aggregate_bwd(inp["residual"], inp["pre"], inp["grad_out"])
+    gr4, gp4 = O.h_aggregate_bwd(inp["residual"][:, 4:].copy(), inp["pre"][:, 4:].copy(),
+                                 inp["grad_out"])
+    assert np.array_equal(gr8[:, 4:], gr4) and np.array_equal(gp8[:, 4:], gp4)
+
+
+# ---------------------------------------------------------------------------
 # Backward: grad_residual
 # ---------------------------------------------------------------------------
 
