@@ -12,7 +12,8 @@ from __future__ import annotations
 _OPS_NAMES = (
     "mhc_h_aggregate_fwd", "mhc_h_aggregate_bwd", "mhc_bf16_rne_probe",
     "mhc_h_aggregate_fwd_timed", "mhc_h_aggregate_bwd_timed", "mhc_h_aggregate_bwd_acc",
-    "mhc_h_aggregate_plan_bwd_acc",
+    "mhc_h_aggregate_plan_bwd_acc", "mhc_h_aggregate_fwd_n", "mhc_h_aggregate_bwd_n",
+    "mhc_h_aggregate_plan_fwd_n", "mhc_h_aggregate_plan_bwd_n",
     "mhc_h_aggregate_plan_fwd", "mhc_h_aggregate_plan_bwd",
     "mhc_h_aggregate_validate_fwd", "mhc_h_aggregate_validate_bwd",
     "h_aggregate", "h_aggregate_backward", "HAggregate", "h_aggregate_autograd",

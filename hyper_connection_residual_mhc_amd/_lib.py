@@ -56,6 +56,18 @@ SIGNATURES = {
     "mhc_h_aggregate_plan_bwd_acc": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                              c_int64, c_int64, POINTER(mhc_launch),
                                              POINTER(mhc_launch), POINTER(c_int64)]),
+    "mhc_h_aggregate_fwd_n": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_int64,
+                                      c_void_p, POINTER(mhc_launch), c_void_p, c_void_p]),
+    "mhc_h_aggregate_bwd_n": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                      c_int64, c_int32, c_int64, c_int32, c_void_p,
+                                      POINTER(mhc_launch), c_void_p, c_void_p]),
+    "mhc_h_aggregate_plan_fwd_n": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int32,
+                                           c_int64, POINTER(mhc_launch), POINTER(mhc_launch),
+                                           POINTER(c_int64)]),
+    "mhc_h_aggregate_plan_bwd_n": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                           c_int64, c_int32, c_int64, c_int32,
+                                           POINTER(mhc_launch), POINTER(mhc_launch),
+                                           POINTER(c_int64)]),
     "mhc_h_aggregate_validate_fwd": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64]),
     "mhc_h_aggregate_validate_bwd": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                              c_int64, c_int64]),

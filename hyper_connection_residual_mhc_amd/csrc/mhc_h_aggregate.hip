@@ -180,7 +180,11 @@ template <> __device__ __forceinline__ void store_vec<1>(Rsrc rs, uint32_t off, 
 // c*blockDim.x*UPT + k*blockDim.x + x for k < UPT, so every load and store
 // instruction of a wave covers 64 consecutive units. All loads of a lane are
 // issued before any arithmetic.
-template <int V, int UPT>
+//
+// N is the expansion rate (residual streams): 4 on the page, 2 and 8 for the
+// generalised operation. The N products are summed as a balanced pairwise
+// tree: adjacent pairs first, then pairs of pairs - (0+1)+(2+3) for N = 4.
+template <int V, int UPT, int N>
 __global__ __launch_bounds__(1024) void hagg_fwd_kernel(
     const uint16_t* __restrict__ residual, const float* __restrict__ pre,
     uint16_t* __restrict__ out, int64_t H, uint32_t units_per_token) {
@@ -188,25 +192,25 @@ __global__ __launch_bounds__(1024) void hagg_fwd_kernel(
   const uint32_t c = blockIdx.x;
   const uint32_t t = blockIdx.y;
 
-  const float* p = pre + 4 * static_cast<int64_t>(t);
-  const float w0 = p[0], w1 = p[1], w2 = p[2], w3 = p[3];
-  // The token's four residual rows (8H bytes) and its output row (2H bytes).
-  const Rsrc res = make_rsrc(residual + static_cast<int64_t>(t) * 4 * H, 8 * H);
+  const float* p = pre + N * static_cast<int64_t>(t);
+  float w[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) w[i] = p[i];
+  // The token's N residual rows (2NH bytes) and its output row (2H bytes).
+  const Rsrc res = make_rsrc(residual + static_cast<int64_t>(t) * N * H, 2 * N * H);
   const Rsrc o = make_rsrc(out + static_cast<int64_t>(t) * H, 2 * H);
   const uint32_t row = 2 * static_cast<uint32_t>(H);  // bytes between residual streams
 
   const uint32_t first = c * blockDim.x * UPT + threadIdx.x;
 
-  VT x0[UPT], x1[UPT], x2[UPT], x3[UPT];
+  VT x[N][UPT];
 #pragma unroll
   for (int k = 0; k < UPT; ++k) {
     const uint32_t u = first + k * blockDim.x;
     if (u < units_per_token) {
       const uint32_t h = u * V;
-      x0[k] = load_vec<V>(res, h, 0);
-      x1[k] = load_vec<V>(res, h, row);
-      x2[k] = load_vec<V>(res, h, 2 * row);
-      x3[k] = load_vec<V>(res, h, 3 * row);
+#pragma unroll
+      for (int i = 0; i < N; ++i) x[i][k] = load_vec<V>(res, h, i * row);
     }
   }
 #pragma unroll
@@ -216,14 +220,17 @@ __global__ __launch_bounds__(1024) void hagg_fwd_kernel(
       float y[V];
 #pragma unroll
       for (int e = 0; e < V; ++e) {
-        // Separate fp32 round-to-nearest products and sums, tree (0+1)+(2+3).
-        const float p0 = w0 * elem<V>(x0[k], e);
-        const float p1 = w1 * elem<V>(x1[k], e);
-        const float p2 = w2 * elem<V>(x2[k], e);
-        const float p3 = w3 * elem<V>(x3[k], e);
-        const float s01 = p0 + p1;
-        const float s23 = p2 + p3;
-        y[e] = s01 + s23;
+        // Separate fp32 round-to-nearest products, then the pairwise tree
+        // of separate round-to-nearest sums.
+        float lv[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) lv[i] = w[i] * elem<V>(x[i][k], e);
+#pragma unroll
+        for (int width = N; width > 1; width /= 2) {
+#pragma unroll
+          for (int j = 0; j < width / 2; ++j) lv[j] = lv[2 * j] + lv[2 * j + 1];
+        }
+        y[e] = lv[0];
       }
       store_vec<V>(o, u * V, pack<V>(y));
     }
@@ -257,13 +264,14 @@ __device__ __forceinline__ float from_lane_plus(float x) {
   }
 }
 
-// Grid: (ceil(T / tokens_per_block), 4 / S) blocks of exactly 256 threads.
-// Block (b, j) handles streams S*j .. S*j + S-1 of tokens
-// b*tokens_per_block .. (b+1)*tokens_per_block - 1, one token after the
-// other. The fixed order is defined per (token, stream), so splitting a
-// token's streams over blocks changes no bit and needs no communication
-// between blocks: S = 4 keeps a token in one block (grad_out read once), S = 1
-// gives four times as many blocks for short batches.
+// Grid: (ceil(T / tokens_per_block), n / S) blocks of exactly 256 threads,
+// n the expansion rate (2, 4 or 8 residual streams per token). Block (b, j)
+// handles streams S*j .. S*j + S-1 of tokens b*tokens_per_block ..
+// (b+1)*tokens_per_block - 1, one token after the other. The fixed order is
+// defined per (token, stream), so splitting a token's streams over blocks
+// changes no bit and needs no communication between blocks: S = 4 keeps a
+// 4-stream token in one block (grad_out read once), S = 1 gives four times
+// as many blocks for short batches.
 //
 // Lane l (= threadIdx.x) is accumulator lane l of the fixed order: it visits
 // groups k = l, l + 256, l + 512, ... (group k = hidden elements 8k .. 8k+7),
@@ -281,7 +289,7 @@ template <int V, int U, int S, bool ACC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void hagg_bwd_kernel(
     const uint16_t* __restrict__ residual, const float* __restrict__ pre,
     const uint16_t* __restrict__ grad_out, uint16_t* __restrict__ grad_residual,
-    float* __restrict__ grad_pre, int64_t T, int64_t H, uint32_t ngroups,
+    float* __restrict__ grad_pre, int64_t T, int32_t n, int64_t H, uint32_t ngroups,
     int32_t tokens_per_block) {
   typedef typename Vec<V>::type VT;
   constexpr int NV = kGroup / V;  // accesses per full group
@@ -295,15 +303,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void h
     const int64_t t = static_cast<int64_t>(blockIdx.x) * tokens_per_block + tt;
     if (t >= T) break;  // uniform across the block
 
-    const float* p = pre + 4 * t + i0;
+    const float* p = pre + n * t + i0;
     float w[S];
 #pragma unroll
     for (int i = 0; i < S; ++i) w[i] = p[i];
     // The token's grad_out row (2H bytes) and the block's S residual /
     // grad_residual rows (2SH bytes each).
     const Rsrc g_row = make_rsrc(grad_out + t * H, 2 * H);
-    const Rsrc r_row = make_rsrc(residual + (t * 4 + i0) * H, 2 * S * H);
-    const Rsrc gr_row = make_rsrc(grad_residual + (t * 4 + i0) * H, 2 * S * H);
+    const Rsrc r_row = make_rsrc(residual + (t * n + i0) * H, 2 * S * H);
+    const Rsrc gr_row = make_rsrc(grad_residual + (t * n + i0) * H, 2 * S * H);
     const uint32_t hs = static_cast<uint32_t>(H);  // elements between streams
     const uint32_t row = 2 * hs;                   // bytes between streams
 
@@ -381,7 +389,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void h
     if (lane < S) {
       const float y02 = wave_sum[0][lane] + wave_sum[2][lane];
       const float y13 = wave_sum[1][lane] + wave_sum[3][lane];
-      grad_pre[4 * t + i0 + lane] = y02 + y13;
+      grad_pre[n * t + i0 + lane] = y02 + y13;
     }
     __syncthreads();  // wave_sum is reused by the next token
   }
@@ -426,22 +434,24 @@ struct Range {
 
 bool overlap(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
 
-// Byte sizes of every tensor, or an error if T, H or the sizes are invalid.
+// Byte sizes of every tensor, or an error if T, n, H or the sizes are invalid.
 struct Sizes {
-  int64_t res_bytes, pre_bytes, row_bytes;  // row = [T,H] bf16
+  int64_t res_bytes, pre_bytes, row_bytes;  // [T,n,H] bf16, [T,n] fp32, [T,H] bf16
 };
 
-mhc_status check_sizes(int64_t T, int64_t H, Sizes* s) {
+mhc_status check_sizes(int64_t T, int32_t n, int64_t H, Sizes* s) {
+  if (n != 2 && n != 4 && n != 8)
+    return fail(MHC_ERROR_INVALID_VALUE, "the expansion rate n must be 2, 4 or 8 (got %d)", n);
   if (T < 0) return fail(MHC_ERROR_INVALID_VALUE, "T must be >= 0 (got %lld)", (long long)T);
   if (H < 1 || H > MHC_MAX_H)
     return fail(MHC_ERROR_INVALID_VALUE, "H must be in [1, %lld] (got %lld)",
                 (long long)MHC_MAX_H, (long long)H);
-  // 8*T*H must fit int64 (residual bytes).
-  if (T > INT64_MAX / 8 / H)
+  // 2*n*T*H must fit int64 (residual bytes).
+  if (T > INT64_MAX / (2 * n) / H)
     return fail(MHC_ERROR_INVALID_VALUE, "T*H too large: byte counts overflow int64");
-  s->res_bytes = 8 * T * H;
+  s->res_bytes = 2 * n * T * H;
   s->row_bytes = 2 * T * H;
-  s->pre_bytes = 16 * T;
+  s->pre_bytes = 4 * n * T;
   return ok();
 }
 
@@ -498,14 +508,22 @@ constexpr int64_t kMaxGridY = 65535;
 constexpr int64_t kTwoStreamsFromT = 128;
 constexpr int64_t kFourStreamsFromT = 512;
 
+// Largest forward batch UPT in {1, 2, 4} whose loaded data (N rows, each
+// access max(V/2, 1) registers) fits 64 VGPRs, within the 128-VGPR budget of
+// a 1024-thread block.
+constexpr int fwd_max_upt(int V, int N) {
+  const int per_unit = N * (V >= 2 ? V / 2 : 1);
+  return 4 * per_unit <= 64 ? 4 : (2 * per_unit <= 64 ? 2 : 1);
+}
+
 struct FwdPlan {
-  int V, block, upt;
+  int V, block, upt, n;
   uint32_t units_per_token, blocks_per_token;
   int64_t tokens_per_launch, total_blocks;
 };
 
-mhc_status plan_fwd(const uint16_t* residual, const uint16_t* out, int64_t T, int64_t H,
-                    const mhc_launch* ov, FwdPlan* pl) {
+mhc_status plan_fwd(const uint16_t* residual, const uint16_t* out, int64_t T, int32_t n,
+                    int64_t H, const mhc_launch* ov, FwdPlan* pl) {
   const void* bufs[2] = {residual, out};
   int V = widest_vec(H, bufs, 2);
   if (ov && ov->vec_width != 0) {
@@ -519,11 +537,16 @@ mhc_status plan_fwd(const uint16_t* residual, const uint16_t* out, int64_t T, in
     return fail(MHC_ERROR_INVALID_VALUE,
                 "tokens_per_block and streams_per_block are backward-only fields");
   const int64_t upt_units = H / V;  // units per token
+  const int max_upt = fwd_max_upt(V, n);
   int upt = 1;
   if (ov && ov->units_per_thread != 0) {
     if (ov->units_per_thread != 1 && ov->units_per_thread != 2 && ov->units_per_thread != 4)
       return fail(MHC_ERROR_INVALID_VALUE, "units_per_thread must be 1, 2 or 4");
     upt = ov->units_per_thread;
+    if (upt > max_upt)
+      return fail(MHC_ERROR_INVALID_VALUE,
+                  "units_per_thread %d exceeds the register budget (at most %d for vec_width "
+                  "%d, n=%d)", upt, max_upt, V, n);
   }
   // One wave per block: on gfx950 the 64-thread shape measured fastest at
   // every bandwidth shape swept (T = 1024 and 8192, H = 7168), since the
@@ -541,6 +564,7 @@ mhc_status plan_fwd(const uint16_t* residual, const uint16_t* out, int64_t T, in
   pl->V = V;
   pl->block = block;
   pl->upt = upt;
+  pl->n = n;
   pl->units_per_token = static_cast<uint32_t>(upt_units);
   pl->blocks_per_token = static_cast<uint32_t>(bpt);
   // Tokens run along the grid's y dimension, at most 65535 per launch, and a
@@ -563,13 +587,13 @@ constexpr int bwd_max_u(int V, int S, bool acc) {
 }
 
 struct BwdPlan {
-  int V, U, S, tpb;
+  int V, U, S, tpb, n;
   bool acc;
   int64_t ngroups, blocks_per_launch, total_blocks;
 };
 
 mhc_status plan_bwd(const uint16_t* residual, const uint16_t* grad_out,
-                    const uint16_t* grad_residual, int64_t T, int64_t H, bool acc,
+                    const uint16_t* grad_residual, int64_t T, int32_t n, int64_t H, bool acc,
                     const mhc_launch* ov, BwdPlan* pl) {
   const void* bufs[3] = {residual, grad_out, grad_residual};
   int V = widest_vec(H, bufs, 3);
@@ -582,14 +606,19 @@ mhc_status plan_bwd(const uint16_t* residual, const uint16_t* grad_out,
   }
   if (ov && ov->block_threads != 0 && ov->block_threads != kLanes)
     return fail(MHC_ERROR_INVALID_VALUE, "backward block_threads must be 0 or 256");
-  // Streams per block: a token's four streams in one block once there are
-  // enough tokens to cover the CUs (grad_out is then read once per token);
-  // shorter batches spread each token over 2 or 4 blocks to use more CUs.
-  // Thresholds measured at H = 4096 and 7168 (T from 1 to 2048).
+  // Streams per block: all of a token's streams (up to four) in one block
+  // once there are enough tokens to cover the CUs (grad_out is then read once
+  // per block); shorter batches spread each token over more blocks to use
+  // more CUs. Thresholds measured at n = 4, H = 4096 and 7168 (T from 1 to
+  // 2048).
   int S = T >= kFourStreamsFromT ? 4 : (T >= kTwoStreamsFromT ? 2 : 1);
+  if (S > n) S = n;
   if (ov && ov->streams_per_block != 0) {
     if (ov->streams_per_block != 1 && ov->streams_per_block != 2 && ov->streams_per_block != 4)
       return fail(MHC_ERROR_INVALID_VALUE, "streams_per_block must be 1, 2 or 4");
+    if (ov->streams_per_block > n)
+      return fail(MHC_ERROR_INVALID_VALUE, "streams_per_block %d exceeds the %d streams",
+                  ov->streams_per_block, n);
     S = ov->streams_per_block;
   }
   // Groups each lane loads before its arithmetic: as many as the register
@@ -618,17 +647,18 @@ mhc_status plan_bwd(const uint16_t* residual, const uint16_t* grad_out,
   pl->U = U;
   pl->S = S;
   pl->tpb = tpb;
+  pl->n = n;
   pl->acc = acc;
   pl->ngroups = (H + kGroup - 1) / kGroup;
-  pl->blocks_per_launch = kMaxLaunchThreads / kLanes;
-  pl->total_blocks = (T + tpb - 1) / tpb * (4 / S);
+  pl->blocks_per_launch = kMaxLaunchThreads / kLanes / (n / S);
+  pl->total_blocks = (T + tpb - 1) / tpb * (n / S);
   return ok();
 }
 
 mhc_status validate_fwd(const uint16_t* residual, const float* pre, const uint16_t* out,
-                        int64_t T, int64_t H) {
+                        int64_t T, int32_t n, int64_t H) {
   Sizes s;
-  mhc_status st = check_sizes(T, H, &s);
+  mhc_status st = check_sizes(T, n, H, &s);
   if (st != MHC_SUCCESS || T == 0) return st;
   if ((st = check_ptr(residual, 2, "residual")) != MHC_SUCCESS) return st;
   if ((st = check_ptr(pre, 4, "pre")) != MHC_SUCCESS) return st;
@@ -640,9 +670,9 @@ mhc_status validate_fwd(const uint16_t* residual, const float* pre, const uint16
 
 mhc_status validate_bwd(const uint16_t* residual, const float* pre, const uint16_t* grad_out,
                         const uint16_t* grad_residual, const float* grad_pre, int64_t T,
-                        int64_t H) {
+                        int32_t n, int64_t H) {
   Sizes s;
-  mhc_status st = check_sizes(T, H, &s);
+  mhc_status st = check_sizes(T, n, H, &s);
   if (st != MHC_SUCCESS || T == 0) return st;
   if ((st = check_ptr(residual, 2, "residual")) != MHC_SUCCESS) return st;
   if ((st = check_ptr(pre, 4, "pre")) != MHC_SUCCESS) return st;
@@ -672,22 +702,36 @@ struct Events {
   hipEvent_t start, stop;
 };
 
-template <int V, int UPT>
+template <int V, int UPT, int N>
 void launch_fwd_t(const FwdPlan& pl, const uint16_t* residual, const float* pre, uint16_t* out,
                   int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
-  hipExtLaunchKernelGGL(hagg_fwd_kernel<V, UPT>,
+  hipExtLaunchKernelGGL(hagg_fwd_kernel<V, UPT, N>,
                         dim3(pl.blocks_per_token, static_cast<uint32_t>(tokens)),
                         dim3(pl.block), 0, stream, ev.start, ev.stop, 0, residual, pre, out, H,
                         pl.units_per_token);
 }
 
+// Instantiates only the batches the register budget allows (the plan never
+// asks for more).
+template <int V, int N>
+void launch_fwd_n(const FwdPlan& pl, const uint16_t* residual, const float* pre, uint16_t* out,
+                  int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
+  constexpr int kMax = fwd_max_upt(V, N);
+  constexpr int kU2 = kMax < 2 ? kMax : 2;
+  switch (pl.upt) {
+    case 1: launch_fwd_t<V, 1, N>(pl, residual, pre, out, tokens, H, stream, ev); break;
+    case 2: launch_fwd_t<V, kU2, N>(pl, residual, pre, out, tokens, H, stream, ev); break;
+    default: launch_fwd_t<V, kMax, N>(pl, residual, pre, out, tokens, H, stream, ev); break;
+  }
+}
+
 template <int V>
 void launch_fwd_v(const FwdPlan& pl, const uint16_t* residual, const float* pre, uint16_t* out,
                   int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
-  switch (pl.upt) {
-    case 1: launch_fwd_t<V, 1>(pl, residual, pre, out, tokens, H, stream, ev); break;
-    case 2: launch_fwd_t<V, 2>(pl, residual, pre, out, tokens, H, stream, ev); break;
-    default: launch_fwd_t<V, 4>(pl, residual, pre, out, tokens, H, stream, ev); break;
+  switch (pl.n) {
+    case 2: launch_fwd_n<V, 2>(pl, residual, pre, out, tokens, H, stream, ev); break;
+    case 8: launch_fwd_n<V, 8>(pl, residual, pre, out, tokens, H, stream, ev); break;
+    default: launch_fwd_n<V, 4>(pl, residual, pre, out, tokens, H, stream, ev); break;
   }
 }
 
@@ -696,10 +740,10 @@ void launch_bwd_t(const BwdPlan& pl, const uint16_t* residual, const float* pre,
                   const uint16_t* grad_out, uint16_t* grad_residual, float* grad_pre,
                   int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
   const uint32_t blocks = static_cast<uint32_t>((tokens + pl.tpb - 1) / pl.tpb);
-  hipExtLaunchKernelGGL(hagg_bwd_kernel<V, U, S, ACC>, dim3(blocks, 4 / S), dim3(kLanes), 0,
+  hipExtLaunchKernelGGL(hagg_bwd_kernel<V, U, S, ACC>, dim3(blocks, pl.n / S), dim3(kLanes), 0,
                         stream, ev.start, ev.stop, 0, residual, pre, grad_out, grad_residual,
-                        grad_pre, tokens, H, static_cast<uint32_t>(pl.ngroups),
-                        static_cast<int32_t>(pl.tpb));
+                        grad_pre, tokens, static_cast<int32_t>(pl.n), H,
+                        static_cast<uint32_t>(pl.ngroups), static_cast<int32_t>(pl.tpb));
 }
 
 // Instantiates only the batches the register budget allows (the plan never
@@ -755,25 +799,25 @@ mhc_status record_empty(const Events& ev, hipStream_t s) {
 }
 
 mhc_status run_fwd(const uint16_t* residual, const float* pre, uint16_t* out, int64_t T,
-                   int64_t H, void* stream, const mhc_launch* launch, Events ev) {
-  mhc_status st = validate_fwd(residual, pre, out, T, H);
+                   int32_t n, int64_t H, void* stream, const mhc_launch* launch, Events ev) {
+  mhc_status st = validate_fwd(residual, pre, out, T, n, H);
   if (st != MHC_SUCCESS) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (T == 0) return record_empty(ev, s);
   FwdPlan pl;
-  if ((st = plan_fwd(residual, out, T, H, launch, &pl)) != MHC_SUCCESS) return st;
+  if ((st = plan_fwd(residual, out, T, n, H, launch, &pl)) != MHC_SUCCESS) return st;
   (void)hipGetLastError();  // start from a clean per-thread error state
   for (int64_t t0 = 0; t0 < T; t0 += pl.tokens_per_launch) {
-    const int64_t n = (T - t0 < pl.tokens_per_launch) ? T - t0 : pl.tokens_per_launch;
-    const Events e = chunk_events(ev, t0, t0 + n, T);
-    const uint16_t* r = residual + t0 * 4 * H;
-    const float* p = pre + 4 * t0;
+    const int64_t m = (T - t0 < pl.tokens_per_launch) ? T - t0 : pl.tokens_per_launch;
+    const Events e = chunk_events(ev, t0, t0 + m, T);
+    const uint16_t* r = residual + t0 * n * H;
+    const float* p = pre + n * t0;
     uint16_t* o = out + t0 * H;
     switch (pl.V) {
-      case 8: launch_fwd_v<8>(pl, r, p, o, n, H, s, e); break;
-      case 4: launch_fwd_v<4>(pl, r, p, o, n, H, s, e); break;
-      case 2: launch_fwd_v<2>(pl, r, p, o, n, H, s, e); break;
-      default: launch_fwd_v<1>(pl, r, p, o, n, H, s, e); break;
+      case 8: launch_fwd_v<8>(pl, r, p, o, m, H, s, e); break;
+      case 4: launch_fwd_v<4>(pl, r, p, o, m, H, s, e); break;
+      case 2: launch_fwd_v<2>(pl, r, p, o, m, H, s, e); break;
+      default: launch_fwd_v<1>(pl, r, p, o, m, H, s, e); break;
     }
     if ((st = launch_error("h_aggregate forward")) != MHC_SUCCESS) return st;
   }
@@ -781,34 +825,65 @@ mhc_status run_fwd(const uint16_t* residual, const float* pre, uint16_t* out, in
 }
 
 mhc_status run_bwd(const uint16_t* residual, const float* pre, const uint16_t* grad_out,
-                   uint16_t* grad_residual, float* grad_pre, int64_t T, int64_t H, void* stream,
-                   const mhc_launch* launch, Events ev, bool acc) {
-  mhc_status st = validate_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, H);
+                   uint16_t* grad_residual, float* grad_pre, int64_t T, int32_t n, int64_t H,
+                   bool acc, void* stream, const mhc_launch* launch, Events ev) {
+  mhc_status st = validate_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, n, H);
   if (st != MHC_SUCCESS) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (T == 0) return record_empty(ev, s);
   BwdPlan pl;
-  if ((st = plan_bwd(residual, grad_out, grad_residual, T, H, acc, launch, &pl)) != MHC_SUCCESS)
+  if ((st = plan_bwd(residual, grad_out, grad_residual, T, n, H, acc, launch, &pl)) != MHC_SUCCESS)
     return st;
   const int64_t tokens_per_launch = pl.blocks_per_launch * pl.tpb;
   (void)hipGetLastError();
   for (int64_t t0 = 0; t0 < T; t0 += tokens_per_launch) {
-    const int64_t n = (T - t0 < tokens_per_launch) ? T - t0 : tokens_per_launch;
-    const Events e = chunk_events(ev, t0, t0 + n, T);
-    const uint16_t* r = residual + t0 * 4 * H;
-    const float* p = pre + 4 * t0;
+    const int64_t m = (T - t0 < tokens_per_launch) ? T - t0 : tokens_per_launch;
+    const Events e = chunk_events(ev, t0, t0 + m, T);
+    const uint16_t* r = residual + t0 * n * H;
+    const float* p = pre + n * t0;
     const uint16_t* g = grad_out + t0 * H;
-    uint16_t* gr = grad_residual + t0 * 4 * H;
-    float* gp = grad_pre + 4 * t0;
+    uint16_t* gr = grad_residual + t0 * n * H;
+    float* gp = grad_pre + n * t0;
     switch (pl.V) {
-      case 8: launch_bwd_v<8>(pl, r, p, g, gr, gp, n, H, s, e); break;
-      case 4: launch_bwd_v<4>(pl, r, p, g, gr, gp, n, H, s, e); break;
-      case 2: launch_bwd_v<2>(pl, r, p, g, gr, gp, n, H, s, e); break;
-      default: launch_bwd_v<1>(pl, r, p, g, gr, gp, n, H, s, e); break;
+      case 8: launch_bwd_v<8>(pl, r, p, g, gr, gp, m, H, s, e); break;
+      case 4: launch_bwd_v<4>(pl, r, p, g, gr, gp, m, H, s, e); break;
+      case 2: launch_bwd_v<2>(pl, r, p, g, gr, gp, m, H, s, e); break;
+      default: launch_bwd_v<1>(pl, r, p, g, gr, gp, m, H, s, e); break;
     }
     if ((st = launch_error("h_aggregate backward")) != MHC_SUCCESS) return st;
   }
   return ok();
+}
+
+mhc_status plan_fwd_query(const uint16_t* residual, const float* pre, const uint16_t* out,
+                          int64_t T, int32_t n, int64_t H, const mhc_launch* launch,
+                          mhc_launch* plan, int64_t* grid_blocks) {
+  mhc_status st = validate_fwd(residual, pre, out, T, n, H);
+  if (st != MHC_SUCCESS) return st;
+  FwdPlan pl;
+  if ((st = plan_fwd(residual, out, T, n, H, launch, &pl)) != MHC_SUCCESS) return st;
+  if (plan) *plan = mhc_launch{pl.block, pl.V, pl.upt, 0, 0};
+  if (grid_blocks) *grid_blocks = pl.total_blocks;
+  return ok();
+}
+
+mhc_status plan_bwd_query(const uint16_t* residual, const float* pre, const uint16_t* grad_out,
+                          const uint16_t* grad_residual, const float* grad_pre, int64_t T,
+                          int32_t n, int64_t H, bool acc, const mhc_launch* launch,
+                          mhc_launch* plan, int64_t* grid_blocks) {
+  mhc_status st = validate_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, n, H);
+  if (st != MHC_SUCCESS) return st;
+  BwdPlan pl;
+  if ((st = plan_bwd(residual, grad_out, grad_residual, T, n, H, acc, launch, &pl)) !=
+      MHC_SUCCESS)
+    return st;
+  if (plan) *plan = mhc_launch{kLanes, pl.V, pl.U, pl.tpb, pl.S};
+  if (grid_blocks) *grid_blocks = pl.total_blocks;
+  return ok();
+}
+
+Events events(void* start_event, void* stop_event) {
+  return Events{static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
 }
 
 }  // namespace
@@ -833,29 +908,25 @@ const char* mhc_status_string(mhc_status status) {
 
 const char* mhc_last_error_message(void) { return g_msg; }
 
+// ---- expansion rate 4 (the page's operation) ------------------------------
+
 mhc_status mhc_h_aggregate_validate_fwd(const uint16_t* residual, const float* pre,
                                         const uint16_t* out, int64_t T, int64_t H) {
-  return validate_fwd(residual, pre, out, T, H);
+  return validate_fwd(residual, pre, out, T, MHC_HC, H);
 }
 
 mhc_status mhc_h_aggregate_validate_bwd(const uint16_t* residual, const float* pre,
                                         const uint16_t* grad_out,
                                         const uint16_t* grad_residual, const float* grad_pre,
                                         int64_t T, int64_t H) {
-  return validate_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, H);
+  return validate_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, MHC_HC, H);
 }
 
 mhc_status mhc_h_aggregate_plan_fwd(const uint16_t* residual, const float* pre,
                                     const uint16_t* out, int64_t T, int64_t H,
                                     const mhc_launch* launch, mhc_launch* plan,
                                     int64_t* grid_blocks) {
-  mhc_status st = validate_fwd(residual, pre, out, T, H);
-  if (st != MHC_SUCCESS) return st;
-  FwdPlan pl;
-  if ((st = plan_fwd(residual, out, T, H, launch, &pl)) != MHC_SUCCESS) return st;
-  if (plan) *plan = mhc_launch{pl.block, pl.V, pl.upt, 0, 0};
-  if (grid_blocks) *grid_blocks = pl.total_blocks;
-  return ok();
+  return plan_fwd_query(residual, pre, out, T, MHC_HC, H, launch, plan, grid_blocks);
 }
 
 mhc_status mhc_h_aggregate_plan_bwd(const uint16_t* residual, const float* pre,
@@ -863,68 +934,8 @@ mhc_status mhc_h_aggregate_plan_bwd(const uint16_t* residual, const float* pre,
                                     const float* grad_pre, int64_t T, int64_t H,
                                     const mhc_launch* launch, mhc_launch* plan,
                                     int64_t* grid_blocks) {
-  mhc_status st = validate_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, H);
-  if (st != MHC_SUCCESS) return st;
-  BwdPlan pl;
-  if ((st = plan_bwd(residual, grad_out, grad_residual, T, H, false, launch, &pl)) != MHC_SUCCESS)
-    return st;
-  if (plan) *plan = mhc_launch{kLanes, pl.V, pl.U, pl.tpb, pl.S};
-  if (grid_blocks) *grid_blocks = pl.total_blocks;
-  return ok();
-}
-
-mhc_status mhc_h_aggregate_fwd_ex(const uint16_t* residual, const float* pre, uint16_t* out,
-                                  int64_t T, int64_t H, void* stream,
-                                  const mhc_launch* launch) {
-  return run_fwd(residual, pre, out, T, H, stream, launch, Events{nullptr, nullptr});
-}
-
-mhc_status mhc_h_aggregate_fwd(const uint16_t* residual, const float* pre, uint16_t* out,
-                               int64_t T, int64_t H, void* stream) {
-  return run_fwd(residual, pre, out, T, H, stream, nullptr, Events{nullptr, nullptr});
-}
-
-mhc_status mhc_h_aggregate_fwd_timed(const uint16_t* residual, const float* pre, uint16_t* out,
-                                     int64_t T, int64_t H, void* stream,
-                                     const mhc_launch* launch, void* start_event,
-                                     void* stop_event) {
-  return run_fwd(residual, pre, out, T, H, stream, launch,
-                 Events{static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)});
-}
-
-mhc_status mhc_h_aggregate_bwd_ex(const uint16_t* residual, const float* pre,
-                                  const uint16_t* grad_out, uint16_t* grad_residual,
-                                  float* grad_pre, int64_t T, int64_t H, void* stream,
-                                  const mhc_launch* launch) {
-  return run_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, H, stream, launch,
-                 Events{nullptr, nullptr}, false);
-}
-
-mhc_status mhc_h_aggregate_bwd(const uint16_t* residual, const float* pre,
-                               const uint16_t* grad_out, uint16_t* grad_residual,
-                               float* grad_pre, int64_t T, int64_t H, void* stream) {
-  return run_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, H, stream, nullptr,
-                 Events{nullptr, nullptr}, false);
-}
-
-mhc_status mhc_h_aggregate_bwd_timed(const uint16_t* residual, const float* pre,
-                                     const uint16_t* grad_out, uint16_t* grad_residual,
-                                     float* grad_pre, int64_t T, int64_t H, void* stream,
-                                     const mhc_launch* launch, void* start_event,
-                                     void* stop_event) {
-  return run_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, H, stream, launch,
-                 Events{static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)},
-                 false);
-}
-
-mhc_status mhc_h_aggregate_bwd_acc(const uint16_t* residual, const float* pre,
-                                   const uint16_t* grad_out, uint16_t* grad_residual,
-                                   float* grad_pre, int64_t T, int64_t H, void* stream,
-                                   const mhc_launch* launch, void* start_event,
-                                   void* stop_event) {
-  return run_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, H, stream, launch,
-                 Events{static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)},
-                 true);
+  return plan_bwd_query(residual, pre, grad_out, grad_residual, grad_pre, T, MHC_HC, H, false,
+                        launch, plan, grid_blocks);
 }
 
 mhc_status mhc_h_aggregate_plan_bwd_acc(const uint16_t* residual, const float* pre,
@@ -932,14 +943,97 @@ mhc_status mhc_h_aggregate_plan_bwd_acc(const uint16_t* residual, const float* p
                                         const float* grad_pre, int64_t T, int64_t H,
                                         const mhc_launch* launch, mhc_launch* plan,
                                         int64_t* grid_blocks) {
-  mhc_status st = validate_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, H);
-  if (st != MHC_SUCCESS) return st;
-  BwdPlan pl;
-  if ((st = plan_bwd(residual, grad_out, grad_residual, T, H, true, launch, &pl)) != MHC_SUCCESS)
-    return st;
-  if (plan) *plan = mhc_launch{kLanes, pl.V, pl.U, pl.tpb, pl.S};
-  if (grid_blocks) *grid_blocks = pl.total_blocks;
-  return ok();
+  return plan_bwd_query(residual, pre, grad_out, grad_residual, grad_pre, T, MHC_HC, H, true,
+                        launch, plan, grid_blocks);
+}
+
+mhc_status mhc_h_aggregate_fwd(const uint16_t* residual, const float* pre, uint16_t* out,
+                               int64_t T, int64_t H, void* stream) {
+  return run_fwd(residual, pre, out, T, MHC_HC, H, stream, nullptr, events(nullptr, nullptr));
+}
+
+mhc_status mhc_h_aggregate_fwd_ex(const uint16_t* residual, const float* pre, uint16_t* out,
+                                  int64_t T, int64_t H, void* stream,
+                                  const mhc_launch* launch) {
+  return run_fwd(residual, pre, out, T, MHC_HC, H, stream, launch, events(nullptr, nullptr));
+}
+
+mhc_status mhc_h_aggregate_fwd_timed(const uint16_t* residual, const float* pre, uint16_t* out,
+                                     int64_t T, int64_t H, void* stream,
+                                     const mhc_launch* launch, void* start_event,
+                                     void* stop_event) {
+  return run_fwd(residual, pre, out, T, MHC_HC, H, stream, launch,
+                 events(start_event, stop_event));
+}
+
+mhc_status mhc_h_aggregate_bwd(const uint16_t* residual, const float* pre,
+                               const uint16_t* grad_out, uint16_t* grad_residual,
+                               float* grad_pre, int64_t T, int64_t H, void* stream) {
+  return run_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, MHC_HC, H, false, stream,
+                 nullptr, events(nullptr, nullptr));
+}
+
+mhc_status mhc_h_aggregate_bwd_ex(const uint16_t* residual, const float* pre,
+                                  const uint16_t* grad_out, uint16_t* grad_residual,
+                                  float* grad_pre, int64_t T, int64_t H, void* stream,
+                                  const mhc_launch* launch) {
+  return run_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, MHC_HC, H, false, stream,
+                 launch, events(nullptr, nullptr));
+}
+
+mhc_status mhc_h_aggregate_bwd_timed(const uint16_t* residual, const float* pre,
+                                     const uint16_t* grad_out, uint16_t* grad_residual,
+                                     float* grad_pre, int64_t T, int64_t H, void* stream,
+                                     const mhc_launch* launch, void* start_event,
+                                     void* stop_event) {
+  return run_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, MHC_HC, H, false, stream,
+                 launch, events(start_event, stop_event));
+}
+
+mhc_status mhc_h_aggregate_bwd_acc(const uint16_t* residual, const float* pre,
+                                   const uint16_t* grad_out, uint16_t* grad_residual,
+                                   float* grad_pre, int64_t T, int64_t H, void* stream,
+                                   const mhc_launch* launch, void* start_event,
+                                   void* stop_event) {
+  return run_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, MHC_HC, H, true, stream,
+                 launch, events(start_event, stop_event));
+}
+
+// ---- any supported expansion rate -----------------------------------------
+
+mhc_status mhc_h_aggregate_fwd_n(const uint16_t* residual, const float* pre, uint16_t* out,
+                                 int64_t T, int32_t n, int64_t H, void* stream,
+                                 const mhc_launch* launch, void* start_event, void* stop_event) {
+  return run_fwd(residual, pre, out, T, n, H, stream, launch, events(start_event, stop_event));
+}
+
+mhc_status mhc_h_aggregate_bwd_n(const uint16_t* residual, const float* pre,
+                                 const uint16_t* grad_out, uint16_t* grad_residual,
+                                 float* grad_pre, int64_t T, int32_t n, int64_t H,
+                                 int32_t accumulate, void* stream, const mhc_launch* launch,
+                                 void* start_event, void* stop_event) {
+  if (accumulate != 0 && accumulate != 1)
+    return fail(MHC_ERROR_INVALID_VALUE, "accumulate must be 0 or 1");
+  return run_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, n, H, accumulate == 1,
+                 stream, launch, events(start_event, stop_event));
+}
+
+mhc_status mhc_h_aggregate_plan_fwd_n(const uint16_t* residual, const float* pre,
+                                      const uint16_t* out, int64_t T, int32_t n, int64_t H,
+                                      const mhc_launch* launch, mhc_launch* plan,
+                                      int64_t* grid_blocks) {
+  return plan_fwd_query(residual, pre, out, T, n, H, launch, plan, grid_blocks);
+}
+
+mhc_status mhc_h_aggregate_plan_bwd_n(const uint16_t* residual, const float* pre,
+                                      const uint16_t* grad_out, const uint16_t* grad_residual,
+                                      const float* grad_pre, int64_t T, int32_t n, int64_t H,
+                                      int32_t accumulate, const mhc_launch* launch,
+                                      mhc_launch* plan, int64_t* grid_blocks) {
+  if (accumulate != 0 && accumulate != 1)
+    return fail(MHC_ERROR_INVALID_VALUE, "accumulate must be 0 or 1");
+  return plan_bwd_query(residual, pre, grad_out, grad_residual, grad_pre, T, n, H,
+                        accumulate == 1, launch, plan, grid_blocks);
 }
 
 mhc_status mhc_bf16_rne_probe(uint32_t first_bits, int64_t n, uint16_t* out, void* stream) {

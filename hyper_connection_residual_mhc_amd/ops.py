@@ -169,6 +169,53 @@ def mhc_h_aggregate_bwd_acc(residual: torch.Tensor, pre: torch.Tensor, grad_out:
     return grad_residual, grad_pre
 
 
+def _shapes_n(residual: torch.Tensor) -> tuple[int, int, int]:
+    if not isinstance(residual, torch.Tensor) or residual.dim() != 3 or \
+            residual.shape[1] not in (2, 4, 8):
+        raise ValueError("residual must have shape [T, n, H] with n in {2, 4, 8}")
+    return int(residual.shape[0]), int(residual.shape[1]), int(residual.shape[2])
+
+
+def mhc_h_aggregate_fwd_n(residual: torch.Tensor, pre: torch.Tensor, out: torch.Tensor,
+                          stream: torch.cuda.Stream | None = None, launch=None,
+                          start_event: int | None = None, stop_event: int | None = None
+                          ) -> torch.Tensor:
+    """Forward for expansion rate n in {2, 4, 8}: residual [T,n,H], pre [T,n]."""
+    T, n, H = _shapes_n(residual)
+    dev = residual.device
+    _require(residual, "residual", torch.bfloat16, (T, n, H))
+    _require(pre, "pre", torch.float32, (T, n), dev)
+    _require(out, "out", torch.bfloat16, (T, H), dev)
+    with torch.cuda.device(dev):
+        st = _lib.lib().mhc_h_aggregate_fwd_n(
+            residual.data_ptr(), pre.data_ptr(), out.data_ptr(), T, n, H,
+            _stream_handle(dev, stream), _launch_arg(launch), start_event, stop_event)
+    check(st)
+    return out
+
+
+def mhc_h_aggregate_bwd_n(residual: torch.Tensor, pre: torch.Tensor, grad_out: torch.Tensor,
+                          grad_residual: torch.Tensor, grad_pre: torch.Tensor,
+                          accumulate: bool = False, stream: torch.cuda.Stream | None = None,
+                          launch=None, start_event: int | None = None,
+                          stop_event: int | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Backward for expansion rate n in {2, 4, 8} (written or accumulating)."""
+    T, n, H = _shapes_n(residual)
+    dev = residual.device
+    _require(residual, "residual", torch.bfloat16, (T, n, H))
+    _require(pre, "pre", torch.float32, (T, n), dev)
+    _require(grad_out, "grad_out", torch.bfloat16, (T, H), dev)
+    _require(grad_residual, "grad_residual", torch.bfloat16, (T, n, H), dev)
+    _require(grad_pre, "grad_pre", torch.float32, (T, n), dev)
+    with torch.cuda.device(dev):
+        st = _lib.lib().mhc_h_aggregate_bwd_n(
+            residual.data_ptr(), pre.data_ptr(), grad_out.data_ptr(),
+            grad_residual.data_ptr(), grad_pre.data_ptr(), T, n, H, 1 if accumulate else 0,
+            _stream_handle(dev, stream), _launch_arg(launch), start_event, stop_event)
+    check(st)
+    return grad_residual, grad_pre
+
+
 def mhc_bf16_rne_probe(first_bits: int, out: torch.Tensor,
                        stream: torch.cuda.Stream | None = None) -> torch.Tensor:
     """out[k] = device bf16 rounding of the fp32 pattern first_bits + k (out: int16/uint16)."""
@@ -227,6 +274,31 @@ def mhc_h_aggregate_plan_bwd_acc(residual, pre, grad_out, grad_residual, grad_pr
                                                   _addr(grad_residual), _addr(grad_pre), T, H,
                                                   _launch_arg(launch), ctypes.byref(plan),
                                                   ctypes.byref(grid)))
+    return plan.as_dict(), int(grid.value)
+
+
+def mhc_h_aggregate_plan_fwd_n(residual, pre, out, T: int, n: int, H: int,
+                               launch=None) -> tuple[dict, int]:
+    """Host-only: forward launch shape for expansion rate n."""
+    plan = mhc_launch()
+    grid = ctypes.c_int64(0)
+    check(_lib.lib().mhc_h_aggregate_plan_fwd_n(_addr(residual), _addr(pre), _addr(out), T, n,
+                                                H, _launch_arg(launch), ctypes.byref(plan),
+                                                ctypes.byref(grid)))
+    return plan.as_dict(), int(grid.value)
+
+
+def mhc_h_aggregate_plan_bwd_n(residual, pre, grad_out, grad_residual, grad_pre, T: int,
+                               n: int, H: int, accumulate: bool = False,
+                               launch=None) -> tuple[dict, int]:
+    """Host-only: backward launch shape for expansion rate n."""
+    plan = mhc_launch()
+    grid = ctypes.c_int64(0)
+    check(_lib.lib().mhc_h_aggregate_plan_bwd_n(_addr(residual), _addr(pre), _addr(grad_out),
+                                                _addr(grad_residual), _addr(grad_pre), T, n,
+                                                H, 1 if accumulate else 0,
+                                                _launch_arg(launch), ctypes.byref(plan),
+                                                ctypes.byref(grid)))
     return plan.as_dict(), int(grid.value)
 
 

@@ -70,7 +70,8 @@ extern "C" {
 
 #define MHC_ABI_VERSION 2
 
-/* Hyper-connection expansion rate, fixed at 4 (Summary: residual [T, 4, H]). */
+/* Hyper-connection expansion rate of the page's operation (Summary: residual
+ * [T, 4, H]). The *_n entry points below also take 2 and 8. */
 #define MHC_HC 4
 
 /* Largest hidden size accepted. */
@@ -95,9 +96,10 @@ typedef enum mhc_status {
  *                     divide H and match the alignment of every bf16 buffer.
  *   units_per_thread  forward: vector units each thread handles; backward:
  *                     8-element groups each lane loads before its
- *                     arithmetic. 1, 2 or 4; in the backward at most what
- *                     the register budget allows for the vec_width and
- *                     streams_per_block (the plan query reports it; more
+ *                     arithmetic. 1, 2 or 4, at most what the register
+ *                     budget allows for the vec_width, expansion rate and
+ *                     streams_per_block (the plan query reports the
+ *                     default, which is that maximum in the backward; more
  *                     gives MHC_ERROR_INVALID_VALUE).
  *   tokens_per_block  backward only: tokens one block handles in sequence,
  *                     1..4096.
@@ -205,6 +207,33 @@ mhc_status mhc_h_aggregate_bwd_acc(const uint16_t* residual, const float* pre,
                                    void* stop_event);
 
 /*
+ * Any supported expansion rate n in {2, 4, 8} (the second page's sibling
+ * implementation covers HC in {2, 4, 8}; the first page fixes 4):
+ *   residual [T, n, H] bf16, pre [T, n] fp32, out [T, H] bf16,
+ *   grad_residual [T, n, H] bf16, grad_pre [T, n] fp32.
+ * Forward: the n products are summed as a balanced pairwise tree, adjacent
+ * pairs first, then pairs of pairs - (0+1)+(2+3) at n = 4 (identical to
+ * mhc_h_aggregate_fwd), p0+p1 at n = 2, ((0+1)+(2+3))+((4+5)+(6+7)) at n = 8;
+ * every product and sum one fp32 round-to-nearest-even operation, one bf16
+ * rounding at the end. Backward: per stream exactly as above (the fixed
+ * grad_pre order is per (token, stream)); accumulate = 1 selects the
+ * accumulating form of mhc_h_aggregate_bwd_acc, 0 the written form. launch,
+ * start_event and stop_event may each be NULL. An n outside {2, 4, 8} gives
+ * MHC_ERROR_INVALID_VALUE; streams_per_block must not exceed n.
+ */
+mhc_status mhc_h_aggregate_fwd_n(const uint16_t* residual, const float* pre,
+                                 uint16_t* out, int64_t T, int32_t n, int64_t H,
+                                 void* stream, const mhc_launch* launch,
+                                 void* start_event, void* stop_event);
+mhc_status mhc_h_aggregate_bwd_n(const uint16_t* residual, const float* pre,
+                                 const uint16_t* grad_out,
+                                 uint16_t* grad_residual, float* grad_pre,
+                                 int64_t T, int32_t n, int64_t H,
+                                 int32_t accumulate, void* stream,
+                                 const mhc_launch* launch, void* start_event,
+                                 void* stop_event);
+
+/*
  * Host-only checks and plan queries. They touch no device and no memory
  * behind the pointers (the pointers are used only as numbers for alignment
  * and overlap tests), so they run without a GPU.
@@ -234,6 +263,17 @@ mhc_status mhc_h_aggregate_plan_bwd(const uint16_t* residual, const float* pre,
                                     const float* grad_pre, int64_t T,
                                     int64_t H, const mhc_launch* launch,
                                     mhc_launch* plan, int64_t* grid_blocks);
+mhc_status mhc_h_aggregate_plan_fwd_n(const uint16_t* residual, const float* pre,
+                                      const uint16_t* out, int64_t T, int32_t n,
+                                      int64_t H, const mhc_launch* launch,
+                                      mhc_launch* plan, int64_t* grid_blocks);
+mhc_status mhc_h_aggregate_plan_bwd_n(const uint16_t* residual, const float* pre,
+                                      const uint16_t* grad_out,
+                                      const uint16_t* grad_residual,
+                                      const float* grad_pre, int64_t T, int32_t n,
+                                      int64_t H, int32_t accumulate,
+                                      const mhc_launch* launch, mhc_launch* plan,
+                                      int64_t* grid_blocks);
 mhc_status mhc_h_aggregate_plan_bwd_acc(const uint16_t* residual,
                                         const float* pre,
                                         const uint16_t* grad_out,

@@ -284,3 +284,31 @@ def test_accumulating_backward_plan(lib):
                                        None) == MHC_ERROR_ALIASING
     assert lib.mhc_h_aggregate_bwd_acc(0, 0, 0, 0, 0, 0, H, None, None, None,
                                        None) == MHC_SUCCESS
+
+
+def test_expansion_rate_rules(lib):
+    """n must be 2, 4 or 8; sizes scale with n; streams_per_block <= n; the
+    register budget caps the forward batch at n = 8."""
+    T, H = 64, 4096
+    r, p, o = fwd_ptrs(T, H * 2)   # room for n = 8
+    for n in (2, 4, 8):
+        plan, grid = ops.mhc_h_aggregate_plan_fwd_n(r, p, o, T, n, H)
+        assert plan["vec_width"] == 8 and grid == T * (H // 8 // 64)
+    for bad_n in (0, 1, 3, 16):
+        with pytest.raises(MhcError, match="expansion rate n must be 2, 4 or 8"):
+            ops.mhc_h_aggregate_plan_fwd_n(r, p, o, T, bad_n, H)
+    with pytest.raises(MhcError, match="exceeds the register budget"):
+        ops.mhc_h_aggregate_plan_fwd_n(r, p, o, T, 8, H, launch={"units_per_thread": 4})
+    # n = 8 residual is twice the n = 4 one: out right after 4-stream bytes overlaps
+    with pytest.raises(MhcError, match="ALIASING"):
+        ops.mhc_h_aggregate_plan_fwd_n(r, r + 8 * T * H * 2, r + 8 * T * H, T, 8, H)
+    rr, pp, g, gr, gp = bwd_ptrs(1024, H * 2)
+    plan, grid = ops.mhc_h_aggregate_plan_bwd_n(rr, pp, g, gr, gp, 1024, 2, H)
+    assert plan["streams_per_block"] == 2 and grid == 1024
+    plan, grid = ops.mhc_h_aggregate_plan_bwd_n(rr, pp, g, gr, gp, 1024, 8, H)
+    assert plan["streams_per_block"] == 4 and grid == 2048
+    with pytest.raises(MhcError, match="exceeds the 2 streams"):
+        ops.mhc_h_aggregate_plan_bwd_n(rr, pp, g, gr, gp, 8, 2, H,
+                                       launch={"streams_per_block": 4})
+    assert lib.mhc_h_aggregate_bwd_n(rr, pp, g, gr, gp, 8, 4, H, 2, None, None, None,
+                                     None) == MHC_ERROR_INVALID_VALUE
