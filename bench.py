@@ -368,6 +368,13 @@ def _rows(path: str) -> list[dict]:
         return list(csv.DictReader(f))
 
 
+def _short_name(name: str) -> str:
+    """Kernel name without return type, namespace or parameter list."""
+    name = name.replace("(anonymous namespace)::", "")
+    name = re.sub(r"^void ", "", name)
+    return re.sub(r"\(.*", "", name)[:90]
+
+
 def summarize_stats(path: str) -> None:
     """Markdown table of a rocprofv3 --stats kernel_stats.csv."""
     rows = _rows(path)
@@ -375,7 +382,7 @@ def summarize_stats(path: str) -> None:
     print("|---|---|---|---|---|---|")
     for r in rows:
         name = r.get("Name", "")
-        short = re.sub(r"\(.*", "", name)[:90]
+        short = _short_name(name)
         avg = float(r.get("AverageNs", 0)) / 1e3
         mn = float(r.get("MinNs", 0)) / 1e3
         mx = float(r.get("MaxNs", 0)) / 1e3
@@ -385,17 +392,18 @@ def summarize_stats(path: str) -> None:
 
 def summarize_pmc(paths: list[str]) -> None:
     """Per-kernel average of each counter (KiB for FETCH_SIZE / WRITE_SIZE)
-    from rocprofv3 --pmc counter_collection.csv files."""
-    acc: dict[tuple[str, str], list[float]] = {}
+    from rocprofv3 --pmc counter_collection.csv files, one row per kernel and
+    grid size (so the calibration copy stands apart from small staging copies)."""
+    acc: dict[tuple[str, int, str], list[float]] = {}
     for p in paths:
         for r in _rows(p):
-            name = re.sub(r"\(.*", "", r.get("Kernel_Name", ""))[:90]
-            key = (name, r.get("Counter_Name", ""))
+            key = (_short_name(r.get("Kernel_Name", "")), int(r.get("Grid_Size", 0) or 0),
+                   r.get("Counter_Name", ""))
             acc.setdefault(key, []).append(float(r.get("Counter_Value", 0)))
-    print("| kernel | counter | dispatches | average per dispatch |")
-    print("|---|---|---|---|")
-    for (name, ctr), vals in sorted(acc.items()):
-        print(f"| {name} | {ctr} | {len(vals)} | {statistics.fmean(vals):.1f} |")
+    print("| kernel | grid size | counter | dispatches | average per dispatch |")
+    print("|---|---|---|---|---|")
+    for (name, grid, ctr), vals in sorted(acc.items()):
+        print(f"| {name} | {grid} | {ctr} | {len(vals)} | {statistics.fmean(vals):.1f} |")
 
 
 # ---------------------------------------------------------------------------
