@@ -307,13 +307,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void h
     float w[S];
 #pragma unroll
     for (int i = 0; i < S; ++i) w[i] = p[i];
-    // The token's grad_out row (2H bytes) and the block's S residual /
-    // grad_residual rows (2SH bytes each).
+    // One resource per row: the token's grad_out row and the block's S
+    // residual and grad_residual rows (2H bytes each). Groups past the end of
+    // the row (k >= ngroups) and elements past H of a short last group read 0
+    // and their stores are dropped, so the plain backward's loop body needs
+    // no per-group branch: a zero element adds +0 * +0 = +0 to an
+    // accumulator, which leaves it bit-unchanged (an accumulator that starts
+    // at +0 is never -0 under round-to-nearest), and its grad_residual store
+    // falls outside the row. Without branches the compiler can wait for each
+    // group's loads separately, so a lane starts computing and storing as
+    // soon as its first group arrives. The accumulating form keeps the
+    // per-group test: with its larger register set, the branch-free body is
+    // scheduled with later loads behind earlier stores, which measured slower.
     const Rsrc g_row = make_rsrc(grad_out + t * H, 2 * H);
-    const Rsrc r_row = make_rsrc(residual + (t * n + i0) * H, 2 * S * H);
-    const Rsrc gr_row = make_rsrc(grad_residual + (t * n + i0) * H, 2 * S * H);
-    const uint32_t hs = static_cast<uint32_t>(H);  // elements between streams
-    const uint32_t row = 2 * hs;                   // bytes between streams
+    Rsrc r_row[S], gr_row[S];
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+      r_row[i] = make_rsrc(residual + (t * n + i0 + i) * H, 2 * H);
+      gr_row[i] = make_rsrc(grad_residual + (t * n + i0 + i) * H, 2 * H);
+    }
 
     float acc[S];
 #pragma unroll
@@ -325,43 +337,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void h
       VT old[ACC ? U : 1][NV][S];  // accumulating form: the stored gradient
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const uint32_t k = k0 + u * kLanes;
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
+          const uint32_t k = k0 + u * kLanes;
           const uint32_t h = k * kGroup + v * V;
-          if (k < ngroups && h < H) {
+          if (!ACC || (k < ngroups && h < H)) {
             g[u][v] = load_vec<V>(g_row, h, 0);
 #pragma unroll
-            for (int i = 0; i < S; ++i) r[u][v][i] = load_vec<V>(r_row, h, i * row);
+            for (int i = 0; i < S; ++i) r[u][v][i] = load_vec<V>(r_row[i], h, 0);
             if constexpr (ACC) {
 #pragma unroll
-              for (int i = 0; i < S; ++i) old[u][v][i] = load_vec<V>(gr_row, h, i * row);
+              for (int i = 0; i < S; ++i) old[u][v][i] = load_vec<V>(gr_row[i], h, 0);
             }
           }
         }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const uint32_t k = k0 + u * kLanes;
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
+          const uint32_t k = k0 + u * kLanes;
           const uint32_t h = k * kGroup + v * V;
-          if (k < ngroups && h < H) {
-            // Stream by stream, so only one stream's values are live at a
-            // time; each accumulator still adds its elements in ascending h.
+          if (ACC && !(k < ngroups && h < H)) continue;
+          // Stream by stream, so only one stream's values are live at a
+          // time; each accumulator still adds its elements in ascending h.
 #pragma unroll
-            for (int i = 0; i < S; ++i) {
-              float gr[V];
+          for (int i = 0; i < S; ++i) {
+            float gr[V];
 #pragma unroll
-              for (int e = 0; e < V; ++e) {
-                const float ge = elem<V>(g[u][v], e);
-                gr[e] = w[i] * ge;
-                if constexpr (ACC) gr[e] = elem<V>(old[u][v][i], e) + gr[e];
-                const float q = ge * elem<V>(r[u][v][i], e);  // exact in the normal range
-                acc[i] = acc[i] + q;
-              }
-              store_vec<V>(gr_row, i * hs + h, pack<V>(gr));
+            for (int e = 0; e < V; ++e) {
+              const float ge = elem<V>(g[u][v], e);
+              gr[e] = w[i] * ge;
+              if constexpr (ACC) gr[e] = elem<V>(old[u][v][i], e) + gr[e];
+              const float q = ge * elem<V>(r[u][v][i], e);  // exact in the normal range
+              acc[i] = acc[i] + q;
             }
+            store_vec<V>(gr_row[i], h, pack<V>(gr));
           }
         }
       }
