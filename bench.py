@@ -117,6 +117,32 @@ def copy_probe(dev, nbytes: int = 1 << 28, reps: int = 3) -> None:
     torch.cuda.synchronize()
 
 
+# Read:write mix of each kernel for the streaming probe (per token: forward
+# 8H read / 2H written, backward 10H / 8H, accumulating backward 18H / 8H).
+PROBE_MIX = {"fwd": (4, 1), "bwd": (5, 4), "bwd_acc": (9, 4)}
+
+
+class ProbeBuffers:
+    """Rotating src/dst pairs for mhc_stream_probe sized to about `nbytes`
+    of traffic with the given mix (whole 1-KiB units)."""
+
+    def __init__(self, nbytes: int, mix: tuple[int, int], pairs: int, dev):
+        import torch
+        r, w = mix
+        self.units = max(1, nbytes // ((r + w) * 1024))
+        self.mix = mix
+        self.bytes = self.units * (r + w) * 1024
+        self.pairs = [(torch.ones(self.units * r * 256, dtype=torch.int32, device=dev),
+                       torch.empty(self.units * w * 256, dtype=torch.int32, device=dev))
+                      for _ in range(pairs)]
+
+    def call(self, lib, k: int, stream_handle: int, a, b) -> int:
+        src, dst = self.pairs[k % len(self.pairs)]
+        r, w = self.mix
+        return lib.mhc_stream_probe(src.data_ptr(), src.numel() * 4, dst.data_ptr(),
+                                    dst.numel() * 4, r, w, stream_handle, a, b)
+
+
 class HipEvents:
     """Timing events from the HIP runtime (created with timing enabled). The
     library attaches them to its kernel dispatches, so their elapsed time is
@@ -217,7 +243,29 @@ def run_gpu(T: int, H: int, steps: int, warmup: int, nsets: int, probe: bool,
     fwd_us = [ev.elapsed_us(4 * j, 4 * j + 1) for j in range(len(sampled))]
     bwd_us = [ev.elapsed_us(4 * j + 2, 4 * j + 3) for j in range(len(sampled))]
     ev.close()
+
+    # Ceiling: the backward and a streaming probe with its read:write byte
+    # mix and no arithmetic, alternating, every launch timed by its own
+    # dispatch events, each from cold buffers. Outside the timed steps.
+    probe = ProbeBuffers(bwd_bytes(T, H), PROBE_MIX["bwd"], nsets, dev)
+    n_ceil = 200
+    cev = HipEvents(4 * n_ceil)
+    C = cev.handles
+    for k in range(10):
+        _lib.check(bwd(*bargs[k % nsets]) | probe.call(lib, k, sh, None, None))
+    torch.cuda.synchronize()
+    for k in range(n_ceil):
+        _lib.check(bwd_t(*bargs[k % nsets], None, C[4 * k], C[4 * k + 1]) |
+                   probe.call(lib, k, sh, C[4 * k + 2], C[4 * k + 3]))
+    torch.cuda.synchronize()
+    ceil_kernel_us = [cev.elapsed_us(4 * k, 4 * k + 1) for k in range(n_ceil)]
+    ceil_probe_us = [cev.elapsed_us(4 * k + 2, 4 * k + 3) for k in range(n_ceil)]
+    cev.close()
+    probe_bytes = probe.bytes
+    del probe
     return {
+        "ceiling": {"kernel_us": ceil_kernel_us, "probe_us": ceil_probe_us,
+                    "probe_bytes": probe_bytes},
         "wall_s": t1 - t0,
         "timed_launches": len(sampled),
         "fwd_us": fwd_us,
@@ -227,6 +275,24 @@ def run_gpu(T: int, H: int, steps: int, warmup: int, nsets: int, probe: bool,
         "device": torch.cuda.get_device_name(dev),
         "torch": torch.__version__,
         "hip": getattr(torch.version, "hip", None),
+    }
+
+
+def ceiling_record(kernel_bytes: int, c: dict) -> dict:
+    k = statistics.fmean(c["kernel_us"])
+    p = statistics.fmean(c["probe_us"])
+    kg = kernel_bytes / k / 1e3
+    pg = c["probe_bytes"] / p / 1e3
+    return {
+        "kind": "mhc_stream_probe: the backward's 5:4 read:write byte mix as a plain "
+                "stream, no arithmetic; launched alternately with the backward, every "
+                "launch timed by its own dispatch events, cold buffers",
+        "probe_bytes": c["probe_bytes"],
+        "probe_us": round(p, 3),
+        "probe_gbps": round(pg, 1),
+        "kernel_us": round(k, 3),
+        "kernel_gbps": round(kg, 1),
+        "frac_of_probe": round(kg / pg, 4),
     }
 
 
@@ -240,11 +306,16 @@ SWEEP_SHAPES = [  # (T, H): latency sweep, bandwidth shapes, backward shape
 ]
 
 
-def run_sweep(path: str, launches: int = 200) -> None:
+def run_sweep(path: str, rounds: int = 7, warm: int = 10, timed: int = 100) -> None:
     """Per-call forward and backward times at SWEEP_SHAPES, one JSON line per
-    (shape, direction) into `path`. Every launch carries dispatch events, so
-    launches run one at a time (each from cold caches: 8 rotating sets, 3 at
-    T=8192) - the per-call latency a caller sees, as in the page's table."""
+    (shape, direction) into `path`. Every timed launch carries its own
+    dispatch events, so launches run one at a time, each from cold caches
+    (8 rotating buffer sets, 3 at T=8192) - the per-call latency a caller
+    sees, as in the page's table. `rounds` rounds of `warm` untimed and
+    `timed` timed launches; p20 / median / p80 are taken over the round
+    medians, GB/s from the median. At T >= 1024 a streaming probe with the
+    kernel's read:write byte mix is launched alternately with the kernel and
+    timed the same way (the ceiling column)."""
     import statistics as st
     import torch
     from hyper_connection_residual_mhc_amd import _lib, ops
@@ -253,12 +324,19 @@ def run_sweep(path: str, launches: int = 200) -> None:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sh = int(torch.cuda.current_stream(dev).cuda_stream)
-    ev = HipEvents(2 * launches)
+    ev = HipEvents(4 * timed)
     E = ev.handles
+
+    def summary(per_round: list[list[float]]) -> tuple[float, list[float], float]:
+        med = [st.median(r) for r in per_round]
+        q = st.quantiles(med, n=10, method="inclusive")
+        mean = st.fmean([x for r in per_round for x in r])
+        return st.median(med), [round(q[1], 3), round(st.median(med), 3), round(q[7], 3)], mean
+
     with open(path, "w") as f:
         for T, H in SWEEP_SHAPES:
-            sets = make_sets(T, H, 8 if T <= 2048 else 3, dev)
-            n = len(sets)
+            nsets = 8 if T <= 2048 else 3
+            sets = make_sets(T, H, nsets, dev)
             s0 = sets[0]
             directions = ("fwd", "bwd", "bwd_acc") if T >= 1024 else ("fwd", "bwd")
             for direction in directions:
@@ -267,7 +345,7 @@ def run_sweep(path: str, launches: int = 200) -> None:
                     nbytes = fwd_bytes(T, H)
 
                     def call(k, a, b):
-                        x = sets[k % n]
+                        x = sets[k % nsets]
                         return lib.mhc_h_aggregate_fwd_timed(
                             x.residual.data_ptr(), x.pre.data_ptr(), x.out.data_ptr(), T, H, sh,
                             None, a, b)
@@ -277,7 +355,7 @@ def run_sweep(path: str, launches: int = 200) -> None:
                     nbytes = bwd_acc_bytes(T, H)
 
                     def call(k, a, b):
-                        x = sets[k % n]
+                        x = sets[k % nsets]
                         return lib.mhc_h_aggregate_bwd_acc(
                             x.residual.data_ptr(), x.pre.data_ptr(), x.grad_out.data_ptr(),
                             x.grad_residual.data_ptr(), x.grad_pre.data_ptr(), T, H, sh, None,
@@ -288,75 +366,48 @@ def run_sweep(path: str, launches: int = 200) -> None:
                     nbytes = bwd_bytes(T, H)
 
                     def call(k, a, b):
-                        x = sets[k % n]
+                        x = sets[k % nsets]
                         return lib.mhc_h_aggregate_bwd_timed(
                             x.residual.data_ptr(), x.pre.data_ptr(), x.grad_out.data_ptr(),
                             x.grad_residual.data_ptr(), x.grad_pre.data_ptr(), T, H, sh, None,
                             a, b)
-                for k in range(10):
-                    _lib.check(call(k, None, None))
-                torch.cuda.synchronize()
-                for k in range(launches):
-                    _lib.check(call(k, E[2 * k], E[2 * k + 1]))
-                torch.cuda.synchronize()
-                us = [ev.elapsed_us(2 * k, 2 * k + 1) for k in range(launches)]
-                q = st.quantiles(us, n=10)
+                probe = (ProbeBuffers(nbytes, PROBE_MIX[direction], nsets, dev)
+                         if T >= 1024 else None)
+                k_rounds, p_rounds = [], []
+                for _ in range(rounds):
+                    for k in range(warm):
+                        _lib.check(call(k, None, None))
+                        if probe:
+                            _lib.check(probe.call(lib, k, sh, None, None))
+                    torch.cuda.synchronize()
+                    for k in range(timed):
+                        _lib.check(call(k, E[4 * k], E[4 * k + 1]))
+                        if probe:
+                            _lib.check(probe.call(lib, k, sh, E[4 * k + 2], E[4 * k + 3]))
+                    torch.cuda.synchronize()
+                    k_rounds.append([ev.elapsed_us(4 * k, 4 * k + 1) for k in range(timed)])
+                    if probe:
+                        p_rounds.append([ev.elapsed_us(4 * k + 2, 4 * k + 3) for k in range(timed)])
+                med, q, mean = summary(k_rounds)
                 rec = {"direction": direction, "T": T, "H": H, "bytes": nbytes,
-                       "us_mean": round(st.fmean(us), 3),
-                       "us_p20_p50_p80": [round(q[1], 3), round(q[4], 3), round(q[7], 3)],
-                       "gbps": round(nbytes / st.fmean(us) / 1e3, 1),
-                       "frac_of_8TBps": round(nbytes / st.fmean(us) / 1e3 / PEAK_HBM_GBPS, 4),
+                       "us_median": round(med, 3), "us_p20_p50_p80": q,
+                       "us_mean": round(mean, 3),
+                       "gbps": round(nbytes / med / 1e3, 1),
+                       "frac_of_8TBps": round(nbytes / med / 1e3 / PEAK_HBM_GBPS, 4),
                        "plan": plan}
+                if probe:
+                    pmed, pq, _ = summary(p_rounds)
+                    pg = probe.bytes / pmed / 1e3
+                    rec["probe"] = {"mix": list(PROBE_MIX[direction]), "bytes": probe.bytes,
+                                    "us_median": round(pmed, 3), "gbps": round(pg, 1),
+                                    "frac_of_probe": round(rec["gbps"] / pg, 4)}
+                    del probe
                 f.write(json.dumps(rec) + "\n")
                 f.flush()
                 print(json.dumps(rec), file=sys.stderr, flush=True)
             del sets
             torch.cuda.empty_cache()
     ev.close()
-
-
-# ---------------------------------------------------------------------------
-# CPU baseline: the oracle on a token sample
-# ---------------------------------------------------------------------------
-
-def run_cpu_baseline(T: int, H: int, min_seconds: float) -> dict:
-    """The oracle, as it stands, on the step's workload: the forward and
-    backward of one seed-0 input set of T tokens, repeated until at least
-    `min_seconds` of CPU time have passed (one thread: numpy ufuncs)."""
-    from hyper_connection_residual_mhc_amd.workloads import make_inputs
-    from oracle import h_aggregate as O
-    host = make_inputs(T, H, seed=0, grad=True)
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        O.h_aggregate_fwd(host["residual"], host["pre"])
-        O.h_aggregate_bwd(host["residual"], host["pre"], host["grad_out"])
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds or reps >= 1000:
-            break
-    gb = reps * (fwd_bytes(T, H) + bwd_bytes(T, H)) / 1e9
-    return {
-        "value": round(gb / dt, 6),
-        "unit": "GB/s",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": (f"{reps} oracle steps (forward + backward) on one seed-0 input set of "
-                   f"T={T}, H={H} (numpy float32 ufuncs, one thread), {dt:.1f} s; "
-                   f"GB/s of the same algorithmic bytes"),
-        "host_cpu": cpu_model(),
-        "host_cores_visible": len(os.sched_getaffinity(0)),
-    }
-
-
-def cpu_model() -> str:
-    try:
-        for line in Path("/proc/cpuinfo").read_text().splitlines():
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
-    except OSError:
-        pass
-    return platform.processor() or "unknown"
 
 
 # ---------------------------------------------------------------------------
@@ -506,6 +557,7 @@ def main() -> int:
             "traffic": recorded_traffic(),
             "kernel": "hagg_bwd_kernel (backward)",
         },
+        "ceiling": ceiling_record(bwd_bytes(T, H), g["ceiling"]),
         "timing": {"per_kernel": "HIP events attached to the dispatches of every "
                                  f"{args.time_every}th step ({g['timed_launches']} launches "
                                  "of each kernel)",

@@ -78,6 +78,8 @@ SIGNATURES = {
                                          c_int64, c_int64, POINTER(mhc_launch),
                                          POINTER(mhc_launch), POINTER(c_int64)]),
     "mhc_bf16_rne_probe": (c_int, [c_uint32, c_int64, c_void_p, c_void_p]),
+    "mhc_stream_probe": (c_int, [c_void_p, c_int64, c_void_p, c_int64, c_int32, c_int32,
+                                 c_void_p, c_void_p, c_void_p]),
 }
 
 _lib: ctypes.CDLL | None = None

@@ -264,6 +264,62 @@ __device__ __forceinline__ float from_lane_plus(float x) {
   }
 }
 
+// The register slots of the backward's ring of loads: for each of U groups,
+// the grad_out vector(s), the S residual vectors and (accumulating form) the
+// S stored-gradient vectors of its 8 elements.
+template <int V, int U, int S, bool ACC>
+struct BwdSlots {
+  typedef typename Vec<V>::type VT;
+  static constexpr int NV = kGroup / V;  // accesses per group
+  VT g[U][NV];
+  VT r[U][NV][S];
+  VT old[ACC ? U : 1][NV][S];
+};
+
+// Issue the loads of group k into slot u (u is a constant after unrolling).
+template <int V, int U, int S, bool ACC>
+__device__ __forceinline__ void bwd_issue(BwdSlots<V, U, S, ACC>& sl, int u, uint32_t k,
+                                          Rsrc g_row, const Rsrc (&r_row)[S],
+                                          const Rsrc (&gr_row)[S]) {
+#pragma unroll
+  for (int v = 0; v < BwdSlots<V, U, S, ACC>::NV; ++v) {
+    const uint32_t h = k * kGroup + v * V;
+    sl.g[u][v] = load_vec<V>(g_row, h, 0);
+#pragma unroll
+    for (int i = 0; i < S; ++i) sl.r[u][v][i] = load_vec<V>(r_row[i], h, 0);
+    if constexpr (ACC) {
+#pragma unroll
+      for (int i = 0; i < S; ++i) sl.old[u][v][i] = load_vec<V>(gr_row[i], h, 0);
+    }
+  }
+}
+
+// Consume slot u holding group k: write its grad_residual vectors and add
+// its products to the accumulators, element by element in ascending h.
+// Stream by stream, so only one stream's results are live at a time.
+template <int V, int U, int S, bool ACC>
+__device__ __forceinline__ void bwd_consume(BwdSlots<V, U, S, ACC>& sl, int u, uint32_t k,
+                                            const float (&w)[S], float (&acc)[S],
+                                            const Rsrc (&gr_row)[S]) {
+#pragma unroll
+  for (int v = 0; v < BwdSlots<V, U, S, ACC>::NV; ++v) {
+    const uint32_t h = k * kGroup + v * V;
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+      float gr[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const float ge = elem<V>(sl.g[u][v], e);
+        gr[e] = w[i] * ge;
+        if constexpr (ACC) gr[e] = elem<V>(sl.old[u][v][i], e) + gr[e];
+        const float q = ge * elem<V>(sl.r[u][v][i], e);  // exact in the normal range
+        acc[i] = acc[i] + q;
+      }
+      store_vec<V>(gr_row[i], h, pack<V>(gr));
+    }
+  }
+}
+
 // Grid: (ceil(T / tokens_per_block), n / S) blocks of exactly 256 threads,
 // n the expansion rate (2, 4 or 8 residual streams per token). Block (b, j)
 // handles streams S*j .. S*j + S-1 of tokens b*tokens_per_block ..
@@ -291,8 +347,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void h
     const uint16_t* __restrict__ grad_out, uint16_t* __restrict__ grad_residual,
     float* __restrict__ grad_pre, int64_t T, int32_t n, int64_t H, uint32_t ngroups,
     int32_t tokens_per_block) {
-  typedef typename Vec<V>::type VT;
-  constexpr int NV = kGroup / V;  // accesses per full group
   __shared__ float wave_sum[4][S];  // [wave][stream of this block]
 
   const int lane = threadIdx.x;
@@ -310,15 +364,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void h
     // One resource per row: the token's grad_out row and the block's S
     // residual and grad_residual rows (2H bytes each). Groups past the end of
     // the row (k >= ngroups) and elements past H of a short last group read 0
-    // and their stores are dropped, so the plain backward's loop body needs
-    // no per-group branch: a zero element adds +0 * +0 = +0 to an
-    // accumulator, which leaves it bit-unchanged (an accumulator that starts
-    // at +0 is never -0 under round-to-nearest), and its grad_residual store
-    // falls outside the row. Without branches the compiler can wait for each
-    // group's loads separately, so a lane starts computing and storing as
-    // soon as its first group arrives. The accumulating form keeps the
-    // per-group test: with its larger register set, the branch-free body is
-    // scheduled with later loads behind earlier stores, which measured slower.
+    // and their stores are dropped, so the loop has no per-group branch: a
+    // zero element adds +0 * +0 = +0 to an accumulator, which leaves it
+    // bit-unchanged (an accumulator that starts at +0 is never -0 under
+    // round-to-nearest), and its grad_residual store falls outside the row.
     const Rsrc g_row = make_rsrc(grad_out + t * H, 2 * H);
     Rsrc r_row[S], gr_row[S];
 #pragma unroll
@@ -331,51 +380,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void h
 #pragma unroll
     for (int i = 0; i < S; ++i) acc[i] = 0.0f;
 
-    for (uint32_t k0 = lane; k0 < ngroups; k0 += kLanes * U) {
-      VT g[U][NV];
-      VT r[U][NV][S];
-      VT old[ACC ? U : 1][NV][S];  // accumulating form: the stored gradient
+    // Lane l visits groups l, l + 256, l + 512, ... in that order, U of them
+    // per round, through a ring of U register slots: slot u holds the group
+    // of round j at position u, and is refilled with its group of round j+1
+    // as soon as it has been consumed, so loads stay in flight while earlier
+    // groups are computed and stored. The round count is taken from the
+    // wave's first lane (the lanes of a wave differ by less than 64 groups),
+    // so it is wave-uniform; a lane with fewer groups meets only zeros in its
+    // last round.
+    BwdSlots<V, U, S, ACC> sl;
+    const uint32_t wave_first = __builtin_amdgcn_readfirstlane(lane & ~63u);
+    const uint32_t step = kLanes * U;
+    const uint32_t rounds = wave_first < ngroups ? (ngroups - wave_first + step - 1) / step : 0;
+    if (rounds > 0) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < U; ++u) bwd_issue(sl, u, lane + u * kLanes, g_row, r_row, gr_row);
+      for (uint32_t j = 0; j + 1 < rounds; ++j) {
+        const uint32_t k0 = lane + j * step;
 #pragma unroll
-        for (int v = 0; v < NV; ++v) {
-          const uint32_t k = k0 + u * kLanes;
-          const uint32_t h = k * kGroup + v * V;
-          if (!ACC || (k < ngroups && h < H)) {
-            g[u][v] = load_vec<V>(g_row, h, 0);
-#pragma unroll
-            for (int i = 0; i < S; ++i) r[u][v][i] = load_vec<V>(r_row[i], h, 0);
-            if constexpr (ACC) {
-#pragma unroll
-              for (int i = 0; i < S; ++i) old[u][v][i] = load_vec<V>(gr_row[i], h, 0);
-            }
-          }
+        for (int u = 0; u < U; ++u) {
+          bwd_consume(sl, u, k0 + u * kLanes, w, acc, gr_row);
+          bwd_issue(sl, u, k0 + step + u * kLanes, g_row, r_row, gr_row);
         }
       }
+      const uint32_t k0 = lane + (rounds - 1) * step;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-          const uint32_t k = k0 + u * kLanes;
-          const uint32_t h = k * kGroup + v * V;
-          if (ACC && !(k < ngroups && h < H)) continue;
-          // Stream by stream, so only one stream's values are live at a
-          // time; each accumulator still adds its elements in ascending h.
-#pragma unroll
-          for (int i = 0; i < S; ++i) {
-            float gr[V];
-#pragma unroll
-            for (int e = 0; e < V; ++e) {
-              const float ge = elem<V>(g[u][v], e);
-              gr[e] = w[i] * ge;
-              if constexpr (ACC) gr[e] = elem<V>(old[u][v][i], e) + gr[e];
-              const float q = ge * elem<V>(r[u][v][i], e);  // exact in the normal range
-              acc[i] = acc[i] + q;
-            }
-            store_vec<V>(gr_row[i], h, pack<V>(gr));
-          }
-        }
-      }
+      for (int u = 0; u < U; ++u) bwd_consume(sl, u, k0 + u * kLanes, w, acc, gr_row);
     }
 
     // Wave stage: x[j] = x[j] + x[j + off] for off = 32, 16, 8, 4, 2, 1.
@@ -416,6 +446,38 @@ __global__ __launch_bounds__(256) void bf16_probe_kernel(uint32_t first_bits,
   if (k >= n) return;
   const uint32_t bits = first_bits + static_cast<uint32_t>(k);
   out[k] = to_bf16(__uint_as_float(bits));
+}
+
+// ---------------------------------------------------------------------------
+// Streaming probe (measurement only)
+// ---------------------------------------------------------------------------
+//
+// The bandwidth a plain stream with a given read:write byte mix reaches on
+// this GPU, with no arithmetic: the ceiling the kernels above are compared
+// with. One 64-lane block per unit; a unit reads R consecutive KiB of src
+// and writes W consecutive KiB of dst (each access instruction covers 1 KiB:
+// 64 lanes x 16 bytes), all loads issued before the first store, nontemporal
+// like the kernels. The written words are the XOR of the unit's loaded words
+// so that no load is dead.
+constexpr int kProbeChunk = 1024;
+
+template <int R, int W>
+__global__ __launch_bounds__(64) void stream_probe_kernel(const uint8_t* __restrict__ src,
+                                                          uint8_t* __restrict__ dst) {
+  const int64_t u = blockIdx.x;
+  const uint32_t lane = threadIdx.x;
+  const Rsrc rs = make_rsrc(src + u * (R * kProbeChunk), R * kProbeChunk);
+  const Rsrc rd = make_rsrc(dst + u * (W * kProbeChunk), W * kProbeChunk);
+  u32x4 x[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    x[r] = __builtin_amdgcn_raw_buffer_load_b128(rs, r * kProbeChunk + lane * 16, 0, kNontemporal);
+  u32x4 acc = x[0];
+#pragma unroll
+  for (int r = 1; r < R; ++r) acc ^= x[r];
+#pragma unroll
+  for (int w = 0; w < W; ++w)
+    __builtin_amdgcn_raw_buffer_store_b128(acc, rd, w * kProbeChunk + lane * 16, 0, kNontemporal);
 }
 
 // ---------------------------------------------------------------------------
@@ -588,13 +650,14 @@ mhc_status plan_fwd(const uint16_t* residual, const uint16_t* out, int64_t T, in
   return ok();
 }
 
-// Largest load batch U in {1, 2, 4} whose loaded data fits 96 VGPRs: per
+// Largest ring size U in {1, 2, 4} whose loaded data fits 88 VGPRs: per
 // group NV = 8/V accesses of each of the 1 + S (+ S stored gradients when
 // accumulating) rows, each access max(V/2, 1) registers. With the rest of
-// the kernel this stays under the 128-VGPR budget without spills.
+// the kernel (and the refill of a slot while the next is consumed) this
+// stays under the 128-VGPR budget without spills.
 constexpr int bwd_max_u(int V, int S, bool acc) {
   const int per_group = (kGroup / V) * (1 + (acc ? 2 : 1) * S) * (V >= 2 ? V / 2 : 1);
-  return 4 * per_group <= 96 ? 4 : (2 * per_group <= 96 ? 2 : 1);
+  return 4 * per_group <= 88 ? 4 : (2 * per_group <= 88 ? 2 : 1);
 }
 
 struct BwdPlan {
@@ -1064,6 +1127,46 @@ mhc_status mhc_bf16_rne_probe(uint32_t first_bits, int64_t n, uint16_t* out, voi
     if ((st = launch_error("bf16 probe")) != MHC_SUCCESS) return st;
   }
   return ok();
+}
+
+mhc_status mhc_stream_probe(const void* src, int64_t src_bytes, void* dst, int64_t dst_bytes,
+                            int32_t reads, int32_t writes, void* stream, void* start_event,
+                            void* stop_event) {
+  const int mix = reads * 100 + writes;
+  if (mix != 101 && mix != 401 && mix != 504 && mix != 904)
+    return fail(MHC_ERROR_INVALID_VALUE,
+                "reads:writes must be 1:1, 4:1, 5:4 or 9:4 (got %d:%d)", reads, writes);
+  if (src_bytes < 0 || dst_bytes < 0 || src_bytes % (int64_t(reads) * kProbeChunk) != 0)
+    return fail(MHC_ERROR_INVALID_VALUE,
+                "src_bytes must be a non-negative multiple of reads KiB (got %lld)",
+                (long long)src_bytes);
+  const int64_t units = src_bytes / (int64_t(reads) * kProbeChunk);
+  if (dst_bytes != units * writes * kProbeChunk)
+    return fail(MHC_ERROR_INVALID_VALUE,
+                "dst_bytes must be writes KiB per unit of src (want %lld, got %lld)",
+                (long long)(units * writes * kProbeChunk), (long long)dst_bytes);
+  if (units > 0x7FFFFFFF)
+    return fail(MHC_ERROR_INVALID_VALUE, "too many units (%lld)", (long long)units);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Events ev{static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
+  if (units == 0) return record_empty(ev, s);
+  mhc_status st;
+  if ((st = check_ptr(src, 16, "src")) != MHC_SUCCESS) return st;
+  if ((st = check_ptr(dst, 16, "dst")) != MHC_SUCCESS) return st;
+  const Range in{reinterpret_cast<uintptr_t>(src), reinterpret_cast<uintptr_t>(src) + src_bytes, "src"};
+  const Range out{reinterpret_cast<uintptr_t>(dst), reinterpret_cast<uintptr_t>(dst) + dst_bytes, "dst"};
+  if (overlap(in, out)) return fail(MHC_ERROR_ALIASING, "dst overlaps src");
+  (void)hipGetLastError();
+  const dim3 grid(static_cast<uint32_t>(units));
+  const auto* sp = static_cast<const uint8_t*>(src);
+  auto* dp = static_cast<uint8_t*>(dst);
+  switch (mix) {
+    case 101: hipExtLaunchKernelGGL(stream_probe_kernel<1, 1>, grid, dim3(64), 0, s, ev.start, ev.stop, 0, sp, dp); break;
+    case 401: hipExtLaunchKernelGGL(stream_probe_kernel<4, 1>, grid, dim3(64), 0, s, ev.start, ev.stop, 0, sp, dp); break;
+    case 504: hipExtLaunchKernelGGL(stream_probe_kernel<5, 4>, grid, dim3(64), 0, s, ev.start, ev.stop, 0, sp, dp); break;
+    default: hipExtLaunchKernelGGL(stream_probe_kernel<9, 4>, grid, dim3(64), 0, s, ev.start, ev.stop, 0, sp, dp); break;
+  }
+  return launch_error("stream probe");
 }
 
 }  // extern "C"

@@ -95,8 +95,9 @@ typedef enum mhc_status {
  *   vec_width         bf16 elements per vector access: 1, 2, 4 or 8. It must
  *                     divide H and match the alignment of every bf16 buffer.
  *   units_per_thread  forward: vector units each thread handles; backward:
- *                     8-element groups each lane loads before its
- *                     arithmetic. 1, 2 or 4, at most what the register
+ *                     8-element groups each lane keeps in flight (a ring
+ *                     of loads, each slot refilled with the lane's next
+ *                     group once consumed). 1, 2 or 4, at most what the register
  *                     budget allows for the vec_width, expansion rate and
  *                     streams_per_block (the plan query reports the
  *                     default, which is that maximum in the backward; more
@@ -293,6 +294,27 @@ mhc_status mhc_h_aggregate_plan_bwd_acc(const uint16_t* residual,
  */
 mhc_status mhc_bf16_rne_probe(uint32_t first_bits, int64_t n, uint16_t* out,
                               void* stream);
+
+/*
+ * Streaming probe (measurement utility, not part of the operation): a kernel
+ * that only moves bytes, with the read:write mix of one of the kernels
+ * above and no arithmetic, so that their time can be compared with what a
+ * plain stream of the same bytes takes on this GPU. Per unit it reads
+ * `reads` consecutive KiB of src and writes `writes` consecutive KiB of dst
+ * (one 64-lane block per unit; the written words are the XOR of the unit's
+ * loaded 16-byte vectors, lane by lane, repeated `writes` times).
+ *   reads:writes  1:1 (copy), 4:1 (forward: 8H read, 2H written),
+ *                 5:4 (backward: 10H read, 8H written),
+ *                 9:4 (accumulating backward: 18H read, 8H written).
+ *   src: src_bytes device bytes, 16-byte aligned, a multiple of reads KiB;
+ *   dst: exactly (src_bytes / (reads KiB)) * writes KiB, 16-byte aligned,
+ *   disjoint from src (else MHC_ERROR_ALIASING). start_event / stop_event
+ *   (hipEvent_t or NULL) are attached to the dispatch as in the _timed calls.
+ *   src_bytes == 0 launches nothing and records the events.
+ */
+mhc_status mhc_stream_probe(const void* src, int64_t src_bytes, void* dst,
+                            int64_t dst_bytes, int32_t reads, int32_t writes,
+                            void* stream, void* start_event, void* stop_event);
 
 #ifdef __cplusplus
 }

@@ -231,6 +231,22 @@ def test_probe_rejects_bad_sizes(lib):
     assert lib.mhc_bf16_rne_probe(0, 16, 1025, None) == MHC_ERROR_INVALID_VALUE
 
 
+def test_stream_probe_rejects_bad_arguments_before_any_hip_call(lib):
+    KiB = 1024
+    src, dst = BASE, BASE + GiB
+    probe = lib.mhc_stream_probe
+    for reads, writes in ((2, 1), (5, 5), (0, 1), (4, 4), (-5, 4)):
+        assert probe(src, 20 * KiB, dst, 16 * KiB, reads, writes, None, None,
+                     None) == MHC_ERROR_INVALID_VALUE, (reads, writes)
+    assert probe(src, 5 * KiB + 16, dst, 4 * KiB, 5, 4, None, None, None) == MHC_ERROR_INVALID_VALUE
+    assert probe(src, 10 * KiB, dst, 4 * KiB, 5, 4, None, None, None) == MHC_ERROR_INVALID_VALUE
+    assert probe(src, -5 * KiB, dst, 4 * KiB, 5, 4, None, None, None) == MHC_ERROR_INVALID_VALUE
+    assert probe(src, 10 * KiB, src + 4 * KiB, 8 * KiB, 5, 4, None, None,
+                 None) == MHC_ERROR_ALIASING
+    assert probe(src + 8, 5 * KiB, dst, 4 * KiB, 5, 4, None, None, None) == MHC_ERROR_INVALID_VALUE
+    assert probe(0, 0, 0, 0, 9, 4, None, None, None) == MHC_SUCCESS
+
+
 def test_binding_rejects_host_tensors_without_calling_the_library(lib):
     res = torch.zeros((2, 4, 8), dtype=torch.bfloat16)
     pre = torch.zeros((2, 4), dtype=torch.float32)

@@ -49,6 +49,7 @@ def test_kernels_present(asm):
     assert any("hagg_fwd_kernel" in n for n in names)
     assert any("hagg_bwd_kernel" in n for n in names)
     assert any("bf16_probe_kernel" in n for n in names)
+    assert sum("stream_probe_kernel" in n for n in names) == 4
 
 
 def test_no_fused_or_packed_float_ops(asm):
@@ -65,6 +66,8 @@ def test_separate_fp32_mul_and_add_present(asm):
 
 def test_bf16_results_use_rne_pack_conversion(asm):
     for name, body in kernel_blocks(asm).items():
+        if "stream_probe_kernel" in name:
+            continue  # moves bytes only, produces no bf16 value
         assert "v_cvt_pk_bf16_f32" in body, name
 
 

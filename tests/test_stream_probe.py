@@ -1,0 +1,48 @@
+"""The streaming probe (a measurement utility beside the operation) moves
+exactly the bytes its header describes: per unit, `reads` KiB in and
+`writes` KiB out, each written 16-byte vector the XOR of the unit's loaded
+vectors at that lane, and nothing written outside dst."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import say
+from hyper_connection_residual_mhc_amd import ops
+
+pytestmark = pytest.mark.gpu
+
+KiB = 1024
+
+
+def expected(src: np.ndarray, reads: int, writes: int) -> np.ndarray:
+    """dst words from src words (uint32), written out unit by unit."""
+    units = src.size * 4 // (reads * KiB)
+    x = src.reshape(units, reads, 64, 4)       # unit, chunk, lane, word
+    acc = np.bitwise_xor.reduce(x, axis=1)     # unit, lane, word
+    return np.repeat(acc[:, None], writes, axis=1).reshape(-1)
+
+
+@pytest.mark.parametrize("reads,writes", [(1, 1), (4, 1), (5, 4), (9, 4)])
+@pytest.mark.parametrize("units", [1, 3, 257])
+def test_stream_probe_moves_the_described_bytes(device, reads, writes, units):
+    say(f"stream probe {reads}:{writes} units={units}")
+    rng = np.random.default_rng(reads * 100 + writes + units)
+    src_words = rng.integers(0, 2**32, size=units * reads * KiB // 4, dtype=np.uint64).astype(np.uint32)
+    src = torch.from_numpy(src_words.view(np.int32)).to(device)
+    guard = 4096
+    buf = torch.full((units * writes * KiB // 4 + 2 * guard,), -1, dtype=torch.int32, device=device)
+    dst = buf[guard:guard + units * writes * KiB // 4]
+    ops.mhc_stream_probe(src, dst, reads, writes)
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy().view(np.uint32)
+    assert np.array_equal(got[guard:-guard], expected(src_words, reads, writes))
+    assert (got[:guard] == 0xFFFFFFFF).all() and (got[-guard:] == 0xFFFFFFFF).all()
+
+
+def test_stream_probe_empty_is_a_no_op(device):
+    e = torch.empty(0, dtype=torch.int32, device=device)
+    ops.mhc_stream_probe(e, e, 5, 4)
+    torch.cuda.synchronize()
