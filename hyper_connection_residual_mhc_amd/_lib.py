@@ -15,7 +15,9 @@ MHC_SUCCESS = 0
 MHC_ERROR_INVALID_VALUE = 1
 MHC_ERROR_ALIASING = 2
 MHC_ERROR_HIP = 3
-MHC_ABI_VERSION = 2
+MHC_ABI_VERSION = 3
+MHC_BWD_SPLIT = 1
+MHC_BWD_ROWS = 2
 MHC_MAX_H = 1 << 26
 
 
@@ -27,6 +29,7 @@ class mhc_launch(ctypes.Structure):
         ("units_per_thread", c_int32),
         ("tokens_per_block", c_int32),
         ("streams_per_block", c_int32),
+        ("layout", c_int32),
     ]
 
     def as_dict(self) -> dict:

@@ -122,6 +122,7 @@ template <> __device__ __forceinline__ uint16_t pack<1>(const float (&y)[1]) {
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr int kRsrcFormat = 0x00020000;  // gfx9 resource word 3: raw 32-bit data
 constexpr int kNontemporal = 2;          // cache-policy bit 1: nt
+constexpr int kCached = 0;               // default policy: kept for other readers
 // Cache-policy bit 4 (sc1): device-scope store, written through the L2 at
 // once. Measured with cold caches: the forward (4 bytes read per byte
 // written) streams 5-8% faster with it than with nt; the backward (5:4) and
@@ -135,19 +136,25 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
 
 // Load V bf16 elements at element `off` (per lane) plus `soff` bytes
 // (wave-uniform, carried in a scalar register) into the resource.
+// POL: cache-policy bits (nontemporal unless a row is read by several waves).
 template <int V>
-__device__ __forceinline__ typename Vec<V>::type load_vec(Rsrc rs, uint32_t off, uint32_t soff);
-template <> __device__ __forceinline__ u32x4 load_vec<8>(Rsrc rs, uint32_t off, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b128(rs, off * 2, soff, kNontemporal);
+__device__ __forceinline__ typename Vec<V>::type load_vec(Rsrc rs, uint32_t off, uint32_t soff,
+                                                          int pol = kNontemporal);
+template <> __device__ __forceinline__ u32x4 load_vec<8>(Rsrc rs, uint32_t off, uint32_t soff, int pol) {
+  return pol == kCached ? __builtin_amdgcn_raw_buffer_load_b128(rs, off * 2, soff, kCached)
+                        : __builtin_amdgcn_raw_buffer_load_b128(rs, off * 2, soff, kNontemporal);
 }
-template <> __device__ __forceinline__ u32x2 load_vec<4>(Rsrc rs, uint32_t off, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b64(rs, off * 2, soff, kNontemporal);
+template <> __device__ __forceinline__ u32x2 load_vec<4>(Rsrc rs, uint32_t off, uint32_t soff, int pol) {
+  return pol == kCached ? __builtin_amdgcn_raw_buffer_load_b64(rs, off * 2, soff, kCached)
+                        : __builtin_amdgcn_raw_buffer_load_b64(rs, off * 2, soff, kNontemporal);
 }
-template <> __device__ __forceinline__ uint32_t load_vec<2>(Rsrc rs, uint32_t off, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b32(rs, off * 2, soff, kNontemporal);
+template <> __device__ __forceinline__ uint32_t load_vec<2>(Rsrc rs, uint32_t off, uint32_t soff, int pol) {
+  return pol == kCached ? __builtin_amdgcn_raw_buffer_load_b32(rs, off * 2, soff, kCached)
+                        : __builtin_amdgcn_raw_buffer_load_b32(rs, off * 2, soff, kNontemporal);
 }
-template <> __device__ __forceinline__ uint16_t load_vec<1>(Rsrc rs, uint32_t off, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b16(rs, off * 2, soff, kNontemporal);
+template <> __device__ __forceinline__ uint16_t load_vec<1>(Rsrc rs, uint32_t off, uint32_t soff, int pol) {
+  return pol == kCached ? __builtin_amdgcn_raw_buffer_load_b16(rs, off * 2, soff, kCached)
+                        : __builtin_amdgcn_raw_buffer_load_b16(rs, off * 2, soff, kNontemporal);
 }
 
 // Stores take no scalar offset: the whole byte offset travels in the VGPR.
@@ -441,6 +448,132 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void h
   }
 }
 
+// Row layout of the backward: one wave per (token, stream) row.
+//
+// Grid: ceil(T*n / R) blocks of 64*R threads (R rows per block, R = 1, 2, 4
+// or 8); wave p of block b owns row q = R*b + p of the flattened [T, n] index,
+// i.e. token q / n, stream q % n, and streams that whole row: grad_out row
+// (shared by the n waves of a token, loaded with the default cache policy so
+// the other waves find it in cache), residual row and grad_residual row.
+//
+// The fixed order is unchanged, only its lanes are laid out differently:
+// physical lane j holds accumulator lanes j, j+64, j+128 and j+192 of the
+// 256 (one accumulator each, acc[m] for lane j + 64m). Group k belongs to
+// accumulator lane k mod 256, which is physical lane k mod 64 with
+// m = (k / 64) mod 4; so lane j visits its groups k = j + 64c in ascending
+// c ("chunk" c, one 1-KiB load per row for V = 8) and adds chunk c into
+// acc[c mod 4] - each accumulator lane still sees its groups in ascending
+// order. The wave stage of accumulator wave m is the halving tree over the
+// 64 physical lanes on acc[m]; lane 0 then holds all four wave results and
+// combines them as (y0+y2)+(y1+y3). No LDS, no barrier.
+//
+// Chunks pass through a ring of B register slots (B a multiple of 4, so a
+// slot's accumulator index is a constant): slot b is refilled with chunk
+// c + B as soon as chunk c has been consumed. Chunks past the end of the
+// row read zeros and their stores are dropped (buffer range checks).
+template <int V, int B, bool ACC>
+struct RowSlots {
+  typedef typename Vec<V>::type VT;
+  static constexpr int NV = kGroup / V;
+  VT g[B][NV];
+  VT r[B][NV];
+  VT old[ACC ? B : 1][NV];
+};
+
+template <int V, int B, bool ACC>
+__device__ __forceinline__ void rows_issue(RowSlots<V, B, ACC>& sl, int b, uint32_t k, Rsrc g_row,
+                                           Rsrc r_row, Rsrc gr_row) {
+#pragma unroll
+  for (int v = 0; v < RowSlots<V, B, ACC>::NV; ++v) {
+    const uint32_t h = k * kGroup + v * V;
+    sl.g[b][v] = load_vec<V>(g_row, h, 0, kCached);
+    sl.r[b][v] = load_vec<V>(r_row, h, 0);
+    if constexpr (ACC) sl.old[b][v] = load_vec<V>(gr_row, h, 0);
+  }
+}
+
+template <int V, int B, bool ACC>
+__device__ __forceinline__ void rows_consume(RowSlots<V, B, ACC>& sl, int b, uint32_t k, float w,
+                                             float& acc, Rsrc gr_row) {
+#pragma unroll
+  for (int v = 0; v < RowSlots<V, B, ACC>::NV; ++v) {
+    const uint32_t h = k * kGroup + v * V;
+    float gr[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const float ge = elem<V>(sl.g[b][v], e);
+      gr[e] = w * ge;
+      if constexpr (ACC) gr[e] = elem<V>(sl.old[b][v], e) + gr[e];
+      const float q = ge * elem<V>(sl.r[b][v], e);  // exact in the normal range
+      acc = acc + q;
+    }
+    store_vec<V, kNontemporal>(gr_row, h, pack<V>(gr));
+  }
+}
+
+template <int V, int B, bool ACC>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void hagg_bwd_rows_kernel(
+    const uint16_t* __restrict__ residual, const float* __restrict__ pre,
+    const uint16_t* __restrict__ grad_out, uint16_t* __restrict__ grad_residual,
+    float* __restrict__ grad_pre, int64_t rows, int32_t n, int64_t H, uint32_t ngroups) {
+  static_assert(B % 4 == 0, "ring size must be a multiple of 4");
+  const uint32_t lane = threadIdx.x & 63;
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) +
+                    __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (q >= rows) return;  // the whole wave
+  const int64_t t = q / n;
+  const float w = pre[q];  // pre[t, q mod n]
+  const Rsrc g_row = make_rsrc(grad_out + t * H, 2 * H);
+  const Rsrc r_row = make_rsrc(residual + q * H, 2 * H);
+  const Rsrc gr_row = make_rsrc(grad_residual + q * H, 2 * H);
+
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const uint32_t chunks = (ngroups + 63) / 64;
+  const uint32_t rounds = (chunks + B - 1) / B;
+  RowSlots<V, B, ACC> sl;
+  // The scheduling barriers keep the loads in chunk order (the compiler
+  // would otherwise be free to issue later chunks first, and the first
+  // chunk's arithmetic would wait for most of the ring).
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    rows_issue(sl, b, lane + 64 * b, g_row, r_row, gr_row);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (uint32_t j = 0; j + 1 < rounds; ++j) {
+    const uint32_t k0 = lane + 64 * B * j;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      rows_consume(sl, b, k0 + 64 * b, w, acc[b & 3], gr_row);
+      rows_issue(sl, b, k0 + 64 * (B + b), g_row, r_row, gr_row);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  {
+    const uint32_t k0 = lane + 64 * B * (rounds - 1);
+#pragma unroll
+    for (int b = 0; b < B; ++b) rows_consume(sl, b, k0 + 64 * b, w, acc[b & 3], gr_row);
+  }
+
+  // Wave stage for each accumulator wave m, then the block stage in lane 0.
+#pragma unroll
+  for (int m = 0; m < 4; ++m) acc[m] = acc[m] + from_lane_plus<32>(acc[m]);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) acc[m] = acc[m] + from_lane_plus<16>(acc[m]);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) acc[m] = acc[m] + from_lane_plus<8>(acc[m]);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) acc[m] = acc[m] + from_lane_plus<4>(acc[m]);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) acc[m] = acc[m] + from_lane_plus<2>(acc[m]);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) acc[m] = acc[m] + from_lane_plus<1>(acc[m]);
+  if (lane == 0) {
+    const float y02 = acc[0] + acc[2];
+    const float y13 = acc[1] + acc[3];
+    grad_pre[q] = y02 + y13;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Conversion probe kernel
 // ---------------------------------------------------------------------------
@@ -584,9 +717,10 @@ bool vec_allowed(int V, int64_t H, const void* const* bufs, int nbufs) {
 // 32-bit work-item count); larger problems are split over whole tokens.
 constexpr int64_t kMaxLaunchThreads = int64_t(1) << 31;
 constexpr int64_t kMaxGridY = 65535;
-// Backward streams per block by batch length (see plan_bwd).
+// Backward layout and streams per block by batch length (see plan_bwd).
 constexpr int64_t kTwoStreamsFromT = 128;
 constexpr int64_t kFourStreamsFromT = 512;
+constexpr int64_t kRowsFromT = 512;
 
 // Largest forward batch UPT in {1, 2, 4} whose loaded data (N rows, each
 // access max(V/2, 1) registers) fits 64 VGPRs, within the 128-VGPR budget of
@@ -613,9 +747,9 @@ mhc_status plan_fwd(const uint16_t* residual, const uint16_t* out, int64_t T, in
                   ov->vec_width, (long long)H);
     V = ov->vec_width;
   }
-  if (ov && (ov->tokens_per_block != 0 || ov->streams_per_block != 0))
+  if (ov && (ov->tokens_per_block != 0 || ov->streams_per_block != 0 || ov->layout != 0))
     return fail(MHC_ERROR_INVALID_VALUE,
-                "tokens_per_block and streams_per_block are backward-only fields");
+                "tokens_per_block, streams_per_block and layout are backward-only fields");
   const int64_t upt_units = H / V;  // units per token
   const int max_upt = fwd_max_upt(V, n);
   int upt = 1;
@@ -667,8 +801,24 @@ constexpr int bwd_max_u(int V, int S, bool acc) {
   return 4 * per_group <= 88 ? 4 : (2 * per_group <= 88 ? 2 : 1);
 }
 
+// Largest ring size B in {4, 8, 12} of the row layout whose loaded data fits
+// 96 VGPRs: per chunk NV = 8/V accesses of the grad_out and residual rows
+// (and the stored gradient when accumulating), each max(V/2, 1) registers.
+// Scalar-width accesses (V = 1) hold one element per register and need
+// widening temporaries, so their budget is 64; 0 means the row layout is not
+// available for that shape (the split layout is used).
+constexpr int rows_max_b(int V, bool acc) {
+  const int per_chunk = (kGroup / V) * (acc ? 3 : 2) * (V >= 2 ? V / 2 : 1);
+  const int budget = V == 1 ? 64 : 96;
+  return 12 * per_chunk <= budget ? 12
+         : 8 * per_chunk <= budget ? 8
+         : 4 * per_chunk <= budget ? 4 : 0;
+}
+
 struct BwdPlan {
+  int layout;  // MHC_BWD_SPLIT or MHC_BWD_ROWS
   int V, U, S, tpb, n;
+  int rows_per_block;  // row layout
   bool acc;
   int64_t ngroups, blocks_per_launch, total_blocks;
 };
@@ -685,8 +835,67 @@ mhc_status plan_bwd(const uint16_t* residual, const uint16_t* grad_out,
                   ov->vec_width, (long long)H);
     V = ov->vec_width;
   }
+  // Row layout from kRowsFromT tokens on, unless a split-layout field is set.
+  const bool rows_ok = rows_max_b(V, acc) > 0;
+  const bool split_fields = ov && (ov->tokens_per_block != 0 || ov->streams_per_block != 0);
+  int layout = T >= kRowsFromT && rows_ok && !split_fields ? MHC_BWD_ROWS : MHC_BWD_SPLIT;
+  if (ov && ov->layout != 0) {
+    if (ov->layout != MHC_BWD_SPLIT && ov->layout != MHC_BWD_ROWS)
+      return fail(MHC_ERROR_INVALID_VALUE, "backward layout must be 0, %d or %d", MHC_BWD_SPLIT,
+                  MHC_BWD_ROWS);
+    if (ov->layout == MHC_BWD_ROWS && !rows_ok)
+      return fail(MHC_ERROR_INVALID_VALUE,
+                  "the row layout exceeds the register budget at vec_width %d%s", V,
+                  acc ? ", accumulating" : "");
+    layout = ov->layout;
+  }
+  pl->layout = layout;
+  pl->V = V;
+  pl->n = n;
+  pl->acc = acc;
+  pl->ngroups = (H + kGroup - 1) / kGroup;
+  if (layout == MHC_BWD_ROWS) {
+    // One wave per (token, stream) row, R rows per block: whole tokens per
+    // block (4 rows, 8 at n = 8), so the waves sharing a grad_out row run on
+    // one CU and read it from HBM once; fewer rows per block measured slower.
+    int R = n > 4 ? n : 4;
+    if (ov && ov->block_threads != 0) {
+      if (ov->block_threads != 64 && ov->block_threads != 128 && ov->block_threads != 256 &&
+          ov->block_threads != 512)
+        return fail(MHC_ERROR_INVALID_VALUE,
+                    "row-layout backward block_threads must be 0, 64, 128, 256 or 512");
+      R = ov->block_threads / 64;
+    }
+    if (ov && (ov->tokens_per_block != 0 || ov->streams_per_block != 0))
+      return fail(MHC_ERROR_INVALID_VALUE,
+                  "tokens_per_block and streams_per_block belong to the split layout");
+    // Ring size: 8 chunks in flight (measured fastest at T = 512 to 2048,
+    // on par with 12 at T = 8192), fewer if the register budget requires.
+    const int max_b = rows_max_b(V, acc);
+    int B = max_b < 8 ? max_b : 8;
+    if (ov && ov->units_per_thread != 0) {
+      if (ov->units_per_thread != 4 && ov->units_per_thread != 8 && ov->units_per_thread != 12)
+        return fail(MHC_ERROR_INVALID_VALUE, "row-layout units_per_thread must be 4, 8 or 12");
+      B = ov->units_per_thread;
+      if (B > max_b)
+        return fail(MHC_ERROR_INVALID_VALUE,
+                    "units_per_thread %d exceeds the register budget (at most %d for vec_width "
+                    "%d%s)",
+                    B, max_b, V, acc ? ", accumulating" : "");
+    }
+    pl->U = B;
+    pl->S = 0;
+    pl->tpb = 0;
+    pl->rows_per_block = R;
+    // Whole tokens per launch: blocks_per_launch * R rows is a multiple of n
+    // (R and n are powers of two, n <= 8, and blocks_per_launch is a
+    // multiple of 8).
+    pl->blocks_per_launch = kMaxLaunchThreads / (64 * R);
+    pl->total_blocks = (T * n + R - 1) / R;
+    return ok();
+  }
   if (ov && ov->block_threads != 0 && ov->block_threads != kLanes)
-    return fail(MHC_ERROR_INVALID_VALUE, "backward block_threads must be 0 or 256");
+    return fail(MHC_ERROR_INVALID_VALUE, "split-layout backward block_threads must be 0 or 256");
   // Streams per block: all of a token's streams (up to four) in one block
   // once there are enough tokens to cover the CUs (grad_out is then read once
   // per block); shorter batches spread each token over more blocks to use
@@ -724,13 +933,10 @@ mhc_status plan_bwd(const uint16_t* residual, const uint16_t* grad_out,
       return fail(MHC_ERROR_INVALID_VALUE, "tokens_per_block must be in [1, 4096]");
     tpb = ov->tokens_per_block;
   }
-  pl->V = V;
   pl->U = U;
   pl->S = S;
   pl->tpb = tpb;
-  pl->n = n;
-  pl->acc = acc;
-  pl->ngroups = (H + kGroup - 1) / kGroup;
+  pl->rows_per_block = 0;
   pl->blocks_per_launch = kMaxLaunchThreads / kLanes / (n / S);
   pl->total_blocks = (T + tpb - 1) / tpb * (n / S);
   return ok();
@@ -857,10 +1063,47 @@ template <int V>
 void launch_bwd_v(const BwdPlan& pl, const uint16_t* residual, const float* pre,
                   const uint16_t* grad_out, uint16_t* grad_residual, float* grad_pre,
                   int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
+  if (pl.layout == MHC_BWD_ROWS) {
+    if (pl.acc)
+      launch_rows_a<V, true>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
+    else
+      launch_rows_a<V, false>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
+    return;
+  }
   if (pl.acc)
     launch_bwd_a<V, true>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
   else
     launch_bwd_a<V, false>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
+}
+
+template <int V, int B, bool ACC>
+void launch_rows_t(const BwdPlan& pl, const uint16_t* residual, const float* pre,
+                   const uint16_t* grad_out, uint16_t* grad_residual, float* grad_pre,
+                   int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
+  const int64_t rows = tokens * pl.n;
+  const uint32_t blocks = static_cast<uint32_t>((rows + pl.rows_per_block - 1) / pl.rows_per_block);
+  hipExtLaunchKernelGGL(hagg_bwd_rows_kernel<V, B, ACC>, dim3(blocks),
+                        dim3(64 * pl.rows_per_block), 0, stream, ev.start, ev.stop, 0, residual,
+                        pre, grad_out, grad_residual, grad_pre, rows,
+                        static_cast<int32_t>(pl.n), H, static_cast<uint32_t>(pl.ngroups));
+}
+
+// Instantiates only the ring sizes the register budget allows.
+template <int V, bool ACC>
+void launch_rows_a(const BwdPlan& pl, const uint16_t* residual, const float* pre,
+                   const uint16_t* grad_out, uint16_t* grad_residual, float* grad_pre,
+                   int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
+  constexpr int kMaxB = rows_max_b(V, ACC);
+  if constexpr (kMaxB == 0) {
+    return;  // never planned: the row layout is not available for this shape
+  } else {
+    constexpr int kB8 = kMaxB < 8 ? kMaxB : 8;
+    switch (pl.U) {
+      case 4: launch_rows_t<V, 4, ACC>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
+      case 8: launch_rows_t<V, kB8, ACC>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
+      default: launch_rows_t<V, kMaxB, ACC>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
+    }
+  }
 }
 
 // Events of the i-th of n launches of one call: start on the first, stop on
@@ -915,7 +1158,9 @@ mhc_status run_bwd(const uint16_t* residual, const float* pre, const uint16_t* g
   BwdPlan pl;
   if ((st = plan_bwd(residual, grad_out, grad_residual, T, n, H, acc, launch, &pl)) != MHC_SUCCESS)
     return st;
-  const int64_t tokens_per_launch = pl.blocks_per_launch * pl.tpb;
+  const int64_t tokens_per_launch = pl.layout == MHC_BWD_ROWS
+                                        ? pl.blocks_per_launch * pl.rows_per_block / n
+                                        : pl.blocks_per_launch * pl.tpb;
   (void)hipGetLastError();
   for (int64_t t0 = 0; t0 < T; t0 += tokens_per_launch) {
     const int64_t m = (T - t0 < tokens_per_launch) ? T - t0 : tokens_per_launch;
@@ -943,7 +1188,7 @@ mhc_status plan_fwd_query(const uint16_t* residual, const float* pre, const uint
   if (st != MHC_SUCCESS) return st;
   FwdPlan pl;
   if ((st = plan_fwd(residual, out, T, n, H, launch, &pl)) != MHC_SUCCESS) return st;
-  if (plan) *plan = mhc_launch{pl.block, pl.V, pl.upt, 0, 0};
+  if (plan) *plan = mhc_launch{pl.block, pl.V, pl.upt, 0, 0, 0};
   if (grid_blocks) *grid_blocks = pl.total_blocks;
   return ok();
 }
@@ -958,7 +1203,10 @@ mhc_status plan_bwd_query(const uint16_t* residual, const float* pre, const uint
   if ((st = plan_bwd(residual, grad_out, grad_residual, T, n, H, acc, launch, &pl)) !=
       MHC_SUCCESS)
     return st;
-  if (plan) *plan = mhc_launch{kLanes, pl.V, pl.U, pl.tpb, pl.S};
+  if (plan)
+    *plan = pl.layout == MHC_BWD_ROWS
+                ? mhc_launch{64 * pl.rows_per_block, pl.V, pl.U, 0, 0, MHC_BWD_ROWS}
+                : mhc_launch{kLanes, pl.V, pl.U, pl.tpb, pl.S, MHC_BWD_SPLIT};
   if (grid_blocks) *grid_blocks = pl.total_blocks;
   return ok();
 }

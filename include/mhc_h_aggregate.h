@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define MHC_ABI_VERSION 2
+#define MHC_ABI_VERSION 3
 
 /* Hyper-connection expansion rate of the page's operation (Summary: residual
  * [T, 4, H]). The *_n entry points below also take 2 and 8. */
@@ -90,24 +90,36 @@ typedef enum mhc_status {
  * with every field filled in. No field changes any result bit: they exist so
  * that tests can prove that and benchmarks can sweep shapes.
  *   block_threads     forward: threads per block, a multiple of 64 in
- *                     [64, 1024]; backward: must be 0 or 256 (one block of
- *                     4 waves owns a token's reduction).
+ *                     [64, 1024]. Backward, split layout: 0 or 256 (one
+ *                     block of 4 waves owns a token's reduction); row
+ *                     layout: 64, 128, 256 or 512 (1, 2, 4 or 8 rows per
+ *                     block; default whole tokens: 256, 512 at n = 8).
  *   vec_width         bf16 elements per vector access: 1, 2, 4 or 8. It must
  *                     divide H and match the alignment of every bf16 buffer.
- *   units_per_thread  forward: vector units each thread handles; backward:
- *                     8-element groups each lane keeps in flight (a ring
- *                     of loads, each slot refilled with the lane's next
- *                     group once consumed). 1, 2 or 4, at most what the register
- *                     budget allows for the vec_width, expansion rate and
- *                     streams_per_block (the plan query reports the
- *                     default, which is that maximum in the backward; more
- *                     gives MHC_ERROR_INVALID_VALUE).
- *   tokens_per_block  backward only: tokens one block handles in sequence,
- *                     1..4096.
- *   streams_per_block backward only: residual streams one block handles,
- *                     1, 2 or 4. The summation order is defined per
- *                     (token, stream), so a token's streams may be spread
- *                     over blocks without any change in the result.
+ *   units_per_thread  forward: vector units each thread handles (1, 2 or
+ *                     4). Backward: 8-element groups each lane keeps in
+ *                     flight, a ring of loads whose slots are refilled with
+ *                     the lane's next group once consumed - 1, 2 or 4 in
+ *                     the split layout, 4, 8 or 12 in the row layout (whose
+ *                     default is 8). At
+ *                     most what the register budget allows for the
+ *                     vec_width, expansion rate and streams_per_block (the
+ *                     plan query reports the default, which is that maximum
+ *                     in the backward; more gives MHC_ERROR_INVALID_VALUE).
+ *   tokens_per_block  backward split layout only: tokens one block handles
+ *                     in sequence, 1..4096.
+ *   streams_per_block backward split layout only: residual streams one
+ *                     block handles, 1, 2 or 4. The summation order is
+ *                     defined per (token, stream), so a token's streams may
+ *                     be spread over blocks without any change in the
+ *                     result.
+ *   layout            backward only: MHC_BWD_SPLIT (a token's 256
+ *                     accumulator lanes are the 256 threads of one block)
+ *                     or MHC_BWD_ROWS (one wave streams one (token, stream)
+ *                     row; each of its 64 lanes holds accumulator lanes
+ *                     j, j+64, j+128, j+192 and the 64-lane trees run inside
+ *                     the wave). The policy takes the row layout from
+ *                     T = 512 on. Same summation order, same bits.
  * Forward calls reject non-zero backward-only fields.
  */
 typedef struct mhc_launch {
@@ -116,7 +128,12 @@ typedef struct mhc_launch {
   int32_t units_per_thread;
   int32_t tokens_per_block;
   int32_t streams_per_block;
+  int32_t layout;
 } mhc_launch;
+
+/* Backward layouts (mhc_launch.layout); both compute the same bits. */
+#define MHC_BWD_SPLIT 1 /* a token's 256 accumulator lanes over a block's 4 waves */
+#define MHC_BWD_ROWS 2  /* one wave per (token, stream) row, 4 lanes per wave lane */
 
 /* Version of this ABI (MHC_ABI_VERSION of the built library). */
 int mhc_abi_version(void);

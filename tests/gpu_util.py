@@ -11,6 +11,7 @@ from hyper_connection_residual_mhc_amd.workloads import (bf16_tensor_to_bits, bi
                                                          to_device)
 
 HC = 4
+SPLIT, ROWS = 1, 2                 # backward layouts (MHC_BWD_SPLIT, MHC_BWD_ROWS)
 SENTINELS = (0x7FC1, 0xFFEE)      # bf16 NaN patterns the kernels never produce
 GUARD = 2048                       # elements of guard region on each side
 

@@ -181,10 +181,10 @@ def test_forward_overrides(lib):
                                                                    "vec_width": 2,
                                                                    "units_per_thread": 4})
     assert plan == {"block_threads": 1024, "vec_width": 2, "units_per_thread": 4,
-                    "tokens_per_block": 0, "streams_per_block": 0}
+                    "tokens_per_block": 0, "streams_per_block": 0, "layout": 0}
     for bad in ({"block_threads": 100}, {"block_threads": 2048}, {"vec_width": 3},
                 {"units_per_thread": 3}, {"units_per_thread": 9}, {"tokens_per_block": 2},
-                {"streams_per_block": 1}):
+                {"streams_per_block": 1}, {"layout": 2}):
         with pytest.raises(MhcError, match="INVALID_VALUE"):
             ops.mhc_h_aggregate_plan_fwd(r, p, o, T, H, launch=bad)
     with pytest.raises(MhcError, match="vec_width 8 not allowed"):
@@ -196,31 +196,55 @@ def test_forward_overrides(lib):
 def test_backward_plan_and_overrides(lib):
     T, H = 2048, 7168
     r, p, g, gr, gp = bwd_ptrs(T, H)
+    SPLIT, ROWS = _lib.MHC_BWD_SPLIT, _lib.MHC_BWD_ROWS
+    # long batches: one wave per (token, stream) row, a token per 256-thread block
     plan, grid = ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T, H)
-    assert plan["block_threads"] == 256 and plan["vec_width"] == 8
-    assert plan["units_per_thread"] == 4 and plan["streams_per_block"] == 4
-    assert grid == -(-T // plan["tokens_per_block"])
+    assert plan == {"block_threads": 256, "vec_width": 8, "units_per_thread": 8,
+                    "tokens_per_block": 0, "streams_per_block": 0, "layout": ROWS}
+    assert grid == T
+    plan, grid = ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T, H,
+                                              launch={"layout": ROWS, "block_threads": 64,
+                                                      "units_per_thread": 12})
+    assert plan["block_threads"] == 64 and plan["units_per_thread"] == 12 and grid == 4 * T
+    # the split layout, asked for or implied by its own fields
+    plan, grid = ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T, H, launch={"layout": SPLIT})
+    assert plan == {"block_threads": 256, "vec_width": 8, "units_per_thread": 4,
+                    "tokens_per_block": 1, "streams_per_block": 4, "layout": SPLIT}
+    assert grid == T
     plan, grid = ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T, H,
                                               launch={"tokens_per_block": 3, "vec_width": 4,
                                                       "units_per_thread": 1})
+    assert plan["layout"] == SPLIT
     assert plan["tokens_per_block"] == 3 and plan["vec_width"] == 4 and grid == -(-T // 3)
     plan, grid = ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T, H,
                                               launch={"streams_per_block": 2})
-    assert plan["streams_per_block"] == 2 and grid == 2 * T
-    # short batches spread each token's streams over more blocks
-    for T_, spb in ((8, 1), (127, 1), (128, 2), (511, 2), (512, 4)):
+    assert plan["streams_per_block"] == 2 and plan["layout"] == SPLIT and grid == 2 * T
+    # short batches spread each token's streams over more blocks (split layout)
+    for T_, spb in ((8, 1), (127, 1), (128, 2), (511, 2)):
         plan, grid = ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T_, H)
+        assert plan["layout"] == SPLIT, (T_, plan)
         assert plan["streams_per_block"] == spb and grid == T_ * (4 // spb), (T_, plan)
-    for bad in ({"block_threads": 128}, {"tokens_per_block": 5000}, {"vec_width": 16},
-                {"units_per_thread": 3}, {"streams_per_block": 3}):
+    plan, grid = ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, 512, H)
+    assert plan["layout"] == ROWS and grid == 512
+    for bad in ({"block_threads": 100}, {"tokens_per_block": 5000}, {"vec_width": 16},
+                {"units_per_thread": 3}, {"streams_per_block": 3}, {"layout": 3},
+                {"tokens_per_block": 1, "block_threads": 128},
+                {"layout": ROWS, "block_threads": 1024}, {"layout": ROWS, "units_per_thread": 2},
+                {"layout": ROWS, "tokens_per_block": 1}, {"layout": ROWS, "streams_per_block": 4},
+                {"layout": SPLIT, "block_threads": 64}):
         with pytest.raises(MhcError, match="INVALID_VALUE"):
             ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T, H, launch=bad)
     with pytest.raises(MhcError, match="exceeds the register budget"):
         ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T, H,
-                                     launch={"vec_width": 1, "units_per_thread": 4})
+                                     launch={"vec_width": 1, "units_per_thread": 4,
+                                             "layout": SPLIT})
+    with pytest.raises(MhcError, match="exceeds the register budget"):
+        ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T, H,
+                                     launch={"vec_width": 1, "units_per_thread": 8,
+                                             "layout": ROWS})
     # grad_out misaligned by one element forces the scalar path
     plan, _ = ops.mhc_h_aggregate_plan_bwd(r, p, g + 2, gr, gp, T, H)
-    assert plan["vec_width"] == 1
+    assert plan["vec_width"] == 1 and plan["layout"] == ROWS and plan["units_per_thread"] == 4
 
 
 def test_probe_rejects_bad_sizes(lib):
@@ -283,17 +307,30 @@ def test_missing_library_raises_import_error(monkeypatch, tmp_path):
 
 
 def test_accumulating_backward_plan(lib):
-    """The accumulating backward also loads the stored gradient, so its load
-    batch is smaller where the register budget requires it; it follows the
-    same streams-per-block policy and the same argument rules."""
+    """The accumulating backward also loads the stored gradient, so its ring
+    is smaller where the register budget requires it; it follows the same
+    layout and streams-per-block policy and the same argument rules."""
     T, H = 2048, 7168
     r, p, g, gr, gp = bwd_ptrs(T, H)
+    SPLIT, ROWS = _lib.MHC_BWD_SPLIT, _lib.MHC_BWD_ROWS
     plan, grid = ops.mhc_h_aggregate_plan_bwd_acc(r, p, g, gr, gp, T, H)
+    assert plan["layout"] == ROWS and plan["units_per_thread"] == 8 and grid == T
+    plan, grid = ops.mhc_h_aggregate_plan_bwd_acc(r, p, g, gr, gp, T, H, launch={"layout": SPLIT})
     assert plan["streams_per_block"] == 4 and plan["units_per_thread"] == 2 and grid == T
     plan, _ = ops.mhc_h_aggregate_plan_bwd_acc(r, p, g, gr, gp, 64, H)
+    assert plan["layout"] == SPLIT
     assert plan["streams_per_block"] == 1 and plan["units_per_thread"] == 4
     with pytest.raises(MhcError, match="exceeds the register budget"):
-        ops.mhc_h_aggregate_plan_bwd_acc(r, p, g, gr, gp, T, H, launch={"units_per_thread": 4})
+        ops.mhc_h_aggregate_plan_bwd_acc(r, p, g, gr, gp, T, H,
+                                         launch={"units_per_thread": 4, "layout": SPLIT})
+    with pytest.raises(MhcError, match="exceeds the register budget"):
+        ops.mhc_h_aggregate_plan_bwd_acc(r, p, g, gr, gp, T, H,
+                                         launch={"units_per_thread": 12, "layout": ROWS})
+    # scalar accesses: the row layout does not fit the budget, the policy splits
+    plan, _ = ops.mhc_h_aggregate_plan_bwd_acc(r, p, g + 2, gr, gp, T, H)
+    assert plan["vec_width"] == 1 and plan["layout"] == SPLIT
+    with pytest.raises(MhcError, match="row layout exceeds the register budget"):
+        ops.mhc_h_aggregate_plan_bwd_acc(r, p, g + 2, gr, gp, T, H, launch={"layout": ROWS})
     with pytest.raises(MhcError, match="ALIASING"):
         ops.mhc_h_aggregate_plan_bwd_acc(r, p, g, r, gp, T, H)
     assert lib.mhc_h_aggregate_bwd_acc(r, p, g, gr, gr, T, H, None, None, None,
@@ -319,9 +356,16 @@ def test_expansion_rate_rules(lib):
     with pytest.raises(MhcError, match="ALIASING"):
         ops.mhc_h_aggregate_plan_fwd_n(r, r + 8 * T * H * 2, r + 8 * T * H, T, 8, H)
     rr, pp, g, gr, gp = bwd_ptrs(1024, H * 2)
+    # row layout: four rows per block (two tokens at n = 2), eight at n = 8
     plan, grid = ops.mhc_h_aggregate_plan_bwd_n(rr, pp, g, gr, gp, 1024, 2, H)
-    assert plan["streams_per_block"] == 2 and grid == 1024
+    assert plan["block_threads"] == 256 and grid == 512
     plan, grid = ops.mhc_h_aggregate_plan_bwd_n(rr, pp, g, gr, gp, 1024, 8, H)
+    assert plan["block_threads"] == 512 and grid == 1024
+    plan, grid = ops.mhc_h_aggregate_plan_bwd_n(rr, pp, g, gr, gp, 1024, 2, H,
+                                                launch={"layout": _lib.MHC_BWD_SPLIT})
+    assert plan["streams_per_block"] == 2 and grid == 1024
+    plan, grid = ops.mhc_h_aggregate_plan_bwd_n(rr, pp, g, gr, gp, 1024, 8, H,
+                                                launch={"layout": _lib.MHC_BWD_SPLIT})
     assert plan["streams_per_block"] == 4 and grid == 2048
     with pytest.raises(MhcError, match="exceeds the 2 streams"):
         ops.mhc_h_aggregate_plan_bwd_n(rr, pp, g, gr, gp, 8, 2, H,

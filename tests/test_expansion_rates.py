@@ -74,8 +74,9 @@ def test_backward_n_bit_exact(device, n, T, H):
 
 
 @pytest.mark.parametrize("n", [2, 8])
-def test_backward_n_accumulate_bit_exact(device, n):
-    T, H = 300, 7168
+@pytest.mark.parametrize("T", [300, 1031])
+def test_backward_n_accumulate_bit_exact(device, n, T):
+    H = 7168
     say(f"accumulate n={n}")
     host = make_inputs(T, H, seed=70 + n, hc=n, grad=True)
     old = make_inputs(T, H, seed=71 + n, hc=n)["residual"]
@@ -124,6 +125,18 @@ def test_n_every_launch_shape_same_bytes(device, n):
         gr, gp = bwd_n(host, device, launch=launch)
         assert_bytes_equal(gr, want_gr, f"grad_residual {launch}")
         assert_bytes_equal(gp, want_gp, f"grad_pre {launch}")
+    old = make_inputs(T, H, seed=99 + n, hc=n)["residual"]
+    want_acc_gr, want_acc_gp = O.h_aggregate_bwd_acc(host["residual"], host["pre"],
+                                                     host["grad_out"], old)
+    for v, bt in itertools.product((2, 4, 8), (64, 128, 256, 512)):
+        launch = {"layout": 2, "vec_width": v, "block_threads": bt}
+        say(f"backward n={n} {launch}")
+        gr, gp = bwd_n(host, device, launch=launch)
+        assert_bytes_equal(gr, want_gr, f"grad_residual {launch}")
+        assert_bytes_equal(gp, want_gp, f"grad_pre {launch}")
+        gr, gp = bwd_n(host, device, old=old, launch=launch)
+        assert_bytes_equal(gr, want_acc_gr, f"accumulated grad_residual {launch}")
+        assert_bytes_equal(gp, want_acc_gp, f"accumulated grad_pre {launch}")
 
 
 @pytest.mark.parametrize("n", [2, 8])

@@ -76,7 +76,7 @@ def test_accumulate_twice_is_two_roundings(device):
     assert_bytes_equal(bf16_tensor_to_bits(gr), twice, "twice")
 
 
-@pytest.mark.parametrize("T,H", [(37, 7168), (9, 1279)])
+@pytest.mark.parametrize("T,H", [(37, 7168), (9, 1279), (6, 4100)])
 def test_accumulate_every_launch_shape_same_bytes(device, T, H):
     host = make_inputs(T, H, seed=8, grad=True)
     old = make_inputs(T, H, seed=9)["residual"]
@@ -95,6 +95,13 @@ def test_accumulate_every_launch_shape_same_bytes(device, T, H):
             gr, gp = run_acc(host, old, device, launch=launch)
             assert_bytes_equal(gr, want_gr, f"grad_residual {launch}")
             assert_bytes_equal(gp, want_gp, f"grad_pre {launch}")
+    # row layout (not available at vec_width 1: register budget)
+    for v, u, bt in itertools.product([w for w in widths if w > 1], (4, 8), (64, 256, 512)):
+        launch = {"layout": 2, "vec_width": v, "units_per_thread": u, "block_threads": bt}
+        say(f"accumulate launch {launch} T={T} H={H}")
+        gr, gp = run_acc(host, old, device, launch=launch)
+        assert_bytes_equal(gr, want_gr, f"grad_residual {launch}")
+        assert_bytes_equal(gp, want_gp, f"grad_pre {launch}")
 
 
 def test_accumulate_batch_split(device):

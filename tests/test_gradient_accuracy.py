@@ -13,7 +13,7 @@ import pytest
 import torch
 
 from conftest import assert_bytes_equal
-from gpu_util import offset_copy_bf16, run_bwd, say
+from gpu_util import ROWS, SPLIT, offset_copy_bf16, run_bwd, say
 from hyper_connection_residual_mhc_amd import ops
 from hyper_connection_residual_mhc_amd.workloads import (bf16_tensor_to_bits, make_inputs,
                                                          to_device)
@@ -47,15 +47,16 @@ def test_backward_bit_exact_page_shapes(device, T, H):
     check_bwd(host, gr, gp, f"T={T} H={H}")
 
 
+@pytest.mark.parametrize("layout", [SPLIT, ROWS])
 @pytest.mark.parametrize("H", [1, 2, 3, 7, 8, 9, 15, 16, 17, 100, 511, 512, 513, 1276, 1278, 2047,
-                               2048, 2049, 2056, 4100, 16392, 20001])
-def test_backward_bit_exact_ragged_hidden_sizes(device, H):
+                               2048, 2049, 2056, 4100, 6152, 16392, 20001])
+def test_backward_bit_exact_ragged_hidden_sizes(device, H, layout):
     """Short and long rows: fewer groups than lanes, exactly one group per
-    lane, several rounds per lane (H > 2048), short last groups, every
-    vector width."""
-    say(f"backward ragged H={H}")
+    lane, several rounds per lane (H > 2048), short last groups, a partial
+    last ring round, every vector width; both layouts."""
+    say(f"backward ragged H={H} layout={layout}")
     host = make_inputs(4, H, seed=H, grad=True)
-    gr, gp = run_bwd(host, device)
+    gr, gp = run_bwd(host, device, launch={"layout": layout})
     check_bwd(host, gr, gp, f"H={H}")
 
 

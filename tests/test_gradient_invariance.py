@@ -17,7 +17,7 @@ import pytest
 import torch
 
 from conftest import assert_bytes_equal
-from gpu_util import GUARD, SENTINELS, guarded_empty_bf16, guards_untouched, run_bwd, say
+from gpu_util import GUARD, ROWS, SENTINELS, SPLIT, guarded_empty_bf16, guards_untouched, run_bwd, say
 from hyper_connection_residual_mhc_amd import ops
 from hyper_connection_residual_mhc_amd.workloads import bf16_tensor_to_bits, make_inputs, to_device
 from oracle import h_aggregate as O
@@ -44,6 +44,7 @@ def test_backward_100_repeats_byte_identical(device):
 
 
 @pytest.mark.parametrize("T,H,splits", [(2048, 7168, (1, 7, 129, 1911)),
+                                        (1500, 7168, (600, 3, 897)),
                                         (129, 4096, (1,) * 129),
                                         (3, 1279, (1, 1, 1))])
 def test_backward_batch_split(device, T, H, splits):
@@ -79,6 +80,15 @@ def test_backward_every_launch_shape_gives_the_same_bytes(device, T, H):
         gr, gp = run_bwd(host, device, launch=launch)
         assert_bytes_equal(gr, want_gr, f"grad_residual {launch}")
         assert_bytes_equal(gp, want_gp, f"grad_pre {launch}")
+    # row layout: one wave per (token, stream) row
+    for v, u, bt in itertools.product(widths, (4, 8, 12), (64, 128, 256, 512)):
+        if v == 1 and u > 4:
+            continue   # rejected by the plan (register budget)
+        launch = {"layout": ROWS, "vec_width": v, "units_per_thread": u, "block_threads": bt}
+        say(f"backward launch {launch} T={T} H={H}")
+        gr, gp = run_bwd(host, device, launch=launch)
+        assert_bytes_equal(gr, want_gr, f"grad_residual {launch}")
+        assert_bytes_equal(gp, want_gp, f"grad_pre {launch}")
 
 
 def test_backward_canaries(device):
@@ -90,7 +100,10 @@ def test_backward_canaries(device):
     res = []
     for s in SENTINELS:
         for launch in (None, {"vec_width": 2, "tokens_per_block": 4}, {"vec_width": 1},
-                       {"streams_per_block": 1}, {"streams_per_block": 2, "tokens_per_block": 3}):
+                       {"streams_per_block": 1}, {"streams_per_block": 2, "tokens_per_block": 3},
+                       {"layout": ROWS}, {"layout": ROWS, "vec_width": 1},
+                       {"layout": ROWS, "block_threads": 64, "units_per_thread": 12},
+                       {"layout": ROWS, "block_threads": 512, "vec_width": 2}):
             say(f"backward canary 0x{s:x} {launch}")
             gr, grbuf = guarded_empty_bf16((T, 4, H), device, s)
             gpbuf = torch.full((T * 4 + 2 * GUARD,), float("nan"), dtype=torch.float32, device=device)
