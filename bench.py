@@ -244,27 +244,31 @@ def run_gpu(T: int, H: int, steps: int, warmup: int, nsets: int, probe: bool,
     bwd_us = [ev.elapsed_us(4 * j + 2, 4 * j + 3) for j in range(len(sampled))]
     ev.close()
 
-    # Ceiling: the backward and a streaming probe with its read:write byte
-    # mix and no arithmetic, alternating, every launch timed by its own
-    # dispatch events, each from cold buffers. Outside the timed steps.
+    # Reference: the backward alone, then a streaming probe with its
+    # read:write byte mix and no arithmetic, each back to back from cold
+    # buffers, every launch timed by its own dispatch events. Outside the
+    # timed steps.
     probe = ProbeBuffers(bwd_bytes(T, H), PROBE_MIX["bwd"], nsets, dev)
     n_ceil = 200
-    cev = HipEvents(4 * n_ceil)
+    cev = HipEvents(2 * n_ceil)
     C = cev.handles
-    for k in range(10):
-        _lib.check(bwd(*bargs[k % nsets]) | probe.call(lib, k, sh, None, None))
-    torch.cuda.synchronize()
-    for k in range(n_ceil):
-        _lib.check(bwd_t(*bargs[k % nsets], None, C[4 * k], C[4 * k + 1]) |
-                   probe.call(lib, k, sh, C[4 * k + 2], C[4 * k + 3]))
-    torch.cuda.synchronize()
-    ceil_kernel_us = [cev.elapsed_us(4 * k, 4 * k + 1) for k in range(n_ceil)]
-    ceil_probe_us = [cev.elapsed_us(4 * k + 2, 4 * k + 3) for k in range(n_ceil)]
+
+    def back_to_back(fn) -> list[float]:
+        for k in range(10):
+            _lib.check(fn(k, None, None))
+        torch.cuda.synchronize()
+        for k in range(n_ceil):
+            _lib.check(fn(k, C[2 * k], C[2 * k + 1]))
+        torch.cuda.synchronize()
+        return [cev.elapsed_us(2 * k, 2 * k + 1) for k in range(n_ceil)]
+
+    ceil_kernel_us = back_to_back(lambda k, a, b: bwd_t(*bargs[k % nsets], None, a, b))
+    ceil_probe_us = back_to_back(lambda k, a, b: probe.call(lib, k, sh, a, b))
     cev.close()
     probe_bytes = probe.bytes
     del probe
     return {
-        "ceiling": {"kernel_us": ceil_kernel_us, "probe_us": ceil_probe_us,
+        "probe": {"kernel_us": ceil_kernel_us, "probe_us": ceil_probe_us,
                     "probe_bytes": probe_bytes},
         "wall_s": t1 - t0,
         "timed_launches": len(sampled),
@@ -278,15 +282,16 @@ def run_gpu(T: int, H: int, steps: int, warmup: int, nsets: int, probe: bool,
     }
 
 
-def ceiling_record(kernel_bytes: int, c: dict) -> dict:
+def probe_record(kernel_bytes: int, c: dict) -> dict:
     k = statistics.fmean(c["kernel_us"])
     p = statistics.fmean(c["probe_us"])
     kg = kernel_bytes / k / 1e3
     pg = c["probe_bytes"] / p / 1e3
     return {
         "kind": "mhc_stream_probe: the backward's 5:4 read:write byte mix as a plain "
-                "stream, no arithmetic; launched alternately with the backward, every "
-                "launch timed by its own dispatch events, cold buffers",
+                "stream (one 64-lane block per 5 KiB read + 4 KiB written), no "
+                "arithmetic; the backward and the probe each timed back to back by "
+                "their own dispatch events, cold buffers",
         "probe_bytes": c["probe_bytes"],
         "probe_us": round(p, 3),
         "probe_gbps": round(pg, 1),
@@ -314,8 +319,8 @@ def run_sweep(path: str, rounds: int = 7, warm: int = 10, timed: int = 100) -> N
     sees, as in the page's table. `rounds` rounds of `warm` untimed and
     `timed` timed launches; p20 / median / p80 are taken over the round
     medians, GB/s from the median. At T >= 1024 a streaming probe with the
-    kernel's read:write byte mix is launched alternately with the kernel and
-    timed the same way (the ceiling column)."""
+    kernel's read:write byte mix is timed the same way in each round, in a
+    block of its own after the kernel's (the reference column)."""
     import statistics as st
     import torch
     from hyper_connection_residual_mhc_amd import _lib, ops
@@ -324,7 +329,7 @@ def run_sweep(path: str, rounds: int = 7, warm: int = 10, timed: int = 100) -> N
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sh = int(torch.cuda.current_stream(dev).cuda_stream)
-    ev = HipEvents(4 * timed)
+    ev = HipEvents(2 * timed)
     E = ev.handles
 
     def summary(per_round: list[list[float]]) -> tuple[float, list[float], float]:
@@ -374,20 +379,21 @@ def run_sweep(path: str, rounds: int = 7, warm: int = 10, timed: int = 100) -> N
                 probe = (ProbeBuffers(nbytes, PROBE_MIX[direction], nsets, dev)
                          if T >= 1024 else None)
                 k_rounds, p_rounds = [], []
+                runs = [(call, k_rounds)]
+                if probe:
+                    runs.append((lambda k, a, b: probe.call(lib, k, sh, a, b), p_rounds))
                 for _ in range(rounds):
-                    for k in range(warm):
-                        _lib.check(call(k, None, None))
-                        if probe:
-                            _lib.check(probe.call(lib, k, sh, None, None))
-                    torch.cuda.synchronize()
-                    for k in range(timed):
-                        _lib.check(call(k, E[4 * k], E[4 * k + 1]))
-                        if probe:
-                            _lib.check(probe.call(lib, k, sh, E[4 * k + 2], E[4 * k + 3]))
-                    torch.cuda.synchronize()
-                    k_rounds.append([ev.elapsed_us(4 * k, 4 * k + 1) for k in range(timed)])
-                    if probe:
-                        p_rounds.append([ev.elapsed_us(4 * k + 2, 4 * k + 3) for k in range(timed)])
+                    # The kernel's launches, then the probe's: each block runs
+                    # back to back after its own warm-up, so neither inherits
+                    # the other's write-back.
+                    for fn, out in runs:
+                        for k in range(warm):
+                            _lib.check(fn(k, None, None))
+                        torch.cuda.synchronize()
+                        for k in range(timed):
+                            _lib.check(fn(k, E[2 * k], E[2 * k + 1]))
+                        torch.cuda.synchronize()
+                        out.append([ev.elapsed_us(2 * k, 2 * k + 1) for k in range(timed)])
                 med, q, mean = summary(k_rounds)
                 rec = {"direction": direction, "T": T, "H": H, "bytes": nbytes,
                        "us_median": round(med, 3), "us_p20_p50_p80": q,
@@ -557,7 +563,7 @@ def main() -> int:
             "traffic": recorded_traffic(),
             "kernel": "hagg_bwd_kernel (backward)",
         },
-        "ceiling": ceiling_record(bwd_bytes(T, H), g["ceiling"]),
+        "stream_probe": probe_record(bwd_bytes(T, H), g["probe"]),
         "timing": {"per_kernel": "HIP events attached to the dispatches of every "
                                  f"{args.time_every}th step ({g['timed_launches']} launches "
                                  "of each kernel)",

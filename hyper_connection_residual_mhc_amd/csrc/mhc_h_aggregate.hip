@@ -199,7 +199,7 @@ __device__ __forceinline__ void store_vec(Rsrc rs, uint32_t off, const typename 
 template <int V, int UPT, int N>
 __global__ __launch_bounds__(1024) void hagg_fwd_kernel(
     const uint16_t* __restrict__ residual, const float* __restrict__ pre,
-    uint16_t* __restrict__ out, int64_t H, uint32_t units_per_token) {
+    uint16_t* __restrict__ out, int64_t H, uint32_t block_threads) {
   typedef typename Vec<V>::type VT;
   const uint32_t c = blockIdx.x;
   const uint32_t t = blockIdx.y;
@@ -208,44 +208,43 @@ __global__ __launch_bounds__(1024) void hagg_fwd_kernel(
   float w[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) w[i] = p[i];
-  // The token's N residual rows (2NH bytes) and its output row (2H bytes).
-  const Rsrc res = make_rsrc(residual + static_cast<int64_t>(t) * N * H, 2 * N * H);
+  // One resource per row: the token's N residual rows and its output row
+  // (2H bytes each). Units past the end of the row read zeros and their
+  // stores are dropped by the range check, so no lane branches: every
+  // argument is fetched at once and the loads issue right after.
+  Rsrc res[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) res[i] = make_rsrc(residual + (static_cast<int64_t>(t) * N + i) * H, 2 * H);
   const Rsrc o = make_rsrc(out + static_cast<int64_t>(t) * H, 2 * H);
-  const uint32_t row = 2 * static_cast<uint32_t>(H);  // bytes between residual streams
 
-  const uint32_t first = c * blockDim.x * UPT + threadIdx.x;
+  const uint32_t first = c * block_threads * UPT + threadIdx.x;
 
   VT x[N][UPT];
 #pragma unroll
   for (int k = 0; k < UPT; ++k) {
-    const uint32_t u = first + k * blockDim.x;
-    if (u < units_per_token) {
-      const uint32_t h = u * V;
+    const uint32_t h = (first + k * block_threads) * V;
 #pragma unroll
-      for (int i = 0; i < N; ++i) x[i][k] = load_vec<V>(res, h, i * row);
-    }
+    for (int i = 0; i < N; ++i) x[i][k] = load_vec<V>(res[i], h, 0);
   }
 #pragma unroll
   for (int k = 0; k < UPT; ++k) {
-    const uint32_t u = first + k * blockDim.x;
-    if (u < units_per_token) {
-      float y[V];
+    const uint32_t h = (first + k * block_threads) * V;
+    float y[V];
 #pragma unroll
-      for (int e = 0; e < V; ++e) {
-        // Separate fp32 round-to-nearest products, then the pairwise tree
-        // of separate round-to-nearest sums.
-        float lv[N];
+    for (int e = 0; e < V; ++e) {
+      // Separate fp32 round-to-nearest products, then the pairwise tree
+      // of separate round-to-nearest sums.
+      float lv[N];
 #pragma unroll
-        for (int i = 0; i < N; ++i) lv[i] = w[i] * elem<V>(x[i][k], e);
+      for (int i = 0; i < N; ++i) lv[i] = w[i] * elem<V>(x[i][k], e);
 #pragma unroll
-        for (int width = N; width > 1; width /= 2) {
+      for (int width = N; width > 1; width /= 2) {
 #pragma unroll
-          for (int j = 0; j < width / 2; ++j) lv[j] = lv[2 * j] + lv[2 * j + 1];
-        }
-        y[e] = lv[0];
+        for (int j = 0; j < width / 2; ++j) lv[j] = lv[2 * j] + lv[2 * j + 1];
       }
-      store_vec<V, kWriteThrough>(o, u * V, pack<V>(y));
+      y[e] = lv[0];
     }
+    store_vec<V, kWriteThrough>(o, h, pack<V>(y));
   }
 }
 
@@ -995,7 +994,7 @@ void launch_fwd_t(const FwdPlan& pl, const uint16_t* residual, const float* pre,
   hipExtLaunchKernelGGL(hagg_fwd_kernel<V, UPT, N>,
                         dim3(pl.blocks_per_token, static_cast<uint32_t>(tokens)),
                         dim3(pl.block), 0, stream, ev.start, ev.stop, 0, residual, pre, out, H,
-                        pl.units_per_token);
+                        static_cast<uint32_t>(pl.block));
 }
 
 // Instantiates only the batches the register budget allows (the plan never
