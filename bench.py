@@ -417,6 +417,50 @@ def run_sweep(path: str, rounds: int = 7, warm: int = 10, timed: int = 100) -> N
 
 
 # ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a token sample
+# ---------------------------------------------------------------------------
+
+def run_cpu_baseline(T: int, H: int, min_seconds: float) -> dict:
+    """The oracle, as it stands, on the step's workload: the forward and
+    backward of one seed-0 input set of T tokens, repeated until at least
+    `min_seconds` of CPU time have passed (one thread: numpy ufuncs)."""
+    from hyper_connection_residual_mhc_amd.workloads import make_inputs
+    from oracle import h_aggregate as O
+    host = make_inputs(T, H, seed=0, grad=True)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        O.h_aggregate_fwd(host["residual"], host["pre"])
+        O.h_aggregate_bwd(host["residual"], host["pre"], host["grad_out"])
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or reps >= 1000:
+            break
+    gb = reps * (fwd_bytes(T, H) + bwd_bytes(T, H)) / 1e9
+    return {
+        "value": round(gb / dt, 6),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{reps} oracle steps (forward + backward) on one seed-0 input set of "
+                   f"T={T}, H={H} (numpy float32 ufuncs, one thread), {dt:.1f} s; "
+                   f"GB/s of the same algorithmic bytes"),
+        "host_cpu": cpu_model(),
+        "host_cores_visible": len(os.sched_getaffinity(0)),
+    }
+
+
+def cpu_model() -> str:
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+# ---------------------------------------------------------------------------
 # rocprofv3 summaries (for the text files in profiles/)
 # ---------------------------------------------------------------------------
 
@@ -561,7 +605,9 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
             "traffic": recorded_traffic(),
-            "kernel": "hagg_bwd_kernel (backward)",
+            "kernel": ("hagg_bwd_rows_kernel (backward, row layout)"
+                       if g["bwd_plan"].get("layout") == 2 else
+                       "hagg_bwd_kernel (backward, split layout)"),
         },
         "stream_probe": probe_record(bwd_bytes(T, H), g["probe"]),
         "timing": {"per_kernel": "HIP events attached to the dispatches of every "

@@ -16,10 +16,12 @@
 //    so the token index, pre[t,:] and every base address are wave-uniform
 //    (scalar registers and scalar loads). Each lane owns one or more
 //    V-element units and is their only writer; no lane ever reduces.
-//  * Backward: one block of 4 waves (256 lanes) owns a token; each lane
-//    streams its 8-element groups in the fixed lane order, writes
-//    grad_residual on the way and keeps 4 fp32 accumulators, which a
-//    fixed-order cross-lane tree and an LDS step reduce to grad_pre[t,:].
+//  * Backward, two layouts of the same fixed summation order: for long
+//    batches one wave streams one (token, stream) row, each lane holding
+//    four of the order's 256 accumulator lanes, and reduces it in registers;
+//    for short batches the 256 accumulator lanes are a block's 256 threads
+//    and the last stage goes through LDS. Both write grad_residual on the
+//    way.
 //  * Bit exactness: contraction is off for the whole file (pragma and
 //    -ffp-contract=off), fast-math builds are refused, fp32 denormals are
 //    kept (the kernel descriptor's default mode), and every bf16 result goes
@@ -1058,23 +1060,6 @@ void launch_bwd_a(const BwdPlan& pl, const uint16_t* residual, const float* pre,
   }
 }
 
-template <int V>
-void launch_bwd_v(const BwdPlan& pl, const uint16_t* residual, const float* pre,
-                  const uint16_t* grad_out, uint16_t* grad_residual, float* grad_pre,
-                  int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
-  if (pl.layout == MHC_BWD_ROWS) {
-    if (pl.acc)
-      launch_rows_a<V, true>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
-    else
-      launch_rows_a<V, false>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
-    return;
-  }
-  if (pl.acc)
-    launch_bwd_a<V, true>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
-  else
-    launch_bwd_a<V, false>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
-}
-
 template <int V, int B, bool ACC>
 void launch_rows_t(const BwdPlan& pl, const uint16_t* residual, const float* pre,
                    const uint16_t* grad_out, uint16_t* grad_residual, float* grad_pre,
@@ -1103,6 +1088,23 @@ void launch_rows_a(const BwdPlan& pl, const uint16_t* residual, const float* pre
       default: launch_rows_t<V, kMaxB, ACC>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
     }
   }
+}
+
+template <int V>
+void launch_bwd_v(const BwdPlan& pl, const uint16_t* residual, const float* pre,
+                  const uint16_t* grad_out, uint16_t* grad_residual, float* grad_pre,
+                  int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
+  if (pl.layout == MHC_BWD_ROWS) {
+    if (pl.acc)
+      launch_rows_a<V, true>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
+    else
+      launch_rows_a<V, false>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
+    return;
+  }
+  if (pl.acc)
+    launch_bwd_a<V, true>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
+  else
+    launch_bwd_a<V, false>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
 }
 
 // Events of the i-th of n launches of one call: start on the first, stop on

@@ -1,0 +1,63 @@
+"""Host-side pieces of bench.py (no GPU): argument rules, the oracle
+baseline record, the profile summaries and the recorded-traffic lookup."""
+
+from __future__ import annotations
+
+import subprocess
+import sys
+from pathlib import Path
+
+import bench
+
+REPO = Path(__file__).resolve().parents[1]
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, str(REPO / "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_cpu_baseline_record():
+    rec = bench.run_cpu_baseline(2, 64, 0.0)
+    assert rec["kind"] == "oracle" and rec["unit"] == "GB/s" and rec["cores"] == 1
+    assert rec["value"] > 0 and "T=2, H=64" in rec["sample"]
+
+
+def test_algorithmic_bytes_per_token():
+    T, H = 3, 7168
+    assert bench.fwd_bytes(T, H) == T * (10 * H + 16)
+    assert bench.bwd_bytes(T, H) == T * (18 * H + 32)
+    assert bench.bwd_acc_bytes(T, H) == T * (26 * H + 32)
+
+
+def test_probe_record_fractions():
+    rec = bench.probe_record(1000, {"kernel_us": [1.0, 1.0], "probe_us": [2.0, 2.0],
+                                    "probe_bytes": 1000})
+    assert rec["kernel_gbps"] == 1.0 and rec["probe_gbps"] == 0.5 and rec["frac_of_probe"] == 2.0
+
+
+def test_summaries_parse_rocprof_csv(tmp_path, capsys):
+    stats = tmp_path / "kernel_stats.csv"
+    stats.write_text('"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs"\n'
+                     '"void (anonymous namespace)::hagg_bwd_rows_kernel<8, 8, false>(unsigned short'
+                     ' const*, float const*)",10,220000,22000.0,60.0,21000,23000\n')
+    bench.summarize_stats(str(stats))
+    out = capsys.readouterr().out
+    assert "| hagg_bwd_rows_kernel<8, 8, false> | 10 | 22.000 |" in out
+    pmc = tmp_path / "counter_collection.csv"
+    pmc.write_text('"Grid_Size","Kernel_Name","Counter_Name","Counter_Value"\n'
+                   '262144,"void (anonymous namespace)::hagg_bwd_rows_kernel<8, 8, false>(int)",'
+                   '"FETCH_SIZE",100.0\n'
+                   '262144,"void (anonymous namespace)::hagg_bwd_rows_kernel<8, 8, false>(int)",'
+                   '"FETCH_SIZE",300.0\n')
+    bench.summarize_pmc([str(pmc)])
+    out = capsys.readouterr().out
+    assert "| hagg_bwd_rows_kernel<8, 8, false> | 262144 | FETCH_SIZE | 2 | 200.0 |" in out
+
+
+def test_recorded_traffic_is_tied_to_the_kernel_source():
+    """The profile's traffic figure is used only while the kernel source it
+    was measured on is unchanged (else null)."""
+    value = bench.recorded_traffic()
+    assert value is None or value > 0
