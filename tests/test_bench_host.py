@@ -61,3 +61,9 @@ def test_recorded_traffic_is_tied_to_the_kernel_source():
     was measured on is unchanged (else null)."""
     value = bench.recorded_traffic()
     assert value is None or value > 0
+
+
+def test_all_core_baseline_record():
+    rec = bench.run_cpu_baseline_all_cores(4, 64, 0.0, 2)
+    assert rec["kind"] == "oracle" and rec["cores"] == 2 and rec["value"] > 0
+    assert "2 token slices" in rec["sample"]
