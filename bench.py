@@ -15,9 +15,12 @@ timed region starts.
 Output: one JSON line. `value` is the step's algorithmic bytes (forward
 10H+16 and backward 18H+32 per token) divided by the measured time per step.
 `roofline` is for the backward kernel (the larger of the two), its duration
-taken from HIP events that the library attaches to every backward dispatch
-in the timed region (start and end timestamps of the dispatch itself).
-`cpu_baseline` times the CPU oracle on a token sample of the same workload.
+taken from HIP events that the library attaches to the backward dispatches
+of every 8th timed step (start and end timestamps of the dispatch itself);
+its `traffic` comes from the committed counter summary while the library's
+device code is the one it was measured on. `stream_probe` compares the
+backward with a plain stream of the same read:write bytes. `cpu_baseline`
+times the CPU oracle on the same workload, on one core and on all cores.
 
 Helpers for the profiles: --summarize-stats and --summarize-pmc turn
 rocprofv3 CSV output into the short text summaries kept in profiles/.
@@ -33,6 +36,7 @@ import os
 import platform
 import re
 import statistics
+import struct
 import sys
 import time
 from pathlib import Path
@@ -45,7 +49,6 @@ METRIC = "h_aggregate fwd/bwd achieved HBM GB/s + µs/call at T=1024,H=7168 (1 G
 HC = 4
 PEAK_HBM_GBPS = 8000.0            # MI355X HBM3E peak, 8 TB/s
 TRAFFIC_FILE = REPO / "profiles" / "hagg_bwd_T1024_H7168_traffic.md"
-KERNEL_SRC = REPO / "hyper_connection_residual_mhc_amd" / "csrc" / "mhc_h_aggregate.hip"
 
 
 def fwd_bytes(T: int, H: int) -> int:
@@ -66,19 +69,60 @@ def bwd_acc_bytes(T: int, H: int) -> int:
     return T * (26 * H + 32)
 
 
-def source_sha256() -> str:
-    return hashlib.sha256(KERNEL_SRC.read_bytes()).hexdigest()
+def _elf_sections(blob: bytes) -> dict[str, bytes]:
+    """Section name -> bytes of a little-endian ELF64 image."""
+    shoff = struct.unpack_from("<Q", blob, 0x28)[0]
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", blob, 0x3A)
+
+    def header(i: int) -> tuple:
+        return struct.unpack_from("<IIQQQQIIQQ", blob, shoff + i * shentsize)
+
+    names = header(shstrndx)[4]
+    out = {}
+    for i in range(shnum):
+        h = header(i)
+        name = blob[names + h[0]:blob.index(b"\0", names + h[0])].decode()
+        out[name] = blob[h[4]:h[4] + h[5]]
+    return out
+
+
+def device_code_sha256(lib_path: Path | None = None) -> str | None:
+    """Digest of the gfx950 kernels in our built library: the machine code,
+    kernel descriptors and kernel metadata (.text, .rodata, .note) of the
+    gfx950 code object in its offload bundle. It changes exactly when a
+    kernel changes (comments and host code leave it alone, and rebuilding
+    the same source gives the same digest). None if there is no library."""
+    from hyper_connection_residual_mhc_amd import _build
+    path = lib_path or _build.LIB_PATH
+    if not path.exists():
+        return None
+    bundle = _elf_sections(path.read_bytes()).get(".hip_fatbin")
+    if not bundle or not bundle.startswith(b"__CLANG_OFFLOAD_BUNDLE__"):
+        return None
+    count = struct.unpack_from("<Q", bundle, 24)[0]
+    pos = 32
+    for _ in range(count):
+        off, size, id_len = struct.unpack_from("<QQQ", bundle, pos)
+        ident = bundle[pos + 24:pos + 24 + id_len].decode()
+        pos += 24 + id_len
+        if ident.endswith("gfx950"):
+            sec = _elf_sections(bundle[off:off + size])
+            h = hashlib.sha256()
+            for name in (".text", ".rodata", ".note"):
+                h.update(sec.get(name, b""))
+            return h.hexdigest()
+    return None
 
 
 def recorded_traffic() -> int | None:
     """HBM bytes per backward launch from the committed counter summary, or
-    None when there is none or the kernel source changed since it was taken."""
+    None when there is none or the kernels changed since it was taken."""
     if not TRAFFIC_FILE.exists():
         return None
     text = TRAFFIC_FILE.read_text()
-    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_sha = re.search(r"device_code_sha256:\s*([0-9a-f]{64})", text)
     m_val = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
-    if not (m_sha and m_val) or m_sha.group(1) != source_sha256():
+    if not (m_sha and m_val) or m_sha.group(1) != device_code_sha256():
         return None
     return int(m_val.group(1))
 

@@ -115,12 +115,14 @@ template <> __device__ __forceinline__ uint16_t pack<1>(const float (&y)[1]) {
   return to_bf16(y[0]);
 }
 
-// Memory access: CDNA buffer instructions. A token's rows are described by a
-// buffer resource (base address and byte length, held in scalar registers,
-// wave-uniform), each lane supplies one 32-bit byte offset. Accesses past the
-// resource's length are dropped by the hardware (loads return 0), so no lane
-// can touch memory outside the row it was given. Every tensor byte is touched
-// exactly once, so every access carries the nontemporal (streaming) hint.
+// Memory access: CDNA buffer instructions. A row (or a token's rows) is
+// described by a buffer resource (base address and byte length, held in
+// scalar registers, wave-uniform), each lane supplies one 32-bit byte offset.
+// Accesses past the resource's length are dropped by the hardware (loads
+// return 0), so no lane can touch memory outside the row it was given.
+// Streamed bytes are touched once, so loads carry the nontemporal hint; the
+// one row several waves read (the backward's grad_out in the row layout)
+// keeps the default policy so that it stays in cache for them.
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr int kRsrcFormat = 0x00020000;  // gfx9 resource word 3: raw 32-bit data
 constexpr int kNontemporal = 2;          // cache-policy bit 1: nt
@@ -137,26 +139,20 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
 }
 
 // Load V bf16 elements at element `off` (per lane) plus `soff` bytes
-// (wave-uniform, carried in a scalar register) into the resource.
-// POL: cache-policy bits (nontemporal unless a row is read by several waves).
-template <int V>
-__device__ __forceinline__ typename Vec<V>::type load_vec(Rsrc rs, uint32_t off, uint32_t soff,
-                                                          int pol = kNontemporal);
-template <> __device__ __forceinline__ u32x4 load_vec<8>(Rsrc rs, uint32_t off, uint32_t soff, int pol) {
-  return pol == kCached ? __builtin_amdgcn_raw_buffer_load_b128(rs, off * 2, soff, kCached)
-                        : __builtin_amdgcn_raw_buffer_load_b128(rs, off * 2, soff, kNontemporal);
-}
-template <> __device__ __forceinline__ u32x2 load_vec<4>(Rsrc rs, uint32_t off, uint32_t soff, int pol) {
-  return pol == kCached ? __builtin_amdgcn_raw_buffer_load_b64(rs, off * 2, soff, kCached)
-                        : __builtin_amdgcn_raw_buffer_load_b64(rs, off * 2, soff, kNontemporal);
-}
-template <> __device__ __forceinline__ uint32_t load_vec<2>(Rsrc rs, uint32_t off, uint32_t soff, int pol) {
-  return pol == kCached ? __builtin_amdgcn_raw_buffer_load_b32(rs, off * 2, soff, kCached)
-                        : __builtin_amdgcn_raw_buffer_load_b32(rs, off * 2, soff, kNontemporal);
-}
-template <> __device__ __forceinline__ uint16_t load_vec<1>(Rsrc rs, uint32_t off, uint32_t soff, int pol) {
-  return pol == kCached ? __builtin_amdgcn_raw_buffer_load_b16(rs, off * 2, soff, kCached)
-                        : __builtin_amdgcn_raw_buffer_load_b16(rs, off * 2, soff, kNontemporal);
+// (wave-uniform, carried in a scalar register) from the resource, with
+// cache-policy bits POL.
+template <int V, int POL = kNontemporal>
+__device__ __forceinline__ typename Vec<V>::type load_vec(Rsrc rs, uint32_t off, uint32_t soff) {
+  if constexpr (V == 8) {
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, off * 2, soff, POL);
+  } else if constexpr (V == 4) {
+    return __builtin_amdgcn_raw_buffer_load_b64(rs, off * 2, soff, POL);
+  } else if constexpr (V == 2) {
+    return __builtin_amdgcn_raw_buffer_load_b32(rs, off * 2, soff, POL);
+  } else {
+    static_assert(V == 1, "vector width");
+    return __builtin_amdgcn_raw_buffer_load_b16(rs, off * 2, soff, POL);
+  }
 }
 
 // Stores take no scalar offset: the whole byte offset travels in the VGPR.
@@ -487,7 +483,7 @@ __device__ __forceinline__ void rows_issue(RowSlots<V, B, ACC>& sl, int b, uint3
 #pragma unroll
   for (int v = 0; v < RowSlots<V, B, ACC>::NV; ++v) {
     const uint32_t h = k * kGroup + v * V;
-    sl.g[b][v] = load_vec<V>(g_row, h, 0, kCached);
+    sl.g[b][v] = load_vec<V, kCached>(g_row, h, 0);
     sl.r[b][v] = load_vec<V>(r_row, h, 0);
     if constexpr (ACC) sl.old[b][v] = load_vec<V>(gr_row, h, 0);
   }
@@ -733,7 +729,7 @@ constexpr int fwd_max_upt(int V, int N) {
 
 struct FwdPlan {
   int V, block, upt, n;
-  uint32_t units_per_token, blocks_per_token;
+  uint32_t blocks_per_token;
   int64_t tokens_per_launch, total_blocks;
 };
 
@@ -780,7 +776,6 @@ mhc_status plan_fwd(const uint16_t* residual, const uint16_t* out, int64_t T, in
   pl->block = block;
   pl->upt = upt;
   pl->n = n;
-  pl->units_per_token = static_cast<uint32_t>(upt_units);
   pl->blocks_per_token = static_cast<uint32_t>(bpt);
   // Tokens run along the grid's y dimension, at most 65535 per launch, and a
   // launch stays within 2^31 work-items.

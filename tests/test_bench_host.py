@@ -67,3 +67,11 @@ def test_all_core_baseline_record():
     rec = bench.run_cpu_baseline_all_cores(4, 64, 0.0, 2)
     assert rec["kind"] == "oracle" and rec["cores"] == 2 and rec["value"] > 0
     assert "2 token slices" in rec["sample"]
+
+
+def test_device_code_digest(built_library, tmp_path):
+    """The digest names the built library's gfx950 kernels; no library, no
+    digest."""
+    d = bench.device_code_sha256(built_library)
+    assert d is not None and len(d) == 64 and int(d, 16) >= 0
+    assert bench.device_code_sha256(tmp_path / "missing.so") is None
