@@ -20,6 +20,7 @@ import torch
 from conftest import assert_bytes_equal
 from gpu_util import run_bwd, say
 from hyper_connection_residual_mhc_amd import ops
+from hyper_connection_residual_mhc_amd._lib import MhcError
 from hyper_connection_residual_mhc_amd.workloads import (bf16_tensor_to_bits, bits_to_bf16_tensor,
                                                          make_inputs, to_device)
 from oracle import h_aggregate as O
@@ -37,7 +38,8 @@ def run_acc(host, old_bits, dev, launch=None):
 
 
 @pytest.mark.parametrize("T,H", [(1, 4096), (8, 7168), (128, 7168), (129, 4096), (1024, 7168),
-                                 (2048, 7168), (3, 1279), (5, 4100), (4, 20001)])
+                                 (2048, 7168), (3, 1279), (5, 4100), (4, 20001), (777, 4096),
+                                 (600, 6144)])
 def test_accumulate_bit_exact(device, T, H):
     say(f"accumulate parity T={T} H={H}")
     host = make_inputs(T, H, seed=T + 3 * H, grad=True)
@@ -76,7 +78,7 @@ def test_accumulate_twice_is_two_roundings(device):
     assert_bytes_equal(bf16_tensor_to_bits(gr), twice, "twice")
 
 
-@pytest.mark.parametrize("T,H", [(37, 7168), (9, 1279), (6, 4100)])
+@pytest.mark.parametrize("T,H", [(37, 7168), (9, 1279), (6, 4100), (11, 4096)])
 def test_accumulate_every_launch_shape_same_bytes(device, T, H):
     host = make_inputs(T, H, seed=8, grad=True)
     old = make_inputs(T, H, seed=9)["residual"]
@@ -96,8 +98,13 @@ def test_accumulate_every_launch_shape_same_bytes(device, T, H):
             assert_bytes_equal(gr, want_gr, f"grad_residual {launch}")
             assert_bytes_equal(gp, want_gp, f"grad_pre {launch}")
     # row layout (not available at vec_width 1: register budget)
-    for v, u, bt in itertools.product([w for w in widths if w > 1], (4, 8), (64, 256, 512)):
+    for v, u, bt in itertools.product([w for w in widths if w > 1], (4, 8, 12), (64, 256, 512)):
         launch = {"layout": 2, "vec_width": v, "units_per_thread": u, "block_threads": bt}
+        try:
+            ops.mhc_h_aggregate_plan_bwd_acc(1 << 34, 1 << 35, 1 << 36, 1 << 37, 1 << 38, T, H,
+                                             launch=launch)
+        except MhcError:
+            continue   # beyond the register budget (rejected by the plan)
         say(f"accumulate launch {launch} T={T} H={H}")
         gr, gp = run_acc(host, old, device, launch=launch)
         assert_bytes_equal(gr, want_gr, f"grad_residual {launch}")

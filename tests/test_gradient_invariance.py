@@ -19,6 +19,7 @@ import torch
 from conftest import assert_bytes_equal
 from gpu_util import GUARD, ROWS, SENTINELS, SPLIT, guarded_empty_bf16, guards_untouched, run_bwd, say
 from hyper_connection_residual_mhc_amd import ops
+from hyper_connection_residual_mhc_amd._lib import MhcError
 from hyper_connection_residual_mhc_amd.workloads import bf16_tensor_to_bits, make_inputs, to_device
 from oracle import h_aggregate as O
 
@@ -66,7 +67,8 @@ def test_backward_batch_split(device, T, H, splits):
     assert_bytes_equal(gp2.cpu().numpy(), gp.cpu().numpy(), "split grad_pre")
 
 
-@pytest.mark.parametrize("T,H", [(37, 7168), (9, 1279), (5, 4100), (4, 20001)])
+@pytest.mark.parametrize("T,H", [(37, 7168), (9, 1279), (5, 4100), (4, 20001), (13, 2048),
+                                 (7, 5000), (6, 8192)])
 def test_backward_every_launch_shape_gives_the_same_bytes(device, T, H):
     host = make_inputs(T, H, seed=2, grad=True)
     want_gr, want_gp = O.h_aggregate_bwd(host["residual"], host["pre"], host["grad_out"])
@@ -80,11 +82,15 @@ def test_backward_every_launch_shape_gives_the_same_bytes(device, T, H):
         gr, gp = run_bwd(host, device, launch=launch)
         assert_bytes_equal(gr, want_gr, f"grad_residual {launch}")
         assert_bytes_equal(gp, want_gp, f"grad_pre {launch}")
-    # row layout: one wave per (token, stream) row
+    # row layout: one wave per (token, stream) row, every ring size and rows
+    # per block the plan accepts (rings longer and shorter than the row)
     for v, u, bt in itertools.product(widths, (4, 8, 12), (64, 128, 256, 512)):
-        if v == 1 and u > 4:
-            continue   # rejected by the plan (register budget)
         launch = {"layout": ROWS, "vec_width": v, "units_per_thread": u, "block_threads": bt}
+        try:
+            ops.mhc_h_aggregate_plan_bwd(1 << 34, 1 << 35, 1 << 36, 1 << 37, 1 << 38, T, H,
+                                         launch=launch)
+        except MhcError:
+            continue   # beyond the register budget (rejected by the plan)
         say(f"backward launch {launch} T={T} H={H}")
         gr, gp = run_bwd(host, device, launch=launch)
         assert_bytes_equal(gr, want_gr, f"grad_residual {launch}")
