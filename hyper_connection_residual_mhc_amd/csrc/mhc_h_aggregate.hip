@@ -340,7 +340,7 @@ __device__ __forceinline__ void bwd_consume(BwdSlots<V, U, S, ACC>& sl, int u, u
 //
 // Lane l (= threadIdx.x) is accumulator lane l of the fixed order: it visits
 // groups k = l, l + 256, l + 512, ... (group k = hidden elements 8k .. 8k+7),
-// U of them per batch of loads, and for each element adds grad_out*residual_i
+// U of them in flight at a time, and for each element adds grad_out*residual_i
 // to its accumulator i in ascending h. It also writes grad_residual for every
 // element it visits (ACC: adds the product to the stored gradient in fp32 and
 // rounds the sum once). Then each wave halves its 64 accumulators with
@@ -348,8 +348,9 @@ __device__ __forceinline__ void bwd_consume(BwdSlots<V, U, S, ACC>& sl, int u, u
 // V elements are moved per access; V divides 8 and H, so a group is 8/V
 // accesses (fewer for a short last group).
 //
-// At most 128 VGPRs (4 waves per SIMD), so that 4 blocks fit on a CU and a
-// 1024-token call is resident at once.
+// At most 128 VGPRs (4 waves per SIMD), so that 4 blocks fit on a CU: the
+// policy uses this layout for batches below 512 tokens, which are then
+// resident at once.
 template <int V, int U, int S, bool ACC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void hagg_bwd_kernel(
     const uint16_t* __restrict__ residual, const float* __restrict__ pre,
