@@ -97,15 +97,16 @@ typedef enum mhc_status {
  *   vec_width         bf16 elements per vector access: 1, 2, 4 or 8. It must
  *                     divide H and match the alignment of every bf16 buffer.
  *   units_per_thread  forward: vector units each thread handles (1, 2 or
- *                     4). Backward: 8-element groups each lane keeps in
- *                     flight, a ring of loads whose slots are refilled with
- *                     the lane's next group once consumed - 1, 2 or 4 in
- *                     the split layout, 4, 8 or 12 in the row layout (whose
- *                     default is 8). At
- *                     most what the register budget allows for the
- *                     vec_width, expansion rate and streams_per_block (the
- *                     plan query reports the default, which is that maximum
- *                     in the backward; more gives MHC_ERROR_INVALID_VALUE).
+ *                     4; default 1). Backward: 8-element groups each lane
+ *                     keeps in flight, a ring of loads whose slots are
+ *                     refilled with the lane's next group once consumed -
+ *                     1, 2 or 4 in the split layout (default: the most the
+ *                     register budget allows), 4, 8 or 12 in the row layout
+ *                     (default 8, fewer where the budget requires). More
+ *                     than the register budget allows for the vec_width,
+ *                     layout, expansion rate and streams_per_block gives
+ *                     MHC_ERROR_INVALID_VALUE; the plan query reports the
+ *                     value a call would use.
  *   tokens_per_block  backward split layout only: tokens one block handles
  *                     in sequence, 1..4096.
  *   streams_per_block backward split layout only: residual streams one
@@ -119,7 +120,10 @@ typedef enum mhc_status {
  *                     row; each of its 64 lanes holds accumulator lanes
  *                     j, j+64, j+128, j+192 and the 64-lane trees run inside
  *                     the wave). The policy takes the row layout from
- *                     T = 512 on. Same summation order, same bits.
+ *                     T = 512 on, unless a split-layout field is set or
+ *                     the row layout does not fit the register budget
+ *                     (scalar-width accumulating calls). Same summation
+ *                     order, same bits.
  * Forward calls reject non-zero backward-only fields.
  */
 typedef struct mhc_launch {
@@ -318,8 +322,10 @@ mhc_status mhc_bf16_rne_probe(uint32_t first_bits, int64_t n, uint16_t* out,
  * above and no arithmetic, so that their time can be compared with what a
  * plain stream of the same bytes takes on this GPU. Per unit it reads
  * `reads` consecutive KiB of src and writes `writes` consecutive KiB of dst
- * (one 64-lane block per unit; the written words are the XOR of the unit's
- * loaded 16-byte vectors, lane by lane, repeated `writes` times).
+ * (one 64-lane block per unit, all loads before the first store; the
+ * written words are the XOR of the unit's loaded 16-byte vectors, lane by
+ * lane, repeated `writes` times), with the cache policy of the kernel whose
+ * mix it stands for.
  *   reads:writes  1:1 (copy), 4:1 (forward: 8H read, 2H written),
  *                 5:4 (backward: 10H read, 8H written),
  *                 9:4 (accumulating backward: 18H read, 8H written).
