@@ -1,0 +1,67 @@
+/* A plain C99 caller of the library's host-only entry points: the header
+ * compiles as C, the library links and loads, and the rules the header
+ * states hold when called from C (no GPU is touched). Exit status 0 on
+ * success; a failed check prints its line. */
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "mhc_h_aggregate.h"
+
+#define CHECK(cond)                                              \
+  do {                                                           \
+    if (!(cond)) {                                               \
+      fprintf(stderr, "check failed at line %d: %s\n", __LINE__, #cond); \
+      return 1;                                                  \
+    }                                                            \
+  } while (0)
+
+int main(void) {
+  const int64_t T = 1024, H = 7168;
+  /* Fake, far-apart, 256-byte-aligned device addresses: the host-only calls
+   * use pointers only as numbers. */
+  const uintptr_t base = (uintptr_t)1 << 34;
+  const uint16_t* residual = (const uint16_t*)base;
+  const float* pre = (const float*)(base + ((uintptr_t)1 << 30));
+  const uint16_t* grad_out = (const uint16_t*)(base + ((uintptr_t)2 << 30));
+  uint16_t* grad_residual = (uint16_t*)(base + ((uintptr_t)3 << 30));
+  float* grad_pre = (float*)(base + ((uintptr_t)4 << 30));
+  uint16_t* out = (uint16_t*)(base + ((uintptr_t)5 << 30));
+  mhc_launch plan, ov;
+  int64_t blocks = 0;
+
+  CHECK(mhc_abi_version() == MHC_ABI_VERSION);
+  CHECK(strcmp(mhc_status_string(MHC_ERROR_ALIASING), "MHC_ERROR_ALIASING") == 0);
+
+  CHECK(mhc_h_aggregate_validate_fwd(residual, pre, out, T, H) == MHC_SUCCESS);
+  CHECK(mhc_h_aggregate_validate_fwd(residual, pre, (uint16_t*)residual, T, H) ==
+        MHC_ERROR_ALIASING);
+  CHECK(strlen(mhc_last_error_message()) > 0);
+  CHECK(mhc_h_aggregate_validate_fwd(residual, pre, out, -1, H) == MHC_ERROR_INVALID_VALUE);
+  CHECK(mhc_h_aggregate_validate_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, H) ==
+        MHC_SUCCESS);
+
+  CHECK(mhc_h_aggregate_plan_fwd(residual, pre, out, T, H, NULL, &plan, &blocks) == MHC_SUCCESS);
+  CHECK(plan.block_threads == 64 && plan.vec_width == 8 && blocks == T * (H / 8 / 64));
+
+  CHECK(mhc_h_aggregate_plan_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, H, NULL,
+                                 &plan, &blocks) == MHC_SUCCESS);
+  CHECK(plan.layout == MHC_BWD_ROWS && plan.block_threads == 256 && blocks == T);
+
+  memset(&ov, 0, sizeof ov);
+  ov.layout = MHC_BWD_SPLIT;
+  CHECK(mhc_h_aggregate_plan_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, H, &ov,
+                                 &plan, &blocks) == MHC_SUCCESS);
+  CHECK(plan.layout == MHC_BWD_SPLIT && plan.streams_per_block == 4 && blocks == T);
+
+  CHECK(mhc_h_aggregate_plan_bwd_n(residual, pre, grad_out, grad_residual, grad_pre, T, 3, H, 0,
+                                   NULL, &plan, &blocks) == MHC_ERROR_INVALID_VALUE);
+  /* compute entry points reject bad arguments before any HIP call */
+  CHECK(mhc_h_aggregate_fwd(residual, pre, (uint16_t*)residual, T, H, NULL) ==
+        MHC_ERROR_ALIASING);
+  CHECK(mhc_h_aggregate_bwd(NULL, NULL, NULL, NULL, NULL, 0, H, NULL) == MHC_SUCCESS);
+  CHECK(mhc_stream_probe((const void*)base, 5 * 1024, out, 4 * 1024, 3, 4, NULL, NULL, NULL) ==
+        MHC_ERROR_INVALID_VALUE);
+  printf("c abi ok\n");
+  return 0;
+}
