@@ -349,8 +349,8 @@ __device__ __forceinline__ void bwd_consume(BwdSlots<V, U, S, ACC>& sl, int u, u
 // accesses (fewer for a short last group).
 //
 // At most 128 VGPRs (4 waves per SIMD), so that 4 blocks fit on a CU: the
-// policy uses this layout for batches below 512 tokens, which are then
-// resident at once.
+// policy uses this layout for batches below 768 rows (192 tokens at
+// n = 4), which are then resident at once.
 template <int V, int U, int S, bool ACC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void hagg_bwd_kernel(
     const uint16_t* __restrict__ residual, const float* __restrict__ pre,
@@ -718,7 +718,11 @@ constexpr int64_t kMaxGridY = 65535;
 // Backward layout and streams per block by batch length (see plan_bwd).
 constexpr int64_t kTwoStreamsFromT = 128;
 constexpr int64_t kFourStreamsFromT = 512;
-constexpr int64_t kRowsFromT = 512;
+// The row layout from this many rows (tokens x streams) per call on: it has
+// one wave per row, the split layout 4 per block of S streams, so short
+// batches keep more CUs busy split. Measured at n = 4: rows faster from
+// T = 192 (except at 320-384 tokens, H = 7168, by 1-7%), split faster at 128.
+constexpr int64_t kRowsFromRows = 768;
 
 // Largest forward batch UPT in {1, 2, 4} whose loaded data (N rows, each
 // access max(V/2, 1) registers) fits 64 VGPRs, within the 128-VGPR budget of
@@ -832,10 +836,11 @@ mhc_status plan_bwd(const uint16_t* residual, const uint16_t* grad_out,
                   ov->vec_width, (long long)H);
     V = ov->vec_width;
   }
-  // Row layout from kRowsFromT tokens on, unless a split-layout field is set.
+  // Row layout from kRowsFromRows rows on, unless a split-layout field is set.
   const bool rows_ok = rows_max_b(V, acc) > 0;
   const bool split_fields = ov && (ov->tokens_per_block != 0 || ov->streams_per_block != 0);
-  int layout = T >= kRowsFromT && rows_ok && !split_fields ? MHC_BWD_ROWS : MHC_BWD_SPLIT;
+  int layout =
+      T * n >= kRowsFromRows && rows_ok && !split_fields ? MHC_BWD_ROWS : MHC_BWD_SPLIT;
   if (ov && ov->layout != 0) {
     if (ov->layout != MHC_BWD_SPLIT && ov->layout != MHC_BWD_ROWS)
       return fail(MHC_ERROR_INVALID_VALUE, "backward layout must be 0, %d or %d", MHC_BWD_SPLIT,
