@@ -93,7 +93,7 @@ typedef enum mhc_status {
  *                     [64, 1024]. Backward, split layout: 0 or 256 (one
  *                     block of 4 waves owns a token's reduction); row
  *                     layout: 64, 128, 256 or 512 (1, 2, 4 or 8 rows per
- *                     block; default whole tokens: 256, 512 at n = 8).
+ *                     block; default 256).
  *   vec_width         bf16 elements per vector access: 1, 2, 4 or 8. It must
  *                     divide H and match the alignment of every bf16 buffer.
  *   units_per_thread  forward: vector units each thread handles (1, 2 or

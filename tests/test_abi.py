@@ -363,11 +363,11 @@ def test_expansion_rate_rules(lib):
     with pytest.raises(MhcError, match="ALIASING"):
         ops.mhc_h_aggregate_plan_fwd_n(r, r + 8 * T * H * 2, r + 8 * T * H, T, 8, H)
     rr, pp, g, gr, gp = bwd_ptrs(1024, H * 2)
-    # row layout: four rows per block (two tokens at n = 2), eight at n = 8
+    # row layout: four rows per block (two tokens at n = 2, half a token at 8)
     plan, grid = ops.mhc_h_aggregate_plan_bwd_n(rr, pp, g, gr, gp, 1024, 2, H)
     assert plan["block_threads"] == 256 and grid == 512
     plan, grid = ops.mhc_h_aggregate_plan_bwd_n(rr, pp, g, gr, gp, 1024, 8, H)
-    assert plan["block_threads"] == 512 and grid == 1024
+    assert plan["block_threads"] == 256 and grid == 2048
     plan, grid = ops.mhc_h_aggregate_plan_bwd_n(rr, pp, g, gr, gp, 1024, 2, H,
                                                 launch={"layout": _lib.MHC_BWD_SPLIT})
     assert plan["streams_per_block"] == 2 and grid == 1024
