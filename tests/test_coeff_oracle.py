@@ -1,0 +1,254 @@
+"""Pins of the coefficient-backward oracle (oracle/coeff_bwd.py).
+
+The page ("perf: fuse mHC coefficient backward epilogue", Summary) names the
+epilogue's parts but prints no formula, so the oracle cannot be compared with
+values from the page; it is pinned here to what the mathematics fixes:
+
+* the calculus of the reading: fp64 central differences of the forward being
+  differentiated (sigmoid gates, affine z = alpha * mix + b) against the
+  oracle's gradients, at every expansion rate and two post scales;
+* hand-derived values: a one-row case worked out by hand in exact binary
+  fractions, and discriminating inputs for every stage of the fixed row
+  order (each expected value derived by hand from the order's definition,
+  and each differing from what a plausible wrong order gives);
+* special cases (alpha = 0, saturated gates, c = 1, one row) and the error
+  bounds against correctly rounded fp64 sums.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import coeff_bwd as cb
+
+U = 2.0 ** -24
+
+
+def _inputs(R, n, seed, c=2.0):
+    rng = np.random.default_rng(seed)
+    m = cb.columns(n)
+    f = lambda a: np.asarray(a, dtype=np.float32)
+    return dict(mix=f(rng.standard_normal((R, m))), pre=f(rng.random((R, n))),
+                post=f(rng.random((R, n)) * c), grad_pre=f(rng.standard_normal((R, n))),
+                grad_post=f(rng.standard_normal((R, n))),
+                grad_res=f(rng.standard_normal((R, n * n))),
+                alpha=f(rng.uniform(0.5, 1.5, 3)))
+
+
+def _run(d, c, n):
+    return cb.coeff_bwd(d["mix"], d["pre"], d["post"], d["grad_pre"], d["grad_post"],
+                        d["grad_res"], d["alpha"], c, n)
+
+
+# ---------------------------------------------------------------------------
+# Hand-computed case (exact binary fractions, every step exact)
+# ---------------------------------------------------------------------------
+
+def test_hand_case_one_row_n2():
+    # n = 2: columns pre0 pre1 | post0 post1 | res00 res01 res10 res11; c = 2.
+    # pre  = (1/2, 1/4), grad_pre  = (1, 2):
+    #   d = 1 * (1/2 * 1/2) = 1/4,  2 * (1/4 * 3/4) = 3/8
+    # post = (1, 1/2) -> s = post / 2 = (1/2, 1/4), grad_post = (1, -1):
+    #   d = 1 * (1 * 1/2) = 1/2,   -1 * (1/2 * 3/4) = -3/8
+    # res: d = grad_res = (1, 2, 3, 4)
+    # alpha = (2, 1/2, 1): grad_mix = (1/2, 3/4, 1/4, -3/16, 1, 2, 3, 4)
+    # one row: grad_b = d
+    # mix = (1..8): alpha grads: pre 1/4*1 + 3/8*2 = 1; post 1/2*3 - 3/8*4 = 0;
+    #   res 1*5 + 2*6 + 3*7 + 4*8 = 70
+    f = lambda *v: np.array([v], dtype=np.float32)
+    gm, gb, ga = cb.coeff_bwd(f(1, 2, 3, 4, 5, 6, 7, 8), f(0.5, 0.25), f(1.0, 0.5), f(1, 2),
+                              f(1, -1), f(1, 2, 3, 4), np.array([2, 0.5, 1], np.float32), 2.0, 2)
+    assert gm.tolist() == [[0.5, 0.75, 0.25, -0.1875, 1, 2, 3, 4]]
+    assert gb.tolist() == [0.25, 0.375, 0.5, -0.375, 1, 2, 3, 4]
+    assert ga.tolist() == [1.0, 0.0, 70.0]
+
+
+# ---------------------------------------------------------------------------
+# The fixed row order: hand-derived discriminators
+# ---------------------------------------------------------------------------
+
+def _col(R, vals):
+    x = np.zeros((R, 1), dtype=np.float32)
+    for r, v in vals.items():
+        x[r, 0] = v
+    return x
+
+
+def test_row_sum_first_stage_is_the_halving_tree():
+    # rows 0..3 = 1, 2^-24, 0, 2^-24. Tree: offset 2 gives x1 = 2^-24 + 2^-24
+    # = 2^-23 and x0 = 1; offset 1 gives 1 + 2^-23 (exact). A sequential sum
+    # rounds 1 + 2^-24 to 1 (tie to even) twice and gives 1.
+    got = cb.row_sum(_col(4, {0: 1.0, 1: U, 3: U}))
+    assert got[0] == np.float32(1.0 + 2 * U)
+
+
+def test_row_sum_chunks_are_64_rows():
+    # rows 0 = 1, 32 = 33 = 2^-24, one chunk of 64: offset 32 adds row 32 to
+    # row 0 (1 + 2^-24 -> 1) and row 33 to row 1; offset 1 adds 2^-24 to 1
+    # again -> 1. With 32-row chunks the second chunk would sum to 2^-23 and
+    # the result would be 1 + 2^-23.
+    assert cb.row_sum(_col(64, {0: 1.0, 32: U, 33: U}))[0] == np.float32(1.0)
+    # rows 0 = 1, 64 = 65 = 2^-24: chunk 1 sums to 2^-23 (offset 1), stage 2
+    # adds it to chunk 0's 1 -> 1 + 2^-23. One 128-row tree would give 1.
+    assert cb.row_sum(_col(128, {0: 1.0, 64: U, 65: U}))[0] == np.float32(1.0 + 2 * U)
+
+
+def test_row_sum_second_stage_strides_chunks_over_64_accumulators():
+    # 66 chunks. Chunk sums: P0 = 1, P1 = 2^-24, P65 = 2^-24. Accumulator 1
+    # gets P1 and P65 (65 mod 64 = 1): 2^-23; the final tree adds it to
+    # accumulator 0's 1 -> 1 + 2^-23. Visiting the chunk sums one after
+    # another would give 1; giving each accumulator a contiguous run of chunks
+    # (0-1 to the first, ...) would also give 1.
+    R = 65 * 64 + 1
+    assert cb.row_sum(_col(R, {0: 1.0, 64: U, 65 * 64: U}))[0] == np.float32(1.0 + 2 * U)
+    # 129 chunks: P0 = 1, P64 = 2^-24, P128 = 2^-24 all go to accumulator 0,
+    # in ascending order: (1 + 2^-24) + 2^-24 rounds to 1 twice.
+    R = 128 * 64 + 1
+    assert cb.row_sum(_col(R, {0: 1.0, 64 * 64: U, 128 * 64: U}))[0] == np.float32(1.0)
+
+
+def test_row_sum_empty_and_single():
+    assert cb.row_sum(np.zeros((0, 3), np.float32)).tolist() == [0.0, 0.0, 0.0]
+    x = np.array([[3.5, -2.0, -0.0]], np.float32)
+    got = cb.row_sum(x)
+    assert got.tolist() == [3.5, -2.0, 0.0]
+    assert not np.signbit(got[2])        # -0 + (+0) is +0
+
+
+@pytest.mark.parametrize("R", [1, 63, 64, 65, 1000, 4097, 9000])
+def test_row_sum_within_error_bound_of_exact_sum(R):
+    rng = np.random.default_rng(R)
+    x = rng.standard_normal((R, 5)).astype(np.float32) * np.float32(3.0)
+    got = cb.row_sum(x)
+    for v in range(5):
+        exact = math.fsum(x[:, v].astype(np.float64))
+        mag = math.fsum(np.abs(x[:, v]).astype(np.float64))
+        assert abs(float(got[v]) - exact) <= cb.reduction_error_bound(R) * mag, v
+
+
+# ---------------------------------------------------------------------------
+# Calculus: the gradients of the forward being differentiated
+# ---------------------------------------------------------------------------
+
+def _loss64(mix, b, alpha, gp, gq, gr, c, n):
+    k = cb.groups(n)
+    z = alpha[k][None, :] * mix + b[None, :]
+    sig = 1.0 / (1.0 + np.exp(-z))
+    return (math.fsum((gp * sig[:, :n]).ravel()) + math.fsum((gq * c * sig[:, n:2 * n]).ravel())
+            + math.fsum((gr * z[:, 2 * n:]).ravel()))
+
+
+@pytest.mark.parametrize("n", [2, 4, 8])
+@pytest.mark.parametrize("c", [1.0, 2.0])
+def test_gradients_match_finite_differences_of_the_forward(n, c):
+    R, m = 5, cb.columns(n)
+    rng = np.random.default_rng(100 + n)
+    mix = rng.standard_normal((R, m))
+    b = rng.standard_normal(m) * 0.5
+    alpha = rng.uniform(0.5, 1.5, 3)
+    gp, gq, gr = (rng.standard_normal((R, n)), rng.standard_normal((R, n)),
+                  rng.standard_normal((R, n * n)))
+    # the saved activations the epilogue receives
+    k = cb.groups(n)
+    z = alpha[k][None, :] * mix + b[None, :]
+    sig = 1.0 / (1.0 + np.exp(-z))
+    f = lambda a: np.asarray(a, dtype=np.float32)
+    gm, gb, ga = cb.coeff_bwd(f(mix), f(sig[:, :n]), f(c * sig[:, n:2 * n]), f(gp), f(gq), f(gr),
+                              f(alpha), c, n)
+    L = lambda mx, bb, al: _loss64(mx, bb, al, gp, gq, gr, c, n)
+    h = 1e-6
+
+    def fd(vec, idx, fn):
+        a, bm = vec.copy(), vec.copy()
+        a[idx] += h
+        bm[idx] -= h
+        return (fn(a) - fn(bm)) / (2 * h)
+
+    # inputs were rounded to fp32 for the oracle: compare at ~1e-5
+    tol = lambda want: 2e-5 * (abs(want) + 1.0)
+    for r in range(R):
+        for j in range(m):
+            want = fd(mix, (r, j), lambda x: L(x, b, alpha))
+            assert abs(gm[r, j] - want) <= tol(want), ("grad_mix", r, j, gm[r, j], want)
+    for j in range(m):
+        want = fd(b, j, lambda x: L(mix, x, alpha))
+        assert abs(gb[j] - want) <= tol(want) * R, ("grad_b", j, gb[j], want)
+    for g in range(3):
+        want = fd(alpha, g, lambda x: L(mix, b, x))
+        assert abs(ga[g] - want) <= tol(want) * R * m, ("grad_alpha", g, ga[g], want)
+
+
+# ---------------------------------------------------------------------------
+# Special cases and error bounds
+# ---------------------------------------------------------------------------
+
+def test_zero_alpha_zeroes_grad_mix_only():
+    d = _inputs(70, 4, 1)
+    d["alpha"] = np.zeros(3, np.float32)
+    gm, gb, ga = _run(d, 2.0, 4)
+    assert np.all(gm == 0)
+    assert np.any(gb != 0) and np.all(ga != 0)
+
+
+def test_saturated_gates_have_zero_derivative():
+    d = _inputs(8, 4, 2)
+    d["pre"][:4] = 0.0
+    d["pre"][4:] = 1.0
+    d["post"][:4] = 0.0
+    d["post"][4:] = 2.0          # post = c: sigmoid saturated at 1
+    gm, gb, _ = _run(d, 2.0, 4)
+    assert np.all(gm[:, :8] == 0) and np.all(gb[:8] == 0)
+
+
+def test_unit_post_scale_makes_post_like_pre():
+    d = _inputs(33, 4, 3, c=1.0)
+    d["post"] = d["pre"].copy()
+    d["grad_post"] = d["grad_pre"].copy()
+    d["alpha"][1] = d["alpha"][0]
+    gm, gb, _ = _run(d, 1.0, 4)
+    assert np.array_equal(gm[:, :4], gm[:, 4:8]) and np.array_equal(gb[:4], gb[4:8])
+
+
+def test_one_row_grad_b_is_the_row_derivative():
+    d = _inputs(1, 8, 4)
+    gm, gb, _ = _run(d, 2.0, 8)
+    dz = cb.dz(d["pre"], d["post"], d["grad_pre"], d["grad_post"], d["grad_res"], 2.0)
+    assert np.array_equal(gb, dz[0])
+
+
+@pytest.mark.parametrize("n,R", [(2, 300), (4, 2048), (8, 257)])
+def test_within_error_bounds_of_fp64(n, R):
+    d = _inputs(R, n, 5 + n)
+    gm, gb, ga = _run(d, 2.0, n)
+    ex = cb.coeff_bwd_exact(d["mix"], d["pre"], d["post"], d["grad_pre"], d["grad_post"],
+                            d["grad_res"], d["alpha"], 2.0, n)
+    k = cb.groups(n)
+    al = np.abs(d["alpha"].astype(np.float64))[k][None, :]
+    assert np.all(np.abs(gm - ex["grad_mix"]) <= 6 * U * al * ex["mag_d"] + 1e-44)
+    rb = cb.reduction_error_bound(R)
+    assert np.all(np.abs(gb - ex["grad_b"]) <= (rb + 5 * U) * ex["mag_b"] * 1.01)
+    width = max(n, n * n)
+    ra = cb.reduction_error_bound(R, width)
+    assert np.all(np.abs(ga - ex["grad_alpha"]) <= (ra + 6 * U) * ex["mag_alpha"] * 1.01)
+
+
+def test_empty_batch_gives_zero_sums():
+    d = _inputs(0, 4, 6)
+    gm, gb, ga = _run(d, 2.0, 4)
+    assert gm.shape == (0, 24) and gb.tolist() == [0.0] * 24 and ga.tolist() == [0.0] * 3
+
+
+def test_argument_checks():
+    d = _inputs(4, 4, 7)
+    with pytest.raises(ValueError):
+        cb.coeff_bwd(d["mix"], d["pre"], d["post"], d["grad_pre"], d["grad_post"],
+                     d["grad_res"], d["alpha"], 2.0, 3)
+    with pytest.raises(ValueError):
+        cb.coeff_bwd(d["mix"][:, :20], d["pre"], d["post"], d["grad_pre"], d["grad_post"],
+                     d["grad_res"], d["alpha"], 2.0, 4)
+    with pytest.raises(ValueError):
+        cb.coeff_bwd(d["mix"].astype(np.float64), d["pre"], d["post"], d["grad_pre"],
+                     d["grad_post"], d["grad_res"], d["alpha"], 2.0, 4)
