@@ -142,7 +142,7 @@ def _loss64(mix, b, alpha, gp, gq, gr, c, n):
 
 
 @pytest.mark.parametrize("n", [2, 4, 8])
-@pytest.mark.parametrize("c", [1.0, 2.0])
+@pytest.mark.parametrize("c", [1.0, 2.0, 3.0])
 def test_gradients_match_finite_differences_of_the_forward(n, c):
     R, m = 5, cb.columns(n)
     rng = np.random.default_rng(100 + n)
@@ -210,6 +210,46 @@ def test_unit_post_scale_makes_post_like_pre():
     d["alpha"][1] = d["alpha"][0]
     gm, gb, _ = _run(d, 1.0, 4)
     assert np.array_equal(gm[:, :4], gm[:, 4:8]) and np.array_equal(gb[:4], gb[4:8])
+
+
+def _rn32(x) -> float:
+    """Exact rational -> nearest fp32 (ties to even), for positive normal x."""
+    from fractions import Fraction as Fr
+    x = Fr(x)
+    e = x.numerator.bit_length() - x.denominator.bit_length()
+    if Fr(2) ** e > x:
+        e -= 1
+    y = x * Fr(2) ** (23 - e)                 # in [2^23, 2^24)
+    fl = y.numerator // y.denominator
+    rem = y - fl
+    if rem > Fr(1, 2) or (rem == Fr(1, 2) and fl % 2 == 1):
+        fl += 1
+    return float(Fr(fl) * Fr(2) ** (e - 23))
+
+
+def test_post_gate_uses_the_fp32_reciprocal_of_the_scale():
+    # c = 3: 1/3 rounds to 11184811 * 2^-25. Find the first post value from
+    # 1.5 upward where d = rn(q * rn(1 - s)) differs between s = rn(q * ic)
+    # and s = rn(q / 3), in exact rational arithmetic (1 - s is exact for s
+    # in [1/2, 1]), and check that the oracle follows the reciprocal form.
+    from fractions import Fraction as Fr
+    ic = Fr(float(np.divide(np.float32(1), np.float32(3))))
+    assert ic == Fr(11184811, 2 ** 25)
+    q = np.float32(1.5)
+    for _ in range(100000):
+        Q = Fr(float(q))
+        want = _rn32(Q * (1 - Fr(_rn32(Q * ic))))
+        other = _rn32(Q * (1 - Fr(_rn32(Q / 3))))
+        if want != other:
+            break
+        q = np.nextafter(q, np.float32(3.0))
+    else:
+        raise AssertionError("no discriminating value found")
+    d = _inputs(1, 2, 8)
+    d["post"][0] = [q, q]
+    d["grad_post"][0] = [1.0, -1.0]
+    dz = cb.dz(d["pre"], d["post"], d["grad_pre"], d["grad_post"], d["grad_res"], 3.0)
+    assert dz[0, 2] == np.float32(want) and dz[0, 3] == np.float32(-want)
 
 
 def test_one_row_grad_b_is_the_row_derivative():
