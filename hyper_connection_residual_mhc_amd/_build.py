@@ -1,8 +1,12 @@
 """Build of the gfx950 library (hipcc, in-tree).
 
-Produces hyper_connection_residual_mhc_amd/lib/libmhc_h_aggregate.so from
-csrc/mhc_h_aggregate.hip and the public header in include/. The flags fix the
-arithmetic contract at build time:
+Produces, in hyper_connection_residual_mhc_amd/lib/, one shared library per
+operation from its source in csrc/ and its public header in include/:
+
+* libmhc_h_aggregate.so  (csrc/mhc_h_aggregate.hip, include/mhc_h_aggregate.h)
+* libmhc_coeff_bwd.so    (csrc/mhc_coeff_bwd.hip,   include/mhc_coeff_bwd.h)
+
+The flags fix the arithmetic contract at build time:
 
 * --offload-arch=gfx950           CDNA4 / MI355X code only
 * -ffp-contract=off               no multiply-add contraction (the source also
@@ -27,11 +31,17 @@ from pathlib import Path
 PKG_DIR = Path(__file__).resolve().parent
 REPO_DIR = PKG_DIR.parent
 SRC = PKG_DIR / "csrc" / "mhc_h_aggregate.hip"
+COEFF_SRC = PKG_DIR / "csrc" / "mhc_coeff_bwd.hip"
 INCLUDE_DIR = REPO_DIR / "include"
 HEADER = INCLUDE_DIR / "mhc_h_aggregate.h"
+COEFF_HEADER = INCLUDE_DIR / "mhc_coeff_bwd.h"
 LIB_DIR = PKG_DIR / "lib"
 LIB_PATH = LIB_DIR / "libmhc_h_aggregate.so"
+COEFF_LIB_PATH = LIB_DIR / "libmhc_coeff_bwd.so"
 BUILD_DIR = REPO_DIR / "_build"
+
+# source -> library, header
+LIBRARIES = {SRC: (LIB_PATH, HEADER), COEFF_SRC: (COEFF_LIB_PATH, COEFF_HEADER)}
 
 ARCH = "gfx950"
 
@@ -65,34 +75,42 @@ def _run(cmd: list[str]) -> None:
         print("\n".join(lines))
 
 
-def build_library(extra_flags: list[str] | None = None) -> Path:
-    """Compile the shared library; returns its path. Always recompiles."""
+def _build_one(src: Path, lib: Path, extra_flags: list[str] | None) -> Path:
     LIB_DIR.mkdir(parents=True, exist_ok=True)
-    fd, tmp = tempfile.mkstemp(prefix=".libmhc_h_aggregate.", suffix=".so.tmp", dir=LIB_DIR)
+    fd, tmp = tempfile.mkstemp(prefix=f".{lib.stem}.", suffix=".so.tmp", dir=LIB_DIR)
     os.close(fd)
     try:
         cmd = [hipcc(), *COMMON_FLAGS, "-fPIC", "-shared", *(extra_flags or []),
-               str(SRC), "-o", tmp]
+               str(src), "-o", tmp]
         _run(cmd)
-        os.replace(tmp, LIB_PATH)
+        os.replace(tmp, lib)
     finally:
         if os.path.exists(tmp):
             os.unlink(tmp)
+    return lib
+
+
+def build_library(extra_flags: list[str] | None = None) -> Path:
+    """Compile every shared library (always recompiles); returns the
+    h_aggregate library's path."""
+    for src, (lib, _) in LIBRARIES.items():
+        _build_one(src, lib, extra_flags)
     return LIB_PATH
 
 
-def device_asm(out: Path | None = None, extra_flags: list[str] | None = None) -> Path:
-    """Write the gfx950 assembly of the library source (same flags)."""
+def device_asm(out: Path | None = None, extra_flags: list[str] | None = None,
+               src: Path = SRC) -> Path:
+    """Write the gfx950 assembly of one library source (same flags)."""
     BUILD_DIR.mkdir(parents=True, exist_ok=True)
-    out = Path(out) if out else BUILD_DIR / f"mhc_h_aggregate-{ARCH}.s"
+    out = Path(out) if out else BUILD_DIR / f"{src.stem}-{ARCH}.s"
     cmd = [hipcc(), *COMMON_FLAGS, "--cuda-device-only", "-S", *(extra_flags or []),
-           str(SRC), "-o", str(out)]
+           str(src), "-o", str(out)]
     _run(cmd)
     return out
 
 
 def library_is_built() -> bool:
-    return LIB_PATH.exists()
+    return all(lib.exists() for lib, _ in LIBRARIES.values())
 
 
 if __name__ == "__main__":

@@ -1,15 +1,16 @@
-"""ctypes view of the C ABI in include/mhc_h_aggregate.h.
+"""ctypes view of the C ABIs in include/mhc_h_aggregate.h and
+include/mhc_coeff_bwd.h.
 
-Loading fails loudly (ImportError) when the shared library has not been
+Loading fails loudly (ImportError) when a shared library has not been
 built: there is no other implementation to fall back on.
 """
 
 from __future__ import annotations
 
 import ctypes
-from ctypes import POINTER, c_char_p, c_int, c_int32, c_int64, c_uint32, c_void_p
+from ctypes import POINTER, c_char_p, c_float, c_int, c_int32, c_int64, c_uint32, c_void_p
 
-from ._build import LIB_PATH
+from ._build import COEFF_LIB_PATH, LIB_PATH
 
 MHC_SUCCESS = 0
 MHC_ERROR_INVALID_VALUE = 1
@@ -85,7 +86,23 @@ SIGNATURES = {
                                  c_void_p, c_void_p, c_void_p]),
 }
 
+MHC_COEFF_ABI_VERSION = 1
+MHC_COEFF_CHUNK = 64
+MHC_COEFF_MAX_ROWS = 1 << 28
+
+# Every symbol include/mhc_coeff_bwd.h declares.
+COEFF_SIGNATURES = {
+    "mhc_coeff_abi_version": (c_int, []),
+    "mhc_coeff_last_error_message": (c_char_p, []),
+    "mhc_coeff_bwd_workspace_bytes": (c_int64, [c_int64, c_int32]),
+    "mhc_coeff_bwd_validate": (c_int, [c_void_p] * 7 + [c_float] + [c_void_p] * 4
+                               + [c_int64, c_int64, c_int32]),
+    "mhc_coeff_bwd": (c_int, [c_void_p] * 7 + [c_float] + [c_void_p] * 4
+                      + [c_int64, c_int64, c_int32, c_void_p, c_void_p, c_void_p]),
+}
+
 _lib: ctypes.CDLL | None = None
+_coeff: ctypes.CDLL | None = None
 
 
 def lib() -> ctypes.CDLL:
@@ -107,6 +124,26 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
+def coeff_lib() -> ctypes.CDLL:
+    """The coefficient-backward library (loaded once). Raises ImportError if
+    it is not built."""
+    global _coeff
+    if _coeff is None:
+        if not COEFF_LIB_PATH.exists():
+            raise ImportError(
+                f"{COEFF_LIB_PATH} is missing: build it with __graft_entry__.build() "
+                "(the operation has no other implementation)")
+        handle = ctypes.CDLL(str(COEFF_LIB_PATH))
+        for name, (restype, argtypes) in COEFF_SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = restype
+            fn.argtypes = argtypes
+        if handle.mhc_coeff_abi_version() != MHC_COEFF_ABI_VERSION:
+            raise ImportError("libmhc_coeff_bwd ABI version mismatch")
+        _coeff = handle
+    return _coeff
+
+
 class MhcError(RuntimeError):
     """A non-success status from the library, with its message."""
 
@@ -119,3 +156,8 @@ class MhcError(RuntimeError):
 def check(status: int) -> None:
     if status != MHC_SUCCESS:
         raise MhcError(status, lib().mhc_last_error_message().decode())
+
+
+def check_coeff(status: int) -> None:
+    if status != MHC_SUCCESS:
+        raise MhcError(status, coeff_lib().mhc_coeff_last_error_message().decode())

@@ -1,0 +1,357 @@
+// mhc_coeff_bwd.hip - gfx950 kernels and the C ABI of the mHC coefficient
+// backward epilogue.
+//
+// The operation is the epilogue of the page "perf: fuse mHC coefficient
+// backward epilogue" (Liger-Kernel pull request 1402), section Summary:
+// from the upstream gradients of the pre / post gates and of the
+// residual-mixing logits it forms the gradient of the coefficient
+// projection (grad_mix) and fixed-order sums over rows for the per-column
+// bias gradients and the three gain (alpha) gradients; section Risks and
+// Limitations: the sums run in a deterministic two-stage order. The page
+// prints no formulas; include/mhc_coeff_bwd.h states the reading this
+// library implements, bit for bit.
+//
+// Design for CDNA4 (MI355X):
+//  * The data are small (32n + 12n^2 bytes per row: 320 at n = 4, so 2.6 MB
+//    for the page's largest batch of 4 x 2048 tokens): the cost is two
+//    dispatches, not bandwidth. So: one producer launch with one wave per
+//    64-row chunk (a lane per row, every value of a row in registers) and
+//    one reducer launch with one wave per summed output.
+//  * The producer's per-chunk sums are the first stage of the order itself
+//    (a 64-lane halving tree in registers, lanes = rows), and the reducer's
+//    strided walk over the chunk sums plus the same tree is the second, so
+//    both launches compute exactly the defined order; the workspace holds
+//    the chunk sums column by column so that the reducer's loads of one
+//    output's sums are contiguous across lanes.
+//  * Rows past the end read as 0 through the buffer range check and produce
+//    exactly +0.0 everywhere, which is what the order prescribes for them;
+//    their grad_mix stores are dropped by the same check.
+//  * Bit exactness: contraction off (pragma and -ffp-contract=off), no
+//    fast-math, denormals kept, no division in a kernel (the post gate uses
+//    the host-rounded reciprocal of its scale).
+
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "mhc_coeff_bwd.h"
+#include "mhc_lanes.h"
+
+#if defined(__FAST_MATH__)
+#error "mhc_coeff_bwd must not be built with fast-math: its results are defined bit for bit"
+#endif
+
+#pragma clang fp contract(off)
+
+namespace {
+
+constexpr int kChunk = MHC_COEFF_CHUNK;  // rows per wave and per first-stage sum
+
+__device__ __forceinline__ float ld(Rsrc rs, uint32_t byte_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, byte_off, 0, 0));
+}
+
+__device__ __forceinline__ void st(Rsrc rs, uint32_t byte_off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, byte_off, 0, 0);
+}
+
+// The halving tree over the wave's 64 lanes: for off = 32, 16, 8, 4, 2, 1,
+// x[i] += x[i + off] for i < off; lane 0 ends with the tree's sum.
+template <int K>
+__device__ __forceinline__ void wave_trees(float (&v)[K]) {
+#pragma unroll
+  for (int i = 0; i < K; ++i) v[i] = v[i] + from_lane_plus<32>(v[i]);
+#pragma unroll
+  for (int i = 0; i < K; ++i) v[i] = v[i] + from_lane_plus<16>(v[i]);
+#pragma unroll
+  for (int i = 0; i < K; ++i) v[i] = v[i] + from_lane_plus<8>(v[i]);
+#pragma unroll
+  for (int i = 0; i < K; ++i) v[i] = v[i] + from_lane_plus<4>(v[i]);
+#pragma unroll
+  for (int i = 0; i < K; ++i) v[i] = v[i] + from_lane_plus<2>(v[i]);
+#pragma unroll
+  for (int i = 0; i < K; ++i) v[i] = v[i] + from_lane_plus<1>(v[i]);
+}
+
+// ---------------------------------------------------------------------------
+// Producer: one wave per chunk of 64 rows, lane = row.
+// ---------------------------------------------------------------------------
+//
+// Grid: `chunks` blocks of 64 threads. Writes grad_mix for the chunk's rows
+// and, for each of the m + 3 summed quantities v (d of every column, then
+// e of the three groups), the chunk's first-stage sum to
+// partial[v * chunks + chunk].
+template <int N>
+__global__ __launch_bounds__(64) void coeff_partial_kernel(
+    const float* __restrict__ mix, const float* __restrict__ pre,
+    const float* __restrict__ post, const float* __restrict__ grad_pre,
+    const float* __restrict__ grad_post, const float* __restrict__ grad_res,
+    const float* __restrict__ alpha, float inv_c, float* __restrict__ grad_mix,
+    float* __restrict__ partial, int64_t rows, uint32_t chunks) {
+  constexpr int M = 2 * N + N * N;
+  const uint32_t lane = threadIdx.x;
+  const uint32_t c = blockIdx.x;
+  const int64_t r0 = static_cast<int64_t>(c) * kChunk;
+  const int64_t valid = rows - r0 < kChunk ? rows - r0 : kChunk;
+
+  // Resources cover exactly the chunk's valid rows.
+  const Rsrc rs_mix = make_rsrc(mix + r0 * M, valid * M * 4);
+  const Rsrc rs_pre = make_rsrc(pre + r0 * N, valid * N * 4);
+  const Rsrc rs_post = make_rsrc(post + r0 * N, valid * N * 4);
+  const Rsrc rs_gpre = make_rsrc(grad_pre + r0 * N, valid * N * 4);
+  const Rsrc rs_gpost = make_rsrc(grad_post + r0 * N, valid * N * 4);
+  const Rsrc rs_gres = make_rsrc(grad_res + r0 * N * N, valid * N * N * 4);
+  const Rsrc rs_gmix = make_rsrc(grad_mix + r0 * M, valid * M * 4);
+  const float a_pre = alpha[0], a_post = alpha[1], a_res = alpha[2];
+
+  float d[M];
+  float x[M];
+#pragma unroll
+  for (int j = 0; j < M; ++j) x[j] = ld(rs_mix, (lane * M + j) * 4);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float p = ld(rs_pre, (lane * N + i) * 4);
+    const float gp = ld(rs_gpre, (lane * N + i) * 4);
+    d[i] = gp * (p * (1.0f - p));
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float q = ld(rs_post, (lane * N + i) * 4);
+    const float gq = ld(rs_gpost, (lane * N + i) * 4);
+    d[N + i] = gq * (q * (1.0f - q * inv_c));
+  }
+#pragma unroll
+  for (int i = 0; i < N * N; ++i) d[2 * N + i] = ld(rs_gres, (lane * N * N + i) * 4);
+
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    const float a = j < N ? a_pre : (j < 2 * N ? a_post : a_res);
+    st(rs_gmix, (lane * M + j) * 4, a * d[j]);
+  }
+
+  float v[M + 3];
+  v[M] = 0.0f;
+  v[M + 1] = 0.0f;
+  v[M + 2] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    const int k = j < N ? 0 : (j < 2 * N ? 1 : 2);
+    v[M + k] = v[M + k] + d[j] * x[j];
+    v[j] = d[j];
+  }
+  wave_trees(v);
+  if (lane == 0) {
+    const Rsrc rs_part = make_rsrc(partial, static_cast<int64_t>(M + 3) * chunks * 4);
+#pragma unroll
+    for (int i = 0; i < M + 3; ++i) st(rs_part, (static_cast<uint32_t>(i) * chunks + c) * 4, v[i]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Reducer: one wave per summed output.
+// ---------------------------------------------------------------------------
+//
+// Grid: m + 3 blocks of 64 threads. Block v walks the chunk sums of output v
+// with lane l taking chunks l, l + 64, ... in ascending order, then sums the
+// 64 lanes with the halving tree. Outputs v < m go to grad_b[v], the last
+// three to grad_alpha.
+__global__ __launch_bounds__(64) void coeff_reduce_kernel(const float* __restrict__ partial,
+                                                          uint32_t chunks, int32_t m,
+                                                          float* __restrict__ grad_b,
+                                                          float* __restrict__ grad_alpha) {
+  const uint32_t lane = threadIdx.x;
+  const uint32_t v = blockIdx.x;
+  const Rsrc rs = make_rsrc(partial + static_cast<int64_t>(v) * chunks,
+                            static_cast<int64_t>(chunks) * 4);
+  float acc[1] = {0.0f};
+  // Every lane runs the same trip count; past the last chunk the range
+  // check reads +0.0, and adding +0.0 to a sum that started at +0.0 leaves
+  // it unchanged.
+  const uint32_t rounds = (chunks + 63) / 64;
+  for (uint32_t k = 0; k < rounds; ++k) acc[0] = acc[0] + ld(rs, (k * 64 + lane) * 4);
+  wave_trees(acc);
+  if (lane == 0) {
+    const bool bias = static_cast<int32_t>(v) < m;
+    const Rsrc out = bias ? make_rsrc(grad_b, static_cast<int64_t>(m) * 4) : make_rsrc(grad_alpha, 12);
+    st(out, (bias ? v : v - m) * 4, acc[0]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+
+thread_local char g_msg[256] = "";
+
+mhc_status fail(mhc_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+mhc_status fail(mhc_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+mhc_status ok() {
+  g_msg[0] = '\0';
+  return MHC_SUCCESS;
+}
+
+int columns(int32_t n) { return 2 * n + n * n; }
+
+int64_t chunk_count(int64_t rows) { return (rows + kChunk - 1) / kChunk; }
+
+int64_t workspace_need(int64_t rows, int32_t n) {
+  return static_cast<int64_t>(columns(n) + 3) * chunk_count(rows) * 4;
+}
+
+struct Range {
+  uintptr_t lo, hi;
+  const char* name;
+};
+
+Range range(const void* p, int64_t bytes, const char* name) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + static_cast<uintptr_t>(bytes), name};
+}
+
+bool overlap(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+mhc_status need_ptr(const void* p, const char* name) {
+  if (p == nullptr) return fail(MHC_ERROR_INVALID_VALUE, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(p) % 4 != 0)
+    return fail(MHC_ERROR_INVALID_VALUE, "%s is not 4-byte aligned", name);
+  return ok();
+}
+
+mhc_status validate(const float* mix, const float* pre, const float* post,
+                    const float* grad_pre, const float* grad_post, const float* grad_res,
+                    const float* alpha, float post_scale, const float* grad_mix,
+                    const float* grad_b, const float* grad_alpha, const void* workspace,
+                    int64_t workspace_bytes, int64_t rows, int32_t n) {
+  if (n != 2 && n != 4 && n != 8)
+    return fail(MHC_ERROR_INVALID_VALUE, "the expansion rate n must be 2, 4 or 8 (got %d)", n);
+  if (rows < 0 || rows > MHC_COEFF_MAX_ROWS)
+    return fail(MHC_ERROR_INVALID_VALUE, "rows must be in [0, %lld] (got %lld)",
+                (long long)MHC_COEFF_MAX_ROWS, (long long)rows);
+  if (!(post_scale > 0.0f) || !isfinite(post_scale))
+    return fail(MHC_ERROR_INVALID_VALUE, "post_scale must be finite and positive (got %g)",
+                (double)post_scale);
+  if (!isfinite(1.0f / post_scale) || 1.0f / post_scale == 0.0f)
+    return fail(MHC_ERROR_INVALID_VALUE, "1 / post_scale is not a finite non-zero fp32 (%g)",
+                (double)post_scale);
+  const int m = columns(n);
+  const int64_t need = workspace_need(rows, n);
+  mhc_status st;
+  if ((st = need_ptr(grad_b, "grad_b")) != MHC_SUCCESS) return st;
+  if ((st = need_ptr(grad_alpha, "grad_alpha")) != MHC_SUCCESS) return st;
+  if (rows > 0) {
+    const void* ps[] = {mix, pre, post, grad_pre, grad_post, grad_res, alpha, grad_mix, workspace};
+    const char* names[] = {"mix", "pre", "post", "grad_pre", "grad_post", "grad_res", "alpha",
+                           "grad_mix", "workspace"};
+    for (int i = 0; i < 9; ++i)
+      if ((st = need_ptr(ps[i], names[i])) != MHC_SUCCESS) return st;
+  }
+  if (workspace_bytes < need)
+    return fail(MHC_ERROR_INVALID_VALUE, "workspace_bytes %lld < %lld needed",
+                (long long)workspace_bytes, (long long)need);
+  const Range ins[] = {range(mix, rows * m * 4, "mix"), range(pre, rows * n * 4, "pre"),
+                       range(post, rows * n * 4, "post"), range(grad_pre, rows * n * 4, "grad_pre"),
+                       range(grad_post, rows * n * 4, "grad_post"),
+                       range(grad_res, rows * n * n * 4, "grad_res"),
+                       range(alpha, rows > 0 ? 12 : 0, "alpha")};
+  const Range outs[] = {range(grad_mix, rows * m * 4, "grad_mix"), range(grad_b, m * 4, "grad_b"),
+                        range(grad_alpha, 12, "grad_alpha"), range(workspace, need, "workspace")};
+  for (int a = 0; a < 4; ++a) {
+    for (int b = 0; b < 7; ++b)
+      if (overlap(outs[a], ins[b]))
+        return fail(MHC_ERROR_ALIASING, "output %s overlaps input %s", outs[a].name, ins[b].name);
+    for (int b = a + 1; b < 4; ++b)
+      if (overlap(outs[a], outs[b]))
+        return fail(MHC_ERROR_ALIASING, "output %s overlaps output %s", outs[a].name,
+                    outs[b].name);
+  }
+  return ok();
+}
+
+template <int N>
+void launch_partial(const float* mix, const float* pre, const float* post, const float* grad_pre,
+                    const float* grad_post, const float* grad_res, const float* alpha,
+                    float inv_c, float* grad_mix, float* partial, int64_t rows, uint32_t chunks,
+                    hipStream_t s, hipEvent_t start) {
+  hipExtLaunchKernelGGL(coeff_partial_kernel<N>, dim3(chunks), dim3(64), 0, s, start, nullptr, 0,
+                        mix, pre, post, grad_pre, grad_post, grad_res, alpha, inv_c, grad_mix,
+                        partial, rows, chunks);
+}
+
+mhc_status launch_error(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(MHC_ERROR_HIP, "%s launch failed: %s (%s)", what, hipGetErrorName(e),
+                hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+
+extern "C" {
+
+int mhc_coeff_abi_version(void) { return MHC_COEFF_ABI_VERSION; }
+
+const char* mhc_coeff_last_error_message(void) { return g_msg; }
+
+int64_t mhc_coeff_bwd_workspace_bytes(int64_t rows, int32_t n) {
+  if ((n != 2 && n != 4 && n != 8) || rows < 0 || rows > MHC_COEFF_MAX_ROWS) return -1;
+  return workspace_need(rows, n);
+}
+
+mhc_status mhc_coeff_bwd_validate(const float* mix, const float* pre, const float* post,
+                                  const float* grad_pre, const float* grad_post,
+                                  const float* grad_res, const float* alpha, float post_scale,
+                                  const float* grad_mix, const float* grad_b,
+                                  const float* grad_alpha, const void* workspace,
+                                  int64_t workspace_bytes, int64_t rows, int32_t n) {
+  return validate(mix, pre, post, grad_pre, grad_post, grad_res, alpha, post_scale, grad_mix,
+                  grad_b, grad_alpha, workspace, workspace_bytes, rows, n);
+}
+
+mhc_status mhc_coeff_bwd(const float* mix, const float* pre, const float* post,
+                         const float* grad_pre, const float* grad_post, const float* grad_res,
+                         const float* alpha, float post_scale, float* grad_mix, float* grad_b,
+                         float* grad_alpha, void* workspace, int64_t workspace_bytes,
+                         int64_t rows, int32_t n, void* stream, void* start_event,
+                         void* stop_event) {
+  mhc_status st = validate(mix, pre, post, grad_pre, grad_post, grad_res, alpha, post_scale,
+                           grad_mix, grad_b, grad_alpha, workspace, workspace_bytes, rows, n);
+  if (st != MHC_SUCCESS) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t start = static_cast<hipEvent_t>(start_event);
+  hipEvent_t stop = static_cast<hipEvent_t>(stop_event);
+  const uint32_t chunks = static_cast<uint32_t>(chunk_count(rows));
+  const float inv_c = 1.0f / post_scale;  // rounded to fp32 once
+  float* partial = static_cast<float*>(workspace);
+  (void)hipGetLastError();
+  if (chunks > 0) {
+    switch (n) {
+      case 2: launch_partial<2>(mix, pre, post, grad_pre, grad_post, grad_res, alpha, inv_c, grad_mix, partial, rows, chunks, s, start); break;
+      case 4: launch_partial<4>(mix, pre, post, grad_pre, grad_post, grad_res, alpha, inv_c, grad_mix, partial, rows, chunks, s, start); break;
+      default: launch_partial<8>(mix, pre, post, grad_pre, grad_post, grad_res, alpha, inv_c, grad_mix, partial, rows, chunks, s, start); break;
+    }
+    if ((st = launch_error("coefficient backward (chunk sums)")) != MHC_SUCCESS) return st;
+  }
+  const int m = columns(n);
+  hipExtLaunchKernelGGL(coeff_reduce_kernel, dim3(m + 3), dim3(64), 0, s,
+                        chunks > 0 ? nullptr : start, stop, 0, partial, chunks, m, grad_b,
+                        grad_alpha);
+  return launch_error("coefficient backward (reduction)");
+}
+
+}  // extern "C"

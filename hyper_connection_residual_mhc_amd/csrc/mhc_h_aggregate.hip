@@ -36,6 +36,7 @@
 #include <string.h>
 
 #include "mhc_h_aggregate.h"
+#include "mhc_lanes.h"
 
 #if defined(__FAST_MATH__)
 #error "mhc_h_aggregate must not be built with fast-math: its results are defined bit for bit"
@@ -116,15 +117,14 @@ template <> __device__ __forceinline__ uint16_t pack<1>(const float (&y)[1]) {
 }
 
 // Memory access: CDNA buffer instructions. A row (or a token's rows) is
-// described by a buffer resource (base address and byte length, held in
-// scalar registers, wave-uniform), each lane supplies one 32-bit byte offset.
+// described by a buffer resource (make_rsrc in mhc_lanes.h: base address and
+// byte length, held in scalar registers, wave-uniform), each lane supplies
+// one 32-bit byte offset.
 // Accesses past the resource's length are dropped by the hardware (loads
 // return 0), so no lane can touch memory outside the row it was given.
 // Streamed bytes are touched once, so loads carry the nontemporal hint; the
 // one row several waves read (the backward's grad_out in the row layout)
 // keeps the default policy so that it stays in cache for them.
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-constexpr int kRsrcFormat = 0x00020000;  // gfx9 resource word 3: raw 32-bit data
 constexpr int kNontemporal = 2;          // cache-policy bit 1: nt
 constexpr int kCached = 0;               // default policy: kept for other readers
 // Cache-policy bit 4 (sc1): device-scope store, written through the L2 at
@@ -132,11 +132,6 @@ constexpr int kCached = 0;               // default policy: kept for other reade
 // written) streams 5-8% faster with it than with nt; the backward (5:4) and
 // the accumulating backward (9:4) stream 2-4% slower, so they keep nt.
 constexpr int kWriteThrough = 16;
-
-__device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
-                                           static_cast<int>(bytes), kRsrcFormat);
-}
 
 // Load V bf16 elements at element `off` (per lane) plus `soff` bytes
 // (wave-uniform, carried in a scalar register) from the resource, with
@@ -252,26 +247,6 @@ __global__ __launch_bounds__(1024) void hagg_fwd_kernel(
 
 constexpr int kGroup = 8;
 constexpr int kLanes = 256;
-
-// Lane j (< OFF) of a wave receives x from lane j + OFF; other lanes receive
-// values that are never read. Register-only lane movement on gfx950:
-// permlane32_swap brings the upper half-wave down, permlane16_swap the odd
-// 16-lane rows onto the even ones, and DPP row_shl:n reads lane j + n within
-// a 16-lane row. The whole wave must be active (it is: the tree runs after
-// the divergent loop has reconverged).
-template <int OFF>
-__device__ __forceinline__ float from_lane_plus(float x) {
-  const uint32_t u = __float_as_uint(x);
-  if constexpr (OFF == 32) {
-    return __uint_as_float(__builtin_amdgcn_permlane32_swap(u, u, false, false)[1]);
-  } else if constexpr (OFF == 16) {
-    return __uint_as_float(__builtin_amdgcn_permlane16_swap(u, u, false, false)[1]);
-  } else {
-    static_assert(OFF == 8 || OFF == 4 || OFF == 2 || OFF == 1, "row shift within 16 lanes");
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, static_cast<int>(u), 0x100 + OFF, 0xF,
-                                                      0xF, false));
-  }
-}
 
 // The register slots of the backward's ring of loads: for each of U groups,
 // the grad_out vector(s), the S residual vectors and (accumulating form) the

@@ -48,6 +48,32 @@ def make_inputs(T: int, H: int, seed: int = 0, *, grad: bool = False,
     return out
 
 
+def make_coeff_inputs(rows: int, n: int = HC, seed: int = 0, *,
+                      post_scale: float = 2.0) -> dict[str, np.ndarray]:
+    """Host inputs of the coefficient backward epilogue (all float32).
+
+    Recipe (the page "perf: fuse mHC coefficient backward epilogue" gives the
+    shapes, B = 4 sequences of T in {128, 512, 2048} tokens at HC = 4, but no
+    value distributions): rng = numpy.random.default_rng(seed), drawing in
+    this order: mix [R, m] standard normal (m = 2n + n*n); pre [R, n] U[0,1)
+    (a sigmoid output); post [R, n] U[0,1) times post_scale (a scaled
+    sigmoid output); grad_pre, grad_post [R, n] and grad_res [R, n*n]
+    standard normal; alpha [3] U[0.5, 1.5).
+    """
+    rng = np.random.default_rng(seed)
+    m = 2 * n + n * n
+    f = lambda a: np.ascontiguousarray(a, dtype=np.float32)
+    return {
+        "mix": f(rng.standard_normal((rows, m), dtype=np.float32)),
+        "pre": f(rng.random((rows, n), dtype=np.float32)),
+        "post": f(rng.random((rows, n), dtype=np.float32) * np.float32(post_scale)),
+        "grad_pre": f(rng.standard_normal((rows, n), dtype=np.float32)),
+        "grad_post": f(rng.standard_normal((rows, n), dtype=np.float32)),
+        "grad_res": f(rng.standard_normal((rows, n * n), dtype=np.float32)),
+        "alpha": f(rng.uniform(0.5, 1.5, 3)),
+    }
+
+
 def bits_to_bf16_tensor(bits: np.ndarray, device="cpu") -> torch.Tensor:
     """uint16 bf16 patterns -> torch.bfloat16 tensor (same bits)."""
     t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)

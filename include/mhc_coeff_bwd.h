@@ -1,0 +1,120 @@
+/*
+ * mhc_coeff_bwd.h - C ABI of the MI355X (gfx950) mHC coefficient backward
+ * epilogue: the step after the Sinkhorn backward that turns the upstream
+ * gradients of the pre / post gates and of the residual-mixing logits into
+ * the gradient of the coefficient projection and the bias and gain
+ * gradients.
+ *
+ * Operation (page "perf: fuse mHC coefficient backward epilogue",
+ * Liger-Kernel pull request 1402, section Summary: the pre/post sigmoid
+ * derivatives, grad_mix and fp32 partial sums for grad_b and the alpha
+ * gradients, then a deterministic reducer for the bias columns and the three
+ * scalar alpha gradients; section Risks and Limitations: a fixed two-stage
+ * reduction order). The page prints no formulas; this library implements
+ * the following reading of it.
+ *
+ * Expansion n in {2, 4, 8}; m = 2n + n*n coefficient columns (24 at n = 4):
+ * columns [0, n) are the pre gates, [n, 2n) the post gates, [2n, m) the
+ * n x n residual-mixing logits in row-major order. Column j belongs to group
+ * k(j) = 0, 1, 2 respectively. The forward being differentiated is
+ *     z[r,j] = alpha[k(j)] * mix[r,j] + b[j]
+ *     pre    = sigmoid(z[:, 0:n])
+ *     post   = c * sigmoid(z[:, n:2n])           (c = post_scale)
+ *     z[:, 2n:m] -> Sinkhorn normalisation (its backward supplies grad_res)
+ * and, per row r (R rows; every row is one token of one batch entry):
+ *     d[r,j] = grad_pre[r,j]  * (pre[r,j]  * (1 - pre[r,j]))                j <  n
+ *     d[r,j] = grad_post[r,i] * (post[r,i] * (1 - post[r,i] * inv_c))       i = j - n
+ *     d[r,j] = grad_res[r,j-2n]                                             j >= 2n
+ *     grad_mix[r,j] = alpha[k(j)] * d[r,j]
+ *     e[r,k]        = sum over j of group k, ascending, from +0.0, of d[r,j] * mix[r,j]
+ *     grad_b[j]     = row_sum of d[:,j]
+ *     grad_alpha[k] = row_sum of e[:,k]
+ * inv_c is 1/c rounded to fp32 once (on the host). Every product, sum and
+ * difference is one fp32 round-to-nearest-even operation in exactly the
+ * nesting written, never fused.
+ *
+ * row_sum (fixed; depends only on R):
+ *   1. rows are cut into chunks of 64 consecutive rows (rows past R count as
+ *      +0.0); each chunk is summed by the halving tree: for off = 32, 16, 8,
+ *      4, 2, 1 in that order, x[i] += x[i+off] for all i < off; the chunk
+ *      sum is x[0];
+ *   2. 64 accumulators start at +0.0; chunk sum c is added to accumulator
+ *      c mod 64, in ascending c; the 64 accumulators are summed by the same
+ *      halving tree.
+ * With R = 0 both sums are +0.0.
+ *
+ * Tensors (fp32, contiguous, row-major; DEVICE pointers on the current HIP
+ * device, owned by the caller):
+ *     mix [R, m], pre [R, n], post [R, n], grad_pre [R, n], grad_post [R, n],
+ *     grad_res [R, n*n], alpha [3]                                  (inputs)
+ *     grad_mix [R, m], grad_b [m], grad_alpha [3]                   (outputs)
+ *     workspace: mhc_coeff_bwd_workspace_bytes(R, n) bytes of device memory
+ *     the call may overwrite (the per-chunk sums); its contents before and
+ *     after the call mean nothing to the caller. NULL is allowed when that
+ *     size is 0.
+ *
+ * Rules: calls enqueue two kernels on `stream` (a hipStream_t cast to void*,
+ * NULL = null stream) and never synchronise; inputs must stay valid until
+ * the stream reaches them. The library allocates nothing. n not in {2,4,8},
+ * R < 0, R > MHC_COEFF_MAX_ROWS, c not finite and positive, a NULL or
+ * non-4-byte-aligned pointer that the call needs (the row tensors, alpha and
+ * the workspace when R > 0; grad_b and grad_alpha always), or a workspace
+ * smaller than required give MHC_ERROR_INVALID_VALUE; any overlap between an
+ * output (the workspace counts as one) and an input or another output gives
+ * MHC_ERROR_ALIASING. On either error nothing is launched and nothing is
+ * written. A failed launch gives MHC_ERROR_HIP. mhc_coeff_last_error_message
+ * describes the most recent failure on the calling thread. The status codes
+ * are those of mhc_h_aggregate.h.
+ */
+#ifndef MHC_COEFF_BWD_H
+#define MHC_COEFF_BWD_H
+
+#include <stdint.h>
+
+#include "mhc_h_aggregate.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MHC_COEFF_ABI_VERSION 1
+
+/* Rows per first-stage chunk of row_sum. */
+#define MHC_COEFF_CHUNK 64
+
+/* Most rows one call accepts (2^28: keeps every workspace byte offset and
+ * buffer range within 31 bits at every expansion rate). */
+#define MHC_COEFF_MAX_ROWS (1LL << 28)
+
+int mhc_coeff_abi_version(void);
+
+const char* mhc_coeff_last_error_message(void);
+
+/* Bytes of workspace a call with R rows at expansion n needs:
+ * (m + 3) * ceil(R / 64) * 4. Returns -1 for an invalid n or R. */
+int64_t mhc_coeff_bwd_workspace_bytes(int64_t rows, int32_t n);
+
+/* Checks the arguments exactly as mhc_coeff_bwd does, on the host only:
+ * touches no device memory and launches nothing. */
+mhc_status mhc_coeff_bwd_validate(const float* mix, const float* pre, const float* post,
+                                  const float* grad_pre, const float* grad_post,
+                                  const float* grad_res, const float* alpha, float post_scale,
+                                  const float* grad_mix, const float* grad_b,
+                                  const float* grad_alpha, const void* workspace,
+                                  int64_t workspace_bytes, int64_t rows, int32_t n);
+
+/* The epilogue described above. start_event / stop_event (hipEvent_t cast to
+ * void*, each may be NULL) are recorded when the first of the call's kernels
+ * starts and when the last one ends. */
+mhc_status mhc_coeff_bwd(const float* mix, const float* pre, const float* post,
+                         const float* grad_pre, const float* grad_post, const float* grad_res,
+                         const float* alpha, float post_scale, float* grad_mix, float* grad_b,
+                         float* grad_alpha, void* workspace, int64_t workspace_bytes,
+                         int64_t rows, int32_t n, void* stream, void* start_event,
+                         void* stop_event);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHC_COEFF_BWD_H */

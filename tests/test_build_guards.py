@@ -11,7 +11,11 @@ own gfx950 machine code (compiled here; no GPU needed).
 * no store of more than 8 bytes is followed at once by an instruction that
   overwrites its data registers (gfx950 reads such data over several cycles;
   an immediate overwrite was measured to corrupt the last lanes' data);
+* no scalar memory writes, and no division in the coefficient kernels;
 * the product path never imports the oracle.
+
+Both library sources are checked (the h_aggregate kernels and the
+coefficient-backward epilogue's kernels).
 """
 
 from __future__ import annotations
@@ -30,10 +34,10 @@ FORBIDDEN = re.compile(
     r"v_pk_add_f32|v_fma_f64|v_fma_f16|v_pk_fma_f16)\b")
 
 
-@pytest.fixture(scope="module")
-def asm(tmp_path_factory) -> str:
-    out = tmp_path_factory.mktemp("asm") / "mhc.s"
-    return _build.device_asm(out).read_text()
+@pytest.fixture(scope="module", params=[_build.SRC, _build.COEFF_SRC], ids=lambda p: p.stem)
+def asm(request, tmp_path_factory) -> str:
+    out = tmp_path_factory.mktemp("asm") / f"{request.param.stem}.s"
+    return _build.device_asm(out, src=request.param).read_text()
 
 
 def kernel_blocks(asm: str) -> dict[str, str]:
@@ -46,10 +50,22 @@ def kernel_blocks(asm: str) -> dict[str, str]:
 
 def test_kernels_present(asm):
     names = list(kernel_blocks(asm))
+    if any("coeff_" in n for n in names):
+        assert sum("coeff_partial_kernel" in n for n in names) == 3
+        assert sum("coeff_reduce_kernel" in n for n in names) == 1
+        assert not any("hagg_" in n for n in names)
+        return
     assert any("hagg_fwd_kernel" in n for n in names)
     assert any("hagg_bwd_kernel" in n for n in names)
     assert any("bf16_probe_kernel" in n for n in names)
     assert sum("stream_probe_kernel" in n for n in names) == 4
+
+
+def test_no_scalar_memory_writes(asm):
+    """Every store goes through the vector memory path."""
+    hits = re.findall(r"^\s*(s_store\w*|s_buffer_store\w*|s_scratch_store\w*|s_atomic\w*|"
+                      r"s_buffer_atomic\w*|s_dcache_wb\w*|s_dcache_discard\w*)", asm, flags=re.M)
+    assert not hits, sorted(set(hits))
 
 
 def test_no_fused_or_packed_float_ops(asm):
@@ -60,15 +76,22 @@ def test_no_fused_or_packed_float_ops(asm):
 
 def test_separate_fp32_mul_and_add_present(asm):
     for name, body in kernel_blocks(asm).items():
-        if "hagg_" in name:
+        if "hagg_" in name or "coeff_partial" in name:
             assert "v_mul_f32" in body and "v_add_f32" in body, name
 
 
 def test_bf16_results_use_rne_pack_conversion(asm):
     for name, body in kernel_blocks(asm).items():
-        if "stream_probe_kernel" in name:
-            continue  # moves bytes only, produces no bf16 value
+        if "stream_probe_kernel" in name or "coeff_" in name:
+            continue  # no bf16 value produced (a byte stream; fp32 in and out)
         assert "v_cvt_pk_bf16_f32" in body, name
+
+
+def test_no_division_in_the_coefficient_kernels(asm):
+    """The post gate multiplies by the host-rounded reciprocal of its scale."""
+    for name, body in kernel_blocks(asm).items():
+        if "coeff_" in name:
+            assert not re.search(r"\bv_(div_\w+|rcp_\w+)", body), name
 
 
 STORE_WIDE = re.compile(
@@ -152,9 +175,10 @@ def test_no_scratch_spills(asm):
     assert "scratch_store" not in asm and "buffer_store_dword off" not in asm
 
 
-def test_fast_math_build_is_refused(tmp_path):
+@pytest.mark.parametrize("src", [_build.SRC, _build.COEFF_SRC], ids=lambda p: p.stem)
+def test_fast_math_build_is_refused(tmp_path, src):
     cmd = [_build.hipcc(), *_build.COMMON_FLAGS, "-ffast-math", "--cuda-device-only", "-S",
-           str(_build.SRC), "-o", str(tmp_path / "fm.s")]
+           str(src), "-o", str(tmp_path / "fm.s")]
     proc = subprocess.run(cmd, capture_output=True, text=True)
     assert proc.returncode != 0
     assert "must not be built with fast-math" in proc.stdout + proc.stderr
@@ -166,8 +190,8 @@ def test_build_flags_fix_the_contract():
     assert "-ffp-contract=off" in flags
     assert "-packed-fp32-ops" in flags
     assert "fast-math" not in flags and "-ffast" not in flags
-    src = _build.SRC.read_text()
-    assert "#pragma clang fp contract(off)" in src
+    for path in (_build.SRC, _build.COEFF_SRC):
+        assert "#pragma clang fp contract(off)" in path.read_text(), path
 
 
 def test_product_path_does_not_touch_the_oracle():

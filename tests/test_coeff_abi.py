@@ -1,0 +1,167 @@
+"""The coefficient-backward C ABI on the host (include/mhc_coeff_bwd.h):
+symbols, workspace size and argument rules. No GPU: only host-only entry
+points are called, and the compute entry point only with arguments it
+rejects before any HIP call."""
+
+from __future__ import annotations
+
+import re
+import subprocess
+
+import pytest
+
+from hyper_connection_residual_mhc_amd import _build, _lib
+from hyper_connection_residual_mhc_amd._lib import (MHC_ERROR_ALIASING, MHC_ERROR_INVALID_VALUE,
+                                                    MHC_SUCCESS)
+
+GiB = 1 << 30
+BASE = 16 * GiB
+
+
+@pytest.fixture(scope="module")
+def lib(built_library):
+    return _lib.coeff_lib()
+
+
+def test_header_declarations_are_all_exported(lib):
+    text = re.sub(r"/\*.*?\*/", "", _build.COEFF_HEADER.read_text(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(mhc_\w+)\s*\(", text)))
+    assert len(names) == 5, names
+    out = subprocess.run(["nm", "-D", "--defined-only", str(_build.COEFF_LIB_PATH)],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (mhc_\w+)$", out, flags=re.M))
+    assert set(names) <= exported, set(names) - exported
+    assert set(_lib.COEFF_SIGNATURES) == set(names)
+    ours = [s for s in re.findall(r"\bT (\S+)$", out, flags=re.M) if "mhc" in s or "coeff" in s]
+    assert all(s.startswith("mhc_coeff_") for s in ours), ours
+
+
+def test_constants_match_the_header(lib):
+    text = _build.COEFF_HEADER.read_text()
+    assert f"#define MHC_COEFF_ABI_VERSION {_lib.MHC_COEFF_ABI_VERSION}" in text
+    assert f"#define MHC_COEFF_CHUNK {_lib.MHC_COEFF_CHUNK}" in text
+    assert "#define MHC_COEFF_MAX_ROWS (1LL << 28)" in text and _lib.MHC_COEFF_MAX_ROWS == 1 << 28
+    assert lib.mhc_coeff_abi_version() == _lib.MHC_COEFF_ABI_VERSION
+
+
+@pytest.mark.parametrize("n,m", [(2, 8), (4, 24), (8, 80)])
+def test_workspace_bytes(lib, n, m):
+    f = lib.mhc_coeff_bwd_workspace_bytes
+    assert f(0, n) == 0
+    assert f(1, n) == (m + 3) * 4
+    assert f(64, n) == (m + 3) * 4
+    assert f(65, n) == 2 * (m + 3) * 4
+    assert f(8192, n) == 128 * (m + 3) * 4
+    assert f(1 << 28, n) == (1 << 22) * (m + 3) * 4 < (1 << 31)
+    assert f(-1, n) == -1 and f((1 << 28) + 1, n) == -1
+
+
+def test_workspace_bytes_rejects_bad_n(lib):
+    assert lib.mhc_coeff_bwd_workspace_bytes(10, 3) == -1
+
+
+class Args:
+    """Disjoint fake device addresses for every tensor of an R-row call."""
+
+    def __init__(self, lib, R, n, ws_extra=0):
+        m = 2 * n + n * n
+        sizes = [R * m, R * n, R * n, R * n, R * n, R * n * n, 3, R * m, m, 3]
+        addr, self.p = BASE, []
+        for s in sizes:
+            self.p.append(addr)
+            addr += ((s * 4 + 255) // 256 + 1) * 256
+        self.ws = addr
+        self.ws_bytes = lib.mhc_coeff_bwd_workspace_bytes(R, n) + ws_extra
+        self.R, self.n, self.c = R, n, 2.0
+
+    def tuple(self):
+        p = self.p
+        return (p[0], p[1], p[2], p[3], p[4], p[5], p[6], self.c, p[7], p[8], p[9], self.ws,
+                self.ws_bytes, self.R, self.n)
+
+
+def test_valid_arguments_pass(lib):
+    for n in (2, 4, 8):
+        for R in (0, 1, 65, 8192):
+            assert lib.mhc_coeff_bwd_validate(*Args(lib, R, n).tuple()) == MHC_SUCCESS
+
+
+def test_zero_rows_allow_null_row_tensors_but_not_sum_outputs(lib):
+    a = Args(lib, 0, 4)
+    t = list(a.tuple())
+    for i in (0, 1, 2, 3, 4, 5, 6, 8, 11):
+        t[i] = None
+    assert lib.mhc_coeff_bwd_validate(*t) == MHC_SUCCESS
+    t2 = list(t)
+    t2[9] = None                               # grad_b
+    assert lib.mhc_coeff_bwd_validate(*t2) == MHC_ERROR_INVALID_VALUE
+    t2 = list(t)
+    t2[10] = None                              # grad_alpha
+    assert lib.mhc_coeff_bwd_validate(*t2) == MHC_ERROR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4, 5, 6, 8, 9, 10, 11])
+def test_null_and_misaligned_pointers(lib, idx):
+    t = list(Args(lib, 100, 4).tuple())
+    t0 = list(t)
+    t0[idx] = None
+    assert lib.mhc_coeff_bwd_validate(*t0) == MHC_ERROR_INVALID_VALUE
+    t1 = list(t)
+    t1[idx] = t[idx] + 2
+    assert lib.mhc_coeff_bwd_validate(*t1) == MHC_ERROR_INVALID_VALUE
+    assert b"aligned" in lib.mhc_coeff_last_error_message()
+
+
+def test_size_and_scale_rules(lib):
+    def v(**kw):
+        a = Args(lib, 100, 4)
+        for k, x in kw.items():
+            setattr(a, k, x)
+        return lib.mhc_coeff_bwd_validate(*a.tuple())
+    assert v(n=3) == MHC_ERROR_INVALID_VALUE
+    assert v(R=-1) == MHC_ERROR_INVALID_VALUE
+    assert v(R=(1 << 28) + 1) == MHC_ERROR_INVALID_VALUE
+    for c in (0.0, -2.0, float("inf"), float("nan"), 1e-45):
+        assert v(c=c) == MHC_ERROR_INVALID_VALUE, c
+    assert v(c=3.0) == MHC_SUCCESS and v(c=0.5) == MHC_SUCCESS
+    a = Args(lib, 100, 4, ws_extra=-4)
+    assert lib.mhc_coeff_bwd_validate(*a.tuple()) == MHC_ERROR_INVALID_VALUE
+    assert b"workspace" in lib.mhc_coeff_last_error_message()
+
+
+def test_aliasing(lib):
+    a = Args(lib, 100, 4)
+    t = list(a.tuple())
+    t1 = list(t)
+    t1[8] = t[0]                               # grad_mix on mix
+    assert lib.mhc_coeff_bwd_validate(*t1) == MHC_ERROR_ALIASING
+    t2 = list(t)
+    t2[11] = t[8] + 64                         # workspace inside grad_mix
+    assert lib.mhc_coeff_bwd_validate(*t2) == MHC_ERROR_ALIASING
+    t3 = list(t)
+    t3[10] = t[9] + 4                          # grad_alpha inside grad_b
+    assert lib.mhc_coeff_bwd_validate(*t3) == MHC_ERROR_ALIASING
+    t4 = list(t)
+    t4[9] = t[6]                               # grad_b on alpha
+    assert lib.mhc_coeff_bwd_validate(*t4) == MHC_ERROR_ALIASING
+    assert b"overlaps" in lib.mhc_coeff_last_error_message()
+
+
+def test_compute_entry_rejects_before_any_hip_call(lib):
+    a = Args(lib, 100, 4)
+    t = list(a.tuple())
+    t[8] = t[0]
+    assert lib.mhc_coeff_bwd(*t, None, None, None) == MHC_ERROR_ALIASING
+    t = list(a.tuple())
+    t[14] = 5
+    assert lib.mhc_coeff_bwd(*t, None, None, None) == MHC_ERROR_INVALID_VALUE
+
+
+def test_binding_rejects_host_tensors(lib):
+    import torch
+    from hyper_connection_residual_mhc_amd import coeff
+    z = lambda *s: torch.zeros(s, dtype=torch.float32)
+    with pytest.raises(TypeError, match="must be on a GPU"):
+        coeff.mhc_coeff_bwd(z(4, 24), z(4, 4), z(4, 4), z(4, 4), z(4, 4), z(4, 16), z(3), 2.0)
+    with pytest.raises(ValueError, match=r"\[R, n\]"):
+        coeff.mhc_coeff_bwd(z(4, 24), z(4, 3), z(4, 4), z(4, 4), z(4, 4), z(4, 16), z(3), 2.0)

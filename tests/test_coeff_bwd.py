@@ -1,0 +1,166 @@
+"""The coefficient backward epilogue on the GPU against the oracle
+(oracle/coeff_bwd.py), bit for bit, through the C ABI.
+
+Shapes: the page "perf: fuse mHC coefficient backward epilogue" (Performance
+Method) measures B = 4 sequences of T in {128, 512, 2048} tokens, i.e.
+R = 512, 2048 and 8192 rows, at HC = 4 with HC = 2 and 8 as controls. The
+other row counts span one chunk, a ragged chunk, several chunks and more
+than 64 chunks (the second stage's strided walk).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import assert_bytes_equal
+from gpu_util import HipEvents, say
+from hyper_connection_residual_mhc_amd import coeff
+from hyper_connection_residual_mhc_amd.workloads import make_coeff_inputs
+from oracle import coeff_bwd as cb
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+KEYS = ("mix", "pre", "post", "grad_pre", "grad_post", "grad_res", "alpha")
+
+
+def _gpu(host, c, dev, **kw):
+    d = {k: torch.from_numpy(np.ascontiguousarray(host[k])).to(dev) for k in KEYS}
+    gm, gb, ga = coeff.mhc_coeff_bwd(*(d[k] for k in KEYS), c, **kw)
+    torch.cuda.synchronize()
+    return gm.cpu().numpy(), gb.cpu().numpy(), ga.cpu().numpy()
+
+
+def _oracle(host, c):
+    n = host["pre"].shape[1]
+    return cb.coeff_bwd(*(host[k] for k in KEYS), c, n)
+
+
+def _check(host, c, dev, what):
+    got = _gpu(host, c, dev)
+    want = _oracle(host, c)
+    for name, g, w in zip(("grad_mix", "grad_b", "grad_alpha"), got, want):
+        assert_bytes_equal(g, w, f"{what} {name}")
+
+
+@pytest.mark.parametrize("n", [2, 4, 8])
+@pytest.mark.parametrize("R", [1, 63, 64, 65, 300, 4161, 8257])
+def test_bit_exact_against_the_oracle(device, n, R):
+    say(f"coeff bwd n={n} R={R}")
+    _check(make_coeff_inputs(R, n, seed=R + n), 2.0, device, f"n={n} R={R}")
+
+
+@pytest.mark.parametrize("R", [512, 2048, 8192])
+def test_bit_exact_at_the_page_shapes(device, R):
+    say(f"coeff bwd page shape R={R}")
+    _check(make_coeff_inputs(R, 4, seed=0), 2.0, device, f"R={R}")
+
+
+@pytest.mark.parametrize("c", [1.0, 3.0, 0.75, 2.0 ** 20])
+def test_other_post_scales(device, c):
+    say(f"coeff bwd post_scale={c}")
+    _check(make_coeff_inputs(1000, 4, seed=3, post_scale=c), c, device, f"c={c}")
+
+
+def test_large_batch(device):
+    R = 1 << 20
+    say(f"coeff bwd large R={R}")
+    _check(make_coeff_inputs(R, 4, seed=11), 2.0, device, f"R={R}")
+
+
+def _placed(R, n, col_vals):
+    """Inputs whose derivative is zero except for residual column 0, which
+    carries the given row values (d = grad_res there)."""
+    h = make_coeff_inputs(R, n, seed=1)
+    h["grad_pre"][:] = 0
+    h["grad_post"][:] = 0
+    h["grad_res"][:] = 0
+    for r, v in col_vals.items():
+        h["grad_res"][r, 0] = v
+    return h
+
+
+@pytest.mark.parametrize("R,vals,want", [
+    (4, {0: 1.0, 1: U, 3: U}, 1.0 + 2 * U),                      # first-stage tree
+    (64, {0: 1.0, 32: U, 33: U}, 1.0),                            # 64-row chunks (not 32)
+    (128, {0: 1.0, 64: U, 65: U}, 1.0 + 2 * U),                   # 64-row chunks (not 128)
+    (65 * 64 + 1, {0: 1.0, 64: U, 65 * 64: U}, 1.0 + 2 * U),      # chunks strided over 64
+    (128 * 64 + 1, {0: 1.0, 64 * 64: U, 128 * 64: U}, 1.0),       # ascending per accumulator
+])
+def test_row_order_hand_derived_cases(device, R, vals, want):
+    """The hand-derived values of the row order (derivations beside the same
+    cases in tests/test_coeff_oracle.py), reached on the device."""
+    say(f"coeff bwd row order R={R}")
+    _, gb, _ = _gpu(_placed(R, 4, vals), 2.0, device)
+    assert gb[8] == np.float32(want)
+    assert np.all(gb[:8] == 0) and np.all(gb[9:] == 0)
+
+
+def test_empty_batch_writes_zero_sums(device):
+    say("coeff bwd R=0")
+    d = {k: torch.empty((0,) + make_coeff_inputs(1, 4)[k].shape[1:], dtype=torch.float32,
+                        device=device) for k in KEYS if k != "alpha"}
+    alpha = torch.ones(3, device=device)
+    gb = torch.full((24,), float("nan"), device=device)
+    ga = torch.full((3,), float("nan"), device=device)
+    gm, gb, ga = coeff.mhc_coeff_bwd(d["mix"], d["pre"], d["post"], d["grad_pre"],
+                                     d["grad_post"], d["grad_res"], alpha, 2.0, grad_b=gb,
+                                     grad_alpha=ga)
+    torch.cuda.synchronize()
+    assert gm.shape == (0, 24)
+    assert gb.cpu().tolist() == [0.0] * 24 and ga.cpu().tolist() == [0.0] * 3
+    assert not torch.signbit(gb).any()
+
+
+def test_repeatable_and_independent_of_workspace_contents(device):
+    say("coeff bwd repeat")
+    host = make_coeff_inputs(5000, 4, seed=21)
+    first = _gpu(host, 2.0, device)
+    ws = torch.empty(coeff.mhc_coeff_bwd_workspace_bytes(5000, 4), dtype=torch.uint8,
+                     device=device)
+    for k in range(20):
+        ws.fill_(0xFF if k % 2 else 0x7F)       # NaN patterns / large values
+        got = _gpu(host, 2.0, device, workspace=ws)
+        for a, b, name in zip(got, first, ("grad_mix", "grad_b", "grad_alpha")):
+            assert_bytes_equal(a, b, f"repeat {k} {name}")
+
+
+def test_grad_mix_rows_do_not_depend_on_the_batch(device):
+    say("coeff bwd row independence")
+    host = make_coeff_inputs(700, 8, seed=5)
+    whole = _gpu(host, 2.0, device)[0]
+    parts = []
+    for lo, hi in ((0, 1), (1, 129), (129, 700)):
+        parts.append(_gpu({k: (v if k == "alpha" else v[lo:hi]) for k, v in host.items()},
+                          2.0, device)[0])
+    assert_bytes_equal(np.concatenate(parts), whole, "grad_mix split")
+
+
+def test_special_values(device):
+    say("coeff bwd special values")
+    host = make_coeff_inputs(256, 4, seed=9)
+    host["pre"][:8] = 0.0
+    host["pre"][8:16] = 1.0
+    host["post"][:8] = 2.0                      # post = c: saturated
+    host["grad_pre"][16:24] = -0.0
+    host["grad_post"][24:32] = np.float32(1e-39)  # denormal products
+    host["grad_res"][32:40] = np.float32(3e-41)
+    host["mix"][40:48] = np.float32(1e30)       # large products in the alpha terms
+    host["grad_res"][48:56] = np.float32(3e38)  # overflow to +inf in grad_mix (alpha > 1)
+    host["mix"][48:56] = np.float32(0.5)        # and in the sums, with one sign (no NaN)
+    host["alpha"][2] = np.float32(1.25)
+    _check(host, 2.0, device, "special")
+
+
+def test_timed_call_records_both_events(device):
+    say("coeff bwd timed")
+    host = make_coeff_inputs(2048, 4, seed=2)
+    ev = HipEvents(2)
+    try:
+        _gpu(host, 2.0, device, start_event=ev.h[0], stop_event=ev.h[1])
+        ms = ev.elapsed_ms(0, 1)
+        assert 0 < ms < 100
+    finally:
+        ev.close()
