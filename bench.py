@@ -357,7 +357,8 @@ SWEEP_SHAPES = [  # (T, H): latency sweep, bandwidth shapes, backward shape
 ]
 
 
-def run_sweep(path: str, rounds: int = 7, warm: int = 10, timed: int = 100) -> None:
+def run_sweep(path: str, rounds: int = 7, warm: int = 10, timed: int = 100,
+              part: str = "all") -> None:
     """Per-call forward and backward times at SWEEP_SHAPES, one JSON line per
     (shape, direction) into `path`. Every timed launch carries its own
     dispatch events, so launches run one at a time, each from cold caches
@@ -366,7 +367,9 @@ def run_sweep(path: str, rounds: int = 7, warm: int = 10, timed: int = 100) -> N
     `timed` timed launches; p20 / median / p80 are taken over the round
     medians, GB/s from the median. At T >= 1024 a streaming probe with the
     kernel's read:write byte mix is timed the same way in each round, in a
-    block of its own after the kernel's (the reference column)."""
+    block of its own after the kernel's (the reference column). Then the
+    coefficient backward epilogue at COEFF_SWEEP. `part` limits the sweep to
+    "h_aggregate" or "coeff"."""
     import statistics as st
     import torch
     from hyper_connection_residual_mhc_amd import _lib, ops
@@ -385,7 +388,7 @@ def run_sweep(path: str, rounds: int = 7, warm: int = 10, timed: int = 100) -> N
         return st.median(med), [round(q[1], 3), round(st.median(med), 3), round(q[7], 3)], mean
 
     with open(path, "w") as f:
-        for T, H in SWEEP_SHAPES:
+        for T, H in (SWEEP_SHAPES if part in ("all", "h_aggregate") else []):
             nsets = 8 if T <= 2048 else 3
             sets = make_sets(T, H, nsets, dev)
             s0 = sets[0]
@@ -459,7 +462,79 @@ def run_sweep(path: str, rounds: int = 7, warm: int = 10, timed: int = 100) -> N
                 print(json.dumps(rec), file=sys.stderr, flush=True)
             del sets
             torch.cuda.empty_cache()
+        for R, n in (COEFF_SWEEP if part in ("all", "coeff") else []):
+            # the policy's form, then the two-launch form for comparison
+            for launches in (0, 2):
+                rec = time_coeff(R, n, dev, sh, ev, rounds, warm, timed, summary, launches)
+                f.write(json.dumps(rec) + "\n")
+                f.flush()
+                print(json.dumps(rec), file=sys.stderr, flush=True)
     ev.close()
+
+
+# The coefficient backward epilogue at the shapes of the page "perf: fuse
+# mHC coefficient backward epilogue" (Performance Method: B = 4 sequences of
+# T in {128, 512, 2048} tokens at HC = 4, so R = 4T rows; HC = 2 and 8 as
+# controls at T = 512).
+COEFF_SWEEP = [(512, 4), (2048, 4), (8192, 4), (2048, 2), (2048, 8)]
+COEFF_KEYS = ("mix", "pre", "post", "grad_pre", "grad_post", "grad_res", "alpha")
+
+
+def coeff_bytes(R: int, n: int) -> int:
+    """Algorithmic bytes of one epilogue call: per row mix, pre, post,
+    grad_pre, grad_post, grad_res read and grad_mix written (32n + 12n^2),
+    plus alpha, grad_b and grad_alpha once."""
+    m = 2 * n + n * n
+    return R * (32 * n + 12 * n * n) + 12 + 4 * m + 12
+
+
+def time_coeff(R, n, dev, sh, ev, rounds, warm, timed, summary, launches=0) -> dict:
+    """Per-call time of mhc_coeff_bwd (both of its launches, between the
+    first dispatch's start and the last one's end). Input sets rotate over
+    more than the 256 MB Infinity Cache, so every call starts cold."""
+    import torch
+    from hyper_connection_residual_mhc_amd import _lib
+    from hyper_connection_residual_mhc_amd.workloads import make_coeff_inputs
+    clib = _lib.coeff_lib()
+    host = make_coeff_inputs(R, n, seed=0)
+    m = 2 * n + n * n
+    per_set = coeff_bytes(R, n)
+    nsets = max(8, min(4096, -(-(320 << 20) // per_set)))
+    src = {k: torch.from_numpy(host[k]).to(dev) for k in COEFF_KEYS}
+    ws_bytes = clib.mhc_coeff_bwd_workspace_bytes(R, n)
+    sets = []
+    for _ in range(nsets):
+        x = {k: v.clone() for k, v in src.items()}
+        x["grad_mix"] = torch.empty((R, m), dtype=torch.float32, device=dev)
+        x["grad_b"] = torch.empty((m,), dtype=torch.float32, device=dev)
+        x["grad_alpha"] = torch.empty((3,), dtype=torch.float32, device=dev)
+        x["ws"] = torch.zeros((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+        sets.append(x)
+    E = ev.handles
+
+    def call(k, a, b):
+        x = sets[k % nsets]
+        return clib.mhc_coeff_bwd(*(x[key].data_ptr() for key in COEFF_KEYS), 2.0,
+                                  x["grad_mix"].data_ptr(), x["grad_b"].data_ptr(),
+                                  x["grad_alpha"].data_ptr(), x["ws"].data_ptr(), ws_bytes, R, n,
+                                  launches, sh, a, b)
+    per_round = []
+    for _ in range(rounds):
+        for k in range(warm):
+            _lib.check_coeff(call(k, None, None))
+        torch.cuda.synchronize()
+        for k in range(timed):
+            _lib.check_coeff(call(k, E[2 * k], E[2 * k + 1]))
+        torch.cuda.synchronize()
+        per_round.append([ev.elapsed_us(2 * k, 2 * k + 1) for k in range(timed)])
+    med, q, mean = summary(per_round)
+    del sets, src
+    torch.cuda.empty_cache()
+    return {"op": "coeff_bwd", "rows": R, "n": n, "bytes": per_set, "sets": nsets,
+            "us_median": round(med, 3), "us_p20_p50_p80": q, "us_mean": round(mean, 3),
+            "gbps": round(per_set / med / 1e3, 1),
+            "frac_of_8TBps": round(per_set / med / 1e3 / PEAK_HBM_GBPS, 4),
+            "launches": clib.mhc_coeff_bwd_plan(R, n, launches), "chunks": -(-R // 64)}
 
 
 # ---------------------------------------------------------------------------
@@ -630,6 +705,8 @@ def main() -> int:
     ap.add_argument("--sweep", metavar="OUT_JSONL",
                     help="instead of the step benchmark, time each kernel per call at the "
                          "latency / bandwidth / backward shapes and write JSON lines")
+    ap.add_argument("--sweep-part", choices=("all", "h_aggregate", "coeff"), default="all",
+                    help="with --sweep: which operations to time")
     ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV")
     ap.add_argument("--summarize-pmc", metavar="COUNTER_CSV", nargs="+")
     args = ap.parse_args()
@@ -644,7 +721,7 @@ def main() -> int:
         if args.gpus != 1:
             print("the sweep runs on one GPU", file=sys.stderr)
             return 2
-        run_sweep(args.sweep)
+        run_sweep(args.sweep, part=args.sweep_part)
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this operation is token-parallel with no "

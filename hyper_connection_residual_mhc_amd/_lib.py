@@ -86,7 +86,7 @@ SIGNATURES = {
                                  c_void_p, c_void_p, c_void_p]),
 }
 
-MHC_COEFF_ABI_VERSION = 1
+MHC_COEFF_ABI_VERSION = 2
 MHC_COEFF_CHUNK = 64
 MHC_COEFF_MAX_ROWS = 1 << 28
 
@@ -95,10 +95,11 @@ COEFF_SIGNATURES = {
     "mhc_coeff_abi_version": (c_int, []),
     "mhc_coeff_last_error_message": (c_char_p, []),
     "mhc_coeff_bwd_workspace_bytes": (c_int64, [c_int64, c_int32]),
+    "mhc_coeff_bwd_plan": (c_int32, [c_int64, c_int32, c_int32]),
     "mhc_coeff_bwd_validate": (c_int, [c_void_p] * 7 + [c_float] + [c_void_p] * 4
                                + [c_int64, c_int64, c_int32]),
     "mhc_coeff_bwd": (c_int, [c_void_p] * 7 + [c_float] + [c_void_p] * 4
-                      + [c_int64, c_int64, c_int32, c_void_p, c_void_p, c_void_p]),
+                      + [c_int64, c_int64, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
 }
 
 _lib: ctypes.CDLL | None = None

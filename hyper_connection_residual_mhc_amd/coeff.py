@@ -36,6 +36,14 @@ def mhc_coeff_bwd_workspace_bytes(rows: int, n: int) -> int:
     return int(got)
 
 
+def mhc_coeff_bwd_plan(rows: int, n: int, launches: int = 0) -> int:
+    """Launches (1 or 2) a call with these arguments makes."""
+    got = _lib.coeff_lib().mhc_coeff_bwd_plan(int(rows), int(n), int(launches))
+    if got < 0:
+        raise ValueError(f"invalid rows={rows}, n={n} or launches={launches}")
+    return int(got)
+
+
 def mhc_coeff_bwd_validate(mix: int, pre: int, post: int, grad_pre: int, grad_post: int,
                            grad_res: int, alpha: int, post_scale: float, grad_mix: int,
                            grad_b: int, grad_alpha: int, workspace: int, workspace_bytes: int,
@@ -50,13 +58,16 @@ def mhc_coeff_bwd(mix: torch.Tensor, pre: torch.Tensor, post: torch.Tensor,
                   grad_pre: torch.Tensor, grad_post: torch.Tensor, grad_res: torch.Tensor,
                   alpha: torch.Tensor, post_scale: float, *, grad_mix: torch.Tensor | None = None,
                   grad_b: torch.Tensor | None = None, grad_alpha: torch.Tensor | None = None,
-                  workspace: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None, launches: int = 0,
                   stream: torch.cuda.Stream | None = None, start_event=None, stop_event=None
                   ) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """(grad_mix [R, m], grad_b [m], grad_alpha [3]) from mix [R, m], pre,
     post, grad_pre, grad_post [R, n], grad_res [R, n*n], alpha [3] (all
-    fp32) and the post-gate scale. Asynchronous on `stream`. start_event /
-    stop_event are raw hipEvent_t handles (or None)."""
+    fp32) and the post-gate scale. Asynchronous on `stream`. A workspace
+    given by the caller must have been zeroed once (its first 4 bytes are
+    the arrival counter every completed call leaves at zero); without one, a
+    zeroed workspace is allocated. launches: 0 (policy), 1 or 2.
+    start_event / stop_event are raw hipEvent_t handles (or None)."""
     if not isinstance(pre, torch.Tensor) or pre.dim() != 2 or pre.shape[1] not in SUPPORTED_HC:
         raise ValueError("pre must have shape [R, n] with n in (2, 4, 8)")
     R, n = int(pre.shape[0]), int(pre.shape[1])
@@ -81,7 +92,7 @@ def mhc_coeff_bwd(mix: torch.Tensor, pre: torch.Tensor, post: torch.Tensor,
     _require(grad_alpha, "grad_alpha", f32, (3,), dev)
     need = mhc_coeff_bwd_workspace_bytes(R, n)
     if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+        workspace = torch.zeros((max(need, 1),), dtype=torch.uint8, device=dev)
     if not isinstance(workspace, torch.Tensor) or workspace.device != dev or \
             not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on the inputs' device")
@@ -91,6 +102,6 @@ def mhc_coeff_bwd(mix: torch.Tensor, pre: torch.Tensor, post: torch.Tensor,
             mix.data_ptr(), pre.data_ptr(), post.data_ptr(), grad_pre.data_ptr(),
             grad_post.data_ptr(), grad_res.data_ptr(), alpha.data_ptr(), float(post_scale),
             grad_mix.data_ptr(), grad_b.data_ptr(), grad_alpha.data_ptr(), workspace.data_ptr(),
-            ws_bytes, R, n, _stream_handle(dev, stream), start_event, stop_event)
+            ws_bytes, R, n, int(launches), _stream_handle(dev, stream), start_event, stop_event)
     check_coeff(st)
     return grad_mix, grad_b, grad_alpha

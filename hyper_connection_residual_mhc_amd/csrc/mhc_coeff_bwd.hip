@@ -13,16 +13,18 @@
 //
 // Design for CDNA4 (MI355X):
 //  * The data are small (32n + 12n^2 bytes per row: 320 at n = 4, so 2.6 MB
-//    for the page's largest batch of 4 x 2048 tokens): the cost is two
-//    dispatches, not bandwidth. So: one producer launch with one wave per
-//    64-row chunk (a lane per row, every value of a row in registers) and
-//    one reducer launch with one wave per summed output.
-//  * The producer's per-chunk sums are the first stage of the order itself
-//    (a 64-lane halving tree in registers, lanes = rows), and the reducer's
-//    strided walk over the chunk sums plus the same tree is the second, so
-//    both launches compute exactly the defined order; the workspace holds
-//    the chunk sums column by column so that the reducer's loads of one
-//    output's sums are contiguous across lanes.
+//    for the page's largest batch of 4 x 2048 tokens): the cost is dispatch
+//    latency, not bandwidth. One wave per 64-row chunk (a lane per row,
+//    every value of a row in registers) computes the chunk's sums; the
+//    second stage then runs either in the same launch, by the block that
+//    finishes last (an arrival counter in the workspace, release / acquire
+//    fences, no waiting), or, for long batches, in a second launch with one
+//    wave per summed output.
+//  * The chunk sums are the first stage of the order itself (a 64-lane
+//    halving tree in registers, lanes = rows), and the strided walk over
+//    them plus the same tree is the second, so both forms compute exactly
+//    the defined order; the workspace holds the chunk sums output by output
+//    so that one output's loads are contiguous across lanes.
 //  * Rows past the end read as 0 through the buffer range check and produce
 //    exactly +0.0 everywhere, which is what the order prescribes for them;
 //    their grad_mix stores are dropped by the same check.
@@ -81,20 +83,17 @@ __device__ __forceinline__ void wave_trees(float (&v)[K]) {
 // Producer: one wave per chunk of 64 rows, lane = row.
 // ---------------------------------------------------------------------------
 //
-// Grid: `chunks` blocks of 64 threads. Writes grad_mix for the chunk's rows
-// and, for each of the m + 3 summed quantities v (d of every column, then
-// e of the three groups), the chunk's first-stage sum to
-// partial[v * chunks + chunk].
+// Writes grad_mix for the chunk's rows and, for each of the m + 3 summed
+// quantities v (d of every column, then e of the three groups), the chunk's
+// first-stage sum to partial[v * chunks + chunk] (one lane stores them).
 template <int N>
-__global__ __launch_bounds__(64) void coeff_partial_kernel(
+__device__ __forceinline__ void chunk_sums(
     const float* __restrict__ mix, const float* __restrict__ pre,
     const float* __restrict__ post, const float* __restrict__ grad_pre,
     const float* __restrict__ grad_post, const float* __restrict__ grad_res,
     const float* __restrict__ alpha, float inv_c, float* __restrict__ grad_mix,
-    float* __restrict__ partial, int64_t rows, uint32_t chunks) {
+    float* __restrict__ partial, int64_t rows, uint32_t chunks, uint32_t c, uint32_t lane) {
   constexpr int M = 2 * N + N * N;
-  const uint32_t lane = threadIdx.x;
-  const uint32_t c = blockIdx.x;
   const int64_t r0 = static_cast<int64_t>(c) * kChunk;
   const int64_t valid = rows - r0 < kChunk ? rows - r0 : kChunk;
 
@@ -151,20 +150,13 @@ __global__ __launch_bounds__(64) void coeff_partial_kernel(
   }
 }
 
-// ---------------------------------------------------------------------------
-// Reducer: one wave per summed output.
-// ---------------------------------------------------------------------------
-//
-// Grid: m + 3 blocks of 64 threads. Block v walks the chunk sums of output v
-// with lane l taking chunks l, l + 64, ... in ascending order, then sums the
-// 64 lanes with the halving tree. Outputs v < m go to grad_b[v], the last
-// three to grad_alpha.
-__global__ __launch_bounds__(64) void coeff_reduce_kernel(const float* __restrict__ partial,
-                                                          uint32_t chunks, int32_t m,
-                                                          float* __restrict__ grad_b,
-                                                          float* __restrict__ grad_alpha) {
-  const uint32_t lane = threadIdx.x;
-  const uint32_t v = blockIdx.x;
+// Second stage for output v, by one whole wave: lane l walks the chunk sums
+// l, l + 64, ... in ascending order, then the halving tree; lane 0 stores
+// the result (v < m: grad_b[v], else grad_alpha[v - m]).
+__device__ __forceinline__ void output_sum(const float* __restrict__ partial, uint32_t chunks,
+                                           int32_t m, uint32_t v, uint32_t lane,
+                                           float* __restrict__ grad_b,
+                                           float* __restrict__ grad_alpha) {
   const Rsrc rs = make_rsrc(partial + static_cast<int64_t>(v) * chunks,
                             static_cast<int64_t>(chunks) * 4);
   float acc[1] = {0.0f};
@@ -179,6 +171,95 @@ __global__ __launch_bounds__(64) void coeff_reduce_kernel(const float* __restric
     const Rsrc out = bias ? make_rsrc(grad_b, static_cast<int64_t>(m) * 4) : make_rsrc(grad_alpha, 12);
     st(out, (bias ? v : v - m) * 4, acc[0]);
   }
+}
+
+// Two-launch form, first launch. Grid: `chunks` blocks of 64 threads.
+template <int N>
+__global__ __launch_bounds__(64) void coeff_partial_kernel(
+    const float* __restrict__ mix, const float* __restrict__ pre,
+    const float* __restrict__ post, const float* __restrict__ grad_pre,
+    const float* __restrict__ grad_post, const float* __restrict__ grad_res,
+    const float* __restrict__ alpha, float inv_c, float* __restrict__ grad_mix,
+    float* __restrict__ partial, int64_t rows, uint32_t chunks) {
+  chunk_sums<N>(mix, pre, post, grad_pre, grad_post, grad_res, alpha, inv_c, grad_mix, partial,
+                rows, chunks, blockIdx.x, threadIdx.x);
+}
+
+// Two-launch form, second launch. Grid: m + 3 blocks of 64 threads, block v
+// sums output v.
+__global__ __launch_bounds__(64) void coeff_reduce_kernel(const float* __restrict__ partial,
+                                                          uint32_t chunks, int32_t m,
+                                                          float* __restrict__ grad_b,
+                                                          float* __restrict__ grad_alpha) {
+  output_sum(partial, chunks, m, blockIdx.x, threadIdx.x, grad_b, grad_alpha);
+}
+
+// One-launch form. Grid: ceil(chunks / kFusedWaves) blocks of
+// 64 * kFusedWaves threads; wave w of block b computes chunk
+// b * kFusedWaves + w. After a barrier, one thread makes the block's chunk
+// sums visible device-wide (release fence; it covers the other waves'
+// stores through the barrier) and counts the block in `arrived`. The block
+// that arrives last (it reads blocks - 1) fences again (acquire), computes
+// every output's second stage (the outputs split over its waves) and sets
+// the counter back to 0 for the next call. No block waits for another, so
+// every block runs to completion whatever the others do.
+constexpr int kFusedWaves = 4;
+
+template <int N>
+__global__ __launch_bounds__(64 * kFusedWaves) void coeff_fused_kernel(
+    const float* __restrict__ mix, const float* __restrict__ pre,
+    const float* __restrict__ post, const float* __restrict__ grad_pre,
+    const float* __restrict__ grad_post, const float* __restrict__ grad_res,
+    const float* __restrict__ alpha, float inv_c, float* __restrict__ grad_mix,
+    float* __restrict__ partial, uint32_t* __restrict__ arrived, int64_t rows,
+    uint32_t chunks, float* __restrict__ grad_b, float* __restrict__ grad_alpha) {
+  constexpr int M = 2 * N + N * N;
+  constexpr int Q = (M + 3 + kFusedWaves - 1) / kFusedWaves;  // outputs per wave
+  __shared__ uint32_t last;
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t c = blockIdx.x * kFusedWaves + wave;
+  if (c < chunks)
+    chunk_sums<N>(mix, pre, post, grad_pre, grad_post, grad_res, alpha, inv_c, grad_mix,
+                  partial, rows, chunks, c, lane);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    last = atomicAdd(arrived, 1u) == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!last) return;  // the whole block
+  __threadfence();
+  // Outputs v = wave * Q + q. Each round loads one chunk sum per output per
+  // lane (all independent), then the Q halving trees run interleaved.
+  // Lanes past the last chunk add +0.0, which leaves a sum that started at
+  // +0.0 unchanged; outputs past m + 3 read 0 and are not stored.
+  const Rsrc rs = make_rsrc(partial, static_cast<int64_t>(M + 3) * chunks * 4);
+  float acc[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) acc[q] = 0.0f;
+  const uint32_t rounds = (chunks + 63) / 64;
+  for (uint32_t k = 0; k < rounds; ++k) {
+    const uint32_t idx = k * 64 + lane;
+    const bool in = idx < chunks;
+    float x[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) x[q] = ld(rs, ((wave * Q + q) * chunks + idx) * 4);
+#pragma unroll
+    for (int q = 0; q < Q; ++q) acc[q] = acc[q] + (in ? x[q] : 0.0f);
+  }
+  wave_trees(acc);
+  if (lane == 0) {
+    const Rsrc rb = make_rsrc(grad_b, M * 4);
+    const Rsrc ra = make_rsrc(grad_alpha, 12);
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const uint32_t v = wave * Q + q;
+      if (v < M) st(rb, v * 4, acc[q]);
+      else if (v < M + 3) st(ra, (v - M) * 4, acc[q]);
+    }
+  }
+  if (threadIdx.x == 0) atomicExch(arrived, 0u);
 }
 
 // ---------------------------------------------------------------------------
@@ -205,9 +286,22 @@ int columns(int32_t n) { return 2 * n + n * n; }
 
 int64_t chunk_count(int64_t rows) { return (rows + kChunk - 1) / kChunk; }
 
+// Workspace: the arrival counter of the one-launch form in the first
+// kWsHeader bytes, then the chunk sums, output by output.
+constexpr int64_t kWsHeader = 256;
+
 int64_t workspace_need(int64_t rows, int32_t n) {
-  return static_cast<int64_t>(columns(n) + 3) * chunk_count(rows) * 4;
+  if (rows == 0) return 0;
+  return kWsHeader + static_cast<int64_t>(columns(n) + 3) * chunk_count(rows) * 4;
 }
+
+// The one-launch form is used at n <= 4 up to this many chunks. Measured per
+// call (cold inputs, n = 4): one launch 6.2 / 6.8 / 7.8 us at 512 / 2048 /
+// 8192 rows against 9.1 / 9.1 / 9.2 us for two; even at 16384 rows (9.7 vs
+// 9.6 us); behind beyond (its last block sums every output alone). At n = 8
+// two launches are faster at every size measured (12.1 vs 16.1 us at 2048
+// rows: four 80-column waves per CU load slower than one).
+constexpr int64_t kFusedMaxChunks = 128;
 
 struct Range {
   uintptr_t lo, hi;
@@ -278,14 +372,38 @@ mhc_status validate(const float* mix, const float* pre, const float* post,
   return ok();
 }
 
+struct CoeffArgs {
+  const float *mix, *pre, *post, *grad_pre, *grad_post, *grad_res, *alpha;
+  float inv_c;
+  float *grad_mix, *grad_b, *grad_alpha, *partial;
+  uint32_t* arrived;
+  int64_t rows;
+  uint32_t chunks;
+};
+
 template <int N>
-void launch_partial(const float* mix, const float* pre, const float* post, const float* grad_pre,
-                    const float* grad_post, const float* grad_res, const float* alpha,
-                    float inv_c, float* grad_mix, float* partial, int64_t rows, uint32_t chunks,
-                    hipStream_t s, hipEvent_t start) {
-  hipExtLaunchKernelGGL(coeff_partial_kernel<N>, dim3(chunks), dim3(64), 0, s, start, nullptr, 0,
-                        mix, pre, post, grad_pre, grad_post, grad_res, alpha, inv_c, grad_mix,
-                        partial, rows, chunks);
+void launch_partial(const CoeffArgs& a, hipStream_t s, hipEvent_t start) {
+  hipExtLaunchKernelGGL(coeff_partial_kernel<N>, dim3(a.chunks), dim3(64), 0, s, start, nullptr,
+                        0, a.mix, a.pre, a.post, a.grad_pre, a.grad_post, a.grad_res, a.alpha,
+                        a.inv_c, a.grad_mix, a.partial, a.rows, a.chunks);
+}
+
+template <int N>
+void launch_fused(const CoeffArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+  const uint32_t blocks = (a.chunks + kFusedWaves - 1) / kFusedWaves;
+  hipExtLaunchKernelGGL(coeff_fused_kernel<N>, dim3(blocks), dim3(64 * kFusedWaves), 0, s, start,
+                        stop, 0,
+                        a.mix, a.pre, a.post, a.grad_pre, a.grad_post, a.grad_res, a.alpha,
+                        a.inv_c, a.grad_mix, a.partial, a.arrived, a.rows, a.chunks, a.grad_b,
+                        a.grad_alpha);
+}
+
+// Launches of one call: 1 = one launch (chunk sums + last-block reduction),
+// 2 = chunk-sum launch then reduction launch. 0 lets the policy choose.
+int plan_launches(int64_t rows, int32_t n, int32_t launches) {
+  if (rows == 0) return 2;  // only the reduction launch runs: it writes the +0.0 sums
+  if (launches != 0) return launches;
+  return n <= 4 && chunk_count(rows) <= kFusedMaxChunks ? 1 : 2;
 }
 
 mhc_status launch_error(const char* what) {
@@ -323,33 +441,57 @@ mhc_status mhc_coeff_bwd_validate(const float* mix, const float* pre, const floa
                   grad_b, grad_alpha, workspace, workspace_bytes, rows, n);
 }
 
+int32_t mhc_coeff_bwd_plan(int64_t rows, int32_t n, int32_t launches) {
+  if ((n != 2 && n != 4 && n != 8) || rows < 0 || rows > MHC_COEFF_MAX_ROWS ||
+      launches < 0 || launches > 2)
+    return -1;
+  return plan_launches(rows, n, launches);
+}
+
 mhc_status mhc_coeff_bwd(const float* mix, const float* pre, const float* post,
                          const float* grad_pre, const float* grad_post, const float* grad_res,
                          const float* alpha, float post_scale, float* grad_mix, float* grad_b,
                          float* grad_alpha, void* workspace, int64_t workspace_bytes,
-                         int64_t rows, int32_t n, void* stream, void* start_event,
-                         void* stop_event) {
+                         int64_t rows, int32_t n, int32_t launches, void* stream,
+                         void* start_event, void* stop_event) {
   mhc_status st = validate(mix, pre, post, grad_pre, grad_post, grad_res, alpha, post_scale,
                            grad_mix, grad_b, grad_alpha, workspace, workspace_bytes, rows, n);
   if (st != MHC_SUCCESS) return st;
+  if (launches < 0 || launches > 2)
+    return fail(MHC_ERROR_INVALID_VALUE, "launches must be 0, 1 or 2 (got %d)", launches);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t start = static_cast<hipEvent_t>(start_event);
   hipEvent_t stop = static_cast<hipEvent_t>(stop_event);
-  const uint32_t chunks = static_cast<uint32_t>(chunk_count(rows));
-  const float inv_c = 1.0f / post_scale;  // rounded to fp32 once
-  float* partial = static_cast<float*>(workspace);
+  CoeffArgs a;
+  a.mix = mix; a.pre = pre; a.post = post; a.grad_pre = grad_pre; a.grad_post = grad_post;
+  a.grad_res = grad_res; a.alpha = alpha;
+  a.inv_c = 1.0f / post_scale;  // rounded to fp32 once
+  a.grad_mix = grad_mix; a.grad_b = grad_b; a.grad_alpha = grad_alpha;
+  a.arrived = static_cast<uint32_t*>(workspace);
+  a.partial = rows > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + kWsHeader)
+                       : nullptr;
+  a.rows = rows;
+  a.chunks = static_cast<uint32_t>(chunk_count(rows));
   (void)hipGetLastError();
-  if (chunks > 0) {
+  if (plan_launches(rows, n, launches) == 1) {
     switch (n) {
-      case 2: launch_partial<2>(mix, pre, post, grad_pre, grad_post, grad_res, alpha, inv_c, grad_mix, partial, rows, chunks, s, start); break;
-      case 4: launch_partial<4>(mix, pre, post, grad_pre, grad_post, grad_res, alpha, inv_c, grad_mix, partial, rows, chunks, s, start); break;
-      default: launch_partial<8>(mix, pre, post, grad_pre, grad_post, grad_res, alpha, inv_c, grad_mix, partial, rows, chunks, s, start); break;
+      case 2: launch_fused<2>(a, s, start, stop); break;
+      case 4: launch_fused<4>(a, s, start, stop); break;
+      default: launch_fused<8>(a, s, start, stop); break;
+    }
+    return launch_error("coefficient backward (one launch)");
+  }
+  if (a.chunks > 0) {
+    switch (n) {
+      case 2: launch_partial<2>(a, s, start); break;
+      case 4: launch_partial<4>(a, s, start); break;
+      default: launch_partial<8>(a, s, start); break;
     }
     if ((st = launch_error("coefficient backward (chunk sums)")) != MHC_SUCCESS) return st;
   }
   const int m = columns(n);
   hipExtLaunchKernelGGL(coeff_reduce_kernel, dim3(m + 3), dim3(64), 0, s,
-                        chunks > 0 ? nullptr : start, stop, 0, partial, chunks, m, grad_b,
+                        a.chunks > 0 ? nullptr : start, stop, 0, a.partial, a.chunks, m, grad_b,
                         grad_alpha);
   return launch_error("coefficient backward (reduction)");
 }

@@ -49,13 +49,25 @@
  *     grad_res [R, n*n], alpha [3]                                  (inputs)
  *     grad_mix [R, m], grad_b [m], grad_alpha [3]                   (outputs)
  *     workspace: mhc_coeff_bwd_workspace_bytes(R, n) bytes of device memory
- *     the call may overwrite (the per-chunk sums); its contents before and
- *     after the call mean nothing to the caller. NULL is allowed when that
- *     size is 0.
+ *     (0 when R = 0; NULL is then allowed). Its first 4 bytes are an arrival
+ *     counter: they must be zero before the first call that uses the
+ *     workspace, and every call that completes leaves them zero, so a
+ *     workspace zeroed once when it is allocated serves any sequence of
+ *     calls. The rest holds the per-chunk sums; its contents before and
+ *     after a call mean nothing to the caller. Calls that share a workspace
+ *     must not run concurrently (they are safe one after another on one
+ *     stream).
  *
- * Rules: calls enqueue two kernels on `stream` (a hipStream_t cast to void*,
- * NULL = null stream) and never synchronise; inputs must stay valid until
- * the stream reaches them. The library allocates nothing. n not in {2,4,8},
+ * Launches: the second stage of row_sum runs either in the same launch as
+ * the first (the block that finishes its chunks last does it) or in a second
+ * launch. Both give the same bits. The policy (`launches` = 0) takes one
+ * launch at n = 2 or 4 up to 128 chunks (8192 rows), two otherwise;
+ * `launches` = 1 or 2 forces a form. R = 0 always takes the second form (it
+ * only writes the +0.0 sums).
+ *
+ * Rules: calls enqueue one or two kernels on `stream` (a hipStream_t cast to
+ * void*, NULL = null stream) and never synchronise; inputs must stay valid
+ * until the stream reaches them. The library allocates nothing. n not in {2,4,8},
  * R < 0, R > MHC_COEFF_MAX_ROWS, c not finite and positive, a NULL or
  * non-4-byte-aligned pointer that the call needs (the row tensors, alpha and
  * the workspace when R > 0; grad_b and grad_alpha always), or a workspace
@@ -77,7 +89,7 @@
 extern "C" {
 #endif
 
-#define MHC_COEFF_ABI_VERSION 1
+#define MHC_COEFF_ABI_VERSION 2
 
 /* Rows per first-stage chunk of row_sum. */
 #define MHC_COEFF_CHUNK 64
@@ -91,8 +103,14 @@ int mhc_coeff_abi_version(void);
 const char* mhc_coeff_last_error_message(void);
 
 /* Bytes of workspace a call with R rows at expansion n needs:
- * (m + 3) * ceil(R / 64) * 4. Returns -1 for an invalid n or R. */
+ * 256 + (m + 3) * ceil(R / 64) * 4, or 0 when R = 0. Returns -1 for an
+ * invalid n or R. */
 int64_t mhc_coeff_bwd_workspace_bytes(int64_t rows, int32_t n);
+
+/* Number of launches a call with these arguments makes (1 or 2; see
+ * Launches above), on the host only. Returns -1 for an invalid n, R or
+ * launches value. */
+int32_t mhc_coeff_bwd_plan(int64_t rows, int32_t n, int32_t launches);
 
 /* Checks the arguments exactly as mhc_coeff_bwd does, on the host only:
  * touches no device memory and launches nothing. */
@@ -103,15 +121,16 @@ mhc_status mhc_coeff_bwd_validate(const float* mix, const float* pre, const floa
                                   const float* grad_alpha, const void* workspace,
                                   int64_t workspace_bytes, int64_t rows, int32_t n);
 
-/* The epilogue described above. start_event / stop_event (hipEvent_t cast to
- * void*, each may be NULL) are recorded when the first of the call's kernels
- * starts and when the last one ends. */
+/* The epilogue described above. launches: 0 (policy), 1 or 2; any other
+ * value gives MHC_ERROR_INVALID_VALUE. start_event / stop_event (hipEvent_t
+ * cast to void*, each may be NULL) are recorded when the first of the
+ * call's kernels starts and when the last one ends. */
 mhc_status mhc_coeff_bwd(const float* mix, const float* pre, const float* post,
                          const float* grad_pre, const float* grad_post, const float* grad_res,
                          const float* alpha, float post_scale, float* grad_mix, float* grad_b,
                          float* grad_alpha, void* workspace, int64_t workspace_bytes,
-                         int64_t rows, int32_t n, void* stream, void* start_event,
-                         void* stop_event);
+                         int64_t rows, int32_t n, int32_t launches, void* stream,
+                         void* start_event, void* stop_event);
 
 #ifdef __cplusplus
 }

@@ -75,3 +75,13 @@ def test_device_code_digest(built_library, tmp_path):
     d = bench.device_code_sha256(built_library)
     assert d is not None and len(d) == 64 and int(d, 16) >= 0
     assert bench.device_code_sha256(tmp_path / "missing.so") is None
+
+
+def test_coefficient_epilogue_bytes():
+    # n = 4: per row mix 96 + pre/post/grad_pre/grad_post 64 + grad_res 64
+    # read, grad_mix 96 written = 320; plus alpha, grad_b, grad_alpha.
+    assert bench.coeff_bytes(1, 4) == 320 + 12 + 96 + 12
+    assert bench.coeff_bytes(8192, 4) == 8192 * 320 + 120
+    assert bench.coeff_bytes(10, 2) == 10 * (64 + 48) + 12 + 32 + 12
+    assert bench.coeff_bytes(10, 8) == 10 * (256 + 768) + 12 + 320 + 12
+    assert [r for r, n in bench.COEFF_SWEEP if n == 4] == [512, 2048, 8192]

@@ -26,7 +26,7 @@ def lib(built_library):
 def test_header_declarations_are_all_exported(lib):
     text = re.sub(r"/\*.*?\*/", "", _build.COEFF_HEADER.read_text(), flags=re.S)
     names = sorted(set(re.findall(r"\b(mhc_\w+)\s*\(", text)))
-    assert len(names) == 5, names
+    assert len(names) == 6, names
     out = subprocess.run(["nm", "-D", "--defined-only", str(_build.COEFF_LIB_PATH)],
                          capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (mhc_\w+)$", out, flags=re.M))
@@ -46,14 +46,26 @@ def test_constants_match_the_header(lib):
 
 @pytest.mark.parametrize("n,m", [(2, 8), (4, 24), (8, 80)])
 def test_workspace_bytes(lib, n, m):
+    # a 256-byte header (the arrival counter), then (m + 3) sums per chunk
     f = lib.mhc_coeff_bwd_workspace_bytes
     assert f(0, n) == 0
-    assert f(1, n) == (m + 3) * 4
-    assert f(64, n) == (m + 3) * 4
-    assert f(65, n) == 2 * (m + 3) * 4
-    assert f(8192, n) == 128 * (m + 3) * 4
-    assert f(1 << 28, n) == (1 << 22) * (m + 3) * 4 < (1 << 31)
+    assert f(1, n) == 256 + (m + 3) * 4
+    assert f(64, n) == 256 + (m + 3) * 4
+    assert f(65, n) == 256 + 2 * (m + 3) * 4
+    assert f(8192, n) == 256 + 128 * (m + 3) * 4
+    assert f(1 << 28, n) == 256 + (1 << 22) * (m + 3) * 4 < (1 << 31)
     assert f(-1, n) == -1 and f((1 << 28) + 1, n) == -1
+
+
+def test_launch_policy(lib):
+    plan = lib.mhc_coeff_bwd_plan
+    assert plan(0, 4, 0) == 2 and plan(0, 4, 1) == 2        # R = 0: the sums only
+    assert plan(1, 4, 0) == 1 and plan(1, 2, 0) == 1
+    assert plan(8192, 4, 0) == 1 and plan(8192, 2, 0) == 1  # up to 128 chunks: one launch
+    assert plan(8193, 4, 0) == 2
+    assert plan(1, 8, 0) == 2 and plan(8192, 8, 0) == 2     # n = 8: two launches
+    assert plan(100, 4, 2) == 2 and plan(1 << 20, 2, 1) == 1 and plan(64, 8, 1) == 1
+    assert plan(100, 4, 3) == -1 and plan(100, 4, -1) == -1 and plan(100, 5, 0) == -1
 
 
 def test_workspace_bytes_rejects_bad_n(lib):
@@ -151,10 +163,12 @@ def test_compute_entry_rejects_before_any_hip_call(lib):
     a = Args(lib, 100, 4)
     t = list(a.tuple())
     t[8] = t[0]
-    assert lib.mhc_coeff_bwd(*t, None, None, None) == MHC_ERROR_ALIASING
+    assert lib.mhc_coeff_bwd(*t, 0, None, None, None) == MHC_ERROR_ALIASING
     t = list(a.tuple())
     t[14] = 5
-    assert lib.mhc_coeff_bwd(*t, None, None, None) == MHC_ERROR_INVALID_VALUE
+    assert lib.mhc_coeff_bwd(*t, 0, None, None, None) == MHC_ERROR_INVALID_VALUE
+    assert lib.mhc_coeff_bwd(*a.tuple(), 3, None, None, None) == MHC_ERROR_INVALID_VALUE
+    assert b"launches" in lib.mhc_coeff_last_error_message()
 
 
 def test_binding_rejects_host_tensors(lib):

@@ -38,18 +38,19 @@ def _oracle(host, c):
     return cb.coeff_bwd(*(host[k] for k in KEYS), c, n)
 
 
-def _check(host, c, dev, what):
-    got = _gpu(host, c, dev)
+def _check(host, c, dev, what, **kw):
+    got = _gpu(host, c, dev, **kw)
     want = _oracle(host, c)
     for name, g, w in zip(("grad_mix", "grad_b", "grad_alpha"), got, want):
         assert_bytes_equal(g, w, f"{what} {name}")
 
 
+@pytest.mark.parametrize("launches", [1, 2])
 @pytest.mark.parametrize("n", [2, 4, 8])
 @pytest.mark.parametrize("R", [1, 63, 64, 65, 300, 4161, 8257])
-def test_bit_exact_against_the_oracle(device, n, R):
-    say(f"coeff bwd n={n} R={R}")
-    _check(make_coeff_inputs(R, n, seed=R + n), 2.0, device, f"n={n} R={R}")
+def test_bit_exact_against_the_oracle(device, n, R, launches):
+    say(f"coeff bwd n={n} R={R} launches={launches}")
+    _check(make_coeff_inputs(R, n, seed=R + n), 2.0, device, f"n={n} R={R}", launches=launches)
 
 
 @pytest.mark.parametrize("R", [512, 2048, 8192])
@@ -64,10 +65,15 @@ def test_other_post_scales(device, c):
     _check(make_coeff_inputs(1000, 4, seed=3, post_scale=c), c, device, f"c={c}")
 
 
-def test_large_batch(device):
+@pytest.mark.parametrize("launches", [0, 1])
+def test_large_batch(device, launches):
+    """2^20 rows: 16,384 chunks, past the one-launch policy limit (the
+    policy takes two launches); forced into one launch (its last block then
+    walks 256 rounds of chunk sums) it must agree."""
     R = 1 << 20
-    say(f"coeff bwd large R={R}")
-    _check(make_coeff_inputs(R, 4, seed=11), 2.0, device, f"R={R}")
+    say(f"coeff bwd large R={R} launches={launches}")
+    assert coeff.mhc_coeff_bwd_plan(R, 4, launches) == (2 if launches == 0 else 1)
+    _check(make_coeff_inputs(R, 4, seed=11), 2.0, device, f"R={R}", launches=launches)
 
 
 def _placed(R, n, col_vals):
@@ -82,6 +88,7 @@ def _placed(R, n, col_vals):
     return h
 
 
+@pytest.mark.parametrize("launches", [1, 2])
 @pytest.mark.parametrize("R,vals,want", [
     (4, {0: 1.0, 1: U, 3: U}, 1.0 + 2 * U),                      # first-stage tree
     (64, {0: 1.0, 32: U, 33: U}, 1.0),                            # 64-row chunks (not 32)
@@ -89,11 +96,11 @@ def _placed(R, n, col_vals):
     (65 * 64 + 1, {0: 1.0, 64: U, 65 * 64: U}, 1.0 + 2 * U),      # chunks strided over 64
     (128 * 64 + 1, {0: 1.0, 64 * 64: U, 128 * 64: U}, 1.0),       # ascending per accumulator
 ])
-def test_row_order_hand_derived_cases(device, R, vals, want):
+def test_row_order_hand_derived_cases(device, R, vals, want, launches):
     """The hand-derived values of the row order (derivations beside the same
     cases in tests/test_coeff_oracle.py), reached on the device."""
-    say(f"coeff bwd row order R={R}")
-    _, gb, _ = _gpu(_placed(R, 4, vals), 2.0, device)
+    say(f"coeff bwd row order R={R} launches={launches}")
+    _, gb, _ = _gpu(_placed(R, 4, vals), 2.0, device, launches=launches)
     assert gb[8] == np.float32(want)
     assert np.all(gb[:8] == 0) and np.all(gb[9:] == 0)
 
@@ -115,16 +122,53 @@ def test_empty_batch_writes_zero_sums(device):
 
 
 def test_repeatable_and_independent_of_workspace_contents(device):
+    """Twenty calls in each form on one workspace whose chunk-sum area is
+    refilled with garbage before each call: identical bytes every time, and
+    the arrival counter back at zero after every call."""
     say("coeff bwd repeat")
     host = make_coeff_inputs(5000, 4, seed=21)
     first = _gpu(host, 2.0, device)
-    ws = torch.empty(coeff.mhc_coeff_bwd_workspace_bytes(5000, 4), dtype=torch.uint8,
+    ws = torch.zeros(coeff.mhc_coeff_bwd_workspace_bytes(5000, 4), dtype=torch.uint8,
                      device=device)
-    for k in range(20):
-        ws.fill_(0xFF if k % 2 else 0x7F)       # NaN patterns / large values
-        got = _gpu(host, 2.0, device, workspace=ws)
+    for k in range(40):
+        ws[256:].fill_(0xFF if k % 2 else 0x7F)     # NaN patterns / large values
+        got = _gpu(host, 2.0, device, workspace=ws, launches=1 + k % 2)
         for a, b, name in zip(got, first, ("grad_mix", "grad_b", "grad_alpha")):
             assert_bytes_equal(a, b, f"repeat {k} {name}")
+        assert int(ws[:4].view(torch.int32).item()) == 0
+
+
+def test_one_launch_form_sees_every_chunk_sum(device):
+    """100 one-launch calls at 128 chunks (32 blocks arriving), each after
+    the chunk-sum area was refilled with NaN patterns and each on fresh
+    inputs: the last block must read every other block's sums, never a
+    stale value (which would show as a NaN or a wrong sum)."""
+    say("coeff bwd one-launch visibility")
+    R = 8192
+    ws = torch.zeros(coeff.mhc_coeff_bwd_workspace_bytes(R, 4), dtype=torch.uint8,
+                     device=device)
+    keys = KEYS
+    hosts = [make_coeff_inputs(R, 4, seed=100 + k) for k in range(4)]
+    wants = [_oracle(h, 2.0) for h in hosts]
+    devs = [[torch.from_numpy(h[k]).to(device) for k in keys] for h in hosts]
+    for it in range(100):
+        j = it % 4
+        ws[256:].fill_(0xFF)
+        gm, gb, ga = coeff.mhc_coeff_bwd(*devs[j], 2.0, workspace=ws, launches=1)
+        torch.cuda.synchronize()
+        assert_bytes_equal(gb.cpu().numpy(), wants[j][1], f"call {it} grad_b")
+        assert_bytes_equal(ga.cpu().numpy(), wants[j][2], f"call {it} grad_alpha")
+    assert int(ws[:4].view(torch.int32).item()) == 0
+
+
+def test_calls_of_different_sizes_share_one_workspace(device):
+    say("coeff bwd shared workspace")
+    ws = torch.zeros(coeff.mhc_coeff_bwd_workspace_bytes(8192, 8), dtype=torch.uint8,
+                     device=device)
+    for R, n in ((8192, 8), (3, 4), (700, 2), (1, 8), (4096, 4)):
+        _check(make_coeff_inputs(R, n, seed=R), 2.0, device, f"shared ws R={R} n={n}",
+               workspace=ws)
+        assert int(ws[:4].view(torch.int32).item()) == 0
 
 
 def test_grad_mix_rows_do_not_depend_on_the_batch(device):
@@ -159,8 +203,9 @@ def test_timed_call_records_both_events(device):
     host = make_coeff_inputs(2048, 4, seed=2)
     ev = HipEvents(2)
     try:
-        _gpu(host, 2.0, device, start_event=ev.h[0], stop_event=ev.h[1])
-        ms = ev.elapsed_ms(0, 1)
-        assert 0 < ms < 100
+        for launches in (1, 2):
+            _gpu(host, 2.0, device, launches=launches, start_event=ev.h[0], stop_event=ev.h[1])
+            ms = ev.elapsed_ms(0, 1)
+            assert 0 < ms < 100
     finally:
         ev.close()
