@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include "mhc_coeff_bwd.h"
 #include "mhc_h_aggregate.h"
 
 #define CHECK(cond)                                              \
@@ -62,6 +63,39 @@ int main(void) {
   CHECK(mhc_h_aggregate_bwd(NULL, NULL, NULL, NULL, NULL, 0, H, NULL) == MHC_SUCCESS);
   CHECK(mhc_stream_probe((const void*)base, 5 * 1024, out, 4 * 1024, 3, 4, NULL, NULL, NULL) ==
         MHC_ERROR_INVALID_VALUE);
+
+  /* the coefficient backward epilogue's library */
+  {
+    const int64_t R = 8192;
+    const int32_t n = 4;
+    const uintptr_t cb = (uintptr_t)1 << 40;
+    const uintptr_t step = (uintptr_t)1 << 24; /* 16 MiB apart */
+    const float* mix = (const float*)cb;
+    const float* cpre = (const float*)(cb + 1 * step);
+    const float* post = (const float*)(cb + 2 * step);
+    const float* gpre = (const float*)(cb + 3 * step);
+    const float* gpost = (const float*)(cb + 4 * step);
+    const float* gres = (const float*)(cb + 5 * step);
+    const float* alpha = (const float*)(cb + 6 * step);
+    float* gmix = (float*)(cb + 7 * step);
+    float* gb = (float*)(cb + 8 * step);
+    float* ga = (float*)(cb + 9 * step);
+    void* ws = (void*)(cb + 10 * step);
+    const int64_t ws_bytes = mhc_coeff_bwd_workspace_bytes(R, n);
+    CHECK(mhc_coeff_abi_version() == MHC_COEFF_ABI_VERSION);
+    CHECK(ws_bytes == 256 + 27 * (R / MHC_COEFF_CHUNK) * 4);
+    CHECK(mhc_coeff_bwd_workspace_bytes(R, 3) == -1);
+    CHECK(mhc_coeff_bwd_plan(R, n, 0) == 1 && mhc_coeff_bwd_plan(R + 1, n, 0) == 2);
+    CHECK(mhc_coeff_bwd_validate(mix, cpre, post, gpre, gpost, gres, alpha, 2.0f, gmix, gb, ga,
+                                 ws, ws_bytes, R, n) == MHC_SUCCESS);
+    CHECK(mhc_coeff_bwd_validate(mix, cpre, post, gpre, gpost, gres, alpha, 2.0f, (float*)mix,
+                                 gb, ga, ws, ws_bytes, R, n) == MHC_ERROR_ALIASING);
+    CHECK(mhc_coeff_bwd_validate(mix, cpre, post, gpre, gpost, gres, alpha, 0.0f, gmix, gb, ga,
+                                 ws, ws_bytes, R, n) == MHC_ERROR_INVALID_VALUE);
+    CHECK(strlen(mhc_coeff_last_error_message()) > 0);
+    CHECK(mhc_coeff_bwd(mix, cpre, post, gpre, gpost, gres, alpha, 2.0f, gmix, gb, ga, ws,
+                        ws_bytes - 4, R, n, 0, NULL, NULL, NULL) == MHC_ERROR_INVALID_VALUE);
+  }
   printf("c abi ok\n");
   return 0;
 }

@@ -1,6 +1,6 @@
-"""The boundary from plain C: tests/c_abi/host_calls.c includes the public
-header as C99 with warnings as errors, links against the built library and
-exercises the host-only entry points (no GPU needed)."""
+"""The boundary from plain C: tests/c_abi/host_calls.c includes both public
+headers as C99 with warnings as errors, links against both built libraries
+and exercises the host-only entry points (no GPU needed)."""
 
 from __future__ import annotations
 
@@ -20,7 +20,8 @@ def test_c_caller_compiles_links_and_passes(built_library, tmp_path):
     lib_dir = built_library.parent
     subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
                     "-I", str(_build.INCLUDE_DIR), str(SRC), "-o", str(exe),
-                    "-L", str(lib_dir), "-lmhc_h_aggregate", f"-Wl,-rpath,{lib_dir}"],
+                    "-L", str(lib_dir), "-lmhc_h_aggregate", "-lmhc_coeff_bwd",
+                    f"-Wl,-rpath,{lib_dir}"],
                    check=True, capture_output=True, text=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stderr

@@ -72,3 +72,50 @@ def test_forward_and_backward_replay_from_a_graph(device, T, H):
         eager = ops.h_aggregate(d["residual"], d["pre"])
         torch.cuda.synchronize()
         assert torch.equal(eager.view(torch.int16), out.view(torch.int16))
+
+
+@pytest.mark.parametrize("launches", [1, 2])
+def test_coefficient_backward_replays_from_a_graph(device, launches):
+    """The coefficient epilogue in a captured graph: its arrival counter is
+    left at zero by every replay, so replays keep giving the oracle's bits."""
+    from hyper_connection_residual_mhc_amd import coeff
+    from hyper_connection_residual_mhc_amd.workloads import make_coeff_inputs
+    from oracle import coeff_bwd as CB
+    say(f"graph capture coefficient backward launches={launches}")
+    keys = ("mix", "pre", "post", "grad_pre", "grad_post", "grad_res", "alpha")
+    R, n = 2048, 4
+    d = {k: torch.from_numpy(v).to(device) for k, v in make_coeff_inputs(R, n, seed=50).items()}
+    gm = torch.empty((R, 24), dtype=torch.float32, device=device)
+    gb = torch.empty((24,), dtype=torch.float32, device=device)
+    ga = torch.empty((3,), dtype=torch.float32, device=device)
+    ws = torch.zeros(coeff.mhc_coeff_bwd_workspace_bytes(R, n), dtype=torch.uint8, device=device)
+
+    def step():
+        coeff.mhc_coeff_bwd(*(d[k] for k in keys), 2.0, grad_mix=gm, grad_b=gb, grad_alpha=ga,
+                            workspace=ws, launches=launches)
+
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for replay in range(4):
+        host = make_coeff_inputs(R, n, seed=51 + replay)
+        for k in keys:
+            d[k].copy_(torch.from_numpy(host[k]).to(device))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want = CB.coeff_bwd(*(host[k] for k in keys), 2.0, n)
+        for name, got, w in zip(("grad_mix", "grad_b", "grad_alpha"), (gm, gb, ga), want):
+            assert_bytes_equal(got.cpu().numpy(), w, f"replay {replay} {name}")
+        assert int(ws[:4].view(torch.int32).item()) == 0
+        step()                                  # eager work between replays
+        torch.cuda.synchronize()
+        assert_bytes_equal(gb.cpu().numpy(), want[1], f"eager after replay {replay}")
