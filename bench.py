@@ -472,6 +472,52 @@ def run_sweep(path: str, rounds: int = 7, warm: int = 10, timed: int = 100,
     ev.close()
 
 
+# Launch shapes of the backward whose HBM traffic the counter runs compare
+# (T=1024, H=7168): the policy's row layout with a token per block, the row
+# layout with one row per block (a token's 4 waves in 4 blocks, which land on
+# different XCDs and so different L2s), the split layout, and the row layout
+# at half the vector width.
+COUNTER_CASES = {
+    "rows": {"layout": 2},
+    "rows-1-per-block": {"layout": 2, "block_threads": 64},
+    "split": {"layout": 1},
+    "rows-v4": {"layout": 2, "vec_width": 4},
+}
+
+
+def run_counter_case(case: str, T: int, H: int, launches: int = 64, nsets: int = 8) -> dict:
+    """`launches` backward calls in one launch shape on rotating cold sets
+    (for rocprofv3 --pmc runs: FETCH_SIZE / WRITE_SIZE per dispatch), after
+    the 256 MiB calibration copy. Returns the plan and the mean event time."""
+    import torch
+    from hyper_connection_residual_mhc_amd import _build, _lib, ops
+    if not _build.library_is_built():
+        _build.build_library()
+    lib = _lib.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sets = make_sets(T, H, nsets, dev)
+    sh = int(torch.cuda.current_stream(dev).cuda_stream)
+    launch = ops._launch_arg(COUNTER_CASES[case])
+    s0 = sets[0]
+    plan, grid = ops.mhc_h_aggregate_plan_bwd(s0.residual, s0.pre, s0.grad_out, s0.grad_residual,
+                                              s0.grad_pre, T, H, launch=COUNTER_CASES[case])
+    copy_probe(dev)
+    ev = HipEvents(2 * launches)
+    E = ev.handles
+    for k in range(launches):
+        x = sets[k % nsets]
+        _lib.check(lib.mhc_h_aggregate_bwd_timed(
+            x.residual.data_ptr(), x.pre.data_ptr(), x.grad_out.data_ptr(),
+            x.grad_residual.data_ptr(), x.grad_pre.data_ptr(), T, H, sh, launch,
+            E[2 * k], E[2 * k + 1]))
+    torch.cuda.synchronize()
+    us = statistics.fmean(ev.elapsed_us(2 * k, 2 * k + 1) for k in range(launches))
+    ev.close()
+    return {"case": case, "T": T, "H": H, "plan": plan, "grid_blocks": grid,
+            "launches": launches, "us_mean": round(us, 3), "bytes": bwd_bytes(T, H)}
+
+
 # The coefficient backward epilogue at the shapes of the page "perf: fuse
 # mHC coefficient backward epilogue" (Performance Method: B = 4 sequences of
 # T in {128, 512, 2048} tokens at HC = 4, so R = 4T rows; HC = 2 and 8 as
@@ -707,6 +753,9 @@ def main() -> int:
                          "latency / bandwidth / backward shapes and write JSON lines")
     ap.add_argument("--sweep-part", choices=("all", "h_aggregate", "coeff"), default="all",
                     help="with --sweep: which operations to time")
+    ap.add_argument("--counter-case", choices=sorted(COUNTER_CASES),
+                    help="instead of the step benchmark, run 64 backward calls in one launch "
+                         "shape (for rocprofv3 --pmc runs) and print one JSON line")
     ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV")
     ap.add_argument("--summarize-pmc", metavar="COUNTER_CSV", nargs="+")
     args = ap.parse_args()
@@ -716,6 +765,9 @@ def main() -> int:
         return 0
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc)
+        return 0
+    if args.counter_case:
+        print(json.dumps(run_counter_case(args.counter_case, args.tokens, args.hidden)))
         return 0
     if args.sweep:
         if args.gpus != 1:

@@ -85,3 +85,20 @@ def test_coefficient_epilogue_bytes():
     assert bench.coeff_bytes(10, 2) == 10 * (64 + 48) + 12 + 32 + 12
     assert bench.coeff_bytes(10, 8) == 10 * (256 + 768) + 12 + 320 + 12
     assert [r for r, n in bench.COEFF_SWEEP if n == 4] == [512, 2048, 8192]
+
+
+def test_counter_cases_are_valid_launch_shapes(built_library):
+    """Every launch shape the counter runs compare passes the library's own
+    plan check at T=1024, H=7168 (fake addresses; no GPU)."""
+    from hyper_connection_residual_mhc_amd import ops
+    T, H = 1024, 7168
+    base = 1 << 34
+    res, pre, g, gr, gp = base, base + (1 << 30), base + (2 << 30), base + (3 << 30), base + (4 << 30)
+    layouts = {}
+    for case, launch in bench.COUNTER_CASES.items():
+        plan, grid = ops.mhc_h_aggregate_plan_bwd(res, pre, g, gr, gp, T, H, launch=launch)
+        layouts[case] = (plan["layout"], plan["block_threads"], plan["vec_width"], grid)
+    assert layouts["rows"] == (2, 256, 8, 1024)
+    assert layouts["rows-1-per-block"] == (2, 64, 8, 4096)
+    assert layouts["split"][0] == 1
+    assert layouts["rows-v4"][2] == 4
