@@ -483,10 +483,17 @@ COUNTER_CASES = {
     "split": {"layout": 1},
     "rows-v4": {"layout": 2, "vec_width": 4},
 }
+# And of the forward: the policy (one-wave blocks, 16-byte accesses), the
+# page's 4-byte (bf16x2) accesses, and 1024-thread blocks.
+FWD_COUNTER_CASES = {
+    "fwd": {},
+    "fwd-v2": {"vec_width": 2},
+    "fwd-1024": {"block_threads": 1024},
+}
 
 
 def run_counter_case(case: str, T: int, H: int, launches: int = 64, nsets: int = 8) -> dict:
-    """`launches` backward calls in one launch shape on rotating cold sets
+    """`launches` backward (or forward) calls in one launch shape on rotating cold sets
     (for rocprofv3 --pmc runs: FETCH_SIZE / WRITE_SIZE per dispatch), after
     the 256 MiB calibration copy. Returns the plan and the mean event time."""
     import torch
@@ -498,24 +505,38 @@ def run_counter_case(case: str, T: int, H: int, launches: int = 64, nsets: int =
     torch.cuda.set_device(dev)
     sets = make_sets(T, H, nsets, dev)
     sh = int(torch.cuda.current_stream(dev).cuda_stream)
-    launch = ops._launch_arg(COUNTER_CASES[case])
+    forward = case in FWD_COUNTER_CASES
+    shape = FWD_COUNTER_CASES[case] if forward else COUNTER_CASES[case]
+    launch = ops._launch_arg(shape)
     s0 = sets[0]
-    plan, grid = ops.mhc_h_aggregate_plan_bwd(s0.residual, s0.pre, s0.grad_out, s0.grad_residual,
-                                              s0.grad_pre, T, H, launch=COUNTER_CASES[case])
+    if forward:
+        plan, grid = ops.mhc_h_aggregate_plan_fwd(s0.residual, s0.pre, s0.out, T, H,
+                                                  launch=shape)
+    else:
+        plan, grid = ops.mhc_h_aggregate_plan_bwd(s0.residual, s0.pre, s0.grad_out,
+                                                  s0.grad_residual, s0.grad_pre, T, H,
+                                                  launch=shape)
     copy_probe(dev)
     ev = HipEvents(2 * launches)
     E = ev.handles
     for k in range(launches):
         x = sets[k % nsets]
-        _lib.check(lib.mhc_h_aggregate_bwd_timed(
-            x.residual.data_ptr(), x.pre.data_ptr(), x.grad_out.data_ptr(),
-            x.grad_residual.data_ptr(), x.grad_pre.data_ptr(), T, H, sh, launch,
-            E[2 * k], E[2 * k + 1]))
+        if forward:
+            st = lib.mhc_h_aggregate_fwd_timed(x.residual.data_ptr(), x.pre.data_ptr(),
+                                               x.out.data_ptr(), T, H, sh, launch,
+                                               E[2 * k], E[2 * k + 1])
+        else:
+            st = lib.mhc_h_aggregate_bwd_timed(
+                x.residual.data_ptr(), x.pre.data_ptr(), x.grad_out.data_ptr(),
+                x.grad_residual.data_ptr(), x.grad_pre.data_ptr(), T, H, sh, launch,
+                E[2 * k], E[2 * k + 1])
+        _lib.check(st)
     torch.cuda.synchronize()
     us = statistics.fmean(ev.elapsed_us(2 * k, 2 * k + 1) for k in range(launches))
     ev.close()
     return {"case": case, "T": T, "H": H, "plan": plan, "grid_blocks": grid,
-            "launches": launches, "us_mean": round(us, 3), "bytes": bwd_bytes(T, H)}
+            "launches": launches, "us_mean": round(us, 3),
+            "bytes": fwd_bytes(T, H) if forward else bwd_bytes(T, H)}
 
 
 # The coefficient backward epilogue at the shapes of the page "perf: fuse
@@ -753,9 +774,9 @@ def main() -> int:
                          "latency / bandwidth / backward shapes and write JSON lines")
     ap.add_argument("--sweep-part", choices=("all", "h_aggregate", "coeff"), default="all",
                     help="with --sweep: which operations to time")
-    ap.add_argument("--counter-case", choices=sorted(COUNTER_CASES),
-                    help="instead of the step benchmark, run 64 backward calls in one launch "
-                         "shape (for rocprofv3 --pmc runs) and print one JSON line")
+    ap.add_argument("--counter-case", choices=sorted(COUNTER_CASES) + sorted(FWD_COUNTER_CASES),
+                    help="instead of the step benchmark, run 64 backward (or forward) calls in "
+                         "one launch shape (for rocprofv3 --pmc runs) and print one JSON line")
     ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV")
     ap.add_argument("--summarize-pmc", metavar="COUNTER_CSV", nargs="+")
     args = ap.parse_args()

@@ -102,3 +102,8 @@ def test_counter_cases_are_valid_launch_shapes(built_library):
     assert layouts["rows-1-per-block"] == (2, 64, 8, 4096)
     assert layouts["split"][0] == 1
     assert layouts["rows-v4"][2] == 4
+    fwd = {}
+    for case, launch in bench.FWD_COUNTER_CASES.items():
+        plan, grid = ops.mhc_h_aggregate_plan_fwd(res, pre, base + (5 << 30), T, H, launch=launch)
+        fwd[case] = (plan["block_threads"], plan["vec_width"])
+    assert fwd == {"fwd": (64, 8), "fwd-v2": (64, 2), "fwd-1024": (1024, 8)}
