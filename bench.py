@@ -19,7 +19,9 @@ taken from HIP events that the library attaches to the backward dispatches
 of every 32nd timed step (start and end timestamps of the dispatch itself);
 its `traffic` comes from the committed counter summary while the library's
 device code is the one it was measured on. `stream_probe` compares the
-backward with a plain stream of the same read:write bytes. `cpu_baseline`
+backward with a plain stream of the same read:write bytes, and
+`fwd_stream_probe` does the same for the forward; both are timed back to
+back after the timed steps. `cpu_baseline`
 times the CPU oracle on the same workload, on one core and on all cores.
 
 Helpers for the profiles: --summarize-stats and --summarize-pmc turn
@@ -310,12 +312,20 @@ def run_gpu(T: int, H: int, steps: int, warmup: int, nsets: int, probe: bool,
 
     ceil_kernel_us = back_to_back(lambda k, a, b: bwd_t(*bargs[k % nsets], None, a, b))
     ceil_probe_us = back_to_back(lambda k, a, b: probe.call(lib, k, sh, a, b))
-    cev.close()
     probe_bytes = probe.bytes
     del probe
+    # The same for the forward and its 4:1 mix.
+    fprobe = ProbeBuffers(fwd_bytes(T, H), PROBE_MIX["fwd"], nsets, dev)
+    fwd_ceil_us = back_to_back(lambda k, a, b: fwd_t(*fargs[k % nsets], None, a, b))
+    fwd_probe_us = back_to_back(lambda k, a, b: fprobe.call(lib, k, sh, a, b))
+    fprobe_bytes = fprobe.bytes
+    del fprobe
+    cev.close()
     return {
         "probe": {"kernel_us": ceil_kernel_us, "probe_us": ceil_probe_us,
                     "probe_bytes": probe_bytes},
+        "fwd_probe": {"kernel_us": fwd_ceil_us, "probe_us": fwd_probe_us,
+                      "probe_bytes": fprobe_bytes},
         "wall_s": t1 - t0,
         "timed_launches": len(sampled),
         "fwd_us": fwd_us,
@@ -328,15 +338,16 @@ def run_gpu(T: int, H: int, steps: int, warmup: int, nsets: int, probe: bool,
     }
 
 
-def probe_record(kernel_bytes: int, c: dict) -> dict:
+def probe_record(kernel_bytes: int, c: dict, direction: str = "bwd") -> dict:
     k = statistics.fmean(c["kernel_us"])
     p = statistics.fmean(c["probe_us"])
     kg = kernel_bytes / k / 1e3
     pg = c["probe_bytes"] / p / 1e3
+    name, (r, w) = ("backward" if direction == "bwd" else "forward"), PROBE_MIX[direction]
     return {
-        "kind": "mhc_stream_probe: the backward's 5:4 read:write byte mix as a plain "
-                "stream (one 64-lane block per 5 KiB read + 4 KiB written), no "
-                "arithmetic; the backward and the probe each timed back to back by "
+        "kind": f"mhc_stream_probe: the {name}'s {r}:{w} read:write byte mix as a plain "
+                f"stream (one 64-lane block per {r} KiB read + {w} KiB written), no "
+                f"arithmetic; the {name} and the probe each timed back to back by "
                 "their own dispatch events, cold buffers",
         "probe_bytes": c["probe_bytes"],
         "probe_us": round(p, 3),
@@ -871,6 +882,7 @@ def main() -> int:
                        "hagg_bwd_kernel (backward, split layout)"),
         },
         "stream_probe": probe_record(bwd_bytes(T, H), g["probe"]),
+        "fwd_stream_probe": probe_record(fwd_bytes(T, H), g["fwd_probe"], "fwd"),
         "timing": {"per_kernel": "HIP events attached to the dispatches of every "
                                  f"{args.time_every}th step ({g['timed_launches']} launches "
                                  "of each kernel)",

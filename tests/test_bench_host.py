@@ -35,6 +35,10 @@ def test_probe_record_fractions():
     rec = bench.probe_record(1000, {"kernel_us": [1.0, 1.0], "probe_us": [2.0, 2.0],
                                     "probe_bytes": 1000})
     assert rec["kernel_gbps"] == 1.0 and rec["probe_gbps"] == 0.5 and rec["frac_of_probe"] == 2.0
+    assert "5:4" in rec["kind"] and "backward" in rec["kind"]
+    rec = bench.probe_record(1000, {"kernel_us": [1.0], "probe_us": [1.0], "probe_bytes": 500},
+                             "fwd")
+    assert "4:1" in rec["kind"] and "forward" in rec["kind"] and rec["frac_of_probe"] == 2.0
 
 
 def test_summaries_parse_rocprof_csv(tmp_path, capsys):
