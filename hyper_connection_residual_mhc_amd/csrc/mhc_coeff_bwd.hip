@@ -160,11 +160,19 @@ __device__ __forceinline__ void output_sum(const float* __restrict__ partial, ui
   const Rsrc rs = make_rsrc(partial + static_cast<int64_t>(v) * chunks,
                             static_cast<int64_t>(chunks) * 4);
   float acc[1] = {0.0f};
-  // Every lane runs the same trip count; past the last chunk the range
-  // check reads +0.0, and adding +0.0 to a sum that started at +0.0 leaves
-  // it unchanged.
+  // Every lane runs the same trip count, in steps of kAhead rounds whose
+  // loads are all issued before the first add (the adds stay in ascending
+  // chunk order). Past the last chunk the range check reads +0.0, and
+  // adding +0.0 to a sum that started at +0.0 leaves it unchanged.
+  constexpr uint32_t kAhead = 8;
   const uint32_t rounds = (chunks + 63) / 64;
-  for (uint32_t k = 0; k < rounds; ++k) acc[0] = acc[0] + ld(rs, (k * 64 + lane) * 4);
+  for (uint32_t k = 0; k < rounds; k += kAhead) {
+    float x[kAhead];
+#pragma unroll
+    for (uint32_t u = 0; u < kAhead; ++u) x[u] = ld(rs, ((k + u) * 64 + lane) * 4);
+#pragma unroll
+    for (uint32_t u = 0; u < kAhead; ++u) acc[0] = acc[0] + x[u];
+  }
   wave_trees(acc);
   if (lane == 0) {
     const bool bias = static_cast<int32_t>(v) < m;
