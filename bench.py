@@ -474,9 +474,12 @@ def run_sweep(path: str, rounds: int = 7, warm: int = 10, timed: int = 100,
             del sets
             torch.cuda.empty_cache()
         for R, n in (COEFF_SWEEP if part in ("all", "coeff") else []):
-            # the policy's form, then the two-launch form for comparison
+            # the policy's form, then the two-launch form for comparison; the
+            # oracle timed on the host beside the policy's form
             for launches in (0, 2):
                 rec = time_coeff(R, n, dev, sh, ev, rounds, warm, timed, summary, launches)
+                if launches == 0:
+                    rec["cpu_baseline"] = run_coeff_cpu_baseline(R, n)
                 f.write(json.dumps(rec) + "\n")
                 f.flush()
                 print(json.dumps(rec), file=sys.stderr, flush=True)
@@ -564,6 +567,27 @@ def coeff_bytes(R: int, n: int) -> int:
     plus alpha, grad_b and grad_alpha once."""
     m = 2 * n + n * n
     return R * (32 * n + 12 * n * n) + 12 + 4 * m + 12
+
+
+def run_coeff_cpu_baseline(R: int, n: int, min_seconds: float = 1.0) -> dict:
+    """The coefficient oracle, as it stands (numpy, one thread), on the same
+    seed-0 inputs: calls repeated for at least `min_seconds` after one
+    untimed call; microseconds per call."""
+    from hyper_connection_residual_mhc_amd.workloads import make_coeff_inputs
+    from oracle import coeff_bwd as CB
+    host = make_coeff_inputs(R, n, seed=0)
+    args = [host[k] for k in COEFF_KEYS]
+    CB.coeff_bwd(*args, 2.0, n)
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        CB.coeff_bwd(*args, 2.0, n)
+        calls += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {"value": round(dt / calls * 1e6, 1), "unit": "us/call", "cores": 1, "kind": "oracle",
+            "sample": f"{calls} calls of the oracle on the same {R}-row seed-0 inputs after one "
+                      f"untimed call ({dt:.2f} s)"}
 
 
 def time_coeff(R, n, dev, sh, ev, rounds, warm, timed, summary, launches=0) -> dict:

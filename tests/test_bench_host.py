@@ -111,3 +111,9 @@ def test_counter_cases_are_valid_launch_shapes(built_library):
         plan, grid = ops.mhc_h_aggregate_plan_fwd(res, pre, base + (5 << 30), T, H, launch=launch)
         fwd[case] = (plan["block_threads"], plan["vec_width"])
     assert fwd == {"fwd": (64, 8), "fwd-v2": (64, 2), "fwd-1024": (1024, 8)}
+
+
+def test_coefficient_cpu_baseline_record():
+    rec = bench.run_coeff_cpu_baseline(64, 4, min_seconds=0.05)
+    assert rec["kind"] == "oracle" and rec["cores"] == 1 and rec["unit"] == "us/call"
+    assert rec["value"] > 0 and "64-row" in rec["sample"]
