@@ -85,17 +85,42 @@ __device__ __forceinline__ void wave_trees(float (&v)[K]) {
 //
 // Writes grad_mix for the chunk's rows and, for each of the m + 3 summed
 // quantities v (d of every column, then e of the three groups), the chunk's
-// first-stage sum to partial[v * chunks + chunk] (one lane stores them).
+// first-stage sum to partial[v * chunks + chunk].
+//
+// The first stage runs through LDS: every lane (row) writes its m + 3
+// values into the wave's tile, value-major; then lane j reads value j's 64
+// rows and applies the halving tree to them in its registers, in the order
+// the tree defines (offsets 32, 16, 8, 4, 2, 1; x[i] += x[i + off] for
+// i < off), and stores that chunk sum. That is the same arithmetic as a
+// tree across lanes, with a third of the instructions. More than 64 values
+// (n = 8) take two passes through the tile.
+//
+// Every wave of the block must call this (it holds block barriers); a wave
+// whose chunk is past the end (`active` false) reads zeros, writes no
+// grad_mix and stores no chunk sums.
+constexpr int kTileStride = 68;  // floats per value row: 16-byte aligned, no bank conflicts
+
+template <int N>
+struct Tile {
+  static constexpr int M = 2 * N + N * N;
+  static constexpr int kValues = M + 3;
+  static constexpr int kRows = kValues < 64 ? kValues : 64;  // values per pass
+  static constexpr int kFloats = kRows * kTileStride;
+};
+
 template <int N>
 __device__ __forceinline__ void chunk_sums(
     const float* __restrict__ mix, const float* __restrict__ pre,
     const float* __restrict__ post, const float* __restrict__ grad_pre,
     const float* __restrict__ grad_post, const float* __restrict__ grad_res,
     const float* __restrict__ alpha, float inv_c, float* __restrict__ grad_mix,
-    float* __restrict__ partial, int64_t rows, uint32_t chunks, uint32_t c, uint32_t lane) {
+    float* __restrict__ partial, int64_t rows, uint32_t chunks, uint32_t c, uint32_t lane,
+    bool active, float* tile) {
   constexpr int M = 2 * N + N * N;
+  constexpr int V = M + 3;
   const int64_t r0 = static_cast<int64_t>(c) * kChunk;
-  const int64_t valid = rows - r0 < kChunk ? rows - r0 : kChunk;
+  int64_t valid = rows - r0;
+  valid = valid < 0 ? 0 : (valid > kChunk ? kChunk : valid);
 
   // Resources cover exactly the chunk's valid rows.
   const Rsrc rs_mix = make_rsrc(mix + r0 * M, valid * M * 4);
@@ -132,7 +157,7 @@ __device__ __forceinline__ void chunk_sums(
     st(rs_gmix, (lane * M + j) * 4, a * d[j]);
   }
 
-  float v[M + 3];
+  float v[V];
   v[M] = 0.0f;
   v[M + 1] = 0.0f;
   v[M + 2] = 0.0f;
@@ -142,11 +167,35 @@ __device__ __forceinline__ void chunk_sums(
     v[M + k] = v[M + k] + d[j] * x[j];
     v[j] = d[j];
   }
-  wave_trees(v);
-  if (lane == 0) {
-    const Rsrc rs_part = make_rsrc(partial, static_cast<int64_t>(M + 3) * chunks * 4);
+
+  const Rsrc rs_part = make_rsrc(partial, static_cast<int64_t>(V) * chunks * 4);
 #pragma unroll
-    for (int i = 0; i < M + 3; ++i) st(rs_part, (static_cast<uint32_t>(i) * chunks + c) * 4, v[i]);
+  for (int base = 0; base < V; base += 64) {
+    constexpr int kRows = Tile<N>::kRows;
+    const int cnt = V - base < kRows ? V - base : kRows;
+    if (base > 0) __syncthreads();  // the previous pass has read the tile
+#pragma unroll
+    for (int i = 0; i < kRows; ++i)
+      if (i < cnt) tile[i * kTileStride + lane] = v[base + i];
+    __syncthreads();
+    if (static_cast<int>(lane) < cnt) {
+      float t[64];
+      const float4* row = reinterpret_cast<const float4*>(tile + lane * kTileStride);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const float4 f = row[q];
+        t[4 * q] = f.x;
+        t[4 * q + 1] = f.y;
+        t[4 * q + 2] = f.z;
+        t[4 * q + 3] = f.w;
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off /= 2) {
+#pragma unroll
+        for (int r = 0; r < off; ++r) t[r] = t[r] + t[r + off];
+      }
+      if (active) st(rs_part, ((base + lane) * chunks + c) * 4, t[0]);
+    }
   }
 }
 
@@ -189,8 +238,9 @@ __global__ __launch_bounds__(64) void coeff_partial_kernel(
     const float* __restrict__ grad_post, const float* __restrict__ grad_res,
     const float* __restrict__ alpha, float inv_c, float* __restrict__ grad_mix,
     float* __restrict__ partial, int64_t rows, uint32_t chunks) {
+  __shared__ __align__(16) float tile[Tile<N>::kFloats];
   chunk_sums<N>(mix, pre, post, grad_pre, grad_post, grad_res, alpha, inv_c, grad_mix, partial,
-                rows, chunks, blockIdx.x, threadIdx.x);
+                rows, chunks, blockIdx.x, threadIdx.x, true, tile);
 }
 
 // Two-launch form, second launch. Grid: m + 3 blocks of 64 threads, block v
@@ -224,12 +274,12 @@ __global__ __launch_bounds__(64 * kFusedWaves) void coeff_fused_kernel(
   constexpr int M = 2 * N + N * N;
   constexpr int Q = (M + 3 + kFusedWaves - 1) / kFusedWaves;  // outputs per wave
   __shared__ uint32_t last;
+  __shared__ __align__(16) float tiles[kFusedWaves * Tile<N>::kFloats];
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t c = blockIdx.x * kFusedWaves + wave;
-  if (c < chunks)
-    chunk_sums<N>(mix, pre, post, grad_pre, grad_post, grad_res, alpha, inv_c, grad_mix,
-                  partial, rows, chunks, c, lane);
+  chunk_sums<N>(mix, pre, post, grad_pre, grad_post, grad_res, alpha, inv_c, grad_mix, partial,
+                rows, chunks, c, lane, c < chunks, tiles + wave * Tile<N>::kFloats);
   __syncthreads();
   if (threadIdx.x == 0) {
     __threadfence();
@@ -304,12 +354,12 @@ int64_t workspace_need(int64_t rows, int32_t n) {
 }
 
 // The one-launch form is used at n <= 4 up to this many chunks. Measured per
-// call (cold inputs, n = 4): one launch 6.2 / 6.8 / 7.8 us at 512 / 2048 /
-// 8192 rows against 9.1 / 9.1 / 9.2 us for two; even at 16384 rows (9.7 vs
-// 9.6 us); behind beyond (its last block sums every output alone). At n = 8
-// two launches are faster at every size measured (12.1 vs 16.1 us at 2048
-// rows: four 80-column waves per CU load slower than one).
-constexpr int64_t kFusedMaxChunks = 128;
+// call (cold inputs, n = 4): one launch 5.0 / 5.4 / 6.7 / 8.8 us at 512 /
+// 2048 / 8192 / 16384 rows against 8.9-9.1 us for two; behind from 32768
+// rows (13.6 vs 9.4 us: its last block sums every output alone). At n = 8
+// two launches are faster at every size measured (9.0 vs 12.2 us at 2048
+// rows: four 80-column waves on one CU load more slowly than one).
+constexpr int64_t kFusedMaxChunks = 256;
 
 struct Range {
   uintptr_t lo, hi;

@@ -61,7 +61,7 @@
  * Launches: the second stage of row_sum runs either in the same launch as
  * the first (the block that finishes its chunks last does it) or in a second
  * launch. Both give the same bits. The policy (`launches` = 0) takes one
- * launch at n = 2 or 4 up to 128 chunks (8192 rows), two otherwise;
+ * launch at n = 2 or 4 up to 256 chunks (16384 rows), two otherwise;
  * `launches` = 1 or 2 forces a form. R = 0 always takes the second form (it
  * only writes the +0.0 sums).
  *

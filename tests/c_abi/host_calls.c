@@ -85,7 +85,7 @@ int main(void) {
     CHECK(mhc_coeff_abi_version() == MHC_COEFF_ABI_VERSION);
     CHECK(ws_bytes == 256 + 27 * (R / MHC_COEFF_CHUNK) * 4);
     CHECK(mhc_coeff_bwd_workspace_bytes(R, 3) == -1);
-    CHECK(mhc_coeff_bwd_plan(R, n, 0) == 1 && mhc_coeff_bwd_plan(R + 1, n, 0) == 2);
+    CHECK(mhc_coeff_bwd_plan(2 * R, n, 0) == 1 && mhc_coeff_bwd_plan(2 * R + 1, n, 0) == 2);
     CHECK(mhc_coeff_bwd_validate(mix, cpre, post, gpre, gpost, gres, alpha, 2.0f, gmix, gb, ga,
                                  ws, ws_bytes, R, n) == MHC_SUCCESS);
     CHECK(mhc_coeff_bwd_validate(mix, cpre, post, gpre, gpost, gres, alpha, 2.0f, (float*)mix,

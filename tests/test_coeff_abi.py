@@ -61,8 +61,8 @@ def test_launch_policy(lib):
     plan = lib.mhc_coeff_bwd_plan
     assert plan(0, 4, 0) == 2 and plan(0, 4, 1) == 2        # R = 0: the sums only
     assert plan(1, 4, 0) == 1 and plan(1, 2, 0) == 1
-    assert plan(8192, 4, 0) == 1 and plan(8192, 2, 0) == 1  # up to 128 chunks: one launch
-    assert plan(8193, 4, 0) == 2
+    assert plan(16384, 4, 0) == 1 and plan(16384, 2, 0) == 1  # up to 256 chunks: one launch
+    assert plan(16385, 4, 0) == 2
     assert plan(1, 8, 0) == 2 and plan(8192, 8, 0) == 2     # n = 8: two launches
     assert plan(100, 4, 2) == 2 and plan(1 << 20, 2, 1) == 1 and plan(64, 8, 1) == 1
     assert plan(100, 4, 3) == -1 and plan(100, 4, -1) == -1 and plan(100, 5, 0) == -1
