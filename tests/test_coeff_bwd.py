@@ -198,6 +198,39 @@ def test_special_values(device):
     _check(host, 2.0, device, "special")
 
 
+@pytest.mark.parametrize("launches", [1, 2])
+@pytest.mark.parametrize("shift", [1, 2, 3])
+def test_buffers_aligned_to_4_bytes_only(device, shift, launches):
+    """The header asks for 4-byte alignment only. Every tensor here starts
+    `shift` floats past a 256-byte boundary (and the workspace 4 bytes
+    past one), so no row starts on a 16-byte boundary; the bytes must be
+    the oracle's."""
+    say(f"coeff bwd shift={shift} launches={launches}")
+    R, n = 1000, 4
+    host = make_coeff_inputs(R, n, seed=60 + shift)
+
+    def shifted(a):
+        buf = torch.empty(a.size + shift + 64, dtype=torch.float32, device=device)
+        t = buf[shift:shift + a.size].view(a.shape)
+        t.copy_(torch.from_numpy(np.ascontiguousarray(a)).to(device))
+        assert t.data_ptr() % 16 == 4 * shift
+        return t
+
+    d = {k: shifted(host[k]) for k in KEYS}
+    gm = shifted(np.zeros((R, 24), np.float32))
+    gb = shifted(np.zeros(24, np.float32))
+    ga = shifted(np.zeros(3, np.float32))
+    need = coeff.mhc_coeff_bwd_workspace_bytes(R, n)
+    wbuf = torch.zeros(need + 64, dtype=torch.uint8, device=device)
+    ws = wbuf[4:4 + need]
+    coeff.mhc_coeff_bwd(*(d[k] for k in KEYS), 2.0, grad_mix=gm, grad_b=gb, grad_alpha=ga,
+                        workspace=ws, launches=launches)
+    torch.cuda.synchronize()
+    want = _oracle(host, 2.0)
+    for name, g, w in zip(("grad_mix", "grad_b", "grad_alpha"), (gm, gb, ga), want):
+        assert_bytes_equal(g.cpu().numpy(), w, f"shift {shift} {name}")
+
+
 def test_timed_call_records_both_events(device):
     say("coeff bwd timed")
     host = make_coeff_inputs(2048, 4, seed=2)
