@@ -20,11 +20,12 @@
 //    finishes last (an arrival counter in the workspace, release / acquire
 //    fences, no waiting), or, for long batches, in a second launch with one
 //    wave per summed output.
-//  * The chunk sums are the first stage of the order itself (a 64-lane
-//    halving tree in registers, lanes = rows), and the strided walk over
-//    them plus the same tree is the second, so both forms compute exactly
-//    the defined order; the workspace holds the chunk sums output by output
-//    so that one output's loads are contiguous across lanes.
+//  * The chunk sums are the first stage of the order itself (the halving
+//    tree over a chunk's 64 rows, run per value by one lane after an LDS
+//    transpose), and the strided walk over them plus the same tree across
+//    lanes is the second, so both forms compute exactly the defined order;
+//    the workspace holds the chunk sums output by output so that one
+//    output's loads are contiguous across lanes.
 //  * Rows past the end read as 0 through the buffer range check and produce
 //    exactly +0.0 everywhere, which is what the order prescribes for them;
 //    their grad_mix stores are dropped by the same check.
