@@ -48,6 +48,29 @@ def make_inputs(T: int, H: int, seed: int = 0, *, grad: bool = False,
     return out
 
 
+def make_unit_inputs_device(T: int, H: int, seed: int, device, hc: int = HC
+                            ) -> dict[str, torch.Tensor]:
+    """Device inputs whose backward reduction is exact in any order, drawn on
+    the device (for sizes the host would take minutes to draw) with a
+    torch.Generator seeded with `seed`, in this order: residual codes
+    (uint8 in [0, 16): 0 -> -1, 1 -> +1, otherwise 0, so 1/8 of the entries
+    are non-zero), grad_out signs (+1 or -1), pre U[0,1) fp32. Values are
+    written as bf16 bit patterns directly (+1 is 0x3F80, -1 is 0xBF80)."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    code = torch.randint(0, 16, (T, hc, H), dtype=torch.uint8, device=device, generator=gen)
+    plus = torch.tensor(0x3F80, dtype=torch.int16, device=device)
+    minus = torch.tensor(0xBF80 - 0x10000, dtype=torch.int16, device=device)
+    zero = torch.tensor(0, dtype=torch.int16, device=device)
+    residual = torch.where(code == 1, plus, torch.where(code == 0, minus, zero))
+    del code
+    signs = torch.randint(0, 2, (T, H), dtype=torch.uint8, device=device, generator=gen)
+    grad_out = torch.where(signs == 1, plus, minus)
+    pre = torch.rand((T, hc), dtype=torch.float32, device=device, generator=gen)
+    return {"residual": residual.view(torch.bfloat16), "pre": pre,
+            "grad_out": grad_out.view(torch.bfloat16)}
+
+
 def make_coeff_inputs(rows: int, n: int = HC, seed: int = 0, *,
                       post_scale: float = 2.0) -> dict[str, np.ndarray]:
     """Host inputs of the coefficient backward epilogue (all float32).
