@@ -71,6 +71,35 @@ def make_unit_inputs_device(T: int, H: int, seed: int, device, hc: int = HC
             "grad_out": grad_out.view(torch.bfloat16)}
 
 
+def make_coeff_unit_inputs_device(rows: int, n: int, seed: int, device
+                                  ) -> dict[str, torch.Tensor]:
+    """Device inputs of the coefficient epilogue whose sums are exact in any
+    order, drawn on the device with a torch.Generator seeded with `seed`, in
+    this order: mix sign codes (uint8 0/1 -> -1/+1, every column), residual
+    gradient codes (uint8 in [0, 128): 0 -> -1, 1 -> +1, otherwise 0), pre
+    U[0,1), post U[0,2). grad_pre and grad_post are zero. The uint8 codes
+    are returned too ("mix_code", "grad_res_code") so that a checker can form
+    exact integer sums without reading the fp32 tensors back."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    m = 2 * n + n * n
+    one = torch.tensor(1.0, dtype=torch.float32, device=device)
+    zero = torch.tensor(0.0, dtype=torch.float32, device=device)
+    mix_code = torch.randint(0, 2, (rows, m), dtype=torch.uint8, device=device, generator=gen)
+    mix = torch.where(mix_code == 1, one, -one)
+    res_code = torch.randint(0, 128, (rows, n * n), dtype=torch.uint8, device=device,
+                             generator=gen)
+    grad_res = torch.where(res_code == 1, one, torch.where(res_code == 0, -one, zero))
+    pre = torch.rand((rows, n), dtype=torch.float32, device=device, generator=gen)
+    post = torch.rand((rows, n), dtype=torch.float32, device=device, generator=gen) * 2.0
+    return {"mix": mix, "pre": pre, "post": post,
+            "grad_pre": torch.zeros((rows, n), dtype=torch.float32, device=device),
+            "grad_post": torch.zeros((rows, n), dtype=torch.float32, device=device),
+            "grad_res": grad_res,
+            "alpha": torch.tensor([0.75, 1.25, 1.5], dtype=torch.float32, device=device),
+            "mix_code": mix_code, "grad_res_code": res_code}
+
+
 def make_coeff_inputs(rows: int, n: int = HC, seed: int = 0, *,
                       post_scale: float = 2.0) -> dict[str, np.ndarray]:
     """Host inputs of the coefficient backward epilogue (all float32).
