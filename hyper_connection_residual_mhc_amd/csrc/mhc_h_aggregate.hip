@@ -324,7 +324,7 @@ __device__ __forceinline__ void bwd_consume(BwdSlots<V, U, S, ACC>& sl, int u, u
 // accesses (fewer for a short last group).
 //
 // At most 128 VGPRs (4 waves per SIMD), so that 4 blocks fit on a CU: the
-// policy uses this layout for batches below 768 rows (192 tokens at
+// policy uses this layout for batches below 544 rows (136 tokens at
 // n = 4), which are then resident at once.
 template <int V, int U, int S, bool ACC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void hagg_bwd_kernel(
@@ -695,9 +695,11 @@ constexpr int64_t kTwoStreamsFromT = 128;
 constexpr int64_t kFourStreamsFromT = 512;
 // The row layout from this many rows (tokens x streams) per call on: it has
 // one wave per row, the split layout 4 per block of S streams, so short
-// batches keep more CUs busy split. Measured at n = 4: rows faster from
-// T = 192 (except at 320-384 tokens, H = 7168, by 1-7%), split faster at 128.
-constexpr int64_t kRowsFromRows = 768;
+// batches keep more CUs busy split. Measured at H = 7168: split faster at
+// 512 rows for n = 2, 4 and 8 (by 6-10%); rows faster or equal from 544 rows
+// at n = 4 and from 576 at n = 2 and 8 (at n = 4 except at 320-384 tokens,
+// by 1-7%).
+constexpr int64_t kRowsFromRows = 544;
 
 // Largest forward batch UPT in {1, 2, 4} whose loaded data (N rows, each
 // access max(V/2, 1) registers) fits 64 VGPRs, within the 128-VGPR budget of

@@ -120,7 +120,7 @@ typedef enum mhc_status {
  *                     row; each of its 64 lanes holds accumulator lanes
  *                     j, j+64, j+128, j+192 and the 64-lane trees run inside
  *                     the wave). The policy takes the row layout from
- *                     T * n = 768 rows on, unless a split-layout field is set or
+ *                     T * n = 544 rows on, unless a split-layout field is set or
  *                     the row layout does not fit the register budget
  *                     (scalar-width accumulating calls). Same summation
  *                     order, same bits.

@@ -220,15 +220,15 @@ def test_backward_plan_and_overrides(lib):
                                               launch={"streams_per_block": 2})
     assert plan["streams_per_block"] == 2 and plan["layout"] == SPLIT and grid == 2 * T
     # short batches spread each token's streams over more blocks (split layout)
-    for T_, spb in ((8, 1), (127, 1), (128, 2), (191, 2)):
+    for T_, spb in ((8, 1), (127, 1), (128, 2), (135, 2)):
         plan, grid = ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T_, H)
         assert plan["layout"] == SPLIT, (T_, plan)
         assert plan["streams_per_block"] == spb and grid == T_ * (4 // spb), (T_, plan)
-    # from 768 rows (tokens x streams) on: the row layout
-    plan, grid = ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, 192, H)
-    assert plan["layout"] == ROWS and grid == 192
+    # from 544 rows (tokens x streams) on: the row layout
+    plan, grid = ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, 136, H)
+    assert plan["layout"] == ROWS and grid == 136
     rr, pp, gg, ggr, ggp = bwd_ptrs(1024, 2 * H)
-    for n, t_split, t_rows in ((2, 383, 384), (8, 95, 96)):
+    for n, t_split, t_rows in ((2, 271, 272), (8, 67, 68)):
         plan, _ = ops.mhc_h_aggregate_plan_bwd_n(rr, pp, gg, ggr, ggp, t_split, n, H)
         assert plan["layout"] == SPLIT, (n, plan)
         plan, _ = ops.mhc_h_aggregate_plan_bwd_n(rr, pp, gg, ggr, ggp, t_rows, n, H)
