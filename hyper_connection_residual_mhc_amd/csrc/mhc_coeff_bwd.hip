@@ -253,19 +253,16 @@ __global__ __launch_bounds__(64) void coeff_reduce_kernel(const float* __restric
   output_sum(partial, chunks, m, blockIdx.x, threadIdx.x, grad_b, grad_alpha);
 }
 
-// One-launch form. Grid: ceil(chunks / kFusedWaves) blocks of
-// 64 * kFusedWaves threads; wave w of block b computes chunk
-// b * kFusedWaves + w. After a barrier, one thread makes the block's chunk
+// One-launch form. Grid: ceil(chunks / W) blocks of 64 * W threads (W = 2
+// or 4 waves); wave w of block b computes chunk b * W + w. After a barrier, one thread makes the block's chunk
 // sums visible device-wide (release fence; it covers the other waves'
 // stores through the barrier) and counts the block in `arrived`. The block
 // that arrives last (it reads blocks - 1) fences again (acquire), computes
 // every output's second stage (the outputs split over its waves) and sets
 // the counter back to 0 for the next call. No block waits for another, so
 // every block runs to completion whatever the others do.
-constexpr int kFusedWaves = 4;
-
-template <int N>
-__global__ __launch_bounds__(64 * kFusedWaves) void coeff_fused_kernel(
+template <int N, int W>
+__global__ __launch_bounds__(64 * W) void coeff_fused_kernel(
     const float* __restrict__ mix, const float* __restrict__ pre,
     const float* __restrict__ post, const float* __restrict__ grad_pre,
     const float* __restrict__ grad_post, const float* __restrict__ grad_res,
@@ -273,12 +270,12 @@ __global__ __launch_bounds__(64 * kFusedWaves) void coeff_fused_kernel(
     float* __restrict__ partial, uint32_t* __restrict__ arrived, int64_t rows,
     uint32_t chunks, float* __restrict__ grad_b, float* __restrict__ grad_alpha) {
   constexpr int M = 2 * N + N * N;
-  constexpr int Q = (M + 3 + kFusedWaves - 1) / kFusedWaves;  // outputs per wave
+  constexpr int Q = (M + 3 + W - 1) / W;  // outputs per wave
   __shared__ uint32_t last;
-  __shared__ __align__(16) float tiles[kFusedWaves * Tile<N>::kFloats];
+  __shared__ __align__(16) float tiles[W * Tile<N>::kFloats];
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t c = blockIdx.x * kFusedWaves + wave;
+  const uint32_t c = blockIdx.x * W + wave;
   chunk_sums<N>(mix, pre, post, grad_pre, grad_post, grad_res, alpha, inv_c, grad_mix, partial,
                 rows, chunks, c, lane, c < chunks, tiles + wave * Tile<N>::kFloats);
   __syncthreads();
@@ -355,11 +352,12 @@ int64_t workspace_need(int64_t rows, int32_t n) {
 }
 
 // The one-launch form is used at n <= 4 up to this many chunks. Measured per
-// call (cold inputs, n = 4): one launch 5.0 / 5.4 / 6.7 / 8.8 us at 512 /
-// 2048 / 8192 / 16384 rows against 8.9-9.1 us for two; behind from 32768
+// call (cold inputs, n = 4): one launch 4.6 / 5.2 / 6.9 / 8.8 us at 512 /
+// 2048 / 8192 / 16384 rows against 9.0-9.2 us for two; behind from 32768
 // rows (13.6 vs 9.4 us: its last block sums every output alone). At n = 8
-// two launches are faster at every size measured (9.0 vs 12.2 us at 2048
-// rows: four 80-column waves on one CU load more slowly than one).
+// two launches are faster at every size measured (9.1 vs 10.5 us at 2048
+// rows with 2-wave blocks, 12.2 with 4: the last block sums all 83 outputs,
+// and 80-column waves sharing a CU load more slowly than one alone).
 constexpr int64_t kFusedMaxChunks = 256;
 
 struct Range {
@@ -447,14 +445,29 @@ void launch_partial(const CoeffArgs& a, hipStream_t s, hipEvent_t start) {
                         a.inv_c, a.grad_mix, a.partial, a.rows, a.chunks);
 }
 
-template <int N>
-void launch_fused(const CoeffArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
-  const uint32_t blocks = (a.chunks + kFusedWaves - 1) / kFusedWaves;
-  hipExtLaunchKernelGGL(coeff_fused_kernel<N>, dim3(blocks), dim3(64 * kFusedWaves), 0, s, start,
-                        stop, 0,
-                        a.mix, a.pre, a.post, a.grad_pre, a.grad_post, a.grad_res, a.alpha,
+// Waves per block of the one-launch form: 2 up to this many chunks, 4
+// above. Measured per call (cold inputs, n = 4): 2-wave blocks 4.5 / 4.9 /
+// 5.1 / 5.5 / 5.6 us at 512 / 1024 / 2048 / 3072 / 4096 rows against 5.0 /
+// 5.2 / 5.6 / 5.7 / 5.7 us with 4 (more CUs share the first stage); 4-wave
+// blocks 7.1 / 8.8 us at 8192 / 16384 rows against 7.3 / 10.0 us (the last
+// block's waves each sum fewer outputs). At n = 2 the same or better.
+constexpr uint32_t kTwoWaveMaxChunks = 64;
+
+template <int N, int W>
+void launch_fused_w(const CoeffArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+  const uint32_t blocks = (a.chunks + W - 1) / W;
+  hipExtLaunchKernelGGL(coeff_fused_kernel<N, W>, dim3(blocks), dim3(64 * W), 0, s, start, stop,
+                        0, a.mix, a.pre, a.post, a.grad_pre, a.grad_post, a.grad_res, a.alpha,
                         a.inv_c, a.grad_mix, a.partial, a.arrived, a.rows, a.chunks, a.grad_b,
                         a.grad_alpha);
+}
+
+template <int N>
+void launch_fused(const CoeffArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+  if (a.chunks <= kTwoWaveMaxChunks)
+    launch_fused_w<N, 2>(a, s, start, stop);
+  else
+    launch_fused_w<N, 4>(a, s, start, stop);
 }
 
 // Launches of one call: 1 = one launch (chunk sums + last-block reduction),

@@ -47,7 +47,7 @@ def _check(host, c, dev, what, **kw):
 
 @pytest.mark.parametrize("launches", [1, 2])
 @pytest.mark.parametrize("n", [2, 4, 8])
-@pytest.mark.parametrize("R", [1, 63, 64, 65, 300, 4161, 8257])
+@pytest.mark.parametrize("R", [1, 63, 64, 65, 300, 4096, 4097, 4161, 8257])
 def test_bit_exact_against_the_oracle(device, n, R, launches):
     say(f"coeff bwd n={n} R={R} launches={launches}")
     _check(make_coeff_inputs(R, n, seed=R + n), 2.0, device, f"n={n} R={R}", launches=launches)
