@@ -53,22 +53,23 @@ PEAK_HBM_GBPS = 8000.0            # MI355X HBM3E peak, 8 TB/s
 TRAFFIC_FILE = REPO / "profiles" / "hagg_bwd_T1024_H7168_traffic.md"
 
 
-def fwd_bytes(T: int, H: int) -> int:
+def fwd_bytes(T: int, H: int, n: int = HC) -> int:
     """Algorithmic bytes of one forward call: read residual (8H) and pre (16),
-    write out (2H), per token."""
-    return T * (10 * H + 16)
+    write out (2H), per token (at expansion n: 2nH + 4n read, 2H written)."""
+    return T * (2 * (n + 1) * H + 4 * n)
 
 
-def bwd_bytes(T: int, H: int) -> int:
+def bwd_bytes(T: int, H: int, n: int = HC) -> int:
     """Algorithmic bytes of one backward call: read residual (8H), grad_out
-    (2H), pre (16); write grad_residual (8H), grad_pre (16), per token."""
-    return T * (18 * H + 32)
+    (2H), pre (16); write grad_residual (8H), grad_pre (16), per token (at
+    expansion n: (4n + 2)H + 8n)."""
+    return T * ((4 * n + 2) * H + 8 * n)
 
 
-def bwd_acc_bytes(T: int, H: int) -> int:
+def bwd_acc_bytes(T: int, H: int, n: int = HC) -> int:
     """Accumulating backward: the plain backward's bytes plus reading the
-    stored grad_residual (8H) per token."""
-    return T * (26 * H + 32)
+    stored grad_residual (8H; 2nH at expansion n) per token."""
+    return T * ((6 * n + 2) * H + 8 * n)
 
 
 def _elf_sections(blob: bytes) -> dict[str, bytes]:
@@ -141,15 +142,15 @@ class BufferSet:
         from hyper_connection_residual_mhc_amd.workloads import to_device
         d = to_device(host, dev)
         self.residual, self.pre, self.grad_out = d["residual"], d["pre"], d["grad_out"]
-        T, _, H = self.residual.shape
+        T, hc, H = self.residual.shape
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-        self.grad_residual = torch.empty((T, HC, H), dtype=torch.bfloat16, device=dev)
-        self.grad_pre = torch.empty((T, HC), dtype=torch.float32, device=dev)
+        self.grad_residual = torch.empty((T, hc, H), dtype=torch.bfloat16, device=dev)
+        self.grad_pre = torch.empty((T, hc), dtype=torch.float32, device=dev)
 
 
-def make_sets(T: int, H: int, n: int, dev) -> list[BufferSet]:
+def make_sets(T: int, H: int, n: int, dev, hc: int = HC) -> list[BufferSet]:
     from hyper_connection_residual_mhc_amd.workloads import make_inputs
-    return [BufferSet(make_inputs(T, H, seed=s, grad=True), dev) for s in range(n)]
+    return [BufferSet(make_inputs(T, H, seed=s, grad=True, hc=hc), dev) for s in range(n)]
 
 
 def copy_probe(dev, nbytes: int = 1 << 28, reps: int = 3) -> None:
@@ -366,6 +367,8 @@ SWEEP_SHAPES = [  # (T, H): latency sweep, bandwidth shapes, backward shape
     (1, 4096), (8, 4096), (128, 4096), (1, 7168), (8, 7168), (128, 7168),
     (1024, 7168), (2048, 7168), (8192, 7168),
 ]
+# (T, H, n): the other expansion rates at the bandwidth shapes
+EXPANSION_SWEEP = [(1024, 7168, 2), (2048, 7168, 2), (1024, 7168, 8), (2048, 7168, 8)]
 
 
 def run_sweep(path: str, rounds: int = 7, warm: int = 10, timed: int = 100,
@@ -379,8 +382,10 @@ def run_sweep(path: str, rounds: int = 7, warm: int = 10, timed: int = 100,
     medians, GB/s from the median. At T >= 1024 a streaming probe with the
     kernel's read:write byte mix is timed the same way in each round, in a
     block of its own after the kernel's (the reference column). Then the
-    coefficient backward epilogue at COEFF_SWEEP. `part` limits the sweep to
-    "h_aggregate" or "coeff"."""
+    coefficient backward epilogue at COEFF_SWEEP, then forward, backward and
+    accumulating backward at the other expansion rates (EXPANSION_SWEEP,
+    through the *_n entry points, without probes). `part` limits the sweep
+    to "h_aggregate", "coeff" or "expansion"."""
     import statistics as st
     import torch
     from hyper_connection_residual_mhc_amd import _lib, ops
@@ -483,6 +488,48 @@ def run_sweep(path: str, rounds: int = 7, warm: int = 10, timed: int = 100,
                 f.write(json.dumps(rec) + "\n")
                 f.flush()
                 print(json.dumps(rec), file=sys.stderr, flush=True)
+        for T, H, n in (EXPANSION_SWEEP if part in ("all", "expansion") else []):
+            nsets = 8
+            sets = make_sets(T, H, nsets, dev, hc=n)
+            for direction in ("fwd", "bwd", "bwd_acc"):
+                if direction == "fwd":
+                    nbytes = fwd_bytes(T, H, n)
+
+                    def call(k, a, b):
+                        x = sets[k % nsets]
+                        return lib.mhc_h_aggregate_fwd_n(
+                            x.residual.data_ptr(), x.pre.data_ptr(), x.out.data_ptr(), T, n, H,
+                            sh, None, a, b)
+                else:
+                    acc = int(direction == "bwd_acc")
+                    nbytes = (bwd_acc_bytes if acc else bwd_bytes)(T, H, n)
+
+                    def call(k, a, b, acc=acc):
+                        x = sets[k % nsets]
+                        return lib.mhc_h_aggregate_bwd_n(
+                            x.residual.data_ptr(), x.pre.data_ptr(), x.grad_out.data_ptr(),
+                            x.grad_residual.data_ptr(), x.grad_pre.data_ptr(), T, n, H, acc, sh,
+                            None, a, b)
+                k_rounds = []
+                for _ in range(rounds):
+                    for k in range(warm):
+                        _lib.check(call(k, None, None))
+                    torch.cuda.synchronize()
+                    for k in range(timed):
+                        _lib.check(call(k, E[2 * k], E[2 * k + 1]))
+                    torch.cuda.synchronize()
+                    k_rounds.append([ev.elapsed_us(2 * k, 2 * k + 1) for k in range(timed)])
+                med, q, mean = summary(k_rounds)
+                rec = {"direction": direction, "T": T, "H": H, "n": n, "bytes": nbytes,
+                       "us_median": round(med, 3), "us_p20_p50_p80": q,
+                       "us_mean": round(mean, 3),
+                       "gbps": round(nbytes / med / 1e3, 1),
+                       "frac_of_8TBps": round(nbytes / med / 1e3 / PEAK_HBM_GBPS, 4)}
+                f.write(json.dumps(rec) + "\n")
+                f.flush()
+                print(json.dumps(rec), file=sys.stderr, flush=True)
+            del sets
+            torch.cuda.empty_cache()
     ev.close()
 
 
@@ -807,7 +854,8 @@ def main() -> int:
     ap.add_argument("--sweep", metavar="OUT_JSONL",
                     help="instead of the step benchmark, time each kernel per call at the "
                          "latency / bandwidth / backward shapes and write JSON lines")
-    ap.add_argument("--sweep-part", choices=("all", "h_aggregate", "coeff"), default="all",
+    ap.add_argument("--sweep-part", choices=("all", "h_aggregate", "coeff", "expansion"),
+                    default="all",
                     help="with --sweep: which operations to time")
     ap.add_argument("--counter-case", choices=sorted(COUNTER_CASES) + sorted(FWD_COUNTER_CASES),
                     help="instead of the step benchmark, run 64 backward (or forward) calls in "

@@ -29,6 +29,13 @@ def test_algorithmic_bytes_per_token():
     assert bench.fwd_bytes(T, H) == T * (10 * H + 16)
     assert bench.bwd_bytes(T, H) == T * (18 * H + 32)
     assert bench.bwd_acc_bytes(T, H) == T * (26 * H + 32)
+    # other expansion rates, counted from the buffers: n = 2 reads 2 x 2H of
+    # residual and 8 B of pre per token; n = 8 reads 8 x 2H and 32 B
+    assert bench.fwd_bytes(T, H, 2) == T * (2 * 2 * H + 8 + 2 * H)
+    assert bench.fwd_bytes(T, H, 8) == T * (8 * 2 * H + 32 + 2 * H)
+    assert bench.bwd_bytes(T, H, 2) == T * (2 * 2 * H + 2 * H + 8 + 2 * 2 * H + 8)
+    assert bench.bwd_bytes(T, H, 8) == T * (8 * 2 * H + 2 * H + 32 + 8 * 2 * H + 32)
+    assert bench.bwd_acc_bytes(T, H, 8) == bench.bwd_bytes(T, H, 8) + T * 8 * 2 * H
 
 
 def test_probe_record_fractions():
