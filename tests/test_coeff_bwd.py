@@ -138,13 +138,14 @@ def test_repeatable_and_independent_of_workspace_contents(device):
         assert int(ws[:4].view(torch.int32).item()) == 0
 
 
-def test_one_launch_form_sees_every_chunk_sum(device):
-    """100 one-launch calls at 128 chunks (32 blocks arriving), each after
-    the chunk-sum area was refilled with NaN patterns and each on fresh
-    inputs: the last block must read every other block's sums, never a
-    stale value (which would show as a NaN or a wrong sum)."""
-    say("coeff bwd one-launch visibility")
-    R = 8192
+@pytest.mark.parametrize("R", [4096, 8192])
+def test_one_launch_form_sees_every_chunk_sum(device, R):
+    """100 one-launch calls at 64 chunks (32 two-wave blocks arriving) and at
+    128 chunks (32 four-wave blocks), each after the chunk-sum area was
+    refilled with NaN patterns and each on fresh inputs: the last block must
+    read every other block's sums, never a stale value (which would show as
+    a NaN or a wrong sum)."""
+    say(f"coeff bwd one-launch visibility R={R}")
     ws = torch.zeros(coeff.mhc_coeff_bwd_workspace_bytes(R, 4), dtype=torch.uint8,
                      device=device)
     keys = KEYS
