@@ -342,23 +342,30 @@ def mhc_h_aggregate_validate_bwd(residual, pre, grad_out, grad_residual, grad_pr
 # ---------------------------------------------------------------------------
 
 def h_aggregate(residual: torch.Tensor, pre: torch.Tensor) -> torch.Tensor:
-    """Forward with a freshly allocated output (no autograd)."""
-    T, H = _fwd_shapes(residual)
+    """Forward with a freshly allocated output (no autograd); residual
+    [T, n, H] with n in {2, 4, 8}."""
+    T, n, H = _shapes_n(residual)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=residual.device)
-    return mhc_h_aggregate_fwd(residual, pre, out)
+    if n == HC:
+        return mhc_h_aggregate_fwd(residual, pre, out)
+    return mhc_h_aggregate_fwd_n(residual, pre, out)
 
 
 def h_aggregate_backward(residual: torch.Tensor, pre: torch.Tensor, grad_out: torch.Tensor
                          ) -> tuple[torch.Tensor, torch.Tensor]:
-    """Backward with freshly allocated gradients."""
-    T, H = _fwd_shapes(residual)
-    grad_residual = torch.empty((T, HC, H), dtype=torch.bfloat16, device=residual.device)
-    grad_pre = torch.empty((T, HC), dtype=torch.float32, device=residual.device)
-    return mhc_h_aggregate_bwd(residual, pre, grad_out, grad_residual, grad_pre)
+    """Backward with freshly allocated gradients; residual [T, n, H] with n
+    in {2, 4, 8}."""
+    T, n, H = _shapes_n(residual)
+    grad_residual = torch.empty((T, n, H), dtype=torch.bfloat16, device=residual.device)
+    grad_pre = torch.empty((T, n), dtype=torch.float32, device=residual.device)
+    if n == HC:
+        return mhc_h_aggregate_bwd(residual, pre, grad_out, grad_residual, grad_pre)
+    return mhc_h_aggregate_bwd_n(residual, pre, grad_out, grad_residual, grad_pre)
 
 
 class HAggregate(torch.autograd.Function):
-    """Autograd wrapper: forward and backward both run the gfx950 kernels."""
+    """Autograd wrapper: forward and backward both run the gfx950 kernels
+    (any supported expansion rate)."""
 
     @staticmethod
     def forward(ctx, residual: torch.Tensor, pre: torch.Tensor) -> torch.Tensor:

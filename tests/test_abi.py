@@ -283,8 +283,10 @@ def test_binding_rejects_host_tensors_without_calling_the_library(lib):
     pre = torch.zeros((2, 4), dtype=torch.float32)
     with pytest.raises(TypeError, match="must be on a GPU"):
         ops.h_aggregate(res, pre)
-    with pytest.raises(ValueError, match=r"\[T, 4, H\]"):
+    with pytest.raises(ValueError, match=r"\[T, n, H\] with n in \{2, 4, 8\}"):
         ops.h_aggregate(torch.zeros((2, 3, 8), dtype=torch.bfloat16), pre)
+    with pytest.raises(ValueError, match=r"\[T, 4, H\]"):
+        ops.mhc_h_aggregate_fwd(torch.zeros((2, 2, 8), dtype=torch.bfloat16), pre, res)
 
 
 def test_compute_call_with_invalid_args_returns_before_any_hip_call(lib):

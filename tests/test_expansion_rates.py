@@ -161,3 +161,29 @@ def test_n_batch_split(device, n):
     want_gr, want_gp = O.h_aggregate_bwd(host["residual"], host["pre"], host["grad_out"])
     assert_bytes_equal(bf16_tensor_to_bits(gr), want_gr, "grad_residual split")
     assert_bytes_equal(gp.cpu().numpy(), want_gp, "grad_pre split")
+
+
+@pytest.mark.parametrize("n", [2, 8])
+def test_autograd_and_allocating_calls_at_n(device, n):
+    """h_aggregate / h_aggregate_backward / HAggregate at expansion n: the
+    same bytes as the oracle."""
+    say(f"autograd n={n}")
+    T, H = 16, 4096
+    host = make_inputs(T, H, seed=40 + n, hc=n, grad=True)
+    d = to_device(host, device)
+    want_out = O.h_aggregate_fwd_n(host["residual"], host["pre"])
+    want_gr, want_gp = O.h_aggregate_bwd(host["residual"], host["pre"], host["grad_out"])
+    assert_bytes_equal(bf16_tensor_to_bits(ops.h_aggregate(d["residual"], d["pre"])), want_out,
+                       f"h_aggregate n={n}")
+    gr, gp = ops.h_aggregate_backward(d["residual"], d["pre"], d["grad_out"])
+    torch.cuda.synchronize()
+    assert_bytes_equal(bf16_tensor_to_bits(gr), want_gr, f"h_aggregate_backward n={n} grad_residual")
+    assert_bytes_equal(gp.cpu().numpy(), want_gp, f"h_aggregate_backward n={n} grad_pre")
+    res = d["residual"].clone().requires_grad_(True)
+    pre = d["pre"].clone().requires_grad_(True)
+    out = ops.h_aggregate_autograd(res, pre)
+    out.backward(d["grad_out"])
+    torch.cuda.synchronize()
+    assert_bytes_equal(bf16_tensor_to_bits(out), want_out, f"autograd n={n} out")
+    assert_bytes_equal(bf16_tensor_to_bits(res.grad), want_gr, f"autograd n={n} grad_residual")
+    assert_bytes_equal(pre.grad.cpu().numpy(), want_gp, f"autograd n={n} grad_pre")
