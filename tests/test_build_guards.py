@@ -12,6 +12,10 @@ own gfx950 machine code (compiled here; no GPU needed).
   overwrites its data registers (gfx950 reads such data over several cycles;
   an immediate overwrite was measured to corrupt the last lanes' data);
 * no scalar memory writes, and no division in the coefficient kernels;
+* no __builtin_bit_cast of a vector element in the kernel sources (this
+  toolchain turned `__builtin_bit_cast(float, v[e])` on a 4-wide vector into
+  a copy of element 0 and shrank the vector load to one dword; the
+  kernels copy an element into a scalar first);
 * the product path never imports the oracle.
 
 Both library sources are checked (the h_aggregate kernels and the
@@ -200,3 +204,21 @@ def test_product_path_does_not_touch_the_oracle():
         text = f.read_text()
         assert not re.search(r"^\s*(from|import)\s+oracle\b", text, flags=re.M), f
         assert "oracle/" not in text, f
+
+
+BIT_CAST_OF_ELEMENT = re.compile(r"__builtin_bit_cast\(\s*[\w:]+\s*,\s*[\w.]+\s*\[")
+
+
+def test_no_bit_cast_of_a_vector_element():
+    csrc = Path(_build.PKG_DIR) / "csrc"
+    for f in sorted(list(csrc.glob("*.hip")) + list(csrc.glob("*.h"))):
+        hits = [line for line in f.read_text().splitlines() if BIT_CAST_OF_ELEMENT.search(line)]
+        assert not hits, (f.name, hits)
+
+
+def test_bit_cast_scan_detects_the_pattern():
+    assert BIT_CAST_OF_ELEMENT.search("dst[e] = __builtin_bit_cast(float, v[e]);")
+    assert BIT_CAST_OF_ELEMENT.search("x = __builtin_bit_cast(float, a.b[1]);")
+    assert not BIT_CAST_OF_ELEMENT.search("x = __builtin_bit_cast(float, u);")
+    assert not BIT_CAST_OF_ELEMENT.search(
+        "return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, o, 0, 0));")
