@@ -66,6 +66,19 @@ def test_hand_case_one_row_n2():
     assert ga.tolist() == [1.0, 0.0, 70.0]
 
 
+def test_group_sums_run_over_columns_in_ascending_order():
+    """e[r, k] adds d * mix over the group's columns in ascending order from
+    +0.0. One row, n = 2, only the residual group non-zero, mix = 1 and
+    grad_res = (1, -1, 2^-25, 0): ascending, ((1 + (-1)) + 2^-25) = 2^-25;
+    descending, 2^-25 + (-1) ties to -1 (even), and -1 + 1 = 0. With one row
+    the row sum of e is e itself, so grad_alpha[2] = 2^-25."""
+    f = lambda *v: np.array([v], dtype=np.float32)
+    tiny = 2.0 ** -25
+    _, _, ga = cb.coeff_bwd(f(0, 0, 0, 0, 1, 1, 1, 1), f(0.5, 0.5), f(1.0, 1.0), f(0, 0), f(0, 0),
+                            f(1.0, -1.0, tiny, 0.0), np.array([1, 1, 1], np.float32), 2.0, 2)
+    assert ga.tolist() == [0.0, 0.0, tiny]
+
+
 # ---------------------------------------------------------------------------
 # The fixed row order: hand-derived discriminators
 # ---------------------------------------------------------------------------

@@ -674,6 +674,25 @@ def test_tree_hand_cases_pin_each_level():
     assert _tree_case(8 * 193, {0: 1.0, 8 * 64: E, 8 * 192: E}) == one_plus_2e
 
 
+def test_tree_hand_cases_pin_lane_count_and_pair_partners():
+    """Two more hand-derived cases, each failing for one plausible variant
+    of the order (1 + E ties back to 1; 1 + (-1) = 0 exactly):
+
+    * 256 accumulator lanes, not 128: q = 1, -1, E at groups 0, 128, 256.
+      Groups 0 and 256 share lane 0 (1 + E = 1) and group 128 sits in lane
+      128, the first lane of wave 2, so the block stage gives
+      (1 + (-1)) + 0 = 0. With 128 lanes, lane 0 would chain
+      ((1 + (-1)) + E) = E.
+    * the wave tree pairs lane j with lane j + off, not its mirror
+      2 off - 1 - j: q = 1, -1, E in lanes 0, 32, 63. At off = 32, lane 0
+      becomes 1 + (-1) = 0 and lane 31 takes E, which reaches lane 0 at
+      off = 1: the result is E. Mirrored pairs would give lane 0 = 1 + E = 1,
+      lane 31 = -1, and then 0.
+    """
+    assert _tree_case(8 * 257, {0: 1.0, 8 * 128: -1.0, 8 * 256: E}) == np.float32(0.0)
+    assert _tree_case(8 * 64, {0: 1.0, 8 * 32: -1.0, 8 * 63: E}) == np.float32(E)
+
+
 def _sequential(q):
     acc = np.zeros(q.shape[:-1], np.float32)
     for h in range(q.shape[-1]):
