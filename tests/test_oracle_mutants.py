@@ -107,6 +107,12 @@ MUTANTS = [
      "grad_mix without alpha"),
     ("coeff_bwd", "        for j in range(m):", "        for j in reversed(range(m)):",
      "descending columns in the group sums"),
+    ("coeff_bwd", "    grad_b = row_sum(d)", "    grad_b = row_sum(grad_mix)",
+     "bias gradient scaled by alpha"),
+    ("coeff_bwd", "d_post = np.multiply(grad_post, np.multiply(post,",
+     "d_post = np.multiply(grad_post, np.multiply(pre,", "post derivative from the pre gate"),
+    ("coeff_bwd", "np.concatenate([d_pre, d_post, grad_res], axis=1)",
+     "np.concatenate([d_post, d_pre, grad_res], axis=1)", "pre and post columns swapped"),
 ]
 
 
