@@ -371,6 +371,55 @@ SWEEP_SHAPES = [  # (T, H): latency sweep, bandwidth shapes, backward shape
 EXPANSION_SWEEP = [(1024, 7168, 2), (2048, 7168, 2), (1024, 7168, 8), (2048, 7168, 8)]
 
 
+class SweepTimer:
+    """Per-call timing of the sweep: every timed launch carries its own
+    dispatch events. `rounds` rounds; in each, every timed function runs in
+    a block of its own: `warm` untimed launches, then `timed` timed ones,
+    back to back."""
+
+    def __init__(self, rounds: int, warm: int, timed: int):
+        self.rounds, self.warm, self.timed = rounds, warm, timed
+        self.ev = HipEvents(2 * timed)
+
+    def blocks(self, fns, check) -> list[list[list[float]]]:
+        """For each fn(k, start_event, stop_event) -> status, its per-round
+        lists of microseconds. Within a round the functions run one after
+        another, so neither inherits the other's write-back."""
+        import torch
+        E = self.ev.handles
+        out = [[] for _ in fns]
+        for _ in range(self.rounds):
+            for fn, per_round in zip(fns, out):
+                for k in range(self.warm):
+                    check(fn(k, None, None))
+                torch.cuda.synchronize()
+                for k in range(self.timed):
+                    check(fn(k, E[2 * k], E[2 * k + 1]))
+                torch.cuda.synchronize()
+                per_round.append([self.ev.elapsed_us(2 * k, 2 * k + 1) for k in range(self.timed)])
+        return out
+
+    @staticmethod
+    def summary(per_round: list[list[float]]) -> tuple[float, list[float], float]:
+        """Median of the round medians, [p20, p50, p80] over the round
+        medians, and the mean of every launch."""
+        import statistics as st
+        med = [st.median(r) for r in per_round]
+        q = st.quantiles(med, n=10, method="inclusive")
+        mean = st.fmean([x for r in per_round for x in r])
+        return st.median(med), [round(q[1], 3), round(st.median(med), 3), round(q[7], 3)], mean
+
+    @classmethod
+    def fields(cls, nbytes: int, per_round: list[list[float]]) -> dict:
+        med, q, mean = cls.summary(per_round)
+        return {"bytes": nbytes, "us_median": round(med, 3), "us_p20_p50_p80": q,
+                "us_mean": round(mean, 3), "gbps": round(nbytes / med / 1e3, 1),
+                "frac_of_8TBps": round(nbytes / med / 1e3 / PEAK_HBM_GBPS, 4)}
+
+    def close(self) -> None:
+        self.ev.close()
+
+
 def run_sweep(path: str, rounds: int = 7, warm: int = 10, timed: int = 100,
               part: str = "all") -> None:
     """Per-call forward and backward times at SWEEP_SHAPES, one JSON line per
@@ -386,7 +435,6 @@ def run_sweep(path: str, rounds: int = 7, warm: int = 10, timed: int = 100,
     accumulating backward at the other expansion rates (EXPANSION_SWEEP,
     through the *_n entry points, without probes). `part` limits the sweep
     to "h_aggregate", "coeff" or "expansion"."""
-    import statistics as st
     import torch
     from hyper_connection_residual_mhc_amd import _lib, ops
 
@@ -394,14 +442,12 @@ def run_sweep(path: str, rounds: int = 7, warm: int = 10, timed: int = 100,
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sh = int(torch.cuda.current_stream(dev).cuda_stream)
-    ev = HipEvents(2 * timed)
-    E = ev.handles
+    tm = SweepTimer(rounds, warm, timed)
 
-    def summary(per_round: list[list[float]]) -> tuple[float, list[float], float]:
-        med = [st.median(r) for r in per_round]
-        q = st.quantiles(med, n=10, method="inclusive")
-        mean = st.fmean([x for r in per_round for x in r])
-        return st.median(med), [round(q[1], 3), round(st.median(med), 3), round(q[7], 3)], mean
+    def emit(f, rec: dict) -> None:
+        f.write(json.dumps(rec) + "\n")
+        f.flush()
+        print(json.dumps(rec), file=sys.stderr, flush=True)
 
     with open(path, "w") as f:
         for T, H in (SWEEP_SHAPES if part in ("all", "h_aggregate") else []):
@@ -443,51 +489,30 @@ def run_sweep(path: str, rounds: int = 7, warm: int = 10, timed: int = 100,
                             a, b)
                 probe = (ProbeBuffers(nbytes, PROBE_MIX[direction], nsets, dev)
                          if T >= 1024 else None)
-                k_rounds, p_rounds = [], []
-                runs = [(call, k_rounds)]
+                fns = [call]
                 if probe:
-                    runs.append((lambda k, a, b: probe.call(lib, k, sh, a, b), p_rounds))
-                for _ in range(rounds):
-                    # The kernel's launches, then the probe's: each block runs
-                    # back to back after its own warm-up, so neither inherits
-                    # the other's write-back.
-                    for fn, out in runs:
-                        for k in range(warm):
-                            _lib.check(fn(k, None, None))
-                        torch.cuda.synchronize()
-                        for k in range(timed):
-                            _lib.check(fn(k, E[2 * k], E[2 * k + 1]))
-                        torch.cuda.synchronize()
-                        out.append([ev.elapsed_us(2 * k, 2 * k + 1) for k in range(timed)])
-                med, q, mean = summary(k_rounds)
-                rec = {"direction": direction, "T": T, "H": H, "bytes": nbytes,
-                       "us_median": round(med, 3), "us_p20_p50_p80": q,
-                       "us_mean": round(mean, 3),
-                       "gbps": round(nbytes / med / 1e3, 1),
-                       "frac_of_8TBps": round(nbytes / med / 1e3 / PEAK_HBM_GBPS, 4),
-                       "plan": plan}
+                    fns.append(lambda k, a, b: probe.call(lib, k, sh, a, b))
+                timings = tm.blocks(fns, _lib.check)
+                rec = {"direction": direction, "T": T, "H": H,
+                       **SweepTimer.fields(nbytes, timings[0]), "plan": plan}
                 if probe:
-                    pmed, pq, _ = summary(p_rounds)
+                    pmed, _, _ = SweepTimer.summary(timings[1])
                     pg = probe.bytes / pmed / 1e3
                     rec["probe"] = {"mix": list(PROBE_MIX[direction]), "bytes": probe.bytes,
                                     "us_median": round(pmed, 3), "gbps": round(pg, 1),
                                     "frac_of_probe": round(rec["gbps"] / pg, 4)}
                     del probe
-                f.write(json.dumps(rec) + "\n")
-                f.flush()
-                print(json.dumps(rec), file=sys.stderr, flush=True)
+                emit(f, rec)
             del sets
             torch.cuda.empty_cache()
         for R, n in (COEFF_SWEEP if part in ("all", "coeff") else []):
             # the policy's form, then the two-launch form for comparison; the
             # oracle timed on the host beside the policy's form
             for launches in (0, 2):
-                rec = time_coeff(R, n, dev, sh, ev, rounds, warm, timed, summary, launches)
+                rec = time_coeff(R, n, dev, sh, tm, launches)
                 if launches == 0:
                     rec["cpu_baseline"] = run_coeff_cpu_baseline(R, n)
-                f.write(json.dumps(rec) + "\n")
-                f.flush()
-                print(json.dumps(rec), file=sys.stderr, flush=True)
+                emit(f, rec)
         for T, H, n in (EXPANSION_SWEEP if part in ("all", "expansion") else []):
             nsets = 8
             sets = make_sets(T, H, nsets, dev, hc=n)
@@ -510,27 +535,12 @@ def run_sweep(path: str, rounds: int = 7, warm: int = 10, timed: int = 100,
                             x.residual.data_ptr(), x.pre.data_ptr(), x.grad_out.data_ptr(),
                             x.grad_residual.data_ptr(), x.grad_pre.data_ptr(), T, n, H, acc, sh,
                             None, a, b)
-                k_rounds = []
-                for _ in range(rounds):
-                    for k in range(warm):
-                        _lib.check(call(k, None, None))
-                    torch.cuda.synchronize()
-                    for k in range(timed):
-                        _lib.check(call(k, E[2 * k], E[2 * k + 1]))
-                    torch.cuda.synchronize()
-                    k_rounds.append([ev.elapsed_us(2 * k, 2 * k + 1) for k in range(timed)])
-                med, q, mean = summary(k_rounds)
-                rec = {"direction": direction, "T": T, "H": H, "n": n, "bytes": nbytes,
-                       "us_median": round(med, 3), "us_p20_p50_p80": q,
-                       "us_mean": round(mean, 3),
-                       "gbps": round(nbytes / med / 1e3, 1),
-                       "frac_of_8TBps": round(nbytes / med / 1e3 / PEAK_HBM_GBPS, 4)}
-                f.write(json.dumps(rec) + "\n")
-                f.flush()
-                print(json.dumps(rec), file=sys.stderr, flush=True)
+                timings = tm.blocks([call], _lib.check)
+                emit(f, {"direction": direction, "T": T, "H": H, "n": n,
+                         **SweepTimer.fields(nbytes, timings[0])})
             del sets
             torch.cuda.empty_cache()
-    ev.close()
+    tm.close()
 
 
 # Launch shapes of the backward whose HBM traffic the counter runs compare
@@ -637,7 +647,7 @@ def run_coeff_cpu_baseline(R: int, n: int, min_seconds: float = 1.0) -> dict:
                       f"untimed call ({dt:.2f} s)"}
 
 
-def time_coeff(R, n, dev, sh, ev, rounds, warm, timed, summary, launches=0) -> dict:
+def time_coeff(R, n, dev, sh, tm: SweepTimer, launches=0) -> dict:
     """Per-call time of mhc_coeff_bwd (both of its launches, between the
     first dispatch's start and the last one's end). Input sets rotate over
     more than the 256 MB Infinity Cache, so every call starts cold."""
@@ -659,7 +669,6 @@ def time_coeff(R, n, dev, sh, ev, rounds, warm, timed, summary, launches=0) -> d
         x["grad_alpha"] = torch.empty((3,), dtype=torch.float32, device=dev)
         x["ws"] = torch.zeros((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
         sets.append(x)
-    E = ev.handles
 
     def call(k, a, b):
         x = sets[k % nsets]
@@ -667,22 +676,11 @@ def time_coeff(R, n, dev, sh, ev, rounds, warm, timed, summary, launches=0) -> d
                                   x["grad_mix"].data_ptr(), x["grad_b"].data_ptr(),
                                   x["grad_alpha"].data_ptr(), x["ws"].data_ptr(), ws_bytes, R, n,
                                   launches, sh, a, b)
-    per_round = []
-    for _ in range(rounds):
-        for k in range(warm):
-            _lib.check_coeff(call(k, None, None))
-        torch.cuda.synchronize()
-        for k in range(timed):
-            _lib.check_coeff(call(k, E[2 * k], E[2 * k + 1]))
-        torch.cuda.synchronize()
-        per_round.append([ev.elapsed_us(2 * k, 2 * k + 1) for k in range(timed)])
-    med, q, mean = summary(per_round)
+    timings = tm.blocks([call], _lib.check_coeff)
     del sets, src
     torch.cuda.empty_cache()
-    return {"op": "coeff_bwd", "rows": R, "n": n, "bytes": per_set, "sets": nsets,
-            "us_median": round(med, 3), "us_p20_p50_p80": q, "us_mean": round(mean, 3),
-            "gbps": round(per_set / med / 1e3, 1),
-            "frac_of_8TBps": round(per_set / med / 1e3 / PEAK_HBM_GBPS, 4),
+    return {"op": "coeff_bwd", "rows": R, "n": n, "sets": nsets,
+            **SweepTimer.fields(per_set, timings[0]),
             "launches": clib.mhc_coeff_bwd_plan(R, n, launches), "chunks": -(-R // 64)}
 
 
