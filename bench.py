@@ -222,8 +222,13 @@ class HipEvents:
         self.handles = []
 
 
-def run_gpu(T: int, H: int, steps: int, warmup: int, nsets: int, probe: bool,
+def run_gpu(T: int, H: int, steps: int, warmup: int, nsets: int, copy_calibration: bool,
             sample_every: int) -> dict:
+    """The timed forward + backward steps on nsets rotating cold buffer sets
+    (per-kernel dispatch events on every `sample_every`-th step), then the
+    back-to-back reference runs of each kernel and of the stream probe with
+    its byte mix. copy_calibration: first run the plain device copy whose
+    counter readings calibrate the traffic figures."""
     import torch
     from hyper_connection_residual_mhc_amd import _build, _lib, ops
 
@@ -247,7 +252,7 @@ def run_gpu(T: int, H: int, steps: int, warmup: int, nsets: int, probe: bool,
     fwd, bwd = lib.mhc_h_aggregate_fwd, lib.mhc_h_aggregate_bwd
     fwd_t, bwd_t = lib.mhc_h_aggregate_fwd_timed, lib.mhc_h_aggregate_bwd_timed
 
-    if probe:
+    if copy_calibration:
         copy_probe(dev)
 
     # Every `sample_every`-th step goes through the timed entry points, which
@@ -298,18 +303,10 @@ def run_gpu(T: int, H: int, steps: int, warmup: int, nsets: int, probe: bool,
     # buffers, every launch timed by its own dispatch events. Outside the
     # timed steps.
     probe = ProbeBuffers(bwd_bytes(T, H), PROBE_MIX["bwd"], nsets, dev)
-    n_ceil = 200
-    cev = HipEvents(2 * n_ceil)
-    C = cev.handles
+    ref = SweepTimer(rounds=1, warm=10, timed=200)
 
     def back_to_back(fn) -> list[float]:
-        for k in range(10):
-            _lib.check(fn(k, None, None))
-        torch.cuda.synchronize()
-        for k in range(n_ceil):
-            _lib.check(fn(k, C[2 * k], C[2 * k + 1]))
-        torch.cuda.synchronize()
-        return [cev.elapsed_us(2 * k, 2 * k + 1) for k in range(n_ceil)]
+        return ref.blocks([fn], _lib.check)[0][0]
 
     ceil_kernel_us = back_to_back(lambda k, a, b: bwd_t(*bargs[k % nsets], None, a, b))
     ceil_probe_us = back_to_back(lambda k, a, b: probe.call(lib, k, sh, a, b))
@@ -321,7 +318,7 @@ def run_gpu(T: int, H: int, steps: int, warmup: int, nsets: int, probe: bool,
     fwd_probe_us = back_to_back(lambda k, a, b: fprobe.call(lib, k, sh, a, b))
     fprobe_bytes = fprobe.bytes
     del fprobe
-    cev.close()
+    ref.close()
     return {
         "probe": {"kernel_us": ceil_kernel_us, "probe_us": ceil_probe_us,
                     "probe_bytes": probe_bytes},
