@@ -117,15 +117,24 @@ def device_code_sha256(lib_path: Path | None = None) -> str | None:
     return None
 
 
-def recorded_traffic() -> int | None:
+def recorded_traffic(T: int, H: int, kernel: str, text: str | None = None) -> int | None:
     """HBM bytes per backward launch from the committed counter summary, or
-    None when there is none or the kernels changed since it was taken."""
-    if not TRAFFIC_FILE.exists():
-        return None
-    text = TRAFFIC_FILE.read_text()
+    None when there is none, when it covers another kernel or shape than the
+    one timed (its title names both), or when the kernels changed since it
+    was taken (device-code digest)."""
+    if text is None:
+        if not TRAFFIC_FILE.exists():
+            return None
+        text = TRAFFIC_FILE.read_text()
+    title = text.splitlines()[0] if text else ""
+    m_shape = re.search(r"\bT=(\d+), H=(\d+)\b", title)
     m_sha = re.search(r"device_code_sha256:\s*([0-9a-f]{64})", text)
     m_val = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
-    if not (m_sha and m_val) or m_sha.group(1) != device_code_sha256():
+    if not (m_shape and m_sha and m_val) or kernel not in title:
+        return None
+    if (int(m_shape.group(1)), int(m_shape.group(2))) != (T, H):
+        return None
+    if m_sha.group(1) != device_code_sha256():
         return None
     return int(m_val.group(1))
 
@@ -902,6 +911,8 @@ def main() -> int:
     fwd_avg = statistics.fmean(g["fwd_us"])
     bwd_avg = statistics.fmean(g["bwd_us"])
     achieved = bwd_bytes(T, H) / (bwd_avg * 1e-6) / 1e9
+    bwd_kernel = ("hagg_bwd_rows_kernel" if g["bwd_plan"].get("layout") == 2 else
+                  "hagg_bwd_kernel")
 
     line = {
         "metric": METRIC,
@@ -943,10 +954,9 @@ def main() -> int:
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
-            "traffic": recorded_traffic(),
-            "kernel": ("hagg_bwd_rows_kernel (backward, row layout)"
-                       if g["bwd_plan"].get("layout") == 2 else
-                       "hagg_bwd_kernel (backward, split layout)"),
+            "traffic": recorded_traffic(T, H, bwd_kernel),
+            "kernel": bwd_kernel + (" (backward, row layout)" if bwd_kernel == "hagg_bwd_rows_kernel"
+                                    else " (backward, split layout)"),
         },
         "stream_probe": probe_record(bwd_bytes(T, H), g["probe"]),
         "fwd_stream_probe": probe_record(fwd_bytes(T, H), g["fwd_probe"], "fwd"),

@@ -68,10 +68,17 @@ def test_summaries_parse_rocprof_csv(tmp_path, capsys):
 
 
 def test_recorded_traffic_is_tied_to_the_kernel_source():
-    """The profile's traffic figure is used only while the kernel source it
-    was measured on is unchanged (else null)."""
-    value = bench.recorded_traffic()
+    """The profile's traffic figure is used only for the kernel and shape it
+    was measured on, and only while that kernel's code is unchanged (else
+    null)."""
+    value = bench.recorded_traffic(1024, 7168, "hagg_bwd_rows_kernel")
     assert value is None or value > 0
+    assert bench.recorded_traffic(512, 7168, "hagg_bwd_rows_kernel") is None
+    assert bench.recorded_traffic(1024, 4096, "hagg_bwd_rows_kernel") is None
+    assert bench.recorded_traffic(1024, 7168, "hagg_bwd_kernel (split") is None
+    fake = ("# HBM traffic - hagg_bwd_rows_kernel, T=1024, H=7168\n"
+            "traffic_bytes_per_launch: 123\ndevice_code_sha256: " + "0" * 64 + "\n")
+    assert bench.recorded_traffic(1024, 7168, "hagg_bwd_rows_kernel", fake) is None  # digest
 
 
 def test_all_core_baseline_record():
