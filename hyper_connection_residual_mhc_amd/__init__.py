@@ -2,9 +2,10 @@
 hyper-connection residual stream and its backward, as hand-written HIP
 kernels behind a C ABI (include/mhc_h_aggregate.h).
 
-The torch-facing names live in `hyper_connection_residual_mhc_amd.ops`; they
-are re-exported here on first access, which loads the shared library (and
-raises ImportError if it has not been built).
+The torch-facing names live in `hyper_connection_residual_mhc_amd.ops` (and
+`.coeff` for the coefficient backward epilogue); they are re-exported here
+on first access. Calling them loads the shared libraries (ImportError if
+they have not been built).
 """
 
 from __future__ import annotations
@@ -17,13 +18,21 @@ _OPS_NAMES = (
     "mhc_h_aggregate_plan_fwd", "mhc_h_aggregate_plan_bwd",
     "mhc_h_aggregate_validate_fwd", "mhc_h_aggregate_validate_bwd",
     "h_aggregate", "h_aggregate_backward", "HAggregate", "h_aggregate_autograd",
+    "mhc_pre_h_aggregate",
+)
+_COEFF_NAMES = (
+    "mhc_coeff_bwd", "mhc_coeff_bwd_workspace_bytes", "mhc_coeff_bwd_plan",
+    "mhc_coeff_bwd_validate", "coeff_columns",
 )
 
-__all__ = list(_OPS_NAMES)
+__all__ = list(_OPS_NAMES) + list(_COEFF_NAMES)
 
 
 def __getattr__(name: str):
     if name in _OPS_NAMES:
         from . import ops
         return getattr(ops, name)
+    if name in _COEFF_NAMES:
+        from . import coeff
+        return getattr(coeff, name)
     raise AttributeError(name)

@@ -351,6 +351,14 @@ def h_aggregate(residual: torch.Tensor, pre: torch.Tensor) -> torch.Tensor:
     return mhc_h_aggregate_fwd_n(residual, pre, out)
 
 
+def mhc_pre_h_aggregate(residual: torch.Tensor, pre: torch.Tensor) -> torch.Tensor:
+    """The forward under the entry-point name the page's tests call (page
+    "Add batch-invariant h_aggregate kernel", section Correctness): a
+    freshly allocated out[T, H] bf16 from residual[T, n, H] bf16 and
+    pre[T, n] fp32. Same as h_aggregate."""
+    return h_aggregate(residual, pre)
+
+
 def h_aggregate_backward(residual: torch.Tensor, pre: torch.Tensor, grad_out: torch.Tensor
                          ) -> tuple[torch.Tensor, torch.Tensor]:
     """Backward with freshly allocated gradients; residual [T, n, H] with n

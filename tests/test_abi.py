@@ -278,6 +278,17 @@ def test_stream_probe_rejects_bad_arguments_before_any_hip_call(lib):
     assert probe(0, 0, 0, 0, 9, 4, None, None, None) == MHC_SUCCESS
 
 
+def test_package_exports_every_binding_name():
+    import hyper_connection_residual_mhc_amd as pkg
+    from hyper_connection_residual_mhc_amd import coeff
+    for name in pkg.__all__:
+        got = getattr(pkg, name)
+        assert got is getattr(ops, name, None) or got is getattr(coeff, name, None), name
+    assert pkg.mhc_pre_h_aggregate is ops.mhc_pre_h_aggregate
+    with pytest.raises(AttributeError):
+        getattr(pkg, "no_such_name")
+
+
 def test_binding_rejects_host_tensors_without_calling_the_library(lib):
     res = torch.zeros((2, 4, 8), dtype=torch.bfloat16)
     pre = torch.zeros((2, 4), dtype=torch.float32)

@@ -153,3 +153,13 @@ def test_forward_matches_torch_reference_within_page_tolerance(device):
     out = ops.h_aggregate(d["residual"], d["pre"]).float()
     ref = (d["pre"][:, :, None] * d["residual"].float()).sum(dim=1).to(torch.bfloat16).float()
     torch.testing.assert_close(out, ref, atol=5e-2, rtol=1e-2)
+
+
+def test_page_entry_point_name_runs_the_kernel(device):
+    """mhc_pre_h_aggregate (the name the page's tests call) gives the
+    oracle's bytes, at the page's correctness shape T=129, H=4096."""
+    say("mhc_pre_h_aggregate")
+    host = make_inputs(129, 4096, seed=3)
+    d = to_device(host, device)
+    got = bf16_tensor_to_bits(ops.mhc_pre_h_aggregate(d["residual"], d["pre"]))
+    assert_bytes_equal(got, O.h_aggregate_fwd(host["residual"], host["pre"]), "entry point")
