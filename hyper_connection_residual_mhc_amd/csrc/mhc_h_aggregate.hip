@@ -326,12 +326,15 @@ __device__ __forceinline__ void bwd_consume(BwdSlots<V, U, S, ACC>& sl, int u, u
 // At most 128 VGPRs (4 waves per SIMD), so that 4 blocks fit on a CU: the
 // policy uses this layout for batches below 544 rows (136 tokens at
 // n = 4), which are then resident at once.
+//
+// As in the row layout, the arguments the first loads need come first (the
+// build preloads them into scalar registers); pre and grad_pre follow.
 template <int V, int U, int S, bool ACC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void hagg_bwd_kernel(
-    const uint16_t* __restrict__ residual, const float* __restrict__ pre,
-    const uint16_t* __restrict__ grad_out, uint16_t* __restrict__ grad_residual,
-    float* __restrict__ grad_pre, int64_t T, int32_t n, int64_t H, uint32_t ngroups,
-    int32_t tokens_per_block) {
+    const uint16_t* __restrict__ residual, const uint16_t* __restrict__ grad_out,
+    uint16_t* __restrict__ grad_residual, int64_t H, int64_t T, uint32_t ngroups,
+    int32_t tokens_per_block, int32_t n, const float* __restrict__ pre,
+    float* __restrict__ grad_pre) {
   __shared__ float wave_sum[4][S];  // [wave][stream of this block]
 
   const int lane = threadIdx.x;
@@ -342,10 +345,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void h
     const int64_t t = static_cast<int64_t>(blockIdx.x) * tokens_per_block + tt;
     if (t >= T) break;  // uniform across the block
 
-    const float* p = pre + n * t + i0;
-    float w[S];
-#pragma unroll
-    for (int i = 0; i < S; ++i) w[i] = p[i];
     // One resource per row: the token's grad_out row and the block's S
     // residual and grad_residual rows (2H bytes each). Groups past the end of
     // the row (k >= ngroups) and elements past H of a short last group read 0
@@ -380,6 +379,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void h
     if (rounds > 0) {
 #pragma unroll
       for (int u = 0; u < U; ++u) bwd_issue(sl, u, lane + u * kLanes, g_row, r_row, gr_row);
+      __builtin_amdgcn_sched_barrier(0);
+      // The token's weights, read once the ring's first loads are out.
+      const float* p = pre + n * t + i0;
+      float w[S];
+#pragma unroll
+      for (int i = 0; i < S; ++i) w[i] = p[i];
       for (uint32_t j = 0; j + 1 < rounds; ++j) {
         const uint32_t k0 = lane + j * step;
 #pragma unroll
@@ -484,18 +489,24 @@ __device__ __forceinline__ void rows_consume(RowSlots<V, B, ACC>& sl, int b, uin
   }
 }
 
+//
+// The arguments a wave needs before its first loads come first, so that the
+// build's kernel-argument preloading places them in scalar registers: no
+// argument load, block-size read or 64-bit division precedes the ring's
+// first requests (n is a power of two, passed as log2n; rows_per_block is
+// the block's wave count).
 template <int V, int B, bool ACC>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void hagg_bwd_rows_kernel(
-    const uint16_t* __restrict__ residual, const float* __restrict__ pre,
-    const uint16_t* __restrict__ grad_out, uint16_t* __restrict__ grad_residual,
-    float* __restrict__ grad_pre, int64_t rows, int32_t n, int64_t H, uint32_t ngroups) {
+    const uint16_t* __restrict__ residual, const uint16_t* __restrict__ grad_out,
+    uint16_t* __restrict__ grad_residual, int64_t H, int64_t rows, uint32_t log2n,
+    uint32_t rows_per_block, uint32_t ngroups, const float* __restrict__ pre,
+    float* __restrict__ grad_pre) {
   static_assert(B % 4 == 0, "ring size must be a multiple of 4");
   const uint32_t lane = threadIdx.x & 63;
-  const int64_t q = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) +
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * rows_per_block +
                     __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (q >= rows) return;  // the whole wave
-  const int64_t t = q / n;
-  const float w = pre[q];  // pre[t, q mod n]
+  const int64_t t = q >> log2n;
   const Rsrc g_row = make_rsrc(grad_out + t * H, 2 * H);
   const Rsrc r_row = make_rsrc(residual + q * H, 2 * H);
   const Rsrc gr_row = make_rsrc(grad_residual + q * H, 2 * H);
@@ -512,6 +523,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void h
     rows_issue(sl, b, lane + 64 * b, g_row, r_row, gr_row);
     __builtin_amdgcn_sched_barrier(0);
   }
+  const float w = pre[q];  // pre[t, q mod n], read once the ring's first loads are out
   for (uint32_t j = 0; j + 1 < rounds; ++j) {
     const uint32_t k0 = lane + 64 * B * j;
 #pragma unroll
@@ -1008,9 +1020,9 @@ void launch_bwd_t(const BwdPlan& pl, const uint16_t* residual, const float* pre,
                   int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
   const uint32_t blocks = static_cast<uint32_t>((tokens + pl.tpb - 1) / pl.tpb);
   hipExtLaunchKernelGGL(hagg_bwd_kernel<V, U, S, ACC>, dim3(blocks, pl.n / S), dim3(kLanes), 0,
-                        stream, ev.start, ev.stop, 0, residual, pre, grad_out, grad_residual,
-                        grad_pre, tokens, static_cast<int32_t>(pl.n), H,
-                        static_cast<uint32_t>(pl.ngroups), static_cast<int32_t>(pl.tpb));
+                        stream, ev.start, ev.stop, 0, residual, grad_out, grad_residual, H,
+                        tokens, static_cast<uint32_t>(pl.ngroups), static_cast<int32_t>(pl.tpb),
+                        static_cast<int32_t>(pl.n), pre, grad_pre);
 }
 
 // Instantiates only the batches the register budget allows (the plan never
@@ -1047,8 +1059,10 @@ void launch_rows_t(const BwdPlan& pl, const uint16_t* residual, const float* pre
   const uint32_t blocks = static_cast<uint32_t>((rows + pl.rows_per_block - 1) / pl.rows_per_block);
   hipExtLaunchKernelGGL(hagg_bwd_rows_kernel<V, B, ACC>, dim3(blocks),
                         dim3(64 * pl.rows_per_block), 0, stream, ev.start, ev.stop, 0, residual,
-                        pre, grad_out, grad_residual, grad_pre, rows,
-                        static_cast<int32_t>(pl.n), H, static_cast<uint32_t>(pl.ngroups));
+                        grad_out, grad_residual, H, rows,
+                        static_cast<uint32_t>(__builtin_ctz(static_cast<unsigned>(pl.n))),
+                        static_cast<uint32_t>(pl.rows_per_block),
+                        static_cast<uint32_t>(pl.ngroups), pre, grad_pre);
 }
 
 // Instantiates only the ring sizes the register budget allows.
