@@ -24,7 +24,8 @@ Per library, one performance flag (no effect on any result):
   T=1024). Measured per call at H=7168: forward 11.76 -> 11.44 us at T=1024
   and 22.62 -> 22.24 us at T=2048, backward 22.08 -> 21.80 us at T=1024;
   about 1% slower at T=128. The coefficient library was 1-3% slower with
-  it (few, latency-bound waves) and builds without it.
+  it (few, latency-bound waves), also with its row count moved among the
+  preloaded arguments, and builds without it.
 
 `device_asm()` writes the gfx950 assembly of the same source with the same
 flags, so tests can scan the machine code this library runs.
