@@ -37,19 +37,19 @@ reading instead):
 * The epilogue gets mix, the saved activations pre and post, the upstream
   gradients grad_pre, grad_post, grad_res, alpha[3] and c, and computes
     d[r, j] = dL/dz[r, j]:
-      pre  columns: grad_pre  * (pre  * (1 - pre))       sigmoid' = s(1-s)
-      post columns: grad_post * (post * (1 - post * inv_c))  (c s)' = c s(1-s)
+      pre  columns: grad_pre  * (pre  * (1 - pre))        sigmoid' = s(1-s)
+      post columns: grad_post * (post * (1 - post / c))   (c s)' = c s(1-s), s = post / c
       res  columns: grad_res
     grad_mix[r, j] = alpha[k(j)] * d[r, j]
     grad_b[j]      = row_sum over r of d[r, j]
     grad_alpha[k]  = row_sum over r of e[r, k], where e[r, k] adds
                      d[r, j] * mix[r, j] over the columns j of group k in
                      ascending j, starting from +0.0.
-  inv_c is 1/c rounded to fp32 once (so sigma = post / c becomes one
-  multiply: no division in the per-row work; for a power-of-two c such as 2
-  it is exactly post / c). Every product, sum and difference is one fp32
-  round-to-nearest operation, evaluated in exactly the nesting written
-  above.
+  The post gate's sigmoid is recovered from its saved output as post / c,
+  one fp32 division rounded to nearest even (the plain derivative of
+  post = c * sigmoid(z), written in the saved output). Every product,
+  quotient, sum and difference is one fp32 round-to-nearest operation,
+  evaluated in exactly the nesting written above.
 * row_sum is this repository's fixed two-stage order (see `row_sum`); it
   depends only on the number of rows.
 
@@ -138,10 +138,9 @@ def _check(mix, pre, post, grad_pre, grad_post, grad_res, alpha, n):
 def dz(pre, post, grad_pre, grad_post, grad_res, post_scale) -> np.ndarray:
     """d[r, j] = dL/dz[r, j] for all m columns, float32 [R, m]."""
     one = np.float32(1.0)
-    inv_c = np.divide(one, np.float32(post_scale))       # fp32, rounded once
-    with np.errstate(over="ignore", invalid="ignore", under="ignore"):
+    with np.errstate(over="ignore", invalid="ignore", under="ignore", divide="ignore"):
         d_pre = np.multiply(grad_pre, np.multiply(pre, np.subtract(one, pre)))
-        s = np.multiply(post, inv_c)
+        s = np.divide(post, np.float32(post_scale))      # the post gate's sigmoid
         d_post = np.multiply(grad_post, np.multiply(post, np.subtract(one, s)))
     return np.concatenate([d_pre, d_post, grad_res], axis=1).astype(np.float32)
 

@@ -240,19 +240,21 @@ def _rn32(x) -> float:
     return float(Fr(fl) * Fr(2) ** (e - 23))
 
 
-def test_post_gate_uses_the_fp32_reciprocal_of_the_scale():
-    # c = 3: 1/3 rounds to 11184811 * 2^-25. Find the first post value from
-    # 1.5 upward where d = rn(q * rn(1 - s)) differs between s = rn(q * ic)
-    # and s = rn(q / 3), in exact rational arithmetic (1 - s is exact for s
-    # in [1/2, 1]), and check that the oracle follows the reciprocal form.
+def test_post_gate_divides_by_the_scale():
+    # c = 3: the sigmoid is s = rn(q / 3), one correctly rounded division. A
+    # reciprocal form rn(q * rn(1/3)) is a plausible shortcut that differs
+    # from it; find the first post value from 1.5 upward where
+    # d = rn(q * rn(1 - s)) differs between the two, in exact rational
+    # arithmetic (1 - s is exact for s in [1/2, 1]), and check that the oracle
+    # follows the division.
     from fractions import Fraction as Fr
-    ic = Fr(float(np.divide(np.float32(1), np.float32(3))))
+    ic = Fr(_rn32(Fr(1, 3)))
     assert ic == Fr(11184811, 2 ** 25)
     q = np.float32(1.5)
     for _ in range(100000):
         Q = Fr(float(q))
-        want = _rn32(Q * (1 - Fr(_rn32(Q * ic))))
-        other = _rn32(Q * (1 - Fr(_rn32(Q / 3))))
+        want = _rn32(Q * (1 - Fr(_rn32(Q / 3))))
+        other = _rn32(Q * (1 - Fr(_rn32(Q * ic))))
         if want != other:
             break
         q = np.nextafter(q, np.float32(3.0))
@@ -265,6 +267,31 @@ def test_post_gate_uses_the_fp32_reciprocal_of_the_scale():
     assert dz[0, 2] == np.float32(want) and dz[0, 3] == np.float32(-want)
 
 
+@pytest.mark.parametrize("c", [3.0, 0.75, 7.0, 1.0 / 3.0])
+def test_post_sigmoid_is_the_correctly_rounded_quotient(c):
+    """s = post / c is the fp32 value nearest the exact quotient, for
+    non-power-of-two scales, checked in exact rational arithmetic on the
+    quantity the post derivative is built from (1 - s, exact for s in
+    [1/2, 1])."""
+    from fractions import Fraction as Fr
+    rng = np.random.default_rng(11)
+    cf = np.float32(c)
+    C = Fr(float(cf))
+    post = (cf * rng.uniform(0.5, 1.0, 64)).astype(np.float32)
+    d = _inputs(64, 2, 9)
+    d["post"][:, 0] = post
+    d["post"][:, 1] = post
+    d["grad_post"][:] = 1.0
+    dz = cb.dz(d["pre"], d["post"], d["grad_pre"], d["grad_post"], d["grad_res"], float(cf))
+    for r, q in enumerate(post):
+        Q = Fr(float(q))
+        s = Fr(_rn32(Q / C))
+        if not (Fr(1, 2) <= s <= 1):
+            continue
+        want = _rn32(Q * (1 - s)) if s < 1 else 0.0
+        assert dz[r, 2] == np.float32(want), (c, float(q))
+
+
 def test_one_row_grad_b_is_the_row_derivative():
     d = _inputs(1, 8, 4)
     gm, gb, _ = _run(d, 2.0, 8)
@@ -272,12 +299,13 @@ def test_one_row_grad_b_is_the_row_derivative():
     assert np.array_equal(gb, dz[0])
 
 
+@pytest.mark.parametrize("c", [2.0, 3.0, 0.75])
 @pytest.mark.parametrize("n,R", [(2, 300), (4, 2048), (8, 257)])
-def test_within_error_bounds_of_fp64(n, R):
-    d = _inputs(R, n, 5 + n)
-    gm, gb, ga = _run(d, 2.0, n)
+def test_within_error_bounds_of_fp64(n, R, c):
+    d = _inputs(R, n, 5 + n, c)
+    gm, gb, ga = _run(d, c, n)
     ex = cb.coeff_bwd_exact(d["mix"], d["pre"], d["post"], d["grad_pre"], d["grad_post"],
-                            d["grad_res"], d["alpha"], 2.0, n)
+                            d["grad_res"], d["alpha"], c, n)
     k = cb.groups(n)
     al = np.abs(d["alpha"].astype(np.float64))[k][None, :]
     assert np.all(np.abs(gm - ex["grad_mix"]) <= 6 * U * al * ex["mag_d"] + 1e-44)

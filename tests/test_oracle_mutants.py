@@ -86,10 +86,11 @@ MUTANTS = [
     ("h_aggregate", "        q = np.multiply(g[:, None, :], r)",
      "        q = np.multiply(g[:, None, :], r[:, ::-1, :])", "streams transposed"),
     # coefficient epilogue
-    ("coeff_bwd", "        s = np.multiply(post, inv_c)", "        s = post",
+    ("coeff_bwd", "        s = np.divide(post, np.float32(post_scale))", "        s = post",
      "post gate ignores its scale"),
-    ("coeff_bwd", "        s = np.multiply(post, inv_c)",
-     "        s = np.divide(post, np.float32(post_scale))", "division instead of the reciprocal"),
+    ("coeff_bwd", "        s = np.divide(post, np.float32(post_scale))",
+     "        s = np.multiply(post, np.divide(one, np.float32(post_scale)))",
+     "reciprocal of the scale instead of the division"),
     ("coeff_bwd", "np.multiply(pre, np.subtract(one, pre))", "np.multiply(pre, np.add(one, pre))",
      "sign in the sigmoid derivative"),
     ("coeff_bwd", "np.multiply(grad_post, np.multiply(post, np.subtract(one, s)))",
