@@ -11,7 +11,7 @@ they have not been built).
 from __future__ import annotations
 
 _OPS_NAMES = (
-    "mhc_h_aggregate_fwd", "mhc_h_aggregate_bwd", "mhc_bf16_rne_probe",
+    "mhc_h_aggregate_fwd", "mhc_h_aggregate_bwd",
     "mhc_h_aggregate_fwd_timed", "mhc_h_aggregate_bwd_timed", "mhc_h_aggregate_bwd_acc",
     "mhc_h_aggregate_plan_bwd_acc", "mhc_h_aggregate_fwd_n", "mhc_h_aggregate_bwd_n",
     "mhc_h_aggregate_plan_fwd_n", "mhc_h_aggregate_plan_bwd_n",

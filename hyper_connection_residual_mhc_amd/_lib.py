@@ -1,8 +1,11 @@
 """ctypes view of the C ABIs in include/mhc_h_aggregate.h and
-include/mhc_coeff_bwd.h.
+include/mhc_coeff_bwd.h, and of the measurement library (csrc/mhc_probes.h)
+that the tests and the benchmark use.
 
-Loading fails loudly (ImportError) when a shared library has not been
-built: there is no other implementation to fall back on.
+Loading fails loudly (ImportError) when a shared library has not been built,
+or was built from other sources than the ones in the tree (the digest
+recorded beside it at build time no longer matches): there is no other
+implementation to fall back on, and a stale binary is never run by mistake.
 """
 
 from __future__ import annotations
@@ -10,13 +13,14 @@ from __future__ import annotations
 import ctypes
 from ctypes import POINTER, c_char_p, c_float, c_int, c_int32, c_int64, c_uint32, c_void_p
 
-from ._build import COEFF_LIB_PATH, LIB_PATH
+from . import _build
+from ._build import COEFF_LIB_PATH, COEFF_SRC, LIB_PATH, PROBE_LIB_PATH, PROBE_SRC, SRC
 
 MHC_SUCCESS = 0
 MHC_ERROR_INVALID_VALUE = 1
 MHC_ERROR_ALIASING = 2
 MHC_ERROR_HIP = 3
-MHC_ABI_VERSION = 3
+MHC_ABI_VERSION = 4
 MHC_BWD_SPLIT = 1
 MHC_BWD_ROWS = 2
 MHC_MAX_H = 1 << 26
@@ -81,12 +85,9 @@ SIGNATURES = {
     "mhc_h_aggregate_plan_bwd": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                          c_int64, c_int64, POINTER(mhc_launch),
                                          POINTER(mhc_launch), POINTER(c_int64)]),
-    "mhc_bf16_rne_probe": (c_int, [c_uint32, c_int64, c_void_p, c_void_p]),
-    "mhc_stream_probe": (c_int, [c_void_p, c_int64, c_void_p, c_int64, c_int32, c_int32,
-                                 c_void_p, c_void_p, c_void_p]),
 }
 
-MHC_COEFF_ABI_VERSION = 2
+MHC_COEFF_ABI_VERSION = 3
 MHC_COEFF_CHUNK = 64
 MHC_COEFF_MAX_ROWS = 1 << 28
 
@@ -102,47 +103,65 @@ COEFF_SIGNATURES = {
                       + [c_int64, c_int64, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
 }
 
-_lib: ctypes.CDLL | None = None
-_coeff: ctypes.CDLL | None = None
+MHC_PROBE_ABI_VERSION = 1
+
+# Every symbol csrc/mhc_probes.h declares.
+PROBE_SIGNATURES = {
+    "mhc_probe_abi_version": (c_int, []),
+    "mhc_probe_last_error_message": (c_char_p, []),
+    "mhc_bf16_rne_probe": (c_int, [c_uint32, c_int64, c_void_p, c_void_p]),
+    "mhc_stream_probe": (c_int, [c_void_p, c_int64, c_void_p, c_int64, c_int32, c_int32,
+                                 c_void_p, c_void_p, c_void_p]),
+}
+
+_loaded: dict[str, ctypes.CDLL] = {}
+
+
+def open_checked(path, src, signatures: dict, version_fn: str, version: int) -> ctypes.CDLL:
+    """Load the library at `path` after checking that it exists and that the
+    digest recorded beside it matches `src` and the headers now in the tree;
+    declare every signature and check the ABI version. ImportError otherwise."""
+    if not path.exists():
+        raise ImportError(f"{path} is missing: build it with __graft_entry__.build() "
+                          "(the operation has no other implementation)")
+    want = _build.source_digest(src)
+    have = _build.recorded_digest(path)
+    if have != want:
+        raise ImportError(f"{path} was built from other sources than the ones in the tree "
+                          f"(recorded digest {str(have)[:16]}, sources {want[:16]}): rebuild it "
+                          "with __graft_entry__.build()")
+    handle = ctypes.CDLL(str(path))
+    for name, (restype, argtypes) in signatures.items():
+        fn = getattr(handle, name)
+        fn.restype = restype
+        fn.argtypes = argtypes
+    if getattr(handle, version_fn)() != version:
+        raise ImportError(f"{path.name}: ABI version mismatch")
+    return handle
+
+
+def _get(key: str, *args) -> ctypes.CDLL:
+    if key not in _loaded:
+        _loaded[key] = open_checked(*args)
+    return _loaded[key]
 
 
 def lib() -> ctypes.CDLL:
-    """The loaded library (loaded once). Raises ImportError if not built."""
-    global _lib
-    if _lib is None:
-        if not LIB_PATH.exists():
-            raise ImportError(
-                f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
-                "(the operation has no other implementation)")
-        handle = ctypes.CDLL(str(LIB_PATH))
-        for name, (restype, argtypes) in SIGNATURES.items():
-            fn = getattr(handle, name)
-            fn.restype = restype
-            fn.argtypes = argtypes
-        if handle.mhc_abi_version() != MHC_ABI_VERSION:
-            raise ImportError("libmhc_h_aggregate ABI version mismatch")
-        _lib = handle
-    return _lib
+    """The h_aggregate library (loaded once). ImportError if missing or stale."""
+    return _get("h_aggregate", LIB_PATH, SRC, SIGNATURES, "mhc_abi_version", MHC_ABI_VERSION)
 
 
 def coeff_lib() -> ctypes.CDLL:
-    """The coefficient-backward library (loaded once). Raises ImportError if
-    it is not built."""
-    global _coeff
-    if _coeff is None:
-        if not COEFF_LIB_PATH.exists():
-            raise ImportError(
-                f"{COEFF_LIB_PATH} is missing: build it with __graft_entry__.build() "
-                "(the operation has no other implementation)")
-        handle = ctypes.CDLL(str(COEFF_LIB_PATH))
-        for name, (restype, argtypes) in COEFF_SIGNATURES.items():
-            fn = getattr(handle, name)
-            fn.restype = restype
-            fn.argtypes = argtypes
-        if handle.mhc_coeff_abi_version() != MHC_COEFF_ABI_VERSION:
-            raise ImportError("libmhc_coeff_bwd ABI version mismatch")
-        _coeff = handle
-    return _coeff
+    """The coefficient-backward library (loaded once). ImportError if missing
+    or stale."""
+    return _get("coeff", COEFF_LIB_PATH, COEFF_SRC, COEFF_SIGNATURES, "mhc_coeff_abi_version",
+                MHC_COEFF_ABI_VERSION)
+
+
+def probe_lib() -> ctypes.CDLL:
+    """The measurement library (loaded once). ImportError if missing or stale."""
+    return _get("probes", PROBE_LIB_PATH, PROBE_SRC, PROBE_SIGNATURES, "mhc_probe_abi_version",
+                MHC_PROBE_ABI_VERSION)
 
 
 class MhcError(RuntimeError):
@@ -162,3 +181,8 @@ def check(status: int) -> None:
 def check_coeff(status: int) -> None:
     if status != MHC_SUCCESS:
         raise MhcError(status, coeff_lib().mhc_coeff_last_error_message().decode())
+
+
+def check_probe(status: int) -> None:
+    if status != MHC_SUCCESS:
+        raise MhcError(status, probe_lib().mhc_probe_last_error_message().decode())

@@ -30,10 +30,11 @@
 //    exactly +0.0 everywhere, which is what the order prescribes for them;
 //    their grad_mix stores are dropped by the same check.
 //  * Bit exactness: contraction off (pragma and -ffp-contract=off), no
-//    fast-math, denormals kept, no division in a kernel (the post gate uses
-//    the host-rounded reciprocal of its scale).
+//    fast-math, denormals kept. The post gate's sigmoid is post / c, one
+//    fp32 division rounded to nearest even (hipcc's default, correctly
+//    rounded division; its expansion is the only place fused multiply-adds
+//    appear in this library's machine code, which the build guards check).
 
-#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -43,6 +44,7 @@
 
 #include "mhc_coeff_bwd.h"
 #include "mhc_lanes.h"
+#include "mhc_launch.h"
 
 #if defined(__FAST_MATH__)
 #error "mhc_coeff_bwd must not be built with fast-math: its results are defined bit for bit"
@@ -114,7 +116,7 @@ __device__ __forceinline__ void chunk_sums(
     const float* __restrict__ mix, const float* __restrict__ pre,
     const float* __restrict__ post, const float* __restrict__ grad_pre,
     const float* __restrict__ grad_post, const float* __restrict__ grad_res,
-    const float* __restrict__ alpha, float inv_c, float* __restrict__ grad_mix,
+    const float* __restrict__ alpha, float post_scale, float* __restrict__ grad_mix,
     float* __restrict__ partial, int64_t rows, uint32_t chunks, uint32_t c, uint32_t lane,
     bool active, float* tile) {
   constexpr int M = 2 * N + N * N;
@@ -147,7 +149,7 @@ __device__ __forceinline__ void chunk_sums(
   for (int i = 0; i < N; ++i) {
     const float q = ld(rs_post, (lane * N + i) * 4);
     const float gq = ld(rs_gpost, (lane * N + i) * 4);
-    d[N + i] = gq * (q * (1.0f - q * inv_c));
+    d[N + i] = gq * (q * (1.0f - q / post_scale));
   }
 #pragma unroll
   for (int i = 0; i < N * N; ++i) d[2 * N + i] = ld(rs_gres, (lane * N * N + i) * 4);
@@ -237,10 +239,11 @@ __global__ __launch_bounds__(64) void coeff_partial_kernel(
     const float* __restrict__ mix, const float* __restrict__ pre,
     const float* __restrict__ post, const float* __restrict__ grad_pre,
     const float* __restrict__ grad_post, const float* __restrict__ grad_res,
-    const float* __restrict__ alpha, float inv_c, float* __restrict__ grad_mix,
+    const float* __restrict__ alpha, float post_scale, float* __restrict__ grad_mix,
     float* __restrict__ partial, int64_t rows, uint32_t chunks) {
   __shared__ __align__(16) float tile[Tile<N>::kFloats];
-  chunk_sums<N>(mix, pre, post, grad_pre, grad_post, grad_res, alpha, inv_c, grad_mix, partial,
+  chunk_sums<N>(mix, pre, post, grad_pre, grad_post, grad_res, alpha, post_scale, grad_mix,
+                partial,
                 rows, chunks, blockIdx.x, threadIdx.x, true, tile);
 }
 
@@ -266,7 +269,7 @@ __global__ __launch_bounds__(64 * W) void coeff_fused_kernel(
     const float* __restrict__ mix, const float* __restrict__ pre,
     const float* __restrict__ post, const float* __restrict__ grad_pre,
     const float* __restrict__ grad_post, const float* __restrict__ grad_res,
-    const float* __restrict__ alpha, float inv_c, float* __restrict__ grad_mix,
+    const float* __restrict__ alpha, float post_scale, float* __restrict__ grad_mix,
     float* __restrict__ partial, uint32_t* __restrict__ arrived, int64_t rows,
     uint32_t chunks, float* __restrict__ grad_b, float* __restrict__ grad_alpha) {
   constexpr int M = 2 * N + N * N;
@@ -276,7 +279,8 @@ __global__ __launch_bounds__(64 * W) void coeff_fused_kernel(
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t c = blockIdx.x * W + wave;
-  chunk_sums<N>(mix, pre, post, grad_pre, grad_post, grad_res, alpha, inv_c, grad_mix, partial,
+  chunk_sums<N>(mix, pre, post, grad_pre, grad_post, grad_res, alpha, post_scale, grad_mix,
+                partial,
                 rows, chunks, c, lane, c < chunks, tiles + wave * Tile<N>::kFloats);
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -392,9 +396,6 @@ mhc_status validate(const float* mix, const float* pre, const float* post,
   if (!(post_scale > 0.0f) || !isfinite(post_scale))
     return fail(MHC_ERROR_INVALID_VALUE, "post_scale must be finite and positive (got %g)",
                 (double)post_scale);
-  if (!isfinite(1.0f / post_scale) || 1.0f / post_scale == 0.0f)
-    return fail(MHC_ERROR_INVALID_VALUE, "1 / post_scale is not a finite non-zero fp32 (%g)",
-                (double)post_scale);
   const int m = columns(n);
   const int64_t need = workspace_need(rows, n);
   mhc_status st;
@@ -431,7 +432,7 @@ mhc_status validate(const float* mix, const float* pre, const float* post,
 
 struct CoeffArgs {
   const float *mix, *pre, *post, *grad_pre, *grad_post, *grad_res, *alpha;
-  float inv_c;
+  float c;  // post_scale
   float *grad_mix, *grad_b, *grad_alpha, *partial;
   uint32_t* arrived;
   int64_t rows;
@@ -439,10 +440,10 @@ struct CoeffArgs {
 };
 
 template <int N>
-void launch_partial(const CoeffArgs& a, hipStream_t s, hipEvent_t start) {
-  hipExtLaunchKernelGGL(coeff_partial_kernel<N>, dim3(a.chunks), dim3(64), 0, s, start, nullptr,
-                        0, a.mix, a.pre, a.post, a.grad_pre, a.grad_post, a.grad_res, a.alpha,
-                        a.inv_c, a.grad_mix, a.partial, a.rows, a.chunks);
+hipError_t launch_partial(const CoeffArgs& a, hipStream_t s, hipEvent_t start) {
+  return launch_kernel(coeff_partial_kernel<N>, dim3(a.chunks), dim3(64), s, start, nullptr,
+                       a.mix, a.pre, a.post, a.grad_pre, a.grad_post, a.grad_res, a.alpha, a.c,
+                       a.grad_mix, a.partial, a.rows, a.chunks);
 }
 
 // Waves per block of the one-launch form: 2 up to this many chunks, 4
@@ -454,20 +455,18 @@ void launch_partial(const CoeffArgs& a, hipStream_t s, hipEvent_t start) {
 constexpr uint32_t kTwoWaveMaxChunks = 64;
 
 template <int N, int W>
-void launch_fused_w(const CoeffArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+hipError_t launch_fused_w(const CoeffArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   const uint32_t blocks = (a.chunks + W - 1) / W;
-  hipExtLaunchKernelGGL(coeff_fused_kernel<N, W>, dim3(blocks), dim3(64 * W), 0, s, start, stop,
-                        0, a.mix, a.pre, a.post, a.grad_pre, a.grad_post, a.grad_res, a.alpha,
-                        a.inv_c, a.grad_mix, a.partial, a.arrived, a.rows, a.chunks, a.grad_b,
-                        a.grad_alpha);
+  return launch_kernel(coeff_fused_kernel<N, W>, dim3(blocks), dim3(64 * W), s, start, stop,
+                       a.mix, a.pre, a.post, a.grad_pre, a.grad_post, a.grad_res, a.alpha, a.c,
+                       a.grad_mix, a.partial, a.arrived, a.rows, a.chunks, a.grad_b,
+                       a.grad_alpha);
 }
 
 template <int N>
-void launch_fused(const CoeffArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
-  if (a.chunks <= kTwoWaveMaxChunks)
-    launch_fused_w<N, 2>(a, s, start, stop);
-  else
-    launch_fused_w<N, 4>(a, s, start, stop);
+hipError_t launch_fused(const CoeffArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+  if (a.chunks <= kTwoWaveMaxChunks) return launch_fused_w<N, 2>(a, s, start, stop);
+  return launch_fused_w<N, 4>(a, s, start, stop);
 }
 
 // Launches of one call: 1 = one launch (chunk sums + last-block reduction),
@@ -478,12 +477,61 @@ int plan_launches(int64_t rows, int32_t n, int32_t launches) {
   return n <= 4 && chunk_count(rows) <= kFusedMaxChunks ? 1 : 2;
 }
 
-mhc_status launch_error(const char* what) {
-  const hipError_t e = hipGetLastError();
+// The status of one launch (the value hipExtLaunchKernel returned for it).
+mhc_status launch_status(hipError_t e, const char* what) {
   if (e != hipSuccess)
     return fail(MHC_ERROR_HIP, "%s launch failed: %s (%s)", what, hipGetErrorName(e),
                 hipGetErrorString(e));
   return ok();
+}
+
+// The arguments of a call whose pointers and sizes have been validated;
+// `workspace` is device memory of at least workspace_need(rows, n) bytes
+// whose first 4 bytes (the arrival counter) are zero.
+CoeffArgs make_args(const float* mix, const float* pre, const float* post,
+                    const float* grad_pre, const float* grad_post, const float* grad_res,
+                    const float* alpha, float post_scale, float* grad_mix, float* grad_b,
+                    float* grad_alpha, void* workspace, int64_t rows) {
+  CoeffArgs a;
+  a.mix = mix; a.pre = pre; a.post = post; a.grad_pre = grad_pre; a.grad_post = grad_post;
+  a.grad_res = grad_res; a.alpha = alpha;
+  a.c = post_scale;
+  a.grad_mix = grad_mix; a.grad_b = grad_b; a.grad_alpha = grad_alpha;
+  a.arrived = static_cast<uint32_t*>(workspace);
+  a.partial = rows > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + kWsHeader)
+                       : nullptr;
+  a.rows = rows;
+  a.chunks = static_cast<uint32_t>(chunk_count(rows));
+  return a;
+}
+
+// Enqueue one call's kernels (one launch or two, as planned).
+mhc_status run(const CoeffArgs& a, int32_t n, int32_t launches, hipStream_t s, hipEvent_t start,
+               hipEvent_t stop) {
+  mhc_status st;
+  if (plan_launches(a.rows, n, launches) == 1) {
+    hipError_t e;
+    switch (n) {
+      case 2: e = launch_fused<2>(a, s, start, stop); break;
+      case 4: e = launch_fused<4>(a, s, start, stop); break;
+      default: e = launch_fused<8>(a, s, start, stop); break;
+    }
+    return launch_status(e, "coefficient backward (one launch)");
+  }
+  if (a.chunks > 0) {
+    hipError_t e;
+    switch (n) {
+      case 2: e = launch_partial<2>(a, s, start); break;
+      case 4: e = launch_partial<4>(a, s, start); break;
+      default: e = launch_partial<8>(a, s, start); break;
+    }
+    if ((st = launch_status(e, "coefficient backward (chunk sums)")) != MHC_SUCCESS) return st;
+  }
+  const int32_t m = columns(n);
+  const hipError_t e =
+      launch_kernel(coeff_reduce_kernel, dim3(m + 3), dim3(64), s, a.chunks > 0 ? nullptr : start,
+                    stop, a.partial, a.chunks, m, a.grad_b, a.grad_alpha);
+  return launch_status(e, "coefficient backward (reduction)");
 }
 
 }  // namespace
@@ -531,41 +579,10 @@ mhc_status mhc_coeff_bwd(const float* mix, const float* pre, const float* post,
   if (st != MHC_SUCCESS) return st;
   if (launches < 0 || launches > 2)
     return fail(MHC_ERROR_INVALID_VALUE, "launches must be 0, 1 or 2 (got %d)", launches);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipEvent_t start = static_cast<hipEvent_t>(start_event);
-  hipEvent_t stop = static_cast<hipEvent_t>(stop_event);
-  CoeffArgs a;
-  a.mix = mix; a.pre = pre; a.post = post; a.grad_pre = grad_pre; a.grad_post = grad_post;
-  a.grad_res = grad_res; a.alpha = alpha;
-  a.inv_c = 1.0f / post_scale;  // rounded to fp32 once
-  a.grad_mix = grad_mix; a.grad_b = grad_b; a.grad_alpha = grad_alpha;
-  a.arrived = static_cast<uint32_t*>(workspace);
-  a.partial = rows > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + kWsHeader)
-                       : nullptr;
-  a.rows = rows;
-  a.chunks = static_cast<uint32_t>(chunk_count(rows));
-  (void)hipGetLastError();
-  if (plan_launches(rows, n, launches) == 1) {
-    switch (n) {
-      case 2: launch_fused<2>(a, s, start, stop); break;
-      case 4: launch_fused<4>(a, s, start, stop); break;
-      default: launch_fused<8>(a, s, start, stop); break;
-    }
-    return launch_error("coefficient backward (one launch)");
-  }
-  if (a.chunks > 0) {
-    switch (n) {
-      case 2: launch_partial<2>(a, s, start); break;
-      case 4: launch_partial<4>(a, s, start); break;
-      default: launch_partial<8>(a, s, start); break;
-    }
-    if ((st = launch_error("coefficient backward (chunk sums)")) != MHC_SUCCESS) return st;
-  }
-  const int m = columns(n);
-  hipExtLaunchKernelGGL(coeff_reduce_kernel, dim3(m + 3), dim3(64), 0, s,
-                        a.chunks > 0 ? nullptr : start, stop, 0, a.partial, a.chunks, m, grad_b,
-                        grad_alpha);
-  return launch_error("coefficient backward (reduction)");
+  const CoeffArgs a = make_args(mix, pre, post, grad_pre, grad_post, grad_res, alpha, post_scale,
+                                grad_mix, grad_b, grad_alpha, workspace, rows);
+  return run(a, n, launches, static_cast<hipStream_t>(stream),
+             static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event));
 }
 
 }  // extern "C"

@@ -35,8 +35,10 @@
 #include <stdio.h>
 #include <string.h>
 
+#include "mhc_bf16.h"
 #include "mhc_h_aggregate.h"
 #include "mhc_lanes.h"
+#include "mhc_launch.h"
 
 #if defined(__FAST_MATH__)
 #error "mhc_h_aggregate must not be built with fast-math: its results are defined bit for bit"
@@ -47,29 +49,8 @@
 namespace {
 
 // ---------------------------------------------------------------------------
-// Device helpers: exact widening and round-to-nearest-even narrowing
+// Device helpers: V-element vectors (conversions in mhc_bf16.h)
 // ---------------------------------------------------------------------------
-
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// Two fp32 values -> two bf16 patterns packed low|high in one dword, rounded
-// to nearest even (v_cvt_pk_bf16_f32 on gfx950).
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  f32x2 v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
-
-__device__ __forceinline__ uint16_t to_bf16(float x) {
-  return static_cast<uint16_t>(pack_bf16x2(x, 0.0f));
-}
-
-// bf16 pattern -> fp32, exact (the bf16 pattern is the top half of the fp32).
-__device__ __forceinline__ float lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float hi_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-__device__ __forceinline__ float bf16_f32(uint16_t b) {
-  return __uint_as_float(static_cast<uint32_t>(b) << 16);
-}
 
 // A V-element bf16 vector as a native vector of 32-bit words (V = 8, 4), one
 // word (V = 2) or one half-word (V = 1).
@@ -125,13 +106,11 @@ template <> __device__ __forceinline__ uint16_t pack<1>(const float (&y)[1]) {
 // Streamed bytes are touched once, so loads carry the nontemporal hint; the
 // one row several waves read (the backward's grad_out in the row layout)
 // keeps the default policy so that it stays in cache for them.
-constexpr int kNontemporal = 2;          // cache-policy bit 1: nt
-constexpr int kCached = 0;               // default policy: kept for other readers
-// Cache-policy bit 4 (sc1): device-scope store, written through the L2 at
-// once. Measured with cold caches: the forward (4 bytes read per byte
-// written) streams 5-8% faster with it than with nt; the backward (5:4) and
-// the accumulating backward (9:4) stream 2-4% slower, so they keep nt.
-constexpr int kWriteThrough = 16;
+// (kNontemporal, kCached and kWriteThrough in mhc_lanes.h.) Stores: the
+// forward's output is written through at device scope (sc1); measured with
+// cold caches, the forward (4 bytes read per byte written) streams 5-8%
+// faster with it than with nt; the backward (5:4) and the accumulating
+// backward (9:4) stream 2-4% slower, so they keep nt.
 
 // Load V bf16 elements at element `off` (per lane) plus `soff` bytes
 // (wave-uniform, carried in a scalar register) from the resource, with
@@ -560,52 +539,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void h
 }
 
 // ---------------------------------------------------------------------------
-// Conversion probe kernel
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bf16_probe_kernel(uint32_t first_bits,
-                                                         int64_t n,
-                                                         uint16_t* __restrict__ out) {
-  const int64_t k = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (k >= n) return;
-  const uint32_t bits = first_bits + static_cast<uint32_t>(k);
-  out[k] = to_bf16(__uint_as_float(bits));
-}
-
-// ---------------------------------------------------------------------------
-// Streaming probe (measurement only)
-// ---------------------------------------------------------------------------
-//
-// The bandwidth a plain stream with a given read:write byte mix reaches on
-// this GPU, with no arithmetic: the ceiling the kernels above are compared
-// with. One 64-lane block per unit; a unit reads R consecutive KiB of src
-// and writes W consecutive KiB of dst (each access instruction covers 1 KiB:
-// 64 lanes x 16 bytes), all loads issued before the first store, with the
-// cache policy of the kernel whose mix it stands for (nontemporal loads;
-// write-through stores for the forward's 4:1, nontemporal for the others).
-// The written words are the XOR of the unit's loaded words so that no load
-// is dead.
-constexpr int kProbeChunk = 1024;
-
-template <int R, int W, int POL>
-__global__ __launch_bounds__(64) void stream_probe_kernel(const uint8_t* __restrict__ src,
-                                                          uint8_t* __restrict__ dst) {
-  const int64_t u = blockIdx.x;
-  const uint32_t lane = threadIdx.x;
-  const Rsrc rs = make_rsrc(src + u * (R * kProbeChunk), R * kProbeChunk);
-  const Rsrc rd = make_rsrc(dst + u * (W * kProbeChunk), W * kProbeChunk);
-  u32x4 x[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-    x[r] = __builtin_amdgcn_raw_buffer_load_b128(rs, r * kProbeChunk + lane * 16, 0, kNontemporal);
-  u32x4 acc = x[0];
-#pragma unroll
-  for (int r = 1; r < R; ++r) acc ^= x[r];
-#pragma unroll
-  for (int w = 0; w < W; ++w)
-    __builtin_amdgcn_raw_buffer_store_b128(acc, rd, w * kProbeChunk + lane * 16, 0, POL);
-}
-
-// ---------------------------------------------------------------------------
 // Host side: error text, validation, launch policy
 // ---------------------------------------------------------------------------
 
@@ -965,139 +898,136 @@ mhc_status validate_bwd(const uint16_t* residual, const float* pre, const uint16
   return check_disjoint(outs, 2, ins, 3);
 }
 
-mhc_status launch_error(const char* what) {
-  const hipError_t e = hipGetLastError();
+// The status of one launch (the value hipExtLaunchKernel returned for it).
+mhc_status launch_status(hipError_t e, const char* what) {
   if (e != hipSuccess)
     return fail(MHC_ERROR_HIP, "%s launch failed: %s (%s)", what, hipGetErrorName(e),
                 hipGetErrorString(e));
   return ok();
 }
 
-// Kernel launches go through hipExtLaunchKernelGGL so that a caller's timing
-// events can be attached to the dispatch itself: the start event takes the
-// dispatch's start timestamp and the stop event its end timestamp, with no
-// extra marker packets between kernels. Null events give a plain launch.
+// Kernel launches go through launch_kernel (mhc_launch.h): each returns the
+// status of its own launch, and a caller's timing events can be attached to
+// the dispatch itself (the start event takes the dispatch's start timestamp
+// and the stop event its end timestamp, with no extra marker packets between
+// kernels). Null events give a plain launch.
 struct Events {
   hipEvent_t start, stop;
 };
 
 template <int V, int UPT, int N>
-void launch_fwd_t(const FwdPlan& pl, const uint16_t* residual, const float* pre, uint16_t* out,
-                  int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
-  hipExtLaunchKernelGGL(hagg_fwd_kernel<V, UPT, N>,
-                        dim3(pl.blocks_per_token, static_cast<uint32_t>(tokens)),
-                        dim3(pl.block), 0, stream, ev.start, ev.stop, 0, residual, pre, out, H,
-                        static_cast<uint32_t>(pl.block));
+hipError_t launch_fwd_t(const FwdPlan& pl, const uint16_t* residual, const float* pre, uint16_t* out,
+                        int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
+  return launch_kernel(hagg_fwd_kernel<V, UPT, N>,
+                       dim3(pl.blocks_per_token, static_cast<uint32_t>(tokens)), dim3(pl.block),
+                       stream, ev.start, ev.stop, residual, pre, out, H,
+                       static_cast<uint32_t>(pl.block));
 }
 
 // Instantiates only the batches the register budget allows (the plan never
 // asks for more).
 template <int V, int N>
-void launch_fwd_n(const FwdPlan& pl, const uint16_t* residual, const float* pre, uint16_t* out,
-                  int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
+hipError_t launch_fwd_n(const FwdPlan& pl, const uint16_t* residual, const float* pre, uint16_t* out,
+                        int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
   constexpr int kMax = fwd_max_upt(V, N);
   constexpr int kU2 = kMax < 2 ? kMax : 2;
   switch (pl.upt) {
-    case 1: launch_fwd_t<V, 1, N>(pl, residual, pre, out, tokens, H, stream, ev); break;
-    case 2: launch_fwd_t<V, kU2, N>(pl, residual, pre, out, tokens, H, stream, ev); break;
-    default: launch_fwd_t<V, kMax, N>(pl, residual, pre, out, tokens, H, stream, ev); break;
+    case 1: return launch_fwd_t<V, 1, N>(pl, residual, pre, out, tokens, H, stream, ev);
+    case 2: return launch_fwd_t<V, kU2, N>(pl, residual, pre, out, tokens, H, stream, ev);
+    default: return launch_fwd_t<V, kMax, N>(pl, residual, pre, out, tokens, H, stream, ev);
   }
 }
 
 template <int V>
-void launch_fwd_v(const FwdPlan& pl, const uint16_t* residual, const float* pre, uint16_t* out,
-                  int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
+hipError_t launch_fwd_v(const FwdPlan& pl, const uint16_t* residual, const float* pre, uint16_t* out,
+                        int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
   switch (pl.n) {
-    case 2: launch_fwd_n<V, 2>(pl, residual, pre, out, tokens, H, stream, ev); break;
-    case 8: launch_fwd_n<V, 8>(pl, residual, pre, out, tokens, H, stream, ev); break;
-    default: launch_fwd_n<V, 4>(pl, residual, pre, out, tokens, H, stream, ev); break;
+    case 2: return launch_fwd_n<V, 2>(pl, residual, pre, out, tokens, H, stream, ev);
+    case 8: return launch_fwd_n<V, 8>(pl, residual, pre, out, tokens, H, stream, ev);
+    default: return launch_fwd_n<V, 4>(pl, residual, pre, out, tokens, H, stream, ev);
   }
 }
 
 template <int V, int U, int S, bool ACC>
-void launch_bwd_t(const BwdPlan& pl, const uint16_t* residual, const float* pre,
-                  const uint16_t* grad_out, uint16_t* grad_residual, float* grad_pre,
-                  int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
+hipError_t launch_bwd_t(const BwdPlan& pl, const uint16_t* residual, const float* pre,
+                        const uint16_t* grad_out, uint16_t* grad_residual, float* grad_pre,
+                        int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
   const uint32_t blocks = static_cast<uint32_t>((tokens + pl.tpb - 1) / pl.tpb);
-  hipExtLaunchKernelGGL(hagg_bwd_kernel<V, U, S, ACC>, dim3(blocks, pl.n / S), dim3(kLanes), 0,
-                        stream, ev.start, ev.stop, 0, residual, grad_out, grad_residual, H,
-                        tokens, static_cast<uint32_t>(pl.ngroups), static_cast<int32_t>(pl.tpb),
-                        static_cast<int32_t>(pl.n), pre, grad_pre);
+  return launch_kernel(hagg_bwd_kernel<V, U, S, ACC>, dim3(blocks, pl.n / S), dim3(kLanes), stream,
+                       ev.start, ev.stop, residual, grad_out, grad_residual, H, tokens,
+                       static_cast<uint32_t>(pl.ngroups), static_cast<int32_t>(pl.tpb),
+                       static_cast<int32_t>(pl.n), pre, grad_pre);
 }
 
 // Instantiates only the batches the register budget allows (the plan never
 // asks for more): U is clamped to bwd_max_u at compile time.
 template <int V, int S, bool ACC>
-void launch_bwd_s(const BwdPlan& pl, const uint16_t* residual, const float* pre,
-                  const uint16_t* grad_out, uint16_t* grad_residual, float* grad_pre,
-                  int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
+hipError_t launch_bwd_s(const BwdPlan& pl, const uint16_t* residual, const float* pre,
+                        const uint16_t* grad_out, uint16_t* grad_residual, float* grad_pre,
+                        int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
   constexpr int kMaxU = bwd_max_u(V, S, ACC);
   constexpr int kU2 = kMaxU < 2 ? kMaxU : 2;
   switch (pl.U) {
-    case 1: launch_bwd_t<V, 1, S, ACC>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
-    case 2: launch_bwd_t<V, kU2, S, ACC>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
-    default: launch_bwd_t<V, kMaxU, S, ACC>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
+    case 1: return launch_bwd_t<V, 1, S, ACC>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
+    case 2: return launch_bwd_t<V, kU2, S, ACC>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
+    default: return launch_bwd_t<V, kMaxU, S, ACC>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
   }
 }
 
 template <int V, bool ACC>
-void launch_bwd_a(const BwdPlan& pl, const uint16_t* residual, const float* pre,
-                  const uint16_t* grad_out, uint16_t* grad_residual, float* grad_pre,
-                  int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
+hipError_t launch_bwd_a(const BwdPlan& pl, const uint16_t* residual, const float* pre,
+                        const uint16_t* grad_out, uint16_t* grad_residual, float* grad_pre,
+                        int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
   switch (pl.S) {
-    case 1: launch_bwd_s<V, 1, ACC>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
-    case 2: launch_bwd_s<V, 2, ACC>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
-    default: launch_bwd_s<V, 4, ACC>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
+    case 1: return launch_bwd_s<V, 1, ACC>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
+    case 2: return launch_bwd_s<V, 2, ACC>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
+    default: return launch_bwd_s<V, 4, ACC>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
   }
 }
 
 template <int V, int B, bool ACC>
-void launch_rows_t(const BwdPlan& pl, const uint16_t* residual, const float* pre,
-                   const uint16_t* grad_out, uint16_t* grad_residual, float* grad_pre,
-                   int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
+hipError_t launch_rows_t(const BwdPlan& pl, const uint16_t* residual, const float* pre,
+                         const uint16_t* grad_out, uint16_t* grad_residual, float* grad_pre,
+                         int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
   const int64_t rows = tokens * pl.n;
   const uint32_t blocks = static_cast<uint32_t>((rows + pl.rows_per_block - 1) / pl.rows_per_block);
-  hipExtLaunchKernelGGL(hagg_bwd_rows_kernel<V, B, ACC>, dim3(blocks),
-                        dim3(64 * pl.rows_per_block), 0, stream, ev.start, ev.stop, 0, residual,
-                        grad_out, grad_residual, H, rows,
-                        static_cast<uint32_t>(__builtin_ctz(static_cast<unsigned>(pl.n))),
-                        static_cast<uint32_t>(pl.rows_per_block),
-                        static_cast<uint32_t>(pl.ngroups), pre, grad_pre);
+  return launch_kernel(hagg_bwd_rows_kernel<V, B, ACC>, dim3(blocks), dim3(64 * pl.rows_per_block),
+                       stream, ev.start, ev.stop, residual, grad_out, grad_residual, H, rows,
+                       static_cast<uint32_t>(__builtin_ctz(static_cast<unsigned>(pl.n))),
+                       static_cast<uint32_t>(pl.rows_per_block),
+                       static_cast<uint32_t>(pl.ngroups), pre, grad_pre);
 }
 
 // Instantiates only the ring sizes the register budget allows.
 template <int V, bool ACC>
-void launch_rows_a(const BwdPlan& pl, const uint16_t* residual, const float* pre,
-                   const uint16_t* grad_out, uint16_t* grad_residual, float* grad_pre,
-                   int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
+hipError_t launch_rows_a(const BwdPlan& pl, const uint16_t* residual, const float* pre,
+                         const uint16_t* grad_out, uint16_t* grad_residual, float* grad_pre,
+                         int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
   constexpr int kMaxB = rows_max_b(V, ACC);
   if constexpr (kMaxB == 0) {
-    return;  // never planned: the row layout is not available for this shape
+    return hipErrorInvalidValue;  // never planned: no row layout for this shape
   } else {
     constexpr int kB8 = kMaxB < 8 ? kMaxB : 8;
     switch (pl.U) {
-      case 4: launch_rows_t<V, 4, ACC>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
-      case 8: launch_rows_t<V, kB8, ACC>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
-      default: launch_rows_t<V, kMaxB, ACC>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev); break;
+      case 4: return launch_rows_t<V, 4, ACC>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
+      case 8: return launch_rows_t<V, kB8, ACC>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
+      default: return launch_rows_t<V, kMaxB, ACC>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
     }
   }
 }
 
 template <int V>
-void launch_bwd_v(const BwdPlan& pl, const uint16_t* residual, const float* pre,
-                  const uint16_t* grad_out, uint16_t* grad_residual, float* grad_pre,
-                  int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
+hipError_t launch_bwd_v(const BwdPlan& pl, const uint16_t* residual, const float* pre,
+                        const uint16_t* grad_out, uint16_t* grad_residual, float* grad_pre,
+                        int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
   if (pl.layout == MHC_BWD_ROWS) {
     if (pl.acc)
-      launch_rows_a<V, true>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
-    else
-      launch_rows_a<V, false>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
-    return;
+      return launch_rows_a<V, true>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
+    return launch_rows_a<V, false>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
   }
   if (pl.acc)
-    launch_bwd_a<V, true>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
-  else
-    launch_bwd_a<V, false>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
+    return launch_bwd_a<V, true>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
+  return launch_bwd_a<V, false>(pl, residual, pre, grad_out, grad_residual, grad_pre, tokens, H, stream, ev);
 }
 
 // Events of the i-th of n launches of one call: start on the first, stop on
@@ -1124,20 +1054,20 @@ mhc_status run_fwd(const uint16_t* residual, const float* pre, uint16_t* out, in
   if (T == 0) return record_empty(ev, s);
   FwdPlan pl;
   if ((st = plan_fwd(residual, out, T, n, H, launch, &pl)) != MHC_SUCCESS) return st;
-  (void)hipGetLastError();  // start from a clean per-thread error state
   for (int64_t t0 = 0; t0 < T; t0 += pl.tokens_per_launch) {
     const int64_t m = (T - t0 < pl.tokens_per_launch) ? T - t0 : pl.tokens_per_launch;
     const Events e = chunk_events(ev, t0, t0 + m, T);
     const uint16_t* r = residual + t0 * n * H;
     const float* p = pre + n * t0;
     uint16_t* o = out + t0 * H;
+    hipError_t err;
     switch (pl.V) {
-      case 8: launch_fwd_v<8>(pl, r, p, o, m, H, s, e); break;
-      case 4: launch_fwd_v<4>(pl, r, p, o, m, H, s, e); break;
-      case 2: launch_fwd_v<2>(pl, r, p, o, m, H, s, e); break;
-      default: launch_fwd_v<1>(pl, r, p, o, m, H, s, e); break;
+      case 8: err = launch_fwd_v<8>(pl, r, p, o, m, H, s, e); break;
+      case 4: err = launch_fwd_v<4>(pl, r, p, o, m, H, s, e); break;
+      case 2: err = launch_fwd_v<2>(pl, r, p, o, m, H, s, e); break;
+      default: err = launch_fwd_v<1>(pl, r, p, o, m, H, s, e); break;
     }
-    if ((st = launch_error("h_aggregate forward")) != MHC_SUCCESS) return st;
+    if ((st = launch_status(err, "h_aggregate forward")) != MHC_SUCCESS) return st;
   }
   return ok();
 }
@@ -1155,7 +1085,6 @@ mhc_status run_bwd(const uint16_t* residual, const float* pre, const uint16_t* g
   const int64_t tokens_per_launch = pl.layout == MHC_BWD_ROWS
                                         ? pl.blocks_per_launch * pl.rows_per_block / n
                                         : pl.blocks_per_launch * pl.tpb;
-  (void)hipGetLastError();
   for (int64_t t0 = 0; t0 < T; t0 += tokens_per_launch) {
     const int64_t m = (T - t0 < tokens_per_launch) ? T - t0 : tokens_per_launch;
     const Events e = chunk_events(ev, t0, t0 + m, T);
@@ -1164,13 +1093,14 @@ mhc_status run_bwd(const uint16_t* residual, const float* pre, const uint16_t* g
     const uint16_t* g = grad_out + t0 * H;
     uint16_t* gr = grad_residual + t0 * n * H;
     float* gp = grad_pre + n * t0;
+    hipError_t err;
     switch (pl.V) {
-      case 8: launch_bwd_v<8>(pl, r, p, g, gr, gp, m, H, s, e); break;
-      case 4: launch_bwd_v<4>(pl, r, p, g, gr, gp, m, H, s, e); break;
-      case 2: launch_bwd_v<2>(pl, r, p, g, gr, gp, m, H, s, e); break;
-      default: launch_bwd_v<1>(pl, r, p, g, gr, gp, m, H, s, e); break;
+      case 8: err = launch_bwd_v<8>(pl, r, p, g, gr, gp, m, H, s, e); break;
+      case 4: err = launch_bwd_v<4>(pl, r, p, g, gr, gp, m, H, s, e); break;
+      case 2: err = launch_bwd_v<2>(pl, r, p, g, gr, gp, m, H, s, e); break;
+      default: err = launch_bwd_v<1>(pl, r, p, g, gr, gp, m, H, s, e); break;
     }
-    if ((st = launch_error("h_aggregate backward")) != MHC_SUCCESS) return st;
+    if ((st = launch_status(err, "h_aggregate backward")) != MHC_SUCCESS) return st;
   }
   return ok();
 }
@@ -1357,65 +1287,6 @@ mhc_status mhc_h_aggregate_plan_bwd_n(const uint16_t* residual, const float* pre
     return fail(MHC_ERROR_INVALID_VALUE, "accumulate must be 0 or 1");
   return plan_bwd_query(residual, pre, grad_out, grad_residual, grad_pre, T, n, H,
                         accumulate == 1, launch, plan, grid_blocks);
-}
-
-mhc_status mhc_bf16_rne_probe(uint32_t first_bits, int64_t n, uint16_t* out, void* stream) {
-  if (n < 0 || n > (int64_t(1) << 32))
-    return fail(MHC_ERROR_INVALID_VALUE, "n must be in [0, 2^32]");
-  if (n == 0) return ok();
-  mhc_status st = check_ptr(out, 2, "out");
-  if (st != MHC_SUCCESS) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  (void)hipGetLastError();
-  const int64_t per_launch = int64_t(1) << 30;  // work-items per dispatch
-  for (int64_t k0 = 0; k0 < n; k0 += per_launch) {
-    const int64_t m = (n - k0 < per_launch) ? n - k0 : per_launch;
-    const uint32_t blocks = static_cast<uint32_t>((m + 255) / 256);
-    bf16_probe_kernel<<<dim3(blocks), dim3(256), 0, s>>>(
-        first_bits + static_cast<uint32_t>(k0), m, out + k0);
-    if ((st = launch_error("bf16 probe")) != MHC_SUCCESS) return st;
-  }
-  return ok();
-}
-
-mhc_status mhc_stream_probe(const void* src, int64_t src_bytes, void* dst, int64_t dst_bytes,
-                            int32_t reads, int32_t writes, void* stream, void* start_event,
-                            void* stop_event) {
-  const int mix = reads * 100 + writes;
-  if (mix != 101 && mix != 401 && mix != 504 && mix != 904)
-    return fail(MHC_ERROR_INVALID_VALUE,
-                "reads:writes must be 1:1, 4:1, 5:4 or 9:4 (got %d:%d)", reads, writes);
-  if (src_bytes < 0 || dst_bytes < 0 || src_bytes % (int64_t(reads) * kProbeChunk) != 0)
-    return fail(MHC_ERROR_INVALID_VALUE,
-                "src_bytes must be a non-negative multiple of reads KiB (got %lld)",
-                (long long)src_bytes);
-  const int64_t units = src_bytes / (int64_t(reads) * kProbeChunk);
-  if (dst_bytes != units * writes * kProbeChunk)
-    return fail(MHC_ERROR_INVALID_VALUE,
-                "dst_bytes must be writes KiB per unit of src (want %lld, got %lld)",
-                (long long)(units * writes * kProbeChunk), (long long)dst_bytes);
-  if (units > 0x7FFFFFFF)
-    return fail(MHC_ERROR_INVALID_VALUE, "too many units (%lld)", (long long)units);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const Events ev{static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
-  if (units == 0) return record_empty(ev, s);
-  mhc_status st;
-  if ((st = check_ptr(src, 16, "src")) != MHC_SUCCESS) return st;
-  if ((st = check_ptr(dst, 16, "dst")) != MHC_SUCCESS) return st;
-  const Range in{reinterpret_cast<uintptr_t>(src), reinterpret_cast<uintptr_t>(src) + src_bytes, "src"};
-  const Range out{reinterpret_cast<uintptr_t>(dst), reinterpret_cast<uintptr_t>(dst) + dst_bytes, "dst"};
-  if (overlap(in, out)) return fail(MHC_ERROR_ALIASING, "dst overlaps src");
-  (void)hipGetLastError();
-  const dim3 grid(static_cast<uint32_t>(units));
-  const auto* sp = static_cast<const uint8_t*>(src);
-  auto* dp = static_cast<uint8_t*>(dst);
-  switch (mix) {
-    case 101: hipExtLaunchKernelGGL(stream_probe_kernel<1, 1, kNontemporal>, grid, dim3(64), 0, s, ev.start, ev.stop, 0, sp, dp); break;
-    case 401: hipExtLaunchKernelGGL(stream_probe_kernel<4, 1, kWriteThrough>, grid, dim3(64), 0, s, ev.start, ev.stop, 0, sp, dp); break;
-    case 504: hipExtLaunchKernelGGL(stream_probe_kernel<5, 4, kNontemporal>, grid, dim3(64), 0, s, ev.start, ev.stop, 0, sp, dp); break;
-    default: hipExtLaunchKernelGGL(stream_probe_kernel<9, 4, kNontemporal>, grid, dim3(64), 0, s, ev.start, ev.stop, 0, sp, dp); break;
-  }
-  return launch_error("stream probe");
 }
 
 }  // extern "C"

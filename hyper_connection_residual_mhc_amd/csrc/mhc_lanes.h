@@ -23,6 +23,11 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
                                            static_cast<int>(bytes), kRsrcFormat);
 }
 
+// Cache-policy bits of a buffer access (the `aux` operand).
+constexpr int kNontemporal = 2;   // bit 1, nt: streamed bytes, touched once
+constexpr int kCached = 0;        // default policy: kept for other readers
+constexpr int kWriteThrough = 16; // bit 4, sc1: device-scope store, written through the L2
+
 // Lane j (< OFF) of a wave receives x from lane j + OFF; other lanes receive
 // values that are never read. On gfx950: permlane32_swap brings the upper
 // half-wave down, permlane16_swap the odd 16-lane rows onto the even ones,

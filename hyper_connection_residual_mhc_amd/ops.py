@@ -216,41 +216,6 @@ def mhc_h_aggregate_bwd_n(residual: torch.Tensor, pre: torch.Tensor, grad_out: t
     return grad_residual, grad_pre
 
 
-def mhc_bf16_rne_probe(first_bits: int, out: torch.Tensor,
-                       stream: torch.cuda.Stream | None = None) -> torch.Tensor:
-    """out[k] = device bf16 rounding of the fp32 pattern first_bits + k (out: int16/uint16)."""
-    if out.device.type != "cuda" or out.dtype not in (torch.int16, torch.uint16, torch.bfloat16):
-        raise TypeError("out must be a 16-bit GPU tensor")
-    if not out.is_contiguous():
-        raise ValueError("out must be contiguous")
-    with torch.cuda.device(out.device):
-        st = _lib.lib().mhc_bf16_rne_probe(int(first_bits) & 0xFFFFFFFF, out.numel(),
-                                           out.data_ptr(), _stream_handle(out.device, stream))
-    check(st)
-    return out
-
-
-def mhc_stream_probe(src: torch.Tensor, dst: torch.Tensor, reads: int, writes: int,
-                     stream: torch.cuda.Stream | None = None, start_event=None,
-                     stop_event=None) -> torch.Tensor:
-    """Streaming probe (measurement only): per unit, read `reads` consecutive
-    KiB of src and write `writes` KiB of dst with no arithmetic (see the
-    header for the allowed mixes). Events are raw hipEvent_t handles or None."""
-    for name, x in (("src", src), ("dst", dst)):
-        if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
-            raise TypeError(f"{name} must be a GPU tensor")
-        if not x.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    nbytes = lambda x: x.numel() * x.element_size()
-    with torch.cuda.device(dst.device):
-        st = _lib.lib().mhc_stream_probe(src.data_ptr(), nbytes(src), dst.data_ptr(), nbytes(dst),
-                                         int(reads), int(writes),
-                                         _stream_handle(dst.device, stream),
-                                         start_event, stop_event)
-    check(st)
-    return dst
-
-
 def _addr(x) -> int:
     if x is None:
         return 0

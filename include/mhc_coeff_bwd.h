@@ -23,15 +23,17 @@
  *     z[:, 2n:m] -> Sinkhorn normalisation (its backward supplies grad_res)
  * and, per row r (R rows; every row is one token of one batch entry):
  *     d[r,j] = grad_pre[r,j]  * (pre[r,j]  * (1 - pre[r,j]))                j <  n
- *     d[r,j] = grad_post[r,i] * (post[r,i] * (1 - post[r,i] * inv_c))       i = j - n
+ *     d[r,j] = grad_post[r,i] * (post[r,i] * (1 - post[r,i] / c))           i = j - n
  *     d[r,j] = grad_res[r,j-2n]                                             j >= 2n
  *     grad_mix[r,j] = alpha[k(j)] * d[r,j]
  *     e[r,k]        = sum over j of group k, ascending, from +0.0, of d[r,j] * mix[r,j]
  *     grad_b[j]     = row_sum of d[:,j]
  *     grad_alpha[k] = row_sum of e[:,k]
- * inv_c is 1/c rounded to fp32 once (on the host). Every product, sum and
- * difference is one fp32 round-to-nearest-even operation in exactly the
- * nesting written, never fused.
+ * post[r,i] / c is the post gate's sigmoid, so the post derivative is
+ * c * s * (1 - s) written in the saved output. Every product, quotient, sum
+ * and difference is one fp32 operation rounded to nearest even (the
+ * quotient correctly rounded) in exactly the nesting written; products and
+ * sums are never fused.
  *
  * row_sum (fixed; depends only on R):
  *   1. rows are cut into chunks of 64 consecutive rows (rows past R count as
@@ -74,9 +76,10 @@
  * smaller than required give MHC_ERROR_INVALID_VALUE; any overlap between an
  * output (the workspace counts as one) and an input or another output gives
  * MHC_ERROR_ALIASING. On either error nothing is launched and nothing is
- * written. A failed launch gives MHC_ERROR_HIP. mhc_coeff_last_error_message
- * describes the most recent failure on the calling thread. The status codes
- * are those of mhc_h_aggregate.h.
+ * written. A failed launch gives MHC_ERROR_HIP (the status of that launch;
+ * the thread's HIP last-error state is neither read nor cleared).
+ * mhc_coeff_last_error_message describes the most recent failure on the
+ * calling thread. The status codes are those of mhc_h_aggregate.h.
  */
 #ifndef MHC_COEFF_BWD_H
 #define MHC_COEFF_BWD_H
@@ -89,7 +92,7 @@
 extern "C" {
 #endif
 
-#define MHC_COEFF_ABI_VERSION 2
+#define MHC_COEFF_ABI_VERSION 3
 
 /* Rows per first-stage chunk of row_sum. */
 #define MHC_COEFF_CHUNK 64

@@ -53,7 +53,10 @@
  *     int64 give MHC_ERROR_INVALID_VALUE. Any overlap between an output and
  *     an input, or between the two backward outputs, gives
  *     MHC_ERROR_ALIASING. On either error nothing is launched and no output
- *     is touched. A failed kernel launch gives MHC_ERROR_HIP.
+ *     is touched. A failed kernel launch gives MHC_ERROR_HIP (with the
+ *     status of that launch itself; the library never reads or clears the
+ *     thread's HIP last-error state, so an error the caller had pending is
+ *     still pending after the call).
  *   - A misaligned or odd-H buffer is not an error: it only narrows the
  *     vector width, which never changes a result bit.
  *   - mhc_last_error_message() returns a text describing the most recent
@@ -68,7 +71,7 @@
 extern "C" {
 #endif
 
-#define MHC_ABI_VERSION 3
+#define MHC_ABI_VERSION 4
 
 /* Hyper-connection expansion rate of the page's operation (Summary: residual
  * [T, 4, H]). The *_n entry points below also take 2 and 8. */
@@ -303,41 +306,6 @@ mhc_status mhc_h_aggregate_plan_bwd_acc(const uint16_t* residual,
                                         const float* grad_pre, int64_t T,
                                         int64_t H, const mhc_launch* launch,
                                         mhc_launch* plan, int64_t* grid_blocks);
-
-/*
- * Conversion probe: out[k] = bf16 bits of the fp32 value whose bit pattern
- * is (first_bits + k) mod 2^32, for k in [0, n), rounded by the same device
- * routine the kernels use for every bf16 result (round to nearest even,
- * the single output rounding of Batch invariance).
- * Lets tests compare the device rounding with an independent one over any
- * range of fp32 patterns, including all 2^32. out: [n] uint16, device.
- * 0 <= n <= 2^32.
- */
-mhc_status mhc_bf16_rne_probe(uint32_t first_bits, int64_t n, uint16_t* out,
-                              void* stream);
-
-/*
- * Streaming probe (measurement utility, not part of the operation): a kernel
- * that only moves bytes, with the read:write mix of one of the kernels
- * above and no arithmetic, so that their time can be compared with what a
- * plain stream of the same bytes takes on this GPU. Per unit it reads
- * `reads` consecutive KiB of src and writes `writes` consecutive KiB of dst
- * (one 64-lane block per unit, all loads before the first store; the
- * written words are the XOR of the unit's loaded 16-byte vectors, lane by
- * lane, repeated `writes` times), with the cache policy of the kernel whose
- * mix it stands for.
- *   reads:writes  1:1 (copy), 4:1 (forward: 8H read, 2H written),
- *                 5:4 (backward: 10H read, 8H written),
- *                 9:4 (accumulating backward: 18H read, 8H written).
- *   src: src_bytes device bytes, 16-byte aligned, a multiple of reads KiB;
- *   dst: exactly (src_bytes / (reads KiB)) * writes KiB, 16-byte aligned,
- *   disjoint from src (else MHC_ERROR_ALIASING). start_event / stop_event
- *   (hipEvent_t or NULL) are attached to the dispatch as in the _timed calls.
- *   src_bytes == 0 launches nothing and records the events.
- */
-mhc_status mhc_stream_probe(const void* src, int64_t src_bytes, void* dst,
-                            int64_t dst_bytes, int32_t reads, int32_t writes,
-                            void* stream, void* start_event, void* stop_event);
 
 #ifdef __cplusplus
 }

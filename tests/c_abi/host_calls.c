@@ -61,8 +61,6 @@ int main(void) {
   CHECK(mhc_h_aggregate_fwd(residual, pre, (uint16_t*)residual, T, H, NULL) ==
         MHC_ERROR_ALIASING);
   CHECK(mhc_h_aggregate_bwd(NULL, NULL, NULL, NULL, NULL, 0, H, NULL) == MHC_SUCCESS);
-  CHECK(mhc_stream_probe((const void*)base, 5 * 1024, out, 4 * 1024, 3, 4, NULL, NULL, NULL) ==
-        MHC_ERROR_INVALID_VALUE);
 
   /* the coefficient backward epilogue's library */
   {

@@ -44,10 +44,10 @@ def pytest_collection_modifyitems(config, items):
 
 @pytest.fixture(scope="session")
 def built_library():
-    """Path of the shared library; builds it once if it is not there."""
+    """Path of the shared library; builds the libraries once if one is
+    missing or was built from other sources than the tree's."""
     from hyper_connection_residual_mhc_amd import _build
-    if not _build.library_is_built():
-        _build.build_library()
+    _build.ensure_built()
     return _build.LIB_PATH
 
 

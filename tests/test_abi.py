@@ -254,30 +254,6 @@ def test_backward_plan_and_overrides(lib):
     assert plan["vec_width"] == 1 and plan["layout"] == ROWS and plan["units_per_thread"] == 4
 
 
-def test_probe_rejects_bad_sizes(lib):
-    assert lib.mhc_bf16_rne_probe(0, -1, 1024, None) == MHC_ERROR_INVALID_VALUE
-    assert lib.mhc_bf16_rne_probe(0, (1 << 32) + 1, 1024, None) == MHC_ERROR_INVALID_VALUE
-    assert lib.mhc_bf16_rne_probe(0, 0, 0, None) == MHC_SUCCESS
-    assert lib.mhc_bf16_rne_probe(0, 16, 0, None) == MHC_ERROR_INVALID_VALUE
-    assert lib.mhc_bf16_rne_probe(0, 16, 1025, None) == MHC_ERROR_INVALID_VALUE
-
-
-def test_stream_probe_rejects_bad_arguments_before_any_hip_call(lib):
-    KiB = 1024
-    src, dst = BASE, BASE + GiB
-    probe = lib.mhc_stream_probe
-    for reads, writes in ((2, 1), (5, 5), (0, 1), (4, 4), (-5, 4)):
-        assert probe(src, 20 * KiB, dst, 16 * KiB, reads, writes, None, None,
-                     None) == MHC_ERROR_INVALID_VALUE, (reads, writes)
-    assert probe(src, 5 * KiB + 16, dst, 4 * KiB, 5, 4, None, None, None) == MHC_ERROR_INVALID_VALUE
-    assert probe(src, 10 * KiB, dst, 4 * KiB, 5, 4, None, None, None) == MHC_ERROR_INVALID_VALUE
-    assert probe(src, -5 * KiB, dst, 4 * KiB, 5, 4, None, None, None) == MHC_ERROR_INVALID_VALUE
-    assert probe(src, 10 * KiB, src + 4 * KiB, 8 * KiB, 5, 4, None, None,
-                 None) == MHC_ERROR_ALIASING
-    assert probe(src + 8, 5 * KiB, dst, 4 * KiB, 5, 4, None, None, None) == MHC_ERROR_INVALID_VALUE
-    assert probe(0, 0, 0, 0, 9, 4, None, None, None) == MHC_SUCCESS
-
-
 def test_package_exports_every_binding_name():
     import hyper_connection_residual_mhc_amd as pkg
     from hyper_connection_residual_mhc_amd import coeff
@@ -319,11 +295,49 @@ def test_compute_call_with_invalid_args_returns_before_any_hip_call(lib):
                                          None) == MHC_ERROR_INVALID_VALUE
 
 
-def test_missing_library_raises_import_error(monkeypatch, tmp_path):
-    monkeypatch.setattr(_lib, "_lib", None)
-    monkeypatch.setattr(_lib, "LIB_PATH", Path(tmp_path) / "absent.so")
+def test_missing_library_raises_import_error(tmp_path):
     with pytest.raises(ImportError, match="missing"):
-        _lib.lib()
+        _lib.open_checked(Path(tmp_path) / "absent.so", _build.SRC, _lib.SIGNATURES,
+                          "mhc_abi_version", _lib.MHC_ABI_VERSION)
+
+
+def test_stale_library_is_refused(built_library, tmp_path):
+    """A library whose recorded digest does not match the sources in the tree
+    (or that has no record) is not loaded; the same file with a matching
+    record is."""
+    copy = Path(tmp_path) / built_library.name
+    copy.write_bytes(built_library.read_bytes())
+    info = _build.build_info_path(copy)
+    args = (copy, _build.SRC, _lib.SIGNATURES, "mhc_abi_version", _lib.MHC_ABI_VERSION)
+    with pytest.raises(ImportError, match="other sources"):
+        _lib.open_checked(*args)                                    # no record
+    info.write_text('{"source_digest": "' + "0" * 64 + '"}')
+    with pytest.raises(ImportError, match="other sources"):
+        _lib.open_checked(*args)                                    # stale record
+    info.write_text('{"source_digest": "' + _build.source_digest(_build.SRC) + '"}')
+    assert _lib.open_checked(*args).mhc_abi_version() == _lib.MHC_ABI_VERSION
+
+
+def test_source_digest_follows_sources_headers_and_flags(monkeypatch, tmp_path):
+    """The digest changes with the source, any header and the flags, and
+    does not depend on where the repository sits."""
+    base = _build.source_digest(_build.SRC)
+    assert base == _build.source_digest(_build.SRC)
+    assert base != _build.source_digest(_build.COEFF_SRC)
+    assert base != _build.source_digest(_build.SRC, ["-DX=1"])
+    monkeypatch.setitem(_build.SOURCE_FLAGS, _build.SRC, [])
+    assert base != _build.source_digest(_build.SRC)
+    monkeypatch.undo()
+    src = Path(tmp_path) / _build.SRC.name
+    src.write_bytes(_build.SRC.read_bytes() + b"\n")
+    assert base != _build.source_digest(src)
+    assert all(str(_build.REPO_DIR) not in f or f == str(_build.INCLUDE_DIR)
+               for f in _build.COMMON_FLAGS)
+
+
+def test_built_libraries_match_the_tree(built_library):
+    """The libraries in the tree were built from the current sources."""
+    assert _build.library_is_built()
 
 
 def test_accumulating_backward_plan(lib):

@@ -11,15 +11,20 @@ own gfx950 machine code (compiled here; no GPU needed).
 * no store of more than 8 bytes is followed at once by an instruction that
   overwrites its data registers (gfx950 reads such data over several cycles;
   an immediate overwrite was measured to corrupt the last lanes' data);
-* no scalar memory writes, and no division in the coefficient kernels;
+* no scalar memory writes;
+* no division in the h_aggregate kernels; in the coefficient kernels the one
+  fp32 division of the post gate (post / c) is the compiler's correctly
+  rounded expansion, and the fused multiply-adds of that expansion are the
+  only fused operations in them;
 * no __builtin_bit_cast of a vector element in the kernel sources (this
   toolchain turned `__builtin_bit_cast(float, v[e])` on a 4-wide vector into
   a copy of element 0 and shrank the vector load to one dword; the
   kernels copy an element into a scalar first);
 * the product path never imports the oracle.
 
-Both library sources are checked (the h_aggregate kernels and the
-coefficient-backward epilogue's kernels).
+All three library sources are checked (the h_aggregate kernels, the
+coefficient-backward epilogue's kernels and the measurement library's
+probes).
 """
 
 from __future__ import annotations
@@ -32,13 +37,17 @@ import pytest
 
 from hyper_connection_residual_mhc_amd import _build
 
+# Fused or packed fp32 instructions, in any encoding (_e32, _e64, _dpp, _sdwa).
 FORBIDDEN = re.compile(
     r"\b(v_fma_f32|v_fmac_f32|v_mad_f32|v_mac_f32|v_fma_legacy_f32|v_fmac_legacy_f32|"
     r"v_mad_legacy_f32|v_fma_mix\w*|v_mad_mix\w*|v_dot2\w*|v_pk_fma_f32|v_pk_mul_f32|"
-    r"v_pk_add_f32|v_fma_f64|v_fma_f16|v_pk_fma_f16)\b")
+    r"v_pk_add_f32|v_fma_f64|v_fma_f16|v_pk_fma_f16)(_e32|_e64|_dpp|_sdwa)?\b")
 
 
-@pytest.fixture(scope="module", params=[_build.SRC, _build.COEFF_SRC], ids=lambda p: p.stem)
+SOURCES = [_build.SRC, _build.COEFF_SRC, _build.PROBE_SRC]
+
+
+@pytest.fixture(scope="module", params=SOURCES, ids=lambda p: p.stem)
 def asm(request, tmp_path_factory) -> str:
     out = tmp_path_factory.mktemp("asm") / f"{request.param.stem}.s"
     return _build.device_asm(out, src=request.param).read_text()
@@ -57,12 +66,17 @@ def test_kernels_present(asm):
     if any("coeff_" in n for n in names):
         assert sum("coeff_partial_kernel" in n for n in names) == 3
         assert sum("coeff_reduce_kernel" in n for n in names) == 1
-        assert not any("hagg_" in n for n in names)
+        assert not any("hagg_" in n or "probe" in n for n in names)
+        return
+    if any("probe" in n for n in names):
+        assert sum("bf16_probe_kernel" in n for n in names) == 1
+        assert sum("stream_probe_kernel" in n for n in names) == 6
+        assert not any("hagg_" in n or "coeff_" in n for n in names)
         return
     assert any("hagg_fwd_kernel" in n for n in names)
     assert any("hagg_bwd_kernel" in n for n in names)
-    assert any("bf16_probe_kernel" in n for n in names)
-    assert sum("stream_probe_kernel" in n for n in names) == 4
+    assert any("hagg_bwd_rows_kernel" in n for n in names)
+    assert not any("probe" in n or "coeff_" in n for n in names)
 
 
 def test_no_scalar_memory_writes(asm):
@@ -72,10 +86,79 @@ def test_no_scalar_memory_writes(asm):
     assert not hits, sorted(set(hits))
 
 
+DIVISION_FMA = re.compile(r"^\s*(v_fma_f32|v_fmac_f32\w*)\b")
+
+
+def division_spans(ins: list[str]) -> list[tuple[int, int]]:
+    """[first, last] instruction indices of each run of fp32 divisions: from
+    a v_div_scale_f32 that starts one to the v_div_fixup_f32 that completes
+    the last division begun in the run (each division has two div_scale and
+    one div_fixup; the compiler may interleave several)."""
+    spans, start, scales, fixups = [], None, 0, 0
+    for i, line in enumerate(ins):
+        op = line.split()[0] if line.split() else ""
+        if op == "v_div_scale_f32":
+            if start is None:
+                start, scales, fixups = i, 0, 0
+            scales += 1
+        elif op == "v_div_fixup_f32" and start is not None:
+            fixups += 1
+            if 2 * fixups == scales:
+                spans.append((start, i))
+                start = None
+    assert start is None, "unterminated division"
+    return spans
+
+
+def fused_outside_divisions(body: str) -> list[str]:
+    """Forbidden instructions of a kernel, except the fused multiply-adds of
+    the division expansion (five per division, inside its span)."""
+    ins = instructions(body)
+    spans = division_spans(ins)
+    inside = set()
+    for a, b in spans:
+        fmas = [i for i in range(a, b + 1) if DIVISION_FMA.match(ins[i])]
+        divs = sum(1 for i in range(a, b + 1) if ins[i].split()[0] == "v_div_fixup_f32")
+        assert len(fmas) == 5 * divs, (a, b, len(fmas), divs)
+        inside.update(fmas)
+    return [ins[i].strip() for i in range(len(ins))
+            if i not in inside and FORBIDDEN.search(ins[i])]
+
+
 def test_no_fused_or_packed_float_ops(asm):
     for name, body in kernel_blocks(asm).items():
-        hits = FORBIDDEN.findall(body)
+        if "coeff_" in name:
+            hits = fused_outside_divisions(body)
+        else:
+            hits = [m.group(0) for m in FORBIDDEN.finditer(body)]
         assert not hits, f"{name}: {sorted(set(hits))}"
+
+
+def test_forbidden_pattern_covers_every_encoding():
+    for text in ("v_fma_f32 v1, v2, v3, v4", "v_fmac_f32_e32 v2, v4, v2",
+                 "v_fmac_f32_e64 v2, v4, v2", "v_mac_f32_e32 v1, v2, v3",
+                 "v_pk_mul_f32 v[0:1], v[2:3], v[4:5]", "v_dot2_f32_bf16 v1, v2, v3, v4",
+                 "v_fma_mix_f32 v1, v2, v3, v4"):
+        assert FORBIDDEN.search(text), text
+    for text in ("v_mul_f32_e32 v1, v2, v3", "v_add_f32_e32 v1, v2, v3",
+                 "v_cvt_pk_bf16_f32 v1, v2, v3", "v_div_fmas_f32 v1, v2, v3, v4"):
+        assert not FORBIDDEN.search(text), text
+
+
+def test_division_scan_allows_only_the_expansion():
+    """The scan accepts a division's own fused steps and flags any other."""
+    div = ["v_div_scale_f32 v1, s[2:3], s10, s10, v0", "v_rcp_f32_e32 v2, v1",
+           "v_div_scale_f32 v3, vcc, v0, s10, v0", "v_fma_f32 v4, -v1, v2, 1.0",
+           "v_fmac_f32_e32 v2, v4, v2", "v_mul_f32_e32 v4, v3, v2",
+           "v_fma_f32 v5, -v1, v4, v3", "v_fmac_f32_e32 v4, v5, v2",
+           "v_fma_f32 v1, -v1, v4, v3", "v_div_fmas_f32 v1, v1, v2, v4",
+           "v_div_fixup_f32 v1, v1, s10, v0"]
+    body = "\n".join("\t" + x for x in div)
+    assert fused_outside_divisions(body) == []
+    assert fused_outside_divisions(body + "\n\tv_fma_f32 v7, v1, v2, v3") == ["v_fma_f32 v7, v1, v2, v3"]
+    assert fused_outside_divisions("\tv_fmac_f32_e32 v2, v4, v2") == ["v_fmac_f32_e32 v2, v4, v2"]
+    with pytest.raises(AssertionError):
+        fused_outside_divisions("\n".join("\t" + x for x in div[:4] + div[9:]))
 
 
 def test_separate_fp32_mul_and_add_present(asm):
@@ -91,11 +174,18 @@ def test_bf16_results_use_rne_pack_conversion(asm):
         assert "v_cvt_pk_bf16_f32" in body, name
 
 
-def test_no_division_in_the_coefficient_kernels(asm):
-    """The post gate multiplies by the host-rounded reciprocal of its scale."""
+def test_divisions_only_where_the_operation_has_one(asm):
+    """The h_aggregate kernels divide nothing; the coefficient chunk stage
+    divides once per post column (post / c), the reduction never."""
     for name, body in kernel_blocks(asm).items():
-        if "coeff_" in name:
+        fixups = len(re.findall(r"^\s*v_div_fixup_f32\b", body, flags=re.M))
+        if "hagg_" in name:
             assert not re.search(r"\bv_(div_\w+|rcp_\w+)", body), name
+        elif "coeff_reduce" in name:
+            assert fixups == 0, name
+        elif "coeff_" in name:
+            n = int(re.search(r"kernelILi(\d+)E", name).group(1))
+            assert fixups == n, (name, fixups)
 
 
 STORE_WIDE = re.compile(
@@ -179,7 +269,7 @@ def test_no_scratch_spills(asm):
     assert "scratch_store" not in asm and "buffer_store_dword off" not in asm
 
 
-@pytest.mark.parametrize("src", [_build.SRC, _build.COEFF_SRC], ids=lambda p: p.stem)
+@pytest.mark.parametrize("src", SOURCES, ids=lambda p: p.stem)
 def test_fast_math_build_is_refused(tmp_path, src):
     cmd = [_build.hipcc(), *_build.COMMON_FLAGS, "-ffast-math", "--cuda-device-only", "-S",
            str(src), "-o", str(tmp_path / "fm.s")]
@@ -194,7 +284,7 @@ def test_build_flags_fix_the_contract():
     assert "-ffp-contract=off" in flags
     assert "-packed-fp32-ops" in flags
     assert "fast-math" not in flags and "-ffast" not in flags
-    for path in (_build.SRC, _build.COEFF_SRC):
+    for path in SOURCES:
         assert "#pragma clang fp contract(off)" in path.read_text(), path
 
 

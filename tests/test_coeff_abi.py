@@ -133,9 +133,12 @@ def test_size_and_scale_rules(lib):
     assert v(n=3) == MHC_ERROR_INVALID_VALUE
     assert v(R=-1) == MHC_ERROR_INVALID_VALUE
     assert v(R=(1 << 28) + 1) == MHC_ERROR_INVALID_VALUE
-    for c in (0.0, -2.0, float("inf"), float("nan"), 1e-45):
+    for c in (0.0, -0.0, -2.0, float("inf"), float("nan"), -1e-45):
         assert v(c=c) == MHC_ERROR_INVALID_VALUE, c
-    assert v(c=3.0) == MHC_SUCCESS and v(c=0.5) == MHC_SUCCESS
+    # any finite positive scale, down to the smallest subnormal (post / c is
+    # a division, so no reciprocal has to be representable)
+    for c in (3.0, 0.5, 1e-45, 3e38):
+        assert v(c=c) == MHC_SUCCESS, c
     a = Args(lib, 100, 4, ws_extra=-4)
     assert lib.mhc_coeff_bwd_validate(*a.tuple()) == MHC_ERROR_INVALID_VALUE
     assert b"workspace" in lib.mhc_coeff_last_error_message()

@@ -65,6 +65,27 @@ def test_other_post_scales(device, c):
     _check(make_coeff_inputs(1000, 4, seed=3, post_scale=c), c, device, f"c={c}")
 
 
+@pytest.mark.parametrize("launches", [1, 2])
+@pytest.mark.parametrize("c", [3.0, 0.75, 7.0, 1.0 / 3.0, 5e-39, 1e30])
+def test_post_quotient_is_correctly_rounded(device, c, launches):
+    """Post values close to the scale, where s = post / c is near 1 and
+    1 - s is exact, so an error of one unit in the last place of the
+    quotient changes the derivative; plus post values down into the
+    subnormal range. Non-power-of-two scales (and a subnormal one) make the
+    quotient inexact. The kernel's division must give the oracle's
+    correctly rounded quotient every time."""
+    say(f"coeff bwd quotient c={c} launches={launches}")
+    R, n = 4096, 8
+    host = make_coeff_inputs(R, n, seed=77, post_scale=1.0)
+    rng = np.random.default_rng(78)
+    cf = np.float32(c)
+    near = cf * (1.0 - rng.uniform(0.0, 2.0 ** -8, (R // 2, n)))
+    wide = cf * np.exp2(-rng.uniform(0.0, 140.0, (R - R // 2, n)))
+    host["post"] = np.ascontiguousarray(np.concatenate([near, wide]).astype(np.float32))
+    host["grad_post"][:] = 1.0
+    _check(host, float(cf), device, f"quotient c={c}", launches=launches)
+
+
 @pytest.mark.parametrize("launches", [0, 1])
 def test_large_batch(device, launches):
     """2^20 rows: 16,384 chunks, past the one-launch policy limit (the

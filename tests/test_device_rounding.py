@@ -18,7 +18,7 @@ import pytest
 import torch
 
 from gpu_util import say
-from hyper_connection_residual_mhc_amd import ops
+from hyper_connection_residual_mhc_amd import probes
 from oracle import h_aggregate as O
 
 pytestmark = pytest.mark.gpu
@@ -32,7 +32,7 @@ def test_device_bf16_rounding_all_patterns(device):
     for c in range((1 << 16) // ROWS_PER_CHUNK):
         hi0 = c * ROWS_PER_CHUNK
         say(f"rounding probe rows {hi0:#06x}..{hi0 + ROWS_PER_CHUNK - 1:#06x}")
-        ops.mhc_bf16_rne_probe(hi0 << 16, out)
+        probes.mhc_bf16_rne_probe(hi0 << 16, out)
         rows = out.view(ROWS_PER_CHUNK, 1 << 16)
         hi = np.arange(hi0, hi0 + ROWS_PER_CHUNK, dtype=np.uint32)
         exp_all_ones = (hi & 0x7F80) == 0x7F80          # Inf / NaN rows

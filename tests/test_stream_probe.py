@@ -1,7 +1,8 @@
-"""The streaming probe (a measurement utility beside the operation) moves
+"""The streaming probe (measurement library, beside the operation) moves
 exactly the bytes its header describes: per unit, `reads` KiB in and
 `writes` KiB out, each written 16-byte vector the XOR of the unit's loaded
-vectors at that lane, and nothing written outside dst."""
+vectors at that lane (a write-only unit: its unit index), and nothing
+written outside dst."""
 
 from __future__ import annotations
 
@@ -10,7 +11,7 @@ import pytest
 import torch
 
 from gpu_util import say
-from hyper_connection_residual_mhc_amd import ops
+from hyper_connection_residual_mhc_amd import probes
 
 pytestmark = pytest.mark.gpu
 
@@ -35,14 +36,38 @@ def test_stream_probe_moves_the_described_bytes(device, reads, writes, units):
     guard = 4096
     buf = torch.full((units * writes * KiB // 4 + 2 * guard,), -1, dtype=torch.int32, device=device)
     dst = buf[guard:guard + units * writes * KiB // 4]
-    ops.mhc_stream_probe(src, dst, reads, writes)
+    probes.mhc_stream_probe(src, dst, reads, writes)
     torch.cuda.synchronize()
     got = buf.cpu().numpy().view(np.uint32)
     assert np.array_equal(got[guard:-guard], expected(src_words, reads, writes))
     assert (got[:guard] == 0xFFFFFFFF).all() and (got[-guard:] == 0xFFFFFFFF).all()
 
 
+@pytest.mark.parametrize("units", [1, 5, 300])
+def test_read_only_probe_reads_and_writes_nothing(device, units):
+    say(f"stream probe 8:0 units={units}")
+    src = torch.arange(units * 8 * KiB // 4, dtype=torch.int32, device=device)
+    before = src.clone()
+    probes.mhc_stream_probe(src, None, 8, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(src, before)
+
+
+@pytest.mark.parametrize("units", [1, 5, 300])
+def test_write_only_probe_writes_its_unit_index(device, units):
+    say(f"stream probe 0:8 units={units}")
+    guard = 4096
+    buf = torch.full((units * 8 * KiB // 4 + 2 * guard,), -1, dtype=torch.int32, device=device)
+    dst = buf[guard:guard + units * 8 * KiB // 4]
+    probes.mhc_stream_probe(None, dst, 0, 8)
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy()
+    want = np.repeat(np.arange(units, dtype=np.int32), 8 * KiB // 4)
+    assert np.array_equal(got[guard:-guard], want)
+    assert (got[:guard] == -1).all() and (got[-guard:] == -1).all()
+
+
 def test_stream_probe_empty_is_a_no_op(device):
     e = torch.empty(0, dtype=torch.int32, device=device)
-    ops.mhc_stream_probe(e, e, 5, 4)
+    probes.mhc_stream_probe(e, e, 5, 4)
     torch.cuda.synchronize()
