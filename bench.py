@@ -6,23 +6,36 @@ A step is one pass of the whole path on one batch: the forward
 bandwidth shape of the page "Add batch-invariant h_aggregate kernel"
 (RL-Kernel pull request 366), section Performance.
 
-Cold caches: the inputs and outputs rotate over `--sets` independent buffer
-sets (default 8, about 1.2 GB) and the forward and backward of one step use
-different sets, so every set's bytes leave the 256 MB Infinity Cache and
-the L2s before they are touched again. Inputs are resident in HBM before the
-timed region starts.
+Cold caches: inputs and outputs rotate over `--sets` buffer sets (default 8,
+about 1.2 GB) and the forward and backward of one step use different sets,
+so every set's bytes leave the 256 MB Infinity Cache and the L2s before they
+are touched again. Inputs are resident in HBM before anything is timed.
+
+Timing, all on the stream the kernels are launched on:
+* the timed region: `--steps` steps of plain launches, with a synchronize on
+  both sides (host wall clock: `ms_per_step`, `value`) and two HIP events
+  recorded on the stream around it (`step.gpu_us`);
+* per-kernel time: blocks of back-to-back plain launches of one kernel on
+  rotating cold sets, one event pair around each block of 100 launches
+  after 10 untimed ones, 7 rounds (the protocol of the page "perf: fuse mHC
+  coefficient backward epilogue", Performance Method); a round's figure is
+  the block's time over its launch count, so every launch and the gaps
+  between back-to-back dispatches are counted. `roofline` takes the
+  backward's (the dominant kernel) median round;
+* beside it, `dispatch_event_us`: the same kernel with HIP events attached
+  to each dispatch itself (its start and end timestamps), for comparison;
+* `shapes`: the forward and the backward at T=2048 and 8192 (H=7168) timed
+  per call the same way, each with its fraction of the 8 TB/s peak;
+* `stream_probes`: plain byte streams with the backward's 5:4 and the
+  forward's 4:1 read:write mix, read only and write only, at the backward's
+  bytes, timed the same way (the measurement library, not the operation);
+* `cpu_baseline`: the CPU oracle on the same workload, on one core and on
+  all cores, before the GPU is touched.
 
 Output: one JSON line. `value` is the step's algorithmic bytes (forward
 10H+16 and backward 18H+32 per token) divided by the measured time per step.
-`roofline` is for the backward kernel (the larger of the two), its duration
-taken from HIP events that the library attaches to the backward dispatches
-of every 32nd timed step (start and end timestamps of the dispatch itself);
-its `traffic` comes from the committed counter summary while the library's
-device code is the one it was measured on. `stream_probe` compares the
-backward with a plain stream of the same read:write bytes, and
-`fwd_stream_probe` does the same for the forward; both are timed back to
-back after the timed steps. `cpu_baseline`
-times the CPU oracle on the same workload, on one core and on all cores.
+`roofline.traffic` comes from the committed counter summary while the
+library's device code is the one it was measured on.
 
 Helpers for the profiles: --summarize-stats and --summarize-pmc turn
 rocprofv3 CSV output into the short text summaries kept in profiles/.
@@ -39,6 +52,7 @@ import platform
 import re
 import statistics
 import struct
+import subprocess
 import sys
 import time
 from pathlib import Path
@@ -143,23 +157,45 @@ def recorded_traffic(T: int, H: int, kernel: str, text: str | None = None) -> in
 # GPU part
 # ---------------------------------------------------------------------------
 
+SEED = 0
+BLOCK_TOKENS = 1024  # tokens drawn on the host; longer batches repeat them on the device
+
+
 class BufferSet:
     """One independent set of device inputs and outputs for a step."""
 
-    def __init__(self, host: dict, dev):
+    def __init__(self, d: dict, dev, hc: int = HC):
         import torch
-        from hyper_connection_residual_mhc_amd.workloads import to_device
-        d = to_device(host, dev)
         self.residual, self.pre, self.grad_out = d["residual"], d["pre"], d["grad_out"]
-        T, hc, H = self.residual.shape
+        T, _, H = self.residual.shape
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         self.grad_residual = torch.empty((T, hc, H), dtype=torch.bfloat16, device=dev)
         self.grad_pre = torch.empty((T, hc), dtype=torch.float32, device=dev)
 
 
+def device_inputs(T: int, H: int, dev, hc: int = HC) -> dict:
+    """Seeded inputs on the device: min(T, 1024) tokens drawn by the shared
+    generator (seed 0, grad_out, 1% x64 residual outliers), repeated along
+    the token axis up to T (the values only have to have the workload's
+    distribution; drawing 8192 tokens on the host would take longer than
+    the whole timed work)."""
+    import torch
+    from hyper_connection_residual_mhc_amd.workloads import make_inputs, to_device
+    t0 = min(T, BLOCK_TOKENS)
+    d = to_device(make_inputs(t0, H, seed=SEED, grad=True, outliers=True, hc=hc), dev)
+    reps = -(-T // t0)
+    if reps > 1:
+        d = {k: v.repeat((reps,) + (1,) * (v.dim() - 1))[:T].contiguous() for k, v in d.items()}
+    return d
+
+
 def make_sets(T: int, H: int, n: int, dev, hc: int = HC) -> list[BufferSet]:
-    from hyper_connection_residual_mhc_amd.workloads import make_inputs
-    return [BufferSet(make_inputs(T, H, seed=s, grad=True, hc=hc), dev) for s in range(n)]
+    """n sets with the same input values at different addresses (cold caches
+    need distinct bytes in memory, not distinct values)."""
+    src = device_inputs(T, H, dev, hc)
+    sets = [BufferSet({k: v.clone() for k, v in src.items()}, dev, hc) for _ in range(n)]
+    del src
+    return sets
 
 
 def copy_probe(dev, nbytes: int = 1 << 28, reps: int = 3) -> None:
@@ -174,13 +210,14 @@ def copy_probe(dev, nbytes: int = 1 << 28, reps: int = 3) -> None:
 
 
 # Read:write mix of each kernel for the streaming probe (per token: forward
-# 8H read / 2H written, backward 10H / 8H, accumulating backward 18H / 8H).
-PROBE_MIX = {"fwd": (4, 1), "bwd": (5, 4), "bwd_acc": (9, 4)}
+# 8H read / 2H written, backward 10H / 8H, accumulating backward 18H / 8H),
+# and the read-only and write-only streams.
+PROBE_MIX = {"fwd": (4, 1), "bwd": (5, 4), "bwd_acc": (9, 4), "read": (8, 0), "write": (0, 8)}
 
 
 class ProbeBuffers:
     """Rotating src/dst pairs for mhc_stream_probe sized to about `nbytes`
-    of traffic with the given mix (whole 1-KiB units)."""
+    of traffic with the given mix (whole units of r + w KiB)."""
 
     def __init__(self, nbytes: int, mix: tuple[int, int], pairs: int, dev):
         import torch
@@ -188,15 +225,17 @@ class ProbeBuffers:
         self.units = max(1, nbytes // ((r + w) * 1024))
         self.mix = mix
         self.bytes = self.units * (r + w) * 1024
-        self.pairs = [(torch.ones(self.units * r * 256, dtype=torch.int32, device=dev),
-                       torch.empty(self.units * w * 256, dtype=torch.int32, device=dev))
-                      for _ in range(pairs)]
+        mk = lambda kib, fill: (torch.full((self.units * kib * 256,), fill, dtype=torch.int32,
+                                           device=dev) if kib else None)
+        self.pairs = [(mk(r, 1), mk(w, 0)) for _ in range(pairs)]
 
     def call(self, lib, k: int, stream_handle: int, a, b) -> int:
         src, dst = self.pairs[k % len(self.pairs)]
         r, w = self.mix
-        return lib.mhc_stream_probe(src.data_ptr(), src.numel() * 4, dst.data_ptr(),
-                                    dst.numel() * 4, r, w, stream_handle, a, b)
+        ptr = lambda t: 0 if t is None else t.data_ptr()
+        size = lambda t: 0 if t is None else t.numel() * 4
+        return lib.mhc_stream_probe(ptr(src), size(src), ptr(dst), size(dst), r, w,
+                                    stream_handle, a, b)
 
 
 class HipEvents:
@@ -212,12 +251,17 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.handles = []
         for _ in range(n):
             h = ctypes.c_void_p()
             if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
                 raise RuntimeError("hipEventCreate failed")
             self.handles.append(h.value)
+
+    def record(self, i: int, stream_handle: int) -> None:
+        if self.hip.hipEventRecord(self.handles[i], stream_handle) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def elapsed_us(self, a: int, b: int) -> float:
         ms = self._ct.c_float()
@@ -231,18 +275,120 @@ class HipEvents:
         self.handles = []
 
 
+def round_stats(per_round: list[float]) -> dict:
+    """Median and [p20, p50, p80] over per-round figures (any count >= 1)."""
+    med = statistics.median(per_round)
+    if len(per_round) >= 2:
+        q = statistics.quantiles(per_round, n=10, method="inclusive")
+        p20, p80 = q[1], q[7]
+    else:
+        p20 = p80 = med
+    return {"us_median": round(med, 3), "us_p20_p50_p80": [round(p20, 3), round(med, 3),
+                                                            round(p80, 3)],
+            "rounds": len(per_round)}
+
+
+class Timer:
+    """Per-launch time of a callable fn(k, start_event, stop_event) -> status
+    that launches one call on `stream_handle` (k picks the rotating set).
+
+    block(fn): `rounds` rounds of `warm` untimed plain launches, then `timed`
+    plain launches with one event pair recorded on the stream around them;
+    a round's figure is the pair's elapsed time / `timed` (every launch, and
+    the gaps between back-to-back dispatches, counted).
+    dispatch(fn, n): n launches each carrying its own dispatch events (the
+    dispatch's own start and end timestamps); per-launch microseconds.
+    """
+
+    def __init__(self, stream_handle: int, rounds: int = 7, warm: int = 10, timed: int = 100,
+                 check=None):
+        self.sh, self.rounds, self.warm, self.timed = stream_handle, rounds, warm, timed
+        self.check = check
+        self.ev = HipEvents(max(2, 2 * timed))
+
+    def _ok(self, st: int) -> None:
+        if st:
+            self.check(st)
+
+    def block(self, fn) -> list[float]:
+        import torch
+        out = []
+        for _ in range(self.rounds):
+            for k in range(self.warm):
+                self._ok(fn(k, None, None))
+            torch.cuda.synchronize()
+            self.ev.record(0, self.sh)
+            for k in range(self.timed):
+                self._ok(fn(self.warm + k, None, None))
+            self.ev.record(1, self.sh)
+            torch.cuda.synchronize()
+            out.append(self.ev.elapsed_us(0, 1) / self.timed)
+        return out
+
+    def dispatch(self, fn, n: int) -> list[float]:
+        import torch
+        n = min(n, self.timed)
+        E = self.ev.handles
+        for k in range(self.warm):
+            self._ok(fn(k, None, None))
+        torch.cuda.synchronize()
+        for k in range(n):
+            self._ok(fn(self.warm + k, E[2 * k], E[2 * k + 1]))
+        torch.cuda.synchronize()
+        return [self.ev.elapsed_us(2 * k, 2 * k + 1) for k in range(n)]
+
+    def close(self) -> None:
+        self.ev.close()
+
+
+def kernel_record(nbytes: int, block: list[float], sampled: list[float] | None = None) -> dict:
+    """Per-call figures of one kernel: block-timed median (all launches) with
+    its GB/s and fraction of the HBM peak, plus the dispatch-event sample."""
+    rec = {"bytes_per_call": nbytes, **round_stats(block)}
+    med = rec["us_median"]
+    rec["gbps"] = round(nbytes / med / 1e3, 1)
+    rec["frac_of_8TBps"] = round(nbytes / med / 1e3 / PEAK_HBM_GBPS, 4)
+    if sampled:
+        rec["dispatch_event_us"] = {"launches": len(sampled),
+                                    "mean": round(statistics.fmean(sampled), 3),
+                                    "median": round(statistics.median(sampled), 3)}
+    return rec
+
+
+def _kernel_calls(lib, sets, T, H, sh):
+    """fn(k, a, b) launchers of the forward and the backward on set k mod n."""
+    nsets = len(sets)
+    fargs = [(x.residual.data_ptr(), x.pre.data_ptr(), x.out.data_ptr(), T, H, sh) for x in sets]
+    bargs = [(x.residual.data_ptr(), x.pre.data_ptr(), x.grad_out.data_ptr(),
+              x.grad_residual.data_ptr(), x.grad_pre.data_ptr(), T, H, sh) for x in sets]
+
+    def fwd(k, a, b):
+        if a is None and b is None:
+            return lib.mhc_h_aggregate_fwd(*fargs[k % nsets])
+        return lib.mhc_h_aggregate_fwd_timed(*fargs[k % nsets], None, a, b)
+
+    def bwd(k, a, b):
+        if a is None and b is None:
+            return lib.mhc_h_aggregate_bwd(*bargs[k % nsets])
+        return lib.mhc_h_aggregate_bwd_timed(*bargs[k % nsets], None, a, b)
+    return fwd, bwd
+
+
+# Per-call shapes reported beside the step (H = 7168): (direction, T, sets).
+SHAPES = [("fwd", 2048, 8), ("fwd", 8192, 3), ("bwd", 2048, 8), ("bwd", 8192, 3)]
+
+
 def run_gpu(T: int, H: int, steps: int, warmup: int, nsets: int, copy_calibration: bool,
-            sample_every: int) -> dict:
-    """The timed forward + backward steps on nsets rotating cold buffer sets
-    (per-kernel dispatch events on every `sample_every`-th step), then the
-    back-to-back reference runs of each kernel and of the stream probe with
-    its byte mix. copy_calibration: first run the plain device copy whose
-    counter readings calibrate the traffic figures."""
+            sample: int = 32, shapes: bool = True, probes: bool = True) -> dict:
+    """The timed forward + backward steps on nsets rotating cold buffer sets,
+    then the per-kernel block timings (and dispatch-event samples) at the
+    step's shape, at SHAPES and of the stream probes. copy_calibration:
+    first run the plain device copy whose counter readings calibrate the
+    traffic figures."""
     import torch
     from hyper_connection_residual_mhc_amd import _build, _lib, ops
 
-    if not _build.library_is_built():
-        _build.build_library()
+    _build.ensure_built()
     lib = _lib.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -250,119 +396,117 @@ def run_gpu(T: int, H: int, steps: int, warmup: int, nsets: int, copy_calibratio
     stream = torch.cuda.current_stream(dev)
     sh = int(stream.cuda_stream)
 
-    # Plans (host-only queries) and the pre-marshalled argument tuples.
     s0 = sets[0]
     fwd_plan, fwd_grid = ops.mhc_h_aggregate_plan_fwd(s0.residual, s0.pre, s0.out, T, H)
     bwd_plan, bwd_grid = ops.mhc_h_aggregate_plan_bwd(s0.residual, s0.pre, s0.grad_out,
                                                       s0.grad_residual, s0.grad_pre, T, H)
-    fargs = [(s.residual.data_ptr(), s.pre.data_ptr(), s.out.data_ptr(), T, H, sh) for s in sets]
-    bargs = [(s.residual.data_ptr(), s.pre.data_ptr(), s.grad_out.data_ptr(),
-              s.grad_residual.data_ptr(), s.grad_pre.data_ptr(), T, H, sh) for s in sets]
-    fwd, bwd = lib.mhc_h_aggregate_fwd, lib.mhc_h_aggregate_bwd
-    fwd_t, bwd_t = lib.mhc_h_aggregate_fwd_timed, lib.mhc_h_aggregate_bwd_timed
+    fwd, bwd = _kernel_calls(lib, sets, T, H, sh)
 
     if copy_calibration:
         copy_probe(dev)
 
-    # Every `sample_every`-th step goes through the timed entry points, which
-    # attach HIP events to the two kernel dispatches themselves. An
-    # event-carrying dispatch costs the GPU about 5 us more than a plain one
-    # (measured: 35.0 us per step with no events, 36.2 with events every 8th
-    # step, 35.45 every 32nd) and the host about 25 us, so sampling keeps the
-    # timed steps close to the plain ones and the host ahead of the GPU.
-    sampled = [k for k in range(steps) if k % sample_every == 0]
-    ev = HipEvents(4 * len(sampled))
-    E = ev.handles
-
     # Step k: forward on set 2k mod n, backward on set 2k+1 mod n.
-    def step(k: int) -> int:
-        return (fwd(*fargs[(2 * k) % nsets]) |
-                bwd(*bargs[(2 * k + 1) % nsets]))
-
-    def timed_step(k: int, j: int) -> int:
-        return (fwd_t(*fargs[(2 * k) % nsets], None, E[4 * j], E[4 * j + 1]) |
-                bwd_t(*bargs[(2 * k + 1) % nsets], None, E[4 * j + 2], E[4 * j + 3]))
+    def step(k: int, a=None, b=None) -> int:
+        return fwd(2 * k, None, None) | bwd(2 * k + 1, None, None)
 
     for k in range(warmup):
         st = step(k)
         if st:
             _lib.check(st)
+    region = HipEvents(2)
     torch.cuda.synchronize()
-
     st = 0
-    j = 0
     t0 = time.perf_counter()
+    region.record(0, sh)
     for k in range(steps):
-        if k % sample_every == 0:
-            st |= timed_step(warmup + k, j)
-            j += 1
-        else:
-            st |= step(warmup + k)
+        st |= step(warmup + k)
+    region.record(1, sh)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     if st:
         _lib.check(st)
+    region_us = region.elapsed_us(0, 1)
+    region.close()
 
-    fwd_us = [ev.elapsed_us(4 * j, 4 * j + 1) for j in range(len(sampled))]
-    bwd_us = [ev.elapsed_us(4 * j + 2, 4 * j + 3) for j in range(len(sampled))]
-    ev.close()
-
-    # Reference: the backward alone, then a streaming probe with its
-    # read:write byte mix and no arithmetic, each back to back from cold
-    # buffers, every launch timed by its own dispatch events. Outside the
-    # timed steps.
-    probe = ProbeBuffers(bwd_bytes(T, H), PROBE_MIX["bwd"], nsets, dev)
-    ref = SweepTimer(rounds=1, warm=10, timed=200)
-
-    def back_to_back(fn) -> list[float]:
-        return ref.blocks([fn], _lib.check)[0][0]
-
-    ceil_kernel_us = back_to_back(lambda k, a, b: bwd_t(*bargs[k % nsets], None, a, b))
-    ceil_probe_us = back_to_back(lambda k, a, b: probe.call(lib, k, sh, a, b))
-    probe_bytes = probe.bytes
-    del probe
-    # The same for the forward and its 4:1 mix.
-    fprobe = ProbeBuffers(fwd_bytes(T, H), PROBE_MIX["fwd"], nsets, dev)
-    fwd_ceil_us = back_to_back(lambda k, a, b: fwd_t(*fargs[k % nsets], None, a, b))
-    fwd_probe_us = back_to_back(lambda k, a, b: fprobe.call(lib, k, sh, a, b))
-    fprobe_bytes = fprobe.bytes
-    del fprobe
-    ref.close()
-    return {
-        "probe": {"kernel_us": ceil_kernel_us, "probe_us": ceil_probe_us,
-                    "probe_bytes": probe_bytes},
-        "fwd_probe": {"kernel_us": fwd_ceil_us, "probe_us": fwd_probe_us,
-                      "probe_bytes": fprobe_bytes},
+    tm = Timer(sh, check=_lib.check)
+    out = {
         "wall_s": t1 - t0,
-        "timed_launches": len(sampled),
-        "fwd_us": fwd_us,
-        "bwd_us": bwd_us,
+        "region_gpu_us": region_us,
+        "step_block": tm.block(step),
+        "fwd_block": tm.block(fwd),
+        "bwd_block": tm.block(bwd),
+        "fwd_sampled": tm.dispatch(fwd, sample) if sample else None,
+        "bwd_sampled": tm.dispatch(bwd, sample) if sample else None,
         "fwd_plan": fwd_plan, "fwd_grid": fwd_grid,
         "bwd_plan": bwd_plan, "bwd_grid": bwd_grid,
         "device": torch.cuda.get_device_name(dev),
         "torch": torch.__version__,
         "hip": getattr(torch.version, "hip", None),
     }
+    del sets, fwd, bwd
+    torch.cuda.empty_cache()
+
+    if probes:
+        plib = _lib.probe_lib()
+        out["probes"] = {}
+        for name, nbytes in (("bwd", bwd_bytes(T, H)), ("fwd", fwd_bytes(T, H)),
+                             ("read", bwd_bytes(T, H)), ("write", bwd_bytes(T, H))):
+            pb = ProbeBuffers(nbytes, PROBE_MIX[name], nsets, dev)
+            ptm = Timer(sh, check=_lib.check_probe)
+            out["probes"][name] = {"bytes": pb.bytes,
+                                   "block": ptm.block(lambda k, a, b: pb.call(plib, k, sh, a, b))}
+            ptm.close()
+            del pb
+            torch.cuda.empty_cache()
+
+    if shapes:
+        out["shapes"] = []
+        for direction, Ts, ns in SHAPES:
+            ssets = make_sets(Ts, H, ns, dev)
+            f, b = _kernel_calls(lib, ssets, Ts, H, sh)
+            fn = f if direction == "fwd" else b
+            out["shapes"].append({"direction": direction, "T": Ts, "H": H, "sets": ns,
+                                  "block": tm.block(fn),
+                                  "sampled": tm.dispatch(fn, sample) if sample else None})
+            del ssets, f, b, fn
+            torch.cuda.empty_cache()
+    tm.close()
+    return out
 
 
-def probe_record(kernel_bytes: int, c: dict, direction: str = "bwd") -> dict:
-    k = statistics.fmean(c["kernel_us"])
-    p = statistics.fmean(c["probe_us"])
-    kg = kernel_bytes / k / 1e3
-    pg = c["probe_bytes"] / p / 1e3
-    name, (r, w) = ("backward" if direction == "bwd" else "forward"), PROBE_MIX[direction]
-    return {
-        "kind": f"mhc_stream_probe: the {name}'s {r}:{w} read:write byte mix as a plain "
-                f"stream (one 64-lane block per {r} KiB read + {w} KiB written), no "
-                f"arithmetic; the {name} and the probe each timed back to back by "
-                "their own dispatch events, cold buffers",
-        "probe_bytes": c["probe_bytes"],
-        "probe_us": round(p, 3),
-        "probe_gbps": round(pg, 1),
-        "kernel_us": round(k, 3),
-        "kernel_gbps": round(kg, 1),
-        "frac_of_probe": round(kg / pg, 4),
-    }
+def probe_record(kernel_bytes: int, kernel_us: float, probe: dict, mix: str) -> dict:
+    """A kernel against the plain stream with the given mix (block-timed medians)."""
+    r, w = PROBE_MIX[mix]
+    p = statistics.median(probe["block"])
+    pg = probe["bytes"] / p / 1e3
+    kg = kernel_bytes / kernel_us / 1e3
+    return {"mix": f"{r}:{w}", "probe_bytes": probe["bytes"], "probe_us": round(p, 3),
+            "probe_gbps": round(pg, 1), "kernel_us": round(kernel_us, 3),
+            "kernel_gbps": round(kg, 1), "frac_of_probe": round(kg / pg, 4)}
+
+
+def git_revision() -> str | None:
+    """HEAD of the repository this file is in, or None where there is no
+    git metadata (a copied tree)."""
+    try:
+        r = subprocess.run(["git", "-C", str(REPO), "rev-parse", "HEAD"], capture_output=True,
+                           text=True, timeout=10)
+        return r.stdout.strip() if r.returncode == 0 and r.stdout.strip() else None
+    except (OSError, subprocess.SubprocessError):
+        return None
+
+
+def tree_digest() -> str:
+    """sha256 over the files that define a run: the kernel sources and
+    headers, the Python package and this file (name and content, sorted)."""
+    files = sorted(list((REPO / "hyper_connection_residual_mhc_amd").glob("*.py")) +
+                   list((REPO / "hyper_connection_residual_mhc_amd" / "csrc").glob("*")) +
+                   list((REPO / "include").glob("*.h")) + [Path(__file__).resolve()])
+    h = hashlib.sha256()
+    for f in files:
+        if f.is_file():
+            h.update(f.relative_to(REPO).as_posix().encode() + b"\0" + f.read_bytes())
+    return h.hexdigest()
 
 
 # ---------------------------------------------------------------------------
@@ -409,11 +553,10 @@ class SweepTimer:
     def summary(per_round: list[list[float]]) -> tuple[float, list[float], float]:
         """Median of the round medians, [p20, p50, p80] over the round
         medians, and the mean of every launch."""
-        import statistics as st
-        med = [st.median(r) for r in per_round]
-        q = st.quantiles(med, n=10, method="inclusive")
-        mean = st.fmean([x for r in per_round for x in r])
-        return st.median(med), [round(q[1], 3), round(st.median(med), 3), round(q[7], 3)], mean
+        med = [statistics.median(r) for r in per_round]
+        rs = round_stats(med)
+        mean = statistics.fmean([x for r in per_round for x in r])
+        return statistics.median(med), rs["us_p20_p50_p80"], mean
 
     @classmethod
     def fields(cls, nbytes: int, per_round: list[list[float]]) -> dict:
@@ -442,9 +585,11 @@ def run_sweep(path: str, rounds: int = 7, warm: int = 10, timed: int = 100,
     through the *_n entry points, without probes). `part` limits the sweep
     to "h_aggregate", "coeff" or "expansion"."""
     import torch
-    from hyper_connection_residual_mhc_amd import _lib, ops
+    from hyper_connection_residual_mhc_amd import _build, _lib, ops
 
+    _build.ensure_built()
     lib = _lib.lib()
+    plib = _lib.probe_lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sh = int(torch.cuda.current_stream(dev).cuda_stream)
@@ -497,7 +642,10 @@ def run_sweep(path: str, rounds: int = 7, warm: int = 10, timed: int = 100,
                          if T >= 1024 else None)
                 fns = [call]
                 if probe:
-                    fns.append(lambda k, a, b: probe.call(lib, k, sh, a, b))
+                    def probe_call(k, a, b, probe=probe):
+                        _lib.check_probe(probe.call(plib, k, sh, a, b))
+                        return 0
+                    fns.append(probe_call)
                 timings = tm.blocks(fns, _lib.check)
                 rec = {"direction": direction, "T": T, "H": H,
                        **SweepTimer.fields(nbytes, timings[0]), "plan": plan}
@@ -575,8 +723,7 @@ def run_counter_case(case: str, T: int, H: int, launches: int = 64, nsets: int =
     the 256 MiB calibration copy. Returns the plan and the mean event time."""
     import torch
     from hyper_connection_residual_mhc_amd import _build, _lib, ops
-    if not _build.library_is_built():
-        _build.build_library()
+    _build.ensure_built()
     lib = _lib.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -840,7 +987,97 @@ def summarize_pmc(paths: list[str]) -> None:
 
 # ---------------------------------------------------------------------------
 
-def main() -> int:
+def build_record(args, g: dict, cpu: dict | None) -> dict:
+    """The JSON line from run_gpu's measurements (no GPU needed here)."""
+    T, H = args.tokens, args.hidden
+    ms_per_step = g["wall_s"] * 1e3 / args.steps
+    step_bytes = fwd_bytes(T, H) + bwd_bytes(T, H)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    fwd = kernel_record(fwd_bytes(T, H), g["fwd_block"], g.get("fwd_sampled"))
+    bwd = kernel_record(bwd_bytes(T, H), g["bwd_block"], g.get("bwd_sampled"))
+    fwd.update(plan=g["fwd_plan"], grid_blocks=g["fwd_grid"])
+    bwd.update(plan=g["bwd_plan"], grid_blocks=g["bwd_grid"])
+    step_block = round_stats(g["step_block"])
+    bwd_us = bwd["us_median"]
+    achieved = bwd_bytes(T, H) / (bwd_us * 1e-6) / 1e9
+    bwd_kernel = ("hagg_bwd_rows_kernel" if g["bwd_plan"].get("layout") == 2 else
+                  "hagg_bwd_kernel")
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"h_aggregate forward+backward, T={T}, H={H}, HC=4, bf16 in/out, "
+                        f"fp32 pre and arithmetic",
+            "T": T, "H": H, "hc": HC,
+            "rotating_sets": args.sets,
+            "bytes_per_step": step_bytes,
+            "seed": SEED,
+            "inputs": f"seed-{SEED} draws of the shared generator (residual N(0,1) with 1% x64 "
+                      f"outliers, pre U[0,1), grad_out N(0,0.1)), {BLOCK_TOKENS}-token blocks "
+                      f"repeated for longer batches; the same values in every rotating set",
+        },
+        "step": {"wall_us": round(ms_per_step * 1e3, 3),
+                 "gpu_us": round(g["region_gpu_us"] / args.steps, 3),
+                 "block": step_block,
+                 "fwd_plus_bwd_block_us": round(fwd["us_median"] + bwd_us, 3)},
+        "fwd": fwd,
+        "bwd": bwd,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": recorded_traffic(T, H, bwd_kernel),
+            "kernel": bwd_kernel + (" (backward, row layout)" if bwd_kernel == "hagg_bwd_rows_kernel"
+                                    else " (backward, split layout)"),
+            "timing": "median over 7 rounds of one event pair around 100 back-to-back plain "
+                      "launches on rotating cold sets (every launch and dispatch gap counted)",
+        },
+        "timing": {"per_step": "host wall clock over the timed steps, synchronized on both "
+                               "sides; step.gpu_us from HIP events recorded on the stream "
+                               "around the same region",
+                   "per_kernel": "blocks of back-to-back plain launches (7 rounds x (10 + 100)), "
+                                 "one event pair per block on the kernels' stream; "
+                                 "dispatch_event_us: events attached to each dispatch"},
+        "device": g["device"],
+        "torch": g["torch"],
+        "hip": g["hip"],
+        "git_sha": git_revision(),
+        "tree_sha256": tree_digest(),
+        "device_code_sha256": device_code_sha256(),
+    }
+    if g.get("probes"):
+        pr = g["probes"]
+        line["stream_probes"] = {
+            "bwd": probe_record(bwd_bytes(T, H), bwd_us, pr["bwd"], "bwd"),
+            "fwd": probe_record(fwd_bytes(T, H), fwd["us_median"], pr["fwd"], "fwd"),
+            "read_only": probe_record(bwd_bytes(T, H), bwd_us, pr["read"], "read"),
+            "write_only": probe_record(bwd_bytes(T, H), bwd_us, pr["write"], "write"),
+        }
+    if g.get("shapes"):
+        line["shapes"] = []
+        for sh in g["shapes"]:
+            nb = (fwd_bytes if sh["direction"] == "fwd" else bwd_bytes)(sh["T"], sh["H"])
+            line["shapes"].append({"direction": sh["direction"], "T": sh["T"], "H": sh["H"],
+                                   "rotating_sets": sh["sets"],
+                                   **kernel_record(nb, sh["block"], sh.get("sampled"))})
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
+    return line
+
+
+def main(argv: list[str] | None = None, gpu_runner=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
@@ -848,8 +1085,10 @@ def main() -> int:
     ap.add_argument("--sets", type=int, default=8, help="rotating buffer sets (cold caches)")
     ap.add_argument("--tokens", type=int, default=1024)
     ap.add_argument("--hidden", type=int, default=7168)
-    ap.add_argument("--time-every", type=int, default=32,
-                    help="attach timing events to every N-th step's dispatches")
+    ap.add_argument("--sample", type=int, default=32,
+                    help="launches of each kernel timed by per-dispatch events (0: none)")
+    ap.add_argument("--no-shapes", action="store_true", help="skip the T=2048/8192 figures")
+    ap.add_argument("--no-probes", action="store_true", help="skip the stream probes")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -866,7 +1105,7 @@ def main() -> int:
                          "one launch shape (for rocprofv3 --pmc runs) and print one JSON line")
     ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV")
     ap.add_argument("--summarize-pmc", metavar="COUNTER_CSV", nargs="+")
-    args = ap.parse_args()
+    args = ap.parse_args(argv)
 
     if args.summarize_stats:
         summarize_stats(args.summarize_stats)
@@ -891,11 +1130,11 @@ def main() -> int:
     if args.sets < 2:
         print("--sets must be >= 2 (forward and backward use different sets)", file=sys.stderr)
         return 2
+    if args.steps < 1 or args.warmup < 0 or args.sample < 0:
+        print("--steps must be >= 1, --warmup and --sample >= 0", file=sys.stderr)
+        return 2
 
     T, H = args.tokens, args.hidden
-    if args.time_every < 1:
-        print("--time-every must be >= 1", file=sys.stderr)
-        return 2
     # The oracle baselines run first, before anything touches the GPU (the
     # all-core one forks worker processes).
     cpu = None
@@ -904,73 +1143,10 @@ def main() -> int:
         workers = min(16, len(os.sched_getaffinity(0)))
         if workers > 1:
             cpu["all_cores"] = run_cpu_baseline_all_cores(T, H, args.cpu_seconds, workers)
-    g = run_gpu(T, H, args.steps, args.warmup, args.sets, args.copy_probe, args.time_every)
-    ms_per_step = g["wall_s"] * 1e3 / args.steps
-    step_bytes = fwd_bytes(T, H) + bwd_bytes(T, H)
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    fwd_avg = statistics.fmean(g["fwd_us"])
-    bwd_avg = statistics.fmean(g["bwd_us"])
-    achieved = bwd_bytes(T, H) / (bwd_avg * 1e-6) / 1e9
-    bwd_kernel = ("hagg_bwd_rows_kernel" if g["bwd_plan"].get("layout") == 2 else
-                  "hagg_bwd_kernel")
-
-    line = {
-        "metric": METRIC,
-        "value": round(value, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {
-            "workload": f"h_aggregate forward+backward, T={T}, H={H}, HC=4, bf16 in/out, "
-                        f"fp32 pre and arithmetic",
-            "T": T, "H": H, "hc": HC,
-            "rotating_sets": args.sets,
-            "bytes_per_step": step_bytes,
-        },
-        "fwd": {
-            "us_per_call": round(fwd_avg, 3),
-            "us_p20_p50_p80": [round(x, 3) for x in statistics.quantiles(g["fwd_us"], n=10)[1:8:3]],
-            "gbps": round(fwd_bytes(T, H) / (fwd_avg * 1e-6) / 1e9, 1),
-            "bytes_per_call": fwd_bytes(T, H),
-            "plan": g["fwd_plan"], "grid_blocks": g["fwd_grid"],
-        },
-        "bwd": {
-            "us_per_call": round(bwd_avg, 3),
-            "us_p20_p50_p80": [round(x, 3) for x in statistics.quantiles(g["bwd_us"], n=10)[1:8:3]],
-            "gbps": round(achieved, 1),
-            "bytes_per_call": bwd_bytes(T, H),
-            "plan": g["bwd_plan"], "grid_blocks": g["bwd_grid"],
-        },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": PEAK_HBM_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBPS, 4),
-            "traffic": recorded_traffic(T, H, bwd_kernel),
-            "kernel": bwd_kernel + (" (backward, row layout)" if bwd_kernel == "hagg_bwd_rows_kernel"
-                                    else " (backward, split layout)"),
-        },
-        "stream_probe": probe_record(bwd_bytes(T, H), g["probe"]),
-        "fwd_stream_probe": probe_record(fwd_bytes(T, H), g["fwd_probe"], "fwd"),
-        "timing": {"per_kernel": "HIP events attached to the dispatches of every "
-                                 f"{args.time_every}th step ({g['timed_launches']} launches "
-                                 "of each kernel)",
-                   "per_step": "host wall clock over the timed steps, synchronized on both sides"},
-        "device": g["device"],
-        "torch": g["torch"],
-        "hip": g["hip"],
-    }
-    if cpu is not None:
-        line["cpu_baseline"] = cpu
-    print(json.dumps(line), flush=True)
+    runner = gpu_runner or run_gpu
+    g = runner(T, H, args.steps, args.warmup, args.sets, args.copy_probe, sample=args.sample,
+               shapes=not args.no_shapes, probes=not args.no_probes)
+    print(json.dumps(build_record(args, g, cpu)), flush=True)
     return 0
 
 

@@ -3,9 +3,12 @@ baseline record, the profile summaries and the recorded-traffic lookup."""
 
 from __future__ import annotations
 
+import json
 import subprocess
 import sys
 from pathlib import Path
+
+import pytest
 
 import bench
 
@@ -39,13 +42,82 @@ def test_algorithmic_bytes_per_token():
 
 
 def test_probe_record_fractions():
-    rec = bench.probe_record(1000, {"kernel_us": [1.0, 1.0], "probe_us": [2.0, 2.0],
-                                    "probe_bytes": 1000})
+    rec = bench.probe_record(1000, 1.0, {"block": [2.0, 2.0, 2.0], "bytes": 1000}, "bwd")
     assert rec["kernel_gbps"] == 1.0 and rec["probe_gbps"] == 0.5 and rec["frac_of_probe"] == 2.0
-    assert "5:4" in rec["kind"] and "backward" in rec["kind"]
-    rec = bench.probe_record(1000, {"kernel_us": [1.0], "probe_us": [1.0], "probe_bytes": 500},
-                             "fwd")
-    assert "4:1" in rec["kind"] and "forward" in rec["kind"] and rec["frac_of_probe"] == 2.0
+    assert rec["mix"] == "5:4"
+    rec = bench.probe_record(1000, 1.0, {"block": [1.0], "bytes": 500}, "fwd")
+    assert rec["mix"] == "4:1" and rec["frac_of_probe"] == 2.0
+    assert bench.probe_record(10, 1.0, {"block": [1.0], "bytes": 8192}, "read")["mix"] == "8:0"
+
+
+def test_round_stats_any_count():
+    """One round gives its value for every percentile (the driver's short
+    runs never reach a quantile of a single point)."""
+    assert bench.round_stats([5.0]) == {"us_median": 5.0, "us_p20_p50_p80": [5.0, 5.0, 5.0],
+                                        "rounds": 1}
+    r = bench.round_stats([1.0, 2.0, 3.0, 4.0, 5.0, 6.0, 7.0])
+    assert r["us_median"] == 4.0 and r["us_p20_p50_p80"][1] == 4.0
+    assert r["us_p20_p50_p80"][0] < 4.0 < r["us_p20_p50_p80"][2]
+
+
+def _fake_gpu(steps_seen):
+    """A stand-in for run_gpu with the shape of its result (made-up times)."""
+    def run(T, H, steps, warmup, nsets, copy_calibration, sample=32, shapes=True, probes=True):
+        steps_seen.append(steps)
+        blk = [22.0 + 0.01 * i for i in range(7)]
+        out = {"wall_s": steps * 35e-6, "region_gpu_us": steps * 34.8,
+               "step_block": [34.7] * 7, "fwd_block": [12.1] * 7, "bwd_block": blk,
+               "fwd_sampled": [11.9] * sample if sample else None,
+               "bwd_sampled": [21.3] * sample if sample else None,
+               "fwd_plan": {"block_threads": 64}, "fwd_grid": 14336,
+               "bwd_plan": {"layout": 2}, "bwd_grid": 1024,
+               "device": "stub", "torch": "stub", "hip": None}
+        if probes:
+            out["probes"] = {k: {"bytes": 132153344, "block": [22.5] * 7}
+                             for k in ("bwd", "fwd", "read", "write")}
+        if shapes:
+            out["shapes"] = [{"direction": d, "T": t, "H": H, "sets": n, "block": [40.0] * 7,
+                              "sampled": [39.0]} for d, t, n in bench.SHAPES]
+        return out
+    return run
+
+
+@pytest.mark.parametrize("argv", [["--gpus", "1", "--steps", "20", "--warmup", "5"],
+                                  ["--steps", "1", "--warmup", "0"],
+                                  ["--steps", "3", "--sample", "0", "--no-shapes",
+                                   "--no-probes"]])
+def test_main_record_at_the_driver_command_line(argv, capsys):
+    """main() at the driver's command line (and at 1 step) prints one JSON
+    line with the contract's fields, a roofline from the block-timed
+    backward and the CPU baseline; the GPU part is stubbed."""
+    seen = []
+    rc = bench.main(argv + ["--cpu-seconds", "0", "--tokens", "4", "--hidden", "64"],
+                    gpu_runner=_fake_gpu(seen))
+    assert rc == 0
+    lines = [ln for ln in capsys.readouterr().out.splitlines() if ln.strip()]
+    assert len(lines) == 1
+    rec = json.loads(lines[0])
+    steps = int(argv[argv.index("--steps") + 1])
+    assert seen == [steps] and rec["steps"] == steps
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                "roofline", "cpu_baseline", "git_sha", "tree_sha256"):
+        assert key in rec, key
+    assert rec["config"]["workload"].startswith("h_aggregate forward+backward")
+    assert rec["config"]["seed"] == 0
+    rf = rec["roofline"]
+    assert rf["bound"] == "hbm" and rf["peak"] == 8000.0 and rf["unit"] == "GB/s"
+    assert rf["achieved"] == pytest.approx(bench.bwd_bytes(4, 64) / 22.03e-6 / 1e9, abs=0.05)
+    assert rf["frac"] == pytest.approx(rf["achieved"] / 8000.0, abs=1e-4)
+    assert rec["cpu_baseline"]["kind"] == "oracle" and rec["cpu_baseline"]["cores"] >= 1
+    assert rec["ms_per_step"] * rec["steps"] == pytest.approx(steps * 35e-3, rel=1e-3)
+    if "--no-shapes" not in argv:
+        assert [(s["direction"], s["T"]) for s in rec["shapes"]] == \
+            [(d, t) for d, t, _ in bench.SHAPES]
+        assert set(rec["stream_probes"]) == {"bwd", "fwd", "read_only", "write_only"}
+    else:
+        assert "shapes" not in rec and "stream_probes" not in rec
+    assert (rec["bwd"].get("dispatch_event_us") is None) == ("--sample" in argv)
 
 
 def test_summaries_parse_rocprof_csv(tmp_path, capsys):
