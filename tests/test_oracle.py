@@ -796,3 +796,72 @@ def test_to_bf16_bits_is_round_to_nearest_even():
     """The generator's torch CPU conversion rounds like an independent RNE."""
     x = np.random.default_rng(2).standard_normal(1 << 16).astype(np.float32)
     assert np.array_equal(to_bf16_bits(x), indep_bf16_round(x.view(np.uint32)))
+
+
+# ---------------------------------------------------------------------------
+# bf16 ulp and the forward's acceptance bound (the helpers the fp64 gates use)
+# ---------------------------------------------------------------------------
+
+def test_bf16_ulp_hand_values():
+    """ulp of 1.0 is 2^-7 (7 fraction bits); 2.0 is one binade up; the
+    largest finite bf16 (0x7F7F, exponent 127) has 2^120; zero, every
+    subnormal and the smallest normal share the subnormal spacing 2^-133;
+    the sign does not matter."""
+    cases = {0x3F80: 2.0 ** -7, 0xBF80: 2.0 ** -7, 0x3FFF: 2.0 ** -7, 0x4000: 2.0 ** -6,
+             0x7F7F: 2.0 ** 120, 0xFF7F: 2.0 ** 120, 0x0000: 2.0 ** -133, 0x8000: 2.0 ** -133,
+             0x0001: 2.0 ** -133, 0x007F: 2.0 ** -133, 0x0080: 2.0 ** -133,
+             0x0100: 2.0 ** -132, 0x3E80: 2.0 ** -9}
+    bits = np.array(list(cases), dtype=np.uint16)
+    got = O.bf16_ulp(bits)
+    for b, g in zip(cases, got):
+        assert g == cases[b], hex(b)
+
+
+def test_bf16_ulp_is_the_spacing_of_neighbouring_patterns():
+    """Exhaustive over every positive finite bf16 pattern: the ulp is the
+    gap to the next pattern up inside a binade (mantissa below 0x7F), and
+    the gap to the next pattern down at the top of a binade - computed from
+    the patterns themselves, not from an exponent formula."""
+    b = np.arange(0x0000, 0x7F80, dtype=np.uint32)
+    v = (b << 16).view(np.float32).astype(np.float64)
+    up = ((np.minimum(b + 1, 0x7F7F)) << 16).view(np.float32).astype(np.float64)
+    down = ((np.maximum(b, 1) - 1) << 16).view(np.float32).astype(np.float64)
+    top = (b & 0x7F) == 0x7F
+    gap = np.where(top, v - down, up - v)
+    assert np.array_equal(O.bf16_ulp(b.astype(np.uint16)), gap)
+
+
+def test_forward_error_bound_hand_values():
+    """Depth 1 + log2(n) (one product, log2(n) sum levels): with mag = 0 the
+    bound is half an ulp plus the subnormal term; with mag = 1 it adds
+    ((1 + 2^-24)^d - 1) + (n + 1) 2^-53."""
+    one = np.array([0x3F80], dtype=np.uint16)
+    u = 2.0 ** -24
+    for n, d in ((2, 2), (4, 3), (8, 4)):
+        assert O.fwd_error_bound(one, np.array([0.0]), n)[0] == 2.0 ** -8 + d * 2.0 ** -150
+        want = 2.0 ** -8 + (((1 + u) ** d - 1) + (n + 1) * 2.0 ** -53) + d * 2.0 ** -150
+        assert O.fwd_error_bound(one, np.array([1.0]), n)[0] == want
+    # scales with the magnitude sum and with the output's ulp
+    two = np.array([0x4000], dtype=np.uint16)
+    assert O.fwd_error_bound(two, np.array([0.0]))[0] == 2.0 ** -7 + 3 * 2.0 ** -150
+    b1 = O.fwd_error_bound(one, np.array([1.0]))[0] - 2.0 ** -8
+    b4 = O.fwd_error_bound(one, np.array([4.0]))[0] - 2.0 ** -8
+    assert abs(b4 - 4 * b1) <= 4 * 3 * 2.0 ** -150
+
+
+def test_forward_error_bound_on_a_hand_built_cancellation():
+    """pre = (1, 1, 1, 1), r = (1+2^-7, -1, 2^-9, 2^-30): p0 + p1 cancels to
+    2^-7 exactly, p2 + p3 = 2^-9 + 2^-30 exactly, y = 2^-7 + 2^-9 + 2^-30 in
+    fp32 (exact), then bf16 keeps 2^-7 + 2^-9 = 0x3C20 (the 2^-30 term is
+    below half an ulp). The error 2^-30 is the output rounding alone: within
+    half an ulp and within the bound."""
+    res = np.array([[[0x3F81], [0xBF80], [0x3B00], [0x3080]]], dtype=np.uint16)
+    pre = np.ones((1, 4), dtype=np.float32)
+    out = O.h_aggregate_fwd(res, pre)
+    assert out[0, 0] == 0x3C20
+    exact, mag = O.h_aggregate_fwd_exact(res, pre)
+    assert exact[0, 0] == 2.0 ** -7 + 2.0 ** -9 + 2.0 ** -30
+    err = abs(float(O.widen_bf16(out)[0, 0]) - exact[0, 0])
+    assert err == 2.0 ** -30
+    assert err <= O.fwd_error_bound(out, mag)[0, 0]
+    assert err <= 0.5 * O.bf16_ulp(out)[0, 0]

@@ -114,6 +114,15 @@ MUTANTS = [
      "d_post = np.multiply(grad_post, np.multiply(pre,", "post derivative from the pre gate"),
     ("coeff_bwd", "np.concatenate([d_pre, d_post, grad_res], axis=1)",
      "np.concatenate([d_post, d_pre, grad_res], axis=1)", "pre and post columns swapped"),
+    # the helpers of the fp64 gates
+    ("h_aggregate", "    return np.ldexp(1.0, expo - 7)", "    return np.ldexp(1.0, expo - 8)",
+     "ulp of a 9-bit significand"),
+    ("h_aggregate", "    expo = np.where(v == 0.0, -126, np.maximum(e - 1, -126))",
+     "    expo = np.where(v == 0.0, -126, e - 1)", "subnormal ulp not clamped"),
+    ("h_aggregate", "    depth = 1 + int(np.log2(n))", "    depth = int(np.log2(n))",
+     "error bound without the product's rounding"),
+    ("h_aggregate", "    return 0.5 * bf16_ulp(out_bits) + (gamma",
+     "    return 1.0 * bf16_ulp(out_bits) + (gamma", "a whole ulp for the output rounding"),
 ]
 
 
