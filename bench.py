@@ -969,6 +969,28 @@ def summarize_stats(path: str) -> None:
               f"{float(r.get('Percentage', 0)):.2f} |")
 
 
+def summarize_db(path: str, match: str = "") -> None:
+    """Markdown table of a rocprofv3 database (rocpd SQLite, the default
+    output of ROCm 7): per kernel and grid size, the number of dispatches
+    and the mean / median / min / max duration, for kernels whose name
+    contains `match`."""
+    import sqlite3
+    con = sqlite3.connect(path)
+    groups: dict[tuple[str, int, int, int], list[float]] = {}
+    for name, gx, gy, wx, dur in con.execute(
+            "select name, grid_x, grid_y, workgroup_x, duration from kernels"):
+        if match and match not in name:
+            continue
+        groups.setdefault((_short_name(name), gx, gy, wx), []).append(dur / 1e3)
+    con.close()
+    print("| kernel | grid (work-items x, y) | block | dispatches | mean us | median us | "
+          "min us | max us |")
+    print("|---|---|---|---|---|---|---|---|")
+    for (name, gx, gy, wx), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        print(f"| {name} | {gx} x {gy} | {wx} | {len(v)} | {statistics.fmean(v):.3f} | "
+              f"{statistics.median(v):.3f} | {min(v):.3f} | {max(v):.3f} |")
+
+
 def summarize_pmc(paths: list[str]) -> None:
     """Per-kernel average of each counter (KiB for FETCH_SIZE / WRITE_SIZE)
     from rocprofv3 --pmc counter_collection.csv files, one row per kernel and
@@ -1105,8 +1127,14 @@ def main(argv: list[str] | None = None, gpu_runner=None) -> int:
                          "one launch shape (for rocprofv3 --pmc runs) and print one JSON line")
     ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV")
     ap.add_argument("--summarize-pmc", metavar="COUNTER_CSV", nargs="+")
+    ap.add_argument("--summarize-db", metavar="ROCPD_DB",
+                    help="per-kernel, per-grid durations from a rocprofv3 database")
+    ap.add_argument("--match", default="", help="with --summarize-db: kernel name filter")
     args = ap.parse_args(argv)
 
+    if args.summarize_db:
+        summarize_db(args.summarize_db, args.match)
+        return 0
     if args.summarize_stats:
         summarize_stats(args.summarize_stats)
         return 0

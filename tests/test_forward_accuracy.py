@@ -59,21 +59,20 @@ def test_forward_bit_exact_bandwidth_shape_with_outliers(device):
     assert c["fail"] == 0, c
 
 
-def test_forward_large_batch_sampled_tokens(device):
-    """T=8192, H=7168 (the largest bandwidth shape), run in one call; 192
-    sampled tokens compared with the oracle token by token (the oracle is
-    per-token), and a whole-tensor property: every output is within the fp64
-    gate."""
+def test_forward_large_batch_every_token(device):
+    """T=8192, H=7168 (the largest bandwidth shape, with 1% x64 outliers),
+    run in one call; every token compared with the oracle byte for byte,
+    1024 tokens at a time (the oracle is per token), and every output within
+    the fp64 gate."""
     T, H = 8192, 7168
-    say(f"forward parity T={T} H={H} sampled")
+    say(f"forward parity T={T} H={H} every token")
     host = make_inputs(T, H, seed=0, outliers=True)
     got = run_fwd(host, device)
-    rng = np.random.default_rng(99)
-    toks = np.unique(np.concatenate([[0, 1, T - 2, T - 1], rng.choice(T, 188, replace=False)]))
-    want = O.h_aggregate_fwd(host["residual"][toks], host["pre"][toks])
-    assert_bytes_equal(got[toks], want, "forward sampled tokens")
     for lo in range(0, T, 1024):
-        exact, mag = O.h_aggregate_fwd_exact(host["residual"][lo:lo + 1024], host["pre"][lo:lo + 1024])
+        r, p = host["residual"][lo:lo + 1024], host["pre"][lo:lo + 1024]
+        assert_bytes_equal(got[lo:lo + 1024], O.h_aggregate_fwd(r, p),
+                           f"forward T={T} tokens {lo}..{lo + 1023}")
+        exact, mag = O.h_aggregate_fwd_exact(r, p)
         assert O.classify_fwd(got[lo:lo + 1024], exact, mag)["fail"] == 0
 
 
