@@ -101,7 +101,10 @@ COEFF_SIGNATURES = {
                                + [c_int64, c_int64, c_int32]),
     "mhc_coeff_bwd": (c_int, [c_void_p] * 7 + [c_float] + [c_void_p] * 4
                       + [c_int64, c_int64, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
+    "mhc_coeff_bwd_noalloc": (c_int, [c_void_p] * 7 + [c_float] + [c_void_p] * 3
+                              + [c_int64, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
 }
+MHC_COEFF_SCRATCH_BYTES = 2 << 20
 
 MHC_PROBE_ABI_VERSION = 1
 

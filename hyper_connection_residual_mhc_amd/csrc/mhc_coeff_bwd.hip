@@ -42,6 +42,9 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "mhc_coeff_bwd.h"
 #include "mhc_lanes.h"
 #include "mhc_launch.h"
@@ -322,6 +325,18 @@ __global__ __launch_bounds__(64 * W) void coeff_fused_kernel(
   if (threadIdx.x == 0) atomicExch(arrived, 0u);
 }
 
+// One lane stores +0.0 (bit pattern 0) into the arrival counter: the set-up
+// of the no-allocation entry point's scratch array on a device.
+__global__ __launch_bounds__(64) void coeff_clear_counter_kernel(uint32_t* __restrict__ counter) {
+  if (threadIdx.x == 0) st(make_rsrc(counter, 4), 0, 0.0f);
+}
+
+// The no-allocation entry point's workspace: a fixed array in device memory,
+// one copy per GPU, held until the process ends. Host code never uses its
+// name as an address (that is a host-side stand-in): the device address
+// comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) uint32_t scratch[MHC_COEFF_SCRATCH_BYTES / 4];
+
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
@@ -383,11 +398,14 @@ mhc_status need_ptr(const void* p, const char* name) {
   return ok();
 }
 
+// Argument checks of a call. With has_workspace false (the no-allocation
+// entry point), the workspace is the library's own scratch array: it is not
+// checked and takes no part in the overlap tests.
 mhc_status validate(const float* mix, const float* pre, const float* post,
                     const float* grad_pre, const float* grad_post, const float* grad_res,
                     const float* alpha, float post_scale, const float* grad_mix,
                     const float* grad_b, const float* grad_alpha, const void* workspace,
-                    int64_t workspace_bytes, int64_t rows, int32_t n) {
+                    int64_t workspace_bytes, int64_t rows, int32_t n, bool has_workspace = true) {
   if (n != 2 && n != 4 && n != 8)
     return fail(MHC_ERROR_INVALID_VALUE, "the expansion rate n must be 2, 4 or 8 (got %d)", n);
   if (rows < 0 || rows > MHC_COEFF_MAX_ROWS)
@@ -397,7 +415,7 @@ mhc_status validate(const float* mix, const float* pre, const float* post,
     return fail(MHC_ERROR_INVALID_VALUE, "post_scale must be finite and positive (got %g)",
                 (double)post_scale);
   const int m = columns(n);
-  const int64_t need = workspace_need(rows, n);
+  const int64_t need = has_workspace ? workspace_need(rows, n) : 0;
   mhc_status st;
   if ((st = need_ptr(grad_b, "grad_b")) != MHC_SUCCESS) return st;
   if ((st = need_ptr(grad_alpha, "grad_alpha")) != MHC_SUCCESS) return st;
@@ -405,7 +423,7 @@ mhc_status validate(const float* mix, const float* pre, const float* post,
     const void* ps[] = {mix, pre, post, grad_pre, grad_post, grad_res, alpha, grad_mix, workspace};
     const char* names[] = {"mix", "pre", "post", "grad_pre", "grad_post", "grad_res", "alpha",
                            "grad_mix", "workspace"};
-    for (int i = 0; i < 9; ++i)
+    for (int i = 0; i < (has_workspace ? 9 : 8); ++i)
       if ((st = need_ptr(ps[i], names[i])) != MHC_SUCCESS) return st;
   }
   if (workspace_bytes < need)
@@ -418,11 +436,12 @@ mhc_status validate(const float* mix, const float* pre, const float* post,
                        range(alpha, rows > 0 ? 12 : 0, "alpha")};
   const Range outs[] = {range(grad_mix, rows * m * 4, "grad_mix"), range(grad_b, m * 4, "grad_b"),
                         range(grad_alpha, 12, "grad_alpha"), range(workspace, need, "workspace")};
-  for (int a = 0; a < 4; ++a) {
+  const int nout = has_workspace ? 4 : 3;
+  for (int a = 0; a < nout; ++a) {
     for (int b = 0; b < 7; ++b)
       if (overlap(outs[a], ins[b]))
         return fail(MHC_ERROR_ALIASING, "output %s overlaps input %s", outs[a].name, ins[b].name);
-    for (int b = a + 1; b < 4; ++b)
+    for (int b = a + 1; b < nout; ++b)
       if (overlap(outs[a], outs[b]))
         return fail(MHC_ERROR_ALIASING, "output %s overlaps output %s", outs[a].name,
                     outs[b].name);
@@ -534,6 +553,47 @@ mhc_status run(const CoeffArgs& a, int32_t n, int32_t launches, hipStream_t s, h
   return launch_status(e, "coefficient backward (reduction)");
 }
 
+// The scratch array's device address on each device, looked up once per
+// device with that device current, and whether its arrival counter has been
+// cleared there.
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::atomic<bool> g_scratch_cleared[kMaxDevices];
+
+// The current device's scratch address; on the first call on a device, also
+// enqueue on `s` the kernel that zeroes its arrival counter (device memory
+// starts zeroed at load; clearing once more makes the first call independent
+// of that).
+mhc_status device_scratch(hipStream_t s, void** out) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return fail(MHC_ERROR_HIP, "hipGetDevice failed: %s", hipGetErrorName(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MHC_ERROR_INVALID_VALUE, "device %d is beyond the %d devices supported", dev,
+                kMaxDevices);
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = ptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr)
+    return fail(MHC_ERROR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                hipGetErrorName(g_scratch_err[dev]));
+  if (!g_scratch_cleared[dev].exchange(true)) {
+    const hipError_t c = launch_kernel(coeff_clear_counter_kernel, dim3(1), dim3(64), s, nullptr,
+                                       nullptr, static_cast<uint32_t*>(g_scratch_ptr[dev]));
+    if (c != hipSuccess) {
+      g_scratch_cleared[dev] = false;
+      return launch_status(c, "coefficient backward (scratch set-up)");
+    }
+  }
+  *out = g_scratch_ptr[dev];
+  return ok();
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -583,6 +643,40 @@ mhc_status mhc_coeff_bwd(const float* mix, const float* pre, const float* post,
                                 grad_mix, grad_b, grad_alpha, workspace, rows);
   return run(a, n, launches, static_cast<hipStream_t>(stream),
              static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event));
+}
+
+mhc_status mhc_coeff_bwd_noalloc(const float* mix, const float* pre, const float* post,
+                                 const float* grad_pre, const float* grad_post,
+                                 const float* grad_res, const float* alpha, float post_scale,
+                                 float* grad_mix, float* grad_b, float* grad_alpha, int64_t rows,
+                                 int32_t n, int32_t launches, void* stream, void* start_event,
+                                 void* stop_event) {
+  // Sizes first, on the host alone: nothing is touched for a call that
+  // does not fit the scratch array.
+  if (n != 2 && n != 4 && n != 8)
+    return fail(MHC_ERROR_INVALID_VALUE, "the expansion rate n must be 2, 4 or 8 (got %d)", n);
+  if (rows < 0 || rows > MHC_COEFF_MAX_ROWS)
+    return fail(MHC_ERROR_INVALID_VALUE, "rows must be in [0, %lld] (got %lld)",
+                (long long)MHC_COEFF_MAX_ROWS, (long long)rows);
+  const int64_t need = workspace_need(rows, n);
+  if (need > MHC_COEFF_SCRATCH_BYTES)
+    return fail(MHC_ERROR_INVALID_VALUE,
+                "%lld rows at n=%d need %lld bytes of workspace, more than the %lld-byte scratch "
+                "array of the no-allocation entry point (use mhc_coeff_bwd with a workspace)",
+                (long long)rows, n, (long long)need, (long long)MHC_COEFF_SCRATCH_BYTES);
+  if (launches < 0 || launches > 2)
+    return fail(MHC_ERROR_INVALID_VALUE, "launches must be 0, 1 or 2 (got %d)", launches);
+  // Every other argument as mhc_coeff_bwd checks it.
+  mhc_status st = validate(mix, pre, post, grad_pre, grad_post, grad_res, alpha, post_scale,
+                           grad_mix, grad_b, grad_alpha, nullptr, 0, rows, n, false);
+  if (st != MHC_SUCCESS) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if (rows > 0 && (st = device_scratch(s, &ws)) != MHC_SUCCESS) return st;
+  const CoeffArgs a = make_args(mix, pre, post, grad_pre, grad_post, grad_res, alpha, post_scale,
+                                grad_mix, grad_b, grad_alpha, ws, rows);
+  return run(a, n, launches, s, static_cast<hipEvent_t>(start_event),
+             static_cast<hipEvent_t>(stop_event));
 }
 
 }  // extern "C"

@@ -69,7 +69,9 @@
  *
  * Rules: calls enqueue one or two kernels on `stream` (a hipStream_t cast to
  * void*, NULL = null stream) and never synchronise; inputs must stay valid
- * until the stream reaches them. The library allocates nothing. n not in {2,4,8},
+ * until the stream reaches them. The library allocates no memory at run time
+ * (mhc_coeff_bwd_noalloc's fixed array is part of the loaded device code).
+ * n not in {2,4,8},
  * R < 0, R > MHC_COEFF_MAX_ROWS, c not finite and positive, a NULL or
  * non-4-byte-aligned pointer that the call needs (the row tensors, alpha and
  * the workspace when R > 0; grad_b and grad_alpha always), or a workspace
@@ -100,6 +102,10 @@ extern "C" {
 /* Most rows one call accepts (2^28: keeps every workspace byte offset and
  * buffer range within 31 bits at every expansion rate). */
 #define MHC_COEFF_MAX_ROWS (1LL << 28)
+
+/* Bytes of the fixed device array that mhc_coeff_bwd_noalloc uses as its
+ * workspace (one array per GPU the library runs on). */
+#define MHC_COEFF_SCRATCH_BYTES (2LL << 20)
 
 int mhc_coeff_abi_version(void);
 
@@ -134,6 +140,37 @@ mhc_status mhc_coeff_bwd(const float* mix, const float* pre, const float* post,
                          float* grad_alpha, void* workspace, int64_t workspace_bytes,
                          int64_t rows, int32_t n, int32_t launches, void* stream,
                          void* start_event, void* stop_event);
+
+/*
+ * No-allocation variant of mhc_coeff_bwd, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Same operation, arguments and results as
+ * mhc_coeff_bwd, except that the workspace is a fixed array of
+ * MHC_COEFF_SCRATCH_BYTES (2 MiB) inside the library's device code, one per
+ * GPU, held until the process ends; the caller still passes every input
+ * and output. The call allocates nothing (no hipMalloc, no hipFree).
+ *   - Limit: mhc_coeff_bwd_workspace_bytes(R, n) must not exceed
+ *     MHC_COEFF_SCRATCH_BYTES, i.e. at most 47,656 chunks of 64 rows at
+ *     n = 2 (3,049,984 rows), 19,415 at n = 4 (1,242,560 rows) and 6,315 at
+ *     n = 8 (404,160 rows); larger calls give MHC_ERROR_INVALID_VALUE before
+ *     anything else is touched.
+ *   - Sharing: every call on one GPU uses that GPU's array, which keeps the
+ *     last call's contents. Calls that overlap in time on one GPU (other
+ *     streams, other threads) race and give undefined results; calls one
+ *     after another on one stream are safe.
+ *   - Set-up: the first call on a device looks up the array's address there
+ *     (hipGetSymbolAddress) and enqueues, ahead of its own kernels, a
+ *     one-wave kernel that zeroes the array's arrival counter; every
+ *     completed call leaves the counter at zero. start_event / stop_event
+ *     time the operation's kernels, not that set-up kernel.
+ *   - R == 0 touches no scratch (it only writes the +0.0 sums).
+ */
+mhc_status mhc_coeff_bwd_noalloc(const float* mix, const float* pre, const float* post,
+                                 const float* grad_pre, const float* grad_post,
+                                 const float* grad_res, const float* alpha, float post_scale,
+                                 float* grad_mix, float* grad_b, float* grad_alpha, int64_t rows,
+                                 int32_t n, int32_t launches, void* stream, void* start_event,
+                                 void* stop_event);
 
 #ifdef __cplusplus
 }

@@ -66,6 +66,7 @@ def test_kernels_present(asm):
     if any("coeff_" in n for n in names):
         assert sum("coeff_partial_kernel" in n for n in names) == 3
         assert sum("coeff_reduce_kernel" in n for n in names) == 1
+        assert sum("coeff_clear_counter_kernel" in n for n in names) == 1
         assert not any("hagg_" in n or "probe" in n for n in names)
         return
     if any("probe" in n for n in names):
@@ -181,7 +182,7 @@ def test_divisions_only_where_the_operation_has_one(asm):
         fixups = len(re.findall(r"^\s*v_div_fixup_f32\b", body, flags=re.M))
         if "hagg_" in name:
             assert not re.search(r"\bv_(div_\w+|rcp_\w+)", body), name
-        elif "coeff_reduce" in name:
+        elif "coeff_reduce" in name or "coeff_clear" in name:
             assert fixups == 0, name
         elif "coeff_" in name:
             n = int(re.search(r"kernelILi(\d+)E", name).group(1))

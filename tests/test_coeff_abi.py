@@ -26,7 +26,7 @@ def lib(built_library):
 def test_header_declarations_are_all_exported(lib):
     text = re.sub(r"/\*.*?\*/", "", _build.COEFF_HEADER.read_text(), flags=re.S)
     names = sorted(set(re.findall(r"\b(mhc_\w+)\s*\(", text)))
-    assert len(names) == 6, names
+    assert len(names) == 7, names
     out = subprocess.run(["nm", "-D", "--defined-only", str(_build.COEFF_LIB_PATH)],
                          capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (mhc_\w+)$", out, flags=re.M))
@@ -41,6 +41,8 @@ def test_constants_match_the_header(lib):
     assert f"#define MHC_COEFF_ABI_VERSION {_lib.MHC_COEFF_ABI_VERSION}" in text
     assert f"#define MHC_COEFF_CHUNK {_lib.MHC_COEFF_CHUNK}" in text
     assert "#define MHC_COEFF_MAX_ROWS (1LL << 28)" in text and _lib.MHC_COEFF_MAX_ROWS == 1 << 28
+    assert "#define MHC_COEFF_SCRATCH_BYTES (2LL << 20)" in text
+    assert _lib.MHC_COEFF_SCRATCH_BYTES == 2 << 20
     assert lib.mhc_coeff_abi_version() == _lib.MHC_COEFF_ABI_VERSION
 
 
@@ -182,3 +184,43 @@ def test_binding_rejects_host_tensors(lib):
         coeff.mhc_coeff_bwd(z(4, 24), z(4, 4), z(4, 4), z(4, 4), z(4, 4), z(4, 16), z(3), 2.0)
     with pytest.raises(ValueError, match=r"\[R, n\]"):
         coeff.mhc_coeff_bwd(z(4, 24), z(4, 3), z(4, 4), z(4, 4), z(4, 4), z(4, 16), z(3), 2.0)
+
+
+def _noalloc_max_rows(n: int) -> int:
+    """Most rows the no-allocation entry point takes: whole 64-row chunks
+    whose (m + 3) sums fit the scratch array after its 256-byte header."""
+    m = 2 * n + n * n
+    return (_lib.MHC_COEFF_SCRATCH_BYTES - 256) // ((m + 3) * 4) * 64
+
+
+@pytest.mark.parametrize("n,rows", [(2, 3049984), (4, 1242560), (8, 404160)])
+def test_noalloc_limit_is_the_scratch_size(lib, n, rows):
+    """The header's row limits are the scratch array's capacity, and a call
+    one chunk past them is refused before anything else is touched (no GPU
+    needed: the size check comes first)."""
+    assert _noalloc_max_rows(n) == rows
+    assert lib.mhc_coeff_bwd_workspace_bytes(rows, n) <= _lib.MHC_COEFF_SCRATCH_BYTES
+    assert lib.mhc_coeff_bwd_workspace_bytes(rows + 1, n) > _lib.MHC_COEFF_SCRATCH_BYTES
+    m = 2 * n + n * n
+    p = [BASE + k * GiB for k in range(11)]
+    args = p[:7] + [2.0] + p[7:10]
+    assert lib.mhc_coeff_bwd_noalloc(*args, rows + 1, n, 0, None, None,
+                                     None) == MHC_ERROR_INVALID_VALUE
+    assert b"scratch" in lib.mhc_coeff_last_error_message()
+    assert m > 0
+
+
+def test_noalloc_rejects_bad_arguments_before_any_hip_call(lib):
+    p = [BASE + k * GiB for k in range(11)]
+    ok_args = p[:7] + [2.0] + p[7:10]
+    call = lambda args, rows=100, n=4, launches=0: lib.mhc_coeff_bwd_noalloc(
+        *args, rows, n, launches, None, None, None)
+    assert call(ok_args, n=3) == MHC_ERROR_INVALID_VALUE
+    assert call(ok_args, rows=-1) == MHC_ERROR_INVALID_VALUE
+    assert call(ok_args, launches=3) == MHC_ERROR_INVALID_VALUE
+    bad_scale = p[:7] + [0.0] + p[7:10]
+    assert call(bad_scale) == MHC_ERROR_INVALID_VALUE
+    aliased = p[:7] + [2.0] + [p[0]] + p[8:10]          # grad_mix over mix
+    assert call(aliased) == MHC_ERROR_ALIASING
+    misaligned = p[:7] + [2.0] + [p[7] + 2] + p[8:10]
+    assert call(misaligned) == MHC_ERROR_INVALID_VALUE
