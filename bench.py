@@ -199,13 +199,19 @@ def make_sets(T: int, H: int, n: int, dev, hc: int = HC) -> list[BufferSet]:
 
 
 def copy_probe(dev, nbytes: int = 1 << 28, reps: int = 3) -> None:
-    """A plain device copy of known size (read nbytes, write nbytes), run
-    outside the timed region so counter runs can scale FETCH/WRITE sizes."""
+    """A plain copy of known size, run outside the timed region so that
+    counter runs can scale FETCH_SIZE / WRITE_SIZE: the measurement
+    library's 1:1 stream (stream_probe_kernel<1, 1, 2>: reads nbytes, writes
+    nbytes, nothing else), `reps` times."""
     import torch
+    from hyper_connection_residual_mhc_amd import _lib
+    plib = _lib.probe_lib()
     src = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
     dst = torch.empty_like(src)
+    sh = int(torch.cuda.current_stream(dev).cuda_stream)
     for _ in range(reps):
-        dst.copy_(src)
+        _lib.check_probe(plib.mhc_stream_probe(src.data_ptr(), nbytes, dst.data_ptr(), nbytes,
+                                               1, 1, sh, None, None))
     torch.cuda.synchronize()
 
 
