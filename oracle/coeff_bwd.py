@@ -53,6 +53,15 @@ reading instead):
 * row_sum is this repository's fixed two-stage order (see `row_sum`); it
   depends only on the number of rows.
 
+* Input precision (page section Testing Done: the sibling implementation's
+  tests run FP16, BF16 and FP32 inputs; section Performance Method: BF16 is
+  the primary matrix). With 16-bit inputs (`coeff_bwd_typed`), the six row
+  tensors mix, pre, post, grad_pre, grad_post and grad_res are bf16 or fp16
+  bit patterns; each value is widened to fp32 exactly, the computation above
+  runs unchanged in fp32, grad_mix is rounded once to the input's format
+  (round to nearest even, subnormals kept, overflow to infinity), and alpha,
+  grad_b and grad_alpha stay fp32 (the page's fp32 partial sums).
+
 Arithmetic model: as in oracle.h_aggregate, every fp32 operation is one
 numpy float32 ufunc call; numpy vectorises only across independent rows or
 columns. No np.sum, np.dot or einsum appears in an fp32 path.
@@ -63,6 +72,8 @@ from __future__ import annotations
 import math
 
 import numpy as np
+
+from oracle.h_aggregate import bf16_rne, widen_bf16
 
 # Rows per first-stage chunk and lanes of the second stage of row_sum.
 CHUNK = 64
@@ -163,6 +174,55 @@ def coeff_bwd(mix, pre, post, grad_pre, grad_post, grad_res, alpha, post_scale, 
     grad_b = row_sum(d)
     grad_alpha = row_sum(e)
     return grad_mix.astype(np.float32), grad_b, grad_alpha
+
+
+# Storage formats of the six row tensors and grad_mix.
+DTYPES = ("f32", "bf16", "f16")
+ROW_INPUTS = ("mix", "pre", "post", "grad_pre", "grad_post", "grad_res")
+
+
+def widen(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored values -> float32, exactly: f32 as is; bf16 and f16 from their
+    uint16 bit patterns (every bf16 and fp16 value is an fp32 value)."""
+    if dtype == "f32":
+        if x.dtype != np.float32:
+            raise ValueError("f32 tensors must be float32")
+        return x
+    if x.dtype != np.uint16:
+        raise ValueError(f"{dtype} tensors must be uint16 bit patterns")
+    if dtype == "bf16":
+        return widen_bf16(x)
+    if dtype == "f16":
+        with np.errstate(invalid="ignore"):
+            return x.view(np.float16).astype(np.float32)
+    raise ValueError(f"dtype must be one of {DTYPES}")
+
+
+def narrow(x: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 -> the stored format, rounded to nearest even (subnormals
+    kept, overflow to infinity): f32 unchanged; bf16 and f16 as uint16 bit
+    patterns."""
+    x = np.asarray(x, dtype=np.float32)
+    if dtype == "f32":
+        return x
+    if dtype == "bf16":
+        return bf16_rne(x)
+    if dtype == "f16":
+        with np.errstate(over="ignore"):
+            return x.astype(np.float16).view(np.uint16)
+    raise ValueError(f"dtype must be one of {DTYPES}")
+
+
+def coeff_bwd_typed(mix, pre, post, grad_pre, grad_post, grad_res, alpha, post_scale, n,
+                    dtype: str) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """The epilogue on stored inputs of the given format: the six row
+    tensors widened exactly, coeff_bwd in fp32, grad_mix narrowed once.
+
+    Returns (grad_mix [R, m] in the stored format, grad_b float32 [m],
+    grad_alpha float32 [3])."""
+    rows = [widen(np.asarray(t), dtype) for t in (mix, pre, post, grad_pre, grad_post, grad_res)]
+    gm, gb, ga = coeff_bwd(*rows, alpha, post_scale, n)
+    return narrow(gm, dtype), gb, ga
 
 
 def coeff_bwd_exact(mix, pre, post, grad_pre, grad_post, grad_res, alpha, post_scale, n

@@ -333,3 +333,129 @@ def test_argument_checks():
     with pytest.raises(ValueError):
         cb.coeff_bwd(d["mix"].astype(np.float64), d["pre"], d["post"], d["grad_pre"],
                      d["grad_post"], d["grad_res"], d["alpha"], 2.0, 4)
+
+
+# ---------------------------------------------------------------------------
+# 16-bit inputs (bf16 / fp16 row tensors; grad_mix in the input's format)
+# ---------------------------------------------------------------------------
+
+def _f16_nearest(x: float) -> float:
+    """Independent round-to-nearest-even of a finite float to IEEE binary16,
+    by integer rounding of x / quantum in float64 (exact: the quotient is a
+    power-of-two scaling; Python's round() breaks ties to even)."""
+    a = abs(x)
+    if a == 0.0:
+        return x
+    m, e = math.frexp(a)                      # a = m 2^e, m in [0.5, 1)
+    quantum = 2.0 ** max(e - 11, -24)         # 11 significant bits; subnormal spacing 2^-24
+    r = round(a / quantum) * quantum
+    if r > 65504.0:                          # 65520 and up round past the largest finite
+        r = math.inf
+    return math.copysign(r, x)
+
+
+def _f16_decode(b: int) -> float:
+    """binary16 bit pattern -> value, from the format's definition."""
+    s, e, f = b >> 15, (b >> 10) & 0x1F, b & 0x3FF
+    if e == 0x1F:
+        return math.nan if f else math.copysign(math.inf, -1.0 if s else 1.0)
+    v = (f / 1024.0) * 2.0 ** -14 if e == 0 else (1.0 + f / 1024.0) * 2.0 ** (e - 15)
+    return -v if s else v
+
+
+def test_f16_widening_is_exact_on_every_pattern():
+    b = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = cb.widen(b, "f16").astype(np.float64)
+    want = np.array([_f16_decode(int(v)) for v in b])
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def test_f16_narrowing_matches_an_independent_rounding():
+    """Hand ties and overflow, then every fp32 binade from 2^-27 to 2^16:
+    random patterns plus each binade's exact ties and their neighbours."""
+    hand = {1.0 + 2.0 ** -11: 0x3C00, 1.0 + 3 * 2.0 ** -11: 0x3C02, 65504.0: 0x7BFF,
+            65519.996: 0x7BFF, 65520.0: 0x7C00, 2.0 ** -24: 0x0001, 2.0 ** -25: 0x0000,
+            3 * 2.0 ** -26: 0x0001, -2.0 ** -14: 0x8400, 1e-9: 0x0000}
+    for x, bits in hand.items():
+        assert int(cb.narrow(np.array([x], np.float32), "f16")[0]) == bits, x
+    rng = np.random.default_rng(16)
+    pats = []
+    for e in range(-27 + 127, 17 + 127):
+        base = np.uint32(e) << np.uint32(23)
+        mant = rng.integers(0, 1 << 23, 600, dtype=np.uint32)
+        ties = (np.arange(0, 1 << 10, dtype=np.uint32) << np.uint32(13)) | np.uint32(0x1000)
+        pats += [base | mant, base | ties, base | (ties + 1), base | (ties - 1)]
+    p = np.concatenate(pats)
+    p = np.concatenate([p, p | np.uint32(0x80000000)])
+    x = p.view(np.float32)
+    got = cb.widen(cb.narrow(x, "f16"), "f16").astype(np.float64)
+    want = np.array([_f16_nearest(float(v)) for v in x])
+    assert np.array_equal(got, want)
+    assert np.array_equal(np.signbit(got), np.signbit(want))
+
+
+def test_bf16_and_f32_formats_round_trip():
+    x = np.array([1.0, -2.5, 3e38, 1e-40], np.float32)
+    assert np.array_equal(cb.narrow(x, "f32"), x) and cb.widen(x, "f32") is x
+    b = cb.narrow(x, "bf16")
+    assert b.dtype == np.uint16 and np.array_equal(cb.widen(b, "bf16")[:2], x[:2])
+    with pytest.raises(ValueError):
+        cb.widen(x, "f16")
+    with pytest.raises(ValueError):
+        cb.narrow(x, "f8")
+
+
+def _typed_inputs(R, n, seed, dtype, c=2.0):
+    d = _inputs(R, n, seed, c)
+    return {k: (cb.narrow(v, dtype) if k != "alpha" else v) for k, v in d.items()}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_typed_hand_case_one_row_n2(dtype):
+    # The fp32 hand case's inputs and results are exact in both 16-bit
+    # formats, so the typed epilogue gives the same values.
+    f = lambda v: cb.narrow(np.array([v], np.float32), dtype)
+    mix = f([1, 2, 3, 4, 5, 6, 7, 8])
+    pre, post = f([0.5, 0.25]), f([1.0, 0.5])
+    gp, gq, gr = f([1, 2]), f([1, -1]), f([1, 2, 3, 4])
+    alpha = np.array([2.0, 0.5, 1.0], np.float32)
+    gm, gb, ga = cb.coeff_bwd_typed(mix, pre, post, gp, gq, gr, alpha, 2.0, 2, dtype)
+    assert gm.dtype == np.uint16 and gb.dtype == np.float32 and ga.dtype == np.float32
+    assert cb.widen(gm, dtype)[0].tolist() == [0.5, 0.75, 0.25, -0.1875, 1, 2, 3, 4]
+    assert gb.tolist() == [0.25, 0.375, 0.5, -0.375, 1, 2, 3, 4]
+    assert ga.tolist() == [1.0, 0.0, 70.0]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("n,R", [(2, 300), (4, 2048), (8, 257)])
+def test_typed_within_error_bounds_of_fp64(dtype, n, R):
+    """grad_mix within half an ulp of the 16-bit format plus the fp32
+    evaluation error; the fp32 sums within the fp32 bounds: the sums are
+    taken from the fp32 derivatives, never from the rounded grad_mix."""
+    d = _typed_inputs(R, n, 30 + n, dtype)
+    gm, gb, ga = cb.coeff_bwd_typed(*(d[k] for k in cb.ROW_INPUTS), d["alpha"], 2.0, n, dtype)
+    w = {k: cb.widen(d[k], dtype) for k in cb.ROW_INPUTS}
+    ex = cb.coeff_bwd_exact(*(w[k] for k in cb.ROW_INPUTS), d["alpha"], 2.0, n)
+    k = cb.groups(n)
+    al = np.abs(d["alpha"].astype(np.float64))[k][None, :]
+    got = cb.widen(gm, dtype).astype(np.float64)
+    bits = 8 if dtype == "bf16" else 11
+    half_ulp = np.ldexp(1.0, np.frexp(np.abs(got))[1] - bits - 1)
+    half_ulp = np.maximum(half_ulp, 2.0 ** -134 if dtype == "bf16" else 2.0 ** -25)
+    assert np.all(np.abs(got - ex["grad_mix"]) <= half_ulp * 1.0001 + 6 * U * al * ex["mag_d"]
+                  + 1e-44)
+    rb = cb.reduction_error_bound(R)
+    assert np.all(np.abs(gb - ex["grad_b"]) <= (rb + 5 * U) * ex["mag_b"] * 1.01)
+    ra = cb.reduction_error_bound(R, max(n, n * n))
+    assert np.all(np.abs(ga - ex["grad_alpha"]) <= (ra + 6 * U) * ex["mag_alpha"] * 1.01)
+
+
+def test_typed_f32_is_the_plain_epilogue():
+    d = _inputs(70, 4, 12)
+    a = cb.coeff_bwd_typed(*(d[k] for k in cb.ROW_INPUTS), d["alpha"], 2.0, 4, "f32")
+    b = _run(d, 2.0, 4)
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))

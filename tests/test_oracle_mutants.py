@@ -114,6 +114,18 @@ MUTANTS = [
      "d_post = np.multiply(grad_post, np.multiply(pre,", "post derivative from the pre gate"),
     ("coeff_bwd", "np.concatenate([d_pre, d_post, grad_res], axis=1)",
      "np.concatenate([d_post, d_pre, grad_res], axis=1)", "pre and post columns swapped"),
+    # 16-bit inputs of the coefficient epilogue
+    ("coeff_bwd", "            return x.view(np.float16).astype(np.float32)",
+     "            return widen_bf16(x)", "fp16 patterns widened as bf16"),
+    ("coeff_bwd", "            return x.astype(np.float16).view(np.uint16)",
+     "            return widen_bf16(bf16_rne(x)).astype(np.float16).view(np.uint16)",
+     "fp16 rounding through bf16 (double rounding)"),
+    ("coeff_bwd", "    return narrow(gm, dtype), gb, ga",
+     "    return narrow(gm, dtype), widen(narrow(gb, dtype), dtype), ga",
+     "bias sums rounded to the input format"),
+    ("coeff_bwd", "    gm, gb, ga = coeff_bwd(*rows, alpha, post_scale, n)",
+     "    gm, gb, ga = coeff_bwd(*rows[:5], widen(narrow(rows[5], 'bf16'), 'bf16'), alpha, "
+     "post_scale, n)", "residual gradient re-rounded to bf16"),
     # the helpers of the fp64 gates
     ("h_aggregate", "    return np.ldexp(1.0, expo - 7)", "    return np.ldexp(1.0, expo - 8)",
      "ulp of a 9-bit significand"),
