@@ -1148,7 +1148,8 @@ def main(argv: list[str] | None = None, gpu_runner=None) -> int:
         summarize_pmc(args.summarize_pmc)
         return 0
     if args.counter_case:
-        print(json.dumps(run_counter_case(args.counter_case, args.tokens, args.hidden)))
+        print(json.dumps(run_counter_case(args.counter_case, args.tokens, args.hidden,
+                                          nsets=args.sets)))
         return 0
     if args.sweep:
         if args.gpus != 1:

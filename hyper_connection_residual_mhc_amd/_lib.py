@@ -87,7 +87,7 @@ SIGNATURES = {
                                          POINTER(mhc_launch), POINTER(c_int64)]),
 }
 
-MHC_COEFF_ABI_VERSION = 3
+MHC_COEFF_ABI_VERSION = 4
 MHC_COEFF_CHUNK = 64
 MHC_COEFF_MAX_ROWS = 1 << 28
 
@@ -103,7 +103,13 @@ COEFF_SIGNATURES = {
                       + [c_int64, c_int64, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
     "mhc_coeff_bwd_noalloc": (c_int, [c_void_p] * 7 + [c_float] + [c_void_p] * 3
                               + [c_int64, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
+    "mhc_coeff_bwd_validate_ex": (c_int, [c_void_p] * 7 + [c_float] + [c_void_p] * 4
+                                  + [c_int64, c_int64, c_int32, c_int32]),
+    "mhc_coeff_bwd_ex": (c_int, [c_void_p] * 7 + [c_float] + [c_void_p] * 4
+                         + [c_int64, c_int64, c_int32, c_int32, c_int32, c_void_p, c_void_p,
+                            c_void_p]),
 }
+MHC_COEFF_F32, MHC_COEFF_BF16, MHC_COEFF_F16 = 0, 1, 2
 MHC_COEFF_SCRATCH_BYTES = 2 << 20
 
 MHC_PROBE_ABI_VERSION = 1

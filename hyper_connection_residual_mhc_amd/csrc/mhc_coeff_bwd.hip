@@ -46,6 +46,7 @@
 #include <mutex>
 
 #include "mhc_coeff_bwd.h"
+#include "mhc_convert.h"
 #include "mhc_lanes.h"
 #include "mhc_launch.h"
 
@@ -65,6 +66,36 @@ __device__ __forceinline__ float ld(Rsrc rs, uint32_t byte_off) {
 
 __device__ __forceinline__ void st(Rsrc rs, uint32_t byte_off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, byte_off, 0, 0);
+}
+
+// Storage format F of the row tensors and grad_mix (MHC_COEFF_F32, _BF16,
+// _F16): element bytes, the exact widening of a stored element and the
+// round-to-nearest-even narrowing of a result (mhc_convert.h).
+template <int F> constexpr int elem_bytes() { return F == MHC_COEFF_F32 ? 4 : 2; }
+
+template <int F>
+__device__ __forceinline__ float ld_elem(Rsrc rs, uint32_t index) {
+  if constexpr (F == MHC_COEFF_F32) {
+    return ld(rs, index * 4);
+  } else {
+    const uint16_t b = __builtin_amdgcn_raw_buffer_load_b16(rs, index * 2, 0, 0);
+    return F == MHC_COEFF_BF16 ? bf16_f32(b) : f16_f32(b);
+  }
+}
+
+// The fp32 value is first fixed in a register (an empty asm that takes and
+// returns it): otherwise the compiler folds the product that made it into
+// the fp16 conversion (v_fma_mixlo_f16), rounding once instead of rounding
+// the product to fp32 and then to fp16.
+template <int F>
+__device__ __forceinline__ void st_elem(Rsrc rs, uint32_t index, float v) {
+  if constexpr (F == MHC_COEFF_F32) {
+    st(rs, index * 4, v);
+  } else {
+    __asm__ volatile("" : "+v"(v));
+    const uint16_t b = F == MHC_COEFF_BF16 ? to_bf16(v) : to_f16(v);
+    __builtin_amdgcn_raw_buffer_store_b16(b, rs, index * 2, 0, 0);
+  }
 }
 
 // The halving tree over the wave's 64 lanes: for off = 32, 16, 8, 4, 2, 1,
@@ -114,53 +145,56 @@ struct Tile {
   static constexpr int kFloats = kRows * kTileStride;
 };
 
-template <int N>
+template <int N, int F>
 __device__ __forceinline__ void chunk_sums(
-    const float* __restrict__ mix, const float* __restrict__ pre,
-    const float* __restrict__ post, const float* __restrict__ grad_pre,
-    const float* __restrict__ grad_post, const float* __restrict__ grad_res,
-    const float* __restrict__ alpha, float post_scale, float* __restrict__ grad_mix,
-    float* __restrict__ partial, int64_t rows, uint32_t chunks, uint32_t c, uint32_t lane,
-    bool active, float* tile) {
+    const void* __restrict__ mix, const void* __restrict__ pre, const void* __restrict__ post,
+    const void* __restrict__ grad_pre, const void* __restrict__ grad_post,
+    const void* __restrict__ grad_res, const float* __restrict__ alpha, float post_scale,
+    void* __restrict__ grad_mix, float* __restrict__ partial, int64_t rows, uint32_t chunks,
+    uint32_t c, uint32_t lane, bool active, float* tile) {
   constexpr int M = 2 * N + N * N;
   constexpr int V = M + 3;
+  constexpr int64_t E = elem_bytes<F>();
   const int64_t r0 = static_cast<int64_t>(c) * kChunk;
   int64_t valid = rows - r0;
   valid = valid < 0 ? 0 : (valid > kChunk ? kChunk : valid);
 
   // Resources cover exactly the chunk's valid rows.
-  const Rsrc rs_mix = make_rsrc(mix + r0 * M, valid * M * 4);
-  const Rsrc rs_pre = make_rsrc(pre + r0 * N, valid * N * 4);
-  const Rsrc rs_post = make_rsrc(post + r0 * N, valid * N * 4);
-  const Rsrc rs_gpre = make_rsrc(grad_pre + r0 * N, valid * N * 4);
-  const Rsrc rs_gpost = make_rsrc(grad_post + r0 * N, valid * N * 4);
-  const Rsrc rs_gres = make_rsrc(grad_res + r0 * N * N, valid * N * N * 4);
-  const Rsrc rs_gmix = make_rsrc(grad_mix + r0 * M, valid * M * 4);
+  const auto at = [r0](const void* base, int64_t width) {
+    return static_cast<const char*>(base) + r0 * width * E;
+  };
+  const Rsrc rs_mix = make_rsrc(at(mix, M), valid * M * E);
+  const Rsrc rs_pre = make_rsrc(at(pre, N), valid * N * E);
+  const Rsrc rs_post = make_rsrc(at(post, N), valid * N * E);
+  const Rsrc rs_gpre = make_rsrc(at(grad_pre, N), valid * N * E);
+  const Rsrc rs_gpost = make_rsrc(at(grad_post, N), valid * N * E);
+  const Rsrc rs_gres = make_rsrc(at(grad_res, N * N), valid * N * N * E);
+  const Rsrc rs_gmix = make_rsrc(at(grad_mix, M), valid * M * E);
   const float a_pre = alpha[0], a_post = alpha[1], a_res = alpha[2];
 
   float d[M];
   float x[M];
 #pragma unroll
-  for (int j = 0; j < M; ++j) x[j] = ld(rs_mix, (lane * M + j) * 4);
+  for (int j = 0; j < M; ++j) x[j] = ld_elem<F>(rs_mix, lane * M + j);
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    const float p = ld(rs_pre, (lane * N + i) * 4);
-    const float gp = ld(rs_gpre, (lane * N + i) * 4);
+    const float p = ld_elem<F>(rs_pre, lane * N + i);
+    const float gp = ld_elem<F>(rs_gpre, lane * N + i);
     d[i] = gp * (p * (1.0f - p));
   }
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    const float q = ld(rs_post, (lane * N + i) * 4);
-    const float gq = ld(rs_gpost, (lane * N + i) * 4);
+    const float q = ld_elem<F>(rs_post, lane * N + i);
+    const float gq = ld_elem<F>(rs_gpost, lane * N + i);
     d[N + i] = gq * (q * (1.0f - q / post_scale));
   }
 #pragma unroll
-  for (int i = 0; i < N * N; ++i) d[2 * N + i] = ld(rs_gres, (lane * N * N + i) * 4);
+  for (int i = 0; i < N * N; ++i) d[2 * N + i] = ld_elem<F>(rs_gres, lane * N * N + i);
 
 #pragma unroll
   for (int j = 0; j < M; ++j) {
     const float a = j < N ? a_pre : (j < 2 * N ? a_post : a_res);
-    st(rs_gmix, (lane * M + j) * 4, a * d[j]);
+    st_elem<F>(rs_gmix, lane * M + j, a * d[j]);
   }
 
   float v[V];
@@ -237,17 +271,15 @@ __device__ __forceinline__ void output_sum(const float* __restrict__ partial, ui
 }
 
 // Two-launch form, first launch. Grid: `chunks` blocks of 64 threads.
-template <int N>
+template <int N, int F>
 __global__ __launch_bounds__(64) void coeff_partial_kernel(
-    const float* __restrict__ mix, const float* __restrict__ pre,
-    const float* __restrict__ post, const float* __restrict__ grad_pre,
-    const float* __restrict__ grad_post, const float* __restrict__ grad_res,
-    const float* __restrict__ alpha, float post_scale, float* __restrict__ grad_mix,
-    float* __restrict__ partial, int64_t rows, uint32_t chunks) {
+    const void* __restrict__ mix, const void* __restrict__ pre, const void* __restrict__ post,
+    const void* __restrict__ grad_pre, const void* __restrict__ grad_post,
+    const void* __restrict__ grad_res, const float* __restrict__ alpha, float post_scale,
+    void* __restrict__ grad_mix, float* __restrict__ partial, int64_t rows, uint32_t chunks) {
   __shared__ __align__(16) float tile[Tile<N>::kFloats];
-  chunk_sums<N>(mix, pre, post, grad_pre, grad_post, grad_res, alpha, post_scale, grad_mix,
-                partial,
-                rows, chunks, blockIdx.x, threadIdx.x, true, tile);
+  chunk_sums<N, F>(mix, pre, post, grad_pre, grad_post, grad_res, alpha, post_scale, grad_mix,
+                   partial, rows, chunks, blockIdx.x, threadIdx.x, true, tile);
 }
 
 // Two-launch form, second launch. Grid: m + 3 blocks of 64 threads, block v
@@ -267,14 +299,13 @@ __global__ __launch_bounds__(64) void coeff_reduce_kernel(const float* __restric
 // every output's second stage (the outputs split over its waves) and sets
 // the counter back to 0 for the next call. No block waits for another, so
 // every block runs to completion whatever the others do.
-template <int N, int W>
+template <int N, int W, int F>
 __global__ __launch_bounds__(64 * W) void coeff_fused_kernel(
-    const float* __restrict__ mix, const float* __restrict__ pre,
-    const float* __restrict__ post, const float* __restrict__ grad_pre,
-    const float* __restrict__ grad_post, const float* __restrict__ grad_res,
-    const float* __restrict__ alpha, float post_scale, float* __restrict__ grad_mix,
-    float* __restrict__ partial, uint32_t* __restrict__ arrived, int64_t rows,
-    uint32_t chunks, float* __restrict__ grad_b, float* __restrict__ grad_alpha) {
+    const void* __restrict__ mix, const void* __restrict__ pre, const void* __restrict__ post,
+    const void* __restrict__ grad_pre, const void* __restrict__ grad_post,
+    const void* __restrict__ grad_res, const float* __restrict__ alpha, float post_scale,
+    void* __restrict__ grad_mix, float* __restrict__ partial, uint32_t* __restrict__ arrived,
+    int64_t rows, uint32_t chunks, float* __restrict__ grad_b, float* __restrict__ grad_alpha) {
   constexpr int M = 2 * N + N * N;
   constexpr int Q = (M + 3 + W - 1) / W;  // outputs per wave
   __shared__ uint32_t last;
@@ -282,9 +313,8 @@ __global__ __launch_bounds__(64 * W) void coeff_fused_kernel(
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t c = blockIdx.x * W + wave;
-  chunk_sums<N>(mix, pre, post, grad_pre, grad_post, grad_res, alpha, post_scale, grad_mix,
-                partial,
-                rows, chunks, c, lane, c < chunks, tiles + wave * Tile<N>::kFloats);
+  chunk_sums<N, F>(mix, pre, post, grad_pre, grad_post, grad_res, alpha, post_scale, grad_mix,
+                   partial, rows, chunks, c, lane, c < chunks, tiles + wave * Tile<N>::kFloats);
   __syncthreads();
   if (threadIdx.x == 0) {
     __threadfence();
@@ -391,23 +421,28 @@ Range range(const void* p, int64_t bytes, const char* name) {
 
 bool overlap(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
 
-mhc_status need_ptr(const void* p, const char* name) {
+mhc_status need_ptr(const void* p, int64_t align, const char* name) {
   if (p == nullptr) return fail(MHC_ERROR_INVALID_VALUE, "%s is NULL", name);
-  if (reinterpret_cast<uintptr_t>(p) % 4 != 0)
-    return fail(MHC_ERROR_INVALID_VALUE, "%s is not 4-byte aligned", name);
+  if (reinterpret_cast<uintptr_t>(p) % align != 0)
+    return fail(MHC_ERROR_INVALID_VALUE, "%s is not %lld-byte aligned", name, (long long)align);
   return ok();
 }
+
+int64_t fmt_bytes(int32_t fmt) { return fmt == MHC_COEFF_F32 ? 4 : 2; }
 
 // Argument checks of a call. With has_workspace false (the no-allocation
 // entry point), the workspace is the library's own scratch array: it is not
 // checked and takes no part in the overlap tests.
-mhc_status validate(const float* mix, const float* pre, const float* post,
-                    const float* grad_pre, const float* grad_post, const float* grad_res,
-                    const float* alpha, float post_scale, const float* grad_mix,
-                    const float* grad_b, const float* grad_alpha, const void* workspace,
-                    int64_t workspace_bytes, int64_t rows, int32_t n, bool has_workspace = true) {
+mhc_status validate(const void* mix, const void* pre, const void* post, const void* grad_pre,
+                    const void* grad_post, const void* grad_res, const float* alpha,
+                    float post_scale, const void* grad_mix, const float* grad_b,
+                    const float* grad_alpha, const void* workspace, int64_t workspace_bytes,
+                    int64_t rows, int32_t n, int32_t fmt, bool has_workspace = true) {
   if (n != 2 && n != 4 && n != 8)
     return fail(MHC_ERROR_INVALID_VALUE, "the expansion rate n must be 2, 4 or 8 (got %d)", n);
+  if (fmt != MHC_COEFF_F32 && fmt != MHC_COEFF_BF16 && fmt != MHC_COEFF_F16)
+    return fail(MHC_ERROR_INVALID_VALUE, "dtype must be MHC_COEFF_F32, _BF16 or _F16 (got %d)",
+                fmt);
   if (rows < 0 || rows > MHC_COEFF_MAX_ROWS)
     return fail(MHC_ERROR_INVALID_VALUE, "rows must be in [0, %lld] (got %lld)",
                 (long long)MHC_COEFF_MAX_ROWS, (long long)rows);
@@ -415,26 +450,27 @@ mhc_status validate(const float* mix, const float* pre, const float* post,
     return fail(MHC_ERROR_INVALID_VALUE, "post_scale must be finite and positive (got %g)",
                 (double)post_scale);
   const int m = columns(n);
+  const int64_t E = fmt_bytes(fmt);
   const int64_t need = has_workspace ? workspace_need(rows, n) : 0;
   mhc_status st;
-  if ((st = need_ptr(grad_b, "grad_b")) != MHC_SUCCESS) return st;
-  if ((st = need_ptr(grad_alpha, "grad_alpha")) != MHC_SUCCESS) return st;
+  if ((st = need_ptr(grad_b, 4, "grad_b")) != MHC_SUCCESS) return st;
+  if ((st = need_ptr(grad_alpha, 4, "grad_alpha")) != MHC_SUCCESS) return st;
   if (rows > 0) {
-    const void* ps[] = {mix, pre, post, grad_pre, grad_post, grad_res, alpha, grad_mix, workspace};
-    const char* names[] = {"mix", "pre", "post", "grad_pre", "grad_post", "grad_res", "alpha",
-                           "grad_mix", "workspace"};
+    const void* ps[] = {mix, pre, post, grad_pre, grad_post, grad_res, grad_mix, alpha, workspace};
+    const char* names[] = {"mix", "pre", "post", "grad_pre", "grad_post", "grad_res",
+                           "grad_mix", "alpha", "workspace"};
     for (int i = 0; i < (has_workspace ? 9 : 8); ++i)
-      if ((st = need_ptr(ps[i], names[i])) != MHC_SUCCESS) return st;
+      if ((st = need_ptr(ps[i], i < 7 ? E : 4, names[i])) != MHC_SUCCESS) return st;
   }
   if (workspace_bytes < need)
     return fail(MHC_ERROR_INVALID_VALUE, "workspace_bytes %lld < %lld needed",
                 (long long)workspace_bytes, (long long)need);
-  const Range ins[] = {range(mix, rows * m * 4, "mix"), range(pre, rows * n * 4, "pre"),
-                       range(post, rows * n * 4, "post"), range(grad_pre, rows * n * 4, "grad_pre"),
-                       range(grad_post, rows * n * 4, "grad_post"),
-                       range(grad_res, rows * n * n * 4, "grad_res"),
+  const Range ins[] = {range(mix, rows * m * E, "mix"), range(pre, rows * n * E, "pre"),
+                       range(post, rows * n * E, "post"), range(grad_pre, rows * n * E, "grad_pre"),
+                       range(grad_post, rows * n * E, "grad_post"),
+                       range(grad_res, rows * n * n * E, "grad_res"),
                        range(alpha, rows > 0 ? 12 : 0, "alpha")};
-  const Range outs[] = {range(grad_mix, rows * m * 4, "grad_mix"), range(grad_b, m * 4, "grad_b"),
+  const Range outs[] = {range(grad_mix, rows * m * E, "grad_mix"), range(grad_b, m * 4, "grad_b"),
                         range(grad_alpha, 12, "grad_alpha"), range(workspace, need, "workspace")};
   const int nout = has_workspace ? 4 : 3;
   for (int a = 0; a < nout; ++a) {
@@ -450,19 +486,31 @@ mhc_status validate(const float* mix, const float* pre, const float* post,
 }
 
 struct CoeffArgs {
-  const float *mix, *pre, *post, *grad_pre, *grad_post, *grad_res, *alpha;
+  const void *mix, *pre, *post, *grad_pre, *grad_post, *grad_res;  // stored format
+  const float* alpha;
   float c;  // post_scale
-  float *grad_mix, *grad_b, *grad_alpha, *partial;
+  void* grad_mix;                                                   // stored format
+  float *grad_b, *grad_alpha, *partial;
   uint32_t* arrived;
   int64_t rows;
   uint32_t chunks;
+  int32_t fmt;
 };
+
+template <int N, int F>
+hipError_t launch_partial_f(const CoeffArgs& a, hipStream_t s, hipEvent_t start) {
+  return launch_kernel(coeff_partial_kernel<N, F>, dim3(a.chunks), dim3(64), s, start, nullptr,
+                       a.mix, a.pre, a.post, a.grad_pre, a.grad_post, a.grad_res, a.alpha, a.c,
+                       a.grad_mix, a.partial, a.rows, a.chunks);
+}
 
 template <int N>
 hipError_t launch_partial(const CoeffArgs& a, hipStream_t s, hipEvent_t start) {
-  return launch_kernel(coeff_partial_kernel<N>, dim3(a.chunks), dim3(64), s, start, nullptr,
-                       a.mix, a.pre, a.post, a.grad_pre, a.grad_post, a.grad_res, a.alpha, a.c,
-                       a.grad_mix, a.partial, a.rows, a.chunks);
+  switch (a.fmt) {
+    case MHC_COEFF_BF16: return launch_partial_f<N, MHC_COEFF_BF16>(a, s, start);
+    case MHC_COEFF_F16: return launch_partial_f<N, MHC_COEFF_F16>(a, s, start);
+    default: return launch_partial_f<N, MHC_COEFF_F32>(a, s, start);
+  }
 }
 
 // Waves per block of the one-launch form: 2 up to this many chunks, 4
@@ -473,19 +521,28 @@ hipError_t launch_partial(const CoeffArgs& a, hipStream_t s, hipEvent_t start) {
 // block's waves each sum fewer outputs). At n = 2 the same or better.
 constexpr uint32_t kTwoWaveMaxChunks = 64;
 
-template <int N, int W>
+template <int N, int W, int F>
 hipError_t launch_fused_w(const CoeffArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   const uint32_t blocks = (a.chunks + W - 1) / W;
-  return launch_kernel(coeff_fused_kernel<N, W>, dim3(blocks), dim3(64 * W), s, start, stop,
+  return launch_kernel(coeff_fused_kernel<N, W, F>, dim3(blocks), dim3(64 * W), s, start, stop,
                        a.mix, a.pre, a.post, a.grad_pre, a.grad_post, a.grad_res, a.alpha, a.c,
                        a.grad_mix, a.partial, a.arrived, a.rows, a.chunks, a.grad_b,
                        a.grad_alpha);
 }
 
+template <int N, int F>
+hipError_t launch_fused_f(const CoeffArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+  if (a.chunks <= kTwoWaveMaxChunks) return launch_fused_w<N, 2, F>(a, s, start, stop);
+  return launch_fused_w<N, 4, F>(a, s, start, stop);
+}
+
 template <int N>
 hipError_t launch_fused(const CoeffArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
-  if (a.chunks <= kTwoWaveMaxChunks) return launch_fused_w<N, 2>(a, s, start, stop);
-  return launch_fused_w<N, 4>(a, s, start, stop);
+  switch (a.fmt) {
+    case MHC_COEFF_BF16: return launch_fused_f<N, MHC_COEFF_BF16>(a, s, start, stop);
+    case MHC_COEFF_F16: return launch_fused_f<N, MHC_COEFF_F16>(a, s, start, stop);
+    default: return launch_fused_f<N, MHC_COEFF_F32>(a, s, start, stop);
+  }
 }
 
 // Launches of one call: 1 = one launch (chunk sums + last-block reduction),
@@ -507,10 +564,10 @@ mhc_status launch_status(hipError_t e, const char* what) {
 // The arguments of a call whose pointers and sizes have been validated;
 // `workspace` is device memory of at least workspace_need(rows, n) bytes
 // whose first 4 bytes (the arrival counter) are zero.
-CoeffArgs make_args(const float* mix, const float* pre, const float* post,
-                    const float* grad_pre, const float* grad_post, const float* grad_res,
-                    const float* alpha, float post_scale, float* grad_mix, float* grad_b,
-                    float* grad_alpha, void* workspace, int64_t rows) {
+CoeffArgs make_args(const void* mix, const void* pre, const void* post, const void* grad_pre,
+                    const void* grad_post, const void* grad_res, const float* alpha,
+                    float post_scale, void* grad_mix, float* grad_b, float* grad_alpha,
+                    void* workspace, int64_t rows, int32_t fmt) {
   CoeffArgs a;
   a.mix = mix; a.pre = pre; a.post = post; a.grad_pre = grad_pre; a.grad_post = grad_post;
   a.grad_res = grad_res; a.alpha = alpha;
@@ -521,6 +578,7 @@ CoeffArgs make_args(const float* mix, const float* pre, const float* post,
                        : nullptr;
   a.rows = rows;
   a.chunks = static_cast<uint32_t>(chunk_count(rows));
+  a.fmt = fmt;
   return a;
 }
 
@@ -618,7 +676,18 @@ mhc_status mhc_coeff_bwd_validate(const float* mix, const float* pre, const floa
                                   const float* grad_alpha, const void* workspace,
                                   int64_t workspace_bytes, int64_t rows, int32_t n) {
   return validate(mix, pre, post, grad_pre, grad_post, grad_res, alpha, post_scale, grad_mix,
-                  grad_b, grad_alpha, workspace, workspace_bytes, rows, n);
+                  grad_b, grad_alpha, workspace, workspace_bytes, rows, n, MHC_COEFF_F32);
+}
+
+mhc_status mhc_coeff_bwd_validate_ex(const void* mix, const void* pre, const void* post,
+                                     const void* grad_pre, const void* grad_post,
+                                     const void* grad_res, const float* alpha, float post_scale,
+                                     const void* grad_mix, const float* grad_b,
+                                     const float* grad_alpha, const void* workspace,
+                                     int64_t workspace_bytes, int64_t rows, int32_t n,
+                                     int32_t dtype) {
+  return validate(mix, pre, post, grad_pre, grad_post, grad_res, alpha, post_scale, grad_mix,
+                  grad_b, grad_alpha, workspace, workspace_bytes, rows, n, dtype);
 }
 
 int32_t mhc_coeff_bwd_plan(int64_t rows, int32_t n, int32_t launches) {
@@ -628,21 +697,33 @@ int32_t mhc_coeff_bwd_plan(int64_t rows, int32_t n, int32_t launches) {
   return plan_launches(rows, n, launches);
 }
 
+mhc_status mhc_coeff_bwd_ex(const void* mix, const void* pre, const void* post,
+                            const void* grad_pre, const void* grad_post, const void* grad_res,
+                            const float* alpha, float post_scale, void* grad_mix, float* grad_b,
+                            float* grad_alpha, void* workspace, int64_t workspace_bytes,
+                            int64_t rows, int32_t n, int32_t dtype, int32_t launches,
+                            void* stream, void* start_event, void* stop_event) {
+  mhc_status st = validate(mix, pre, post, grad_pre, grad_post, grad_res, alpha, post_scale,
+                           grad_mix, grad_b, grad_alpha, workspace, workspace_bytes, rows, n,
+                           dtype);
+  if (st != MHC_SUCCESS) return st;
+  if (launches < 0 || launches > 2)
+    return fail(MHC_ERROR_INVALID_VALUE, "launches must be 0, 1 or 2 (got %d)", launches);
+  const CoeffArgs a = make_args(mix, pre, post, grad_pre, grad_post, grad_res, alpha, post_scale,
+                                grad_mix, grad_b, grad_alpha, workspace, rows, dtype);
+  return run(a, n, launches, static_cast<hipStream_t>(stream),
+             static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event));
+}
+
 mhc_status mhc_coeff_bwd(const float* mix, const float* pre, const float* post,
                          const float* grad_pre, const float* grad_post, const float* grad_res,
                          const float* alpha, float post_scale, float* grad_mix, float* grad_b,
                          float* grad_alpha, void* workspace, int64_t workspace_bytes,
                          int64_t rows, int32_t n, int32_t launches, void* stream,
                          void* start_event, void* stop_event) {
-  mhc_status st = validate(mix, pre, post, grad_pre, grad_post, grad_res, alpha, post_scale,
-                           grad_mix, grad_b, grad_alpha, workspace, workspace_bytes, rows, n);
-  if (st != MHC_SUCCESS) return st;
-  if (launches < 0 || launches > 2)
-    return fail(MHC_ERROR_INVALID_VALUE, "launches must be 0, 1 or 2 (got %d)", launches);
-  const CoeffArgs a = make_args(mix, pre, post, grad_pre, grad_post, grad_res, alpha, post_scale,
-                                grad_mix, grad_b, grad_alpha, workspace, rows);
-  return run(a, n, launches, static_cast<hipStream_t>(stream),
-             static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event));
+  return mhc_coeff_bwd_ex(mix, pre, post, grad_pre, grad_post, grad_res, alpha, post_scale,
+                          grad_mix, grad_b, grad_alpha, workspace, workspace_bytes, rows, n,
+                          MHC_COEFF_F32, launches, stream, start_event, stop_event);
 }
 
 mhc_status mhc_coeff_bwd_noalloc(const float* mix, const float* pre, const float* post,
@@ -668,13 +749,14 @@ mhc_status mhc_coeff_bwd_noalloc(const float* mix, const float* pre, const float
     return fail(MHC_ERROR_INVALID_VALUE, "launches must be 0, 1 or 2 (got %d)", launches);
   // Every other argument as mhc_coeff_bwd checks it.
   mhc_status st = validate(mix, pre, post, grad_pre, grad_post, grad_res, alpha, post_scale,
-                           grad_mix, grad_b, grad_alpha, nullptr, 0, rows, n, false);
+                           grad_mix, grad_b, grad_alpha, nullptr, 0, rows, n, MHC_COEFF_F32,
+                           false);
   if (st != MHC_SUCCESS) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   void* ws = nullptr;
   if (rows > 0 && (st = device_scratch(s, &ws)) != MHC_SUCCESS) return st;
   const CoeffArgs a = make_args(mix, pre, post, grad_pre, grad_post, grad_res, alpha, post_scale,
-                                grad_mix, grad_b, grad_alpha, ws, rows);
+                                grad_mix, grad_b, grad_alpha, ws, rows, MHC_COEFF_F32);
   return run(a, n, launches, s, static_cast<hipEvent_t>(start_event),
              static_cast<hipEvent_t>(stop_event));
 }

@@ -35,7 +35,7 @@
 #include <stdio.h>
 #include <string.h>
 
-#include "mhc_bf16.h"
+#include "mhc_convert.h"
 #include "mhc_h_aggregate.h"
 #include "mhc_lanes.h"
 #include "mhc_launch.h"
@@ -49,7 +49,7 @@
 namespace {
 
 // ---------------------------------------------------------------------------
-// Device helpers: V-element vectors (conversions in mhc_bf16.h)
+// Device helpers: V-element vectors (conversions in mhc_convert.h)
 // ---------------------------------------------------------------------------
 
 // A V-element bf16 vector as a native vector of 32-bit words (V = 8, 4), one

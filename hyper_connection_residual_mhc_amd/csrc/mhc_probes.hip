@@ -8,7 +8,7 @@
 #include <stdint.h>
 #include <stdio.h>
 
-#include "mhc_bf16.h"
+#include "mhc_convert.h"
 #include "mhc_lanes.h"
 #include "mhc_launch.h"
 #include "mhc_probes.h"

@@ -94,7 +94,7 @@
 extern "C" {
 #endif
 
-#define MHC_COEFF_ABI_VERSION 3
+#define MHC_COEFF_ABI_VERSION 4
 
 /* Rows per first-stage chunk of row_sum. */
 #define MHC_COEFF_CHUNK 64
@@ -102,6 +102,11 @@ extern "C" {
 /* Most rows one call accepts (2^28: keeps every workspace byte offset and
  * buffer range within 31 bits at every expansion rate). */
 #define MHC_COEFF_MAX_ROWS (1LL << 28)
+
+/* Storage formats of the six row tensors and grad_mix (mhc_coeff_bwd_ex). */
+#define MHC_COEFF_F32 0
+#define MHC_COEFF_BF16 1
+#define MHC_COEFF_F16 2
 
 /* Bytes of the fixed device array that mhc_coeff_bwd_noalloc uses as its
  * workspace (one array per GPU the library runs on). */
@@ -140,6 +145,36 @@ mhc_status mhc_coeff_bwd(const float* mix, const float* pre, const float* post,
                          float* grad_alpha, void* workspace, int64_t workspace_bytes,
                          int64_t rows, int32_t n, int32_t launches, void* stream,
                          void* start_event, void* stop_event);
+
+/*
+ * The epilogue on 16-bit (or fp32) inputs (page Testing Done: FP16, BF16
+ * and FP32 inputs; Performance Method: BF16 is the primary case).
+ * dtype = MHC_COEFF_F32, MHC_COEFF_BF16 or MHC_COEFF_F16 is the storage
+ * format of mix, pre, post, grad_pre, grad_post, grad_res and grad_mix (raw
+ * bit patterns for the 16-bit formats; 2-byte alignment). Every stored
+ * input value is widened to fp32 exactly, the computation above runs in
+ * fp32 unchanged, and grad_mix is rounded once to the format (nearest even,
+ * subnormals kept, overflow to infinity). alpha, grad_b and grad_alpha
+ * stay fp32, and so do the row sums, which add the fp32 values of d and e
+ * (never the rounded grad_mix). Everything else as in mhc_coeff_bwd, which
+ * is this call with MHC_COEFF_F32; an unknown dtype gives
+ * MHC_ERROR_INVALID_VALUE.
+ */
+mhc_status mhc_coeff_bwd_ex(const void* mix, const void* pre, const void* post,
+                            const void* grad_pre, const void* grad_post, const void* grad_res,
+                            const float* alpha, float post_scale, void* grad_mix, float* grad_b,
+                            float* grad_alpha, void* workspace, int64_t workspace_bytes,
+                            int64_t rows, int32_t n, int32_t dtype, int32_t launches,
+                            void* stream, void* start_event, void* stop_event);
+
+/* The argument checks of mhc_coeff_bwd_ex, on the host only. */
+mhc_status mhc_coeff_bwd_validate_ex(const void* mix, const void* pre, const void* post,
+                                     const void* grad_pre, const void* grad_post,
+                                     const void* grad_res, const float* alpha, float post_scale,
+                                     const void* grad_mix, const float* grad_b,
+                                     const float* grad_alpha, const void* workspace,
+                                     int64_t workspace_bytes, int64_t rows, int32_t n,
+                                     int32_t dtype);
 
 /*
  * No-allocation variant of mhc_coeff_bwd, for callers that cannot allocate

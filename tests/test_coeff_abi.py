@@ -26,7 +26,7 @@ def lib(built_library):
 def test_header_declarations_are_all_exported(lib):
     text = re.sub(r"/\*.*?\*/", "", _build.COEFF_HEADER.read_text(), flags=re.S)
     names = sorted(set(re.findall(r"\b(mhc_\w+)\s*\(", text)))
-    assert len(names) == 7, names
+    assert len(names) == 9, names
     out = subprocess.run(["nm", "-D", "--defined-only", str(_build.COEFF_LIB_PATH)],
                          capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (mhc_\w+)$", out, flags=re.M))
@@ -224,3 +224,36 @@ def test_noalloc_rejects_bad_arguments_before_any_hip_call(lib):
     assert call(aliased) == MHC_ERROR_ALIASING
     misaligned = p[:7] + [2.0] + [p[7] + 2] + p[8:10]
     assert call(misaligned) == MHC_ERROR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("dtype,elem", [(0, 4), (1, 2), (2, 2)])
+def test_typed_argument_rules(lib, dtype, elem):
+    """mhc_coeff_bwd_validate_ex: the row tensors and grad_mix need their
+    element's alignment (4 bytes fp32, 2 bytes bf16 / fp16) and their sizes
+    scale with it; alpha and the fp32 outputs keep 4-byte alignment; an
+    unknown format is refused; the plain call is the fp32 format."""
+    v = lib.mhc_coeff_bwd_validate_ex
+    a = Args(lib, 100, 4)
+    t = list(a.tuple())
+    assert v(*t, dtype) == MHC_SUCCESS
+    assert v(*t, 3) == MHC_ERROR_INVALID_VALUE and v(*t, -1) == MHC_ERROR_INVALID_VALUE
+    assert b"dtype" in lib.mhc_coeff_last_error_message()
+    for idx in (0, 1, 2, 3, 4, 5, 8):                       # row tensors and grad_mix
+        t1 = list(t)
+        t1[idx] = t[idx] + 2
+        assert v(*t1, dtype) == (MHC_SUCCESS if elem == 2 else MHC_ERROR_INVALID_VALUE), idx
+        t1[idx] = t[idx] + 1
+        assert v(*t1, dtype) == MHC_ERROR_INVALID_VALUE, idx
+    for idx in (6, 9, 10, 11):                              # alpha, grad_b, grad_alpha, workspace
+        t1 = list(t)
+        t1[idx] = t[idx] + 2
+        assert v(*t1, dtype) == MHC_ERROR_INVALID_VALUE, idx
+    # grad_mix ending right where mix starts (nothing lies below mix):
+    # disjoint at the format's size; one element later it overlaps
+    m, R = 24, 100
+    t2 = list(t)
+    t2[8] = t[0] - R * m * elem
+    assert v(*t2, dtype) == MHC_SUCCESS
+    t2[8] = t[0] - R * m * elem + elem
+    assert v(*t2, dtype) == MHC_ERROR_ALIASING
+    assert lib.mhc_coeff_bwd_validate(*t) == v(*t, 0)

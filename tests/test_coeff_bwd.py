@@ -264,3 +264,100 @@ def test_timed_call_records_both_events(device):
             assert 0 < ms < 100
     finally:
         ev.close()
+
+
+# ---------------------------------------------------------------------------
+# 16-bit row tensors (mhc_coeff_bwd_ex through the binding's dtype dispatch)
+# ---------------------------------------------------------------------------
+
+TORCH16 = {"bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def _typed_host(R, n, seed, dtype, c=2.0):
+    h = make_coeff_inputs(R, n, seed=seed, post_scale=c)
+    return {k: (cb.narrow(v, dtype) if k != "alpha" else v) for k, v in h.items()}
+
+
+def _gpu_typed(host, c, dev, dtype, **kw):
+    d = {k: (torch.from_numpy(np.ascontiguousarray(host[k]).view(np.int16)).to(dev)
+             .view(TORCH16[dtype]) if k != "alpha" else torch.from_numpy(host[k]).to(dev))
+         for k in KEYS}
+    gm, gb, ga = coeff.mhc_coeff_bwd(*(d[k] for k in KEYS), c, **kw)
+    torch.cuda.synchronize()
+    assert gm.dtype == TORCH16[dtype] and gb.dtype == torch.float32
+    return gm.view(torch.int16).cpu().numpy().view(np.uint16), gb.cpu().numpy(), ga.cpu().numpy()
+
+
+def _check_typed(host, c, dev, dtype, what, **kw):
+    n = host["pre"].shape[1]
+    got = _gpu_typed(host, c, dev, dtype, **kw)
+    want = cb.coeff_bwd_typed(*(host[k] for k in KEYS), c, n, dtype)
+    for name, g, w in zip(("grad_mix", "grad_b", "grad_alpha"), got, want):
+        assert_bytes_equal(g, w, f"{what} {name}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("launches", [1, 2])
+@pytest.mark.parametrize("n", [2, 4, 8])
+@pytest.mark.parametrize("R", [1, 63, 65, 4097, 8257])
+def test_typed_bit_exact_against_the_oracle(device, dtype, n, R, launches):
+    say(f"coeff bwd {dtype} n={n} R={R} launches={launches}")
+    _check_typed(_typed_host(R, n, R + n, dtype), 2.0, device, dtype, f"{dtype} n={n} R={R}",
+                 launches=launches)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("R", [512, 2048, 8192])
+def test_typed_page_shapes(device, dtype, R):
+    say(f"coeff bwd {dtype} page shape R={R}")
+    _check_typed(_typed_host(R, 4, 0, dtype), 2.0, device, dtype, f"{dtype} R={R}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("a2", [1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, 1.0 + 2.0 ** -8,
+                                1.0 + 3 * 2.0 ** -8, 1.0003, 0.7, 3.0])
+def test_typed_grad_mix_rounding(device, dtype, a2):
+    """grad_mix = alpha * d on the residual columns with d = grad_res = +-2^k
+    over the whole range of the format (and its largest values): with these
+    gains the products are exact fp32 values on the format's ties (every
+    binade, subnormals included) or just past its largest finite value, so
+    the device's narrowing is checked at its decision points."""
+    say(f"coeff bwd {dtype} grad_mix rounding alpha2={a2}")
+    n, R = 4, 1024
+    host = _typed_host(R, n, 5, dtype)
+    lo, hi = (-24, 16) if dtype == "f16" else (-133, 128)
+    k = np.arange(lo, hi)
+    vals = np.concatenate([np.exp2(k), -np.exp2(k),
+                           [65504.0, -65504.0, 65472.0] if dtype == "f16" else
+                           [3.3895314e38, -3.3895314e38, 1.0]]).astype(np.float32)
+    vals = np.resize(vals, R * n * n).reshape(R, n * n)
+    host["grad_res"] = cb.narrow(vals, dtype)
+    host["alpha"] = np.array([1.0, 1.0, a2], np.float32)
+    _check_typed(host, 2.0, device, dtype, f"{dtype} rounding a2={a2}", launches=2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_typed_buffers_aligned_to_2_bytes_only(device, dtype):
+    """Row tensors and grad_mix one element past a 256-byte boundary (the
+    16-bit forms need only 2-byte alignment)."""
+    say(f"coeff bwd {dtype} 2-byte alignment")
+    R, n = 1000, 4
+    host = _typed_host(R, n, 61, dtype)
+
+    def shifted(a, dt):
+        buf = torch.empty(a.size + 64, dtype=dt, device=device)
+        t = buf[1:1 + a.size].view(a.shape)
+        t.copy_(torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(dt))
+        assert t.data_ptr() % 4 == 2
+        return t
+
+    dt = TORCH16[dtype]
+    d = {k: shifted(host[k], dt) for k in KEYS if k != "alpha"}
+    alpha = torch.from_numpy(host["alpha"]).to(device)
+    gm = shifted(np.zeros((R, 24), np.uint16), dt)
+    got = coeff.mhc_coeff_bwd(*(d[k] for k in KEYS if k != "alpha"), alpha, 2.0, grad_mix=gm)
+    torch.cuda.synchronize()
+    want = cb.coeff_bwd_typed(*(host[k] for k in KEYS), 2.0, n, dtype)
+    assert_bytes_equal(gm.view(torch.int16).cpu().numpy().view(np.uint16), want[0],
+                       f"{dtype} shifted grad_mix")
+    assert_bytes_equal(got[1].cpu().numpy(), want[1], f"{dtype} shifted grad_b")
