@@ -150,3 +150,38 @@ def test_backward_matches_torch_autograd_loosely(device):
     gr, gp = ops.h_aggregate_backward(d["residual"], d["pre"], d["grad_out"])
     torch.testing.assert_close(gr.float(), r32.grad.to(torch.bfloat16).float(), atol=1e-2, rtol=1e-2)
     torch.testing.assert_close(gp, p32.grad, atol=1e-3, rtol=1e-4)
+
+
+@pytest.mark.parametrize("acc", [False, True])
+@pytest.mark.parametrize("ring", [4, 8, 12])
+def test_row_layout_every_compiled_chunk_count(device, ring, acc):
+    """The row layout runs a kernel compiled for the row's chunk count when
+    the row has at most 16 chunks of 512 elements (16-byte accesses), the
+    looping kernel above that. H = 512c - 8, 512c and 512c + 8 reach every
+    count from 1 to 17 with full and partly filled last chunks; every ring
+    size and both the written and the accumulating backward; bit-exact
+    against the oracle."""
+    for c in range(1, 18):
+        for H in (512 * c - 8, 512 * c, 512 * c + 8):
+            if H <= 0 or (acc and ring == 12):
+                continue
+            say(f"row layout chunks H={H} ring={ring} acc={acc}")
+            host = make_inputs(3, H, seed=H + ring, grad=True)
+            launch = {"layout": ROWS, "units_per_thread": ring}
+            if not acc:
+                gr, gp = run_bwd(host, device, launch=launch)
+                check_bwd(host, gr, gp, f"H={H} ring={ring}")
+                continue
+            old = (np.random.default_rng(H).standard_normal((3, 4, H)) * 0.01).astype(np.float32)
+            from hyper_connection_residual_mhc_amd.workloads import to_bf16_bits
+            old_bits = to_bf16_bits(old)
+            d = to_device({**host, "grad_residual": old_bits}, device)
+            gp = torch.empty((3, 4), dtype=torch.float32, device=device)
+            ops.mhc_h_aggregate_bwd_acc(d["residual"], d["pre"], d["grad_out"], d["grad_residual"],
+                                        gp, launch=launch)
+            torch.cuda.synchronize()
+            want_gr, want_gp = O.h_aggregate_bwd_acc(host["residual"], host["pre"],
+                                                     host["grad_out"], old_bits)
+            assert_bytes_equal(bf16_tensor_to_bits(d["grad_residual"]), want_gr,
+                               f"acc H={H} ring={ring} grad_residual")
+            assert_bytes_equal(gp.cpu().numpy(), want_gp, f"acc H={H} ring={ring} grad_pre")
