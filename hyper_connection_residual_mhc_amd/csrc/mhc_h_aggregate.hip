@@ -823,10 +823,17 @@ mhc_status plan_bwd(const uint16_t* residual, const uint16_t* grad_out,
     if (ov && (ov->tokens_per_block != 0 || ov->streams_per_block != 0))
       return fail(MHC_ERROR_INVALID_VALUE,
                   "tokens_per_block and streams_per_block belong to the split layout");
-    // Ring size: 8 chunks in flight (measured fastest at T = 512 to 2048,
-    // on par with 12 at T = 8192), fewer if the register budget requires.
+    // Ring size, fewer where the register budget requires: 12 chunks in
+    // flight for rows compiled for their exact chunk count (the whole row
+    // up to H = 6144; measured at H = 7168 against 8: 22.01 / 41.38 / 171.4
+    // us against 22.09 / 41.69 / 174.2 at T = 1024 / 2048 / 8192), 8 for the
+    // looping kernel, whose last round would visit 12 slots for any
+    // remainder (8 measured fastest there at T = 512 to 2048).
     const int max_b = rows_max_b(V, acc);
-    int B = max_b < 8 ? max_b : 8;
+    const int64_t row_chunks = (pl->ngroups + 63) / 64;
+    const bool exact = V == 8 && row_chunks <= kMaxFixedChunks;
+    const int want_b = exact ? 12 : 8;
+    int B = max_b < want_b ? max_b : want_b;
     if (ov && ov->units_per_thread != 0) {
       if (ov->units_per_thread != 4 && ov->units_per_thread != 8 && ov->units_per_thread != 12)
         return fail(MHC_ERROR_INVALID_VALUE, "row-layout units_per_thread must be 4, 8 or 12");

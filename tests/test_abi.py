@@ -198,10 +198,15 @@ def test_backward_plan_and_overrides(lib):
     r, p, g, gr, gp = bwd_ptrs(T, H)
     SPLIT, ROWS = _lib.MHC_BWD_SPLIT, _lib.MHC_BWD_ROWS
     # long batches: one wave per (token, stream) row, a token per 256-thread block
+    # (rows of at most 16 chunks of 512 elements keep 12 chunks in flight,
+    # longer rows 8)
     plan, grid = ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T, H)
-    assert plan == {"block_threads": 256, "vec_width": 8, "units_per_thread": 8,
+    assert plan == {"block_threads": 256, "vec_width": 8, "units_per_thread": 12,
                     "tokens_per_block": 0, "streams_per_block": 0, "layout": ROWS}
     assert grid == T
+    for H2, ring in ((8192, 12), (8200, 8)):
+        plan, _ = ops.mhc_h_aggregate_plan_bwd(*bwd_ptrs(T, H2), T, H2)
+        assert plan["layout"] == ROWS and plan["units_per_thread"] == ring, H2
     plan, grid = ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T, H,
                                               launch={"layout": ROWS, "block_threads": 64,
                                                       "units_per_thread": 12})
