@@ -600,6 +600,7 @@ def run_sweep(path: str, rounds: int = 7, warm: int = 10, timed: int = 100,
     torch.cuda.set_device(dev)
     sh = int(torch.cuda.current_stream(dev).cuda_stream)
     tm = SweepTimer(rounds, warm, timed)
+    blk = Timer(sh, rounds, warm, timed, check=_lib.check)
 
     def emit(f, rec: dict) -> None:
         f.write(json.dumps(rec) + "\n")
@@ -654,7 +655,8 @@ def run_sweep(path: str, rounds: int = 7, warm: int = 10, timed: int = 100,
                     fns.append(probe_call)
                 timings = tm.blocks(fns, _lib.check)
                 rec = {"direction": direction, "T": T, "H": H,
-                       **SweepTimer.fields(nbytes, timings[0]), "plan": plan}
+                       **SweepTimer.fields(nbytes, timings[0]), "plan": plan,
+                       "block": block_fields(nbytes, blk.block(call))}
                 if probe:
                     pmed, _, _ = SweepTimer.summary(timings[1])
                     pg = probe.bytes / pmed / 1e3
@@ -665,12 +667,12 @@ def run_sweep(path: str, rounds: int = 7, warm: int = 10, timed: int = 100,
                 emit(f, rec)
             del sets
             torch.cuda.empty_cache()
-        for R, n in (COEFF_SWEEP if part in ("all", "coeff") else []):
+        for R, n, dtype in (COEFF_SWEEP if part in ("all", "coeff") else []):
             # the policy's form, then the two-launch form for comparison; the
-            # oracle timed on the host beside the policy's form
+            # oracle timed on the host beside the policy's fp32 form
             for launches in (0, 2):
-                rec = time_coeff(R, n, dev, sh, tm, launches)
-                if launches == 0:
+                rec = time_coeff(R, n, dev, sh, tm, launches, dtype)
+                if launches == 0 and dtype == "f32":
                     rec["cpu_baseline"] = run_coeff_cpu_baseline(R, n)
                 emit(f, rec)
         for T, H, n in (EXPANSION_SWEEP if part in ("all", "expansion") else []):
@@ -697,10 +699,20 @@ def run_sweep(path: str, rounds: int = 7, warm: int = 10, timed: int = 100,
                             None, a, b)
                 timings = tm.blocks([call], _lib.check)
                 emit(f, {"direction": direction, "T": T, "H": H, "n": n,
-                         **SweepTimer.fields(nbytes, timings[0])})
+                         **SweepTimer.fields(nbytes, timings[0]),
+                         "block": block_fields(nbytes, blk.block(call))})
             del sets
             torch.cuda.empty_cache()
     tm.close()
+    blk.close()
+
+
+def block_fields(nbytes: int, per_round: list[float]) -> dict:
+    """Block-timed figures (every launch and dispatch gap counted)."""
+    rs = round_stats(per_round)
+    med = rs["us_median"]
+    return {**rs, "gbps": round(nbytes / med / 1e3, 1),
+            "frac_of_8TBps": round(nbytes / med / 1e3 / PEAK_HBM_GBPS, 4)}
 
 
 # Launch shapes of the backward whose HBM traffic the counter runs compare
@@ -773,16 +785,18 @@ def run_counter_case(case: str, T: int, H: int, launches: int = 64, nsets: int =
 # mHC coefficient backward epilogue" (Performance Method: B = 4 sequences of
 # T in {128, 512, 2048} tokens at HC = 4, so R = 4T rows; HC = 2 and 8 as
 # controls at T = 512).
-COEFF_SWEEP = [(512, 4), (2048, 4), (8192, 4), (2048, 2), (2048, 8)]
+COEFF_SWEEP = [(512, 4, "f32"), (2048, 4, "f32"), (8192, 4, "f32"), (2048, 2, "f32"),
+               (2048, 8, "f32"), (512, 4, "bf16"), (2048, 4, "bf16"), (8192, 4, "bf16")]
 COEFF_KEYS = ("mix", "pre", "post", "grad_pre", "grad_post", "grad_res", "alpha")
 
 
-def coeff_bytes(R: int, n: int) -> int:
-    """Algorithmic bytes of one epilogue call: per row mix, pre, post,
-    grad_pre, grad_post, grad_res read and grad_mix written (32n + 12n^2),
-    plus alpha, grad_b and grad_alpha once."""
+def coeff_bytes(R: int, n: int, elem: int = 4) -> int:
+    """Algorithmic bytes of one epilogue call with row tensors of `elem`
+    bytes per value: per row mix, pre, post, grad_pre, grad_post, grad_res
+    read and grad_mix written ((8n + 3n^2) values: 32n + 12n^2 bytes in
+    fp32), plus alpha, grad_b and grad_alpha (fp32) once."""
     m = 2 * n + n * n
-    return R * (32 * n + 12 * n * n) + 12 + 4 * m + 12
+    return R * (8 * n + 3 * n * n) * elem + 12 + 4 * m + 12
 
 
 def run_coeff_cpu_baseline(R: int, n: int, min_seconds: float = 1.0) -> dict:
@@ -806,24 +820,29 @@ def run_coeff_cpu_baseline(R: int, n: int, min_seconds: float = 1.0) -> dict:
                       f"untimed call ({dt:.2f} s)"}
 
 
-def time_coeff(R, n, dev, sh, tm: SweepTimer, launches=0) -> dict:
-    """Per-call time of mhc_coeff_bwd (both of its launches, between the
-    first dispatch's start and the last one's end). Input sets rotate over
+def time_coeff(R, n, dev, sh, tm: SweepTimer, launches=0, dtype: str = "f32") -> dict:
+    """Per-call time of the coefficient epilogue (both of its launches,
+    between the first dispatch's start and the last one's end) on row
+    tensors stored as `dtype` (f32, bf16 or f16). Input sets rotate over
     more than the 256 MB Infinity Cache, so every call starts cold."""
     import torch
     from hyper_connection_residual_mhc_amd import _lib
     from hyper_connection_residual_mhc_amd.workloads import make_coeff_inputs
     clib = _lib.coeff_lib()
+    fmt = {"f32": (_lib.MHC_COEFF_F32, torch.float32, 4),
+           "bf16": (_lib.MHC_COEFF_BF16, torch.bfloat16, 2),
+           "f16": (_lib.MHC_COEFF_F16, torch.float16, 2)}[dtype]
     host = make_coeff_inputs(R, n, seed=0)
     m = 2 * n + n * n
-    per_set = coeff_bytes(R, n)
+    per_set = coeff_bytes(R, n, fmt[2])
     nsets = max(8, min(4096, -(-(320 << 20) // per_set)))
     src = {k: torch.from_numpy(host[k]).to(dev) for k in COEFF_KEYS}
+    src = {k: (v if k == "alpha" else v.to(fmt[1])) for k, v in src.items()}
     ws_bytes = clib.mhc_coeff_bwd_workspace_bytes(R, n)
     sets = []
     for _ in range(nsets):
         x = {k: v.clone() for k, v in src.items()}
-        x["grad_mix"] = torch.empty((R, m), dtype=torch.float32, device=dev)
+        x["grad_mix"] = torch.empty((R, m), dtype=fmt[1], device=dev)
         x["grad_b"] = torch.empty((m,), dtype=torch.float32, device=dev)
         x["grad_alpha"] = torch.empty((3,), dtype=torch.float32, device=dev)
         x["ws"] = torch.zeros((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
@@ -831,14 +850,14 @@ def time_coeff(R, n, dev, sh, tm: SweepTimer, launches=0) -> dict:
 
     def call(k, a, b):
         x = sets[k % nsets]
-        return clib.mhc_coeff_bwd(*(x[key].data_ptr() for key in COEFF_KEYS), 2.0,
-                                  x["grad_mix"].data_ptr(), x["grad_b"].data_ptr(),
-                                  x["grad_alpha"].data_ptr(), x["ws"].data_ptr(), ws_bytes, R, n,
-                                  launches, sh, a, b)
+        return clib.mhc_coeff_bwd_ex(*(x[key].data_ptr() for key in COEFF_KEYS), 2.0,
+                                     x["grad_mix"].data_ptr(), x["grad_b"].data_ptr(),
+                                     x["grad_alpha"].data_ptr(), x["ws"].data_ptr(), ws_bytes, R,
+                                     n, fmt[0], launches, sh, a, b)
     timings = tm.blocks([call], _lib.check_coeff)
     del sets, src
     torch.cuda.empty_cache()
-    return {"op": "coeff_bwd", "rows": R, "n": n, "sets": nsets,
+    return {"op": "coeff_bwd", "rows": R, "n": n, "dtype": dtype, "sets": nsets,
             **SweepTimer.fields(per_set, timings[0]),
             "launches": clib.mhc_coeff_bwd_plan(R, n, launches), "chunks": -(-R // 64)}
 

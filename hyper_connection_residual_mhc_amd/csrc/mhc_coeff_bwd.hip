@@ -98,6 +98,59 @@ __device__ __forceinline__ void st_elem(Rsrc rs, uint32_t index, float v) {
   }
 }
 
+// A lane's K consecutive stored values from element `first` (even, K even
+// for 16-bit formats in the word form). WIDE (16-bit formats with every row
+// tensor 4-byte aligned): two values per 32-bit access, low half first,
+// which the compiler merges into wider loads and stores; otherwise one
+// access per value.
+template <int F, bool WIDE>
+__device__ __forceinline__ float word_lo(uint32_t w) {
+  return F == MHC_COEFF_BF16 ? lo_f32(w) : f16_f32(static_cast<uint16_t>(w & 0xFFFFu));
+}
+template <int F, bool WIDE>
+__device__ __forceinline__ float word_hi(uint32_t w) {
+  return F == MHC_COEFF_BF16 ? hi_f32(w) : f16_f32(static_cast<uint16_t>(w >> 16));
+}
+
+template <int F, bool WIDE, int K>
+__device__ __forceinline__ void ld_row(Rsrc rs, uint32_t first, float (&out)[K]) {
+  if constexpr (F == MHC_COEFF_F32 || !WIDE) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) out[k] = ld_elem<F>(rs, first + k);
+  } else {
+    static_assert(K % 2 == 0, "rows hold an even number of values");
+#pragma unroll
+    for (int k = 0; k < K / 2; ++k) {
+      const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(rs, (first + 2 * k) * 2, 0, 0);
+      out[2 * k] = word_lo<F, WIDE>(w);
+      out[2 * k + 1] = word_hi<F, WIDE>(w);
+    }
+  }
+}
+
+template <int F, bool WIDE, int K>
+__device__ __forceinline__ void st_row(Rsrc rs, uint32_t first, const float (&v)[K]) {
+  if constexpr (F == MHC_COEFF_F32 || !WIDE) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) st_elem<F>(rs, first + k, v[k]);
+  } else {
+    // All words first, then the stores back to back (so that the compiler
+    // can merge them; nothing with side effects sits between them).
+    uint32_t w[K / 2];
+#pragma unroll
+    for (int k = 0; k < K / 2; ++k) {
+      float a = v[2 * k], b = v[2 * k + 1];
+      __asm__ volatile("" : "+v"(a), "+v"(b));  // as in st_elem
+      w[k] = F == MHC_COEFF_BF16 ? pack_bf16x2(a, b)
+                                 : static_cast<uint32_t>(to_f16(a)) |
+                                       (static_cast<uint32_t>(to_f16(b)) << 16);
+    }
+#pragma unroll
+    for (int k = 0; k < K / 2; ++k)
+      __builtin_amdgcn_raw_buffer_store_b32(w[k], rs, (first + 2 * k) * 2, 0, 0);
+  }
+}
+
 // The halving tree over the wave's 64 lanes: for off = 32, 16, 8, 4, 2, 1,
 // x[i] += x[i + off] for i < off; lane 0 ends with the tree's sum.
 template <int K>
@@ -145,7 +198,7 @@ struct Tile {
   static constexpr int kFloats = kRows * kTileStride;
 };
 
-template <int N, int F>
+template <int N, int F, bool WIDE>
 __device__ __forceinline__ void chunk_sums(
     const void* __restrict__ mix, const void* __restrict__ pre, const void* __restrict__ post,
     const void* __restrict__ grad_pre, const void* __restrict__ grad_post,
@@ -174,28 +227,27 @@ __device__ __forceinline__ void chunk_sums(
 
   float d[M];
   float x[M];
+  float p[N], gp[N], q[N], gq[N], gr[N * N];
+  ld_row<F, WIDE>(rs_mix, lane * M, x);
+  ld_row<F, WIDE>(rs_pre, lane * N, p);
+  ld_row<F, WIDE>(rs_gpre, lane * N, gp);
+  ld_row<F, WIDE>(rs_post, lane * N, q);
+  ld_row<F, WIDE>(rs_gpost, lane * N, gq);
+  ld_row<F, WIDE>(rs_gres, lane * N * N, gr);
 #pragma unroll
-  for (int j = 0; j < M; ++j) x[j] = ld_elem<F>(rs_mix, lane * M + j);
+  for (int i = 0; i < N; ++i) d[i] = gp[i] * (p[i] * (1.0f - p[i]));
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const float p = ld_elem<F>(rs_pre, lane * N + i);
-    const float gp = ld_elem<F>(rs_gpre, lane * N + i);
-    d[i] = gp * (p * (1.0f - p));
-  }
+  for (int i = 0; i < N; ++i) d[N + i] = gq[i] * (q[i] * (1.0f - q[i] / post_scale));
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const float q = ld_elem<F>(rs_post, lane * N + i);
-    const float gq = ld_elem<F>(rs_gpost, lane * N + i);
-    d[N + i] = gq * (q * (1.0f - q / post_scale));
-  }
-#pragma unroll
-  for (int i = 0; i < N * N; ++i) d[2 * N + i] = ld_elem<F>(rs_gres, lane * N * N + i);
+  for (int i = 0; i < N * N; ++i) d[2 * N + i] = gr[i];
 
+  float gm[M];
 #pragma unroll
   for (int j = 0; j < M; ++j) {
     const float a = j < N ? a_pre : (j < 2 * N ? a_post : a_res);
-    st_elem<F>(rs_gmix, lane * M + j, a * d[j]);
+    gm[j] = a * d[j];
   }
+  st_row<F, WIDE>(rs_gmix, lane * M, gm);
 
   float v[V];
   v[M] = 0.0f;
@@ -271,15 +323,15 @@ __device__ __forceinline__ void output_sum(const float* __restrict__ partial, ui
 }
 
 // Two-launch form, first launch. Grid: `chunks` blocks of 64 threads.
-template <int N, int F>
+template <int N, int F, bool WIDE>
 __global__ __launch_bounds__(64) void coeff_partial_kernel(
     const void* __restrict__ mix, const void* __restrict__ pre, const void* __restrict__ post,
     const void* __restrict__ grad_pre, const void* __restrict__ grad_post,
     const void* __restrict__ grad_res, const float* __restrict__ alpha, float post_scale,
     void* __restrict__ grad_mix, float* __restrict__ partial, int64_t rows, uint32_t chunks) {
   __shared__ __align__(16) float tile[Tile<N>::kFloats];
-  chunk_sums<N, F>(mix, pre, post, grad_pre, grad_post, grad_res, alpha, post_scale, grad_mix,
-                   partial, rows, chunks, blockIdx.x, threadIdx.x, true, tile);
+  chunk_sums<N, F, WIDE>(mix, pre, post, grad_pre, grad_post, grad_res, alpha, post_scale,
+                         grad_mix, partial, rows, chunks, blockIdx.x, threadIdx.x, true, tile);
 }
 
 // Two-launch form, second launch. Grid: m + 3 blocks of 64 threads, block v
@@ -299,7 +351,7 @@ __global__ __launch_bounds__(64) void coeff_reduce_kernel(const float* __restric
 // every output's second stage (the outputs split over its waves) and sets
 // the counter back to 0 for the next call. No block waits for another, so
 // every block runs to completion whatever the others do.
-template <int N, int W, int F>
+template <int N, int W, int F, bool WIDE>
 __global__ __launch_bounds__(64 * W) void coeff_fused_kernel(
     const void* __restrict__ mix, const void* __restrict__ pre, const void* __restrict__ post,
     const void* __restrict__ grad_pre, const void* __restrict__ grad_post,
@@ -313,8 +365,9 @@ __global__ __launch_bounds__(64 * W) void coeff_fused_kernel(
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t c = blockIdx.x * W + wave;
-  chunk_sums<N, F>(mix, pre, post, grad_pre, grad_post, grad_res, alpha, post_scale, grad_mix,
-                   partial, rows, chunks, c, lane, c < chunks, tiles + wave * Tile<N>::kFloats);
+  chunk_sums<N, F, WIDE>(mix, pre, post, grad_pre, grad_post, grad_res, alpha, post_scale,
+                         grad_mix, partial, rows, chunks, c, lane, c < chunks,
+                         tiles + wave * Tile<N>::kFloats);
   __syncthreads();
   if (threadIdx.x == 0) {
     __threadfence();
@@ -495,21 +548,26 @@ struct CoeffArgs {
   int64_t rows;
   uint32_t chunks;
   int32_t fmt;
+  bool wide;  // 16-bit formats: every row tensor 4-byte aligned (32-bit accesses)
 };
 
-template <int N, int F>
+template <int N, int F, bool WIDE>
 hipError_t launch_partial_f(const CoeffArgs& a, hipStream_t s, hipEvent_t start) {
-  return launch_kernel(coeff_partial_kernel<N, F>, dim3(a.chunks), dim3(64), s, start, nullptr,
-                       a.mix, a.pre, a.post, a.grad_pre, a.grad_post, a.grad_res, a.alpha, a.c,
-                       a.grad_mix, a.partial, a.rows, a.chunks);
+  return launch_kernel(coeff_partial_kernel<N, F, WIDE>, dim3(a.chunks), dim3(64), s, start,
+                       nullptr, a.mix, a.pre, a.post, a.grad_pre, a.grad_post, a.grad_res,
+                       a.alpha, a.c, a.grad_mix, a.partial, a.rows, a.chunks);
 }
 
 template <int N>
 hipError_t launch_partial(const CoeffArgs& a, hipStream_t s, hipEvent_t start) {
   switch (a.fmt) {
-    case MHC_COEFF_BF16: return launch_partial_f<N, MHC_COEFF_BF16>(a, s, start);
-    case MHC_COEFF_F16: return launch_partial_f<N, MHC_COEFF_F16>(a, s, start);
-    default: return launch_partial_f<N, MHC_COEFF_F32>(a, s, start);
+    case MHC_COEFF_BF16:
+      return a.wide ? launch_partial_f<N, MHC_COEFF_BF16, true>(a, s, start)
+                    : launch_partial_f<N, MHC_COEFF_BF16, false>(a, s, start);
+    case MHC_COEFF_F16:
+      return a.wide ? launch_partial_f<N, MHC_COEFF_F16, true>(a, s, start)
+                    : launch_partial_f<N, MHC_COEFF_F16, false>(a, s, start);
+    default: return launch_partial_f<N, MHC_COEFF_F32, false>(a, s, start);
   }
 }
 
@@ -521,27 +579,31 @@ hipError_t launch_partial(const CoeffArgs& a, hipStream_t s, hipEvent_t start) {
 // block's waves each sum fewer outputs). At n = 2 the same or better.
 constexpr uint32_t kTwoWaveMaxChunks = 64;
 
-template <int N, int W, int F>
+template <int N, int W, int F, bool WIDE>
 hipError_t launch_fused_w(const CoeffArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   const uint32_t blocks = (a.chunks + W - 1) / W;
-  return launch_kernel(coeff_fused_kernel<N, W, F>, dim3(blocks), dim3(64 * W), s, start, stop,
-                       a.mix, a.pre, a.post, a.grad_pre, a.grad_post, a.grad_res, a.alpha, a.c,
-                       a.grad_mix, a.partial, a.arrived, a.rows, a.chunks, a.grad_b,
+  return launch_kernel(coeff_fused_kernel<N, W, F, WIDE>, dim3(blocks), dim3(64 * W), s, start,
+                       stop, a.mix, a.pre, a.post, a.grad_pre, a.grad_post, a.grad_res, a.alpha,
+                       a.c, a.grad_mix, a.partial, a.arrived, a.rows, a.chunks, a.grad_b,
                        a.grad_alpha);
 }
 
-template <int N, int F>
+template <int N, int F, bool WIDE>
 hipError_t launch_fused_f(const CoeffArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
-  if (a.chunks <= kTwoWaveMaxChunks) return launch_fused_w<N, 2, F>(a, s, start, stop);
-  return launch_fused_w<N, 4, F>(a, s, start, stop);
+  if (a.chunks <= kTwoWaveMaxChunks) return launch_fused_w<N, 2, F, WIDE>(a, s, start, stop);
+  return launch_fused_w<N, 4, F, WIDE>(a, s, start, stop);
 }
 
 template <int N>
 hipError_t launch_fused(const CoeffArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   switch (a.fmt) {
-    case MHC_COEFF_BF16: return launch_fused_f<N, MHC_COEFF_BF16>(a, s, start, stop);
-    case MHC_COEFF_F16: return launch_fused_f<N, MHC_COEFF_F16>(a, s, start, stop);
-    default: return launch_fused_f<N, MHC_COEFF_F32>(a, s, start, stop);
+    case MHC_COEFF_BF16:
+      return a.wide ? launch_fused_f<N, MHC_COEFF_BF16, true>(a, s, start, stop)
+                    : launch_fused_f<N, MHC_COEFF_BF16, false>(a, s, start, stop);
+    case MHC_COEFF_F16:
+      return a.wide ? launch_fused_f<N, MHC_COEFF_F16, true>(a, s, start, stop)
+                    : launch_fused_f<N, MHC_COEFF_F16, false>(a, s, start, stop);
+    default: return launch_fused_f<N, MHC_COEFF_F32, false>(a, s, start, stop);
   }
 }
 
@@ -579,6 +641,12 @@ CoeffArgs make_args(const void* mix, const void* pre, const void* post, const vo
   a.rows = rows;
   a.chunks = static_cast<uint32_t>(chunk_count(rows));
   a.fmt = fmt;
+  // Rows hold an even number of values at every n (2n + n^2, n and n^2),
+  // so with 4-byte-aligned bases every row starts 4-byte aligned.
+  a.wide = true;
+  for (const void* t : {mix, pre, post, grad_pre, grad_post, grad_res,
+                        static_cast<const void*>(grad_mix)})
+    if (reinterpret_cast<uintptr_t>(t) % 4 != 0) a.wide = false;
   return a;
 }
 

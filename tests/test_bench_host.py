@@ -174,7 +174,9 @@ def test_coefficient_epilogue_bytes():
     assert bench.coeff_bytes(8192, 4) == 8192 * 320 + 120
     assert bench.coeff_bytes(10, 2) == 10 * (64 + 48) + 12 + 32 + 12
     assert bench.coeff_bytes(10, 8) == 10 * (256 + 768) + 12 + 320 + 12
-    assert [r for r, n in bench.COEFF_SWEEP if n == 4] == [512, 2048, 8192]
+    assert [r for r, n, d in bench.COEFF_SWEEP if n == 4 and d == "f32"] == [512, 2048, 8192]
+    assert [r for r, n, d in bench.COEFF_SWEEP if d == "bf16"] == [512, 2048, 8192]
+    assert bench.coeff_bytes(10, 4, 2) == 10 * 160 + 12 + 96 + 12
 
 
 def test_counter_cases_are_valid_launch_shapes(built_library):
