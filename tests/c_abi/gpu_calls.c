@@ -5,8 +5,11 @@
  *          DIR/grad_out.bin (bf16 bits, T*H) and the coefficient epilogue's
  *          inputs DIR/c_mix.bin, c_pre.bin, c_post.bin, c_grad_pre.bin,
  *          c_grad_post.bin, c_grad_res.bin, c_alpha.bin (fp32, R rows, n = 4);
- *   writes DIR/out.bin, grad_residual.bin, grad_pre.bin and c_grad_mix.bin,
- *          c_grad_b.bin, c_grad_alpha.bin.
+ *          and the same six row tensors as bf16 bits in DIR/c16_*.bin;
+ *   writes DIR/out.bin, grad_residual.bin, grad_pre.bin, c_grad_mix.bin,
+ *          c_grad_b.bin, c_grad_alpha.bin (workspace entry point), the same
+ *          from the entry point that allocates nothing (c_na_*.bin), and the
+ *          bf16 call's c16_grad_mix.bin, c16_grad_b.bin, c16_grad_alpha.bin.
  * Exit status 0 on success; a failure prints what failed. */
 #define __HIP_PLATFORM_AMD__
 #include <hip/hip_runtime_api.h>
@@ -122,6 +125,37 @@ int main(int argc, char** argv) {
   if (download(dir, "c_grad_mix.bin", gmix, (size_t)(R * m * 4)) ||
       download(dir, "c_grad_b.bin", gb, (size_t)(m * 4)) ||
       download(dir, "c_grad_alpha.bin", ga, 12))
+    return 1;
+
+  /* the entry point that allocates nothing, into fresh outputs */
+  void *na_gmix, *na_gb, *na_ga;
+  HIP_CHECK(hipMalloc(&na_gmix, (size_t)(R * m * 4)));
+  HIP_CHECK(hipMalloc(&na_gb, (size_t)(m * 4)));
+  HIP_CHECK(hipMalloc(&na_ga, 12));
+  MHC_CHECK(mhc_coeff_bwd_noalloc(mix, cpre, post, gpre, gpost, gres, alpha, 2.0f, na_gmix,
+                                  na_gb, na_ga, R, n, 0, NULL, NULL, NULL));
+  HIP_CHECK(hipDeviceSynchronize());
+  if (download(dir, "c_na_grad_mix.bin", na_gmix, (size_t)(R * m * 4)) ||
+      download(dir, "c_na_grad_b.bin", na_gb, (size_t)(m * 4)) ||
+      download(dir, "c_na_grad_alpha.bin", na_ga, 12))
+    return 1;
+
+  /* bf16 row tensors through mhc_coeff_bwd_ex, on the same workspace */
+  void *b_mix, *b_pre, *b_post, *b_gpre, *b_gpost, *b_gres, *b_gmix;
+  if (upload(dir, "c16_mix.bin", (size_t)(R * m * 2), &b_mix) ||
+      upload(dir, "c16_pre.bin", (size_t)(R * n * 2), &b_pre) ||
+      upload(dir, "c16_post.bin", (size_t)(R * n * 2), &b_post) ||
+      upload(dir, "c16_grad_pre.bin", (size_t)(R * n * 2), &b_gpre) ||
+      upload(dir, "c16_grad_post.bin", (size_t)(R * n * 2), &b_gpost) ||
+      upload(dir, "c16_grad_res.bin", (size_t)(R * n * n * 2), &b_gres))
+    return 1;
+  HIP_CHECK(hipMalloc(&b_gmix, (size_t)(R * m * 2)));
+  MHC_CHECK(mhc_coeff_bwd_ex(b_mix, b_pre, b_post, b_gpre, b_gpost, b_gres, alpha, 2.0f, b_gmix,
+                             gb, ga, ws, ws_bytes, R, n, MHC_COEFF_BF16, 0, NULL, NULL, NULL));
+  HIP_CHECK(hipDeviceSynchronize());
+  if (download(dir, "c16_grad_mix.bin", b_gmix, (size_t)(R * m * 2)) ||
+      download(dir, "c16_grad_b.bin", gb, (size_t)(m * 4)) ||
+      download(dir, "c16_grad_alpha.bin", ga, 12))
     return 1;
   printf("c gpu calls ok\n");
   return 0;

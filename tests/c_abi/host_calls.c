@@ -93,6 +93,16 @@ int main(void) {
     CHECK(strlen(mhc_coeff_last_error_message()) > 0);
     CHECK(mhc_coeff_bwd(mix, cpre, post, gpre, gpost, gres, alpha, 2.0f, gmix, gb, ga, ws,
                         ws_bytes - 4, R, n, 0, NULL, NULL, NULL) == MHC_ERROR_INVALID_VALUE);
+    /* 16-bit row tensors need 2-byte alignment only; an unknown format is refused */
+    CHECK(mhc_coeff_bwd_validate_ex(mix, (const char*)cpre + 2, post, gpre, gpost, gres, alpha,
+                                    2.0f, gmix, gb, ga, ws, ws_bytes, R, n, MHC_COEFF_BF16) ==
+          MHC_SUCCESS);
+    CHECK(mhc_coeff_bwd_validate_ex(mix, cpre, post, gpre, gpost, gres, alpha, 2.0f, gmix, gb,
+                                    ga, ws, ws_bytes, R, n, 7) == MHC_ERROR_INVALID_VALUE);
+    /* the entry point that allocates nothing refuses calls past its array */
+    CHECK(mhc_coeff_bwd_noalloc(mix, cpre, post, gpre, gpost, gres, alpha, 2.0f, gmix, gb, ga,
+                                MHC_COEFF_SCRATCH_BYTES, n, 0, NULL, NULL, NULL) ==
+          MHC_ERROR_INVALID_VALUE);
   }
   printf("c abi ok\n");
   return 0;

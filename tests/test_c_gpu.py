@@ -1,4 +1,6 @@
-"""Both libraries on the GPU from a plain C99 program (tests/c_abi/gpu_calls.c):
+"""Both operation libraries on the GPU from a plain C99 program
+(tests/c_abi/gpu_calls.c), including the coefficient epilogue's bf16 and
+no-allocation entry points:
 device memory from the HIP runtime, the null stream, no Python or torch in
 the process. Its outputs are compared with the oracle byte for byte."""
 
@@ -39,6 +41,9 @@ def test_c_program_on_the_gpu_matches_the_oracle(built_library, tmp_path):
     ch = make_coeff_inputs(R, 4, seed=71)
     for k in ("mix", "pre", "post", "grad_pre", "grad_post", "grad_res", "alpha"):
         np.ascontiguousarray(ch[k]).tofile(tmp_path / f"c_{k}.bin")
+    c16 = {k: CB.narrow(ch[k], "bf16") for k in CB.ROW_INPUTS}
+    for k, v in c16.items():
+        np.ascontiguousarray(v).tofile(tmp_path / f"c16_{k}.bin")
     say(f"C program on the GPU: T={T} H={H} R={R}")
     r = subprocess.run([str(exe), str(tmp_path), str(T), str(H), str(R)], capture_output=True,
                        text=True, timeout=120)
@@ -56,3 +61,11 @@ def test_c_program_on_the_gpu_matches_the_oracle(built_library, tmp_path):
     assert_bytes_equal(read("c_grad_mix.bin", np.float32, (R, 24)), want[0], "C grad_mix")
     assert_bytes_equal(read("c_grad_b.bin", np.float32, (24,)), want[1], "C grad_b")
     assert_bytes_equal(read("c_grad_alpha.bin", np.float32, (3,)), want[2], "C grad_alpha")
+    assert_bytes_equal(read("c_na_grad_mix.bin", np.float32, (R, 24)), want[0], "C noalloc grad_mix")
+    assert_bytes_equal(read("c_na_grad_b.bin", np.float32, (24,)), want[1], "C noalloc grad_b")
+    assert_bytes_equal(read("c_na_grad_alpha.bin", np.float32, (3,)), want[2],
+                       "C noalloc grad_alpha")
+    w16 = CB.coeff_bwd_typed(*(c16[k] for k in CB.ROW_INPUTS), ch["alpha"], 2.0, 4, "bf16")
+    assert_bytes_equal(read("c16_grad_mix.bin", np.uint16, (R, 24)), w16[0], "C bf16 grad_mix")
+    assert_bytes_equal(read("c16_grad_b.bin", np.float32, (24,)), w16[1], "C bf16 grad_b")
+    assert_bytes_equal(read("c16_grad_alpha.bin", np.float32, (3,)), w16[2], "C bf16 grad_alpha")
