@@ -575,6 +575,100 @@ class SweepTimer:
         self.ev.close()
 
 
+def wave_clock_summary(stamps, khz: int, dispatch_us: float | None = None) -> dict:
+    """Where and when a launch's waves ran, from mhc_clock_probe's stamps
+    ([units, 4]: start, loads returned, stores completed, XCD | HW_ID << 32).
+    Times in us from the launch's first wave start; per XCD (by id): its first
+    wave start, its last wave end, its wave count and median wave duration."""
+    import numpy as np
+    s = np.asarray(stamps, dtype=np.int64).reshape(-1, 4)
+    us = 1000.0 / khz
+    t0 = int(s[:, 0].min())
+    xcc = s[:, 3] & 0xFFFFFFFF
+    ids = sorted(int(x) for x in np.unique(xcc))
+    first = [round((int(s[xcc == x, 0].min()) - t0) * us, 3) for x in ids]
+    last = [round((int(s[xcc == x, 2].max()) - t0) * us, 3) for x in ids]
+    rec = {"waves": int(s.shape[0]), "span_us": round((int(s[:, 2].max()) - t0) * us, 3),
+           "xcd": ids, "xcd_waves": [int((xcc == x).sum()) for x in ids],
+           "xcd_first_start_us": first, "xcd_last_end_us": last,
+           "xcd_wave_us_median": [round(float(np.median(s[xcc == x, 2] - s[xcc == x, 0])) * us, 3)
+                                  for x in ids],
+           "start_stagger_us": round(max(first) - min(first), 3),
+           "end_spread_us": round(max(last) - min(last), 3)}
+    if dispatch_us is not None:
+        rec["dispatch_us"] = round(dispatch_us, 3)
+    return rec
+
+
+def median_records(recs: list[dict]) -> dict:
+    """Element-wise medians of wave_clock_summary records of one launch shape
+    (lists by position; the XCD ids must agree)."""
+    out = {}
+    for k, v in recs[0].items():
+        if k == "xcd":
+            assert all(r["xcd"] == v for r in recs), "XCD ids differ between launches"
+            out[k] = v
+        elif isinstance(v, list):
+            out[k] = [round(statistics.median(r[k][i] for r in recs), 3) for i in range(len(v))]
+        else:
+            out[k] = round(statistics.median(r[k] for r in recs), 3)
+    return out
+
+
+def run_wave_clock(path: str, T: int = 1024, H: int = 7168, reps: int = 5) -> None:
+    """Per-wave clock stamps of the streaming probe at the bytes and read:write
+    mix of the backward and of the forward at T, H, in blocks of 1, 4 and 16
+    waves: how a launch's waves spread over the XCDs and over time, with no
+    arithmetic in the way. Per shape, `reps` stamped launches that end a run
+    of 10 back-to-back launches ("stream") and `reps` launched on an idle
+    GPU ("alone"), each with its dispatch events; one JSON line per shape and
+    mode with the element-wise medians over the reps."""
+    import torch
+    from hyper_connection_residual_mhc_amd import _build, _lib, probes
+
+    _build.ensure_built()
+    plib = _lib.probe_lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sh = int(torch.cuda.current_stream(dev).cuda_stream)
+    khz = probes.mhc_probe_wall_clock_khz(dev)
+    ev = HipEvents(2)
+    ptr = lambda t: 0 if t is None else t.data_ptr()
+    size = lambda t: 0 if t is None else t.numel() * 4
+    with open(path, "w") as f:
+        for name in ("bwd", "fwd"):
+            nbytes = (bwd_bytes if name == "bwd" else fwd_bytes)(T, H)
+            pb = ProbeBuffers(nbytes, PROBE_MIX[name], 8, dev)
+            r, w = pb.mix
+            stamps = torch.zeros(4 * pb.units, dtype=torch.int64, device=dev)
+            for wpb in (1, 4, 16):
+                def launch(k, a, b, wpb=wpb):
+                    src, dst = pb.pairs[k % len(pb.pairs)]
+                    _lib.check_probe(plib.mhc_clock_probe(
+                        ptr(src), size(src), ptr(dst), size(dst), r, w, wpb, stamps.data_ptr(),
+                        stamps.numel(), sh, a, b))
+                for mode in ("stream", "alone"):
+                    recs = []
+                    for rep in range(reps):
+                        for k in range(10):
+                            launch(k, None, None)
+                        if mode == "alone":
+                            torch.cuda.synchronize()
+                        launch(10 + rep, ev.handles[0], ev.handles[1])
+                        torch.cuda.synchronize()
+                        recs.append(wave_clock_summary(stamps.cpu().numpy(), khz,
+                                                       ev.elapsed_us(0, 1)))
+                    rec = {"probe": f"{r}:{w}", "like": name, "T": T, "H": H,
+                           "bytes": pb.bytes, "units": pb.units, "waves_per_block": wpb,
+                           "mode": mode, "reps": reps, "wall_clock_khz": khz,
+                           **median_records(recs)}
+                    f.write(json.dumps(rec) + "\n")
+                    f.flush()
+                    print(json.dumps(rec), flush=True)
+            del pb, stamps
+    ev.close()
+
+
 def run_sweep(path: str, rounds: int = 7, warm: int = 10, timed: int = 100,
               part: str = "all") -> None:
     """Per-call forward and backward times at SWEEP_SHAPES, one JSON line per
@@ -1147,6 +1241,9 @@ def main(argv: list[str] | None = None, gpu_runner=None) -> int:
     ap.add_argument("--sweep-part", choices=("all", "h_aggregate", "coeff", "expansion"),
                     default="all",
                     help="with --sweep: which operations to time")
+    ap.add_argument("--wave-clock", metavar="OUT_JSONL",
+                    help="instead of the step benchmark, stamp the streaming probe's waves at "
+                         "the kernels' bytes (where and when each wave ran) and write JSON lines")
     ap.add_argument("--counter-case", choices=sorted(COUNTER_CASES) + sorted(FWD_COUNTER_CASES),
                     help="instead of the step benchmark, run 64 backward (or forward) calls in "
                          "one launch shape (for rocprofv3 --pmc runs) and print one JSON line")
@@ -1169,6 +1266,12 @@ def main(argv: list[str] | None = None, gpu_runner=None) -> int:
     if args.counter_case:
         print(json.dumps(run_counter_case(args.counter_case, args.tokens, args.hidden,
                                           nsets=args.sets)))
+        return 0
+    if args.wave_clock:
+        if args.gpus != 1:
+            print("the wave clock runs on one GPU", file=sys.stderr)
+            return 2
+        run_wave_clock(args.wave_clock, args.tokens, args.hidden)
         return 0
     if args.sweep:
         if args.gpus != 1:

@@ -112,7 +112,7 @@ COEFF_SIGNATURES = {
 MHC_COEFF_F32, MHC_COEFF_BF16, MHC_COEFF_F16 = 0, 1, 2
 MHC_COEFF_SCRATCH_BYTES = 2 << 20
 
-MHC_PROBE_ABI_VERSION = 1
+MHC_PROBE_ABI_VERSION = 2
 
 # Every symbol csrc/mhc_probes.h declares.
 PROBE_SIGNATURES = {
@@ -121,6 +121,9 @@ PROBE_SIGNATURES = {
     "mhc_bf16_rne_probe": (c_int, [c_uint32, c_int64, c_void_p, c_void_p]),
     "mhc_stream_probe": (c_int, [c_void_p, c_int64, c_void_p, c_int64, c_int32, c_int32,
                                  c_void_p, c_void_p, c_void_p]),
+    "mhc_clock_probe": (c_int, [c_void_p, c_int64, c_void_p, c_int64, c_int32, c_int32, c_int32,
+                                c_void_p, c_int64, c_void_p, c_void_p, c_void_p]),
+    "mhc_probe_wall_clock_khz": (c_int, [POINTER(c_int32)]),
 }
 
 _loaded: dict[str, ctypes.CDLL] = {}

@@ -22,7 +22,7 @@
 extern "C" {
 #endif
 
-#define MHC_PROBE_ABI_VERSION 1
+#define MHC_PROBE_ABI_VERSION 2
 
 int mhc_probe_abi_version(void);
 
@@ -65,6 +65,33 @@ mhc_status mhc_bf16_rne_probe(uint32_t first_bits, int64_t n, uint16_t* out, voi
 mhc_status mhc_stream_probe(const void* src, int64_t src_bytes, void* dst, int64_t dst_bytes,
                             int32_t reads, int32_t writes, void* stream, void* start_event,
                             void* stop_event);
+
+/*
+ * Clock probe: the streaming probe's units and mixes (same byte layout,
+ * cache policies and stored values), launched with `waves_per_block` units
+ * per block (1, 4 or 16: blocks of 64, 256 or 1024 threads), where every
+ * wave also stamps when it ran and where. Shows how a launch's waves are
+ * spread over the accelerator complexes (XCDs) and over time, for any
+ * launch shape, with no arithmetic in the way.
+ *   stamps: [4 * units] uint64, 8-byte aligned, disjoint from src and dst;
+ *   stamps_len is its element count (at least 4 * units). For unit u:
+ *     stamps[4u + 0]  device wall clock as the wave starts,
+ *     stamps[4u + 1]  ... once all its loads have returned,
+ *     stamps[4u + 2]  ... once all its stores have completed,
+ *     stamps[4u + 3]  XCC_ID (the XCD the wave ran on) in the low 32 bits,
+ *                     the wave's HW_ID register in the high 32 bits.
+ *   The wall clock is the device's constant-rate real-time counter (read
+ *   with s_memrealtime); mhc_probe_wall_clock_khz gives its rate.
+ *   start_event / stop_event as for mhc_stream_probe. Zero units launch
+ *   nothing and record the events.
+ */
+mhc_status mhc_clock_probe(const void* src, int64_t src_bytes, void* dst, int64_t dst_bytes,
+                           int32_t reads, int32_t writes, int32_t waves_per_block,
+                           uint64_t* stamps, int64_t stamps_len, void* stream,
+                           void* start_event, void* stop_event);
+
+/* Rate of the wall clock the clock probe reads, in kHz, for the current device. */
+mhc_status mhc_probe_wall_clock_khz(int32_t* khz);
 
 #ifdef __cplusplus
 }

@@ -205,3 +205,26 @@ def test_coefficient_cpu_baseline_record():
     rec = bench.run_coeff_cpu_baseline(64, 4, min_seconds=0.05)
     assert rec["kind"] == "oracle" and rec["cores"] == 1 and rec["unit"] == "us/call"
     assert rec["value"] > 0 and "64-row" in rec["sample"]
+
+
+def test_wave_clock_summary_reads_the_stamps():
+    import numpy as np
+    # 100 kHz ticks of 10 us; XCD 3 starts 2 ticks after XCD 0 and ends last
+    stamps = np.array([
+        [100, 105, 110, 0 | (7 << 32)],
+        [101, 104, 108, 0],
+        [102, 110, 120, 3],
+        [104, 106, 107, 3],
+    ], dtype=np.int64)
+    rec = bench.wave_clock_summary(stamps, 100, dispatch_us=250.0)
+    assert rec["waves"] == 4 and rec["xcd"] == [0, 3] and rec["xcd_waves"] == [2, 2]
+    assert rec["span_us"] == 200.0
+    assert rec["xcd_first_start_us"] == [0.0, 20.0]
+    assert rec["xcd_last_end_us"] == [100.0, 200.0]
+    assert rec["xcd_wave_us_median"] == [85.0, 105.0]
+    assert rec["start_stagger_us"] == 20.0 and rec["end_spread_us"] == 100.0
+    assert rec["dispatch_us"] == 250.0
+    med = bench.median_records([rec, dict(rec, span_us=100.0), dict(rec, span_us=300.0)])
+    assert med["span_us"] == 200.0 and med["xcd"] == [0, 3]
+    with pytest.raises(AssertionError):
+        bench.median_records([rec, dict(rec, xcd=[0, 4])])

@@ -73,6 +73,7 @@ def test_kernels_present(asm):
     if any("probe" in n for n in names):
         assert sum("bf16_probe_kernel" in n for n in names) == 1
         assert sum("stream_probe_kernel" in n for n in names) == 6
+        assert sum("clock_probe_kernel" in n for n in names) == 6
         assert not any("hagg_" in n or "coeff_" in n for n in names)
         return
     assert any("hagg_fwd_kernel" in n for n in names)
@@ -171,8 +172,8 @@ def test_separate_fp32_mul_and_add_present(asm):
 
 def test_bf16_results_use_rne_pack_conversion(asm):
     for name, body in kernel_blocks(asm).items():
-        if "stream_probe_kernel" in name or "coeff_" in name:
-            continue  # no bf16 value produced (a byte stream; fp32 in and out)
+        if "stream_probe_kernel" in name or "clock_probe_kernel" in name or "coeff_" in name:
+            continue  # no bf16 value produced (byte streams; fp32 in and out)
         assert "v_cvt_pk_bf16_f32" in body, name
 
 

@@ -69,3 +69,26 @@ def test_stream_probe_rejects_bad_arguments_before_any_hip_call(lib):
     assert probe(0, 0, dst, 12 * KiB, 0, 8, None, None, None) == MHC_ERROR_INVALID_VALUE
     assert probe(0, 0, dst + 8, 16 * KiB, 0, 8, None, None, None) == MHC_ERROR_INVALID_VALUE
     assert probe(0, 0, 0, 0, 0, 8, None, None, None) == MHC_SUCCESS
+
+
+def test_clock_probe_rejects_bad_arguments_before_any_hip_call(lib):
+    src, dst, st = BASE, BASE + GiB, BASE + 2 * GiB
+    probe = lib.mhc_clock_probe
+    # 10 units of the 5:4 mix need 40 stamps
+    good = (src, 50 * KiB, dst, 40 * KiB, 5, 4)
+    for wpb in (0, 2, 3, 8, 32, -4):
+        assert probe(*good, wpb, st, 40, None, None, None) == MHC_ERROR_INVALID_VALUE, wpb
+    assert probe(*good, 4, st, 39, None, None, None) == MHC_ERROR_INVALID_VALUE
+    assert b"stamps" in lib.mhc_probe_last_error_message()
+    assert probe(*good, 4, st + 4, 40, None, None, None) == MHC_ERROR_INVALID_VALUE
+    assert probe(*good, 4, 0, 40, None, None, None) == MHC_ERROR_INVALID_VALUE
+    assert probe(*good, 4, src + 8 * KiB, 40, None, None, None) == MHC_ERROR_ALIASING
+    assert probe(*good, 4, dst + 39 * KiB, 40, None, None, None) == MHC_ERROR_ALIASING
+    # the stream probe's own rules apply
+    assert probe(src, 50 * KiB, dst, 40 * KiB, 5, 5, 4, st, 40, None, None,
+                 None) == MHC_ERROR_INVALID_VALUE
+    assert probe(src, 50 * KiB, src + 16 * KiB, 40 * KiB, 5, 4, 4, st, 40, None, None,
+                 None) == MHC_ERROR_ALIASING
+    # zero units launch nothing and need no stamps
+    assert probe(0, 0, 0, 0, 5, 4, 16, 0, 0, None, None, None) == MHC_SUCCESS
+    assert lib.mhc_probe_wall_clock_khz(None) == MHC_ERROR_INVALID_VALUE

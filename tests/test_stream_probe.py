@@ -71,3 +71,40 @@ def test_stream_probe_empty_is_a_no_op(device):
     e = torch.empty(0, dtype=torch.int32, device=device)
     probes.mhc_stream_probe(e, e, 5, 4)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("reads,writes", [(5, 4), (8, 0), (0, 8)])
+@pytest.mark.parametrize("waves_per_block", [1, 4, 16])
+@pytest.mark.parametrize("units", [1, 5, 300])
+def test_clock_probe_moves_the_same_bytes_and_stamps_every_wave(device, reads, writes,
+                                                                waves_per_block, units):
+    say(f"clock probe {reads}:{writes} waves_per_block={waves_per_block} units={units}")
+    rng = np.random.default_rng(reads * 100 + writes + units + 7 * waves_per_block)
+    src_words = rng.integers(0, 2**32, size=units * reads * KiB // 4,
+                             dtype=np.uint64).astype(np.uint32)
+    src = torch.from_numpy(src_words.view(np.int32)).to(device) if reads else None
+    guard = 4096
+    buf = torch.full((units * writes * KiB // 4 + 2 * guard,), -1, dtype=torch.int32,
+                     device=device)
+    dst = buf[guard:guard + units * writes * KiB // 4] if writes else None
+    stamps = torch.full((4 * units + 64,), -1, dtype=torch.int64, device=device)
+    probes.mhc_clock_probe(src, dst, reads, writes, waves_per_block, stamps)
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy().view(np.uint32)
+    if writes:
+        want = (expected(src_words, reads, writes) if reads else
+                np.repeat(np.arange(units, dtype=np.uint32), writes * KiB // 4))
+        assert np.array_equal(got[guard:-guard], want)
+    assert (got[:guard] == 0xFFFFFFFF).all() and (got[-guard:] == 0xFFFFFFFF).all()
+    s = stamps.cpu().numpy()
+    assert (s[4 * units:] == -1).all()
+    s = s[:4 * units].reshape(units, 4)
+    assert (s[:, 0] > 0).all()
+    assert (s[:, 0] <= s[:, 1]).all() and (s[:, 1] <= s[:, 2]).all()
+    assert ((s[:, 3] & 0xFFFFFFFF) < 16).all()
+    # a wave's clock readings span at most a second
+    assert ((s[:, 2] - s[:, 0]) < probes.mhc_probe_wall_clock_khz(device) * 1000).all()
+
+
+def test_wall_clock_rate_is_known(device):
+    assert probes.mhc_probe_wall_clock_khz(device) > 0
