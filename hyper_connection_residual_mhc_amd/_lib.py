@@ -20,9 +20,11 @@ MHC_SUCCESS = 0
 MHC_ERROR_INVALID_VALUE = 1
 MHC_ERROR_ALIASING = 2
 MHC_ERROR_HIP = 3
-MHC_ABI_VERSION = 4
+MHC_ABI_VERSION = 5
 MHC_BWD_SPLIT = 1
 MHC_BWD_ROWS = 2
+MHC_PRIO_FLAT = 1
+MHC_PRIO_PROGRESS = 2
 MHC_MAX_H = 1 << 26
 
 
@@ -35,6 +37,7 @@ class mhc_launch(ctypes.Structure):
         ("tokens_per_block", c_int32),
         ("streams_per_block", c_int32),
         ("layout", c_int32),
+        ("wave_priority", c_int32),
     ]
 
     def as_dict(self) -> dict:

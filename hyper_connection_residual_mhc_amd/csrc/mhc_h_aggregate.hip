@@ -30,6 +30,8 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -479,18 +481,31 @@ __device__ __forceinline__ void rows_consume(RowSlots<V, B, ACC>& sl, int b, uin
 // 16 chunk slots for 14 chunks; the exact count measured 1.2-1.7% faster
 // at T = 1024 to 8192).
 //
+// PROGRESS (exact-count rows only): the wave starts at issue priority 3 and
+// lowers it by one each time it has consumed another quarter of its row's
+// chunks (s_setprio; the priority among the waves of a SIMD). Without it
+// all waves share one priority and a CU serves its waves oldest first, so
+// a launch whose blocks are all resident at once finishes in a tail where
+// only each CU's youngest waves still stream; with it the waves of such a
+// launch progress together (measured at H = 7168: T = 512 12.18 -> 11.47
+// us, T = 1024 22.15 -> 21.28 us). When blocks start in several
+// generations, the new waves would outrank the old ones and delay the
+// slots they free (T = 2048 +10%, T = 8192 +13%), so the host uses it only
+// when every block of the launch can be resident at once.
+//
 // The arguments a wave needs before its first loads come first, so that the
 // build's kernel-argument preloading places them in scalar registers: no
 // argument load, block-size read or 64-bit division precedes the ring's
 // first requests (n is a power of two, passed as log2n; rows_per_block is
 // the block's wave count).
-template <int V, int B, bool ACC, int C>
+template <int V, int B, bool ACC, int C, bool PROGRESS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void hagg_bwd_rows_kernel(
     const uint16_t* __restrict__ residual, const uint16_t* __restrict__ grad_out,
     uint16_t* __restrict__ grad_residual, int64_t H, int64_t rows, uint32_t log2n,
     uint32_t rows_per_block, uint32_t ngroups, const float* __restrict__ pre,
     float* __restrict__ grad_pre) {
   static_assert(B % 4 == 0, "ring size must be a multiple of 4");
+  static_assert(!PROGRESS || C > 0, "progress priority needs the exact chunk count");
   const uint32_t lane = threadIdx.x & 63;
   const int64_t q = static_cast<int64_t>(blockIdx.x) * rows_per_block +
                     __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -507,6 +522,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void h
     // would otherwise be free to issue later chunks first, and the first
     // chunk's arithmetic would wait for most of the ring).
     constexpr int kFirst = C < B ? C : B;
+    if constexpr (PROGRESS) __builtin_amdgcn_s_setprio(3);
 #pragma unroll
     for (int b = 0; b < kFirst; ++b) {
       rows_issue(sl, b, lane + 64 * b, g_row, r_row, gr_row);
@@ -517,6 +533,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void h
     for (int c = 0; c < C; ++c) {
       rows_consume(sl, c % B, lane + 64 * c, w, acc[c & 3], gr_row);
       if (c + B < C) rows_issue(sl, c % B, lane + 64 * (c + B), g_row, r_row, gr_row);
+      if constexpr (PROGRESS) {
+        // Quarters of the row consumed before and after chunk c, capped at 3
+        // (constants once the loop is unrolled); priority 3 - quarters.
+        const int before = 4 * c / C < 3 ? 4 * c / C : 3;
+        const int after = 4 * (c + 1) / C < 3 ? 4 * (c + 1) / C : 3;
+        if (after != before) {
+          if (after == 1) __builtin_amdgcn_s_setprio(2);
+          if (after == 2) __builtin_amdgcn_s_setprio(1);
+          if (after == 3) __builtin_amdgcn_s_setprio(0);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
@@ -699,9 +726,11 @@ mhc_status plan_fwd(const uint16_t* residual, const uint16_t* out, int64_t T, in
                   ov->vec_width, (long long)H);
     V = ov->vec_width;
   }
-  if (ov && (ov->tokens_per_block != 0 || ov->streams_per_block != 0 || ov->layout != 0))
+  if (ov && (ov->tokens_per_block != 0 || ov->streams_per_block != 0 || ov->layout != 0 ||
+             ov->wave_priority != 0))
     return fail(MHC_ERROR_INVALID_VALUE,
-                "tokens_per_block, streams_per_block and layout are backward-only fields");
+                "tokens_per_block, streams_per_block, layout and wave_priority are backward-only "
+                "fields");
   const int64_t upt_units = H / V;  // units per token
   const int max_upt = fwd_max_upt(V, n);
   int upt = 1;
@@ -766,11 +795,36 @@ constexpr int rows_max_b(int V, bool acc) {
          : 4 * per_chunk <= budget ? 4 : 0;
 }
 
+// Compute units of the current device, cached per device; 256 (every gfx950
+// part) when no device can be queried, as when a plan is computed on a host
+// without a GPU.
+int64_t compute_units() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < kMaxDevices) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return 256;
+  if (dev < kMaxDevices) cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+// Waves every CU holds of any row-layout instance: the kernels are built for
+// at least 4 waves per SIMD (amdgpu_waves_per_eu), 4 SIMDs per CU.
+constexpr int64_t kResidentRowsPerCU = 16;
+
 struct BwdPlan {
   int layout;  // MHC_BWD_SPLIT or MHC_BWD_ROWS
   int V, U, S, tpb, n;
   int rows_per_block;  // row layout
   int fixed_chunks;    // row layout: the row's chunk count if compiled in, else 0
+  bool progress;       // row layout: issue priority by progress (PROGRESS instances)
   bool acc;
   int64_t ngroups, blocks_per_launch, total_blocks;
 };
@@ -850,6 +904,22 @@ mhc_status plan_bwd(const uint16_t* residual, const uint16_t* grad_out,
     pl->rows_per_block = R;
     const int64_t chunks = (pl->ngroups + 63) / 64;
     pl->fixed_chunks = V == 8 && chunks <= kMaxFixedChunks ? static_cast<int>(chunks) : 0;
+    // Issue priority by progress when every row of the call has a wave slot
+    // from the start (hagg_bwd_rows_kernel, PROGRESS): at n = 4 and 256 CUs,
+    // up to T = 1024.
+    bool progress = pl->fixed_chunks > 0 && T * n <= kResidentRowsPerCU * compute_units();
+    if (ov && ov->wave_priority != 0) {
+      if (ov->wave_priority != MHC_PRIO_FLAT && ov->wave_priority != MHC_PRIO_PROGRESS)
+        return fail(MHC_ERROR_INVALID_VALUE, "wave_priority must be 0, %d or %d", MHC_PRIO_FLAT,
+                    MHC_PRIO_PROGRESS);
+      if (ov->wave_priority == MHC_PRIO_PROGRESS && pl->fixed_chunks == 0)
+        return fail(MHC_ERROR_INVALID_VALUE,
+                    "wave_priority %d needs rows of at most %d chunks of 16-byte accesses "
+                    "(vec_width 8, H <= %d)",
+                    MHC_PRIO_PROGRESS, kMaxFixedChunks, kMaxFixedChunks * 64 * kGroup);
+      progress = ov->wave_priority == MHC_PRIO_PROGRESS;
+    }
+    pl->progress = progress;
     // Whole tokens per launch: blocks_per_launch * R rows is a multiple of n
     // (R and n are powers of two, n <= 8, and blocks_per_launch is a
     // multiple of 8).
@@ -859,6 +929,9 @@ mhc_status plan_bwd(const uint16_t* residual, const uint16_t* grad_out,
   }
   if (ov && ov->block_threads != 0 && ov->block_threads != kLanes)
     return fail(MHC_ERROR_INVALID_VALUE, "split-layout backward block_threads must be 0 or 256");
+  if (ov && ov->wave_priority != 0 && ov->wave_priority != MHC_PRIO_FLAT)
+    return fail(MHC_ERROR_INVALID_VALUE, "the split layout runs its waves at one priority "
+                "(wave_priority 0 or %d)", MHC_PRIO_FLAT);
   // Streams per block: all of a token's streams (up to four) in one block
   // once there are enough tokens to cover the CUs (grad_out is then read once
   // per block); shorter batches spread each token over more blocks to use
@@ -901,6 +974,7 @@ mhc_status plan_bwd(const uint16_t* residual, const uint16_t* grad_out,
   pl->tpb = tpb;
   pl->rows_per_block = 0;
   pl->fixed_chunks = 0;
+  pl->progress = false;
   pl->blocks_per_launch = kMaxLaunchThreads / kLanes / (n / S);
   pl->total_blocks = (T + tpb - 1) / tpb * (n / S);
   return ok();
@@ -1030,11 +1104,18 @@ hipError_t launch_rows_c(const BwdPlan& pl, const uint16_t* residual, const floa
                          int64_t tokens, int64_t H, hipStream_t stream, Events ev) {
   const int64_t rows = tokens * pl.n;
   const uint32_t blocks = static_cast<uint32_t>((rows + pl.rows_per_block - 1) / pl.rows_per_block);
-  return launch_kernel(hagg_bwd_rows_kernel<V, B, ACC, C>, dim3(blocks),
+  const uint32_t log2n = static_cast<uint32_t>(__builtin_ctz(static_cast<unsigned>(pl.n)));
+  if constexpr (C > 0) {
+    if (pl.progress)
+      return launch_kernel(hagg_bwd_rows_kernel<V, B, ACC, C, true>, dim3(blocks),
+                           dim3(64 * pl.rows_per_block), stream, ev.start, ev.stop, residual,
+                           grad_out, grad_residual, H, rows, log2n,
+                           static_cast<uint32_t>(pl.rows_per_block),
+                           static_cast<uint32_t>(pl.ngroups), pre, grad_pre);
+  }
+  return launch_kernel(hagg_bwd_rows_kernel<V, B, ACC, C, false>, dim3(blocks),
                        dim3(64 * pl.rows_per_block), stream, ev.start, ev.stop, residual, grad_out,
-                       grad_residual, H, rows,
-                       static_cast<uint32_t>(__builtin_ctz(static_cast<unsigned>(pl.n))),
-                       static_cast<uint32_t>(pl.rows_per_block),
+                       grad_residual, H, rows, log2n, static_cast<uint32_t>(pl.rows_per_block),
                        static_cast<uint32_t>(pl.ngroups), pre, grad_pre);
 }
 
@@ -1171,7 +1252,7 @@ mhc_status plan_fwd_query(const uint16_t* residual, const float* pre, const uint
   if (st != MHC_SUCCESS) return st;
   FwdPlan pl;
   if ((st = plan_fwd(residual, out, T, n, H, launch, &pl)) != MHC_SUCCESS) return st;
-  if (plan) *plan = mhc_launch{pl.block, pl.V, pl.upt, 0, 0, 0};
+  if (plan) *plan = mhc_launch{pl.block, pl.V, pl.upt, 0, 0, 0, 0};
   if (grid_blocks) *grid_blocks = pl.total_blocks;
   return ok();
 }
@@ -1188,8 +1269,9 @@ mhc_status plan_bwd_query(const uint16_t* residual, const float* pre, const uint
     return st;
   if (plan)
     *plan = pl.layout == MHC_BWD_ROWS
-                ? mhc_launch{64 * pl.rows_per_block, pl.V, pl.U, 0, 0, MHC_BWD_ROWS}
-                : mhc_launch{kLanes, pl.V, pl.U, pl.tpb, pl.S, MHC_BWD_SPLIT};
+                ? mhc_launch{64 * pl.rows_per_block, pl.V, pl.U, 0, 0, MHC_BWD_ROWS,
+                             pl.progress ? MHC_PRIO_PROGRESS : MHC_PRIO_FLAT}
+                : mhc_launch{kLanes, pl.V, pl.U, pl.tpb, pl.S, MHC_BWD_SPLIT, MHC_PRIO_FLAT};
   if (grid_blocks) *grid_blocks = pl.total_blocks;
   return ok();
 }

@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define MHC_ABI_VERSION 4
+#define MHC_ABI_VERSION 5
 
 /* Hyper-connection expansion rate of the page's operation (Summary: residual
  * [T, 4, H]). The *_n entry points below also take 2 and 8. */
@@ -105,7 +105,9 @@ typedef enum mhc_status {
  *                     refilled with the lane's next group once consumed -
  *                     1, 2 or 4 in the split layout (default: the most the
  *                     register budget allows), 4, 8 or 12 in the row layout
- *                     (default 8, fewer where the budget requires). More
+ *                     (default 12 for rows the library compiles for their
+ *                     exact chunk count, 8 otherwise, fewer where the
+ *                     budget requires). More
  *                     than the register budget allows for the vec_width,
  *                     layout, expansion rate and streams_per_block gives
  *                     MHC_ERROR_INVALID_VALUE; the plan query reports the
@@ -127,6 +129,19 @@ typedef enum mhc_status {
  *                     the row layout does not fit the register budget
  *                     (scalar-width accumulating calls). Same summation
  *                     order, same bits.
+ *   wave_priority     backward only: MHC_PRIO_FLAT (every wave at one issue
+ *                     priority; a CU then serves its waves oldest first) or
+ *                     MHC_PRIO_PROGRESS (row layout, rows of at most 16
+ *                     chunks of 16-byte accesses, i.e. vec_width 8 and
+ *                     H <= 8192: each wave starts at the highest priority
+ *                     and steps down as it consumes each quarter of its row,
+ *                     so the waves of a launch progress together). The
+ *                     policy takes MHC_PRIO_PROGRESS when every row of the
+ *                     call has a wave slot from the start (T * n <= 16 x
+ *                     the device's compute units: T <= 1024 at n = 4 on
+ *                     256 CUs; 256 CUs are assumed when no device can be
+ *                     queried), MHC_PRIO_FLAT otherwise. Issue order only:
+ *                     same bits.
  * Forward calls reject non-zero backward-only fields.
  */
 typedef struct mhc_launch {
@@ -136,11 +151,16 @@ typedef struct mhc_launch {
   int32_t tokens_per_block;
   int32_t streams_per_block;
   int32_t layout;
+  int32_t wave_priority;
 } mhc_launch;
 
 /* Backward layouts (mhc_launch.layout); both compute the same bits. */
 #define MHC_BWD_SPLIT 1 /* a token's 256 accumulator lanes over a block's 4 waves */
 #define MHC_BWD_ROWS 2  /* one wave per (token, stream) row, 4 lanes per wave lane */
+
+/* Backward issue priorities (mhc_launch.wave_priority); same bits. */
+#define MHC_PRIO_FLAT 1     /* one priority for every wave */
+#define MHC_PRIO_PROGRESS 2 /* row layout: priority steps down with the row's progress */
 
 /* Version of this ABI (MHC_ABI_VERSION of the built library). */
 int mhc_abi_version(void);

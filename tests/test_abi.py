@@ -181,10 +181,11 @@ def test_forward_overrides(lib):
                                                                    "vec_width": 2,
                                                                    "units_per_thread": 4})
     assert plan == {"block_threads": 1024, "vec_width": 2, "units_per_thread": 4,
-                    "tokens_per_block": 0, "streams_per_block": 0, "layout": 0}
+                    "tokens_per_block": 0, "streams_per_block": 0, "layout": 0,
+                    "wave_priority": 0}
     for bad in ({"block_threads": 100}, {"block_threads": 2048}, {"vec_width": 3},
                 {"units_per_thread": 3}, {"units_per_thread": 9}, {"tokens_per_block": 2},
-                {"streams_per_block": 1}, {"layout": 2}):
+                {"streams_per_block": 1}, {"layout": 2}, {"wave_priority": 1}):
         with pytest.raises(MhcError, match="INVALID_VALUE"):
             ops.mhc_h_aggregate_plan_fwd(r, p, o, T, H, launch=bad)
     with pytest.raises(MhcError, match="vec_width 8 not allowed"):
@@ -202,7 +203,8 @@ def test_backward_plan_and_overrides(lib):
     # longer rows 8)
     plan, grid = ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T, H)
     assert plan == {"block_threads": 256, "vec_width": 8, "units_per_thread": 12,
-                    "tokens_per_block": 0, "streams_per_block": 0, "layout": ROWS}
+                    "tokens_per_block": 0, "streams_per_block": 0, "layout": ROWS,
+                    "wave_priority": _lib.MHC_PRIO_FLAT}
     assert grid == T
     for H2, ring in ((8192, 12), (8200, 8)):
         plan, _ = ops.mhc_h_aggregate_plan_bwd(*bwd_ptrs(T, H2), T, H2)
@@ -214,7 +216,8 @@ def test_backward_plan_and_overrides(lib):
     # the split layout, asked for or implied by its own fields
     plan, grid = ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T, H, launch={"layout": SPLIT})
     assert plan == {"block_threads": 256, "vec_width": 8, "units_per_thread": 4,
-                    "tokens_per_block": 1, "streams_per_block": 4, "layout": SPLIT}
+                    "tokens_per_block": 1, "streams_per_block": 4, "layout": SPLIT,
+                    "wave_priority": _lib.MHC_PRIO_FLAT}
     assert grid == T
     plan, grid = ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T, H,
                                               launch={"tokens_per_block": 3, "vec_width": 4,
@@ -254,6 +257,10 @@ def test_backward_plan_and_overrides(lib):
         ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T, H,
                                      launch={"vec_width": 1, "units_per_thread": 8,
                                              "layout": ROWS})
+    for bad in ({"wave_priority": 3}, {"wave_priority": -1},
+                {"layout": SPLIT, "wave_priority": _lib.MHC_PRIO_PROGRESS}):
+        with pytest.raises(MhcError, match="INVALID_VALUE"):
+            ops.mhc_h_aggregate_plan_bwd(r, p, g, gr, gp, T, H, launch=bad)
     # grad_out misaligned by one element forces the scalar path
     plan, _ = ops.mhc_h_aggregate_plan_bwd(r, p, g + 2, gr, gp, T, H)
     assert plan["vec_width"] == 1 and plan["layout"] == ROWS and plan["units_per_thread"] == 4
@@ -411,3 +418,29 @@ def test_expansion_rate_rules(lib):
                                        launch={"streams_per_block": 4})
     assert lib.mhc_h_aggregate_bwd_n(rr, pp, g, gr, gp, 8, 4, H, 2, None, None, None,
                                      None) == MHC_ERROR_INVALID_VALUE
+
+
+def test_backward_issue_priority_policy(lib):
+    """Progress priority exactly when every row of the call has a wave slot
+    from the start: T * n <= 16 x compute units (256 here: the plan is
+    computed without a device, or on an MI355X), rows of at most 16 chunks
+    of 16-byte accesses; overridable both ways within those rows."""
+    FLAT, PROGRESS = _lib.MHC_PRIO_FLAT, _lib.MHC_PRIO_PROGRESS
+    H = 7168
+    r, p, g, gr, gp = bwd_ptrs(2048, 2 * H)
+    prio = lambda T, n=4, H=H, acc=0, **launch: ops.mhc_h_aggregate_plan_bwd_n(
+        r, p, g, gr, gp, T, n, H, accumulate=acc, launch=launch or None)[0]["wave_priority"]
+    assert prio(1024) == PROGRESS and prio(1025) == FLAT and prio(136) == PROGRESS
+    assert prio(1024, acc=1) == PROGRESS and prio(2048, acc=1) == FLAT
+    assert prio(2048, n=2) == PROGRESS and prio(2049, n=2) == FLAT
+    assert prio(512, n=8) == PROGRESS and prio(513, n=8) == FLAT
+    assert prio(1024, H=8192) == PROGRESS and prio(1024, H=8200) == FLAT   # looping rows
+    assert prio(100) == FLAT                                                 # split layout
+    assert prio(2048, wave_priority=PROGRESS) == PROGRESS
+    assert prio(1024, wave_priority=FLAT) == FLAT
+    assert prio(100, wave_priority=FLAT) == FLAT
+    for T, H2, launch in ((1024, 8200, {}), (1024, H, {"vec_width": 4}),
+                          (100, H, {"layout": _lib.MHC_BWD_SPLIT})):
+        with pytest.raises(MhcError, match="INVALID_VALUE"):
+            ops.mhc_h_aggregate_plan_bwd_n(r, p, g, gr, gp, T, 4, H2,
+                                           launch=dict(launch, wave_priority=PROGRESS))

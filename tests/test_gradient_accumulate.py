@@ -98,8 +98,10 @@ def test_accumulate_every_launch_shape_same_bytes(device, T, H):
             assert_bytes_equal(gr, want_gr, f"grad_residual {launch}")
             assert_bytes_equal(gp, want_gp, f"grad_pre {launch}")
     # row layout (not available at vec_width 1: register budget)
-    for v, u, bt in itertools.product([w for w in widths if w > 1], (4, 8, 12), (64, 256, 512)):
-        launch = {"layout": 2, "vec_width": v, "units_per_thread": u, "block_threads": bt}
+    for v, u, bt, prio in itertools.product([w for w in widths if w > 1], (4, 8, 12),
+                                            (64, 256, 512), (1, 2)):
+        launch = {"layout": 2, "vec_width": v, "units_per_thread": u, "block_threads": bt,
+                  "wave_priority": prio}
         try:
             ops.mhc_h_aggregate_plan_bwd_acc(1 << 34, 1 << 35, 1 << 36, 1 << 37, 1 << 38, T, H,
                                              launch=launch)

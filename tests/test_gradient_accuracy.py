@@ -152,22 +152,24 @@ def test_backward_matches_torch_autograd_loosely(device):
     torch.testing.assert_close(gp, p32.grad, atol=1e-3, rtol=1e-4)
 
 
+@pytest.mark.parametrize("prio", [1, 2])
 @pytest.mark.parametrize("acc", [False, True])
 @pytest.mark.parametrize("ring", [4, 8, 12])
-def test_row_layout_every_compiled_chunk_count(device, ring, acc):
+def test_row_layout_every_compiled_chunk_count(device, ring, acc, prio):
     """The row layout runs a kernel compiled for the row's chunk count when
     the row has at most 16 chunks of 512 elements (16-byte accesses), the
     looping kernel above that. H = 512c - 8, 512c and 512c + 8 reach every
     count from 1 to 17 with full and partly filled last chunks; every ring
-    size and both the written and the accumulating backward; bit-exact
-    against the oracle."""
+    size, both issue priorities (progress only for the compiled counts) and
+    both the written and the accumulating backward; bit-exact against the
+    oracle."""
     for c in range(1, 18):
         for H in (512 * c - 8, 512 * c, 512 * c + 8):
-            if H <= 0 or (acc and ring == 12):
+            if H <= 0 or (acc and ring == 12) or (prio == 2 and H > 8192):
                 continue
-            say(f"row layout chunks H={H} ring={ring} acc={acc}")
+            say(f"row layout chunks H={H} ring={ring} acc={acc} prio={prio}")
             host = make_inputs(3, H, seed=H + ring, grad=True)
-            launch = {"layout": ROWS, "units_per_thread": ring}
+            launch = {"layout": ROWS, "units_per_thread": ring, "wave_priority": prio}
             if not acc:
                 gr, gp = run_bwd(host, device, launch=launch)
                 check_bwd(host, gr, gp, f"H={H} ring={ring}")

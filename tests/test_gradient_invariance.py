@@ -82,10 +82,12 @@ def test_backward_every_launch_shape_gives_the_same_bytes(device, T, H):
         gr, gp = run_bwd(host, device, launch=launch)
         assert_bytes_equal(gr, want_gr, f"grad_residual {launch}")
         assert_bytes_equal(gp, want_gp, f"grad_pre {launch}")
-    # row layout: one wave per (token, stream) row, every ring size and rows
-    # per block the plan accepts (rings longer and shorter than the row)
-    for v, u, bt in itertools.product(widths, (4, 8, 12), (64, 128, 256, 512)):
-        launch = {"layout": ROWS, "vec_width": v, "units_per_thread": u, "block_threads": bt}
+    # row layout: one wave per (token, stream) row, every ring size, rows
+    # per block and issue priority the plan accepts (rings longer and shorter
+    # than the row)
+    for v, u, bt, prio in itertools.product(widths, (4, 8, 12), (64, 128, 256, 512), (1, 2)):
+        launch = {"layout": ROWS, "vec_width": v, "units_per_thread": u, "block_threads": bt,
+                  "wave_priority": prio}
         try:
             ops.mhc_h_aggregate_plan_bwd(1 << 34, 1 << 35, 1 << 36, 1 << 37, 1 << 38, T, H,
                                          launch=launch)
@@ -109,7 +111,8 @@ def test_backward_canaries(device):
                        {"streams_per_block": 1}, {"streams_per_block": 2, "tokens_per_block": 3},
                        {"layout": ROWS}, {"layout": ROWS, "vec_width": 1},
                        {"layout": ROWS, "block_threads": 64, "units_per_thread": 12},
-                       {"layout": ROWS, "block_threads": 512, "vec_width": 2}):
+                       {"layout": ROWS, "block_threads": 512, "vec_width": 2},
+                       {"layout": ROWS, "wave_priority": 1}, {"layout": ROWS, "wave_priority": 2}):
             say(f"backward canary 0x{s:x} {launch}")
             gr, grbuf = guarded_empty_bf16((T, 4, H), device, s)
             gpbuf = torch.full((T * 4 + 2 * GUARD,), float("nan"), dtype=torch.float32, device=device)
