@@ -488,7 +488,8 @@ __device__ __forceinline__ void rows_consume(RowSlots<V, B, ACC>& sl, int b, uin
 // a launch whose blocks are all resident at once finishes in a tail where
 // only each CU's youngest waves still stream; with it the waves of such a
 // launch progress together (measured at H = 7168: T = 512 12.18 -> 11.47
-// us, T = 1024 22.15 -> 21.28 us). When blocks start in several
+// us, T = 1024 22.15 -> 21.28 us; the accumulating form, with a third
+// stream of loads, gets 3-5% slower instead). When blocks start in several
 // generations, the new waves would outrank the old ones and delay the
 // slots they free (T = 2048 +10%, T = 8192 +13%), so the host uses it only
 // when every block of the launch can be resident at once.
@@ -906,8 +907,10 @@ mhc_status plan_bwd(const uint16_t* residual, const uint16_t* grad_out,
     pl->fixed_chunks = V == 8 && chunks <= kMaxFixedChunks ? static_cast<int>(chunks) : 0;
     // Issue priority by progress when every row of the call has a wave slot
     // from the start (hagg_bwd_rows_kernel, PROGRESS): at n = 4 and 256 CUs,
-    // up to T = 1024.
-    bool progress = pl->fixed_chunks > 0 && T * n <= kResidentRowsPerCU * compute_units();
+    // up to T = 1024. Not for the accumulating backward, which it slows
+    // (H = 7168, T * n = 2048 to 4096 rows, n = 2, 4, 8: 3-6% faster
+    // written, 3-5% slower accumulating).
+    bool progress = !acc && pl->fixed_chunks > 0 && T * n <= kResidentRowsPerCU * compute_units();
     if (ov && ov->wave_priority != 0) {
       if (ov->wave_priority != MHC_PRIO_FLAT && ov->wave_priority != MHC_PRIO_PROGRESS)
         return fail(MHC_ERROR_INVALID_VALUE, "wave_priority must be 0, %d or %d", MHC_PRIO_FLAT,

@@ -136,7 +136,8 @@ typedef enum mhc_status {
  *                     H <= 8192: each wave starts at the highest priority
  *                     and steps down as it consumes each quarter of its row,
  *                     so the waves of a launch progress together). The
- *                     policy takes MHC_PRIO_PROGRESS when every row of the
+ *                     policy takes MHC_PRIO_PROGRESS for the written (not
+ *                     the accumulating) backward when every row of the
  *                     call has a wave slot from the start (T * n <= 16 x
  *                     the device's compute units: T <= 1024 at n = 4 on
  *                     256 CUs; 256 CUs are assumed when no device can be

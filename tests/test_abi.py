@@ -421,17 +421,18 @@ def test_expansion_rate_rules(lib):
 
 
 def test_backward_issue_priority_policy(lib):
-    """Progress priority exactly when every row of the call has a wave slot
-    from the start: T * n <= 16 x compute units (256 here: the plan is
-    computed without a device, or on an MI355X), rows of at most 16 chunks
-    of 16-byte accesses; overridable both ways within those rows."""
+    """Progress priority for the written backward exactly when every row of
+    the call has a wave slot from the start: T * n <= 16 x compute units
+    (256 here: the plan is computed without a device, or on an MI355X),
+    rows of at most 16 chunks of 16-byte accesses; overridable both ways
+    within those rows, also for the accumulating backward."""
     FLAT, PROGRESS = _lib.MHC_PRIO_FLAT, _lib.MHC_PRIO_PROGRESS
     H = 7168
     r, p, g, gr, gp = bwd_ptrs(2048, 2 * H)
     prio = lambda T, n=4, H=H, acc=0, **launch: ops.mhc_h_aggregate_plan_bwd_n(
         r, p, g, gr, gp, T, n, H, accumulate=acc, launch=launch or None)[0]["wave_priority"]
     assert prio(1024) == PROGRESS and prio(1025) == FLAT and prio(136) == PROGRESS
-    assert prio(1024, acc=1) == PROGRESS and prio(2048, acc=1) == FLAT
+    assert prio(1024, acc=1) == FLAT and prio(1024, acc=1, wave_priority=PROGRESS) == PROGRESS
     assert prio(2048, n=2) == PROGRESS and prio(2049, n=2) == FLAT
     assert prio(512, n=8) == PROGRESS and prio(513, n=8) == FLAT
     assert prio(1024, H=8192) == PROGRESS and prio(1024, H=8200) == FLAT   # looping rows
