@@ -525,6 +525,11 @@ SWEEP_SHAPES = [  # (T, H): latency sweep, bandwidth shapes, backward shape
 ]
 # (T, H, n): the other expansion rates at the bandwidth shapes
 EXPANSION_SWEEP = [(1024, 7168, 2), (2048, 7168, 2), (1024, 7168, 8), (2048, 7168, 8)]
+# (T, H, n): the row-layout backward's two issue priorities, written and
+# accumulating, below, at and above one resident generation (T * n = 4,096
+# rows on 256 CUs)
+PRIORITY_SWEEP = [(512, 7168, 4), (768, 7168, 4), (1024, 7168, 4), (1536, 7168, 4),
+                  (2048, 7168, 4), (8192, 7168, 4), (2048, 7168, 2), (512, 7168, 8)]
 
 
 class SweepTimer:
@@ -682,8 +687,10 @@ def run_sweep(path: str, rounds: int = 7, warm: int = 10, timed: int = 100,
     block of its own after the kernel's (the reference column). Then the
     coefficient backward epilogue at COEFF_SWEEP, then forward, backward and
     accumulating backward at the other expansion rates (EXPANSION_SWEEP,
-    through the *_n entry points, without probes). `part` limits the sweep
-    to "h_aggregate", "coeff" or "expansion"."""
+    through the *_n entry points, without probes), then the row-layout
+    backward with each issue priority forced (PRIORITY_SWEEP, block-timed,
+    the two alternating round by round). `part` limits the sweep to
+    "h_aggregate", "coeff", "expansion" or "priority"."""
     import torch
     from hyper_connection_residual_mhc_amd import _build, _lib, ops
 
@@ -795,6 +802,40 @@ def run_sweep(path: str, rounds: int = 7, warm: int = 10, timed: int = 100,
                 emit(f, {"direction": direction, "T": T, "H": H, "n": n,
                          **SweepTimer.fields(nbytes, timings[0]),
                          "block": block_fields(nbytes, blk.block(call))})
+            del sets
+            torch.cuda.empty_cache()
+        for T, H, n in (PRIORITY_SWEEP if part in ("all", "priority") else []):
+            nsets = 8 if T <= 2048 else 3
+            sets = make_sets(T, H, nsets, dev, hc=n)
+            for acc in (0, 1):
+                nbytes = (bwd_acc_bytes if acc else bwd_bytes)(T, H, n)
+                s0 = sets[0]
+                policy, _ = ops.mhc_h_aggregate_plan_bwd_n(s0.residual, s0.pre, s0.grad_out,
+                                                           s0.grad_residual, s0.grad_pre, T, n,
+                                                           H, accumulate=bool(acc))
+                blocks = {}
+                # FLAT and PROGRESS alternate round by round, so that both
+                # see the same state of the GPU
+                one = Timer(sh, 1, warm, timed, check=_lib.check)
+                for _ in range(rounds):
+                    for prio in (_lib.MHC_PRIO_FLAT, _lib.MHC_PRIO_PROGRESS):
+                        launch = ops._launch_arg({"layout": _lib.MHC_BWD_ROWS,
+                                                  "wave_priority": prio})
+
+                        def call(k, a, b, acc=acc, launch=launch):
+                            x = sets[k % nsets]
+                            return lib.mhc_h_aggregate_bwd_n(
+                                x.residual.data_ptr(), x.pre.data_ptr(), x.grad_out.data_ptr(),
+                                x.grad_residual.data_ptr(), x.grad_pre.data_ptr(), T, n, H,
+                                acc, sh, launch, a, b)
+                        blocks.setdefault(prio, []).extend(one.block(call))
+                one.close()
+                flat = block_fields(nbytes, blocks[_lib.MHC_PRIO_FLAT])
+                prog = block_fields(nbytes, blocks[_lib.MHC_PRIO_PROGRESS])
+                emit(f, {"direction": "bwd_acc" if acc else "bwd", "T": T, "H": H, "n": n,
+                         "bytes": nbytes, "policy_wave_priority": policy["wave_priority"],
+                         "flat": flat, "progress": prog,
+                         "progress_over_flat": round(prog["us_median"] / flat["us_median"], 4)})
             del sets
             torch.cuda.empty_cache()
     tm.close()
@@ -1238,7 +1279,8 @@ def main(argv: list[str] | None = None, gpu_runner=None) -> int:
     ap.add_argument("--sweep", metavar="OUT_JSONL",
                     help="instead of the step benchmark, time each kernel per call at the "
                          "latency / bandwidth / backward shapes and write JSON lines")
-    ap.add_argument("--sweep-part", choices=("all", "h_aggregate", "coeff", "expansion"),
+    ap.add_argument("--sweep-part",
+                    choices=("all", "h_aggregate", "coeff", "expansion", "priority"),
                     default="all",
                     help="with --sweep: which operations to time")
     ap.add_argument("--wave-clock", metavar="OUT_JSONL",
