@@ -487,12 +487,15 @@ __device__ __forceinline__ void rows_consume(RowSlots<V, B, ACC>& sl, int b, uin
 // all waves share one priority and a CU serves its waves oldest first, so
 // a launch whose blocks are all resident at once finishes in a tail where
 // only each CU's youngest waves still stream; with it the waves of such a
-// launch progress together (measured at H = 7168: T = 512 12.18 -> 11.47
-// us, T = 1024 22.15 -> 21.28 us; the accumulating form, with a third
-// stream of loads, gets 3-5% slower instead). When blocks start in several
+// launch progress together (measured at H = 7168: T = 512 12.10 -> 11.35
+// us, T = 1024 22.02 -> 21.24 us; the accumulating form, with a third
+// stream of loads, gets 3-6% slower instead). When blocks start in several
 // generations, the new waves would outrank the old ones and delay the
-// slots they free (T = 2048 +10%, T = 8192 +13%), so the host uses it only
-// when every block of the launch can be resident at once.
+// slots they free (T = 2048 +14%, T = 8192 +12%), so the host uses it only
+// when every block of the launch can be resident at once. The choice is a
+// template argument, not a runtime branch: a branch joining inside the
+// ring makes the compiler wait for every outstanding access at each later
+// chunk.
 //
 // The arguments a wave needs before its first loads come first, so that the
 // build's kernel-argument preloading places them in scalar registers: no
@@ -908,8 +911,8 @@ mhc_status plan_bwd(const uint16_t* residual, const uint16_t* grad_out,
     // Issue priority by progress when every row of the call has a wave slot
     // from the start (hagg_bwd_rows_kernel, PROGRESS): at n = 4 and 256 CUs,
     // up to T = 1024. Not for the accumulating backward, which it slows
-    // (H = 7168, T * n = 2048 to 4096 rows, n = 2, 4, 8: 3-6% faster
-    // written, 3-5% slower accumulating).
+    // (H = 7168, T * n = 2048 to 4096 rows, n = 2, 4, 8: 3.5-6% faster
+    // written, 3-6% slower accumulating).
     bool progress = !acc && pl->fixed_chunks > 0 && T * n <= kResidentRowsPerCU * compute_units();
     if (ov && ov->wave_priority != 0) {
       if (ov->wave_priority != MHC_PRIO_FLAT && ov->wave_priority != MHC_PRIO_PROGRESS)
