@@ -527,9 +527,10 @@ SWEEP_SHAPES = [  # (T, H): latency sweep, bandwidth shapes, backward shape
 EXPANSION_SWEEP = [(1024, 7168, 2), (2048, 7168, 2), (1024, 7168, 8), (2048, 7168, 8)]
 # (T, H, n): the row-layout backward's two issue priorities, written and
 # accumulating, below, at and above one resident generation (T * n = 4,096
-# rows on 256 CUs)
+# rows on 256 CUs), and at other hidden sizes
 PRIORITY_SWEEP = [(512, 7168, 4), (768, 7168, 4), (1024, 7168, 4), (1536, 7168, 4),
-                  (2048, 7168, 4), (8192, 7168, 4), (2048, 7168, 2), (512, 7168, 8)]
+                  (2048, 7168, 4), (8192, 7168, 4), (2048, 7168, 2), (512, 7168, 8),
+                  (1024, 2048, 4), (512, 4096, 4), (1024, 4096, 4), (1024, 8192, 4)]
 
 
 class SweepTimer:
