@@ -128,3 +128,29 @@ def test_backward_canaries(device):
     want_gr, want_gp = O.h_aggregate_bwd(host["residual"], host["pre"], host["grad_out"])
     assert_bytes_equal(res[0][0], want_gr, "canary grad_residual")
     assert_bytes_equal(res[0][1], want_gp, "canary grad_pre")
+
+
+@pytest.mark.parametrize("acc", [False, True])
+def test_issue_priorities_give_the_same_bytes_at_full_size(device, acc):
+    """T=1024, H=7168 (the benchmark's backward, whose policy picks the
+    progress priority for the written form): both issue priorities, both
+    byte for byte equal to the policy's call."""
+    T, H = 1024, 7168
+    say(f"issue priorities T={T} H={H} acc={acc}")
+    host = make_inputs(T, H, seed=5, grad=True)
+    d = to_device(host, device)
+    old = to_device(make_inputs(T, H, seed=6), device)["residual"]
+    outs = []
+    for launch in (None, {"layout": ROWS, "wave_priority": 1}, {"layout": ROWS, "wave_priority": 2}):
+        gp = torch.empty((T, 4), dtype=torch.float32, device=device)
+        if acc:
+            gr = old.clone()
+            ops.mhc_h_aggregate_bwd_acc(d["residual"], d["pre"], d["grad_out"], gr, gp, launch=launch)
+        else:
+            gr = torch.empty((T, 4, H), dtype=torch.bfloat16, device=device)
+            ops.mhc_h_aggregate_bwd(d["residual"], d["pre"], d["grad_out"], gr, gp, launch=launch)
+        torch.cuda.synchronize()
+        outs.append((bf16_tensor_to_bits(gr), gp.cpu().numpy()))
+    for gr, gp in outs[1:]:
+        assert np.array_equal(gr, outs[0][0])
+        assert np.array_equal(gp.view(np.uint32), outs[0][1].view(np.uint32))
