@@ -54,6 +54,26 @@ int main(void) {
   CHECK(mhc_h_aggregate_plan_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, H, &ov,
                                  &plan, &blocks) == MHC_SUCCESS);
   CHECK(plan.layout == MHC_BWD_SPLIT && plan.streams_per_block == 4 && blocks == T);
+  CHECK(plan.wave_priority == MHC_PRIO_FLAT);
+
+  /* issue priority: the policy's choice is reported, an override is honoured
+     within the row layout and refused outside it */
+  memset(&ov, 0, sizeof ov);
+  ov.wave_priority = T * MHC_HC <= 16 * 256 ? MHC_PRIO_FLAT : MHC_PRIO_PROGRESS;
+  CHECK(mhc_h_aggregate_plan_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, H, &ov,
+                                 &plan, &blocks) == MHC_SUCCESS);
+  CHECK(plan.layout == MHC_BWD_ROWS && plan.wave_priority == ov.wave_priority);
+  ov.wave_priority = 3;
+  CHECK(mhc_h_aggregate_plan_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, H, &ov,
+                                 &plan, &blocks) == MHC_ERROR_INVALID_VALUE);
+  ov.wave_priority = MHC_PRIO_PROGRESS;
+  ov.layout = MHC_BWD_SPLIT;
+  CHECK(mhc_h_aggregate_plan_bwd(residual, pre, grad_out, grad_residual, grad_pre, T, H, &ov,
+                                 &plan, &blocks) == MHC_ERROR_INVALID_VALUE);
+  memset(&ov, 0, sizeof ov);
+  ov.wave_priority = MHC_PRIO_FLAT;
+  CHECK(mhc_h_aggregate_plan_fwd(residual, pre, out, T, H, &ov, &plan, &blocks) ==
+        MHC_ERROR_INVALID_VALUE);
 
   CHECK(mhc_h_aggregate_plan_bwd_n(residual, pre, grad_out, grad_residual, grad_pre, T, 3, H, 0,
                                    NULL, &plan, &blocks) == MHC_ERROR_INVALID_VALUE);
