@@ -142,7 +142,9 @@ typedef enum mhc_status {
  *                     the device's compute units: T <= 1024 at n = 4 on
  *                     256 CUs; 256 CUs are assumed when no device can be
  *                     queried), MHC_PRIO_FLAT otherwise. Issue order only:
- *                     same bits.
+ *                     same bits. The policy assumes the call has the GPU
+ *                     to itself; alongside other kernels that hold CUs,
+ *                     MHC_PRIO_FLAT may be the faster choice.
  * Forward calls reject non-zero backward-only fields.
  */
 typedef struct mhc_launch {
