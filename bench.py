@@ -861,6 +861,8 @@ COUNTER_CASES = {
     "rows-1-per-block": {"layout": 2, "block_threads": 64},
     "split": {"layout": 1},
     "rows-v4": {"layout": 2, "vec_width": 4},
+    "rows-flat": {"layout": 2, "wave_priority": 1},
+    "rows-progress": {"layout": 2, "wave_priority": 2},
 }
 # And of the forward: the policy (one-wave blocks, 16-byte accesses), the
 # page's 4-byte (bf16x2) accesses, and 1024-thread blocks.
